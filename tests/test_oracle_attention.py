@@ -1,0 +1,148 @@
+"""Pins of the oracle's attention over the compressed, paged cache."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (attention_dense, codebook_fp32, decode_paged, dequant_k, dequant_v,
+                    encode_k, encode_v, fwht, gaussian_matrix)
+from oracle.pages import K_PAGE_BYTES, V_PAGE_BYTES, write_slots_fast
+from oracle.qjl import qjl_alpha
+
+
+def _sdpa(q, k, v, scale):
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None], torch.from_numpy(k)[None, None],
+        torch.from_numpy(v)[None, None], scale=scale)
+    return out[0, 0, 0].numpy()
+
+
+def test_dense_attention_is_library_softmax_attention():
+    rng = np.random.default_rng(0)
+    for L in (1, 5, 300):
+        q = rng.standard_normal(16)
+        k = rng.standard_normal((L, 16)) * 3
+        v = rng.standard_normal((L, 16))
+        np.testing.assert_allclose(attention_dense(q, k, v, 0.25), _sdpa(q, k, v, 0.25), rtol=1e-12, atol=1e-13)
+    assert np.all(attention_dense(q, k[:0], v[:0], 1.0) == 0)
+
+
+@pytest.mark.parametrize("d", [4, 8, 16, 128])
+def test_rotated_domain_form_equals_definition(d):
+    # The fast form scores with H q and S q, accumulates codebook values in
+    # the rotated domain and applies one inverse rotation at the end.  It
+    # must equal the explicit definition up to rounding.
+    rng = np.random.default_rng(d)
+    c32, t32 = codebook_fp32(d, 3)
+    S = rng.standard_normal((d, d)).astype(np.float32)
+    L = 8 if d < 128 else 200
+    x = rng.standard_normal((L, d)) * 4
+    xv = rng.standard_normal((L, d)) * 2
+    q = rng.standard_normal(d)
+    ek = encode_k(x, c32, t32, S)
+    ev = encode_v(xv, c32, t32)
+    scale = 1 / math.sqrt(d)
+    ref = attention_dense(q, dequant_k(ek["codes"], ek["signs"], ek["norm_f16"], ek["gamma_f16"], c32, S),
+                          dequant_v(ev["codes"], ev["norm_f16"], c32), scale)
+    c = c32.astype(np.float64)
+    qr = fwht(q)
+    s = S.astype(np.float64) @ q
+    sig = 2.0 * ek["signs"] - 1.0
+    nk = ek["norm_f16"].astype(np.float64)
+    gk = ek["gamma_f16"].astype(np.float64)
+    sc = scale * nk * (c[ek["codes"].astype(int)] @ qr + qjl_alpha(d) * gk * (sig @ s))
+    p = np.exp(sc - sc.max())
+    acc = (p * ev["norm_f16"].astype(np.float64)) @ c[ev["codes"].astype(int)]
+    fast = fwht(acc / p.sum())
+    np.testing.assert_allclose(fast, ref, rtol=1e-11, atol=1e-12)
+
+
+def _pool(rng, T, Hkv, c32, t32, S, x=None, xv=None):
+    nb = (T + 15) // 16
+    x = rng.standard_normal((T, Hkv, 128)) * 3 if x is None else x
+    xv = rng.standard_normal((T, Hkv, 128)) if xv is None else xv
+    ek = encode_k(x, c32, t32, S)
+    ev = encode_v(xv, c32, t32)
+    kp = np.zeros((nb, Hkv, K_PAGE_BYTES), np.uint8)
+    vp = np.zeros((nb, Hkv, V_PAGE_BYTES), np.uint8)
+    perm = rng.permutation(nb)
+    slots = perm[np.arange(T) // 16] * 16 + np.arange(T) % 16
+    write_slots_fast(kp, vp, slots, ek, ev)
+    return kp, vp, perm[None].astype(np.int32), ek, ev
+
+
+def test_paged_special_cases():
+    rng = np.random.default_rng(1)
+    c32, t32 = codebook_fp32()
+    S = gaussian_matrix(42)
+    kp, vp, table, ek, ev = _pool(rng, 40, 2, c32, t32, S)
+    q = rng.standard_normal((1, 1, 4, 128))
+    vals = [dequant_v(ev["codes"][:, h], ev["norm_f16"][:, h], c32) for h in range(2)]
+    # one visible token -> its value
+    o = decode_paged(q, kp, vp, table, np.array([1]), c32, S)
+    for hq in range(4):
+        np.testing.assert_allclose(o[0, 0, hq], vals[hq // 2][0], rtol=1e-12)
+    # zero query -> plain mean of the values
+    o = decode_paged(np.zeros_like(q), kp, vp, table, np.array([40]), c32, S)
+    for hq in range(4):
+        np.testing.assert_allclose(o[0, 0, hq], vals[hq // 2].mean(axis=0), rtol=1e-12, atol=1e-14)
+    # empty context -> zeros
+    o = decode_paged(q, kp, vp, table, np.array([0]), c32, S)
+    assert np.all(o == 0)
+
+
+def test_without_qjl_term_is_softmax_attention_on_rotated_back_levels():
+    rng = np.random.default_rng(2)
+    c32, t32 = codebook_fp32()
+    S = gaussian_matrix(42)
+    T = 50
+    x = rng.standard_normal((T, 1, 128)) * 3
+    kp, vp, table, ek, ev = _pool(rng, T, 1, c32, t32, S, x=x)
+    # force every gamma to +0.0 in the pool
+    kp[:, :, 1056:1088] = 0
+    q = rng.standard_normal((1, 1, 1, 128))
+    o = decode_paged(q, kp, vp, table, np.array([T]), c32, S)
+    keys = ek["norm_f16"][:, 0, None].astype(np.float64) * fwht(c32.astype(np.float64)[ek["codes"][:, 0].astype(int)])
+    vals = ev["norm_f16"][:, 0, None].astype(np.float64) * fwht(c32.astype(np.float64)[ev["codes"][:, 0].astype(int)])
+    np.testing.assert_allclose(o[0, 0, 0], _sdpa(q[0, 0, 0], keys, vals, 1 / math.sqrt(128)), rtol=1e-11)
+
+
+def test_block_table_permutation_and_gqa_mapping():
+    rng = np.random.default_rng(3)
+    c32, t32 = codebook_fp32()
+    S = gaussian_matrix(42)
+    T, Hkv = 70, 2
+    kp, vp, table, ek, ev = _pool(rng, T, Hkv, c32, t32, S)
+    q = rng.standard_normal((1, 1, 8, 128))
+    o1 = decode_paged(q, kp, vp, table, np.array([T]), c32, S)
+    # relabel the physical blocks: same logical content, same answer
+    nb = kp.shape[0]
+    relabel = rng.permutation(nb)
+    kp2 = np.empty_like(kp)
+    vp2 = np.empty_like(vp)
+    kp2[relabel] = kp
+    vp2[relabel] = vp
+    o2 = decode_paged(q, kp2, vp2, relabel[table], np.array([T]), c32, S)
+    np.testing.assert_array_equal(o1, o2)
+    # q-heads 0..3 read KV head 0, 4..7 read KV head 1
+    for hq in range(8):
+        h = hq // 4
+        keys = dequant_k(ek["codes"][:, h], ek["signs"][:, h], ek["norm_f16"][:, h], ek["gamma_f16"][:, h], c32, S)
+        vals = dequant_v(ev["codes"][:, h], ev["norm_f16"][:, h], c32)
+        np.testing.assert_allclose(o1[0, 0, hq], attention_dense(q[0, 0, hq], keys, vals, 1 / math.sqrt(128)), rtol=1e-12)
+
+
+def test_causal_rows_equal_single_query_calls():
+    rng = np.random.default_rng(4)
+    c32, t32 = codebook_fp32()
+    S = gaussian_matrix(42)
+    T, q_len = 45, 6
+    kp, vp, table, _, _ = _pool(rng, T, 1, c32, t32, S)
+    q = rng.standard_normal((1, q_len, 2, 128))
+    o = decode_paged(q, kp, vp, table, np.array([T]), c32, S)
+    for t in range(q_len):
+        single = decode_paged(q[:, t:t + 1], kp, vp, table, np.array([T - q_len + t + 1]), c32, S)
+        np.testing.assert_array_equal(o[:, t], single[:, 0])
+    # the rows differ: each sees one more key than the previous
+    assert not np.allclose(o[0, 0], o[0, 1])

@@ -1,0 +1,92 @@
+"""Pins of the page layout: sizes, bit positions, round trips, fast forms."""
+import numpy as np
+
+from oracle import pages as P
+
+
+def test_page_sizes_give_the_pages_bit_widths():
+    assert P.K_PAGE_BYTES == 1088 and P.V_PAGE_BYTES == 800
+    assert P.K_PAGE_BYTES * 8 / (P.BLOCK * P.HEAD_DIM) == 4.25
+    assert P.V_PAGE_BYTES * 8 / (P.BLOCK * P.HEAD_DIM) == 3.125
+    overall = (P.K_PAGE_BYTES + P.V_PAGE_BYTES) * 8 / (2 * P.BLOCK * P.HEAD_DIM)
+    assert overall == 3.6875
+    assert abs(16 / overall - 4.339) < 1e-3
+
+
+def test_hand_placed_bits():
+    codes = np.zeros((16, 128), np.uint8)
+    signs = np.zeros((16, 128), np.uint8)
+    codes[3, 9] = 5            # binary 101 -> planes 0 and 2
+    signs[3, 9] = 1
+    n16 = np.zeros(16, np.float16)
+    g16 = np.zeros(16, np.float16)
+    n16[3] = np.float16(2.0)   # 0x4000
+    g16[3] = np.float16(-0.5)  # 0xB800
+    k = P.pack_k_page(codes, signs, n16, g16)
+    # coordinate 9 -> byte 1, bit 1 of token 3's 16-byte record
+    assert k[0 * 256 + 16 * 3 + 1] == 0b10
+    assert k[1 * 256 + 16 * 3 + 1] == 0
+    assert k[2 * 256 + 16 * 3 + 1] == 0b10
+    assert k[768 + 16 * 3 + 1] == 0b10
+    assert (k[1024 + 6], k[1025 + 6]) == (0x00, 0x40)
+    assert (k[1056 + 6], k[1057 + 6]) == (0x00, 0xB8)
+    assert int(np.count_nonzero(k)) == 5
+    v = P.pack_v_page(codes, n16)
+    # coordinate 9's 16-bit word holds token 3 at bit 3
+    assert v[0 * 256 + 2 * 9] == 0b1000 and v[0 * 256 + 2 * 9 + 1] == 0
+    assert v[2 * 256 + 2 * 9] == 0b1000
+    assert v[1 * 256 + 2 * 9] == 0
+    assert (v[768 + 6], v[769 + 6]) == (0x00, 0x40)
+    assert int(np.count_nonzero(v)) == 3
+
+
+def test_round_trips():
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 8, (16, 128)).astype(np.uint8)
+    signs = rng.integers(0, 2, (16, 128)).astype(np.uint8)
+    n16 = rng.uniform(0, 100, 16).astype(np.float16)
+    g16 = rng.uniform(0, 1, 16).astype(np.float16)
+    c2, s2, n2, g2 = P.unpack_k_page(P.pack_k_page(codes, signs, n16, g16))
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2, signs)
+    np.testing.assert_array_equal(n2, n16)
+    np.testing.assert_array_equal(g2, g16)
+    c3, n3 = P.unpack_v_page(P.pack_v_page(codes, n16))
+    np.testing.assert_array_equal(c3, codes)
+    np.testing.assert_array_equal(n3, n16)
+
+
+def _random_enc(rng, T, H):
+    return ({"codes": rng.integers(0, 8, (T, H, 128)).astype(np.uint8),
+             "signs": rng.integers(0, 2, (T, H, 128)).astype(np.uint8),
+             "norm_f16": rng.uniform(0, 100, (T, H)).astype(np.float16),
+             "gamma_f16": rng.uniform(0, 1, (T, H)).astype(np.float16)},
+            {"codes": rng.integers(0, 8, (T, H, 128)).astype(np.uint8),
+             "norm_f16": rng.uniform(0, 100, (T, H)).astype(np.float16)})
+
+
+def test_fast_writer_and_readers_match_plain_ones():
+    rng = np.random.default_rng(1)
+    nb, H, T = 7, 2, 40
+    base_k = rng.integers(0, 256, (nb, H, P.K_PAGE_BYTES)).astype(np.uint8)
+    base_v = rng.integers(0, 256, (nb, H, P.V_PAGE_BYTES)).astype(np.uint8)
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[[3, 17]] = -1                                   # skipped tokens
+    ek, ev = _random_enc(rng, T, H)
+    k1, v1 = base_k.copy(), base_v.copy()
+    k2, v2 = base_k.copy(), base_v.copy()
+    P.write_slots(k1, v1, slots, ek, ev)
+    P.write_slots_fast(k2, v2, slots, ek, ev)
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)
+    row = rng.permutation(nb)
+    for L in (0, 1, 16, 37, nb * 16):
+        for h in range(H):
+            a = P.read_k_tokens(k1, row, L, h)
+            b = P.read_k_tokens_fast(k1, row, L, h)
+            for x, y in zip(a, b):
+                np.testing.assert_array_equal(x, y)
+            a = P.read_v_tokens(v1, row, L, h)
+            b = P.read_v_tokens_fast(v1, row, L, h)
+            for x, y in zip(a, b):
+                np.testing.assert_array_equal(x, y)
