@@ -1,0 +1,340 @@
+// C-ABI host layer of libtq: argument checking, the Lloyd-Max codebook and
+// QJL matrix (double precision on the host), workspace planning and kernel
+// dispatch.  Every check happens before any HIP call, so rejected calls touch
+// nothing on the device.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tq_status hip_fail(hipError_t e, const char *what) {
+  return fail(TQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- Lloyd-Max for N(0,1), symmetric half ---------------------------------
+// The levels of a symmetric density come in +- pairs and (for an even count)
+// the middle threshold is 0, so only the positive cells are iterated:
+// cells (0, t_1], (t_1, t_2], ..., (t_{n-1}, inf) with levels c_1 < ... < c_n,
+// t_k = (c_k + c_{k+1}) / 2, c_k = E[X | cell k] = (phi(a) - phi(b)) / (Q(a) - Q(b))
+// (lilting.ch article, "Lloyd-Maxコードブックとは": levels fitted to the known
+// N(0, 1/d) density by the Lloyd-Max iteration, once, before inference).
+
+double std_pdf(double x) {
+  if (std::isinf(x)) return 0.0;
+  return std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+}
+
+double std_q(double x) {  // P(X > x), x >= 0
+  if (std::isinf(x)) return 0.0;
+  return 0.5 * std::erfc(x / std::sqrt(2.0));
+}
+
+void lloyd_max_positive_half(int half, std::vector<double> &c) {
+  c.resize(half);
+  for (int k = 0; k < half; ++k) c[k] = (k + 0.5) * (2.0 / half);  // any increasing start
+  std::vector<double> edge(half + 1);
+  for (int it = 0; it < 100000; ++it) {
+    edge[0] = 0.0;
+    for (int k = 1; k < half; ++k) edge[k] = 0.5 * (c[k - 1] + c[k]);
+    edge[half] = INFINITY;
+    double moved = 0.0;
+    for (int k = 0; k < half; ++k) {
+      const double a = edge[k], b = edge[k + 1];
+      const double nc = (std_pdf(a) - std_pdf(b)) / (std_q(a) - std_q(b));
+      moved = std::fmax(moved, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (moved < 1e-15) break;
+  }
+}
+
+bool codebook_supported(int head_dim, int bits, int qjl_dim) {
+  return head_dim == tq::kHeadDim && bits == 3 && qjl_dim == tq::kQjlDim;
+}
+
+tq_status check_cb(const tq_codebook *cb) {
+  if (!cb) return fail(TQ_ERR_INVALID_ARGUMENT, "codebook is NULL");
+  if (cb->magic != tq::kMagic) return fail(TQ_ERR_NOT_INITIALIZED, "codebook not initialised by tq_codebook_init");
+  if (!cb->d_tables) return fail(TQ_ERR_NOT_INITIALIZED, "codebook has no device tables");
+  return TQ_OK;
+}
+
+tq::Codebook device_codebook(const tq_codebook *cb) {
+  tq::Codebook d;
+  for (int i = 0; i < 8; ++i) d.c[i] = cb->centroids[i];
+  for (int i = 0; i < 7; ++i) d.t[i] = cb->thresholds[i];
+  d.qjl_scale = cb->qjl_scale;
+  return d;
+}
+
+bool dtype_ok(int d) { return d == TQ_F32 || d == TQ_F16 || d == TQ_BF16; }
+
+// ---- split-K planning ------------------------------------------------------
+// Chunks are multiples of 256 tokens (the workgroup's 4 waves x 64 tokens);
+// the automatic choice aims at about 1024 workgroups so that all 256 compute
+// units get several, and depends only on the call's sizes (no device query),
+// so the workspace size and the launch always agree.
+void plan_splits(int num_seqs, int q_len, int num_kv_heads, int max_ctx, int requested,
+                 int *split_tokens, int *num_splits) {
+  int st;
+  if (requested > 0) {
+    st = requested;
+  } else {
+    const long rows = (long)num_seqs * q_len * num_kv_heads;
+    long want = (1024 + rows - 1) / rows;
+    if (want < 1) want = 1;
+    long per = (max_ctx + want - 1) / want;
+    per = ((per + 255) / 256) * 256;
+    if (per < 256) per = 256;
+    st = (int)per;
+  }
+  int ns = max_ctx > 0 ? (max_ctx + st - 1) / st : 1;
+  *split_tokens = st;
+  *num_splits = ns;
+}
+
+constexpr size_t kPartStride = 132;  // floats per partial record: m, l, pad, pad, acc[128]
+
+}  // namespace
+
+namespace tq {
+size_t decode_qprep_floats(int64_t rows) { return (size_t)rows * 256; }
+size_t decode_partial_floats(int64_t rows, int num_splits) {
+  return (size_t)rows * (size_t)num_splits * kPartStride;
+}
+}  // namespace tq
+
+extern "C" {
+
+const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+tq_status tq_codebook_compute(int head_dim, int bits, float *centroids, float *thresholds) {
+  if (!centroids || !thresholds) return fail(TQ_ERR_INVALID_ARGUMENT, "null output array");
+  if (bits < 1 || bits > 4) return fail(TQ_ERR_UNSUPPORTED, "bits must be in [1, 4], got %d", bits);
+  if (head_dim < 1) return fail(TQ_ERR_INVALID_ARGUMENT, "head_dim must be positive");
+  const int levels = 1 << bits, half = levels / 2;
+  std::vector<double> pos;
+  lloyd_max_positive_half(half, pos);
+  const double s = std::sqrt((double)head_dim);
+  for (int k = 0; k < half; ++k) {
+    centroids[half + k] = (float)(pos[k] / s);
+    centroids[half - 1 - k] = (float)(-pos[k] / s);
+  }
+  thresholds[half - 1] = 0.0f;
+  for (int k = 1; k < half; ++k) {
+    const double t = 0.5 * (pos[k - 1] + pos[k]);
+    thresholds[half - 1 + k] = (float)(t / s);
+    thresholds[half - 1 - k] = (float)(-t / s);
+  }
+  return TQ_OK;
+}
+
+tq_status tq_qjl_matrix(uint64_t seed, int rows, int cols, float *out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARGUMENT, "null output");
+  if (rows < 1 || cols < 1) return fail(TQ_ERR_INVALID_ARGUMENT, "rows and cols must be positive");
+  uint64_t state = seed;
+  auto next = [&state]() -> uint64_t {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  };
+  const long n = (long)rows * cols;
+  for (long k = 0; k < n; k += 2) {
+    const double u1 = ((double)(next() >> 11) + 0.5) * 0x1.0p-53;
+    const double u2 = ((double)(next() >> 11) + 0.5) * 0x1.0p-53;
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    const double th = 2.0 * M_PI * u2;
+    out[k] = (float)(r * std::cos(th));
+    if (k + 1 < n) out[k + 1] = (float)(r * std::sin(th));
+  }
+  return TQ_OK;
+}
+
+size_t tq_codebook_device_bytes(int head_dim, int qjl_dim) {
+  if (head_dim < 1 || qjl_dim < 1) return 0;
+  return 2 * (size_t)head_dim * (size_t)qjl_dim * sizeof(float);
+}
+
+tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl_seed,
+                           const float *qjl_host, void *d_tables, void *stream) {
+  if (!cb) return fail(TQ_ERR_INVALID_ARGUMENT, "codebook is NULL");
+  if (!d_tables) return fail(TQ_ERR_INVALID_ARGUMENT, "d_tables is NULL");
+  if (!codebook_supported(head_dim, bits, tq::kQjlDim))
+    return fail(TQ_ERR_UNSUPPORTED, "only head_dim=128, bits=3 are supported (got %d, %d)", head_dim, bits);
+  tq_codebook c;
+  std::memset(&c, 0, sizeof c);
+  c.head_dim = head_dim;
+  c.bits = bits;
+  c.qjl_dim = tq::kQjlDim;
+  c.block_size = tq::kBlock;
+  c.qjl_seed = qjl_host ? 0 : qjl_seed;
+  tq_status st = tq_codebook_compute(head_dim, bits, c.centroids, c.thresholds);
+  if (st != TQ_OK) return st;
+  c.qjl_scale = (float)(std::sqrt(M_PI / 2.0) / tq::kQjlDim);
+  const int m = tq::kQjlDim, d = head_dim;
+  std::vector<float> host(2 * (size_t)m * d);
+  if (qjl_host) {
+    std::memcpy(host.data(), qjl_host, sizeof(float) * m * d);
+  } else {
+    st = tq_qjl_matrix(qjl_seed, m, d, host.data());
+    if (st != TQ_OK) return st;
+  }
+  for (int i = 0; i < m; ++i)
+    for (int k = 0; k < d; ++k) host[(size_t)m * d + (size_t)k * m + i] = host[(size_t)i * d + k];
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(d_tables, host.data(), host.size() * sizeof(float),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables)");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  c.d_tables = d_tables;
+  c.magic = tq::kMagic;
+  *cb = c;
+  return TQ_OK;
+}
+
+size_t tq_k_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::kKPage : 0; }
+size_t tq_v_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::kVPage : 0; }
+
+tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_dtype in_dtype,
+                       int64_t num_tokens, int num_kv_heads, int64_t tok_stride,
+                       int64_t head_stride, const int64_t *slot_mapping, uint8_t *k_cache,
+                       uint8_t *v_cache, float *norms_out, void *stream) {
+  tq_status st = check_cb(cb);
+  if (st != TQ_OK) return st;
+  if (num_tokens < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_tokens < 0");
+  if (num_kv_heads < 1) return fail(TQ_ERR_INVALID_ARGUMENT, "num_kv_heads must be >= 1");
+  if (num_kv_heads > 65535) return fail(TQ_ERR_UNSUPPORTED, "num_kv_heads > 65535");
+  if (!dtype_ok(in_dtype)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown in_dtype %d", (int)in_dtype);
+  if (num_tokens == 0) return TQ_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (tok_stride < 0 || head_stride < 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "negative stride");
+  if (num_tokens > 1 && tok_stride < tq::kHeadDim && head_stride < tq::kHeadDim)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "strides overlap the 128 contiguous coordinates");
+  if ((num_tokens + 15) / 16 > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_tokens too large");
+  tq::EncodeArgs a;
+  a.k = k;
+  a.v = v;
+  a.dtype = in_dtype;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.tok_stride = tok_stride;
+  a.head_stride = head_stride;
+  a.slots = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.norms_out = norms_out;
+  a.S = (const float *)cb->d_tables;
+  a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
+  a.cb = device_codebook(cb);
+  hipError_t e = tq::launch_encode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "encode launch");
+  return TQ_OK;
+}
+
+size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
+                                 int num_q_heads, int num_kv_heads, int max_context_len,
+                                 int tokens_per_split) {
+  (void)cb;
+  if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0)
+    return 0;
+  int stok, ns;
+  plan_splits(num_seqs, q_len, num_kv_heads, max_context_len, tokens_per_split, &stok, &ns);
+  const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
+  return (tq::decode_qprep_floats(rows) + tq::decode_partial_floats(rows, ns)) * sizeof(float);
+}
+
+tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                              const uint8_t *k_cache, const uint8_t *v_cache,
+                              const int32_t *block_tables, int max_blocks_per_seq,
+                              const int32_t *context_lens, int num_seqs, int q_len,
+                              int num_q_heads, int num_kv_heads, int max_context_len,
+                              float softmax_scale, void *out, tq_dtype out_dtype,
+                              int tokens_per_split, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  tq_status st = check_cb(cb);
+  if (st != TQ_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "num_seqs, q_len and head counts must be >= 1");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "num_q_heads (%d) not a multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  const int group = num_q_heads / num_kv_heads;
+  if (group > tq::kMaxGroup) return fail(TQ_ERR_UNSUPPORTED, "more than %d query heads per KV head", tq::kMaxGroup);
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return fail(TQ_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8 or 16 (got %d)", group);
+  if (max_context_len < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "max_context_len < 0");
+  if (q_len > 1 && q_len > max_context_len)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "q_len (%d) > max_context_len (%d)", q_len, max_context_len);
+  if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * tq::kBlock < max_context_len)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "max_blocks_per_seq (%d) cannot hold max_context_len (%d)",
+                max_blocks_per_seq, max_context_len);
+  if (tokens_per_split < 0 || (tokens_per_split > 0 && tokens_per_split % 256 != 0))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "tokens_per_split must be 0 or a positive multiple of 256");
+  if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
+    return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if ((int64_t)num_seqs * q_len > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_seqs * q_len too large");
+  int stok, ns;
+  plan_splits(num_seqs, q_len, num_kv_heads, max_context_len, tokens_per_split, &stok, &ns);
+  if (ns > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many splits (%d); raise tokens_per_split", ns);
+  const size_t need = tq_decode_workspace_bytes(cb, num_seqs, q_len, num_q_heads, num_kv_heads,
+                                                max_context_len, tokens_per_split);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  tq::DecodeArgs a;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.q_len = q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)tq::kHeadDim));
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.split_tokens = stok;
+  a.num_splits = ns;
+  a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
+  const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
+  a.qprep = (float *)workspace;
+  a.partials = (float *)workspace + tq::decode_qprep_floats(rows);
+  a.cb = device_codebook(cb);
+  hipError_t e = tq::launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return TQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal interface between the C-ABI host layer (tq_host.cpp) and the HIP
+// kernels (tq_encode.hip, tq_decode.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kHeadDim = 128;
+constexpr int kQjlDim = 128;
+constexpr int kBlock = 16;
+constexpr int kKPage = 1088;
+constexpr int kVPage = 800;
+constexpr int kMaxGroup = 16;       // query heads per KV head handled by one workgroup
+constexpr uint32_t kMagic = 0x54513031u;  // "TQ01"
+
+// Offsets inside a K page / V page (see tq.h).
+constexpr int kKPlane = 256;        // bytes per code bit-plane
+constexpr int kKSigns = 768;
+constexpr int kKNorm = 1024;
+constexpr int kKGamma = 1056;
+constexpr int kVNorm = 768;
+
+struct Codebook {
+  float c[8];        // ascending levels
+  float t[7];        // thresholds
+  float qjl_scale;   // sqrt(pi/2)/m
+};
+
+struct EncodeArgs {
+  const void *k;
+  const void *v;
+  int dtype;
+  int64_t num_tokens;
+  int num_kv_heads;
+  int64_t tok_stride;
+  int64_t head_stride;
+  const int64_t *slots;
+  uint8_t *k_cache;
+  uint8_t *v_cache;
+  float *norms_out;
+  const float *S;    // [m][d]
+  const float *St;   // [d][m]
+  Codebook cb;
+};
+
+struct DecodeArgs {
+  const void *q;
+  int q_dtype;
+  const uint8_t *k_cache;
+  const uint8_t *v_cache;
+  const int32_t *block_tables;
+  int max_blocks;
+  const int32_t *context_lens;
+  int num_seqs;
+  int q_len;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;           // num_q_heads / num_kv_heads
+  float scale;
+  void *out;
+  int out_dtype;
+  int split_tokens;
+  int num_splits;
+  const float *St;     // [d][m]
+  float *qprep;        // workspace: [rows][256] = rotated q | qjl_scale * S q
+  float *partials;     // workspace: [rows][num_splits][2 + 128]
+  Codebook cb;
+};
+
+// Workspace split of tq_decode_attention.
+size_t decode_qprep_floats(int64_t rows);
+size_t decode_partial_floats(int64_t rows, int num_splits);
+
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace tq

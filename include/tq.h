@@ -1,0 +1,186 @@
+/*
+ * tq.h -- C ABI of libtq: TurboQuant KV-cache compression and attention read
+ * directly from the compressed, paged cache, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources: SwiftLM README, section "TurboQuantization: KV Cache
+ * Compression"; lilting.ch SwiftLM article, sections "Lloyd-Maxコードブックとは",
+ * "KVキャッシュ圧縮の内訳" and "Walsh-Hadamard Transform（WHT）の役割"; 0h-n0
+ * vLLM-MLX explainer, section "Paged KVキャッシュ"):
+ *   key   (4.25 bits/coordinate): norm -> normalise -> Walsh-Hadamard rotation
+ *         -> 3-bit Lloyd-Max code per coordinate for N(0, 1/d) -> residual
+ *         against the quantised vector -> 1-bit signs of a random Gaussian
+ *         (QJL) projection of that residual;
+ *   value (3.125 bits/coordinate): the same without the QJL stage.
+ *
+ * Conventions for every entry point:
+ *   - All functions return tq_status; nothing throws across the ABI.  On a
+ *     non-OK status tq_last_error() returns a thread-local message.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     rejected call launches nothing and leaves every buffer untouched.
+ *   - Device pointers are plain HIP device addresses owned by the caller.
+ *     The library never allocates, frees or synchronises in the encode and
+ *     attention calls; work is enqueued on the caller's HIP stream
+ *     (hipStream_t passed as void*, NULL = default stream) and is complete
+ *     when that stream is.
+ *   - Only head_dim = 128, qjl_dim = 128, 3-bit codes and 16-token blocks are
+ *     supported; other values give TQ_ERR_UNSUPPORTED.
+ *   - Not checked (caller contract): block-table entries lie inside the
+ *     pools, context lengths cover only slots that were encoded, and
+ *     slot_mapping holds no duplicate slot.
+ *
+ * Page layout (little-endian; bit b of a byte has weight 2^b), one page per
+ * (block, KV head), pools k_cache[num_blocks][num_kv_heads][1088] and
+ * v_cache[num_blocks][num_kv_heads][800], slot = block * 16 + offset:
+ *   K page: [256p, 256p+256), p = 0..2: bit-plane p of the codes, token t at
+ *           256p + 16t, coordinate i at bit i of that 128-bit record;
+ *           [768, 1024): QJL sign bits (1 = projection >= 0), token t at
+ *           768 + 16t; [1024, 1056): half norm of token t at 1024 + 2t;
+ *           [1056, 1088): half residual length gamma at 1056 + 2t.
+ *   V page: [256p, 256p+256), p = 0..2: bit-plane p, coordinate-major:
+ *           coordinate i owns the 16-bit word at 256p + 2i, token t at its
+ *           bit t; [768, 800): half norm of token t at 768 + 2t.
+ *   Code value = rank of the codebook level in ascending order.
+ *   1088*8/(16*128) = 4.25 and 800*8/(16*128) = 3.125 bits per coordinate.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARGUMENT = -1,   /* null pointer, negative size, bad stride ... */
+  TQ_ERR_UNSUPPORTED = -2,        /* valid but not implemented (e.g. head_dim != 128) */
+  TQ_ERR_WORKSPACE_TOO_SMALL = -3,
+  TQ_ERR_NOT_INITIALIZED = -4,    /* codebook not set up by tq_codebook_init */
+  TQ_ERR_HIP = -5                 /* a HIP runtime call failed; see tq_last_error() */
+} tq_status;
+
+typedef enum tq_dtype { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
+
+#define TQ_HEAD_DIM 128
+#define TQ_QJL_DIM 128
+#define TQ_BITS 3
+#define TQ_BLOCK 16
+#define TQ_K_PAGE_BYTES 1088
+#define TQ_V_PAGE_BYTES 800
+
+/* Codebook and projection context.  Caller-owned storage, filled by
+ * tq_codebook_init and read-only afterwards; several threads and streams may
+ * share one.  d_tables points at the caller's device buffer of
+ * tq_codebook_device_bytes() bytes, which must outlive every call using it. */
+typedef struct tq_codebook {
+  int32_t head_dim;        /* 128 */
+  int32_t bits;            /* 3 */
+  int32_t qjl_dim;         /* 128 */
+  int32_t block_size;      /* 16 */
+  uint64_t qjl_seed;       /* seed of the generated S (0 if caller-supplied) */
+  float centroids[8];      /* ascending fp32 levels for N(0, 1/d) */
+  float thresholds[7];     /* fp32 midpoints of adjacent levels */
+  float qjl_scale;         /* sqrt(pi/2) / qjl_dim */
+  void *d_tables;          /* device: S [m][d] fp32 row-major, then S^T [d][m] fp32 */
+  uint32_t magic;          /* set by tq_codebook_init */
+  uint32_t reserved;
+} tq_codebook;
+
+/* ---- host-only helpers (no device needed) ------------------------------ */
+
+/* Lloyd-Max codebook for N(0, 1/head_dim) with 2^bits levels (lilting.ch
+ * article, "Lloyd-Maxコードブックとは"): the fixed point of "thresholds are
+ * midpoints, levels are conditional means", iterated in double precision on
+ * N(0,1), scaled by 1/sqrt(head_dim) and rounded once to fp32.  Writes
+ * 2^bits levels and 2^bits - 1 thresholds, ascending.  bits in [1, 4]. */
+tq_status tq_codebook_compute(int head_dim, int bits, float *centroids, float *thresholds);
+
+/* QJL matrix S (rows x cols, fp32, row-major) from a seed: SplitMix64
+ * (Steele, Lea, Flood 2014) uniforms u = ((x >> 11) + 0.5) * 2^-53, pairs
+ * turned into normals by Box-Muller in double (r cos, r sin), row-major fill,
+ * one rounding to fp32.  The SwiftLM README ("TurboQuantization", K-cache
+ * step 5) names a random Johnson-Lindenstrauss projection; this generator is
+ * this library's fixed choice so results are reproducible from the seed. */
+tq_status tq_qjl_matrix(uint64_t seed, int rows, int cols, float *out);
+
+/* ---- context ------------------------------------------------------------ */
+
+/* Bytes of the device table buffer for a codebook of this size. */
+size_t tq_codebook_device_bytes(int head_dim, int qjl_dim);
+
+/* Fill *cb (host struct) and upload [S | S^T] to d_tables with a copy on
+ * `stream`, then wait for `stream` (a one-time set-up call; it is the only
+ * call that copies host data to the device or synchronises).
+ * qjl_host: NULL -> S generated from qjl_seed by tq_qjl_matrix; else the
+ * caller's S (qjl_dim x head_dim fp32 row-major host array).
+ * Errors: TQ_ERR_UNSUPPORTED for head_dim/bits/qjl_dim other than 128/3/128,
+ * TQ_ERR_INVALID_ARGUMENT for null cb/d_tables, TQ_ERR_HIP on copy failure. */
+tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl_seed,
+                           const float *qjl_host, void *d_tables, void *stream);
+
+size_t tq_k_page_bytes(const tq_codebook *cb);   /* 1088 */
+size_t tq_v_page_bytes(const tq_codebook *cb);   /* 800 */
+
+/* ---- encode --------------------------------------------------------------
+ * Compress num_tokens x num_kv_heads key and value vectors and store each
+ * (token, head) record in its slot (SwiftLM README, "TurboQuantization",
+ * K-cache steps 1-5 and the V-cache paragraph; paging per the vLLM-MLX
+ * explainer, "Paged KVキャッシュ").
+ *   k, v        device, element (t, h, i) at k[t*tok_stride + h*head_stride + i]
+ *               (strides in elements; i contiguous), dtype in_dtype.
+ *   slot_mapping device int64[num_tokens]; a negative slot skips the token.
+ *   k_cache, v_cache device pools as laid out above.
+ *   norms_out   nullable device fp32[num_tokens][num_kv_heads][3]: the fp32
+ *               |k|, gamma and |v| the encoder computed (before rounding to
+ *               half), for checking; skipped tokens are left untouched.
+ * num_tokens == 0 is a no-op.  Decision thresholds are compared in fp32. */
+tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_dtype in_dtype,
+                       int64_t num_tokens, int num_kv_heads, int64_t tok_stride,
+                       int64_t head_stride, const int64_t *slot_mapping, uint8_t *k_cache,
+                       uint8_t *v_cache, float *norms_out, void *stream);
+
+/* ---- attention ------------------------------------------------------------
+ * out[b][t][h] = sum_j softmax_j(scale * <q[b][t][h], k~_j>) v~_j over the
+ * compressed keys/values of sequence b and KV head h / (Hq/Hkv), where
+ * k~ = |k| (H^T c[idx] + sqrt(pi/2)/m * gamma * S^T sigma) and
+ * v~ = |v| H^T c[idx_v] -- the QJL-corrected inner-product estimate of the
+ * SwiftLM README's K-cache step 5, attention over the whole compressed
+ * history (its note on --turbo-kv recall) read through a block table.
+ * q_len > 1 (chunked prefill, the README's --prefill-size) is causal: query t
+ * sees keys 0 .. context_len - q_len + t.
+ *   q           device [num_seqs][q_len][num_q_heads][128], dtype q_dtype.
+ *   block_tables device int32[num_seqs][max_blocks_per_seq].
+ *   context_lens device int32[num_seqs], each in [0, max_context_len]; the
+ *               length includes the q_len new tokens.  0 gives zero output.
+ *   softmax_scale 0 -> 1/sqrt(128).
+ *   out         device [num_seqs][q_len][num_q_heads][128], dtype out_dtype.
+ *   tokens_per_split  0 -> chosen by the library; else a multiple of 64
+ *               giving the split-K chunk (results agree to rounding).
+ *   workspace   device scratch of tq_decode_workspace_bytes() bytes (same
+ *               arguments); contents on entry do not matter.
+ * Errors: TQ_ERR_INVALID_ARGUMENT (nulls, Hq % Hkv != 0, q_len < 1,
+ * q_len > max_context_len, bad tokens_per_split), TQ_ERR_UNSUPPORTED
+ * (num_q_heads / num_kv_heads > 16), TQ_ERR_WORKSPACE_TOO_SMALL. */
+size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
+                                 int num_q_heads, int num_kv_heads, int max_context_len,
+                                 int tokens_per_split);
+
+tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                              const uint8_t *k_cache, const uint8_t *v_cache,
+                              const int32_t *block_tables, int max_blocks_per_seq,
+                              const int32_t *context_lens, int num_seqs, int q_len,
+                              int num_q_heads, int num_kv_heads, int max_context_len,
+                              float softmax_scale, void *out, tq_dtype out_dtype,
+                              int tokens_per_split, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Thread-local text describing the last non-OK status on this thread. */
+const char *tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

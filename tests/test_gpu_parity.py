@@ -1,0 +1,223 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases are checked element by element; the full-size workloads, in the
+launch configuration the benchmark uses, are checked on sampled heads,
+positions and query rows.  Tolerances: see gpu_helpers."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import (check_decode, check_encoded_sequence, codebook, decode_gpu, dev,
+                         encode_gpu, new_pools, oracle_tables, rel_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def test_single_head_fp32_1024_tokens():
+    case = synth.single_head_case(seed=1, T=1024)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 1)
+    norms = encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, dtype=torch.float32)
+    kp, vp = _np(kpool), _np(vpool)
+    stats = {}
+    check_encoded_sequence(case["k"], case["v"], kp, vp, case["table"][0], np.arange(1024), norms,
+                           stats=stats)
+    print("ambiguous codes:", stats)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 1,
+                     q_dtype=torch.float32)
+    err = check_decode(out, case["q"], kp, vp, case["table"], case["context_lens"])
+    print("max rel err", err.max())
+
+
+@pytest.mark.parametrize("T", [1000, 8192])
+def test_gqa_32q_8kv(T):
+    case = synth.gqa_case(seed=2, T=T, Hq=32, Hkv=8)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 8)
+    norms = encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool)
+    kp, vp = _np(kpool), _np(vpool)
+    check_encoded_sequence(case["k"], case["v"], kp, vp, case["table"][0], np.arange(T), norms)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 8)
+    err = check_decode(out, case["q"], kp, vp, case["table"], case["context_lens"])
+    print("max rel err", err.max())
+
+
+def test_ragged_batch_with_appends():
+    # 16 sequences, log-uniform lengths in [512, 32768], random block table,
+    # then two decode steps that each append and encode one token per sequence.
+    case = synth.ragged_case(seed=3, B=16, Hq=32, Hkv=8, steps=2)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 8)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    L = case["lengths"].copy()
+    starts = np.concatenate([[0], np.cumsum(L)])
+    for step in range(2):
+        norms = encode_gpu(cb, case["new_k"][step], case["new_v"][step], case["new_slots"][step],
+                           kpool, vpool)
+        L = L + 1
+        kp, vp = _np(kpool), _np(vpool)
+        for b in (0, 7):       # sampled sequences: whole history + the appended tokens
+            hist_k = np.concatenate([case["k"][starts[b]:starts[b + 1]]] +
+                                    [case["new_k"][s][b:b + 1] for s in range(step + 1)])
+            hist_v = np.concatenate([case["v"][starts[b]:starts[b + 1]]] +
+                                    [case["new_v"][s][b:b + 1] for s in range(step + 1)])
+            check_encoded_sequence(hist_k, hist_v, kp, vp, case["table"][b], np.arange(L[b]), None)
+        out = decode_gpu(cb, case["q"][step], kpool, vpool, case["table"], L.astype(np.int32), 8)
+        err = check_decode(out, case["q"][step], kp, vp, case["table"], L, kv_heads=[0, 5])
+        print("step", step, "max rel err", err.max())
+
+
+def test_long_context_131072_split_k():
+    case = synth.gqa_case(seed=4, T=131072, Hq=32, Hkv=4)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 4, fill="zeros")
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    kp, vp = _np(kpool), _np(vpool)
+    pos = np.r_[0:2048, 131072 - 2048:131072]
+    check_encoded_sequence(case["k"][pos], case["v"][pos], kp, vp, case["table"][0], pos, None)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 4)
+    err = check_decode(out, case["q"], kp, vp, case["table"], case["context_lens"], kv_heads=[0, 3])
+    print("max rel err", err.max())
+
+
+@pytest.mark.parametrize("cached,new", [(300, 37), (32768, 2048)])
+def test_chunked_prefill_causal(cached, new):
+    T = cached + new
+    case = synth.gqa_case(seed=5, T=T, Hq=32, Hkv=8, q_len=new)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 8)
+    encode_gpu(cb, case["k"][:cached], case["v"][:cached], case["slots"][:cached], kpool, vpool,
+               with_norms=False)
+    norms = encode_gpu(cb, case["k"][cached:], case["v"][cached:], case["slots"][cached:],
+                       kpool, vpool)
+    kp, vp = _np(kpool), _np(vpool)
+    sample = np.arange(T) if T < 1000 else np.r_[0:256, cached - 16:T]
+    check_encoded_sequence(case["k"][sample], case["v"][sample], kp, vp, case["table"][0], sample, None)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 8)
+    sub = {} if T < 1000 else dict(kv_heads=[0, 7], q_positions=[0, 1, new // 2, new - 1])
+    err = check_decode(out, case["q"], kp, vp, case["table"], case["context_lens"], **sub)
+    print("max rel err", err.max())
+
+
+def test_edge_cases_encode():
+    cb = codebook()
+    rng = np.random.default_rng(6)
+    T, H = 40, 2
+    k = synth.kv_tensor(rng, T, H)
+    v = synth.kv_tensor(rng, T, H)
+    k[3] = 0.0                    # zero key vector
+    v[4] = 0.0                    # zero value vector
+    table = np.array([[2, 0, 1]], dtype=np.int32)
+    slots = synth.slots_for(table, 0, np.arange(T))
+    slots[[7, 30]] = -1           # skipped tokens keep their old bytes
+    kpool, vpool = new_pools(3, H, seed=1)
+    before_k, before_v = _np(kpool), _np(vpool)
+    norms = encode_gpu(cb, k, v, slots, kpool, vpool)
+    kp, vp = _np(kpool), _np(vpool)
+    keep = np.array([j for j in range(T) if slots[j] >= 0])
+    check_encoded_sequence(k[keep], v[keep], kp, vp, table[0], keep, norms[keep])
+    from oracle.pages import read_k_tokens_fast, read_v_tokens_fast
+    for h in range(H):
+        for j in (7, 30):
+            a = read_k_tokens_fast(kp, table[0], T, h)
+            b = read_k_tokens_fast(before_k, table[0], T, h)
+            for x, y in zip(a, b):
+                np.testing.assert_array_equal(x[j], y[j])
+            a = read_v_tokens_fast(vp, table[0], T, h)
+            b = read_v_tokens_fast(before_v, table[0], T, h)
+            for x, y in zip(a, b):
+                np.testing.assert_array_equal(x[j], y[j])
+        codes = read_k_tokens_fast(kp, table[0], T, h)[0]
+        np.testing.assert_array_equal(codes[3], np.full(128, 3))
+    assert np.all(norms[3, :, 0] == 0) and np.all(norms[4, :, 2] == 0)
+    # zero tokens: a no-op
+    e = torch.empty((0, H, 128), dtype=torch.bfloat16, device="cuda")
+    import decode_attention_tq_amd as tq
+    tq.tq_encode_kv(cb, e, e, torch.empty(0, dtype=torch.int64, device="cuda"), kpool, vpool)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(kpool), kp)
+
+
+def test_partial_pages_across_calls_and_fp16_input():
+    # tokens of one page arrive in several calls (the atomic merge path)
+    cb = codebook()
+    rng = np.random.default_rng(7)
+    T, H = 70, 3
+    k = synth.kv_tensor(rng, T, H, bf16=False).astype(np.float16).astype(np.float32)
+    v = synth.kv_tensor(rng, T, H, bf16=False).astype(np.float16).astype(np.float32)
+    table = np.array([[4, 1, 3, 0, 2]], dtype=np.int32)
+    slots = synth.slots_for(table, 0, np.arange(T))
+    kpool, vpool = new_pools(5, H, seed=2)
+    order = rng.permutation(T)
+    for chunk in np.array_split(order, 7):
+        sl = np.full(T, -1, dtype=np.int64)
+        sl[chunk] = slots[chunk]
+        encode_gpu(cb, k, v, sl, kpool, vpool, dtype=torch.float16, with_norms=False)
+    check_encoded_sequence(k, v, _np(kpool), _np(vpool), table[0], np.arange(T), None)
+
+
+def test_decode_edge_cases_and_dtypes():
+    cb = codebook()
+    case = synth.ragged_case(seed=8, B=5, Hq=16, Hkv=1, lengths=[0, 1, 15, 16, 700])
+    kpool, vpool = new_pools(case["num_blocks"], 1)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    kp, vp = _np(kpool), _np(vpool)
+    L = case["lengths"].astype(np.int32)
+    q = case["q"][0]
+    for qd, od in ((torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16),
+                   (torch.float16, torch.float16)):
+        out = decode_gpu(cb, q, kpool, vpool, case["table"], L, 1, q_dtype=qd, out_dtype=od)
+        tol = 2e-3 if od == torch.float32 else 1e-2
+        qq = dev(q, qd).float().cpu().numpy()
+        check_decode(out, qq, kp, vp, case["table"], L, rtol=tol)
+    assert np.all(out[0] == 0)                       # empty context -> zeros
+    # a custom softmax scale
+    out = decode_gpu(cb, q, kpool, vpool, case["table"], L, 1, scale=0.3)
+    check_decode(out, q, kp, vp, case["table"], L, scale=0.3)
+
+
+def test_split_invariance_permutation_invariance_determinism():
+    cb = codebook()
+    case = synth.gqa_case(seed=9, T=3000, Hq=16, Hkv=2)
+    kpool, vpool = new_pools(case["num_blocks"], 2)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    outs = [decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 2,
+                       tokens_per_split=tps) for tps in (0, 256, 512, 3072)]
+    for o in outs[1:]:
+        assert rel_rows(o, outs[0].astype(np.float64)).max() < 1e-5
+    again = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 2)
+    np.testing.assert_array_equal(again, outs[0])
+    # relabel physical blocks: identical results
+    nb = case["num_blocks"]
+    perm = np.random.default_rng(0).permutation(nb)
+    k2 = torch.empty_like(kpool)
+    v2 = torch.empty_like(vpool)
+    k2[torch.from_numpy(perm).cuda()] = kpool
+    v2[torch.from_numpy(perm).cuda()] = vpool
+    out2 = decode_gpu(cb, case["q"], k2, v2, perm[case["table"]], case["context_lens"], 2)
+    np.testing.assert_array_equal(out2, outs[0])
+    # encode is deterministic too
+    kp3, vp3 = new_pools(nb, 2)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kp3, vp3, with_norms=False)
+    np.testing.assert_array_equal(_np(kp3), _np(kpool))
+    np.testing.assert_array_equal(_np(vp3), _np(vpool))
+
+
+def test_caller_supplied_qjl_matrix():
+    import decode_attention_tq_amd as tq
+    S = np.random.default_rng(10).standard_normal((128, 128)).astype(np.float32)
+    cb = tq.tq_codebook_init(128, 3, 0, qjl_host=S, device="cuda")
+    c32, t32, _ = oracle_tables()
+    case = synth.gqa_case(seed=10, T=500, Hq=8, Hkv=2)
+    kpool, vpool = new_pools(case["num_blocks"], 2)
+    norms = encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool)
+    kp, vp = _np(kpool), _np(vpool)
+    check_encoded_sequence(case["k"], case["v"], kp, vp, case["table"][0], np.arange(500), norms,
+                           tables=(c32, t32, S))
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 2)
+    check_decode(out, case["q"], kp, vp, case["table"], case["context_lens"], tables=(c32, t32, S))

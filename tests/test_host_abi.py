@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI: the library loads, exports everything tq.h
+declares, reproduces the oracle's codebook and QJL matrix, and rejects bad
+arguments before touching the device.  No GPU needed: every call here either
+is host-only or fails validation before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_tq_amd as tq
+from oracle import codebook_fp32, gaussian_matrix
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: every call using it is rejected on the host
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert "tq_encode_kv" in names and "tq_decode_attention" in names
+    for n in names:
+        assert hasattr(tq._lib, n), n
+    assert sorted(tq.EXPORTED) == names
+
+
+def test_codebook_matches_oracle_within_one_ulp():
+    for bits in (1, 2, 3, 4):
+        c, t = tq.tq_codebook_compute(128, bits)
+        oc, ot = codebook_fp32(128, bits)
+        ulps_c = np.abs(c.view(np.int32).astype(np.int64) - oc.view(np.int32).astype(np.int64))
+        ulps_t = np.abs(t.view(np.int32).astype(np.int64) - ot.view(np.int32).astype(np.int64))
+        assert ulps_c.max() <= 1 and ulps_t.max() <= 1, bits
+    c, t = tq.tq_codebook_compute(128, 3)
+    oc, ot = codebook_fp32(128, 3)
+    np.testing.assert_array_equal(c, oc)   # identical in practice
+    np.testing.assert_array_equal(t, ot)
+
+
+@pytest.mark.parametrize("seed", [0, 42, 2 ** 63 + 5])
+def test_qjl_matrix_bit_identical_to_oracle(seed):
+    np.testing.assert_array_equal(tq.tq_qjl_matrix(seed, 128, 128), gaussian_matrix(seed, 128, 128))
+    np.testing.assert_array_equal(tq.tq_qjl_matrix(seed, 3, 5), gaussian_matrix(seed, 3, 5))
+
+
+def test_host_helper_errors():
+    assert tq._lib.tq_codebook_compute(128, 0, FAKE, FAKE) == tq.TQ_ERR_UNSUPPORTED
+    assert tq._lib.tq_codebook_compute(128, 3, None, FAKE) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert tq._lib.tq_qjl_matrix(1, 0, 4, FAKE) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert "positive" in tq.tq_last_error()
+    assert tq.tq_codebook_device_bytes(128, 128) == 2 * 128 * 128 * 4
+
+
+def test_codebook_init_rejects_before_any_device_call():
+    s = tq.tq_codebook_t()
+    assert tq._lib.tq_codebook_init(ctypes.byref(s), 64, 3, 1, None, FAKE, None) == tq.TQ_ERR_UNSUPPORTED
+    assert tq._lib.tq_codebook_init(ctypes.byref(s), 128, 4, 1, None, FAKE, None) == tq.TQ_ERR_UNSUPPORTED
+    assert tq._lib.tq_codebook_init(ctypes.byref(s), 128, 3, 1, None, None, None) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert tq._lib.tq_codebook_init(None, 128, 3, 1, None, FAKE, None) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert s.magic == 0
+
+
+def _fake_cb(initialised=True):
+    s = tq.tq_codebook_t()
+    s.head_dim, s.bits, s.qjl_dim, s.block_size = 128, 3, 128, 16
+    s.d_tables = FAKE
+    s.magic = 0x54513031 if initialised else 0
+    return s
+
+
+def _enc(cb, **kw):
+    a = dict(k=FAKE, v=FAKE, dtype=tq.TQ_BF16, T=4, H=2, ts=256, hs=128, slots=FAKE,
+             kc=FAKE, vc=FAKE, norms=None)
+    a.update(kw)
+    return tq._lib.tq_encode_kv(ctypes.byref(cb), a["k"], a["v"], a["dtype"], a["T"], a["H"],
+                                a["ts"], a["hs"], a["slots"], a["kc"], a["vc"], a["norms"], None)
+
+
+def test_encode_validation():
+    cb = _fake_cb()
+    assert _enc(_fake_cb(False)) == tq.TQ_ERR_NOT_INITIALIZED
+    assert tq._lib.tq_encode_kv(None, FAKE, FAKE, 0, 1, 1, 128, 128, FAKE, FAKE, FAKE, None, None) \
+        == tq.TQ_ERR_INVALID_ARGUMENT
+    assert _enc(cb, T=-1) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert _enc(cb, H=0) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert _enc(cb, dtype=7) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert _enc(cb, k=None) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert _enc(cb, slots=None) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert _enc(cb, ts=-256) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert _enc(cb, ts=64, hs=64) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert "overlap" in tq.tq_last_error()
+    # zero tokens is a no-op that succeeds without touching anything
+    assert _enc(cb, T=0, k=None, v=None, slots=None, kc=None, vc=None) == tq.TQ_OK
+
+
+def _dec(cb, **kw):
+    a = dict(q=FAKE, qd=tq.TQ_BF16, kc=FAKE, vc=FAKE, bt=FAKE, mb=64, cl=FAKE, B=1, q_len=1,
+             Hq=32, Hkv=8, maxc=1024, scale=0.0, out=FAKE, od=tq.TQ_F32, tps=0, ws=FAKE,
+             wsb=1 << 40)
+    a.update(kw)
+    return tq._lib.tq_decode_attention(
+        ctypes.byref(cb), a["q"], a["qd"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["B"],
+        a["q_len"], a["Hq"], a["Hkv"], a["maxc"], a["scale"], a["out"], a["od"], a["tps"],
+        a["ws"], a["wsb"], None)
+
+
+def test_decode_validation():
+    cb = _fake_cb()
+    E = tq.TQ_ERR_INVALID_ARGUMENT
+    assert _dec(_fake_cb(False)) == tq.TQ_ERR_NOT_INITIALIZED
+    assert _dec(cb, q=None) == E
+    assert _dec(cb, ws=None) == E
+    assert _dec(cb, qd=9) == E
+    assert _dec(cb, od=-1) == E
+    assert _dec(cb, B=0) == E
+    assert _dec(cb, q_len=0) == E
+    assert _dec(cb, Hq=30, Hkv=8) == E
+    assert "multiple" in tq.tq_last_error()
+    assert _dec(cb, Hq=64, Hkv=2) == tq.TQ_ERR_UNSUPPORTED      # 32 heads per KV head
+    assert _dec(cb, Hq=24, Hkv=8) == tq.TQ_ERR_UNSUPPORTED      # group of 3
+    assert _dec(cb, maxc=-1) == E
+    assert _dec(cb, q_len=8, maxc=4, mb=1) == E                  # more queries than context
+    assert _dec(cb, mb=63) == E                                  # 63 blocks < 1024 tokens
+    assert _dec(cb, tps=100) == E
+    assert _dec(cb, tps=-256) == E
+    assert _dec(cb, scale=float("nan")) == E
+    assert _dec(cb, scale=-1.0) == E
+    need = tq._lib.tq_decode_workspace_bytes(ctypes.byref(cb), 1, 1, 32, 8, 1024, 0)
+    assert need > 0
+    assert _dec(cb, wsb=need - 1) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_plan_is_consistent():
+    cb = _fake_cb()
+    ref = ctypes.byref(cb)
+    rows = 32
+    # rows * (256 prep floats + splits * 132 partial floats) * 4 bytes
+    for maxc, tps in ((8192, 256), (8192, 1024), (131072, 0), (0, 0), (1, 0)):
+        ws = tq._lib.tq_decode_workspace_bytes(ref, 1, 1, 32, 8, maxc, tps)
+        per_row = ws // 4 // rows - 256
+        assert per_row % 132 == 0 and per_row >= 132
+        if tps:
+            assert per_row // 132 == max(1, -(-maxc // tps))
+    assert tq._lib.tq_decode_workspace_bytes(ref, 0, 1, 32, 8, 10, 0) == 0
+    assert tq._lib.tq_k_page_bytes(ref) == 1088 and tq._lib.tq_v_page_bytes(ref) == 800
