@@ -1,0 +1,227 @@
+"""Benchmark of the TurboQuant compressed-KV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (default): one GQA decode layer, 32 query heads over 8 KV heads,
+head_dim 128, batch 1, 8192 cached tokens of bf16 outlier-channel Gaussian
+KV.  One step is the whole hot path: encode the full cache (65,536 key and
+65,536 value vectors: norm, rotation, 3-bit codes, residual, QJL signs, paged
+store) and one decode query per head over the compressed cache (query prep,
+split-K attention, merge with one inverse rotation).
+
+Inputs are resident in HBM before timing.  The 256 MB Infinity Cache is
+defeated by rotating over enough independent replicas of inputs and pools
+that consecutive steps never share data (> 512 MB in total).
+
+Prints one JSON line: the whole step's effective HBM rate (algorithmic bytes /
+time) as ``value``, the encode rate in vectors/s and the attention rate in
+GB/s alongside, the roofline of the dominant kernel from HIP events recorded
+around it on its stream, and the CPU oracle timed on the host for the same
+step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 64 lanes x 2 FLOP x 2.4 GHz, packed FP32 disabled
+MALL_BYTES = 256 << 20
+
+T, HQ, HKV, D = 8192, 32, 8, 128
+WORKLOAD = ("GQA decode layer: 32 q-heads / 8 KV heads, d=128, batch 1, context 8192, "
+            "bf16 outlier-channel KV; step = encode full cache (65536 K + 65536 V vectors) "
+            "+ 1 decode query per head")
+
+
+def algorithmic_bytes():
+    """Bytes a step must move at minimum (inputs read once, outputs written once)."""
+    per_tok = HKV * (2 * D * 2 + 68 + 50) + 8          # bf16 K and V in, records out, slot
+    encode = T * per_tok
+    blocks = T // 16
+    decode = T * HKV * 118 + blocks * 4 + HQ * D * 2 + HQ * D * 4 + 4
+    return encode, decode
+
+
+def encode_flops_per_key():
+    # QJL projection 2*m*d plus two rotations, norm, residual (small terms)
+    return 2 * 128 * 128 + 2 * 7 * 128 + 6 * 128
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("tq_encode.hip", "tq_decode.hip", "tq_common.hpp"):
+        with open(os.path.join(ROOT, "decode_attention_tq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = rec.get(kernel)
+    if not k or k.get("source_hash") != kernel_source_hash():
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, target_s=10.0, max_s=30.0):
+    """The oracle (float64 NumPy) on the same step, repeated for ~10 s."""
+    from threadpoolctl import threadpool_info
+    from oracle import codebook_fp32, decode_paged, encode_k, encode_v, gaussian_matrix
+    from oracle.pages import K_PAGE_BYTES, V_PAGE_BYTES, write_slots_fast
+    import synth
+    c32, t32 = codebook_fp32(128, 3)
+    S = gaussian_matrix(synth.QJL_SEED)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ek = encode_k(case["k"], c32, t32, S)
+        ev = encode_v(case["v"], c32, t32)
+        kp = np.zeros((case["num_blocks"], HKV, K_PAGE_BYTES), np.uint8)
+        vp = np.zeros((case["num_blocks"], HKV, V_PAGE_BYTES), np.uint8)
+        write_slots_fast(kp, vp, case["slots"], ek, ev)
+        decode_paged(case["q"], kp, vp, case["table"], case["context_lens"], c32, S)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el + el / reps > max_s:
+            break
+    enc_b, dec_b = algorithmic_bytes()
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round((enc_b + dec_b) * reps / el / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"the full step (same workload) run {reps}x in {el:.1f} s, float64 NumPy, "
+                      f"{threads} BLAS threads on {os.cpu_count()} host cpus",
+            "s_per_step": round(el / reps, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the method's multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_tq_amd as tq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = synth.gqa_case(seed=2, T=T, Hq=HQ, Hkv=HKV)
+    cb = tq.tq_codebook_init(128, 3, synth.QJL_SEED, device=dev)
+
+    enc_b, dec_b = algorithmic_bytes()
+    per_replica = 2 * T * HKV * D * 2 + case["num_blocks"] * HKV * (1088 + 800)
+    R = max(2, -(-2 * MALL_BYTES // per_replica) + 1)
+    k0 = torch.from_numpy(case["k"]).to(dev, torch.bfloat16)
+    v0 = torch.from_numpy(case["v"]).to(dev, torch.bfloat16)
+    reps = []
+    for r in range(R):
+        reps.append(dict(
+            k=k0.clone(), v=v0.clone(),
+            kp=torch.zeros((case["num_blocks"], HKV, 1088), dtype=torch.uint8, device=dev),
+            vp=torch.zeros((case["num_blocks"], HKV, 800), dtype=torch.uint8, device=dev)))
+    slots = torch.from_numpy(case["slots"]).to(dev)
+    q = torch.from_numpy(case["q"]).to(dev, torch.bfloat16)
+    table = torch.from_numpy(case["table"]).to(dev)
+    clens = torch.from_numpy(case["context_lens"]).to(dev)
+    out = torch.empty((1, 1, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_decode_workspace_bytes(cb, 1, 1, HQ, HKV, T), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        r = reps[i % R]
+        if ev is not None:
+            ev[0].record(stream)
+        tq.tq_encode_kv(cb, r["k"], r["v"], slots, r["kp"], r["vp"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        tq.tq_decode_attention(cb, q, r["kp"], r["vp"], table, clens, T, HKV, out=out,
+                               workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = t_start.elapsed_time(t_end)
+    total_s = max(wall, gpu_ms / 1e3)
+    ms_per_step = total_s * 1e3 / args.steps
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    value = (enc_b + dec_b) / (ms_per_step / 1e3) / 1e9
+    n_vec = 2 * T * HKV
+    # dominant kernel: the single-launch encode kernel (the attention call is
+    # three launches: query prep, split pass, merge)
+    if enc_ms >= dec_ms:
+        name, dur_ms, traffic = "encode_kernel", enc_ms, load_traffic("encode_kernel")
+        achieved = enc_b / (dur_ms / 1e3) / 1e9
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "avg_launch_us": round(dur_ms * 1e3, 2),
+                "alu_tflops": round(T * HKV * encode_flops_per_key() / (dur_ms / 1e3) / 1e12, 2),
+                "alu_peak_tflops": FP32_VALU_PEAK_TFLOPS}
+    else:
+        name, dur_ms, traffic = "attention (prep+split+merge)", dec_ms, load_traffic("attention")
+        achieved = dec_b / (dur_ms / 1e3) / 1e9
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "avg_launch_us": round(dur_ms * 1e3, 2)}
+
+    line = {
+        "metric": "compressed-KV decode attention effective HBM GB/s (% peak); encode vectors/s",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": 1, "context": T, "q_heads": HQ, "kv_heads": HKV,
+                   "head_dim": D, "kv_dtype": "bf16", "replicas": R,
+                   "algorithmic_bytes_per_step": enc_b + dec_b},
+        "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "encode_vectors_per_s": round(n_vec / (enc_ms / 1e3), 1),
+        "encode_us": round(enc_ms * 1e3, 2),
+        "attention_GBps": round(dec_b / (dec_ms / 1e3) / 1e9, 1),
+        "attention_us": round(dec_ms * 1e3, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
