@@ -10,6 +10,15 @@ namespace tq {
 
 constexpr float kInvSqrt128 = 0.08838834764831845f;
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also makes every
+// outstanding global store visible first (a full vmcnt wait); kernels whose
+// barriers guard nothing but LDS use this one and keep stores in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float load_as_float(const void *p, int dtype, int64_t i) {
   if (dtype == TQ_F32) return static_cast<const float *>(p)[i];
   if (dtype == TQ_F16) return (float)static_cast<const _Float16 *>(p)[i];
@@ -34,15 +43,54 @@ __device__ __forceinline__ void store_from_float(void *p, int dtype, int64_t i, 
   }
 }
 
+// ---- lane exchanges: value held by lane (lane ^ s), all in VALU ----------------
+// strides 1, 2: DPP quad_perm; 4: row_half_mirror then quad_perm [3,2,1,0]
+// (lane ^ 7 ^ 3); 8: row_ror:8 inside a 16-lane row; 16 and 32: the gfx950
+// permlane16/permlane32 swaps (each returns both halves; the lane keeps the
+// one that came from the other row / half).
+__device__ __forceinline__ float xchg1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xchg2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xchg4(float x) {
+  const int m = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false);
+  return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xchg8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xchg16(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((lane >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xchg32(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((lane >> 5) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xchg(float x, int s, int lane) {
+  switch (s) {
+    case 1: return xchg1(x);
+    case 2: return xchg2(x);
+    case 4: return xchg4(x);
+    case 8: return xchg8(x);
+    case 16: return xchg16(x, lane);
+    default: return xchg32(x, lane);
+  }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  for (int o = 1; o <= 32; o <<= 1) v += xchg(v, o, lane);
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = 1; o <= 32; o <<= 1) v = fmaxf(v, xchg(v, o, lane));
   return v;
 }
 
@@ -57,13 +105,73 @@ __device__ __forceinline__ void wave_fwht128(float &r0, float &r1, int lane) {
   r1 = b;
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
-    const float p0 = __shfl_xor(r0, s), p1 = __shfl_xor(r1, s);
+    const float p0 = xchg(r0, s, lane), p1 = xchg(r1, s, lane);
     const bool upper = (lane & s) != 0;
     r0 = upper ? (p0 - r0) : (r0 + p0);
     r1 = upper ? (p1 - r1) : (r1 + p1);
   }
   r0 *= kInvSqrt128;
   r1 *= kInvSqrt128;
+}
+
+// Sum over the wave, returned in every lane: inclusive scans inside each
+// 16-lane row (DPP row_shr 1, 2, 4, 8; out-of-row sources read 0), then
+// row_bcast:15 and row_bcast:31 carry the row totals up to lane 63, which is
+// read back as a uniform value.
+__device__ __forceinline__ float wave_sum_u(float v) {
+  int x = __float_as_int(v);
+  x = __float_as_int(__int_as_float(x) + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+}
+
+// Walsh-Hadamard transform (unnormalised, Sylvester order) of 128 values held
+// two per lane, lane l starting with coordinates l (in a) and l + 64 (in b).
+// The stride-64 butterfly is in-lane; permlane32_swap then regroups so that
+// lane m < 32 holds (m, m+32) and lane 32+m holds (64+m, 96+m), making the
+// stride-32 butterfly in-lane; permlane16_swap regroups again so that lane
+// 16r+i holds (32r+i, 32r+16+i) for stride 16.  Strides 8..1 stay inside
+// 16-lane rows (DPP).  On return lane 16r+i holds coordinate 32r+i in a and
+// 32r+16+i in b.
+__device__ __forceinline__ void fwht128_regroup(float &a, float &b, int lane) {
+  float s = a + b, d = a - b;
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(d), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+  s = a + b;
+  d = a - b;
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(d), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+  s = a + b;
+  d = a - b;
+  a = s;
+  b = d;
+#pragma unroll
+  for (int st = 8; st >= 1; st >>= 1) {
+    const float sg = (lane & st) ? -1.0f : 1.0f;
+    const float pa = xchg(a, st, lane), pb = xchg(b, st, lane);
+    a = fmaf(sg, a, pa);
+    b = fmaf(sg, b, pb);
+  }
+}
+
+// Coordinates held by lane l after fwht128_regroup.
+__device__ __forceinline__ int regroup_coord_a(int lane) { return 32 * (lane >> 4) + (lane & 15); }
+__device__ __forceinline__ int regroup_coord_b(int lane) { return 32 * (lane >> 4) + 16 + (lane & 15); }
+
+// 32-bit word r (coordinates 32r .. 32r+31) of a 128-bit plane record from
+// the ballots of the a and b halves in the regrouped layout.
+__device__ __forceinline__ uint32_t regroup_plane_word(uint64_t ma, uint64_t mb, int r) {
+  return (uint32_t)((ma >> (16 * r)) & 0xFFFFull) | ((uint32_t)((mb >> (16 * r)) & 0xFFFFull) << 16);
 }
 
 // Level index of y: the number of thresholds strictly below y (a value on a

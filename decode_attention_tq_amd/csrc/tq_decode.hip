@@ -33,11 +33,18 @@ __device__ __forceinline__ int clamped_context(const DecodeArgs &a, int b) {
   return min(max(a.context_lens[b], 0), cap);
 }
 
-// ---- 1. query prep: one wave per query row --------------------------------
+// ---- 1. query prep: a workgroup per 4 query rows ----------------------------
+// Thread (i, half) keeps S[i][64*half .. +64) in registers (all 64 loads in
+// flight at once), then forms the partial S q for each row; LDS adds the two
+// halves.  The rotation runs on wave w for row w.
+constexpr int kPrepRows = 4;
+
 __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a, int64_t rows) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  __shared__ float qs[4][kHeadDim];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
+  __shared__ float qs[kPrepRows][kHeadDim];
+  __shared__ float part[2][kPrepRows][kHeadDim];
+  const int64_t r = r0 + wave;
   float x0 = 0.0f, x1 = 0.0f;
   if (r < rows) {
     x0 = load_as_float(a.q, a.q_dtype, r * kHeadDim + lane);
@@ -45,20 +52,26 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a, int64_t r
   }
   qs[wave][lane] = x0;
   qs[wave][lane + 64] = x1;
-  __syncthreads();
-  if (r >= rows) return;
-  float s0 = 0.0f, s1 = 0.0f;
-  for (int k = 0; k < kHeadDim; ++k) {
-    const float qk = qs[wave][k];
-    s0 = fmaf(a.St[k * kQjlDim + lane], qk, s0);
-    s1 = fmaf(a.St[k * kQjlDim + lane + 64], qk, s1);
+  const int i = tid & 127, half = tid >> 7;
+  float sk[64];
+#pragma unroll
+  for (int k = 0; k < 64; ++k) sk[k] = a.St[(half * 64 + k) * kQjlDim + i];
+  lds_barrier();
+#pragma unroll
+  for (int rr = 0; rr < kPrepRows; ++rr) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) acc = fmaf(sk[k], qs[rr][half * 64 + k], acc);
+    part[half][rr][i] = acc;
   }
+  lds_barrier();
+  if (r >= rows) return;
   wave_fwht128(x0, x1, lane);
   float *out = a.qprep + r * 256;
   out[lane] = x0;
   out[lane + 64] = x1;
-  out[128 + lane] = a.cb.qjl_scale * s0;
-  out[128 + lane + 64] = a.cb.qjl_scale * s1;
+  out[128 + lane] = a.cb.qjl_scale * (part[0][wave][lane] + part[1][wave][lane]);
+  out[128 + lane + 64] = a.cb.qjl_scale * (part[0][wave][lane + 64] + part[1][wave][lane + 64]);
 }
 
 // ---- 2. split pass (vector ALU) --------------------------------------------
@@ -90,12 +103,17 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
     if (c < 128) qp[g * 128 + c] = v; else sq[g * 128 + c - 128] = v;
   }
   if (tid < 8) {
-    float c = a.cb.c[0];
+    // read the levels into registers first: a select over kernel-argument
+    // fields can be folded into a lane-indexed memory load
+    float cv[8];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) c = (tid == j) ? a.cb.c[j] : c;
+    for (int j = 0; j < 8; ++j) cv[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[j])));
+    float c = cv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) c = (tid == j) ? cv[j] : c;
     lut[tid] = c;
   }
-  __syncthreads();
+  lds_barrier();
 
   const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
   float m[G], l[G], acc0[G], acc1[G];
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
       m[g] = mn;
       pn[(wave * G + g) * 64 + lane] = p * nv;
     }
-    __syncthreads();
+    lds_barrier();
     // values: lane owns coordinates lane and lane + 64
     if (c < nchunks) {
 #pragma unroll 1
@@ -199,7 +217,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // combine the four waves, write this chunk's partial
@@ -216,7 +234,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
     red[(wave * G + g) * 128 + lane] = acc0[g];
     red[(wave * G + g) * 128 + lane + 64] = acc1[g];
   }
-  __syncthreads();
+  lds_barrier();
   for (int idx = tid; idx < G * 128; idx += 256) {
     const int g = idx >> 7, d = idx & 127;
     float M = red_m[0][g];
@@ -239,9 +257,12 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 }
 
 // ---- 3. merge: one wave per output row --------------------------------------
+// Lanes read the chunk maxima and sums in parallel; the weighted sum of the
+// chunk accumulators issues its loads eight chunks at a time.
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  __shared__ float fw[4][64];
   if (r >= rows) return;
   const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
   const int b = (int)(r / per_seq);
@@ -251,19 +272,52 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
   const int ns = (vis + a.split_tokens - 1) / a.split_tokens;
   const float *part = a.partials + r * a.num_splits * kPartStride;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part[s * kPartStride]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part[s * kPartStride]);
+  M = wave_max(M);
   float Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float *p = part + s * kPartStride;
-    const float f = (p[0] == -INFINITY) ? 0.0f : __expf(p[0] - M);
-    Ls = fmaf(f, p[1], Ls);
-    A0 = fmaf(f, p[4 + lane], A0);
-    A1 = fmaf(f, p[4 + 64 + lane], A1);
+  for (int base = 0; base < ns; base += 64) {
+    const int s = base + lane;
+    float f = 0.0f;
+    if (s < ns) {
+      const float m = part[s * kPartStride];
+      f = (m == -INFINITY) ? 0.0f : __expf(m - M);
+      Ls = fmaf(f, part[s * kPartStride + 1], Ls);
+    }
+    fw[wave][lane] = f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int cnt = min(64, ns - base);
+    int u = 0;
+    for (; u + 8 <= cnt; u += 8) {
+      float v0[8], v1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float *p = part + (int64_t)(base + u + e) * kPartStride + 4;
+        v0[e] = p[lane];
+        v1[e] = p[64 + lane];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f2 = fw[wave][u + e];
+        A0 = fmaf(f2, v0[e], A0);
+        A1 = fmaf(f2, v1[e], A1);
+      }
+    }
+    for (; u < cnt; ++u) {
+      const float *p = part + (int64_t)(base + u) * kPartStride + 4;
+      const float f2 = fw[wave][u];
+      A0 = fmaf(f2, p[lane], A0);
+      A1 = fmaf(f2, p[64 + lane], A1);
+    }
+    __builtin_amdgcn_wave_barrier();
   }
+  Ls = wave_sum(Ls);
   float o0 = 0.0f, o1 = 0.0f;
   if (Ls > 0.0f) {
-    o0 = A0 / Ls;
-    o1 = A1 / Ls;
+    const float inv = 1.0f / Ls;
+    o0 = A0 * inv;
+    o1 = A1 * inv;
   }
   wave_fwht128(o0, o1, lane);
   store_from_float(a.out, a.out_dtype, r * kHeadDim + lane, o0);
@@ -282,7 +336,8 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.q_len * a.num_q_heads;
   const unsigned row_blocks = (unsigned)((rows + 3) / 4);
-  hipLaunchKernelGGL(query_prep_kernel, dim3(row_blocks), dim3(256), 0, stream, a, rows);
+  hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)),
+                     dim3(256), 0, stream, a, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (a.group) {

@@ -175,7 +175,8 @@ tq_status tq_qjl_matrix(uint64_t seed, int rows, int cols, float *out) {
 
 size_t tq_codebook_device_bytes(int head_dim, int qjl_dim) {
   if (head_dim < 1 || qjl_dim < 1) return 0;
-  return 2 * (size_t)head_dim * (size_t)qjl_dim * sizeof(float);
+  const size_t n = (size_t)head_dim * (size_t)qjl_dim;
+  return 2 * n * sizeof(float) + 2 * n * sizeof(uint16_t);
 }
 
 tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl_seed,
@@ -204,9 +205,31 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
   }
   for (int i = 0; i < m; ++i)
     for (int k = 0; k < d; ++k) host[(size_t)m * d + (size_t)k * m + i] = host[(size_t)i * d + k];
+  // S H (the projection applied to a residual that is still in the rotated
+  // domain: S r = S H^T e = (S H) e, H symmetric), in double, then split into
+  // a half "hi" part and a half "lo" part of the remainder for the matrix
+  // cores: hi + lo carries ~22 significant bits.
+  std::vector<uint16_t> halves(2 * (size_t)m * d);
+  const double inv_sqrt_d = 1.0 / std::sqrt((double)d);
+  for (int i = 0; i < m; ++i) {
+    for (int k = 0; k < d; ++k) {
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j) {
+        const double hjk = (__builtin_popcount((unsigned)(j & k)) & 1) ? -inv_sqrt_d : inv_sqrt_d;
+        acc += (double)host[(size_t)i * d + j] * hjk;
+      }
+      const _Float16 hi = (_Float16)acc;
+      const _Float16 lo = (_Float16)(acc - (double)hi);
+      std::memcpy(&halves[(size_t)i * d + k], &hi, 2);
+      std::memcpy(&halves[(size_t)m * d + (size_t)i * d + k], &lo, 2);
+    }
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(d_tables, host.data(), host.size() * sizeof(float),
                                 hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables)");
+  e = hipMemcpyAsync((char *)d_tables + host.size() * sizeof(float), halves.data(),
+                     halves.size() * sizeof(uint16_t), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables)");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -237,6 +260,15 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
   if (num_tokens > 1 && tok_stride < tq::kHeadDim && head_stride < tq::kHeadDim)
     return fail(TQ_ERR_INVALID_ARGUMENT, "strides overlap the 128 contiguous coordinates");
   if ((num_tokens + 15) / 16 > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_tokens too large");
+  {
+    // inputs are read 16 bytes per lane: 8 coordinates (4 for fp32) at a time
+    const int64_t vec = in_dtype == TQ_F32 ? 4 : 8;
+    if (tok_stride % vec != 0 || head_stride % vec != 0 ||
+        (reinterpret_cast<uintptr_t>(k) & 15) != 0 || (reinterpret_cast<uintptr_t>(v) & 15) != 0)
+      return fail(TQ_ERR_UNSUPPORTED,
+                  "k and v must be 16-byte aligned with strides that are multiples of %d elements",
+                  (int)vec);
+  }
   tq::EncodeArgs a;
   a.k = k;
   a.v = v;
@@ -251,6 +283,8 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
   a.norms_out = norms_out;
   a.S = (const float *)cb->d_tables;
   a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
+  a.SHhi = (const uint16_t *)(a.St + (size_t)tq::kQjlDim * tq::kHeadDim);
+  a.SHlo = a.SHhi + (size_t)tq::kQjlDim * tq::kHeadDim;
   a.cb = device_codebook(cb);
   hipError_t e = tq::launch_encode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "encode launch");

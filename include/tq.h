@@ -83,7 +83,8 @@ typedef struct tq_codebook {
   float centroids[8];      /* ascending fp32 levels for N(0, 1/d) */
   float thresholds[7];     /* fp32 midpoints of adjacent levels */
   float qjl_scale;         /* sqrt(pi/2) / qjl_dim */
-  void *d_tables;          /* device: S [m][d] fp32 row-major, then S^T [d][m] fp32 */
+  void *d_tables;          /* device: S [m][d] fp32, S^T [d][m] fp32, then S*H as two
+                              half arrays [m][d] (hi, and lo = S*H - hi) */
   uint32_t magic;          /* set by tq_codebook_init */
   uint32_t reserved;
 } tq_codebook;
@@ -110,7 +111,7 @@ tq_status tq_qjl_matrix(uint64_t seed, int rows, int cols, float *out);
 /* Bytes of the device table buffer for a codebook of this size. */
 size_t tq_codebook_device_bytes(int head_dim, int qjl_dim);
 
-/* Fill *cb (host struct) and upload [S | S^T] to d_tables with a copy on
+/* Fill *cb (host struct) and upload [S | S^T | S*H hi | S*H lo] to d_tables on
  * `stream`, then wait for `stream` (a one-time set-up call; it is the only
  * call that copies host data to the device or synchronises).
  * qjl_host: NULL -> S generated from qjl_seed by tq_qjl_matrix; else the
@@ -129,7 +130,9 @@ size_t tq_v_page_bytes(const tq_codebook *cb);   /* 800 */
  * K-cache steps 1-5 and the V-cache paragraph; paging per the vLLM-MLX
  * explainer, "Paged KVキャッシュ").
  *   k, v        device, element (t, h, i) at k[t*tok_stride + h*head_stride + i]
- *               (strides in elements; i contiguous), dtype in_dtype.
+ *               (strides in elements; i contiguous), dtype in_dtype; both
+ *               16-byte aligned with strides that are multiples of 8 elements
+ *               (4 for fp32), else TQ_ERR_UNSUPPORTED.
  *   slot_mapping device int64[num_tokens]; a negative slot skips the token.
  *   k_cache, v_cache device pools as laid out above.
  *   norms_out   nullable device fp32[num_tokens][num_kv_heads][3]: the fp32
@@ -156,7 +159,7 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
  *               length includes the q_len new tokens.  0 gives zero output.
  *   softmax_scale 0 -> 1/sqrt(128).
  *   out         device [num_seqs][q_len][num_q_heads][128], dtype out_dtype.
- *   tokens_per_split  0 -> chosen by the library; else a multiple of 64
+ *   tokens_per_split  0 -> chosen by the library; else a multiple of 256
  *               giving the split-K chunk (results agree to rounding).
  *   workspace   device scratch of tq_decode_workspace_bytes() bytes (same
  *               arguments); contents on entry do not matter.

@@ -54,7 +54,7 @@ def test_host_helper_errors():
     assert tq._lib.tq_codebook_compute(128, 3, None, FAKE) == tq.TQ_ERR_INVALID_ARGUMENT
     assert tq._lib.tq_qjl_matrix(1, 0, 4, FAKE) == tq.TQ_ERR_INVALID_ARGUMENT
     assert "positive" in tq.tq_last_error()
-    assert tq.tq_codebook_device_bytes(128, 128) == 2 * 128 * 128 * 4
+    assert tq.tq_codebook_device_bytes(128, 128) == 2 * 128 * 128 * 4 + 2 * 128 * 128 * 2
 
 
 def test_codebook_init_rejects_before_any_device_call():
@@ -95,6 +95,9 @@ def test_encode_validation():
     assert _enc(cb, ts=-256) == tq.TQ_ERR_INVALID_ARGUMENT
     assert _enc(cb, ts=64, hs=64) == tq.TQ_ERR_INVALID_ARGUMENT
     assert "overlap" in tq.tq_last_error()
+    assert _enc(cb, ts=1028) == tq.TQ_ERR_UNSUPPORTED               # stride not a multiple of 8
+    assert _enc(cb, k=FAKE + 2) == tq.TQ_ERR_UNSUPPORTED             # misaligned base
+    assert _enc(cb, dtype=tq.TQ_F32, ts=258, hs=128) == tq.TQ_ERR_UNSUPPORTED  # not a multiple of 4
     # zero tokens is a no-op that succeeds without touching anything
     assert _enc(cb, T=0, k=None, v=None, slots=None, kc=None, vc=None) == tq.TQ_OK
 
