@@ -45,43 +45,14 @@ constexpr float kResidualScale = 256.0f;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-// Levels held in registers.  Selecting among values read straight from the
-// kernel-argument struct lets the compiler fold the select chain into one
-// lane-indexed memory load (a round trip per vector); values that went
-// through readfirstlane cannot be folded that way.
-struct Levels {
-  float c[8];
-};
-
-__device__ __forceinline__ Levels levels_in_registers(const Codebook &cb) {
-  Levels L;
+// Level index of y: the number of thresholds strictly below it (a value on
+// a threshold goes to the lower cell), compared in fp32.  Each compare is
+// folded into the count at once, so no lane mask stays live.
+__device__ __forceinline__ int level_index(float y, const Codebook &cb) {
+  int idx = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) L.c[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cb.c[j])));
-  return L;
-}
-
-// Level-rank bits of y from the compares c_j = (t_j < y) in fp32:
-// bit2 = c3, bit1 = c5 | (c1 & !c3), bit0 = (c4^c5^c6) | ((c0^c1^c2) & !c3),
-// plus the level c[idx] itself when wanted.
-template <bool kLevel>
-__device__ __forceinline__ void quantize(float y, const Codebook &cb, const Levels &lv, int &bits,
-                                         float &level) {
-  const bool c0 = cb.t[0] < y, c1 = cb.t[1] < y, c2 = cb.t[2] < y, c3 = cb.t[3] < y;
-  const bool c4 = cb.t[4] < y, c5 = cb.t[5] < y, c6 = cb.t[6] < y;
-  const bool b1 = c5 | (c1 & !c3);
-  const bool b0 = (c4 ^ c5 ^ c6) | ((c0 ^ c1 ^ c2) & !c3);
-  bits = (b0 ? 1 : 0) | (b1 ? 2 : 0) | (c3 ? 4 : 0);
-  if (kLevel) {
-    float c = lv.c[0];
-    c = c0 ? lv.c[1] : c;
-    c = c1 ? lv.c[2] : c;
-    c = c2 ? lv.c[3] : c;
-    c = c3 ? lv.c[4] : c;
-    c = c4 ? lv.c[5] : c;
-    c = c5 ? lv.c[6] : c;
-    c = c6 ? lv.c[7] : c;
-    level = c;
-  }
+  for (int j = 0; j < 7; ++j) idx += (cb.t[j] < y) ? 1 : 0;
+  return idx;
 }
 
 // 8 coordinates of one vector as raw bytes: one 16-byte load (bf16, f16) or
@@ -176,7 +147,6 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a, int64_t num_t
   const int row = lane >> 4, oct = lane & 15;   // token 4*wave+row, coordinates 8*oct..+7
   const int H = a.num_kv_heads;
   const int tok = 4 * wave + row;
-  const Levels lv = levels_in_registers(a.cb);
 
   __shared__ __align__(16) _Float16 ehi[kEncTokens][kEStride];
   __shared__ __align__(16) _Float16 elo[kEncTokens][kEStride];
@@ -186,6 +156,17 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a, int64_t num_t
   __shared__ __align__(16) uint16_t vnorm[kEncTokens];
   __shared__ int blk[kEncTokens], off[kEncTokens], valid[kEncTokens], leader[kEncTokens];
   __shared__ int full_page;
+  __shared__ float lut[8];
+
+  if (tid < 8) {
+    float cv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cv[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[j])));
+    float c = cv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) c = (tid == j) ? cv[j] : c;
+    lut[tid] = c;
+  }
 
   // This wave's projection rows: 16 * (2 * wave + nt) + (lane % 16), columns
   // 32 * kk + 8 * (lane / 16) + 0..7 -- the B operand layout of the f16 MFMA.
@@ -272,16 +253,13 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a, int64_t num_t
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float yk = xk[j] * sk, yv = xv[j] * sv;
-        int bk, bv;
-        float lvk = 0.0f, dummy = 0.0f;
-        quantize<true>(yk, a.cb, lv, bk, lvk);
-        quantize<false>(yv, a.cb, lv, bv, dummy);
+        const int bk = level_index(yk, a.cb), bv = level_index(yv, a.cb);
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
           kb[p] |= ((bk >> p) & 1) << j;
           vb[p] |= ((bv >> p) & 1) << j;
         }
-        e[j] = yk - lvk;
+        e[j] = yk - lut[bk];
         ge = fmaf(e[j], e[j], ge);
       }
       const float gam = sqrtf(row_sum(ge));

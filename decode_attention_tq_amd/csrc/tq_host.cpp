@@ -85,6 +85,14 @@ tq::Codebook device_codebook(const tq_codebook *cb) {
   for (int i = 0; i < 8; ++i) d.c[i] = cb->centroids[i];
   for (int i = 0; i < 7; ++i) d.t[i] = cb->thresholds[i];
   d.qjl_scale = cb->qjl_scale;
+  // c4 = -b0 - b1 + b2 + b3, c5 = b0 - b1 + b2 - b3, c6 = -b0 + b1 + b2 - b3,
+  // c7 = b0 + b1 + b2 + b3 (signs of B_p at the codes 4..7), solved in double.
+  const double c4 = cb->centroids[4], c5 = cb->centroids[5], c6 = cb->centroids[6],
+               c7 = cb->centroids[7];
+  d.beta[0] = (float)((-c4 + c5 - c6 + c7) / 4.0);
+  d.beta[1] = (float)((-c4 - c5 + c6 + c7) / 4.0);
+  d.beta[2] = (float)((c4 + c5 + c6 + c7) / 4.0);
+  d.beta[3] = (float)((c4 - c5 - c6 + c7) / 4.0);
   return d;
 }
 

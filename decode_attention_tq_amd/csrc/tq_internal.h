@@ -28,6 +28,10 @@ struct Codebook {
   float c[8];        // ascending levels
   float t[7];        // thresholds
   float qjl_scale;   // sqrt(pi/2)/m
+  // Bit-plane form of the levels: with B_p = 1 - 2 b_p for the code bits
+  // b0, b1, b2 and their xor, c[idx] = -(beta0 B0 + beta1 B1 + beta2 B2 + beta3 Bx)
+  // exactly (the levels are an odd function of the bits: c[7-i] = -c[i]).
+  float beta[4];
 };
 
 struct EncodeArgs {
