@@ -18,12 +18,13 @@
 
 #include <math.h>
 
-#include "tq_common.hpp"
+#include "tq_mfma.hpp"
 
 namespace tq {
 namespace {
 
-constexpr int kPartStride = 132;  // m, l, pad, pad, acc[128]
+constexpr int kPartStride = 132;  // m (log2 units), l, pad, pad, acc[128]
+constexpr float kLog2e = 1.4426950408889634f;
 
 // A context length above the planned maximum breaks the caller contract; it
 // is cut to what the block table row and the split plan cover, so that no
@@ -33,45 +34,121 @@ __device__ __forceinline__ int clamped_context(const DecodeArgs &a, int b) {
   return min(max(a.context_lens[b], 0), cap);
 }
 
-// ---- 1. query prep: a workgroup per 4 query rows ----------------------------
-// Thread (i, half) keeps S[i][64*half .. +64) in registers (all 64 loads in
-// flight at once), then forms the partial S q for each row; LDS adds the two
-// halves.  The rotation runs on wave w for row w.
-constexpr int kPrepRows = 4;
+// ---- 1. query prep: a workgroup per (sequence, query position, KV head) ----
+// Thread (i, half) keeps S[i][64*half .. +64) in registers, then forms the
+// partial S q of every head of the group; LDS adds the two halves.  Wave w
+// rotates heads w, w+4, ...  For the matrix-core pass the workgroup also
+// writes the score contraction's A operands (see split_mfma_kernel): rows
+// (head, digit r).  With 2^E bounding |x| over the head, Y = rint(x 2^(19-E))
+// is written in balanced base 32, Y = d0 2^15 + d1 2^10 + d2 2^5 + d3 with
+// every |d_r| <= 16 (exact in e4m3), and row r carries d_r with scale
+// 2^(E-4-5r): x to 2^-20 of the head's largest magnitude.  Logits of keys
+// with large norms need these 19 bits; 16 (base-16 digits) leave errors near
+// 1e-3 in peaked rows.
+__device__ __forceinline__ int bound_exponent(float M) {  // M < 2^E for finite M > 0
+  const int ex = (int)((__float_as_uint(M) >> 23) & 0xFFu);
+  return ex == 0 ? -126 : ex - 126;
+}
 
-__global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a, int64_t rows) {
+__device__ __forceinline__ uint32_t fp8_digit(float d) {  // exact for integers |d| <= 16
+  return __builtin_amdgcn_cvt_pk_fp8_f32(d, 0.0f, 0, false) & 0xFFu;
+}
+
+__global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * kPrepRows;
-  __shared__ float qs[kPrepRows][kHeadDim];
-  __shared__ float part[2][kPrepRows][kHeadDim];
-  const int64_t r = r0 + wave;
-  float x0 = 0.0f, x1 = 0.0f;
-  if (r < rows) {
-    x0 = load_as_float(a.q, a.q_dtype, r * kHeadDim + lane);
-    x1 = load_as_float(a.q, a.q_dtype, r * kHeadDim + 64 + lane);
-  }
-  qs[wave][lane] = x0;
-  qs[wave][lane + 64] = x1;
+  const int G = a.group;
+  const int64_t grp = blockIdx.x;
+  const int64_t row0 = grp * G;
+  __shared__ float qs[kMaxGroup][kHeadDim];
+  __shared__ float part[2][kMaxGroup][kQjlDim];
+  __shared__ float qp[kMaxGroup][256];
+  __shared__ float hmax[kMaxGroup][2];
+  for (int idx = tid; idx < G * kHeadDim; idx += 256)
+    qs[idx >> 7][idx & 127] = load_as_float(a.q, a.q_dtype, row0 * kHeadDim + idx);
   const int i = tid & 127, half = tid >> 7;
   float sk[64];
 #pragma unroll
   for (int k = 0; k < 64; ++k) sk[k] = a.St[(half * 64 + k) * kQjlDim + i];
   lds_barrier();
-#pragma unroll
-  for (int rr = 0; rr < kPrepRows; ++rr) {
+  for (int g = 0; g < G; ++g) {
     float acc = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 64; ++k) acc = fmaf(sk[k], qs[rr][half * 64 + k], acc);
-    part[half][rr][i] = acc;
+    for (int k = 0; k < 64; ++k) acc = fmaf(sk[k], qs[g][half * 64 + k], acc);
+    part[half][g][i] = acc;
+  }
+  for (int g = wave; g < G; g += 4) {
+    float x0 = qs[g][lane], x1 = qs[g][lane + 64];
+    wave_fwht128(x0, x1, lane);
+    qp[g][lane] = x0;
+    qp[g][lane + 64] = x1;
   }
   lds_barrier();
-  if (r >= rows) return;
-  wave_fwht128(x0, x1, lane);
-  float *out = a.qprep + r * 256;
-  out[lane] = x0;
-  out[lane + 64] = x1;
-  out[128 + lane] = a.cb.qjl_scale * (part[0][wave][lane] + part[1][wave][lane]);
-  out[128 + lane + 64] = a.cb.qjl_scale * (part[0][wave][lane + 64] + part[1][wave][lane + 64]);
+  for (int idx = tid; idx < G * kQjlDim; idx += 256) {
+    const int g = idx >> 7, c = idx & 127;
+    qp[g][128 + c] = a.cb.qjl_scale * (part[0][g][c] + part[1][g][c]);
+  }
+  lds_barrier();
+  for (int idx = tid; idx < G * 256; idx += 256) a.qprep[row0 * 256 + idx] = qp[idx >> 8][idx & 255];
+  if (a.qa == nullptr) return;
+
+  for (int g = wave; g < G; g += 4) {
+    float mq = fmaxf(fabsf(qp[g][lane]), fabsf(qp[g][lane + 64]));
+    float ms = fmaxf(fabsf(qp[g][128 + lane]), fabsf(qp[g][192 + lane]));
+    mq = wave_max(mq);
+    ms = wave_max(ms);
+    if (lane == 0) {
+      hmax[g][0] = mq;
+      hmax[g][1] = ms;
+    }
+  }
+  lds_barrier();
+  float beta[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
+  const int NT = a.qk_tiles;
+  const int nwords = NT * 5 * 64 * 8;
+  uint32_t *qa = a.qa + grp * (int64_t)(NT * 5 * 64 * 9);
+  for (int widx = tid; widx < nwords; widx += 256) {
+    const int j = widx & 7, ln = (widx >> 3) & 63, pt = widx >> 9;
+    const int p = pt % 5, nt = pt / 5;
+    const int g = 4 * nt + ((ln & 15) >> 2), r = ln & 3, ga = ln >> 4;
+    uint32_t word = 0;
+    if (g < G) {
+      const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
+      const float M = p < 4 ? fabsf(bp) * hmax[g][0] : hmax[g][1];
+      if (M > 0.0f) {
+        const int E = bound_exponent(M);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int sl = 4 * j + bb;
+          const int ci = b_coord(mfma_a_slot_k(ga, sl));
+          const float x = p < 4 ? -bp * qp[g][ci] : -qp[g][128 + ci];
+          const float y = rintf(ldexpf(x, 19 - E));  // |y| <= 2^19
+          const float d0 = rintf(y * 0x1p-15f);
+          float rem = y - d0 * 32768.0f;
+          const float d1 = rintf(rem * 0x1p-10f);
+          rem -= d1 * 1024.0f;
+          const float d2 = rintf(rem * 0.03125f);
+          const float d3 = rem - d2 * 32.0f;
+          const float d = r == 0 ? d0 : r == 1 ? d1 : r == 2 ? d2 : d3;
+          word |= fp8_digit(d) << (8 * bb);
+        }
+      }
+    }
+    qa[widx] = word;
+  }
+  for (int sidx = tid; sidx < NT * 5 * 64; sidx += 256) {
+    const int ln = sidx & 63, pt = sidx >> 6;
+    const int p = pt % 5, nt = pt / 5;
+    const int g = 4 * nt + ((ln & 15) >> 2), r = ln & 3;
+    int sc = kE8M0One;
+    if (g < G) {
+      const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
+      const float M = p < 4 ? fabsf(bp) * hmax[g][0] : hmax[g][1];
+      if (M > 0.0f) sc = min(max(bound_exponent(M) - 4 - 5 * r + kE8M0One, 0), 254);
+    }
+    qa[nwords + sidx] = (uint32_t)sc;
+  }
 }
 
 // ---- 2. split pass (vector ALU) --------------------------------------------
@@ -116,6 +193,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
   lds_barrier();
 
   const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
+  const float cs = a.scale * kLog2e;  // scores in log2 units
   float m[G], l[G], acc0[G], acc1[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -172,7 +250,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
         }
       }
 #pragma unroll
-      for (int g = 0; g < G; ++g) score[g] = a.scale * nk * fmaf(gm, ds[g], dk[g]);
+      for (int g = 0; g < G; ++g) score[g] = cs * nk * fmaf(gm, ds[g], dk[g]);
     } else {
 #pragma unroll
       for (int g = 0; g < G; ++g) score[g] = -INFINITY;
@@ -181,8 +259,8 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float mn = fmaxf(m[g], wave_max(score[g]));
-      const float p = (mn == -INFINITY) ? 0.0f : __expf(score[g] - mn);
-      const float corr = (mn == -INFINITY) ? 1.0f : __expf(m[g] - mn);
+      const float p = (mn == -INFINITY) ? 0.0f : exp2f(score[g] - mn);
+      const float corr = (mn == -INFINITY) ? 1.0f : exp2f(m[g] - mn);
       l[g] = l[g] * corr + wave_sum(p);
       acc0[g] *= corr;
       acc1[g] *= corr;
@@ -243,7 +321,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
     float Ls = 0.0f, A = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = (red_m[w][g] == -INFINITY) ? 0.0f : __expf(red_m[w][g] - M);
+      const float f = (red_m[w][g] == -INFINITY) ? 0.0f : exp2f(red_m[w][g] - M);
       Ls = fmaf(f, red_l[w][g], Ls);
       A = fmaf(f, red[(w * G + g) * 128 + d], A);
     }
@@ -253,6 +331,337 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
       part[1] = Ls;
     }
     part[4 + d] = A;
+  }
+}
+
+// ---- 2'. split pass on the matrix cores (single-query decode, G <= 8) -----
+// Both contractions run on the scaled fp8 x fp4 MFMA, with the stored bits as
+// the fp4 operand (B = 1 - 2 bit, one and_or per 8 values) and the float side
+// split into four fp8 digits in four A rows (the query side in balanced base
+// 32, see query_prep_kernel; the weights in base 16).  With the bit-plane form
+// of the levels, c[idx] = -(beta0 B0 + beta1 B1 + beta2 B2 + beta3 Bx) where
+// Bx = B0 B1 B2 is the plane of b0^b1^b2:
+//   <q', c[idx]> = sum_p <-beta_p q', B_p>        (4 MFMAs per page)
+//   gamma <s, sigma> = gamma <-s, B_sign>          (1 MFMA per page)
+//   o' = -sum_p beta_p sum_j w_j B_p,j  with w_j = p_j n_v,j  (4 planes)
+// A workgroup (4 waves) walks its chunk in tiles of 128 tokens (8 pages).
+// Wave w scores pages 2w, 2w+1 of a tile (MFMA K-block w of the value
+// contraction), keeps the block maximum m_w (integer, log2 units) and writes
+// the digits of w_j / 2^E_w to LDS; 2^(E_w + m_w - m) enters as the E8M0
+// scale of K-block w, so no cross-wave agreement on exponents is needed.
+// The value contraction is split by coordinates: wave w owns N-tiles 2w and
+// 2w+1 (32 coordinates) for all four planes.  The running maximum m is
+// shared by all waves and moves only when a tile exceeds it by 2^64.
+template <int NT>
+struct MfmaTile {
+  uint8_t wq[NT][4][4][128];   // [tile][head][digit][K] fp8 digits of w
+  uint32_t vs[4][400];         // [page pair][plane * 128 + coord], padded
+  float mi[NT][4][4];          // [tile][K-block][head] block maxima
+  int ex[NT][4][4];            // [tile][K-block][head] digit exponents
+};
+
+struct MfmaLoads {
+  uint4 kr[2];                 // K page records: plane lane/16, token lane%16
+  uint32_t nk[2], gm[2], nv[2];
+  uint4 va, vb;                // value planes of a page pair (threads < 192)
+};
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, xchg1(v));
+  v = fmaxf(v, xchg2(v));
+  v = fmaxf(v, xchg4(v));
+  return fmaxf(v, xchg8(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += xchg1(v);
+  v += xchg2(v);
+  v += xchg4(v);
+  return v + xchg8(v);
+}
+__device__ __forceinline__ float half_bits(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+__device__ __forceinline__ float sel4(const float (&v)[4], int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// 4x4 transpose of (16-lane row, register): row g register j -> row j register g.
+__device__ __forceinline__ void transpose_rows(uint32_t &r0, uint32_t &r1, uint32_t &r2, uint32_t &r3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  r0 = c[0];
+  r1 = c[1];
+  r2 = d[0];
+  r3 = d[1];
+}
+
+__device__ __forceinline__ void mfma_load_tile(MfmaLoads &R, const DecodeArgs &a, const int32_t *btab,
+                                               int h, int tok0, int s1, int wave, int lane, int tid) {
+  const int pg0 = tok0 >> 4;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int k = 2 * wave + kk;
+    // a page past the visible range re-reads the tile's first page (always
+    // visible); its tokens are masked
+    const int pg = (tok0 + 16 * k < s1) ? pg0 + k : pg0;
+    const int64_t blk = btab[pg];
+    const uint8_t *kp = a.k_cache + (blk * a.num_kv_heads + h) * kKPage;
+    const uint8_t *vp = a.v_cache + (blk * a.num_kv_heads + h) * kVPage;
+    R.kr[kk] = *reinterpret_cast<const uint4 *>(kp + 16 * lane);
+    R.nk[kk] = *reinterpret_cast<const uint16_t *>(kp + kKNorm + 2 * (lane & 15));
+    R.gm[kk] = *reinterpret_cast<const uint16_t *>(kp + kKGamma + 2 * (lane & 15));
+    R.nv[kk] = *reinterpret_cast<const uint16_t *>(vp + kVNorm + 2 * (lane & 15));
+  }
+  if (tid < 192) {
+    const int pr = tid / 48, rem = tid - 48 * pr;
+    const int pa = (tok0 + 32 * pr < s1) ? pg0 + 2 * pr : pg0;
+    const int pb = (tok0 + 32 * pr + 16 < s1) ? pg0 + 2 * pr + 1 : pg0;
+    const int off = kKPlane * (rem >> 4) + 16 * (rem & 15);
+    R.va = *reinterpret_cast<const uint4 *>(a.v_cache + ((int64_t)btab[pa] * a.num_kv_heads + h) * kVPage + off);
+    R.vb = *reinterpret_cast<const uint4 *>(a.v_cache + ((int64_t)btab[pb] * a.num_kv_heads + h) * kVPage + off);
+  }
+}
+
+// Two operand tiles (8 heads) need more than the 256 registers that two waves
+// per SIMD leave each wave.
+template <int NT>
+__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(DecodeArgs a) {
+  const int b = blockIdx.x;  // q_len == 1
+  const int h = blockIdx.y;
+  const int split = blockIdx.z;
+  const int L = clamped_context(a, b);
+  const int s0 = split * a.split_tokens;
+  const int s1 = min(s0 + a.split_tokens, L);
+  if (s0 >= s1) return;  // uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t16 = lane & 15, grow = lane >> 4;
+  const int64_t grp = (int64_t)b * a.num_kv_heads + h;
+  const int G = a.group;
+
+  __shared__ MfmaTile<NT> buf[2];
+  __shared__ float lred[4][NT][4];
+
+  // query-side operands of the score contraction
+  v8i Aq[NT][5];
+  int scq[NT][5];
+  {
+    const uint32_t *qa = a.qa + grp * (int64_t)(NT * 5 * 64 * 9);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int p = 0; p < 5; ++p) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((nt * 5 + p) * 64 + lane) * 8);
+        const uint4 u0 = src[0], u1 = src[1];
+        Aq[nt][p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        scq[nt][p] = (int)qa[NT * 5 * 64 * 8 + (nt * 5 + p) * 64 + lane];
+      }
+    }
+  }
+  float beta[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
+  const float cs = a.scale * kLog2e;
+  const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
+
+  float mref[NT][4];
+  float lsum[NT];
+  v4f acc[NT][4][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    lsum[nt] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) mref[nt][g] = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[nt][p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int gA = t16 >> 2, rA = lane & 3, kb = grow;  // A-operand row and scale block of this lane
+
+  auto process = [&](const MfmaLoads &R, int tok0, MfmaTile<NT> &Bf) {
+    // scores of pages 2*wave, 2*wave+1: lane (head grow, token t16).  The
+    // matrix ops write all 64 lanes whatever the exec mask, so they must never
+    // sit under a lane-dependent branch: every lane computes its score, and
+    // keys past the visible range are masked afterwards with a select.
+    float sc[2][NT];
+    bool valid[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t r0 = R.kr[kk].x, r1 = R.kr[kk].y, r2 = R.kr[kk].z, r3 = R.kr[kk].w;
+      transpose_rows(r0, r1, r2, r3);  // now plane p's word grow in r_p, signs in r3
+      const v8i B0 = b_pm1(r0), B1 = b_pm1(r1), B2 = b_pm1(r2), Bx = b_pm1(r0 ^ r1 ^ r2), Bs = b_pm1(r3);
+      const float nk = half_bits(R.nk[kk] & 0xFFFFu), gm = half_bits(R.gm[kk] & 0xFFFFu);
+      valid[kk] = tok0 + 16 * (2 * wave + kk) + t16 < s1;
+      float raw[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        v4f c = mfma_f8f4(Aq[nt][0], B0, zero, scq[nt][0]);
+        c = mfma_f8f4(Aq[nt][1], B1, c, scq[nt][1]);
+        c = mfma_f8f4(Aq[nt][2], B2, c, scq[nt][2]);
+        c = mfma_f8f4(Aq[nt][3], Bx, c, scq[nt][3]);
+        const v4f q = mfma_f8f4(Aq[nt][4], Bs, zero, scq[nt][4]);
+        const float code = (c[0] + c[1]) + (c[2] + c[3]);
+        const float qj = (q[0] + q[1]) + (q[2] + q[3]);
+        raw[nt] = cs * nk * fmaf(gm, qj, code);
+        // pin the score (and the matrix ops feeding it) to the unconditional
+        // path: otherwise they may be sunk into the branch of the select below
+        asm volatile("" : "+v"(raw[nt]));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sc[kk][nt] = valid[kk] ? raw[nt] : -INFINITY;
+    }
+    // block maximum, weights, digits
+    float mi[NT], ps[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      mi[nt] = ceilf(row_max16(fmaxf(sc[0][nt], sc[1][nt])));
+      float w[2];
+      ps[nt] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const float p = sc[kk][nt] == -INFINITY ? 0.0f : exp2f(sc[kk][nt] - mi[nt]);
+        ps[nt] += p;
+        // the norm of a slot past the visible range may hold any bits
+        w[kk] = (valid[kk] && p > 0.0f) ? p * half_bits(R.nv[kk] & 0xFFFFu) : 0.0f;
+      }
+      const float wm = row_max16(fmaxf(w[0], w[1]));
+      const int E = wm > 0.0f ? bound_exponent(wm) : 0;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint32_t X = (uint32_t)fminf(rintf(ldexpf(w[kk], 16 - E)), 65535.0f);
+        uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)(X >> 12), (float)((X >> 8) & 15u), 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)((X >> 4) & 15u), (float)(X & 15u), pk, true);
+        const int kap = b_kappa(32 * wave + 16 * kk + t16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Bf.wq[nt][grow][r][kap] = (uint8_t)(pk >> (8 * r));
+      }
+      if (t16 == 0) {
+        Bf.mi[nt][wave][grow] = mi[nt];
+        Bf.ex[nt][wave][grow] = E;
+      }
+    }
+    // value planes: interleave the 16-bit words of a page pair
+    if (tid < 192) {
+      const int pr = tid / 48, rem = tid - 48 * pr;
+      const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
+      uint4 o0, o1;
+      o0.x = __builtin_amdgcn_perm(R.vb.x, R.va.x, sel_lo);
+      o0.y = __builtin_amdgcn_perm(R.vb.x, R.va.x, sel_hi);
+      o0.z = __builtin_amdgcn_perm(R.vb.y, R.va.y, sel_lo);
+      o0.w = __builtin_amdgcn_perm(R.vb.y, R.va.y, sel_hi);
+      o1.x = __builtin_amdgcn_perm(R.vb.z, R.va.z, sel_lo);
+      o1.y = __builtin_amdgcn_perm(R.vb.z, R.va.z, sel_hi);
+      o1.z = __builtin_amdgcn_perm(R.vb.w, R.va.w, sel_lo);
+      o1.w = __builtin_amdgcn_perm(R.vb.w, R.va.w, sel_hi);
+      uint4 *dst = reinterpret_cast<uint4 *>(&Bf.vs[pr][128 * (rem >> 4) + 8 * (rem & 15)]);
+      dst[0] = o0;
+      dst[1] = o1;
+    }
+    lds_barrier();
+    // shared running maximum: moves only when a tile exceeds it by 2^64
+    bool moved = false;
+    float fct[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float Mt = uniform(fmaxf(fmaxf(Bf.mi[nt][0][g], Bf.mi[nt][1][g]), fmaxf(Bf.mi[nt][2][g], Bf.mi[nt][3][g])));
+        fct[nt][g] = 1.0f;
+        if (Mt > mref[nt][g] + 64.0f) {
+          fct[nt][g] = exp2f(mref[nt][g] - Mt);
+          mref[nt][g] = Mt;
+          moved = true;
+        }
+      }
+    }
+    if (moved) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float f = sel4(fct[nt], grow);
+        lsum[nt] *= f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[nt][p][j] *= f;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (ps[nt] > 0.0f) lsum[nt] += ps[nt] * exp2f(mi[nt] - sel4(mref[nt], grow));
+    // weight operand: row (head gA, digit rA), K-block scale from wave kb
+    v8i Aw[NT];
+    int sw[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint4 u0 = *reinterpret_cast<const uint4 *>(&Bf.wq[nt][gA][rA][16 * grow]);
+      const uint4 u1 = *reinterpret_cast<const uint4 *>(&Bf.wq[nt][gA][rA][64 + 16 * grow]);
+      Aw[nt] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      const float mb = Bf.mi[nt][kb][gA];
+      int scl = kE8M0One;
+      if (mb != -INFINITY) {
+        const float d = fmaxf(mb - sel4(mref[nt], gA), -300.0f);
+        scl = min(max(Bf.ex[nt][kb][gA] - 4 - 4 * rA + (int)d + kE8M0One, 0), 254);
+      }
+      sw[nt] = scl;
+    }
+    // value contraction: this wave's coordinates 32*wave .. +31
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = 16 * (2 * wave + j) + t16;
+      const uint32_t p0 = Bf.vs[grow][col], p1 = Bf.vs[grow][128 + col], p2 = Bf.vs[grow][256 + col];
+      const v8i V0 = b_pm1(p0), V1 = b_pm1(p1), V2 = b_pm1(p2), Vx = b_pm1(p0 ^ p1 ^ p2);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt][0][j] = mfma_f8f4(Aw[nt], V0, acc[nt][0][j], sw[nt]);
+        acc[nt][1][j] = mfma_f8f4(Aw[nt], V1, acc[nt][1][j], sw[nt]);
+        acc[nt][2][j] = mfma_f8f4(Aw[nt], V2, acc[nt][2][j], sw[nt]);
+        acc[nt][3][j] = mfma_f8f4(Aw[nt], Vx, acc[nt][3][j], sw[nt]);
+      }
+    }
+  };
+
+  const int ntiles = (s1 - s0 + 127) >> 7;
+  MfmaLoads RA, RB;
+  mfma_load_tile(RA, a, btab, h, s0, s1, wave, lane, tid);
+  for (int it = 0; it < ntiles; it += 2) {
+    if (it + 1 < ntiles) mfma_load_tile(RB, a, btab, h, s0 + 128 * (it + 1), s1, wave, lane, tid);
+    process(RA, s0 + 128 * it, buf[0]);
+    if (it + 1 < ntiles) {
+      if (it + 2 < ntiles) mfma_load_tile(RA, a, btab, h, s0 + 128 * (it + 2), s1, wave, lane, tid);
+      process(RB, s0 + 128 * (it + 1), buf[1]);
+    }
+  }
+
+  // row sums over the 16 lanes of a head, then over the waves
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float ls = row_sum16(lsum[nt]);
+    if (t16 == 0) lred[wave][nt][grow] = ls;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int g = 4 * nt + grow;
+    if (g >= G) continue;
+    float *part = a.partials + ((grp * G + g) * a.num_splits + split) * kPartStride;
+    if (wave == 0 && t16 == 0) {
+      part[0] = sel4(mref[nt], grow);
+      part[1] = (lred[0][nt][grow] + lred[1][nt][grow]) + (lred[2][nt][grow] + lred[3][nt][grow]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float o = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const v4f &c = acc[nt][p][j];
+        o = fmaf(-beta[p], (c[0] + c[1]) + (c[2] + c[3]), o);
+      }
+      part[4 + 16 * (2 * wave + j) + t16] = o;
+    }
   }
 }
 
@@ -280,7 +689,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
     float f = 0.0f;
     if (s < ns) {
       const float m = part[s * kPartStride];
-      f = (m == -INFINITY) ? 0.0f : __expf(m - M);
+      f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
       Ls = fmaf(f, part[s * kPartStride + 1], Ls);
     }
     fw[wave][lane] = f;
@@ -336,10 +745,24 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.q_len * a.num_q_heads;
   const unsigned row_blocks = (unsigned)((rows + 3) / 4);
-  hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)((rows + kPrepRows - 1) / kPrepRows)),
-                     dim3(256), 0, stream, a, rows);
+  const int64_t groups = (int64_t)a.num_seqs * a.q_len * a.num_kv_heads;
+  hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.qa != nullptr) {
+    dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
+    if (a.qk_tiles == 1) {
+      hipLaunchKernelGGL(split_mfma_kernel<1>, grid, dim3(256), 0, stream, a);
+    } else if (a.qk_tiles == 2) {
+      hipLaunchKernelGGL(split_mfma_kernel<2>, grid, dim3(256), 0, stream, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(merge_kernel, dim3(row_blocks), dim3(256), 0, stream, a, rows);
+    return hipGetLastError();
+  }
   switch (a.group) {
     case 1: e = launch_split<1>(a, stream); break;
     case 2: e = launch_split<2>(a, stream); break;

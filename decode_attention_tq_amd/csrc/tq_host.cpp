@@ -131,6 +131,11 @@ size_t decode_qprep_floats(int64_t rows) { return (size_t)rows * 256; }
 size_t decode_partial_floats(int64_t rows, int num_splits) {
   return (size_t)rows * (size_t)num_splits * kPartStride;
 }
+bool decode_uses_mfma(int q_len, int group) { return q_len == 1 && group <= 8; }
+int decode_qk_tiles(int group) { return group <= 4 ? 1 : group / 4; }
+size_t decode_qa_words(int64_t groups, int qk_tiles) {
+  return (size_t)groups * (size_t)qk_tiles * 5 * 64 * 9;  // 8 operand words + 1 scale per lane
+}
 }  // namespace tq
 
 extern "C" {
@@ -308,7 +313,13 @@ size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
   int stok, ns;
   plan_splits(num_seqs, q_len, num_kv_heads, max_context_len, tokens_per_split, &stok, &ns);
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
-  return (tq::decode_qprep_floats(rows) + tq::decode_partial_floats(rows, ns)) * sizeof(float);
+  size_t words = tq::decode_qprep_floats(rows) + tq::decode_partial_floats(rows, ns);
+  if (num_q_heads % num_kv_heads == 0) {
+    const int group = num_q_heads / num_kv_heads;
+    if (tq::decode_uses_mfma(q_len, group))
+      words += tq::decode_qa_words((int64_t)num_seqs * num_kv_heads, tq::decode_qk_tiles(group));
+  }
+  return words * sizeof(float);
 }
 
 tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
@@ -372,7 +383,15 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
   a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   a.qprep = (float *)workspace;
-  a.partials = (float *)workspace + tq::decode_qprep_floats(rows);
+  float *rest = (float *)workspace + tq::decode_qprep_floats(rows);
+  a.qa = nullptr;
+  a.qk_tiles = 0;
+  if (tq::decode_uses_mfma(q_len, group)) {
+    a.qa = (uint32_t *)rest;
+    a.qk_tiles = tq::decode_qk_tiles(group);
+    rest += tq::decode_qa_words((int64_t)num_seqs * num_kv_heads, a.qk_tiles);
+  }
+  a.partials = rest;
   a.cb = device_codebook(cb);
   hipError_t e = tq::launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -73,13 +73,23 @@ struct DecodeArgs {
   int num_splits;
   const float *St;     // [d][m]
   float *qprep;        // workspace: [rows][256] = rotated q | qjl_scale * S q
-  float *partials;     // workspace: [rows][num_splits][2 + 128]
+  // Matrix-core path only (else null): per (sequence, KV head) group the
+  // query-side A operands of the score contraction, [tiles][5][64 lanes][8]
+  // words, followed by their E8M0 scales [tiles][5][64].
+  uint32_t *qa;
+  int qk_tiles;        // 16-row operand tiles per group: 4 heads x 4 pieces each
+  float *partials;     // workspace: [rows][num_splits][4 + 128], m in log2 units
   Codebook cb;
 };
 
 // Workspace split of tq_decode_attention.
 size_t decode_qprep_floats(int64_t rows);
 size_t decode_partial_floats(int64_t rows, int num_splits);
+// The matrix-core split pass serves single-query decode with up to 8 query
+// heads per KV head; chunked prefill and larger groups use the vector pass.
+bool decode_uses_mfma(int q_len, int group);
+int decode_qk_tiles(int group);
+size_t decode_qa_words(int64_t groups, int qk_tiles);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

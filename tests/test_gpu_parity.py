@@ -221,3 +221,34 @@ def test_caller_supplied_qjl_matrix():
                            tables=(c32, t32, S))
     out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 2)
     check_decode(out, case["q"], kp, vp, case["table"], case["context_lens"], tables=(c32, t32, S))
+
+
+@pytest.mark.parametrize("Hq,Hkv,T", [(4, 4, 777), (8, 4, 777), (8, 2, 131)])
+def test_small_groups(Hq, Hkv, T):
+    """One and two query heads per KV head (unused operand rows), and a
+    context shorter than one 128-token tile."""
+    case = synth.gqa_case(seed=11, T=T, Hq=Hq, Hkv=Hkv)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], Hkv)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], Hkv)
+    check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"], case["context_lens"])
+
+
+def test_running_maximum_moves_along_the_sequence():
+    """Key norms ramp up 8x along the context with softmax scale 0.25: the
+    maximum log2-score grows from about 40 to about 350, so later tiles
+    overtake the running maximum by more than the rescale threshold (64)
+    several times; the output must still match."""
+    T = 4096
+    case = synth.gqa_case(seed=12, T=T, Hq=32, Hkv=8)
+    ramp = (1.0 + 7.0 * np.arange(T) / T)[:, None, None]
+    k = synth.round_to_bf16(case["k"] * ramp)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 8)
+    encode_gpu(cb, k, case["v"], case["slots"], kpool, vpool, with_norms=False)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 8,
+                     scale=0.25, tokens_per_split=4096)
+    err = check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"],
+                       case["context_lens"], scale=0.25)
+    print("max rel err", err.max())

@@ -139,16 +139,30 @@ def test_decode_validation():
     assert _dec(cb, wsb=need - 1) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
 
 
-def test_workspace_plan_is_consistent():
+def _operand_words(B, q_len, Hq, Hkv):
+    """Matrix-core operand words: single-query decode with <= 8 heads per KV
+    head keeps, per (sequence, KV head), tiles x 5 x 64 lanes x (8 + 1) words."""
+    G = Hq // Hkv
+    if q_len != 1 or G > 8:
+        return 0
+    tiles = 1 if G <= 4 else G // 4
+    return B * Hkv * tiles * 5 * 64 * 9
+
+
+@pytest.mark.parametrize("B,q_len,Hq,Hkv", [(1, 1, 32, 8), (2, 1, 32, 4), (1, 1, 32, 32),
+                                            (1, 4, 32, 8), (1, 1, 32, 2)])
+def test_workspace_plan_is_consistent(B, q_len, Hq, Hkv):
     cb = _fake_cb()
     ref = ctypes.byref(cb)
-    rows = 32
-    # rows * (256 prep floats + splits * 132 partial floats) * 4 bytes
+    rows = B * q_len * Hq
+    # 4 bytes x (rows x 256 prep floats + operand words + rows x splits x 132 partial floats)
     for maxc, tps in ((8192, 256), (8192, 1024), (131072, 0), (0, 0), (1, 0)):
-        ws = tq._lib.tq_decode_workspace_bytes(ref, 1, 1, 32, 8, maxc, tps)
-        per_row = ws // 4 // rows - 256
-        assert per_row % 132 == 0 and per_row >= 132
+        ws = tq._lib.tq_decode_workspace_bytes(ref, B, q_len, Hq, Hkv, max(maxc, q_len), tps)
+        words = ws // 4 - rows * 256 - _operand_words(B, q_len, Hq, Hkv)
+        assert ws % 4 == 0 and words % (rows * 132) == 0
+        splits = words // (rows * 132)
+        assert splits >= 1
         if tps:
-            assert per_row // 132 == max(1, -(-maxc // tps))
+            assert splits == max(1, -(-max(maxc, q_len) // tps))
     assert tq._lib.tq_decode_workspace_bytes(ref, 0, 1, 32, 8, 10, 0) == 0
     assert tq._lib.tq_k_page_bytes(ref) == 1088 and tq._lib.tq_v_page_bytes(ref) == 800
