@@ -1,6 +1,6 @@
 // Attention read directly from the compressed, paged cache (gfx950).
 //
-// Three launches on the caller's stream:
+// Launches on the caller's stream:
 //   1. query prep  : per query row, q' = H q (rotated once) and
 //                    s = sqrt(pi/2)/m * S q (the QJL side of the score), so
 //                    no split repeats them;
@@ -34,11 +34,67 @@ __device__ __forceinline__ int clamped_context(const DecodeArgs &a, int b) {
   return min(max(a.context_lens[b], 0), cap);
 }
 
-// ---- 1. query prep: a workgroup per (sequence, query position, KV head) ----
-// Thread (i, half) keeps S[i][64*half .. +64) in registers, then forms the
-// partial S q of every head of the group; LDS adds the two halves.  Wave w
-// rotates heads w, w+4, ...  For the matrix-core pass the workgroup also
-// writes the score contraction's A operands (see split_mfma_kernel): rows
+// LSE combine of the chunk partials of output row r by one wave, o' = acc'/l,
+// one inverse FWHT, store.  Lane l owns coordinates l and l + 64.  The chunk
+// accumulators are loaded 32 chunks at a time, the first batch issued before
+// the maxima are reduced, so a typical row costs one round trip to memory;
+// lane e computes the weight of chunk base + e and readlane broadcasts it.
+__device__ void merge_row(const DecodeArgs &a, int64_t r, int lane) {
+  const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
+  const int b = (int)(r / per_seq);
+  const int t = (int)((r / a.num_q_heads) % a.q_len);
+  const int L = clamped_context(a, b);
+  const int vis = max(0, L - a.q_len + t + 1);
+  const int ns = (vis + a.split_tokens - 1) / a.split_tokens;
+  const float *part = a.partials + r * a.num_splits * kPartStride;
+  constexpr int kBatch = 32;
+  float v0[kBatch], v1[kBatch];
+  auto load_batch = [&](int base) {
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const float *p = part + (int64_t)max(min(base + e, ns - 1), 0) * kPartStride;
+      v0[e] = p[4 + lane];
+      v1[e] = p[68 + lane];
+    }
+  };
+  if (ns > 0) load_batch(0);
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part[(int64_t)s * kPartStride]);
+  M = wave_max(M);
+  float Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;
+  for (int base = 0; base < ns; base += kBatch) {
+    if (base > 0) load_batch(base);
+    const int se = base + (lane & (kBatch - 1));
+    float f = 0.0f;
+    if (se < ns && lane < kBatch) {
+      const float m = part[(int64_t)se * kPartStride];
+      f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+      Ls = fmaf(f, part[(int64_t)se * kPartStride + 1], Ls);
+    }
+#pragma unroll
+    for (int e = 0; e < kBatch; ++e) {
+      const float fe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), e));  // 0 past ns
+      A0 = fmaf(fe, v0[e], A0);
+      A1 = fmaf(fe, v1[e], A1);
+    }
+  }
+  Ls = wave_sum(Ls);
+  float o0 = 0.0f, o1 = 0.0f;
+  if (Ls > 0.0f) {
+    const float inv = 1.0f / Ls;
+    o0 = A0 * inv;
+    o1 = A1 * inv;
+  }
+  wave_fwht128(o0, o1, lane);
+  store_from_float(a.out, a.out_dtype, r * kHeadDim + lane, o0);
+  store_from_float(a.out, a.out_dtype, r * kHeadDim + 64 + lane, o1);
+}
+
+// ---- 1. query prep: a workgroup per query row --------------------------------
+// Grid (sequence x position x KV head, head of the group).  Thread (i, half)
+// forms half of (S q)_i from S[i][64*half .. +64) held in registers; wave 0
+// rotates q.  For the matrix-core pass the workgroup also writes its head's
+// rows of the score contraction's A operands (see split_mfma_kernel): rows
 // (head, digit r).  With 2^E bounding |x| over the head, Y = rint(x 2^(19-E))
 // is written in balanced base 32, Y = d0 2^15 + d1 2^10 + d2 2^5 + d3 with
 // every |d_r| <= 16 (exact in e4m3), and row r carries d_r with scale
@@ -58,48 +114,39 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
   const int64_t grp = blockIdx.x;
-  const int64_t row0 = grp * G;
-  __shared__ float qs[kMaxGroup][kHeadDim];
-  __shared__ float part[2][kMaxGroup][kQjlDim];
-  __shared__ float qp[kMaxGroup][256];
-  __shared__ float hmax[kMaxGroup][2];
-  for (int idx = tid; idx < G * kHeadDim; idx += 256)
-    qs[idx >> 7][idx & 127] = load_as_float(a.q, a.q_dtype, row0 * kHeadDim + idx);
+  const int g = blockIdx.y;
+  const int64_t row = grp * G + g;
+  __shared__ float qs[kHeadDim];
+  __shared__ float part[2][kQjlDim];
+  __shared__ float qp[256];
+  __shared__ float hmax[2];
+  if (tid < kHeadDim) qs[tid] = load_as_float(a.q, a.q_dtype, row * kHeadDim + tid);
   const int i = tid & 127, half = tid >> 7;
   float sk[64];
 #pragma unroll
   for (int k = 0; k < 64; ++k) sk[k] = a.St[(half * 64 + k) * kQjlDim + i];
   lds_barrier();
-  for (int g = 0; g < G; ++g) {
-    float acc = 0.0f;
+  float acc = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 64; ++k) acc = fmaf(sk[k], qs[g][half * 64 + k], acc);
-    part[half][g][i] = acc;
-  }
-  for (int g = wave; g < G; g += 4) {
-    float x0 = qs[g][lane], x1 = qs[g][lane + 64];
+  for (int k = 0; k < 64; ++k) acc = fmaf(sk[k], qs[half * 64 + k], acc);
+  part[half][i] = acc;
+  if (wave == 0) {
+    float x0 = qs[lane], x1 = qs[lane + 64];
     wave_fwht128(x0, x1, lane);
-    qp[g][lane] = x0;
-    qp[g][lane + 64] = x1;
+    qp[lane] = x0;
+    qp[lane + 64] = x1;
+    const float mq = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    if (lane == 0) hmax[0] = mq;
   }
   lds_barrier();
-  for (int idx = tid; idx < G * kQjlDim; idx += 256) {
-    const int g = idx >> 7, c = idx & 127;
-    qp[g][128 + c] = a.cb.qjl_scale * (part[0][g][c] + part[1][g][c]);
-  }
+  if (tid < kQjlDim) qp[128 + tid] = a.cb.qjl_scale * (part[0][tid] + part[1][tid]);
   lds_barrier();
-  for (int idx = tid; idx < G * 256; idx += 256) a.qprep[row0 * 256 + idx] = qp[idx >> 8][idx & 255];
+  a.qprep[row * 256 + tid] = qp[tid];
   if (a.qa == nullptr) return;
 
-  for (int g = wave; g < G; g += 4) {
-    float mq = fmaxf(fabsf(qp[g][lane]), fabsf(qp[g][lane + 64]));
-    float ms = fmaxf(fabsf(qp[g][128 + lane]), fabsf(qp[g][192 + lane]));
-    mq = wave_max(mq);
-    ms = wave_max(ms);
-    if (lane == 0) {
-      hmax[g][0] = mq;
-      hmax[g][1] = ms;
-    }
+  if (wave == 1) {
+    const float ms = wave_max(fmaxf(fabsf(qp[128 + lane]), fabsf(qp[192 + lane])));
+    if (lane == 0) hmax[1] = ms;
   }
   lds_barrier();
   float beta[4];
@@ -107,47 +154,52 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
   const int NT = a.qk_tiles;
   const int nwords = NT * 5 * 64 * 8;
+  const int nt = g >> 2, gp = g & 3;
   uint32_t *qa = a.qa + grp * (int64_t)(NT * 5 * 64 * 9);
-  for (int widx = tid; widx < nwords; widx += 256) {
-    const int j = widx & 7, ln = (widx >> 3) & 63, pt = widx >> 9;
-    const int p = pt % 5, nt = pt / 5;
-    const int g = 4 * nt + ((ln & 15) >> 2), r = ln & 3, ga = ln >> 4;
+  // this head's rows: lanes 16*ga + 4*gp + r of tile nt
+  for (int widx = tid; widx < 5 * 16 * 8; widx += 256) {
+    const int j = widx & 7, li = (widx >> 3) & 15, p = widx >> 7;
+    const int ga = li >> 2, r = li & 3, ln = 16 * ga + 4 * gp + r;
+    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
+    const float M = p < 4 ? fabsf(bp) * hmax[0] : hmax[1];
     uint32_t word = 0;
-    if (g < G) {
-      const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-      const float M = p < 4 ? fabsf(bp) * hmax[g][0] : hmax[g][1];
-      if (M > 0.0f) {
-        const int E = bound_exponent(M);
+    if (M > 0.0f) {
+      const int E = bound_exponent(M);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int sl = 4 * j + bb;
-          const int ci = b_coord(mfma_a_slot_k(ga, sl));
-          const float x = p < 4 ? -bp * qp[g][ci] : -qp[g][128 + ci];
-          const float y = rintf(ldexpf(x, 19 - E));  // |y| <= 2^19
-          const float d0 = rintf(y * 0x1p-15f);
-          float rem = y - d0 * 32768.0f;
-          const float d1 = rintf(rem * 0x1p-10f);
-          rem -= d1 * 1024.0f;
-          const float d2 = rintf(rem * 0.03125f);
-          const float d3 = rem - d2 * 32.0f;
-          const float d = r == 0 ? d0 : r == 1 ? d1 : r == 2 ? d2 : d3;
-          word |= fp8_digit(d) << (8 * bb);
-        }
+      for (int bb = 0; bb < 4; ++bb) {
+        const int ci = b_coord(mfma_a_slot_k(ga, 4 * j + bb));
+        const float x = p < 4 ? -bp * qp[ci] : -qp[128 + ci];
+        const float y = rintf(ldexpf(x, 19 - E));  // |y| <= 2^19
+        const float d0 = rintf(y * 0x1p-15f);
+        float rem = y - d0 * 32768.0f;
+        const float d1 = rintf(rem * 0x1p-10f);
+        rem -= d1 * 1024.0f;
+        const float d2 = rintf(rem * 0.03125f);
+        const float d3 = rem - d2 * 32.0f;
+        const float d = r == 0 ? d0 : r == 1 ? d1 : r == 2 ? d2 : d3;
+        word |= fp8_digit(d) << (8 * bb);
       }
     }
-    qa[widx] = word;
+    qa[((nt * 5 + p) * 64 + ln) * 8 + j] = word;
   }
-  for (int sidx = tid; sidx < NT * 5 * 64; sidx += 256) {
-    const int ln = sidx & 63, pt = sidx >> 6;
-    const int p = pt % 5, nt = pt / 5;
-    const int g = 4 * nt + ((ln & 15) >> 2), r = ln & 3;
-    int sc = kE8M0One;
-    if (g < G) {
-      const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-      const float M = p < 4 ? fabsf(bp) * hmax[g][0] : hmax[g][1];
-      if (M > 0.0f) sc = min(max(bound_exponent(M) - 4 - 5 * r + kE8M0One, 0), 254);
+  if (tid < 5 * 16) {
+    const int li = tid & 15, p = tid >> 4;
+    const int r = li & 3, ln = 16 * (li >> 2) + 4 * gp + r;
+    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
+    const float M = p < 4 ? fabsf(bp) * hmax[0] : hmax[1];
+    const int sc = M > 0.0f ? min(max(bound_exponent(M) - 4 - 5 * r + kE8M0One, 0), 254) : kE8M0One;
+    qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)sc;
+  }
+  // rows of absent heads (groups of one or two heads) stay zero
+  if (g == 0 && G < 4) {
+    for (int widx = tid; widx < 5 * 64 * 8; widx += 256) {
+      const int ln = (widx >> 3) & 63;
+      if (((ln & 15) >> 2) >= G) qa[widx] = 0u;
     }
-    qa[nwords + sidx] = (uint32_t)sc;
+    for (int sidx = tid; sidx < 5 * 64; sidx += 256) {
+      const int ln = sidx & 63;
+      if (((ln & 15) >> 2) >= G) qa[nwords + sidx] = (uint32_t)kE8M0One;
+    }
   }
 }
 
@@ -663,74 +715,15 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
       part[4 + 16 * (2 * wave + j) + t16] = o;
     }
   }
+
 }
 
 // ---- 3. merge: one wave per output row --------------------------------------
-// Lanes read the chunk maxima and sums in parallel; the weighted sum of the
-// chunk accumulators issues its loads eight chunks at a time.
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  __shared__ float fw[4][64];
   if (r >= rows) return;
-  const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
-  const int b = (int)(r / per_seq);
-  const int t = (int)((r / a.num_q_heads) % a.q_len);
-  const int L = clamped_context(a, b);
-  const int vis = max(0, L - a.q_len + t + 1);
-  const int ns = (vis + a.split_tokens - 1) / a.split_tokens;
-  const float *part = a.partials + r * a.num_splits * kPartStride;
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part[s * kPartStride]);
-  M = wave_max(M);
-  float Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;
-  for (int base = 0; base < ns; base += 64) {
-    const int s = base + lane;
-    float f = 0.0f;
-    if (s < ns) {
-      const float m = part[s * kPartStride];
-      f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-      Ls = fmaf(f, part[s * kPartStride + 1], Ls);
-    }
-    fw[wave][lane] = f;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int cnt = min(64, ns - base);
-    int u = 0;
-    for (; u + 8 <= cnt; u += 8) {
-      float v0[8], v1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float *p = part + (int64_t)(base + u + e) * kPartStride + 4;
-        v0[e] = p[lane];
-        v1[e] = p[64 + lane];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f2 = fw[wave][u + e];
-        A0 = fmaf(f2, v0[e], A0);
-        A1 = fmaf(f2, v1[e], A1);
-      }
-    }
-    for (; u < cnt; ++u) {
-      const float *p = part + (int64_t)(base + u) * kPartStride + 4;
-      const float f2 = fw[wave][u];
-      A0 = fmaf(f2, p[lane], A0);
-      A1 = fmaf(f2, p[64 + lane], A1);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  Ls = wave_sum(Ls);
-  float o0 = 0.0f, o1 = 0.0f;
-  if (Ls > 0.0f) {
-    const float inv = 1.0f / Ls;
-    o0 = A0 * inv;
-    o1 = A1 * inv;
-  }
-  wave_fwht128(o0, o1, lane);
-  store_from_float(a.out, a.out_dtype, r * kHeadDim + lane, o0);
-  store_from_float(a.out, a.out_dtype, r * kHeadDim + 64 + lane, o1);
+  merge_row(a, r, lane);
 }
 
 template <int G>
@@ -746,10 +739,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.q_len * a.num_q_heads;
   const unsigned row_blocks = (unsigned)((rows + 3) / 4);
   const int64_t groups = (int64_t)a.num_seqs * a.q_len * a.num_kv_heads;
-  hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups, (unsigned)a.group), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.qa != nullptr) {
+  if (a.qa != nullptr) {  // matrix-core pass
     dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
     if (a.qk_tiles == 1) {
       hipLaunchKernelGGL(split_mfma_kernel<1>, grid, dim3(256), 0, stream, a);
@@ -758,19 +751,18 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     } else {
       return hipErrorInvalidValue;
     }
-    e = hipGetLastError();
+  } else {
+    switch (a.group) {
+      case 1: e = launch_split<1>(a, stream); break;
+      case 2: e = launch_split<2>(a, stream); break;
+      case 4: e = launch_split<4>(a, stream); break;
+      case 8: e = launch_split<8>(a, stream); break;
+      case 16: e = launch_split<16>(a, stream); break;
+      default: return hipErrorInvalidValue;
+    }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(merge_kernel, dim3(row_blocks), dim3(256), 0, stream, a, rows);
-    return hipGetLastError();
   }
-  switch (a.group) {
-    case 1: e = launch_split<1>(a, stream); break;
-    case 2: e = launch_split<2>(a, stream); break;
-    case 4: e = launch_split<4>(a, stream); break;
-    case 8: e = launch_split<8>(a, stream); break;
-    case 16: e = launch_split<16>(a, stream); break;
-    default: return hipErrorInvalidValue;
-  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_kernel, dim3(row_blocks), dim3(256), 0, stream, a, rows);
   return hipGetLastError();

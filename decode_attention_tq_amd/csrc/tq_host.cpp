@@ -387,9 +387,10 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
   a.qa = nullptr;
   a.qk_tiles = 0;
   if (tq::decode_uses_mfma(q_len, group)) {
+    const int64_t groups = (int64_t)num_seqs * num_kv_heads;
     a.qa = (uint32_t *)rest;
     a.qk_tiles = tq::decode_qk_tiles(group);
-    rest += tq::decode_qa_words((int64_t)num_seqs * num_kv_heads, a.qk_tiles);
+    rest += tq::decode_qa_words(groups, a.qk_tiles);
   }
   a.partials = rest;
   a.cb = device_codebook(cb);

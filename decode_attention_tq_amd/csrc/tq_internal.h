@@ -77,7 +77,7 @@ struct DecodeArgs {
   // query-side A operands of the score contraction, [tiles][5][64 lanes][8]
   // words, followed by their E8M0 scales [tiles][5][64].
   uint32_t *qa;
-  int qk_tiles;        // 16-row operand tiles per group: 4 heads x 4 pieces each
+  int qk_tiles;        // 16-row operand tiles per group: 4 heads x 4 digits each
   float *partials;     // workspace: [rows][num_splits][4 + 128], m in log2 units
   Codebook cb;
 };

@@ -1,10 +1,12 @@
 """Invariants of the compiled gfx950 kernels, checked on the assembly that
 hipcc emits for the kernel sources (no GPU needed).
 
-Matrix-core instructions write all 64 lanes of their destination registers
-whatever the exec mask, so they must never be issued while exec is partial
-(inside a lane-dependent branch): the compiler assumes masked lanes keep
-their register values and may reuse such registers."""
+* Matrix-core instructions write all 64 lanes of their destination registers
+  whatever the exec mask, so they must never be issued while exec is partial
+  (inside a lane-dependent branch): the compiler assumes masked lanes keep
+  their register values and may reuse such registers.
+* Every store and atomic is a vector-memory instruction: nothing writes
+  through the scalar data cache."""
 import os
 import re
 import shutil
@@ -56,3 +58,7 @@ def test_no_matrix_op_under_partial_exec(src, tmp_path):
     asm = out.read_text()
     assert "v_mfma" in asm
     assert mfma_under_partial_exec(asm) == []
+    # all stores and atomics go through the vector memory path
+    scalar_writes = [l.strip() for l in asm.splitlines()
+                     if re.match(r"\s*s_(store|atomic|buffer_store|buffer_atomic|dcache_wb|dcache_discard)", l)]
+    assert scalar_writes == []
