@@ -106,8 +106,21 @@ __device__ __forceinline__ int bound_exponent(float M) {  // M < 2^E for finite 
   return ex == 0 ? -126 : ex - 126;
 }
 
-__device__ __forceinline__ uint32_t fp8_digit(float d) {  // exact for integers |d| <= 16
+__device__ __forceinline__ uint32_t fp8_digit(float d) {  // exact for d = k 2^e, |k| <= 16
   return __builtin_amdgcn_cvt_pk_fp8_f32(d, 0.0f, 0, false) & 0xFFu;
+}
+
+// Digit r (0..3) of x in balanced base 32 under bound 2^E: with
+// Y = rint(x 2^(19-E)), Y = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16.
+__device__ __forceinline__ float query_digit(float x, int E, int r) {
+  const float y = rintf(ldexpf(x, 19 - E));  // |y| <= 2^19
+  const float d0 = rintf(y * 0x1p-15f);
+  float rem = y - d0 * 32768.0f;
+  const float d1 = rintf(rem * 0x1p-10f);
+  rem -= d1 * 1024.0f;
+  const float d2 = rintf(rem * 0.03125f);
+  const float d3 = rem - d2 * 32.0f;
+  return r == 0 ? d0 : r == 1 ? d1 : r == 2 ? d2 : d3;
 }
 
 __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
@@ -120,6 +133,7 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   __shared__ float part[2][kQjlDim];
   __shared__ float qp[256];
   __shared__ float hmax[2];
+  __shared__ float cpart[2][8];
   if (tid < kHeadDim) qs[tid] = load_as_float(a.q, a.q_dtype, row * kHeadDim + tid);
   const int i = tid & 127, half = tid >> 7;
   float sk[64];
@@ -152,46 +166,83 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   float beta[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
+  // per plane: 2^E bounds |x| (E >= -100 keeps every scale encodable); no
+  // digits at all when the plane is zero
+  int Ep[5];
+  bool nz[5];
+#pragma unroll
+  for (int p = 0; p < 5; ++p) {
+    const float M = p < 4 ? fabsf(beta[p]) * hmax[0] : hmax[1];
+    nz[p] = M > 0.0f;
+    Ep[p] = max(bound_exponent(M), -100);
+  }
   const int NT = a.qk_tiles;
   const int nwords = NT * 5 * 64 * 8;
   const int nt = g >> 2, gp = g & 3;
-  uint32_t *qa = a.qa + grp * (int64_t)(NT * 5 * 64 * 9);
-  // this head's rows: lanes 16*ga + 4*gp + r of tile nt
+  uint32_t *qa = a.qa + grp * (int64_t)(NT * (5 * 64 * 9 + 32));
+  // this head's rows: lanes 16*ga + 4*gp + r of tile nt.  The digit of a K
+  // slot is scaled by the factor that goes with the b_split operands.
   for (int widx = tid; widx < 5 * 16 * 8; widx += 256) {
     const int j = widx & 7, li = (widx >> 3) & 15, p = widx >> 7;
     const int ga = li >> 2, r = li & 3, ln = 16 * ga + 4 * gp + r;
     const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-    const float M = p < 4 ? fabsf(bp) * hmax[0] : hmax[1];
     uint32_t word = 0;
-    if (M > 0.0f) {
-      const int E = bound_exponent(M);
+    if (p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4]) {
+      const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const int ci = b_coord(mfma_a_slot_k(ga, 4 * j + bb));
-        const float x = p < 4 ? -bp * qp[ci] : -qp[128 + ci];
-        const float y = rintf(ldexpf(x, 19 - E));  // |y| <= 2^19
-        const float d0 = rintf(y * 0x1p-15f);
-        float rem = y - d0 * 32768.0f;
-        const float d1 = rintf(rem * 0x1p-10f);
-        rem -= d1 * 1024.0f;
-        const float d2 = rintf(rem * 0.03125f);
-        const float d3 = rem - d2 * 32.0f;
-        const float d = r == 0 ? d0 : r == 1 ? d1 : r == 2 ? d2 : d3;
-        word |= fp8_digit(d) << (8 * bb);
+        const int kap = mfma_a_slot_k(ga, 4 * j + bb);
+        const float x = p < 4 ? -bp * qp[b_coord(kap)] : -qp[128 + b_coord(kap)];
+        word |= fp8_digit(query_digit(x, E, r) * b_split_factor(kap)) << (8 * bb);
       }
     }
     qa[((nt * 5 + p) * 64 + ln) * 8 + j] = word;
   }
+  // accumulator start values: per row (digit r) the weighted sum of the
+  // unscaled A values (b_split_weight), for the code planes (summed over
+  // p < 4) and the sign plane.  Lanes 0-127 take one K slot.
+  {
+    float sc4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (tid < 128 && b_reg(tid) < 3) {
+      const int ci = b_coord(tid);
+      const float wgt = b_split_weight(tid);
+#pragma unroll
+      for (int p = 0; p < 5; ++p) {
+        if (!nz[p]) continue;
+        const int E = Ep[p];
+        const float x = p < 4 ? -beta[p] * qp[ci] : -qp[128 + ci];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = wgt * ldexpf(query_digit(x, E, r), E - 4 - 5 * r);
+          if (p < 4) sc4[r] += v; else sq4[r] += v;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc4[r] = wave_sum(sc4[r]);
+      sq4[r] = wave_sum(sq4[r]);
+    }
+    if (wave < 2 && lane == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        cpart[wave][r] = sc4[r];
+        cpart[wave][4 + r] = sq4[r];
+      }
+    }
+    lds_barrier();
+    if (tid < 8) qa[nwords + NT * 5 * 64 + (nt * 4 + gp) * 8 + tid] = __float_as_uint(cpart[0][tid] + cpart[1][tid]);
+  }
   if (tid < 5 * 16) {
     const int li = tid & 15, p = tid >> 4;
     const int r = li & 3, ln = 16 * (li >> 2) + 4 * gp + r;
-    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-    const float M = p < 4 ? fabsf(bp) * hmax[0] : hmax[1];
-    const int sc = M > 0.0f ? min(max(bound_exponent(M) - 4 - 5 * r + kE8M0One, 0), 254) : kE8M0One;
-    qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)sc;
+    const bool pz = p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4];
+    const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
+    qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)(pz ? min(E - 4 - 5 * r + kE8M0One, 254) : kE8M0One);
   }
   // rows of absent heads (groups of one or two heads) stay zero
   if (g == 0 && G < 4) {
+    for (int i = tid; i < (4 - G) * 8; i += 256) qa[nwords + NT * 5 * 64 + G * 8 + i] = 0u;
     for (int widx = tid; widx < 5 * 64 * 8; widx += 256) {
       const int ln = (widx >> 3) & 63;
       if (((ln & 15) >> 2) >= G) qa[widx] = 0u;
@@ -415,14 +466,24 @@ struct MfmaTile {
 struct MfmaLoads {
   uint4 kr[2];                 // K page records: plane lane/16, token lane%16
   uint32_t nk[2], gm[2], nv[2];
-  uint4 va, vb;                // value planes of a page pair (threads < 192)
+  uint4 vp[2];                 // value planes of the wave's page pair (lanes < 48)
 };
 
+// Maximum over the 16 lanes of a row on integer keys that order like the
+// floats (NaN-free inputs): no canonicalisation between the DPP steps.
+__device__ __forceinline__ int float_key(float v) {
+  const int b = __float_as_int(v);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ int row_max16_key(int k) {
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0xB1, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_mov_dpp(k, 0x4E, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(k, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false));
+  return max(k, __builtin_amdgcn_mov_dpp(k, 0x128, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, xchg1(v));
-  v = fmaxf(v, xchg2(v));
-  v = fmaxf(v, xchg4(v));
-  return fmaxf(v, xchg8(v));
+  const int k = row_max16_key(float_key(v));
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
 }
 __device__ __forceinline__ float row_sum16(float v) {
   v += xchg1(v);
@@ -450,30 +511,36 @@ __device__ __forceinline__ void transpose_rows(uint32_t &r0, uint32_t &r1, uint3
   r3 = d[1];
 }
 
+// Block ids of the chunk's first kBtCap pages are staged in LDS once, so a
+// tile's page loads depend on no global load and the prefetch of the next
+// tile runs fully in the shadow of the current one.
+constexpr int kBtCap = 1024;
+
+__device__ __forceinline__ int64_t block_of(const int32_t *bts, const int32_t *btab, int pg_first, int pg) {
+  const int i = pg - pg_first;
+  return i < kBtCap ? bts[i] : btab[pg];
+}
+
 __device__ __forceinline__ void mfma_load_tile(MfmaLoads &R, const DecodeArgs &a, const int32_t *btab,
-                                               int h, int tok0, int s1, int wave, int lane, int tid) {
+                                               const int32_t *bts, int pg_first, int h, int tok0, int s1,
+                                               int wave, int lane) {
   const int pg0 = tok0 >> 4;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int k = 2 * wave + kk;
     // a page past the visible range re-reads the tile's first page (always
-    // visible); its tokens are masked
+    // visible); its tokens are masked.  The page is the same for the whole
+    // wave, so its address is formed in scalar registers.
     const int pg = (tok0 + 16 * k < s1) ? pg0 + k : pg0;
-    const int64_t blk = btab[pg];
+    const int64_t blk = __builtin_amdgcn_readfirstlane((int)block_of(bts, btab, pg_first, pg));
     const uint8_t *kp = a.k_cache + (blk * a.num_kv_heads + h) * kKPage;
     const uint8_t *vp = a.v_cache + (blk * a.num_kv_heads + h) * kVPage;
     R.kr[kk] = *reinterpret_cast<const uint4 *>(kp + 16 * lane);
     R.nk[kk] = *reinterpret_cast<const uint16_t *>(kp + kKNorm + 2 * (lane & 15));
     R.gm[kk] = *reinterpret_cast<const uint16_t *>(kp + kKGamma + 2 * (lane & 15));
     R.nv[kk] = *reinterpret_cast<const uint16_t *>(vp + kVNorm + 2 * (lane & 15));
-  }
-  if (tid < 192) {
-    const int pr = tid / 48, rem = tid - 48 * pr;
-    const int pa = (tok0 + 32 * pr < s1) ? pg0 + 2 * pr : pg0;
-    const int pb = (tok0 + 32 * pr + 16 < s1) ? pg0 + 2 * pr + 1 : pg0;
-    const int off = kKPlane * (rem >> 4) + 16 * (rem & 15);
-    R.va = *reinterpret_cast<const uint4 *>(a.v_cache + ((int64_t)btab[pa] * a.num_kv_heads + h) * kVPage + off);
-    R.vb = *reinterpret_cast<const uint4 *>(a.v_cache + ((int64_t)btab[pb] * a.num_kv_heads + h) * kVPage + off);
+    // value planes of the wave's own page pair: lane < 48 takes 16 bytes
+    if (lane < 48) R.vp[kk] = *reinterpret_cast<const uint4 *>(vp + kKPlane * (lane >> 4) + 16 * (lane & 15));
   }
 }
 
@@ -495,12 +562,14 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
 
   __shared__ MfmaTile<NT> buf[2];
   __shared__ float lred[4][NT][4];
+  __shared__ int32_t bts[kBtCap];
 
   // query-side operands of the score contraction
   v8i Aq[NT][5];
   int scq[NT][5];
+  v4f cinit[NT], qinit[NT];  // accumulator start values (see b_split)
   {
-    const uint32_t *qa = a.qa + grp * (int64_t)(NT * 5 * 64 * 9);
+    const uint32_t *qa = a.qa + grp * (int64_t)(NT * (5 * 64 * 9 + 32));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -510,6 +579,9 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
         Aq[nt][p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
         scq[nt][p] = (int)qa[NT * 5 * 64 * 8 + (nt * 5 + p) * 64 + lane];
       }
+      const float *ci = reinterpret_cast<const float *>(qa + NT * 5 * 64 * 9) + (nt * 4 + grow) * 8;
+      cinit[nt] = v4f{ci[0], ci[1], ci[2], ci[3]};
+      qinit[nt] = v4f{ci[4], ci[5], ci[6], ci[7]};
     }
   }
   float beta[4];
@@ -517,6 +589,12 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
   for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
   const float cs = a.scale * kLog2e;
   const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
+  const int pg_first = s0 >> 4;
+  {
+    const int npg = min((s1 - s0 + 15) >> 4, kBtCap);
+    for (int i = tid; i < npg; i += 256) bts[i] = btab[pg_first + i];
+  }
+  lds_barrier();
 
   float mref[NT][4];
   float lsum[NT];
@@ -545,17 +623,18 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
     for (int kk = 0; kk < 2; ++kk) {
       uint32_t r0 = R.kr[kk].x, r1 = R.kr[kk].y, r2 = R.kr[kk].z, r3 = R.kr[kk].w;
       transpose_rows(r0, r1, r2, r3);  // now plane p's word grow in r_p, signs in r3
-      const v8i B0 = b_pm1(r0), B1 = b_pm1(r1), B2 = b_pm1(r2), Bx = b_pm1(r0 ^ r1 ^ r2), Bs = b_pm1(r3);
+      const v8i B0 = b_split(r0), B1 = b_split(r1), B2 = b_split(r2), Bx = b_split(r0 ^ r1 ^ r2),
+                Bs = b_split(r3);
       const float nk = half_bits(R.nk[kk] & 0xFFFFu), gm = half_bits(R.gm[kk] & 0xFFFFu);
       valid[kk] = tok0 + 16 * (2 * wave + kk) + t16 < s1;
       float raw[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        v4f c = mfma_f8f4(Aq[nt][0], B0, zero, scq[nt][0]);
+        v4f c = mfma_f8f4(Aq[nt][0], B0, cinit[nt], scq[nt][0]);
         c = mfma_f8f4(Aq[nt][1], B1, c, scq[nt][1]);
         c = mfma_f8f4(Aq[nt][2], B2, c, scq[nt][2]);
         c = mfma_f8f4(Aq[nt][3], Bx, c, scq[nt][3]);
-        const v4f q = mfma_f8f4(Aq[nt][4], Bs, zero, scq[nt][4]);
+        const v4f q = mfma_f8f4(Aq[nt][4], Bs, qinit[nt], scq[nt][4]);
         const float code = (c[0] + c[1]) + (c[2] + c[3]);
         const float qj = (q[0] + q[1]) + (q[2] + q[3]);
         raw[nt] = cs * nk * fmaf(gm, qj, code);
@@ -596,20 +675,20 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
         Bf.ex[nt][wave][grow] = E;
       }
     }
-    // value planes: interleave the 16-bit words of a page pair
-    if (tid < 192) {
-      const int pr = tid / 48, rem = tid - 48 * pr;
+    // value planes of this wave's page pair: interleave the 16-bit words
+    if (lane < 48) {
+      const uint4 &va = R.vp[0], &vb = R.vp[1];
       const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
       uint4 o0, o1;
-      o0.x = __builtin_amdgcn_perm(R.vb.x, R.va.x, sel_lo);
-      o0.y = __builtin_amdgcn_perm(R.vb.x, R.va.x, sel_hi);
-      o0.z = __builtin_amdgcn_perm(R.vb.y, R.va.y, sel_lo);
-      o0.w = __builtin_amdgcn_perm(R.vb.y, R.va.y, sel_hi);
-      o1.x = __builtin_amdgcn_perm(R.vb.z, R.va.z, sel_lo);
-      o1.y = __builtin_amdgcn_perm(R.vb.z, R.va.z, sel_hi);
-      o1.z = __builtin_amdgcn_perm(R.vb.w, R.va.w, sel_lo);
-      o1.w = __builtin_amdgcn_perm(R.vb.w, R.va.w, sel_hi);
-      uint4 *dst = reinterpret_cast<uint4 *>(&Bf.vs[pr][128 * (rem >> 4) + 8 * (rem & 15)]);
+      o0.x = __builtin_amdgcn_perm(vb.x, va.x, sel_lo);
+      o0.y = __builtin_amdgcn_perm(vb.x, va.x, sel_hi);
+      o0.z = __builtin_amdgcn_perm(vb.y, va.y, sel_lo);
+      o0.w = __builtin_amdgcn_perm(vb.y, va.y, sel_hi);
+      o1.x = __builtin_amdgcn_perm(vb.z, va.z, sel_lo);
+      o1.y = __builtin_amdgcn_perm(vb.z, va.z, sel_hi);
+      o1.z = __builtin_amdgcn_perm(vb.w, va.w, sel_lo);
+      o1.w = __builtin_amdgcn_perm(vb.w, va.w, sel_hi);
+      uint4 *dst = reinterpret_cast<uint4 *>(&Bf.vs[wave][128 * (lane >> 4) + 8 * (lane & 15)]);
       dst[0] = o0;
       dst[1] = o1;
     }
@@ -678,12 +757,12 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
 
   const int ntiles = (s1 - s0 + 127) >> 7;
   MfmaLoads RA, RB;
-  mfma_load_tile(RA, a, btab, h, s0, s1, wave, lane, tid);
+  mfma_load_tile(RA, a, btab, bts, pg_first, h, s0, s1, wave, lane);
   for (int it = 0; it < ntiles; it += 2) {
-    if (it + 1 < ntiles) mfma_load_tile(RB, a, btab, h, s0 + 128 * (it + 1), s1, wave, lane, tid);
+    if (it + 1 < ntiles) mfma_load_tile(RB, a, btab, bts, pg_first, h, s0 + 128 * (it + 1), s1, wave, lane);
     process(RA, s0 + 128 * it, buf[0]);
     if (it + 1 < ntiles) {
-      if (it + 2 < ntiles) mfma_load_tile(RA, a, btab, h, s0 + 128 * (it + 2), s1, wave, lane, tid);
+      if (it + 2 < ntiles) mfma_load_tile(RA, a, btab, bts, pg_first, h, s0 + 128 * (it + 2), s1, wave, lane);
       process(RB, s0 + 128 * (it + 1), buf[1]);
     }
   }

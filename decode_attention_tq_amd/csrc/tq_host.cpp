@@ -134,7 +134,8 @@ size_t decode_partial_floats(int64_t rows, int num_splits) {
 bool decode_uses_mfma(int q_len, int group) { return q_len == 1 && group <= 8; }
 int decode_qk_tiles(int group) { return group <= 4 ? 1 : group / 4; }
 size_t decode_qa_words(int64_t groups, int qk_tiles) {
-  return (size_t)groups * (size_t)qk_tiles * 5 * 64 * 9;  // 8 operand words + 1 scale per lane
+  // per tile: 8 operand words + 1 scale per lane and plane, 4 heads x 8 start values
+  return (size_t)groups * (size_t)qk_tiles * (5 * 64 * 9 + 32);
 }
 }  // namespace tq
 

@@ -46,6 +46,38 @@ __device__ __forceinline__ v8i b_pm1(uint32_t P) {
   return b;
 }
 
+// B operand from 32 bits with one instruction per register, avoiding fp4
+// subnormals: register v keeps bit v of each nibble in place, giving the e2m1
+// values alpha_v + beta_v * bit:
+//   v = 0: nibble 0x2 | bit0 -> 1.0 or 1.5   (alpha 1, beta 1/2)
+//   v = 1: nibble bit1       -> 0 or 1.0     (alpha 0, beta 1)
+//   v = 2: nibble bit2       -> 0 or 2.0     (alpha 0, beta 2)
+//   v = 3: nibble 0x2 | bit3 -> 1.0 or -1.0  (alpha 1, beta -2)
+// A contraction against the +-1 values 1 - 2 bit is recovered by scaling the
+// A value of a K slot in register v by f_v = -2/beta_v (-4, -2, -1, +1) and
+// adding sum_k A_k (1 - f_v alpha_v), i.e. weights 5, 1, 1, 0 (b_split_weight):
+//   sum_k A_k (1 - 2 b_k) = sum_k (f_v A_k) B'_k + sum_k (1 - f_v alpha_v) A_k.
+__device__ __forceinline__ v8i b_split(uint32_t P) {
+  v8i b;
+  b[0] = (int)((P & 0x11111111u) | 0x22222222u);
+  b[1] = (int)(P & 0x22222222u);
+  b[2] = (int)(P & 0x44444444u);
+  b[3] = (int)((P & 0x88888888u) | 0x22222222u);
+  b[4] = b[5] = b[6] = b[7] = 0;
+  return b;
+}
+// Register of logical K index kap inside its 32-wide block, the A factor and
+// the start-value weight that go with b_split.
+__device__ __forceinline__ int b_reg(int kap) { return (kap >> 3) & 3; }
+__device__ __forceinline__ float b_split_factor(int kap) {
+  const int v = b_reg(kap);
+  return v == 0 ? -4.0f : v == 1 ? -2.0f : v == 2 ? -1.0f : 1.0f;
+}
+__device__ __forceinline__ float b_split_weight(int kap) {
+  const int v = b_reg(kap);
+  return v == 0 ? 5.0f : v == 3 ? 0.0f : 1.0f;
+}
+
 __device__ __forceinline__ v4f mfma_f8f4(const v8i &A, const v8i &B, const v4f &C, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, 0, 4, 0, scale_a, 0, kE8M0One);
 }

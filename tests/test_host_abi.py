@@ -141,12 +141,13 @@ def test_decode_validation():
 
 def _operand_words(B, q_len, Hq, Hkv):
     """Matrix-core operand words: single-query decode with <= 8 heads per KV
-    head keeps, per (sequence, KV head), tiles x 5 x 64 lanes x (8 + 1) words."""
+    head keeps, per (sequence, KV head) and operand tile, 5 x 64 lanes x (8 + 1)
+    words and 4 heads x 8 accumulator start values."""
     G = Hq // Hkv
     if q_len != 1 or G > 8:
         return 0
     tiles = 1 if G <= 4 else G // 4
-    return B * Hkv * tiles * 5 * 64 * 9
+    return B * Hkv * tiles * (5 * 64 * 9 + 32)
 
 
 @pytest.mark.parametrize("B,q_len,Hq,Hkv", [(1, 1, 32, 8), (2, 1, 32, 4), (1, 1, 32, 32),
