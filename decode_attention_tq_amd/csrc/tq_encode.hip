@@ -1,421 +1,533 @@
-// Fused TurboQuant encoder for gfx950.
+// Fused TurboQuant encoder for gfx950 (SwiftLM README, "TurboQuantization: KV
+// Cache Compression": K-cache steps 1-5 and the V-cache paragraph).
 //
-// A persistent grid of 4-wave workgroups walks tiles of 16 consecutive tokens
-// of one KV head; each tile encodes the 16 keys and the 16 values (SwiftLM
-// README, "TurboQuantization: KV Cache Compression", K-cache steps 1-5 and the
-// V-cache paragraph).
+// A persistent grid of 4-wave workgroups walks rounds of four tiles; a tile
+// is 16 consecutive tokens of one KV head and wave w owns tile w of a round.
 //
-// Vector pass.  Wave w takes tokens 4w..4w+3; in a wave, the 16 lanes of row r
-// hold token 4w+r and lane i of the row holds the 8 consecutive coordinates
-// 8i..8i+7, so every input vector arrives with one 16-byte load per lane
-// (narrow per-lane loads cap HBM throughput well below its peak).
-//   - norm: 8 squares per lane, then a sum over the row (DPP exchanges);
-//   - Walsh-Hadamard rotation: coordinate bits 0-2 are in-lane butterflies,
-//     bits 3-6 pair lanes i and i^1, ^2, ^4, ^8 of the same row (DPP);
-//   - codes: seven fp32 compares per coordinate ("t_j < y"), turned into the
-//     three bits of the level rank; a lane's 8 coordinates give one byte of
-//     each bit-plane record -- for keys exactly byte i of the token's record;
-//   - keys only: residual e = y - c[idx] (rotated domain), its length, and
-//     e * 2^8 (exact scaling) staged in LDS as a half "hi" part plus a half
-//     "lo" remainder.
-// Value planes are coordinate-major (one 16-bit word per coordinate, a bit per
-// token): the per-token bytes are staged, then 8x8 bit-matrix transposes turn
-// 16 tokens x 8 coordinates into 8 coordinate words.
-// QJL projection (matrix cores).  z = S r with r = H^T e is z = (S H) e.  Each
-// wave owns 32 of the 128 projection rows and keeps its rows of S H (hi and lo
-// halves, 64 registers) for the whole run; three f16 MFMA passes
-// (hi.hi + hi.lo + lo.hi) carry ~22 significant bits, so a sign differs from
-// exact arithmetic only within ~1e-6 of zero.  A ballot of "z >= 0" gives
-// 16-bit pieces of four tokens' sign records at once.
-// Output.  A tile that fills one page in order is written as 68 + 50
-// coalesced 16-byte stores from the LDS page images; otherwise records go out
-// token by token and value bits are merged into their pages with 32-bit
-// atomic and/or.  Barriers order LDS only, so stores stay in flight, and the
-// next tile's inputs are loaded while the current one is processed.
+// Rotation on the matrix cores.  The Walsh-Hadamard transform is a product
+// with H_128 = H_8 (x) H_16 (Sylvester, entries +-1), exact in bf16/f16, so
+// y = H x runs as 16x16x32 MFMAs on the raw inputs (fp32 inputs as three bf16
+// pieces).  Every 16x32 block of H is one of four +-1 register sets (the rows
+// of H_16 with the sign of an H_8 entry, which may flip between the two lane
+// halves).  Keys use C = X H (rows = tokens), values C = H X^T (rows =
+// coordinates), so both read the same 16-byte input loads.
+//
+// Codes from wave masks.  With the symmetric codebook, the level rank is
+// idx = [y > 0] ? 4 + c : 3 - c, c = #{k : t_k < |y|} over the three positive
+// thresholds (a tie goes to the lower cell for either sign, as #{t_j < y}).
+// Comparing |y| with t_k * ||y_raw|| gives the masks A_k (thermometer code)
+// and P = [y > 0]; the bit-planes are b2 = P, b1 = ~(A2 ^ P),
+// b0 = ~(A1 ^ A2 ^ A3 ^ P).  A mask of a key MFMA register covers 16 coordinates
+// of four tokens and of a value register 16 tokens of four coordinates: in
+// both cases 16-bit pieces of the page layout, moved out with writelane.
+//
+// Keys: residual e = y - c[idx] (rotated domain), gamma = ||e||, and the QJL
+// projection z = S r = (S H) e (r = H^T e) on the f16 MFMA with e and S H as
+// hi + lo halves (three passes, ~22 bits).  Wave w computes rows
+// 32w .. 32w+31 of z for all four tiles of the round from e staged in LDS;
+// a mask of "z >= 0" is a 16-bit piece of four tokens' sign records.
+//
+// Output: a tile that fills one page in order is written with coalesced
+// 16-byte stores of the LDS page images; otherwise records go out token by
+// token and value bits are merged into their pages with 32-bit atomic and/or.
+
+#include <utility>
 
 #include "tq_common.hpp"
 
 namespace tq {
 namespace {
 
-constexpr int kEncTokens = 16;
-constexpr int kEStride = 136;  // halves per staged residual row (128 + pad: spreads LDS banks)
-constexpr float kResidualScale = 256.0f;
+constexpr int kTok = 16;          // tokens per tile
+constexpr int kTiles = 4;         // tiles per round (one per wave)
+constexpr int kEHalves = 136;     // halves per staged residual row (128 + pad: spreads LDS banks)
+constexpr float kResScale = 256.0f;
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float float4v __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Level index of y: the number of thresholds strictly below it (a value on
-// a threshold goes to the lower cell), compared in fp32.  Each compare is
-// folded into the count at once, so no lane mask stays live.
-__device__ __forceinline__ int level_index(float y, const Codebook &cb) {
-  int idx = 0;
-#pragma unroll
-  for (int j = 0; j < 7; ++j) idx += (cb.t[j] < y) ? 1 : 0;
-  return idx;
-}
+__device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
 
-// 8 coordinates of one vector as raw bytes: one 16-byte load (bf16, f16) or
-// two (fp32).
-struct Raw8 {
-  uint4 a, b;
+// The four +-1 operand sets (8 values of 16 bits a lane).  Lane l holds
+// H_16[8*((l/16)&1) + j][l%16] for j = 0..7, as +-one.  Set 0: as is; 1: negated;
+// 2: negated in lanes 32..63; 3: negated in lanes 0..31.
+struct HSets {
+  v8s s[4];
 };
 
-__device__ __forceinline__ Raw8 load_raw8(const void *base, int dtype, int64_t elem) {
-  Raw8 r;
-  if (dtype == TQ_F32) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
-    r.a = p[0];
-    r.b = p[1];
-  } else {
-    r.a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
-    r.b = make_uint4(0u, 0u, 0u, 0u);
+__device__ __forceinline__ HSets make_hsets(int lane, uint16_t one) {
+  HSets h;
+  const int l16 = lane & 15, half = (lane >> 4) & 1, upper = lane >= 32;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint16_t b = parity((uint32_t)((8 * half + j) & l16)) ? (uint16_t)(one | 0x8000u) : one;
+    h.s[0][j] = (short)b;
+    h.s[1][j] = (short)(b ^ 0x8000u);
+    h.s[2][j] = (short)(upper ? (b ^ 0x8000u) : b);
+    h.s[3][j] = (short)(upper ? b : (b ^ 0x8000u));
   }
-  return r;
+  return h;
 }
 
-__device__ __forceinline__ void unpack8(const Raw8 &r, int dtype, float (&x)[8]) {
-  if (dtype == TQ_F32) {
-    x[0] = __uint_as_float(r.a.x); x[1] = __uint_as_float(r.a.y);
-    x[2] = __uint_as_float(r.a.z); x[3] = __uint_as_float(r.a.w);
-    x[4] = __uint_as_float(r.b.x); x[5] = __uint_as_float(r.b.y);
-    x[6] = __uint_as_float(r.b.z); x[7] = __uint_as_float(r.b.w);
-  } else {
-    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+// Operand for K step k (input coordinates 32k..32k+31) and output block n
+// (coordinates 16n..16n+15): H[32k + 8(l/16) + j][16n + l%16] =
+// H_8[2k + (l >= 32)][n] * H_16[...] -- the lane-half sign is a compile-time
+// function of (k, n).
+__device__ __forceinline__ const v8s &hop(const HSets &h, int k, int n) {
+  const int s0 = parity((uint32_t)((2 * k) & n)), s1 = parity((uint32_t)((2 * k + 1) & n));
+  if (s0 == s1) return s0 ? h.s[1] : h.s[0];
+  return s0 ? h.s[3] : h.s[2];
+}
+
+template <bool F16>
+__device__ __forceinline__ v4f mfma16(const v8s &a, const v8s &b, const v4f &c) {
+  if (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// Raw inputs of one lane: token l%16, coordinates 32k + 8(l/16) .. +7 for
+// k = 0..3, as 16-bit pieces (pc = 1 for bf16/f16, 3 bf16 pieces for fp32).
+template <int PC>
+struct In {
+  v8s x[4][PC];
+};
+
+// bf16 pieces hi + mid + lo of a float (exact for normal values).
+struct Split3 {
+  short h, m, l;
+};
+__device__ __forceinline__ Split3 split3(float v) {
+  const __bf16 bh = (__bf16)v;
+  const float r1 = v - (float)bh;
+  const __bf16 bm = (__bf16)r1;
+  const float r2 = r1 - (float)bm;
+  const __bf16 bl = (__bf16)r2;
+  return {__builtin_bit_cast(short, bh), __builtin_bit_cast(short, bm), __builtin_bit_cast(short, bl)};
+}
+
+template <int PC>
+__device__ __forceinline__ void load_in(In<PC> &r, const void *base, int64_t elem0, bool ok) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (dtype == TQ_BF16) {
-        x[2 * k] = __uint_as_float(w[k] << 16);
-        x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      } else {
-        x[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xFFFFu));
-        x[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
+  for (int k = 0; k < 4; ++k) {
+    if (PC == 1) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem0 + 32 * k);
+      r.x[k][0] = __builtin_bit_cast(v8s, u);
+    } else {
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = 0.0f;
+      if (ok) {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem0 + 32 * k);
+        const float4 a = p[0], b = p[1];
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const Split3 sp = split3(f[j]);
+        r.x[k][0][j] = sp.h;
+        r.x[k][1][j] = sp.m;
+        r.x[k][2][j] = sp.l;
       }
     }
   }
 }
 
-// Sum over the 16 lanes of a row, in every lane of the row.
-__device__ __forceinline__ float row_sum(float v) {
-  v += xchg1(v);
-  v += xchg2(v);
-  v += xchg4(v);
-  v += xchg8(v);
-  return v;
+// Per round LDS state.
+struct RoundLds {
+  uint8_t kimg[kTiles][kKPage];                 // K page images
+  uint8_t vimg[kTiles][kVPage];                 // V page images
+  _Float16 ehi[kTiles][kTok][kEHalves];         // residual * 256 (hi), slot order
+  _Float16 elo[kTiles][kTok][kEHalves];         // remainder (lo)
+  int blk[kTiles][kTok], off[kTiles][kTok], valid[kTiles][kTok], leader[kTiles][kTok];
+  int full[kTiles];
+  int active[kTiles];
+};
+
+// v_writelane_b32 through the LLVM intrinsic (HIP exposes no builtin for it):
+// the compiler then sees the scalar read and inserts the wait states a
+// preceding compare that wrote the mask requires, which it cannot do for
+// hand-written assembly.
+extern "C" __device__ int tq_llvm_writelane(int val, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Lane LANE of v takes the uniform value s.
+template <int LANE>
+__device__ __forceinline__ void writelane(uint32_t &v, uint32_t s) {
+  v = (uint32_t)tq_llvm_writelane((int)s, LANE, (int)v);
+}
+// Moves a 64-bit wave mask into lanes 2Q (bits 0-31) and 2Q+1 (bits 32-63) of v.
+template <int Q>
+__device__ __forceinline__ void put_mask(uint32_t &v, uint64_t m) {
+  writelane<2 * Q>(v, (uint32_t)m);
+  writelane<2 * Q + 1>(v, (uint32_t)(m >> 32));
 }
 
-// Unnormalised Walsh-Hadamard transform of a 128-vector spread over one row:
-// lane i holds coordinates 8i..8i+7.  Bits 0-2 of the coordinate are in-lane,
-// bits 3-6 are lane bits 0-3 (butterfly partner = lane ^ s, kept in the row).
-__device__ __forceinline__ void row_fwht(float (&x)[8], int lane) {
-#pragma unroll
-  for (int s = 1; s < 8; s <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j & s) continue;
-      const float a = x[j], b = x[j + s];
-      x[j] = a + b;
-      x[j + s] = a - b;
-    }
-  }
-#pragma unroll
-  for (int s = 1; s <= 8; s <<= 1) {
-    const float sg = (lane & s) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = fmaf(sg, x[j], xchg(x[j], s, lane));
-  }
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// 8x8 bit-matrix transpose of a 64-bit word: bit c of byte r moves to bit r
-// of byte c (three shift-and-mask exchange steps).
-__device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
-  uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
-  x = x ^ t ^ (t << 7);
-  t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
-  x = x ^ t ^ (t << 14);
-  t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
-  x = x ^ t ^ (t << 28);
-  return x;
-}
-
-__device__ __forceinline__ half8 load_half8(const uint16_t *p) {
-  return *reinterpret_cast<const half8 *>(p);
-}
-
-__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a, int64_t num_tiles) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = lane >> 4, oct = lane & 15;   // token 4*wave+row, coordinates 8*oct..+7
+template <int DT>
+__global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t num_tiles) {
+  constexpr bool kF16 = DT == TQ_F16;
+  constexpr int PC = DT == TQ_F32 ? 3 : 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: no exec masking around matrix ops
+  const int l16 = lane & 15, lg = lane >> 4;
   const int H = a.num_kv_heads;
-  const int tok = 4 * wave + row;
+  const int64_t nrounds = (num_tiles + kTiles - 1) / kTiles;
 
-  __shared__ __align__(16) _Float16 ehi[kEncTokens][kEStride];
-  __shared__ __align__(16) _Float16 elo[kEncTokens][kEStride];
-  __shared__ __align__(16) uint8_t kst[kKPage];               // K page image, by tile position
-  __shared__ __align__(16) uint8_t vst[3][16][kEncTokens];    // V plane bytes [plane][octet][token]
-  __shared__ __align__(16) uint16_t vwords[3][kHeadDim];      // V words, bit t = tile token t
-  __shared__ __align__(16) uint16_t vnorm[kEncTokens];
-  __shared__ int blk[kEncTokens], off[kEncTokens], valid[kEncTokens], leader[kEncTokens];
-  __shared__ int full_page;
-  __shared__ float lut[8];
+  __shared__ __align__(16) RoundLds L;
 
-  if (tid < 8) {
-    float cv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cv[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[j])));
-    float c = cv[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) c = (tid == j) ? cv[j] : c;
-    lut[tid] = c;
-  }
+  const HSets hs = make_hsets(lane, kF16 ? (uint16_t)0x3C00u : (uint16_t)0x3F80u);
 
-  // This wave's projection rows: 16 * (2 * wave + nt) + (lane % 16), columns
-  // 32 * kk + 8 * (lane / 16) + 0..7 -- the B operand layout of the f16 MFMA.
-  half8 bhi[2][4], blo[2][4];
+  // positive thresholds and 256 x positive levels, uniform.  The levels are
+  // separate scalars, chosen by selects: an array indexed by the code would
+  // be moved to LDS and cost a load per coordinate.
+  float tpos[3];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int prow = 16 * (2 * wave + nt) + (lane & 15);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int col = 32 * kk + 8 * (lane >> 4);
-      bhi[nt][kk] = load_half8(a.SHhi + prow * kHeadDim + col);
-      blo[nt][kk] = load_half8(a.SHlo + prow * kHeadDim + col);
-    }
-  }
-
-  // Software pipeline: slot and raw inputs of this lane's token for the next
-  // tile are loaded while the current tile is processed.
-  auto load_tile = [&](int64_t tl, int64_t &slot, Raw8 &rk, Raw8 &rv) {
-    const int hh = (int)(tl % H);
-    const int64_t tb = (tl / H) * kEncTokens;
-    slot = -1;
-    if (tid < kEncTokens && tb + tid < a.num_tokens) slot = a.slots[tb + tid];
-    const int64_t t = tb + tok;
-    rk.a = rk.b = rv.a = rv.b = make_uint4(0u, 0u, 0u, 0u);
-    if (t < a.num_tokens) {
-      const int64_t e = t * a.tok_stride + (int64_t)hh * a.head_stride + 8 * oct;
-      rk = load_raw8(a.k, a.dtype, e);
-      rv = load_raw8(a.v, a.dtype, e);
-    }
+  for (int k = 0; k < 3; ++k) tpos[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.t[4 + k])));
+  auto level = [&](int k) {
+    return kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[4 + k])));
   };
-  int64_t slot_cur = -1;
-  Raw8 rk_cur, rv_cur;
-  rk_cur.a = rk_cur.b = rv_cur.a = rv_cur.b = make_uint4(0u, 0u, 0u, 0u);
-  if ((int64_t)blockIdx.x < num_tiles) load_tile(blockIdx.x, slot_cur, rk_cur, rv_cur);
+  const float cp0 = level(0), cp1 = level(1), cp2 = level(2), cp3 = level(3);
 
-  for (int64_t tile = blockIdx.x; tile < num_tiles; tile += gridDim.x) {
-    const int h = (int)(tile % H);
-    const int64_t t0 = (tile / H) * kEncTokens;
-
-    if (tid < kEncTokens) {
-      valid[tid] = slot_cur >= 0;
-      blk[tid] = slot_cur >= 0 ? (int)(slot_cur / kBlock) : -1;
-      off[tid] = slot_cur >= 0 ? (int)(slot_cur % kBlock) : 0;
-    }
-    lds_barrier();
-    if (tid < kEncTokens) {
-      int lead = valid[tid];
-      for (int u = 0; u < tid; ++u)
-        if (valid[u] && blk[u] == blk[tid]) lead = 0;
-      leader[tid] = lead;
-    }
-    if (tid == 32) {
-      int full = 1;
-      for (int u = 0; u < kEncTokens; ++u)
-        full &= valid[u] && blk[u] == blk[0] && off[u] == u;
-      full_page = full;
-    }
-    int64_t slot_next = -1;
-    Raw8 rk_next, rv_next;
-    rk_next.a = rk_next.b = rv_next.a = rv_next.b = make_uint4(0u, 0u, 0u, 0u);
-    const int64_t next = tile + gridDim.x;
-    if (next < num_tiles) load_tile(next, slot_next, rk_next, rv_next);
-
-    // ---- vector pass: keys and values of token `tok`, 8 coordinates a lane ---
-    {
-      float xk[8], xv[8];
-      unpack8(rk_cur, a.dtype, xk);
-      unpack8(rv_cur, a.dtype, xv);
-      float qk = 0.0f, qv = 0.0f;
+  // This wave's QJL rows 32w .. 32w+31 of S H as the B operand of the f16
+  // MFMA, K slots in the staged residual's order: slot s <-> coordinate
+  // 16 (s & 7) + (s >> 3); lane l of step k holds slots 32k + 8(l/16) .. +7.
+  // The table stores exactly these registers, one 16-byte piece per lane.
+  v8s shi[2][4], slo[2][4];
+  {
+    const uint4 *op = reinterpret_cast<const uint4 *>(a.SHop);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        qk = fmaf(xk[j], xk[j], qk);
-        qv = fmaf(xv[j], xv[j], qv);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int base = (((wave * 2 + u) * 4 + k) * 2) * 64 + lane;
+        shi[u][k] = __builtin_bit_cast(v8s, op[base]);
+        slo[u][k] = __builtin_bit_cast(v8s, op[base + 64]);
       }
-      const float nk = sqrtf(row_sum(qk)), nv = sqrtf(row_sum(qv));
-      row_fwht(xk, lane);
-      row_fwht(xv, lane);
-      const float sk = nk > 0.0f ? kInvSqrt128 / nk : 0.0f;
-      const float sv = nv > 0.0f ? kInvSqrt128 / nv : 0.0f;
+  }
 
-      int kb[3] = {0, 0, 0}, vb[3] = {0, 0, 0};
-      float e[8];
-      float ge = 0.0f;
+  auto tile_src = [&](int64_t tile, int64_t &t0, int &h) {
+    h = (int)(tile % H);
+    t0 = (tile / H) * kTok;
+  };
+  // raw inputs of this lane's token (l%16) for the wave's tile of round R
+  auto load_round = [&](int64_t R, In<PC> &ik, In<PC> &iv) {
+    const int64_t tile = R * kTiles + wave;
+    int64_t t0 = 0;
+    int h = 0;
+    tile_src(tile, t0, h);
+    const int64_t t = t0 + l16;
+    const bool ok = tile < num_tiles && t < a.num_tokens;
+    const int64_t e0 = t * a.tok_stride + (int64_t)h * a.head_stride + 8 * lg;
+    load_in<PC>(ik, a.k, e0, ok);
+    load_in<PC>(iv, a.v, e0, ok);
+  };
+
+  In<PC> ik, iv;
+  if ((int64_t)blockIdx.x < nrounds) load_round(blockIdx.x, ik, iv);
+
+  for (int64_t R = blockIdx.x; R < nrounds; R += gridDim.x) {
+    const int64_t tile = R * kTiles + wave;
+    const bool active = tile < num_tiles;
+    int64_t t0 = 0;
+    int h = 0;
+    tile_src(tile, t0, h);
+
+    // slots of the tile: lane t < 16 holds token t
+    if (lane < kTok) {
+      const int64_t t = t0 + lane;
+      const int64_t slot = (active && t < a.num_tokens) ? a.slots[t] : -1;
+      L.valid[wave][lane] = slot >= 0;
+      L.blk[wave][lane] = slot >= 0 ? (int)(slot / kBlock) : -1;
+      L.off[wave][lane] = slot >= 0 ? (int)(slot % kBlock) : 0;
+    }
+    if (lane == 0) L.active[wave] = active;
+
+    In<PC> nk, nv;
+    const int64_t Rn = R + gridDim.x;
+    if (Rn < nrounds) load_round(Rn, nk, nv);
+
+    if (active) {
+      // ---- values: C = H X^T, lane l reg i = coordinate 16m + 4(l/16) + i, token l%16
+      {
+        v4f vy[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float yk = xk[j] * sk, yv = xv[j] * sv;
-        const int bk = level_index(yk, a.cb), bv = level_index(yv, a.cb);
+        for (int m = 0; m < 8; ++m) {
+          v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          kb[p] |= ((bk >> p) & 1) << j;
-          vb[p] |= ((bv >> p) & 1) << j;
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int pc = 0; pc < PC; ++pc) c = mfma16<kF16>(hop(hs, k, m), iv.x[k][pc], c);
+          vy[m] = c;
         }
-        e[j] = yk - lut[bk];
-        ge = fmaf(e[j], e[j], ge);
-      }
-      const float gam = sqrtf(row_sum(ge));
-      if (valid[tok]) {
+        float s2 = 0.0f;
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          kst[kKPlane * p + 16 * tok + oct] = (uint8_t)kb[p];
-          vst[p][oct][tok] = (uint8_t)vb[p];
-        }
-        half8 hi, lo;
+        for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float s = e[j] * kResidualScale;
-          hi[j] = (_Float16)s;
-          lo[j] = (_Float16)(s - (float)hi[j]);
-        }
-        *reinterpret_cast<half8 *>(&ehi[tok][8 * oct]) = hi;
-        *reinterpret_cast<half8 *>(&elo[tok][8 * oct]) = lo;
-        if (oct == 0) {
-          *reinterpret_cast<_Float16 *>(kst + kKNorm + 2 * tok) = to_half_sat(nk);
-          *reinterpret_cast<_Float16 *>(kst + kKGamma + 2 * tok) = to_half_sat(gam);
-          vnorm[tok] = __builtin_bit_cast(uint16_t, to_half_sat(nv));
-          if (a.norms_out) {
-            float *no = a.norms_out + ((t0 + tok) * H + h) * 3;
-            no[0] = nk;
-            no[1] = gam;
-            no[2] = nv;
+          for (int i = 0; i < 4; ++i) s2 = fmaf(vy[m][i], vy[m][i], s2);
+        s2 += xchg16(s2, lane);
+        s2 += xchg32(s2, lane);
+        const float sn = sqrtf(s2);  // = sqrt(128) |v|
+        float T[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) T[k] = tpos[k] * sn;
+        uint32_t vb[3] = {0u, 0u, 0u};
+        static_for<32>([&](auto qc) {
+          constexpr int q = decltype(qc)::value, m = q >> 2, i = q & 3;
+          const float y = vy[m][i];
+          const uint64_t A1 = __ballot(fabsf(y) > T[0]), A2 = __ballot(fabsf(y) > T[1]);
+          const uint64_t A3 = __ballot(fabsf(y) > T[2]), P = __ballot(y > 0.0f);
+          put_mask<q>(vb[0], ~(A1 ^ A2 ^ A3 ^ P));
+          put_mask<q>(vb[1], ~(A2 ^ P));
+          put_mask<q>(vb[2], P);
+        });
+        // lane L = 2(4m + i) + hf holds the words of coordinates 16m + 4g + i, g = 2hf, 2hf+1
+        {
+          const int q = lane >> 1, hf = lane & 1, m = q >> 2, i = q & 3;
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            uint16_t *img = reinterpret_cast<uint16_t *>(L.vimg[wave] + kKPlane * p);
+            img[16 * m + 4 * (2 * hf) + i] = (uint16_t)vb[p];
+            img[16 * m + 4 * (2 * hf + 1) + i] = (uint16_t)(vb[p] >> 16);
           }
         }
-      } else {
-#pragma unroll
-        for (int p = 0; p < 3; ++p) vst[p][oct][tok] = 0;
-      }
-    }
-    lds_barrier();
-
-    // ---- value words: 16 tokens x 8 coordinates -> 8 coordinate words -------
-    if (tid < 48) {
-      const int p = tid >> 4, c8 = tid & 15;
-      const uint64_t lo = transpose8x8(*reinterpret_cast<const uint64_t *>(&vst[p][c8][0]));
-      const uint64_t hi = transpose8x8(*reinterpret_cast<const uint64_t *>(&vst[p][c8][8]));
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w0 = (uint32_t)((lo >> (16 * q)) & 0xFFu) | ((uint32_t)((hi >> (16 * q)) & 0xFFu) << 8);
-        const uint32_t w1 = (uint32_t)((lo >> (16 * q + 8)) & 0xFFu) | ((uint32_t)((hi >> (16 * q + 8)) & 0xFFu) << 8);
-        w[q] = w0 | (w1 << 16);
-      }
-      *reinterpret_cast<uint4 *>(&vwords[p][8 * c8]) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-
-    // ---- QJL projection on the matrix cores --------------------------------
-    {
-      const int arow = lane & 15, acol = 8 * (lane >> 4);
-      float4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const half8 ah = *reinterpret_cast<const half8 *>(&ehi[arow][32 * kk + acol]);
-        const half8 al = *reinterpret_cast<const half8 *>(&elo[arow][32 * kk + acol]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bhi[nt][kk], acc[nt], 0, 0, 0);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo[nt][kk], acc[nt], 0, 0, 0);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bhi[nt][kk], acc[nt], 0, 0, 0);
+        const float nv = sn * kInvSqrt128;
+        if (lg == 0) {
+          reinterpret_cast<_Float16 *>(L.vimg[wave] + kVNorm)[l16] = to_half_sat(nv);
+          if (a.norms_out && t0 + l16 < a.num_tokens) a.norms_out[((t0 + l16) * H + h) * 3 + 2] = nv;
         }
       }
-      // acc[nt][i] at lane l is z for token 4*(l/16)+i, row 16*(2*wave+nt) + l%16
+      // ---- keys: C = X H, lane l reg i = token 4(l/16) + i, coordinate 16n + l%16
+      {
+        v4f ky[8];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+        for (int n = 0; n < 8; ++n) {
+          v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int pc = 0; pc < PC; ++pc) c = mfma16<kF16>(ik.x[k][pc], hop(hs, k, n), c);
+          ky[n] = c;
+        }
+        float sn[4], r256[4], T[4][3];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint64_t bits = __ballot(acc[nt][i] >= 0.0f);
-          if (lane < 4)
-            *reinterpret_cast<uint16_t *>(kst + kKSigns + 16 * (4 * lane + i) + 2 * (2 * wave + nt)) =
-                (uint16_t)(bits >> (16 * lane));
+          float s2 = 0.0f;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) s2 = fmaf(ky[n][i], ky[n][i], s2);
+          s2 += xchg1(s2);
+          s2 += xchg2(s2);
+          s2 += xchg4(s2);
+          s2 += xchg8(s2);
+          sn[i] = sqrtf(s2);
+          r256[i] = sn[i] > 0.0f ? kResScale / sn[i] : 0.0f;
+#pragma unroll
+          for (int k = 0; k < 3; ++k) T[i][k] = tpos[k] * sn[i];
+        }
+        uint32_t kb[3] = {0u, 0u, 0u};
+        float g2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float es[8][4];
+        static_for<32>([&](auto qc) {
+          constexpr int q = decltype(qc)::value, n = q >> 2, i = q & 3;
+          const float y = ky[n][i], ay = fabsf(y);
+          const bool a1 = ay > T[i][0], a2 = ay > T[i][1], a3 = ay > T[i][2], pp = y > 0.0f;
+          const uint64_t A1 = __ballot(a1), A2 = __ballot(a2), A3 = __ballot(a3), P = __ballot(pp);
+          put_mask<q>(kb[0], ~(A1 ^ A2 ^ A3 ^ P));
+          put_mask<q>(kb[1], ~(A2 ^ P));
+          put_mask<q>(kb[2], P);
+          // e * 256 = y * 256 / |y_raw| - sign * 256 * level
+          float lv = a1 ? cp1 : cp0;
+          lv = a2 ? cp2 : lv;
+          lv = a3 ? cp3 : lv;
+          const float e = fmaf(y, r256[i], pp ? -lv : lv);
+          es[n][i] = e;
+          g2[i] = fmaf(e, e, g2[i]);
+        });
+        // lane L = 2(4n + i) + hf holds 16-bit pieces (coordinates 16n..+15) of tokens 4g + i, g = 2hf, 2hf+1
+        {
+          const int q = lane >> 1, hf = lane & 1, n = q >> 2, i = q & 3;
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[wave] + kKPlane * p);
+            img[8 * (4 * (2 * hf) + i) + n] = (uint16_t)kb[p];
+            img[8 * (4 * (2 * hf + 1) + i) + n] = (uint16_t)(kb[p] >> 16);
+          }
+        }
+        // residual halves, slot 8 (l%16) + n of token 4(l/16) + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v8h hi, lo;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            hi[n] = (_Float16)es[n][i];
+            lo[n] = (_Float16)(es[n][i] - (float)hi[n]);
+          }
+          *reinterpret_cast<v8h *>(&L.ehi[wave][4 * lg + i][8 * l16]) = hi;
+          *reinterpret_cast<v8h *>(&L.elo[wave][4 * lg + i][8 * l16]) = lo;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = g2[i];
+          s += xchg1(s);
+          s += xchg2(s);
+          s += xchg4(s);
+          s += xchg8(s);
+          const float gam = sqrtf(s) * (1.0f / kResScale);
+          const float nk = sn[i] * kInvSqrt128;
+          const int tok = 4 * lg + i;
+          if (l16 == 0) {
+            reinterpret_cast<_Float16 *>(L.kimg[wave] + kKNorm)[tok] = to_half_sat(nk);
+            reinterpret_cast<_Float16 *>(L.kimg[wave] + kKGamma)[tok] = to_half_sat(gam);
+            if (a.norms_out && t0 + tok < a.num_tokens) {
+              float *no = a.norms_out + ((t0 + tok) * H + h) * 3;
+              no[0] = nk;
+              no[1] = gam;
+            }
+          }
         }
       }
+    }
+    // leaders of destination blocks and the full-page test, per tile
+    if (lane < kTok) {
+      int lead = L.valid[wave][lane];
+      for (int u = 0; u < lane; ++u)
+        if (L.valid[wave][u] && L.blk[wave][u] == L.blk[wave][lane]) lead = 0;
+      L.leader[wave][lane] = lead;
+      const bool in_order = L.valid[wave][lane] && L.blk[wave][lane] == L.blk[wave][0] && L.off[wave][lane] == lane;
+      const uint64_t all = __ballot(in_order);
+      if (lane == 0) L.full[wave] = (all & 0xFFFFull) == 0xFFFFull;
     }
     lds_barrier();
 
-    // ---- write the tile out ------------------------------------------------
-    if (full_page) {
-      // one page each: K as 68 and V as 50 coalesced 16-byte stores
-      uint8_t *kp = a.k_cache + ((int64_t)blk[0] * H + h) * kKPage;
-      uint8_t *vp = a.v_cache + ((int64_t)blk[0] * H + h) * kVPage;
-      if (tid < kKPage / 16) {
-        *reinterpret_cast<uint4 *>(kp + 16 * tid) = *reinterpret_cast<const uint4 *>(kst + 16 * tid);
-      } else if (tid < kKPage / 16 + 48) {
-        const int q = tid - kKPage / 16;
-        *reinterpret_cast<uint4 *>(vp + 16 * q) =
-            *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(vwords) + 16 * q);
-      } else if (tid < kKPage / 16 + 50) {
-        const int q = tid - kKPage / 16 - 48;
-        *reinterpret_cast<uint4 *>(vp + kVNorm + 16 * q) =
-            *reinterpret_cast<const uint4 *>(&vnorm[8 * q]);
-      }
-    } else {
-      // token by token: K records (3 planes + signs as 16-byte pieces, two
-      // halves), the V norm, and V bits merged into their pages atomically
-      if (tid < 4 * kEncTokens) {
-        const int n = tid >> 2, piece = tid & 3;
-        if (valid[n]) {
-          uint8_t *kp = a.k_cache + ((int64_t)blk[n] * H + h) * kKPage;
-          const int src = piece < 3 ? kKPlane * piece + 16 * n : kKSigns + 16 * n;
-          const int dst = piece < 3 ? kKPlane * piece + 16 * off[n] : kKSigns + 16 * off[n];
-          *reinterpret_cast<uint4 *>(kp + dst) = *reinterpret_cast<const uint4 *>(kst + src);
-        }
-      } else if (tid < 5 * kEncTokens) {
-        const int n = tid - 4 * kEncTokens;
-        if (valid[n]) {
-          uint8_t *kp = a.k_cache + ((int64_t)blk[n] * H + h) * kKPage;
-          uint8_t *vp = a.v_cache + ((int64_t)blk[n] * H + h) * kVPage;
-          *reinterpret_cast<uint16_t *>(kp + kKNorm + 2 * off[n]) =
-              *reinterpret_cast<const uint16_t *>(kst + kKNorm + 2 * n);
-          *reinterpret_cast<uint16_t *>(kp + kKGamma + 2 * off[n]) =
-              *reinterpret_cast<const uint16_t *>(kst + kKGamma + 2 * n);
-          *reinterpret_cast<uint16_t *>(vp + kVNorm + 2 * off[n]) = vnorm[n];
-        }
-      }
-      for (int w = tid; w < 3 * kHeadDim; w += 256) {
-        const int p = w / kHeadDim, i = w % kHeadDim;
-        const uint32_t word = vwords[p][i];
-        for (int j = 0; j < kEncTokens; ++j) {
-          if (!leader[j]) continue;
-          uint32_t mask = 0, bits = 0;
-          for (int u = j; u < kEncTokens; ++u) {
-            if (valid[u] && blk[u] == blk[j]) {
-              mask |= 1u << off[u];
-              bits |= ((word >> u) & 1u) << off[u];
-            }
+    // ---- QJL projection: rows 32w .. 32w+31 for the four tiles -------------
+    {
+      uint32_t sbits = 0u;
+      static_for<kTiles>([&](auto tc) {
+        constexpr int tl = decltype(tc)::value;
+        v4f z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const v8h ah = *reinterpret_cast<const v8h *>(&L.ehi[tl][l16][32 * k + 8 * lg]);
+          const v8h al = *reinterpret_cast<const v8h *>(&L.elo[tl][l16][32 * k + 8 * lg]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(v8h, shi[u][k]), z[u], 0, 0, 0);
+            z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(v8h, slo[u][k]), z[u], 0, 0, 0);
+            z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(v8h, shi[u][k]), z[u], 0, 0, 0);
           }
-          uint8_t *vp = a.v_cache + ((int64_t)blk[j] * H + h) * kVPage;
-          const uintptr_t addr = reinterpret_cast<uintptr_t>(vp + kKPlane * p + 2 * i);
-          uint32_t *w32 = reinterpret_cast<uint32_t *>(addr & ~uintptr_t(3));
-          const int sh = (addr & 2) ? 16 : 0;
-          const uint32_t set = bits << sh, clr = (mask & ~bits) << sh;
-          if (clr) atomicAnd(w32, ~clr);
-          if (set) atomicOr(w32, set);
+        }
+        // z[u][i] at lane l: token 4(l/16) + i, row 16(2w + u) + l%16
+        static_for<8>([&](auto uc) {
+          constexpr int u = decltype(uc)::value >> 2, i = decltype(uc)::value & 3;
+          put_mask<8 * tl + 4 * u + i>(sbits, __ballot(z[u][i] >= 0.0f));
+        });
+      });
+      // lane L = 2(8 tl + 4u + i) + hf: rows 16(2w+u)..+15 of tokens 4g + i, g = 2hf, 2hf+1
+      const int q = lane >> 1, hf = lane & 1, tl = q >> 3, u = (q >> 2) & 1, i = q & 3;
+      uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[tl] + kKSigns);
+      img[8 * (4 * (2 * hf) + i) + 2 * wave + u] = (uint16_t)sbits;
+      img[8 * (4 * (2 * hf + 1) + i) + 2 * wave + u] = (uint16_t)(sbits >> 16);
+    }
+    lds_barrier();
+
+    // ---- write the round out --------------------------------------------------
+#pragma unroll
+    for (int tl = 0; tl < kTiles; ++tl) {
+      if (!L.active[tl]) continue;  // uniform
+      const int64_t tt = R * kTiles + tl;
+      const int hh = (int)(tt % H);
+      if (L.full[tl]) {
+        const int b0 = L.blk[tl][0];
+        uint8_t *kp = a.k_cache + ((int64_t)b0 * H + hh) * kKPage;
+        uint8_t *vp = a.v_cache + ((int64_t)b0 * H + hh) * kVPage;
+        if (tid < kKPage / 16) {
+          *reinterpret_cast<uint4 *>(kp + 16 * tid) = *reinterpret_cast<const uint4 *>(L.kimg[tl] + 16 * tid);
+        } else if (tid < kKPage / 16 + kVPage / 16) {
+          const int q = tid - kKPage / 16;
+          *reinterpret_cast<uint4 *>(vp + 16 * q) = *reinterpret_cast<const uint4 *>(L.vimg[tl] + 16 * q);
+        }
+      } else {
+        // token by token: K records (3 planes + signs as 16-byte pieces), the
+        // scalars, and value bits merged into their pages atomically
+        if (tid < 4 * kTok) {
+          const int n = tid >> 2, piece = tid & 3;
+          if (L.valid[tl][n]) {
+            uint8_t *kp = a.k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
+            const int src = piece < 3 ? kKPlane * piece + 16 * n : kKSigns + 16 * n;
+            const int dst = piece < 3 ? kKPlane * piece + 16 * L.off[tl][n] : kKSigns + 16 * L.off[tl][n];
+            *reinterpret_cast<uint4 *>(kp + dst) = *reinterpret_cast<const uint4 *>(L.kimg[tl] + src);
+          }
+        } else if (tid < 5 * kTok) {
+          const int n = tid - 4 * kTok;
+          if (L.valid[tl][n]) {
+            uint8_t *kp = a.k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
+            uint8_t *vp = a.v_cache + ((int64_t)L.blk[tl][n] * H + hh) * kVPage;
+            const int o = L.off[tl][n];
+            *reinterpret_cast<uint16_t *>(kp + kKNorm + 2 * o) = *reinterpret_cast<const uint16_t *>(L.kimg[tl] + kKNorm + 2 * n);
+            *reinterpret_cast<uint16_t *>(kp + kKGamma + 2 * o) = *reinterpret_cast<const uint16_t *>(L.kimg[tl] + kKGamma + 2 * n);
+            *reinterpret_cast<uint16_t *>(vp + kVNorm + 2 * o) = *reinterpret_cast<const uint16_t *>(L.vimg[tl] + kVNorm + 2 * n);
+          }
+        }
+        for (int w = tid; w < 3 * kHeadDim; w += 256) {
+          const int p = w / kHeadDim, c = w % kHeadDim;
+          const uint32_t word = reinterpret_cast<const uint16_t *>(L.vimg[tl] + kKPlane * p)[c];
+          for (int j = 0; j < kTok; ++j) {
+            if (!L.leader[tl][j]) continue;
+            uint32_t mask = 0, bits = 0;
+            for (int u = j; u < kTok; ++u) {
+              if (L.valid[tl][u] && L.blk[tl][u] == L.blk[tl][j]) {
+                mask |= 1u << L.off[tl][u];
+                bits |= ((word >> u) & 1u) << L.off[tl][u];
+              }
+            }
+            uint8_t *vp = a.v_cache + ((int64_t)L.blk[tl][j] * H + hh) * kVPage;
+            const uintptr_t addr = reinterpret_cast<uintptr_t>(vp + kKPlane * p + 2 * c);
+            uint32_t *w32 = reinterpret_cast<uint32_t *>(addr & ~uintptr_t(3));
+            const int sh = (addr & 2) ? 16 : 0;
+            const uint32_t set = bits << sh, clr = (mask & ~bits) << sh;
+            if (clr) atomicAnd(w32, ~clr);
+            if (set) atomicOr(w32, set);
+          }
         }
       }
     }
-    lds_barrier();  // LDS tile state is rewritten by the next iteration
-    slot_cur = slot_next;
-    rk_cur = rk_next;
-    rv_cur = rv_next;
+    lds_barrier();  // the round's LDS state is rewritten by the next round
+    ik = nk;
+    iv = nv;
   }
+}
+
+template <int DT>
+hipError_t launch_dt(const EncodeArgs &a, int64_t tiles, hipStream_t stream) {
+  const int64_t rounds = (tiles + kTiles - 1) / kTiles;
+  const int64_t grid = rounds < 512 ? rounds : 512;  // persistent: two workgroups per CU
+  hipLaunchKernelGGL(encode_kernel<DT>, dim3((unsigned)grid), dim3(256), 0, stream, a, tiles);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream) {
-  const int64_t groups = (a.num_tokens + kEncTokens - 1) / kEncTokens;
+  const int64_t groups = (a.num_tokens + kTok - 1) / kTok;
   const int64_t tiles = groups * a.num_kv_heads;
-  const int64_t grid = tiles < 1024 ? tiles : 1024;  // persistent: ~4 workgroups per CU
-  hipLaunchKernelGGL(encode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, tiles);
-  return hipGetLastError();
+  switch (a.dtype) {
+    case TQ_BF16: return launch_dt<TQ_BF16>(a, tiles, stream);
+    case TQ_F16: return launch_dt<TQ_F16>(a, tiles, stream);
+    case TQ_F32: return launch_dt<TQ_F32>(a, tiles, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tq

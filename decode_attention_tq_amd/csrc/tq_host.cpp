@@ -197,6 +197,7 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
                            const float *qjl_host, void *d_tables, void *stream) {
   if (!cb) return fail(TQ_ERR_INVALID_ARGUMENT, "codebook is NULL");
   if (!d_tables) return fail(TQ_ERR_INVALID_ARGUMENT, "d_tables is NULL");
+  if ((uintptr_t)d_tables % 16 != 0) return fail(TQ_ERR_INVALID_ARGUMENT, "d_tables must be 16-byte aligned");
   if (!codebook_supported(head_dim, bits, tq::kQjlDim))
     return fail(TQ_ERR_UNSUPPORTED, "only head_dim=128, bits=3 are supported (got %d, %d)", head_dim, bits);
   tq_codebook c;
@@ -222,8 +223,12 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
   // S H (the projection applied to a residual that is still in the rotated
   // domain: S r = S H^T e = (S H) e, H symmetric), in double, then split into
   // a half "hi" part and a half "lo" part of the remainder for the matrix
-  // cores: hi + lo carries ~22 significant bits.
-  std::vector<uint16_t> halves(2 * (size_t)m * d);
+  // cores: hi + lo carries ~22 significant bits.  The halves are stored in
+  // the order the encoder's matrix operands take them, so that every lane
+  // reads whole 16-byte pieces: for wave w, row tile u, K step k, part
+  // (hi, lo) and lane l, eight halves j = 0..7 of row 16 (2w + u) + l % 16 at
+  // column 16 j + 4 k + l / 16.
+  std::vector<double> sh((size_t)m * d);
   const double inv_sqrt_d = 1.0 / std::sqrt((double)d);
   for (int i = 0; i < m; ++i) {
     for (int k = 0; k < d; ++k) {
@@ -232,12 +237,22 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
         const double hjk = (__builtin_popcount((unsigned)(j & k)) & 1) ? -inv_sqrt_d : inv_sqrt_d;
         acc += (double)host[(size_t)i * d + j] * hjk;
       }
-      const _Float16 hi = (_Float16)acc;
-      const _Float16 lo = (_Float16)(acc - (double)hi);
-      std::memcpy(&halves[(size_t)i * d + k], &hi, 2);
-      std::memcpy(&halves[(size_t)m * d + (size_t)i * d + k], &lo, 2);
+      sh[(size_t)i * d + k] = acc;
     }
   }
+  std::vector<uint16_t> halves(2 * (size_t)m * d);
+  size_t o = 0;
+  for (int w = 0; w < 4; ++w)
+    for (int u = 0; u < 2; ++u)
+      for (int k = 0; k < 4; ++k)
+        for (int part = 0; part < 2; ++part)
+          for (int l = 0; l < 64; ++l)
+            for (int j = 0; j < 8; ++j) {
+              const double v = sh[(size_t)(16 * (2 * w + u) + (l & 15)) * d + 16 * j + 4 * k + (l >> 4)];
+              const _Float16 hi = (_Float16)v;
+              const _Float16 h = part == 0 ? hi : (_Float16)(v - (double)hi);
+              std::memcpy(&halves[o++], &h, 2);
+            }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(d_tables, host.data(), host.size() * sizeof(float),
                                 hipMemcpyHostToDevice, s);
@@ -297,8 +312,7 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
   a.norms_out = norms_out;
   a.S = (const float *)cb->d_tables;
   a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
-  a.SHhi = (const uint16_t *)(a.St + (size_t)tq::kQjlDim * tq::kHeadDim);
-  a.SHlo = a.SHhi + (size_t)tq::kQjlDim * tq::kHeadDim;
+  a.SHop = (const uint16_t *)(a.St + (size_t)tq::kQjlDim * tq::kHeadDim);
   a.cb = device_codebook(cb);
   hipError_t e = tq::launch_encode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "encode launch");

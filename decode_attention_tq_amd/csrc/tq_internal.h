@@ -48,8 +48,7 @@ struct EncodeArgs {
   float *norms_out;
   const float *S;    // [m][d]
   const float *St;   // [d][m]
-  const uint16_t *SHhi;  // half bits of S H, [m][d]
-  const uint16_t *SHlo;  // half bits of S H - hi, [m][d]
+  const uint16_t *SHop;  // half bits of S H (hi, lo) in the encoder's operand order
   Codebook cb;
 };
 

@@ -83,8 +83,9 @@ typedef struct tq_codebook {
   float centroids[8];      /* ascending fp32 levels for N(0, 1/d) */
   float thresholds[7];     /* fp32 midpoints of adjacent levels */
   float qjl_scale;         /* sqrt(pi/2) / qjl_dim */
-  void *d_tables;          /* device: S [m][d] fp32, S^T [d][m] fp32, then S*H as two
-                              half arrays [m][d] (hi, and lo = S*H - hi) */
+  void *d_tables;          /* device, 16-byte aligned: S [m][d] fp32, S^T [d][m] fp32,
+                              then S*H as half pairs (hi, lo = S*H - hi) in an
+                              internal order (2*m*d halves) */
   uint32_t magic;          /* set by tq_codebook_init */
   uint32_t reserved;
 } tq_codebook;
@@ -111,13 +112,14 @@ tq_status tq_qjl_matrix(uint64_t seed, int rows, int cols, float *out);
 /* Bytes of the device table buffer for a codebook of this size. */
 size_t tq_codebook_device_bytes(int head_dim, int qjl_dim);
 
-/* Fill *cb (host struct) and upload [S | S^T | S*H hi | S*H lo] to d_tables on
+/* Fill *cb (host struct) and upload [S | S^T | S*H halves] to d_tables on
  * `stream`, then wait for `stream` (a one-time set-up call; it is the only
  * call that copies host data to the device or synchronises).
  * qjl_host: NULL -> S generated from qjl_seed by tq_qjl_matrix; else the
  * caller's S (qjl_dim x head_dim fp32 row-major host array).
  * Errors: TQ_ERR_UNSUPPORTED for head_dim/bits/qjl_dim other than 128/3/128,
- * TQ_ERR_INVALID_ARGUMENT for null cb/d_tables, TQ_ERR_HIP on copy failure. */
+ * TQ_ERR_INVALID_ARGUMENT for null cb/d_tables or d_tables not 16-byte
+ * aligned, TQ_ERR_HIP on copy failure. */
 tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl_seed,
                            const float *qjl_host, void *d_tables, void *stream);
 
