@@ -166,14 +166,87 @@ __device__ __forceinline__ void put_mask(uint32_t &v, uint64_t m) {
   writelane<2 * Q + 1>(v, (uint32_t)(m >> 32));
 }
 
-// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
+// The unrolled steps below are template functions of their step number with
+// scalar arguments by value (not closures): a closure holding references to
+// the levels turns a select between levels into an indexed load and keeps
+// everything it captures in scratch memory.
+
+// Value masks of register (m, i) = 4m + i of C = H X^T: lanes of coordinate
+// 16m + 4(l/16) + i, token l%16.
+template <int Q>
+__device__ __forceinline__ void value_step(const v4f (&vy)[8], float T0, float T1, float T2, uint32_t (&vb)[3]) {
+  constexpr int m = Q >> 2, i = Q & 3;
+  const float y = vy[m][i];
+  const uint64_t A1 = __ballot(fabsf(y) > T0), A2 = __ballot(fabsf(y) > T1);
+  const uint64_t A3 = __ballot(fabsf(y) > T2), P = __ballot(y > 0.0f);
+  put_mask<Q>(vb[0], ~(A1 ^ A2 ^ A3 ^ P));
+  put_mask<Q>(vb[1], ~(A2 ^ P));
+  put_mask<Q>(vb[2], P);
 }
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
+template <int... Q>
+__device__ __forceinline__ void value_steps(std::integer_sequence<int, Q...>, const v4f (&vy)[8], float T0, float T1,
+                                            float T2, uint32_t (&vb)[3]) {
+  (value_step<Q>(vy, T0, T1, T2, vb), ...);
+}
+
+// Key masks and residual of register (n, i) = 4n + i of C = X H: lanes of
+// token 4(l/16) + i, coordinate 16n + l%16.  e * 256 = y * 256 / |y_raw| -
+// sign * 256 * level, with thresholds T = t_k |y_raw| of the lane's token.
+template <int Q>
+__device__ __forceinline__ void key_step(const v4f (&ky)[8], const float (&T)[4][3], const float (&r256)[4], float c0,
+                                         float c1, float c2, float c3, uint32_t (&kb)[3], float (&es)[8][4],
+                                         float (&g2)[4]) {
+  constexpr int n = Q >> 2, i = Q & 3;
+  const float y = ky[n][i], ay = fabsf(y);
+  const bool a1 = ay > T[i][0], a2 = ay > T[i][1], a3 = ay > T[i][2], pp = y > 0.0f;
+  const uint64_t A1 = __ballot(a1), A2 = __ballot(a2), A3 = __ballot(a3), P = __ballot(pp);
+  put_mask<Q>(kb[0], ~(A1 ^ A2 ^ A3 ^ P));
+  put_mask<Q>(kb[1], ~(A2 ^ P));
+  put_mask<Q>(kb[2], P);
+  float lv = a1 ? c1 : c0;
+  lv = a2 ? c2 : lv;
+  lv = a3 ? c3 : lv;
+  const float e = fmaf(y, r256[i], pp ? -lv : lv);
+  es[n][i] = e;
+  g2[i] = fmaf(e, e, g2[i]);
+}
+template <int... Q>
+__device__ __forceinline__ void key_steps(std::integer_sequence<int, Q...>, const v4f (&ky)[8], const float (&T)[4][3],
+                                          const float (&r256)[4], float c0, float c1, float c2, float c3,
+                                          uint32_t (&kb)[3], float (&es)[8][4], float (&g2)[4]) {
+  (key_step<Q>(ky, T, r256, c0, c1, c2, c3, kb, es, g2), ...);
+}
+
+// Sign masks of register (u, i) = 4u + i of the projection of tile TL: lanes
+// of token 4(l/16) + i, row 16(2w + u) + l%16.
+template <int TL, int... Q>
+__device__ __forceinline__ void sign_masks(std::integer_sequence<int, Q...>, const v4f (&z)[2], uint32_t &sbits) {
+  (put_mask<8 * TL + Q>(sbits, __ballot(z[Q >> 2][Q & 3] >= 0.0f)), ...);
+}
+
+// Rows 32w .. 32w+31 of z = (S H) e for tile TL of the round: three f16
+// passes (e_hi S_hi + e_hi S_lo + e_lo S_hi) per K step, then its sign masks.
+template <int TL>
+__device__ __forceinline__ void qjl_tile(const RoundLds &L, int l16, int lg, const v8s (&shi)[2][4],
+                                         const v8s (&slo)[2][4], uint32_t &sbits) {
+  v4f z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const v8h ah = *reinterpret_cast<const v8h *>(&L.ehi[TL][l16][32 * k + 8 * lg]);
+    const v8h al = *reinterpret_cast<const v8h *>(&L.elo[TL][l16][32 * k + 8 * lg]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(v8h, shi[u][k]), z[u], 0, 0, 0);
+      z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(v8h, slo[u][k]), z[u], 0, 0, 0);
+      z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(v8h, shi[u][k]), z[u], 0, 0, 0);
+    }
+  }
+  sign_masks<TL>(std::make_integer_sequence<int, 8>{}, z, sbits);
+}
+template <int... TL>
+__device__ __forceinline__ void qjl_tiles(std::integer_sequence<int, TL...>, const RoundLds &L, int l16, int lg,
+                                          const v8s (&shi)[2][4], const v8s (&slo)[2][4], uint32_t &sbits) {
+  (qjl_tile<TL>(L, l16, lg, shi, slo, sbits), ...);
 }
 
 template <int DT>
@@ -183,7 +256,15 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: no exec masking around matrix ops
   const int l16 = lane & 15, lg = lane >> 4;
+  // Kernel arguments are copied to locals once: lambdas below must not
+  // capture the argument struct, or it is copied to scratch memory and read
+  // back through pointers.
   const int H = a.num_kv_heads;
+  const void *const kin = a.k, *const vin = a.v;
+  const int64_t ntok = a.num_tokens, tok_stride = a.tok_stride, head_stride = a.head_stride;
+  const int64_t *const slots = a.slots;
+  uint8_t *const k_cache = a.k_cache, *const v_cache = a.v_cache;
+  float *const norms_out = a.norms_out;
   const int64_t nrounds = (num_tiles + kTiles - 1) / kTiles;
 
   __shared__ __align__(16) RoundLds L;
@@ -196,27 +277,18 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
   float tpos[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) tpos[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.t[4 + k])));
-  auto level = [&](int k) {
-    return kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[4 + k])));
-  };
-  const float cp0 = level(0), cp1 = level(1), cp2 = level(2), cp3 = level(3);
+  const float cp0 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[4])));
+  const float cp1 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[5])));
+  const float cp2 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[6])));
+  const float cp3 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[7])));
 
   // This wave's QJL rows 32w .. 32w+31 of S H as the B operand of the f16
   // MFMA, K slots in the staged residual's order: slot s <-> coordinate
   // 16 (s & 7) + (s >> 3); lane l of step k holds slots 32k + 8(l/16) .. +7.
-  // The table stores exactly these registers, one 16-byte piece per lane.
-  v8s shi[2][4], slo[2][4];
-  {
-    const uint4 *op = reinterpret_cast<const uint4 *>(a.SHop);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int base = (((wave * 2 + u) * 4 + k) * 2) * 64 + lane;
-        shi[u][k] = __builtin_bit_cast(v8s, op[base]);
-        slo[u][k] = __builtin_bit_cast(v8s, op[base + 64]);
-      }
-  }
+  // The table stores exactly these registers, one 16-byte piece per lane; it
+  // stays in L2 and is read again each round right before the projection, so
+  // that its 64 registers are not held through the other phases.
+  const uint4 *const shop = reinterpret_cast<const uint4 *>(a.SHop) + wave * 2 * 4 * 2 * 64 + lane;
 
   auto tile_src = [&](int64_t tile, int64_t &t0, int &h) {
     h = (int)(tile % H);
@@ -229,10 +301,10 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
     int h = 0;
     tile_src(tile, t0, h);
     const int64_t t = t0 + l16;
-    const bool ok = tile < num_tiles && t < a.num_tokens;
-    const int64_t e0 = t * a.tok_stride + (int64_t)h * a.head_stride + 8 * lg;
-    load_in<PC>(ik, a.k, e0, ok);
-    load_in<PC>(iv, a.v, e0, ok);
+    const bool ok = tile < num_tiles && t < ntok;
+    const int64_t e0 = t * tok_stride + (int64_t)h * head_stride + 8 * lg;
+    load_in<PC>(ik, kin, e0, ok);
+    load_in<PC>(iv, vin, e0, ok);
   };
 
   In<PC> ik, iv;
@@ -248,16 +320,13 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
     // slots of the tile: lane t < 16 holds token t
     if (lane < kTok) {
       const int64_t t = t0 + lane;
-      const int64_t slot = (active && t < a.num_tokens) ? a.slots[t] : -1;
+      const int64_t slot = (active && t < ntok) ? slots[t] : -1;
       L.valid[wave][lane] = slot >= 0;
       L.blk[wave][lane] = slot >= 0 ? (int)(slot / kBlock) : -1;
       L.off[wave][lane] = slot >= 0 ? (int)(slot % kBlock) : 0;
     }
     if (lane == 0) L.active[wave] = active;
 
-    In<PC> nk, nv;
-    const int64_t Rn = R + gridDim.x;
-    if (Rn < nrounds) load_round(Rn, nk, nv);
 
     if (active) {
       // ---- values: C = H X^T, lane l reg i = coordinate 16m + 4(l/16) + i, token l%16
@@ -284,15 +353,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
 #pragma unroll
         for (int k = 0; k < 3; ++k) T[k] = tpos[k] * sn;
         uint32_t vb[3] = {0u, 0u, 0u};
-        static_for<32>([&](auto qc) {
-          constexpr int q = decltype(qc)::value, m = q >> 2, i = q & 3;
-          const float y = vy[m][i];
-          const uint64_t A1 = __ballot(fabsf(y) > T[0]), A2 = __ballot(fabsf(y) > T[1]);
-          const uint64_t A3 = __ballot(fabsf(y) > T[2]), P = __ballot(y > 0.0f);
-          put_mask<q>(vb[0], ~(A1 ^ A2 ^ A3 ^ P));
-          put_mask<q>(vb[1], ~(A2 ^ P));
-          put_mask<q>(vb[2], P);
-        });
+        value_steps(std::make_integer_sequence<int, 32>{}, vy, T[0], T[1], T[2], vb);
         // lane L = 2(4m + i) + hf holds the words of coordinates 16m + 4g + i, g = 2hf, 2hf+1
         {
           const int q = lane >> 1, hf = lane & 1, m = q >> 2, i = q & 3;
@@ -306,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         const float nv = sn * kInvSqrt128;
         if (lg == 0) {
           reinterpret_cast<_Float16 *>(L.vimg[wave] + kVNorm)[l16] = to_half_sat(nv);
-          if (a.norms_out && t0 + l16 < a.num_tokens) a.norms_out[((t0 + l16) * H + h) * 3 + 2] = nv;
+          if (norms_out && t0 + l16 < ntok) norms_out[((t0 + l16) * H + h) * 3 + 2] = nv;
         }
       }
       // ---- keys: C = X H, lane l reg i = token 4(l/16) + i, coordinate 16n + l%16
@@ -339,22 +400,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         uint32_t kb[3] = {0u, 0u, 0u};
         float g2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float es[8][4];
-        static_for<32>([&](auto qc) {
-          constexpr int q = decltype(qc)::value, n = q >> 2, i = q & 3;
-          const float y = ky[n][i], ay = fabsf(y);
-          const bool a1 = ay > T[i][0], a2 = ay > T[i][1], a3 = ay > T[i][2], pp = y > 0.0f;
-          const uint64_t A1 = __ballot(a1), A2 = __ballot(a2), A3 = __ballot(a3), P = __ballot(pp);
-          put_mask<q>(kb[0], ~(A1 ^ A2 ^ A3 ^ P));
-          put_mask<q>(kb[1], ~(A2 ^ P));
-          put_mask<q>(kb[2], P);
-          // e * 256 = y * 256 / |y_raw| - sign * 256 * level
-          float lv = a1 ? cp1 : cp0;
-          lv = a2 ? cp2 : lv;
-          lv = a3 ? cp3 : lv;
-          const float e = fmaf(y, r256[i], pp ? -lv : lv);
-          es[n][i] = e;
-          g2[i] = fmaf(e, e, g2[i]);
-        });
+        key_steps(std::make_integer_sequence<int, 32>{}, ky, T, r256, cp0, cp1, cp2, cp3, kb, es, g2);
         // lane L = 2(4n + i) + hf holds 16-bit pieces (coordinates 16n..+15) of tokens 4g + i, g = 2hf, 2hf+1
         {
           const int q = lane >> 1, hf = lane & 1, n = q >> 2, i = q & 3;
@@ -390,8 +436,8 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           if (l16 == 0) {
             reinterpret_cast<_Float16 *>(L.kimg[wave] + kKNorm)[tok] = to_half_sat(nk);
             reinterpret_cast<_Float16 *>(L.kimg[wave] + kKGamma)[tok] = to_half_sat(gam);
-            if (a.norms_out && t0 + tok < a.num_tokens) {
-              float *no = a.norms_out + ((t0 + tok) * H + h) * 3;
+            if (norms_out && t0 + tok < ntok) {
+              float *no = norms_out + ((t0 + tok) * H + h) * 3;
               no[0] = nk;
               no[1] = gam;
             }
@@ -399,6 +445,18 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         }
       }
     }
+    // the raw inputs are consumed: load the next round's while the
+    // projection and the stores of this one run
+    if (R + gridDim.x < nrounds) load_round(R + gridDim.x, ik, iv);
+    v8s shi[2][4], slo[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        shi[u][k] = __builtin_bit_cast(v8s, shop[((u * 4 + k) * 2) * 64]);
+        slo[u][k] = __builtin_bit_cast(v8s, shop[((u * 4 + k) * 2 + 1) * 64]);
+      }
+
     // leaders of destination blocks and the full-page test, per tile
     if (lane < kTok) {
       int lead = L.valid[wave][lane];
@@ -414,26 +472,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
     // ---- QJL projection: rows 32w .. 32w+31 for the four tiles -------------
     {
       uint32_t sbits = 0u;
-      static_for<kTiles>([&](auto tc) {
-        constexpr int tl = decltype(tc)::value;
-        v4f z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const v8h ah = *reinterpret_cast<const v8h *>(&L.ehi[tl][l16][32 * k + 8 * lg]);
-          const v8h al = *reinterpret_cast<const v8h *>(&L.elo[tl][l16][32 * k + 8 * lg]);
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(v8h, shi[u][k]), z[u], 0, 0, 0);
-            z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(v8h, slo[u][k]), z[u], 0, 0, 0);
-            z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, __builtin_bit_cast(v8h, shi[u][k]), z[u], 0, 0, 0);
-          }
-        }
-        // z[u][i] at lane l: token 4(l/16) + i, row 16(2w + u) + l%16
-        static_for<8>([&](auto uc) {
-          constexpr int u = decltype(uc)::value >> 2, i = decltype(uc)::value & 3;
-          put_mask<8 * tl + 4 * u + i>(sbits, __ballot(z[u][i] >= 0.0f));
-        });
-      });
+      qjl_tiles(std::make_integer_sequence<int, kTiles>{}, L, l16, lg, shi, slo, sbits);
       // lane L = 2(8 tl + 4u + i) + hf: rows 16(2w+u)..+15 of tokens 4g + i, g = 2hf, 2hf+1
       const int q = lane >> 1, hf = lane & 1, tl = q >> 3, u = (q >> 2) & 1, i = q & 3;
       uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[tl] + kKSigns);
@@ -450,8 +489,8 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
       const int hh = (int)(tt % H);
       if (L.full[tl]) {
         const int b0 = L.blk[tl][0];
-        uint8_t *kp = a.k_cache + ((int64_t)b0 * H + hh) * kKPage;
-        uint8_t *vp = a.v_cache + ((int64_t)b0 * H + hh) * kVPage;
+        uint8_t *kp = k_cache + ((int64_t)b0 * H + hh) * kKPage;
+        uint8_t *vp = v_cache + ((int64_t)b0 * H + hh) * kVPage;
         if (tid < kKPage / 16) {
           *reinterpret_cast<uint4 *>(kp + 16 * tid) = *reinterpret_cast<const uint4 *>(L.kimg[tl] + 16 * tid);
         } else if (tid < kKPage / 16 + kVPage / 16) {
@@ -464,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         if (tid < 4 * kTok) {
           const int n = tid >> 2, piece = tid & 3;
           if (L.valid[tl][n]) {
-            uint8_t *kp = a.k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
+            uint8_t *kp = k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
             const int src = piece < 3 ? kKPlane * piece + 16 * n : kKSigns + 16 * n;
             const int dst = piece < 3 ? kKPlane * piece + 16 * L.off[tl][n] : kKSigns + 16 * L.off[tl][n];
             *reinterpret_cast<uint4 *>(kp + dst) = *reinterpret_cast<const uint4 *>(L.kimg[tl] + src);
@@ -472,8 +511,8 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         } else if (tid < 5 * kTok) {
           const int n = tid - 4 * kTok;
           if (L.valid[tl][n]) {
-            uint8_t *kp = a.k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
-            uint8_t *vp = a.v_cache + ((int64_t)L.blk[tl][n] * H + hh) * kVPage;
+            uint8_t *kp = k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
+            uint8_t *vp = v_cache + ((int64_t)L.blk[tl][n] * H + hh) * kVPage;
             const int o = L.off[tl][n];
             *reinterpret_cast<uint16_t *>(kp + kKNorm + 2 * o) = *reinterpret_cast<const uint16_t *>(L.kimg[tl] + kKNorm + 2 * n);
             *reinterpret_cast<uint16_t *>(kp + kKGamma + 2 * o) = *reinterpret_cast<const uint16_t *>(L.kimg[tl] + kKGamma + 2 * n);
@@ -492,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
                 bits |= ((word >> u) & 1u) << L.off[tl][u];
               }
             }
-            uint8_t *vp = a.v_cache + ((int64_t)L.blk[tl][j] * H + hh) * kVPage;
+            uint8_t *vp = v_cache + ((int64_t)L.blk[tl][j] * H + hh) * kVPage;
             const uintptr_t addr = reinterpret_cast<uintptr_t>(vp + kKPlane * p + 2 * c);
             uint32_t *w32 = reinterpret_cast<uint32_t *>(addr & ~uintptr_t(3));
             const int sh = (addr & 2) ? 16 : 0;
@@ -504,8 +543,6 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
       }
     }
     lds_barrier();  // the round's LDS state is rewritten by the next round
-    ik = nk;
-    iv = nv;
   }
 }
 
