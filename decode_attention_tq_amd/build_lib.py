@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip"]
+SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip", "tq_prefill.hip"]
 
 
 def hipcc() -> str:

@@ -19,6 +19,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A context length above the planned maximum breaks the caller contract; it
+// is cut to what the block table row and the split plan cover, so that no
+// access leaves the block table or the partials.
+__device__ __forceinline__ int clamped_context(const DecodeArgs &a, int b) {
+  const int cap = min(a.max_blocks * kBlock, a.num_splits * a.split_tokens);
+  return min(max(a.context_lens[b], 0), cap);
+}
+
 __device__ __forceinline__ float load_as_float(const void *p, int dtype, int64_t i) {
   if (dtype == TQ_F32) return static_cast<const float *>(p)[i];
   if (dtype == TQ_F16) return (float)static_cast<const _Float16 *>(p)[i];

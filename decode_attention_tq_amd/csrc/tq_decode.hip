@@ -26,14 +26,6 @@ namespace {
 constexpr int kPartStride = 132;  // m (log2 units), l, pad, pad, acc[128]
 constexpr float kLog2e = 1.4426950408889634f;
 
-// A context length above the planned maximum breaks the caller contract; it
-// is cut to what the block table row and the split plan cover, so that no
-// access leaves the block table or the partials.
-__device__ __forceinline__ int clamped_context(const DecodeArgs &a, int b) {
-  const int cap = min(a.max_blocks * kBlock, a.num_splits * a.split_tokens);
-  return min(max(a.context_lens[b], 0), cap);
-}
-
 // LSE combine of the chunk partials of output row r by one wave, o' = acc'/l,
 // one inverse FWHT, store.  Lane l owns coordinates l and l + 64.  The chunk
 // accumulators are loaded 32 chunks at a time, the first batch issued before
@@ -830,6 +822,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     } else {
       return hipErrorInvalidValue;
     }
+  } else if (prefill_uses_mfma(a.q_len, a.group)) {
+    e = launch_prefill(a, stream);
+    if (e != hipSuccess) return e;
   } else {
     switch (a.group) {
       case 1: e = launch_split<1>(a, stream); break;

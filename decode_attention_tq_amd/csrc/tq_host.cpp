@@ -102,14 +102,20 @@ bool dtype_ok(int d) { return d == TQ_F32 || d == TQ_F16 || d == TQ_BF16; }
 // Chunks are multiples of 256 tokens (the workgroup's 4 waves x 64 tokens);
 // the automatic choice aims at about 1024 workgroups so that all 256 compute
 // units get several, and depends only on the call's sizes (no device query),
-// so the workspace size and the launch always agree.
-void plan_splits(int num_seqs, int q_len, int num_kv_heads, int max_ctx, int requested,
+// so the workspace size and the launch always agree.  Several queries per
+// sequence share a workgroup per block of query positions.
+void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested,
                  int *split_tokens, int *num_splits) {
   int st;
   if (requested > 0) {
     st = requested;
   } else {
-    const long rows = (long)num_seqs * q_len * num_kv_heads;
+    long per_seq = q_len;
+    if (tq::prefill_uses_mfma(q_len, group)) {
+      const int bq = tq::prefill_block_queries(group);
+      per_seq = (q_len + bq - 1) / bq;
+    }
+    const long rows = (long)num_seqs * per_seq * num_kv_heads;
     long want = (1024 + rows - 1) / rows;
     if (want < 1) want = 1;
     long per = (max_ctx + want - 1) / want;
@@ -326,7 +332,8 @@ size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
   if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0)
     return 0;
   int stok, ns;
-  plan_splits(num_seqs, q_len, num_kv_heads, max_context_len, tokens_per_split, &stok, &ns);
+  const int grp = num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
+  plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split, &stok, &ns);
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   size_t words = tq::decode_qprep_floats(rows) + tq::decode_partial_floats(rows, ns);
   if (num_q_heads % num_kv_heads == 0) {
@@ -371,7 +378,7 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
     return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
   if ((int64_t)num_seqs * q_len > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_seqs * q_len too large");
   int stok, ns;
-  plan_splits(num_seqs, q_len, num_kv_heads, max_context_len, tokens_per_split, &stok, &ns);
+  plan_splits(num_seqs, q_len, num_kv_heads, group, max_context_len, tokens_per_split, &stok, &ns);
   if (ns > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many splits (%d); raise tokens_per_split", ns);
   const size_t need = tq_decode_workspace_bytes(cb, num_seqs, q_len, num_q_heads, num_kv_heads,
                                                 max_context_len, tokens_per_split);

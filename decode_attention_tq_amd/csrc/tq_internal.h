@@ -85,12 +85,18 @@ struct DecodeArgs {
 size_t decode_qprep_floats(int64_t rows);
 size_t decode_partial_floats(int64_t rows, int num_splits);
 // The matrix-core split pass serves single-query decode with up to 8 query
-// heads per KV head; chunked prefill and larger groups use the vector pass.
+// heads per KV head; single-query decode with 16 uses the vector pass.
 bool decode_uses_mfma(int q_len, int group);
+// Several queries per sequence (chunked prefill, causal) run on the
+// matrix-core prefill pass: 64 query rows (64 / group positions) per
+// workgroup.
+bool prefill_uses_mfma(int q_len, int group);
+int prefill_block_queries(int group);
 int decode_qk_tiles(int group);
 size_t decode_qa_words(int64_t groups, int qk_tiles);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace tq

@@ -1,0 +1,367 @@
+// Chunked-prefill attention over the compressed paged cache on the matrix
+// cores (q_len > 1, causal): query t of a sequence of length L sees keys
+// 0 .. L - q_len + t.
+//
+// Scores and values follow the bit-plane pages (SwiftLM README,
+// "TurboQuantization: KV Cache Compression"; K keeps codes, QJL signs, norm
+// and residual length, V codes and norm):
+//   score(q, j) = scale * n_j * (<H q, c[idx_j]> + gamma_j <alpha S q, sigma_j>)
+//   o' = sum_j p_j n^V_j c[vidx_j]  (rotated domain, one inverse WHT in merge)
+//
+// A workgroup takes 64 query rows (64/G positions x G heads of one KV head)
+// and a chunk of keys, 32 keys (two pages) per step.  Each step the four
+// waves dequantize the two K pages into f16 tiles in LDS (levels hi + lo,
+// signs +-1) and the two V pages (levels hi + lo, transposed), then every
+// wave computes, for its 16 rows,
+//   S^T = K Q^T  on v_mfma_f32_16x16x32_f16: codes in three passes
+//        (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi), signs in two (sigma S_hi +
+//        sigma S_lo): hi + lo halves carry ~22 bits on both sides, which the
+//        logits of large-norm keys need;
+//   O^T += V^T W^T  with W = p n^V as the B operand straight from the score
+//        registers (lane l holds one query row, so no transpose is needed):
+//        two passes (V_hi, V_lo).
+// The running maximum is exact (W <= n^V fits f16); the partial record
+// (m in log2 units, l, acc[128]) goes to the merge pass, which applies the
+// inverse WHT.
+
+#include "tq_common.hpp"
+
+namespace tq {
+namespace {
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kPartStride = 132;  // m (log2 units), l, pad, pad, acc[128]
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kKeys = 32;         // keys per step (two pages)
+constexpr int kKRow = 136;        // halves per K tile row (128 + pad)
+constexpr int kVRow = 40;         // halves per V tile row (32 + pad)
+constexpr float kTabScale = 16.0f;  // levels are tabulated x16: their lo halves stay normal f16
+
+struct PrefillLds {
+  _Float16 kh[kKeys][kKRow];       // key levels x16, hi
+  _Float16 kl[kKeys][kKRow];       // lo
+  _Float16 ks[kKeys][kKRow];       // QJL signs +-1
+  _Float16 vh[kHeadDim][kVRow];    // value levels x16, hi, [coordinate][slot]
+  _Float16 vl[kHeadDim][kVRow];    // lo
+  float kn[kKeys];                 // n_k / 16
+  float kg[kKeys];                 // n_k gamma
+  float vn[kKeys];                 // n_v
+  uint8_t rawk[2][kKPage];         // the step's pages as stored
+  uint8_t rawv[2][kVPage];
+};
+
+// Four 3-bit codes (bytes of sel, 0..7) to four f16 values through byte
+// tables: t0/t1 hold the low bytes of entries 0..3 / 4..7, u0/u1 the high
+// bytes.  Returns f16 pairs (entries 0,1) and (2,3).
+__device__ __forceinline__ uint2 lut4(uint32_t sel, uint32_t t0, uint32_t t1, uint32_t u0, uint32_t u1) {
+  const uint32_t lo = __builtin_amdgcn_perm(t1, t0, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(u1, u0, sel);
+  return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+}
+
+// Bits 0..3 of x to the lowest bit of bytes 0..3.
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 0xFu) * 0x00204081u) & 0x01010101u; }
+
+// Code bytes of four coordinates (or tokens) from bit n, n+1, n+2, n+3 of
+// the three plane words: idx = b0 + 2 b1 + 4 b2.
+__device__ __forceinline__ uint32_t code_bytes(uint32_t p0, uint32_t p1, uint32_t p2, int n) {
+  return spread4(p0 >> n) | (spread4(p1 >> n) << 1) | (spread4(p2 >> n) << 2);
+}
+
+// Two f16 +-1 per bit pair of s starting at bit n: sigma = 2 bit - 1.
+__device__ __forceinline__ uint32_t sign_pair(uint32_t s, int n) {
+  const uint32_t b0 = (s >> n) & 1u, b1 = (s >> (n + 1)) & 1u;
+  return 0x3C003C00u | ((b0 ^ 1u) << 15) | ((b1 ^ 1u) << 31);
+}
+
+__device__ __forceinline__ float half_at(const uint8_t *p) {
+  return (float)*reinterpret_cast<const _Float16 *>(p);
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
+  constexpr int BQ = 64 / G;  // query positions per workgroup
+  const int qblocks = (a.q_len + BQ - 1) / BQ;
+  const int b = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
+  const int h = blockIdx.y, split = blockIdx.z;
+  const int L = clamped_context(a, b);
+  const int t0 = qb * BQ;
+  const int t_last = min(t0 + BQ, a.q_len) - 1;
+  const int s0 = split * a.split_tokens;
+  const int s1 = min(min(s0 + a.split_tokens, L), L - a.q_len + t_last + 1);
+  if (s0 >= s1) return;  // uniform: no key of the chunk is visible to the block
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  __shared__ __align__(16) PrefillLds S;
+
+  // this lane's query row (the column of S^T and O^T)
+  const int rw = 16 * wave + l16;
+  const int t = t0 + rw / G, hq = h * G + rw % G;
+  const bool row_ok = t < a.q_len;
+  const int64_t R = ((int64_t)b * a.q_len + min(t, a.q_len - 1)) * a.num_q_heads + hq;
+  const int lim = L - a.q_len + t;  // last visible key of the row
+
+  // B operands of S^T: chunk kc = 0..3 rotated query, 4..7 alpha S q, scaled
+  // by softmax scale x log2(e), as f16 hi and lo
+  v8h qh[8], ql[8];
+  {
+    const float cs = a.scale * kLog2e;
+    const float *src = a.qprep + R * 256;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const float4 x0 = *reinterpret_cast<const float4 *>(src + 32 * kc + 8 * g4);
+      const float4 x1 = *reinterpret_cast<const float4 *>(src + 32 * kc + 8 * g4 + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = row_ok ? cs * xs[j] : 0.0f;
+        const _Float16 hi = (_Float16)v;
+        qh[kc][j] = hi;
+        ql[kc][j] = (_Float16)(v - (float)hi);
+      }
+    }
+  }
+
+  // byte tables of the levels x16 (hi and lo halves), uniform
+  uint32_t th[4], tl[4];
+  {
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float c = kTabScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[k])));
+      const _Float16 hi = (_Float16)c;
+      const _Float16 lo = (_Float16)(c - (float)hi);
+      hb[k] = __builtin_bit_cast(uint16_t, hi);
+      lb[k] = __builtin_bit_cast(uint16_t, lo);
+    }
+    // th[0..1]: low bytes of hi entries 0..3 / 4..7, th[2..3]: high bytes
+    th[0] = (hb[0] & 0xFF) | (hb[1] & 0xFF) << 8 | (hb[2] & 0xFF) << 16 | (hb[3] & 0xFF) << 24;
+    th[1] = (hb[4] & 0xFF) | (hb[5] & 0xFF) << 8 | (hb[6] & 0xFF) << 16 | (hb[7] & 0xFF) << 24;
+    th[2] = (hb[0] >> 8) | (hb[1] >> 8) << 8 | (hb[2] >> 8) << 16 | (hb[3] >> 8) << 24;
+    th[3] = (hb[4] >> 8) | (hb[5] >> 8) << 8 | (hb[6] >> 8) << 16 | (hb[7] >> 8) << 24;
+    tl[0] = (lb[0] & 0xFF) | (lb[1] & 0xFF) << 8 | (lb[2] & 0xFF) << 16 | (lb[3] & 0xFF) << 24;
+    tl[1] = (lb[4] & 0xFF) | (lb[5] & 0xFF) << 8 | (lb[6] & 0xFF) << 16 | (lb[7] & 0xFF) << 24;
+    tl[2] = (lb[0] >> 8) | (lb[1] >> 8) << 8 | (lb[2] >> 8) << 16 | (lb[3] >> 8) << 24;
+    tl[3] = (lb[4] >> 8) | (lb[5] >> 8) << 8 | (lb[6] >> 8) << 16 | (lb[7] >> 8) << 24;
+  }
+
+  // arguments the lambdas below use, as locals (a captured argument struct
+  // would be copied to scratch memory)
+  const int32_t *const btab = a.block_tables + (int64_t)b * a.max_blocks;
+  const uint8_t *const k_cache = a.k_cache, *const v_cache = a.v_cache;
+  const int64_t hkv = a.num_kv_heads;
+  // 16-byte piece of the step's pages loaded by this thread: K pieces
+  // 0..135, V pieces 136..235
+  auto load_raw = [&](int k0) {
+    uint4 r = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < 2 * (kKPage / 16) + 2 * (kVPage / 16)) {
+      const bool isk = tid < 2 * (kKPage / 16);
+      const int q = isk ? tid : tid - 2 * (kKPage / 16);
+      const int per = isk ? kKPage / 16 : kVPage / 16;
+      const int pgi = q / per, off = 16 * (q % per);
+      // a page past the chunk's end re-reads the step's first page (its keys
+      // are masked)
+      const int pg = (k0 + 16 * pgi < s1) ? (k0 >> 4) + pgi : (k0 >> 4);
+      const int64_t blk = btab[pg];
+      const uint8_t *base = isk ? k_cache + (blk * hkv + h) * kKPage : v_cache + (blk * hkv + h) * kVPage;
+      r = *reinterpret_cast<const uint4 *>(base + off);
+    }
+    return r;
+  };
+  auto store_raw = [&](const uint4 &r) {
+    if (tid < 2 * (kKPage / 16) + 2 * (kVPage / 16)) {
+      const bool isk = tid < 2 * (kKPage / 16);
+      const int q = isk ? tid : tid - 2 * (kKPage / 16);
+      const int per = isk ? kKPage / 16 : kVPage / 16;
+      uint8_t *dst = isk ? &S.rawk[q / per][16 * (q % per)] : &S.rawv[q / per][16 * (q % per)];
+      *reinterpret_cast<uint4 *>(dst) = r;
+    }
+  };
+
+  v4f acc[8];
+#pragma unroll
+  for (int cv = 0; cv < 8; ++cv) acc[cv] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_part = 0.0f;
+
+  const int nsteps = (s1 - s0 + kKeys - 1) / kKeys;
+  uint4 raw = load_raw(s0);
+  for (int st = 0; st < nsteps; ++st) {
+    const int k0 = s0 + kKeys * st;
+    store_raw(raw);
+    lds_barrier();  // previous step's tiles are consumed; the pages are staged
+    if (st + 1 < nsteps) raw = load_raw(k0 + kKeys);
+
+    // ---- dequantize -------------------------------------------------------
+    {
+      // keys: thread (key, 16 coordinates)
+      const int key = tid >> 3, p8 = tid & 7, pg = key >> 4, tok = key & 15;
+      const uint8_t *pk = S.rawk[pg];
+      const uint32_t w0 = *reinterpret_cast<const uint16_t *>(pk + kKPlane * 0 + 16 * tok + 2 * p8);
+      const uint32_t w1 = *reinterpret_cast<const uint16_t *>(pk + kKPlane * 1 + 16 * tok + 2 * p8);
+      const uint32_t w2 = *reinterpret_cast<const uint16_t *>(pk + kKPlane * 2 + 16 * tok + 2 * p8);
+      const uint32_t ws = *reinterpret_cast<const uint16_t *>(pk + kKSigns + 16 * tok + 2 * p8);
+      uint32_t hv[8], lv[8], sv[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t sel = code_bytes(w0, w1, w2, 4 * q);
+        const uint2 hh = lut4(sel, th[0], th[1], th[2], th[3]);
+        const uint2 ll = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
+        hv[2 * q] = hh.x;
+        hv[2 * q + 1] = hh.y;
+        lv[2 * q] = ll.x;
+        lv[2 * q + 1] = ll.y;
+        sv[2 * q] = sign_pair(ws, 4 * q);
+        sv[2 * q + 1] = sign_pair(ws, 4 * q + 2);
+      }
+      uint4 *dh = reinterpret_cast<uint4 *>(&S.kh[key][16 * p8]);
+      uint4 *dl = reinterpret_cast<uint4 *>(&S.kl[key][16 * p8]);
+      uint4 *ds = reinterpret_cast<uint4 *>(&S.ks[key][16 * p8]);
+      dh[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      dh[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
+      dl[0] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+      dl[1] = make_uint4(lv[4], lv[5], lv[6], lv[7]);
+      ds[0] = make_uint4(sv[0], sv[1], sv[2], sv[3]);
+      ds[1] = make_uint4(sv[4], sv[5], sv[6], sv[7]);
+    }
+    {
+      // values: thread (coordinate, page); tokens 4g..4g+3 of page pg go to
+      // slots 8g + 4pg .. +3 (the B operand order of the weights)
+      const int c = tid >> 1, pg = tid & 1;
+      const uint8_t *pv = S.rawv[pg];
+      const uint32_t w0 = *reinterpret_cast<const uint16_t *>(pv + kKPlane * 0 + 2 * c);
+      const uint32_t w1 = *reinterpret_cast<const uint16_t *>(pv + kKPlane * 1 + 2 * c);
+      const uint32_t w2 = *reinterpret_cast<const uint16_t *>(pv + kKPlane * 2 + 2 * c);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t sel = code_bytes(w0, w1, w2, 4 * g);
+        *reinterpret_cast<uint2 *>(&S.vh[c][8 * g + 4 * pg]) = lut4(sel, th[0], th[1], th[2], th[3]);
+        *reinterpret_cast<uint2 *>(&S.vl[c][8 * g + 4 * pg]) = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
+      }
+    }
+    if (tid < kKeys) {
+      const int pg = tid >> 4, tok = tid & 15;
+      const float nk = half_at(&S.rawk[pg][kKNorm + 2 * tok]);
+      S.kn[tid] = nk * (1.0f / kTabScale);
+      S.kg[tid] = nk * half_at(&S.rawk[pg][kKGamma + 2 * tok]);
+      S.vn[tid] = half_at(&S.rawv[pg][kVNorm + 2 * tok]);
+    }
+    lds_barrier();
+
+    // ---- S^T = K Q^T for this wave's 16 rows: lane l, register i of tile ct
+    // holds key 16 ct + 4 (l / 16) + i of row l % 16
+    v4f cc[2], csg[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      v4f c = {0.0f, 0.0f, 0.0f, 0.0f}, s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const v8h ah = *reinterpret_cast<const v8h *>(&S.kh[16 * ct + l16][32 * kc + 8 * g4]);
+        const v8h al = *reinterpret_cast<const v8h *>(&S.kl[16 * ct + l16][32 * kc + 8 * g4]);
+        const v8h as = *reinterpret_cast<const v8h *>(&S.ks[16 * ct + l16][32 * kc + 8 * g4]);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[kc], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[kc], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[kc], c, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as, qh[4 + kc], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as, ql[4 + kc], s, 0, 0, 0);
+      }
+      cc[ct] = c;
+      csg[ct] = s;
+    }
+
+    // ---- online softmax (log2 units), exact running maximum --------------
+    float sc[2][4], vnk[2][4];
+    bool vis[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const float4 kn4 = *reinterpret_cast<const float4 *>(&S.kn[16 * ct + 4 * g4]);
+      const float4 kg4 = *reinterpret_cast<const float4 *>(&S.kg[16 * ct + 4 * g4]);
+      const float4 vn4 = *reinterpret_cast<const float4 *>(&S.vn[16 * ct + 4 * g4]);
+      const float knv[4] = {kn4.x, kn4.y, kn4.z, kn4.w}, kgv[4] = {kg4.x, kg4.y, kg4.z, kg4.w};
+      const float vnv[4] = {vn4.x, vn4.y, vn4.z, vn4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 16 * ct + 4 * g4 + i;
+        vis[ct][i] = key < s1 && key <= lim;
+        const float raw_s = fmaf(knv[i], cc[ct][i], kgv[i] * csg[ct][i]);
+        sc[ct][i] = vis[ct][i] ? raw_s : -INFINITY;
+        vnk[ct][i] = vnv[i];
+        tmax = fmaxf(tmax, sc[ct][i]);
+      }
+    }
+    tmax = fmaxf(tmax, xchg16(tmax, lane));
+    tmax = fmaxf(tmax, xchg32(tmax, lane));
+    const float m_new = fmaxf(m_run, tmax);
+    // m_run = -inf: nothing accumulated yet (acc and l are zero)
+    const float f = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+    m_run = m_new;
+    l_part *= f;
+#pragma unroll
+    for (int cv = 0; cv < 8; ++cv) acc[cv] *= f;
+    v8h wb;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = vis[ct][i] ? exp2f(sc[ct][i] - m_new) : 0.0f;
+        l_part += p;
+        // the norm of a masked key may hold any bits: its weight is selected to 0
+        wb[4 * ct + i] = (_Float16)(vis[ct][i] ? p * vnk[ct][i] : 0.0f);
+      }
+    }
+
+    // ---- O^T += V^T W^T: A = value levels [coordinate][slot] -------------
+#pragma unroll
+    for (int cv = 0; cv < 8; ++cv) {
+      const v8h vh = *reinterpret_cast<const v8h *>(&S.vh[16 * cv + l16][8 * g4]);
+      const v8h vl = *reinterpret_cast<const v8h *>(&S.vl[16 * cv + l16][8 * g4]);
+      acc[cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, wb, acc[cv], 0, 0, 0);
+      acc[cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, wb, acc[cv], 0, 0, 0);
+    }
+  }
+
+  // ---- partial record of the row: lanes of one row hold 4 key groups ----
+  float l_row = l_part + xchg16(l_part, lane);
+  l_row += xchg32(l_row, lane);
+  if (row_ok) {
+    float *part = a.partials + (R * a.num_splits + split) * kPartStride;
+    if (g4 == 0) {
+      part[0] = m_run;
+      part[1] = l_row;
+    }
+#pragma unroll
+    for (int cv = 0; cv < 8; ++cv) {
+      const float4 o = make_float4(acc[cv][0], acc[cv][1], acc[cv][2], acc[cv][3]) * (1.0f / kTabScale);
+      *reinterpret_cast<float4 *>(part + 4 + 16 * cv + 4 * g4) = o;
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_uses_mfma(int q_len, int group) {
+  return q_len > 1 && (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+int prefill_block_queries(int group) { return 64 / group; }
+
+hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
+  const int bq = 64 / a.group;
+  const int qblocks = (a.q_len + bq - 1) / bq;
+  dim3 grid((unsigned)(a.num_seqs * qblocks), (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
+  switch (a.group) {
+    case 1: hipLaunchKernelGGL(prefill_mfma_kernel<1>, grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(prefill_mfma_kernel<2>, grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(prefill_mfma_kernel<4>, grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(prefill_mfma_kernel<8>, grid, dim3(256), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(prefill_mfma_kernel<16>, grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tq

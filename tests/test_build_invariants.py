@@ -218,7 +218,7 @@ def test_checker_follows_copied_exec_saves():
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src", ["tq_encode.hip", "tq_decode.hip"])
+@pytest.mark.parametrize("src", ["tq_encode.hip", "tq_decode.hip", "tq_prefill.hip"])
 def test_no_matrix_op_under_partial_exec(src, tmp_path):
     out = tmp_path / (src + ".s")
     r = subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", str(out)],
