@@ -88,7 +88,7 @@ size_t decode_partial_floats(int64_t rows, int num_splits);
 // heads per KV head; single-query decode with 16 uses the vector pass.
 bool decode_uses_mfma(int q_len, int group);
 // Several queries per sequence (chunked prefill, causal) run on the
-// matrix-core prefill pass: 64 query rows (64 / group positions) per
+// matrix-core prefill pass: 128 query rows (128 / group positions) per
 // workgroup.
 bool prefill_uses_mfma(int q_len, int group);
 int prefill_block_queries(int group);

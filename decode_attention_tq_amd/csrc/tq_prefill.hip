@@ -8,11 +8,11 @@
 //   score(q, j) = scale * n_j * (<H q, c[idx_j]> + gamma_j <alpha S q, sigma_j>)
 //   o' = sum_j p_j n^V_j c[vidx_j]  (rotated domain, one inverse WHT in merge)
 //
-// A workgroup takes 64 query rows (64/G positions x G heads of one KV head)
-// and a chunk of keys, 32 keys (two pages) per step.  Each step the four
-// waves dequantize the two K pages into f16 tiles in LDS (levels hi + lo,
-// signs +-1) and the two V pages (levels hi + lo, transposed), then every
-// wave computes, for its 16 rows,
+// A workgroup of eight waves takes 128 query rows (128/G positions x G heads
+// of one KV head) and a chunk of keys, 32 keys (two pages) per step.  Each
+// step the waves dequantize the two K pages into f16 tiles in LDS (levels
+// hi + lo, signs +-1) and the two V pages (levels hi + lo, transposed), then
+// every wave computes, for its 16 rows,
 //   S^T = K Q^T  on v_mfma_f32_16x16x32_f16: codes in three passes
 //        (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi), signs in two (sigma S_hi +
 //        sigma S_lo): hi + lo halves carry ~22 bits on both sides, which the
@@ -39,7 +39,8 @@ constexpr int kKRow = 136;        // halves per K tile row (128 + pad)
 constexpr int kVRow = 40;         // halves per V tile row (32 + pad)
 constexpr float kTabScale = 16.0f;  // levels are tabulated x16: their lo halves stay normal f16
 
-struct PrefillLds {
+// One step's dequantized tiles.
+struct Tile {
   _Float16 kh[kKeys][kKRow];       // key levels x16, hi
   _Float16 kl[kKeys][kKRow];       // lo
   _Float16 ks[kKeys][kKRow];       // QJL signs +-1
@@ -48,8 +49,15 @@ struct PrefillLds {
   float kn[kKeys];                 // n_k / 16
   float kg[kKeys];                 // n_k gamma
   float vn[kKeys];                 // n_v
-  uint8_t rawk[2][kKPage];         // the step's pages as stored
-  uint8_t rawv[2][kVPage];
+};
+
+// Two steps in flight: the tiles of step i are read while those of step
+// i + 1 are written, and the stored pages of step i + 1 are staged while
+// those of step i are still being dequantized.
+struct PrefillLds {
+  Tile d[2];
+  uint8_t rawk[2][2][kKPage];      // [buffer][page] as stored
+  uint8_t rawv[2][2][kVPage];
 };
 
 // Four 3-bit codes (bytes of sel, 0..7) to four f16 values through byte
@@ -80,9 +88,66 @@ __device__ __forceinline__ float half_at(const uint8_t *p) {
   return (float)*reinterpret_cast<const _Float16 *>(p);
 }
 
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 16 * kWaves;  // query rows per workgroup
+
+// Dequantize a step's staged pages into T (all threads of the workgroup).
+// Keys: thread (key, 8 coordinates); values: thread (coordinate, page, half
+// of the page's tokens), tokens 4g..4g+3 of page pg going to slots
+// 8g + 4pg .. +3 (the B operand order of the weights).
+__device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage], const uint8_t (*rawv)[kVPage],
+                                           int tid, const uint32_t (&th)[4], const uint32_t (&tl)[4]) {
+  {
+    const int key = tid >> 4, p16 = tid & 15, pg = key >> 4, tok = key & 15;
+    const uint8_t *pk = rawk[pg];
+    const uint32_t w0 = pk[kKPlane * 0 + 16 * tok + p16];
+    const uint32_t w1 = pk[kKPlane * 1 + 16 * tok + p16];
+    const uint32_t w2 = pk[kKPlane * 2 + 16 * tok + p16];
+    const uint32_t ws = pk[kKSigns + 16 * tok + p16];
+    uint32_t hv[4], lv[4], sv[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t sel = code_bytes(w0, w1, w2, 4 * q);
+      const uint2 hh = lut4(sel, th[0], th[1], th[2], th[3]);
+      const uint2 ll = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
+      hv[2 * q] = hh.x;
+      hv[2 * q + 1] = hh.y;
+      lv[2 * q] = ll.x;
+      lv[2 * q + 1] = ll.y;
+      sv[2 * q] = sign_pair(ws, 4 * q);
+      sv[2 * q + 1] = sign_pair(ws, 4 * q + 2);
+    }
+    *reinterpret_cast<uint4 *>(&T.kh[key][8 * p16]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    *reinterpret_cast<uint4 *>(&T.kl[key][8 * p16]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+    *reinterpret_cast<uint4 *>(&T.ks[key][8 * p16]) = make_uint4(sv[0], sv[1], sv[2], sv[3]);
+  }
+  {
+    const int c = tid >> 2, pg = (tid >> 1) & 1, th8 = tid & 1;
+    const uint8_t *pv = rawv[pg];
+    const uint32_t w0 = pv[kKPlane * 0 + 2 * c + th8];
+    const uint32_t w1 = pv[kKPlane * 1 + 2 * c + th8];
+    const uint32_t w2 = pv[kKPlane * 2 + 2 * c + th8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int g = 2 * th8 + q;
+      const uint32_t sel = code_bytes(w0, w1, w2, 4 * q);
+      *reinterpret_cast<uint2 *>(&T.vh[c][8 * g + 4 * pg]) = lut4(sel, th[0], th[1], th[2], th[3]);
+      *reinterpret_cast<uint2 *>(&T.vl[c][8 * g + 4 * pg]) = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
+    }
+  }
+  if (tid < kKeys) {
+    const int pg = tid >> 4, tok = tid & 15;
+    const float nk = half_at(&rawk[pg][kKNorm + 2 * tok]);
+    T.kn[tid] = nk * (1.0f / kTabScale);
+    T.kg[tid] = nk * half_at(&rawk[pg][kKGamma + 2 * tok]);
+    T.vn[tid] = half_at(&rawv[pg][kVNorm + 2 * tok]);
+  }
+}
+
 template <int G>
-__global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
-  constexpr int BQ = 64 / G;  // query positions per workgroup
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a) {
+  constexpr int BQ = kRows / G;  // query positions per workgroup
   const int qblocks = (a.q_len + BQ - 1) / BQ;
   const int b = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
   const int h = blockIdx.y, split = blockIdx.z;
@@ -157,6 +222,7 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
   // 16-byte piece of the step's pages loaded by this thread: K pieces
   // 0..135, V pieces 136..235
   auto load_raw = [&](int k0) {
+    k0 = k0 < s1 ? k0 : s0;  // a step past the chunk re-reads the first one (never used)
     uint4 r = make_uint4(0u, 0u, 0u, 0u);
     if (tid < 2 * (kKPage / 16) + 2 * (kVPage / 16)) {
       const bool isk = tid < 2 * (kKPage / 16);
@@ -172,12 +238,12 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
     }
     return r;
   };
-  auto store_raw = [&](const uint4 &r) {
+  auto store_raw = [&](const uint4 &r, int buf) {
     if (tid < 2 * (kKPage / 16) + 2 * (kVPage / 16)) {
       const bool isk = tid < 2 * (kKPage / 16);
       const int q = isk ? tid : tid - 2 * (kKPage / 16);
       const int per = isk ? kKPage / 16 : kVPage / 16;
-      uint8_t *dst = isk ? &S.rawk[q / per][16 * (q % per)] : &S.rawv[q / per][16 * (q % per)];
+      uint8_t *dst = isk ? &S.rawk[buf][q / per][16 * (q % per)] : &S.rawv[buf][q / per][16 * (q % per)];
       *reinterpret_cast<uint4 *>(dst) = r;
     }
   };
@@ -189,67 +255,21 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
 
   const int nsteps = (s1 - s0 + kKeys - 1) / kKeys;
   uint4 raw = load_raw(s0);
+  store_raw(raw, 0);
+  lds_barrier();
+  raw = load_raw(s0 + kKeys);
+  dequantize(S.d[0], S.rawk[0], S.rawv[0], tid, th, tl);
   for (int st = 0; st < nsteps; ++st) {
     const int k0 = s0 + kKeys * st;
-    store_raw(raw);
-    lds_barrier();  // previous step's tiles are consumed; the pages are staged
-    if (st + 1 < nsteps) raw = load_raw(k0 + kKeys);
-
-    // ---- dequantize -------------------------------------------------------
-    {
-      // keys: thread (key, 16 coordinates)
-      const int key = tid >> 3, p8 = tid & 7, pg = key >> 4, tok = key & 15;
-      const uint8_t *pk = S.rawk[pg];
-      const uint32_t w0 = *reinterpret_cast<const uint16_t *>(pk + kKPlane * 0 + 16 * tok + 2 * p8);
-      const uint32_t w1 = *reinterpret_cast<const uint16_t *>(pk + kKPlane * 1 + 16 * tok + 2 * p8);
-      const uint32_t w2 = *reinterpret_cast<const uint16_t *>(pk + kKPlane * 2 + 16 * tok + 2 * p8);
-      const uint32_t ws = *reinterpret_cast<const uint16_t *>(pk + kKSigns + 16 * tok + 2 * p8);
-      uint32_t hv[8], lv[8], sv[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t sel = code_bytes(w0, w1, w2, 4 * q);
-        const uint2 hh = lut4(sel, th[0], th[1], th[2], th[3]);
-        const uint2 ll = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
-        hv[2 * q] = hh.x;
-        hv[2 * q + 1] = hh.y;
-        lv[2 * q] = ll.x;
-        lv[2 * q + 1] = ll.y;
-        sv[2 * q] = sign_pair(ws, 4 * q);
-        sv[2 * q + 1] = sign_pair(ws, 4 * q + 2);
-      }
-      uint4 *dh = reinterpret_cast<uint4 *>(&S.kh[key][16 * p8]);
-      uint4 *dl = reinterpret_cast<uint4 *>(&S.kl[key][16 * p8]);
-      uint4 *ds = reinterpret_cast<uint4 *>(&S.ks[key][16 * p8]);
-      dh[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-      dh[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
-      dl[0] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
-      dl[1] = make_uint4(lv[4], lv[5], lv[6], lv[7]);
-      ds[0] = make_uint4(sv[0], sv[1], sv[2], sv[3]);
-      ds[1] = make_uint4(sv[4], sv[5], sv[6], sv[7]);
-    }
-    {
-      // values: thread (coordinate, page); tokens 4g..4g+3 of page pg go to
-      // slots 8g + 4pg .. +3 (the B operand order of the weights)
-      const int c = tid >> 1, pg = tid & 1;
-      const uint8_t *pv = S.rawv[pg];
-      const uint32_t w0 = *reinterpret_cast<const uint16_t *>(pv + kKPlane * 0 + 2 * c);
-      const uint32_t w1 = *reinterpret_cast<const uint16_t *>(pv + kKPlane * 1 + 2 * c);
-      const uint32_t w2 = *reinterpret_cast<const uint16_t *>(pv + kKPlane * 2 + 2 * c);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t sel = code_bytes(w0, w1, w2, 4 * g);
-        *reinterpret_cast<uint2 *>(&S.vh[c][8 * g + 4 * pg]) = lut4(sel, th[0], th[1], th[2], th[3]);
-        *reinterpret_cast<uint2 *>(&S.vl[c][8 * g + 4 * pg]) = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
-      }
-    }
-    if (tid < kKeys) {
-      const int pg = tid >> 4, tok = tid & 15;
-      const float nk = half_at(&S.rawk[pg][kKNorm + 2 * tok]);
-      S.kn[tid] = nk * (1.0f / kTabScale);
-      S.kg[tid] = nk * half_at(&S.rawk[pg][kKGamma + 2 * tok]);
-      S.vn[tid] = half_at(&S.rawv[pg][kVNorm + 2 * tok]);
-    }
+    const Tile &T = S.d[st & 1];
+    store_raw(raw, (st + 1) & 1);
+    // step st's tiles are complete, step st - 1's are consumed, and the
+    // pages of step st + 1 are staged
     lds_barrier();
+    raw = load_raw(k0 + 2 * kKeys);
+    // tiles of step st + 1 (past the last step: unused), written while this
+    // step's are read, so that vector and matrix work can interleave
+    dequantize(S.d[(st + 1) & 1], S.rawk[(st + 1) & 1], S.rawv[(st + 1) & 1], tid, th, tl);
 
     // ---- S^T = K Q^T for this wave's 16 rows: lane l, register i of tile ct
     // holds key 16 ct + 4 (l / 16) + i of row l % 16
@@ -259,9 +279,9 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
       v4f c = {0.0f, 0.0f, 0.0f, 0.0f}, s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const v8h ah = *reinterpret_cast<const v8h *>(&S.kh[16 * ct + l16][32 * kc + 8 * g4]);
-        const v8h al = *reinterpret_cast<const v8h *>(&S.kl[16 * ct + l16][32 * kc + 8 * g4]);
-        const v8h as = *reinterpret_cast<const v8h *>(&S.ks[16 * ct + l16][32 * kc + 8 * g4]);
+        const v8h ah = *reinterpret_cast<const v8h *>(&T.kh[16 * ct + l16][32 * kc + 8 * g4]);
+        const v8h al = *reinterpret_cast<const v8h *>(&T.kl[16 * ct + l16][32 * kc + 8 * g4]);
+        const v8h as = *reinterpret_cast<const v8h *>(&T.ks[16 * ct + l16][32 * kc + 8 * g4]);
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[kc], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[kc], c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[kc], c, 0, 0, 0);
@@ -278,9 +298,9 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const float4 kn4 = *reinterpret_cast<const float4 *>(&S.kn[16 * ct + 4 * g4]);
-      const float4 kg4 = *reinterpret_cast<const float4 *>(&S.kg[16 * ct + 4 * g4]);
-      const float4 vn4 = *reinterpret_cast<const float4 *>(&S.vn[16 * ct + 4 * g4]);
+      const float4 kn4 = *reinterpret_cast<const float4 *>(&T.kn[16 * ct + 4 * g4]);
+      const float4 kg4 = *reinterpret_cast<const float4 *>(&T.kg[16 * ct + 4 * g4]);
+      const float4 vn4 = *reinterpret_cast<const float4 *>(&T.vn[16 * ct + 4 * g4]);
       const float knv[4] = {kn4.x, kn4.y, kn4.z, kn4.w}, kgv[4] = {kg4.x, kg4.y, kg4.z, kg4.w};
       const float vnv[4] = {vn4.x, vn4.y, vn4.z, vn4.w};
 #pragma unroll
@@ -297,17 +317,19 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
     tmax = fmaxf(tmax, xchg32(tmax, lane));
     const float m_new = fmaxf(m_run, tmax);
     // m_run = -inf: nothing accumulated yet (acc and l are zero)
-    const float f = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+    const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    l_part *= f;
+    if (__ballot(f != 1.0f)) {  // wave-uniform: the maximum moved in some row
+      l_part *= f;
 #pragma unroll
-    for (int cv = 0; cv < 8; ++cv) acc[cv] *= f;
+      for (int cv = 0; cv < 8; ++cv) acc[cv] *= f;
+    }
     v8h wb;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = vis[ct][i] ? exp2f(sc[ct][i] - m_new) : 0.0f;
+        const float p = vis[ct][i] ? __builtin_amdgcn_exp2f(sc[ct][i] - m_new) : 0.0f;
         l_part += p;
         // the norm of a masked key may hold any bits: its weight is selected to 0
         wb[4 * ct + i] = (_Float16)(vis[ct][i] ? p * vnk[ct][i] : 0.0f);
@@ -317,8 +339,8 @@ __global__ __launch_bounds__(256, 3) void prefill_mfma_kernel(DecodeArgs a) {
     // ---- O^T += V^T W^T: A = value levels [coordinate][slot] -------------
 #pragma unroll
     for (int cv = 0; cv < 8; ++cv) {
-      const v8h vh = *reinterpret_cast<const v8h *>(&S.vh[16 * cv + l16][8 * g4]);
-      const v8h vl = *reinterpret_cast<const v8h *>(&S.vl[16 * cv + l16][8 * g4]);
+      const v8h vh = *reinterpret_cast<const v8h *>(&T.vh[16 * cv + l16][8 * g4]);
+      const v8h vl = *reinterpret_cast<const v8h *>(&T.vl[16 * cv + l16][8 * g4]);
       acc[cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, wb, acc[cv], 0, 0, 0);
       acc[cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, wb, acc[cv], 0, 0, 0);
     }
@@ -347,18 +369,18 @@ bool prefill_uses_mfma(int q_len, int group) {
   return q_len > 1 && (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
 }
 
-int prefill_block_queries(int group) { return 64 / group; }
+int prefill_block_queries(int group) { return kRows / group; }
 
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
-  const int bq = 64 / a.group;
+  const int bq = kRows / a.group;
   const int qblocks = (a.q_len + bq - 1) / bq;
   dim3 grid((unsigned)(a.num_seqs * qblocks), (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL(prefill_mfma_kernel<1>, grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(prefill_mfma_kernel<2>, grid, dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(prefill_mfma_kernel<4>, grid, dim3(256), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(prefill_mfma_kernel<8>, grid, dim3(256), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(prefill_mfma_kernel<16>, grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(prefill_mfma_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(prefill_mfma_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(prefill_mfma_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(prefill_mfma_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(prefill_mfma_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

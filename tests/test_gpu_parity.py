@@ -252,3 +252,31 @@ def test_running_maximum_moves_along_the_sequence():
     err = check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"],
                        case["context_lens"], scale=0.25)
     print("max rel err", err.max())
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 4), (32, 2)])
+def test_prefill_groups_batches_and_splits(Hq, Hkv):
+    """Several queries per sequence for every supported group size (1, 2, 8,
+    16 query heads per KV head): two sequences of different lengths, a query
+    count that leaves a partial block of positions, and chunks of 256 keys
+    that cut through the causal boundary."""
+    rng = np.random.default_rng(11 + Hq // Hkv)
+    lens = np.array([200, 517], dtype=np.int64)
+    q_len = 21
+    table, nb = synth.block_tables(rng, lens)
+    cb = codebook()
+    kpool, vpool = new_pools(nb, Hkv)
+    for b in range(len(lens)):
+        k = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        v = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        encode_gpu(cb, k, v, synth.slots_for(table, b, np.arange(lens[b])), kpool, vpool, with_norms=False)
+    q = synth.queries(rng, len(lens), q_len, Hq)
+    kp, vp = _np(kpool), _np(vpool)
+    cl = lens.astype(np.int32)
+    outs = []
+    for tps in (0, 256):
+        out = decode_gpu(cb, q, kpool, vpool, table, cl, Hkv, tokens_per_split=tps)
+        check_decode(out, q, kp, vp, table, cl)
+        outs.append(out)
+    # a different chunking changes only the rounding of the combine
+    assert np.abs(outs[0] - outs[1]).max() <= 1e-4 * max(1.0, np.abs(outs[0]).max())
