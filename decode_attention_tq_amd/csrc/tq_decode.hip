@@ -89,17 +89,13 @@ __device__ void merge_row(const DecodeArgs &a, int64_t r, int lane) {
 // rows of the score contraction's A operands (see split_mfma_kernel): rows
 // (head, digit r).  With 2^E bounding |x| over the head, Y = rint(x 2^(19-E))
 // is written in balanced base 32, Y = d0 2^15 + d1 2^10 + d2 2^5 + d3 with
-// every |d_r| <= 16 (exact in e4m3), and row r carries d_r with scale
-// 2^(E-4-5r): x to 2^-20 of the head's largest magnitude.  Logits of keys
-// with large norms need these 19 bits; 16 (base-16 digits) leave errors near
-// 1e-3 in peaked rows.
+// every |d_r| <= 16, stored as the fp6 e2m3 code of d_r/8 (exact), and row r
+// carries it with scale 2^(E-4-5r+3): x to 2^-20 of the head's largest
+// magnitude.  Logits of keys with large norms need these 19 bits; 16
+// (base-16 digits) leave errors near 1e-3 in peaked rows.
 __device__ __forceinline__ int bound_exponent(float M) {  // M < 2^E for finite M > 0
   const int ex = (int)((__float_as_uint(M) >> 23) & 0xFFu);
   return ex == 0 ? -126 : ex - 126;
-}
-
-__device__ __forceinline__ uint32_t fp8_digit(float d) {  // exact for d = k 2^e, |k| <= 16
-  return __builtin_amdgcn_cvt_pk_fp8_f32(d, 0.0f, 0, false) & 0xFFu;
 }
 
 // Digit r (0..3) of x in balanced base 32 under bound 2^E: with
@@ -172,23 +168,29 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   const int nwords = NT * 5 * 64 * 8;
   const int nt = g >> 2, gp = g & 3;
   uint32_t *qa = a.qa + grp * (int64_t)(NT * (5 * 64 * 9 + 32));
-  // this head's rows: lanes 16*ga + 4*gp + r of tile nt.  The digit of a K
-  // slot is scaled by the factor that goes with the b_split operands.
-  for (int widx = tid; widx < 5 * 16 * 8; widx += 256) {
-    const int j = widx & 7, li = (widx >> 3) & 15, p = widx >> 7;
+  // this head's rows: lanes 16*ga + 4*gp + r of tile nt, as fp6 codes (K
+  // slot 32 ga + s at code s).  The digit of a K slot is scaled by the
+  // factor that goes with the b_split operands.
+  if (tid < 5 * 16) {
+    const int li = tid & 15, p = tid >> 4;
     const int ga = li >> 2, r = li & 3, ln = 16 * ga + 4 * gp + r;
     const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-    uint32_t word = 0;
+    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     if (p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4]) {
       const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int kap = mfma_a_slot_k(ga, 4 * j + bb);
+      for (int s = 0; s < 32; ++s) {
+        const int kap = 32 * ga + s;
         const float x = p < 4 ? -bp * qp[b_coord(kap)] : -qp[128 + b_coord(kap)];
-        word |= fp8_digit(query_digit(x, E, r) * b_split_factor(kap)) << (8 * bb);
+        const uint32_t code = fp6_code(query_digit(x, E, r) * b_split_factor(kap));
+        const int bit = 6 * s;
+        w[bit >> 5] |= code << (bit & 31);
+        if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
       }
     }
-    qa[((nt * 5 + p) * 64 + ln) * 8 + j] = word;
+    uint4 *dst = reinterpret_cast<uint4 *>(qa + ((nt * 5 + p) * 64 + ln) * 8);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], 0u, 0u);
   }
   // accumulator start values: per row (digit r) the weighted sum of the
   // unscaled A values (b_split_weight), for the code planes (summed over
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
     const int r = li & 3, ln = 16 * (li >> 2) + 4 * gp + r;
     const bool pz = p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4];
     const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
-    qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)(pz ? min(E - 4 - 5 * r + kE8M0One, 254) : kE8M0One);
+    qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)(pz ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One);
   }
   // rows of absent heads (groups of one or two heads) stay zero
   if (g == 0 && G < 4) {
@@ -430,10 +432,11 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 }
 
 // ---- 2'. split pass on the matrix cores (single-query decode, G <= 8) -----
-// Both contractions run on the scaled fp8 x fp4 MFMA, with the stored bits as
+// Both contractions run on the scaled f8f6f4 MFMA, with the stored bits as
 // the fp4 operand (B = 1 - 2 bit, one and_or per 8 values) and the float side
-// split into four fp8 digits in four A rows (the query side in balanced base
-// 32, see query_prep_kernel; the weights in base 16).  With the bit-plane form
+// split into four digits in four A rows: the query side in balanced base 32
+// as fp6 codes (see query_prep_kernel; fp6 x fp4 runs at twice the fp8 x fp4
+// rate), the weights in base 16 as fp8.  With the bit-plane form
 // of the levels, c[idx] = -(beta0 B0 + beta1 B1 + beta2 B2 + beta3 Bx) where
 // Bx = B0 B1 B2 is the plane of b0^b1^b2:
 //   <q', c[idx]> = sum_p <-beta_p q', B_p>        (4 MFMAs per page)
@@ -622,11 +625,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
       float raw[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        v4f c = mfma_f8f4(Aq[nt][0], B0, cinit[nt], scq[nt][0]);
-        c = mfma_f8f4(Aq[nt][1], B1, c, scq[nt][1]);
-        c = mfma_f8f4(Aq[nt][2], B2, c, scq[nt][2]);
-        c = mfma_f8f4(Aq[nt][3], Bx, c, scq[nt][3]);
-        const v4f q = mfma_f8f4(Aq[nt][4], Bs, qinit[nt], scq[nt][4]);
+        v4f c = mfma_f6f4(Aq[nt][0], B0, cinit[nt], scq[nt][0]);
+        c = mfma_f6f4(Aq[nt][1], B1, c, scq[nt][1]);
+        c = mfma_f6f4(Aq[nt][2], B2, c, scq[nt][2]);
+        c = mfma_f6f4(Aq[nt][3], Bx, c, scq[nt][3]);
+        const v4f q = mfma_f6f4(Aq[nt][4], Bs, qinit[nt], scq[nt][4]);
         const float code = (c[0] + c[1]) + (c[2] + c[3]);
         const float qj = (q[0] + q[1]) + (q[2] + q[3]);
         raw[nt] = cs * nk * fmaf(gm, qj, code);

@@ -12,7 +12,10 @@
 // of one KV head) and a chunk of keys, 32 keys (two pages) per step.  Each
 // step the waves dequantize the two K pages into f16 tiles in LDS (levels
 // hi + lo, signs +-1) and the two V pages (levels hi + lo, transposed), then
-// every wave computes, for its 16 rows,
+// every wave computes, for its 16 rows (the tiles' LDS reads, about 40 KB
+// per wave and step, bound the step rather than the matrix cores; two row
+// tiles per wave would halve them but leave one wave per SIMD, which
+// measured slower),
 //   S^T = K Q^T  on v_mfma_f32_16x16x32_f16: codes in three passes
 //        (K_hi Q_hi + K_hi Q_lo + K_lo Q_hi), signs in two (sigma S_hi +
 //        sigma S_lo): hi + lo halves carry ~22 bits on both sides, which the
@@ -90,16 +93,18 @@ __device__ __forceinline__ float half_at(const uint8_t *p) {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 16 * kWaves;  // query rows per workgroup
+constexpr int kRowTiles = 1;                  // 16-row tiles per wave (each shares the tile reads)
+constexpr int kRows = 16 * kRowTiles * kWaves;  // query rows per workgroup
 
 // Dequantize a step's staged pages into T (all threads of the workgroup).
-// Keys: thread (key, 8 coordinates); values: thread (coordinate, page, half
-// of the page's tokens), tokens 4g..4g+3 of page pg going to slots
-// 8g + 4pg .. +3 (the B operand order of the weights).
+// Keys: item (key, 8 coordinates); values: item (coordinate, page, half of
+// the page's tokens), tokens 4g..4g+3 of page pg going to slots 8g + 4pg ..
+// +3 (the B operand order of the weights).  512 items of each kind.
 __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage], const uint8_t (*rawv)[kVPage],
                                            int tid, const uint32_t (&th)[4], const uint32_t (&tl)[4]) {
-  {
-    const int key = tid >> 4, p16 = tid & 15, pg = key >> 4, tok = key & 15;
+#pragma unroll
+  for (int it = tid; it < 512; it += kThreads) {
+    const int key = it >> 4, p16 = it & 15, pg = key >> 4, tok = key & 15;
     const uint8_t *pk = rawk[pg];
     const uint32_t w0 = pk[kKPlane * 0 + 16 * tok + p16];
     const uint32_t w1 = pk[kKPlane * 1 + 16 * tok + p16];
@@ -122,8 +127,9 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
     *reinterpret_cast<uint4 *>(&T.kl[key][8 * p16]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
     *reinterpret_cast<uint4 *>(&T.ks[key][8 * p16]) = make_uint4(sv[0], sv[1], sv[2], sv[3]);
   }
-  {
-    const int c = tid >> 2, pg = (tid >> 1) & 1, th8 = tid & 1;
+#pragma unroll
+  for (int it = tid; it < 512; it += kThreads) {
+    const int c = it >> 2, pg = (it >> 1) & 1, th8 = it & 1;
     const uint8_t *pv = rawv[pg];
     const uint32_t w0 = pv[kKPlane * 0 + 2 * c + th8];
     const uint32_t w1 = pv[kKPlane * 1 + 2 * c + th8];
@@ -163,30 +169,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
 
   __shared__ __align__(16) PrefillLds S;
 
-  // this lane's query row (the column of S^T and O^T)
-  const int rw = 16 * wave + l16;
-  const int t = t0 + rw / G, hq = h * G + rw % G;
-  const bool row_ok = t < a.q_len;
-  const int64_t R = ((int64_t)b * a.q_len + min(t, a.q_len - 1)) * a.num_q_heads + hq;
-  const int lim = L - a.q_len + t;  // last visible key of the row
+  // this lane's query rows (columns of S^T and O^T), one per row tile u
+  bool row_ok[kRowTiles];
+  int64_t R[kRowTiles];
+  int lim[kRowTiles];
+#pragma unroll
+  for (int u = 0; u < kRowTiles; ++u) {
+    const int rw = 16 * (kRowTiles * wave + u) + l16;
+    const int t = t0 + rw / G, hq = h * G + rw % G;
+    row_ok[u] = t < a.q_len;
+    R[u] = ((int64_t)b * a.q_len + min(t, a.q_len - 1)) * a.num_q_heads + hq;
+    lim[u] = L - a.q_len + t;  // last visible key of the row
+  }
 
   // B operands of S^T: chunk kc = 0..3 rotated query, 4..7 alpha S q, scaled
   // by softmax scale x log2(e), as f16 hi and lo
-  v8h qh[8], ql[8];
+  v8h qh[kRowTiles][8], ql[kRowTiles][8];
   {
     const float cs = a.scale * kLog2e;
-    const float *src = a.qprep + R * 256;
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const float4 x0 = *reinterpret_cast<const float4 *>(src + 32 * kc + 8 * g4);
-      const float4 x1 = *reinterpret_cast<const float4 *>(src + 32 * kc + 8 * g4 + 4);
-      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int u = 0; u < kRowTiles; ++u) {
+      const float *src = a.qprep + R[u] * 256;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = row_ok ? cs * xs[j] : 0.0f;
-        const _Float16 hi = (_Float16)v;
-        qh[kc][j] = hi;
-        ql[kc][j] = (_Float16)(v - (float)hi);
+      for (int kc = 0; kc < 8; ++kc) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(src + 32 * kc + 8 * g4);
+        const float4 x1 = *reinterpret_cast<const float4 *>(src + 32 * kc + 8 * g4 + 4);
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = row_ok[u] ? cs * xs[j] : 0.0f;
+          const _Float16 hi = (_Float16)v;
+          qh[u][kc][j] = hi;
+          ql[u][kc][j] = (_Float16)(v - (float)hi);
+        }
       }
     }
   }
@@ -248,10 +263,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     }
   };
 
-  v4f acc[8];
+  v4f acc[kRowTiles][8];
+  float m_run[kRowTiles], l_part[kRowTiles];
 #pragma unroll
-  for (int cv = 0; cv < 8; ++cv) acc[cv] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_part = 0.0f;
+  for (int u = 0; u < kRowTiles; ++u) {
+    m_run[u] = -INFINITY;
+    l_part[u] = 0.0f;
+#pragma unroll
+    for (int cv = 0; cv < 8; ++cv) acc[u][cv] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   const int nsteps = (s1 - s0 + kKeys - 1) / kKeys;
   uint4 raw = load_raw(s0);
@@ -271,68 +291,79 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     // step's are read, so that vector and matrix work can interleave
     dequantize(S.d[(st + 1) & 1], S.rawk[(st + 1) & 1], S.rawv[(st + 1) & 1], tid, th, tl);
 
-    // ---- S^T = K Q^T for this wave's 16 rows: lane l, register i of tile ct
-    // holds key 16 ct + 4 (l / 16) + i of row l % 16
-    v4f cc[2], csg[2];
+    // ---- S^T = K Q^T for this wave's rows: lane l, register i of key tile
+    // ct holds key 16 ct + 4 (l / 16) + i of row l % 16 of row tile u
+    v4f cc[kRowTiles][2], csg[kRowTiles][2];
+#pragma unroll
+    for (int u = 0; u < kRowTiles; ++u)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) cc[u][ct] = csg[u][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      v4f c = {0.0f, 0.0f, 0.0f, 0.0f}, s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
         const v8h ah = *reinterpret_cast<const v8h *>(&T.kh[16 * ct + l16][32 * kc + 8 * g4]);
         const v8h al = *reinterpret_cast<const v8h *>(&T.kl[16 * ct + l16][32 * kc + 8 * g4]);
         const v8h as = *reinterpret_cast<const v8h *>(&T.ks[16 * ct + l16][32 * kc + 8 * g4]);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[kc], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[kc], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[kc], c, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as, qh[4 + kc], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as, ql[4 + kc], s, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kRowTiles; ++u) {
+          cc[u][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[u][kc], cc[u][ct], 0, 0, 0);
+          cc[u][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[u][kc], cc[u][ct], 0, 0, 0);
+          cc[u][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[u][kc], cc[u][ct], 0, 0, 0);
+          csg[u][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as, qh[u][4 + kc], csg[u][ct], 0, 0, 0);
+          csg[u][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as, ql[u][4 + kc], csg[u][ct], 0, 0, 0);
+        }
       }
-      cc[ct] = c;
-      csg[ct] = s;
     }
 
     // ---- online softmax (log2 units), exact running maximum --------------
-    float sc[2][4], vnk[2][4];
-    bool vis[2][4];
-    float tmax = -INFINITY;
+    float knv[2][4], kgv[2][4], vnv[2][4];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const float4 kn4 = *reinterpret_cast<const float4 *>(&T.kn[16 * ct + 4 * g4]);
       const float4 kg4 = *reinterpret_cast<const float4 *>(&T.kg[16 * ct + 4 * g4]);
       const float4 vn4 = *reinterpret_cast<const float4 *>(&T.vn[16 * ct + 4 * g4]);
-      const float knv[4] = {kn4.x, kn4.y, kn4.z, kn4.w}, kgv[4] = {kg4.x, kg4.y, kg4.z, kg4.w};
-      const float vnv[4] = {vn4.x, vn4.y, vn4.z, vn4.w};
+      knv[ct][0] = kn4.x; knv[ct][1] = kn4.y; knv[ct][2] = kn4.z; knv[ct][3] = kn4.w;
+      kgv[ct][0] = kg4.x; kgv[ct][1] = kg4.y; kgv[ct][2] = kg4.z; kgv[ct][3] = kg4.w;
+      vnv[ct][0] = vn4.x; vnv[ct][1] = vn4.y; vnv[ct][2] = vn4.z; vnv[ct][3] = vn4.w;
+    }
+    v8h wb[kRowTiles];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * ct + 4 * g4 + i;
-        vis[ct][i] = key < s1 && key <= lim;
-        const float raw_s = fmaf(knv[i], cc[ct][i], kgv[i] * csg[ct][i]);
-        sc[ct][i] = vis[ct][i] ? raw_s : -INFINITY;
-        vnk[ct][i] = vnv[i];
-        tmax = fmaxf(tmax, sc[ct][i]);
+    for (int u = 0; u < kRowTiles; ++u) {
+      float sc[2][4];
+      bool vis[2][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * ct + 4 * g4 + i;
+          vis[ct][i] = key < s1 && key <= lim[u];
+          const float raw_s = fmaf(knv[ct][i], cc[u][ct][i], kgv[ct][i] * csg[u][ct][i]);
+          sc[ct][i] = vis[ct][i] ? raw_s : -INFINITY;
+          tmax = fmaxf(tmax, sc[ct][i]);
+        }
       }
-    }
-    tmax = fmaxf(tmax, xchg16(tmax, lane));
-    tmax = fmaxf(tmax, xchg32(tmax, lane));
-    const float m_new = fmaxf(m_run, tmax);
-    // m_run = -inf: nothing accumulated yet (acc and l are zero)
-    const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    if (__ballot(f != 1.0f)) {  // wave-uniform: the maximum moved in some row
-      l_part *= f;
+      tmax = fmaxf(tmax, xchg16(tmax, lane));
+      tmax = fmaxf(tmax, xchg32(tmax, lane));
+      const float m_new = fmaxf(m_run[u], tmax);
+      // m_run = -inf: nothing accumulated yet (acc and l are zero)
+      const float f = m_run[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
+      m_run[u] = m_new;
+      if (__ballot(f != 1.0f)) {  // wave-uniform: the maximum moved in some row
+        l_part[u] *= f;
 #pragma unroll
-      for (int cv = 0; cv < 8; ++cv) acc[cv] *= f;
-    }
-    v8h wb;
+        for (int cv = 0; cv < 8; ++cv) acc[u][cv] *= f;
+      }
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = vis[ct][i] ? __builtin_amdgcn_exp2f(sc[ct][i] - m_new) : 0.0f;
-        l_part += p;
-        // the norm of a masked key may hold any bits: its weight is selected to 0
-        wb[4 * ct + i] = (_Float16)(vis[ct][i] ? p * vnk[ct][i] : 0.0f);
+        for (int i = 0; i < 4; ++i) {
+          const float p = vis[ct][i] ? __builtin_amdgcn_exp2f(sc[ct][i] - m_new) : 0.0f;
+          l_part[u] += p;
+          // the norm of a masked key may hold any bits: its weight is selected to 0
+          wb[u][4 * ct + i] = (_Float16)(vis[ct][i] ? p * vnv[ct][i] : 0.0f);
+        }
       }
     }
 
@@ -341,24 +372,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     for (int cv = 0; cv < 8; ++cv) {
       const v8h vh = *reinterpret_cast<const v8h *>(&T.vh[16 * cv + l16][8 * g4]);
       const v8h vl = *reinterpret_cast<const v8h *>(&T.vl[16 * cv + l16][8 * g4]);
-      acc[cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, wb, acc[cv], 0, 0, 0);
-      acc[cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, wb, acc[cv], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kRowTiles; ++u) {
+        acc[u][cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, wb[u], acc[u][cv], 0, 0, 0);
+        acc[u][cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, wb[u], acc[u][cv], 0, 0, 0);
+      }
     }
   }
 
-  // ---- partial record of the row: lanes of one row hold 4 key groups ----
-  float l_row = l_part + xchg16(l_part, lane);
-  l_row += xchg32(l_row, lane);
-  if (row_ok) {
-    float *part = a.partials + (R * a.num_splits + split) * kPartStride;
-    if (g4 == 0) {
-      part[0] = m_run;
-      part[1] = l_row;
-    }
+  // ---- partial records: the lanes of one row hold 4 key groups ----------
 #pragma unroll
-    for (int cv = 0; cv < 8; ++cv) {
-      const float4 o = make_float4(acc[cv][0], acc[cv][1], acc[cv][2], acc[cv][3]) * (1.0f / kTabScale);
-      *reinterpret_cast<float4 *>(part + 4 + 16 * cv + 4 * g4) = o;
+  for (int u = 0; u < kRowTiles; ++u) {
+    float l_row = l_part[u] + xchg16(l_part[u], lane);
+    l_row += xchg32(l_row, lane);
+    if (row_ok[u]) {
+      float *part = a.partials + (R[u] * a.num_splits + split) * kPartStride;
+      if (g4 == 0) {
+        part[0] = m_run[u];
+        part[1] = l_row;
+      }
+#pragma unroll
+      for (int cv = 0; cv < 8; ++cv) {
+        const float4 o = make_float4(acc[u][cv][0], acc[u][cv][1], acc[u][cv][2], acc[u][cv][3]) * (1.0f / kTabScale);
+        *reinterpret_cast<float4 *>(part + 4 + 16 * cv + 4 * g4) = o;
+      }
     }
   }
 }
