@@ -450,12 +450,11 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 // The value contraction is split by coordinates: wave w owns N-tiles 2w and
 // 2w+1 (32 coordinates) for all four planes.  The running maximum m is
 // shared by all waves and moves only when a tile exceeds it by 2^64.
-template <int NT>
 struct MfmaTile {
-  uint8_t wq[NT][4][4][128];   // [tile][head][digit][K] fp8 digits of w
-  uint32_t vs[4][400];         // [page pair][plane * 128 + coord], padded
-  float mi[NT][4][4];          // [tile][K-block][head] block maxima
-  int ex[NT][4][4];            // [tile][K-block][head] digit exponents
+  uint8_t wq[4][4][128];   // [head][digit][K] fp8 digits of w
+  uint32_t vs[4][400];     // [page pair][plane * 128 + coord], padded
+  float mi[4][4];          // [head][K-block] block maxima (log2 units)
+  int ex[4][4];            // [head][K-block] digit exponents
 };
 
 struct MfmaLoads {
@@ -539,45 +538,72 @@ __device__ __forceinline__ void mfma_load_tile(MfmaLoads &R, const DecodeArgs &a
   }
 }
 
-// Two operand tiles (8 heads) need more than the 256 registers that two waves
-// per SIMD leave each wave.
-template <int NT>
-__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(DecodeArgs a) {
-  const int b = blockIdx.x;  // q_len == 1
-  const int h = blockIdx.y;
-  const int split = blockIdx.z;
+// A workgroup serves one chunk of one KV head and up to four of its query
+// heads (one operand tile); eight heads per KV head take two workgroups whose
+// dispatch ids differ by 8, so that they run on the same XCD at the same time
+// and the second reads the pages from L2.  Each barrier interval holds two
+// independent chains for the scheduler to interleave: the value contraction
+// of tile i-1 and the scores and weight digits of tile i.
+struct SplitItem {
+  int b, h, hh, split;
+  bool ok;
+};
+__device__ __forceinline__ SplitItem split_item(const DecodeArgs &a, int halves) {
+  const int lin = blockIdx.x;
+  SplitItem it;
+  int item;
+  if (halves == 2) {
+    item = 8 * (lin >> 4) + (lin & 7);
+    it.hh = (lin >> 3) & 1;
+  } else {
+    item = lin;
+    it.hh = 0;
+  }
+  const int per_seq = a.num_kv_heads * a.num_splits;
+  it.ok = item < a.num_seqs * per_seq;
+  item = it.ok ? item : 0;
+  it.b = item / per_seq;
+  it.h = (item / a.num_splits) % a.num_kv_heads;
+  it.split = item % a.num_splits;
+  return it;
+}
+
+__global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
+  const int halves = a.qk_tiles;
+  const SplitItem item = split_item(a, halves);
+  if (!item.ok) return;  // uniform: padding of the interleaved grid
+  const int b = item.b, h = item.h, hh = item.hh, split = item.split;
   const int L = clamped_context(a, b);
   const int s0 = split * a.split_tokens;
   const int s1 = min(s0 + a.split_tokens, L);
   if (s0 >= s1) return;  // uniform
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t16 = lane & 15, grow = lane >> 4;
   const int64_t grp = (int64_t)b * a.num_kv_heads + h;
   const int G = a.group;
 
-  __shared__ MfmaTile<NT> buf[2];
-  __shared__ float lred[4][NT][4];
+  __shared__ __align__(16) MfmaTile buf[2];
+  __shared__ float lred[4][4];
   __shared__ int32_t bts[kBtCap];
 
-  // query-side operands of the score contraction
-  v8i Aq[NT][5];
-  int scq[NT][5];
-  v4f cinit[NT], qinit[NT];  // accumulator start values (see b_split)
+  // query-side operands of the score contraction: tile hh of the group
+  v8i Aq[5];
+  int scq[5];
+  v4f cinit, qinit;  // accumulator start values (see b_split)
   {
-    const uint32_t *qa = a.qa + grp * (int64_t)(NT * (5 * 64 * 9 + 32));
+    const uint32_t *qa = a.qa + grp * (int64_t)(halves * (5 * 64 * 9 + 32));
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int p = 0; p < 5; ++p) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((nt * 5 + p) * 64 + lane) * 8);
-        const uint4 u0 = src[0], u1 = src[1];
-        Aq[nt][p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-        scq[nt][p] = (int)qa[NT * 5 * 64 * 8 + (nt * 5 + p) * 64 + lane];
-      }
-      const float *ci = reinterpret_cast<const float *>(qa + NT * 5 * 64 * 9) + (nt * 4 + grow) * 8;
-      cinit[nt] = v4f{ci[0], ci[1], ci[2], ci[3]};
-      qinit[nt] = v4f{ci[4], ci[5], ci[6], ci[7]};
+    for (int p = 0; p < 5; ++p) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((hh * 5 + p) * 64 + lane) * 8);
+      const uint4 u0 = src[0];
+      const uint2 u1 = *reinterpret_cast<const uint2 *>(src + 1);
+      Aq[p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, 0, 0};
+      scq[p] = (int)qa[halves * 5 * 64 * 8 + (hh * 5 + p) * 64 + lane];
     }
+    const float *ci = reinterpret_cast<const float *>(qa + halves * 5 * 64 * 9) + (hh * 4 + grow) * 8;
+    cinit = v4f{ci[0], ci[1], ci[2], ci[3]};
+    qinit = v4f{ci[4], ci[5], ci[6], ci[7]};
   }
   float beta[4];
 #pragma unroll
@@ -591,28 +617,23 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
   }
   lds_barrier();
 
-  float mref[NT][4];
-  float lsum[NT];
-  v4f acc[NT][4][2];
+  float mref[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // shared running maximum per head
+  float lsum = 0.0f;
+  v4f acc[4][2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    lsum[nt] = 0.0f;
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) mref[nt][g] = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[nt][p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 2; ++j) acc[p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const int gA = t16 >> 2, rA = lane & 3, kb = grow;  // A-operand row and scale block of this lane
 
-  auto process = [&](const MfmaLoads &R, int tok0, MfmaTile<NT> &Bf) {
-    // scores of pages 2*wave, 2*wave+1: lane (head grow, token t16).  The
-    // matrix ops write all 64 lanes whatever the exec mask, so they must never
-    // sit under a lane-dependent branch: every lane computes its score, and
-    // keys past the visible range are masked afterwards with a select.
-    float sc[2][NT];
+  // Scores of pages 2*wave, 2*wave+1 of the tile at tok0 (lane: head grow,
+  // token t16), their block maximum and the weight digits, into Bf; returns
+  // the lane's probability sum and block maximum through ps, mi.  The matrix
+  // ops write all 64 lanes whatever the exec mask, so they must never sit
+  // under a lane-dependent branch: every lane computes its score, and keys
+  // past the visible range are masked afterwards with a select.
+  auto scores = [&](const MfmaLoads &R, int tok0, MfmaTile &Bf, float &ps, float &mi) {
+    float sc[2];
     bool valid[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -622,53 +643,43 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
                 Bs = b_split(r3);
       const float nk = half_bits(R.nk[kk] & 0xFFFFu), gm = half_bits(R.gm[kk] & 0xFFFFu);
       valid[kk] = tok0 + 16 * (2 * wave + kk) + t16 < s1;
-      float raw[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        v4f c = mfma_f6f4(Aq[nt][0], B0, cinit[nt], scq[nt][0]);
-        c = mfma_f6f4(Aq[nt][1], B1, c, scq[nt][1]);
-        c = mfma_f6f4(Aq[nt][2], B2, c, scq[nt][2]);
-        c = mfma_f6f4(Aq[nt][3], Bx, c, scq[nt][3]);
-        const v4f q = mfma_f6f4(Aq[nt][4], Bs, qinit[nt], scq[nt][4]);
-        const float code = (c[0] + c[1]) + (c[2] + c[3]);
-        const float qj = (q[0] + q[1]) + (q[2] + q[3]);
-        raw[nt] = cs * nk * fmaf(gm, qj, code);
-        // pin the score (and the matrix ops feeding it) to the unconditional
-        // path: otherwise they may be sunk into the branch of the select below
-        asm volatile("" : "+v"(raw[nt]));
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sc[kk][nt] = valid[kk] ? raw[nt] : -INFINITY;
+      v4f c = mfma_f6f4(Aq[0], B0, cinit, scq[0]);
+      c = mfma_f6f4(Aq[1], B1, c, scq[1]);
+      c = mfma_f6f4(Aq[2], B2, c, scq[2]);
+      c = mfma_f6f4(Aq[3], Bx, c, scq[3]);
+      const v4f q = mfma_f6f4(Aq[4], Bs, qinit, scq[4]);
+      const float code = (c[0] + c[1]) + (c[2] + c[3]);
+      const float qj = (q[0] + q[1]) + (q[2] + q[3]);
+      float raw = cs * nk * fmaf(gm, qj, code);
+      // pin the score (and the matrix ops feeding it) to the unconditional
+      // path: otherwise they may be sunk into the branch of the select below
+      asm volatile("" : "+v"(raw));
+      sc[kk] = valid[kk] ? raw : -INFINITY;
     }
-    // block maximum, weights, digits
-    float mi[NT], ps[NT];
+    mi = ceilf(row_max16(fmaxf(sc[0], sc[1])));
+    float w[2];
+    ps = 0.0f;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      mi[nt] = ceilf(row_max16(fmaxf(sc[0][nt], sc[1][nt])));
-      float w[2];
-      ps[nt] = 0.0f;
+    for (int kk = 0; kk < 2; ++kk) {
+      const float p = sc[kk] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[kk] - mi);
+      ps += p;
+      // the norm of a slot past the visible range may hold any bits
+      w[kk] = (valid[kk] && p > 0.0f) ? p * half_bits(R.nv[kk] & 0xFFFFu) : 0.0f;
+    }
+    const float wm = row_max16(fmaxf(w[0], w[1]));
+    const int E = wm > 0.0f ? bound_exponent(wm) : 0;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const float p = sc[kk][nt] == -INFINITY ? 0.0f : exp2f(sc[kk][nt] - mi[nt]);
-        ps[nt] += p;
-        // the norm of a slot past the visible range may hold any bits
-        w[kk] = (valid[kk] && p > 0.0f) ? p * half_bits(R.nv[kk] & 0xFFFFu) : 0.0f;
-      }
-      const float wm = row_max16(fmaxf(w[0], w[1]));
-      const int E = wm > 0.0f ? bound_exponent(wm) : 0;
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t X = (uint32_t)fminf(rintf(ldexpf(w[kk], 16 - E)), 65535.0f);
+      uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)(X >> 12), (float)((X >> 8) & 15u), 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)((X >> 4) & 15u), (float)(X & 15u), pk, true);
+      const int kap = b_kappa(32 * wave + 16 * kk + t16);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint32_t X = (uint32_t)fminf(rintf(ldexpf(w[kk], 16 - E)), 65535.0f);
-        uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)(X >> 12), (float)((X >> 8) & 15u), 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)((X >> 4) & 15u), (float)(X & 15u), pk, true);
-        const int kap = b_kappa(32 * wave + 16 * kk + t16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Bf.wq[nt][grow][r][kap] = (uint8_t)(pk >> (8 * r));
-      }
-      if (t16 == 0) {
-        Bf.mi[nt][wave][grow] = mi[nt];
-        Bf.ex[nt][wave][grow] = E;
-      }
+      for (int r = 0; r < 4; ++r) Bf.wq[grow][r][kap] = (uint8_t)(pk >> (8 * r));
+    }
+    if (t16 == 0) {
+      Bf.mi[grow][wave] = mi;
+      Bf.ex[grow][wave] = E;
     }
     // value planes of this wave's page pair: interleave the 16-bit words
     if (lane < 48) {
@@ -687,109 +698,105 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void split_mfma_kernel(Decode
       dst[0] = o0;
       dst[1] = o1;
     }
-    lds_barrier();
+  };
+
+  // Value contraction of a tile whose digits are in Bf (after the barrier),
+  // with the lane's probability sum ps and block maximum mi of that tile.
+  auto values = [&](const MfmaTile &Bf, float ps, float mi) {
     // shared running maximum: moves only when a tile exceeds it by 2^64
     bool moved = false;
-    float fct[NT][4];
+    float fct[4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float Mt = uniform(fmaxf(fmaxf(Bf.mi[nt][0][g], Bf.mi[nt][1][g]), fmaxf(Bf.mi[nt][2][g], Bf.mi[nt][3][g])));
-        fct[nt][g] = 1.0f;
-        if (Mt > mref[nt][g] + 64.0f) {
-          fct[nt][g] = exp2f(mref[nt][g] - Mt);
-          mref[nt][g] = Mt;
-          moved = true;
-        }
+    for (int g = 0; g < 4; ++g) {
+      const float4 m4 = *reinterpret_cast<const float4 *>(&Bf.mi[g][0]);
+      const float Mt = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
+      fct[g] = 1.0f;
+      if (Mt > mref[g] + 64.0f) {
+        fct[g] = __builtin_amdgcn_exp2f(mref[g] - Mt);
+        mref[g] = Mt;
+        moved = true;
       }
     }
     if (moved) {
+      const float f = sel4(fct, grow);
+      lsum *= f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float f = sel4(fct[nt], grow);
-        lsum[nt] *= f;
+      for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[nt][p][j] *= f;
-      }
+        for (int j = 0; j < 2; ++j) acc[p][j] *= f;
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      if (ps[nt] > 0.0f) lsum[nt] += ps[nt] * exp2f(mi[nt] - sel4(mref[nt], grow));
+    if (ps > 0.0f) lsum += ps * __builtin_amdgcn_exp2f(mi - sel4(mref, grow));
     // weight operand: row (head gA, digit rA), K-block scale from wave kb
-    v8i Aw[NT];
-    int sw[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint4 u0 = *reinterpret_cast<const uint4 *>(&Bf.wq[nt][gA][rA][16 * grow]);
-      const uint4 u1 = *reinterpret_cast<const uint4 *>(&Bf.wq[nt][gA][rA][64 + 16 * grow]);
-      Aw[nt] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-      const float mb = Bf.mi[nt][kb][gA];
-      int scl = kE8M0One;
-      if (mb != -INFINITY) {
-        const float d = fmaxf(mb - sel4(mref[nt], gA), -300.0f);
-        scl = min(max(Bf.ex[nt][kb][gA] - 4 - 4 * rA + (int)d + kE8M0One, 0), 254);
-      }
-      sw[nt] = scl;
+    const uint4 u0 = *reinterpret_cast<const uint4 *>(&Bf.wq[gA][rA][16 * grow]);
+    const uint4 u1 = *reinterpret_cast<const uint4 *>(&Bf.wq[gA][rA][64 + 16 * grow]);
+    const v8i Aw = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+    const float mb = Bf.mi[gA][kb];
+    int sw = kE8M0One;
+    if (mb != -INFINITY) {
+      const float d = fmaxf(mb - sel4(mref, gA), -300.0f);
+      sw = min(max(Bf.ex[gA][kb] - 4 - 4 * rA + (int)d + kE8M0One, 0), 254);
     }
-    // value contraction: this wave's coordinates 32*wave .. +31
+    // this wave's coordinates 32*wave .. +31
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = 16 * (2 * wave + j) + t16;
       const uint32_t p0 = Bf.vs[grow][col], p1 = Bf.vs[grow][128 + col], p2 = Bf.vs[grow][256 + col];
       const v8i V0 = b_pm1(p0), V1 = b_pm1(p1), V2 = b_pm1(p2), Vx = b_pm1(p0 ^ p1 ^ p2);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[nt][0][j] = mfma_f8f4(Aw[nt], V0, acc[nt][0][j], sw[nt]);
-        acc[nt][1][j] = mfma_f8f4(Aw[nt], V1, acc[nt][1][j], sw[nt]);
-        acc[nt][2][j] = mfma_f8f4(Aw[nt], V2, acc[nt][2][j], sw[nt]);
-        acc[nt][3][j] = mfma_f8f4(Aw[nt], Vx, acc[nt][3][j], sw[nt]);
-      }
+      acc[0][j] = mfma_f8f4(Aw, V0, acc[0][j], sw);
+      acc[1][j] = mfma_f8f4(Aw, V1, acc[1][j], sw);
+      acc[2][j] = mfma_f8f4(Aw, V2, acc[2][j], sw);
+      acc[3][j] = mfma_f8f4(Aw, Vx, acc[3][j], sw);
     }
   };
 
   const int ntiles = (s1 - s0 + 127) >> 7;
   MfmaLoads RA, RB;
+  float psA = 0.0f, miA = -INFINITY, psB = 0.0f, miB = -INFINITY;
   mfma_load_tile(RA, a, btab, bts, pg_first, h, s0, s1, wave, lane);
-  for (int it = 0; it < ntiles; it += 2) {
-    if (it + 1 < ntiles) mfma_load_tile(RB, a, btab, bts, pg_first, h, s0 + 128 * (it + 1), s1, wave, lane);
-    process(RA, s0 + 128 * it, buf[0]);
-    if (it + 1 < ntiles) {
-      if (it + 2 < ntiles) mfma_load_tile(RA, a, btab, bts, pg_first, h, s0 + 128 * (it + 2), s1, wave, lane);
-      process(RB, s0 + 128 * (it + 1), buf[1]);
-    }
-  }
-
-  // row sums over the 16 lanes of a head, then over the waves
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float ls = row_sum16(lsum[nt]);
-    if (t16 == 0) lred[wave][nt][grow] = ls;
+  if (ntiles > 1) mfma_load_tile(RB, a, btab, bts, pg_first, h, s0 + 128, s1, wave, lane);
+  scores(RA, s0, buf[0], psA, miA);
+  // tile i (odd: RB, buf[1]; even: RA, buf[0]) with the values of tile i-1
+  for (int i = 1; i < ntiles; i += 2) {
+    if (i + 1 < ntiles) mfma_load_tile(RA, a, btab, bts, pg_first, h, s0 + 128 * (i + 1), s1, wave, lane);
+    lds_barrier();
+    values(buf[0], psA, miA);
+    scores(RB, s0 + 128 * i, buf[1], psB, miB);
+    if (i + 1 >= ntiles) break;
+    if (i + 2 < ntiles) mfma_load_tile(RB, a, btab, bts, pg_first, h, s0 + 128 * (i + 2), s1, wave, lane);
+    lds_barrier();
+    values(buf[1], psB, miB);
+    scores(RA, s0 + 128 * (i + 1), buf[0], psA, miA);
   }
   lds_barrier();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int g = 4 * nt + grow;
-    if (g >= G) continue;
+  if (ntiles & 1)
+    values(buf[0], psA, miA);
+  else
+    values(buf[1], psB, miB);
+
+  // row sums over the 16 lanes of a head, then over the waves
+  {
+    const float ls = row_sum16(lsum);
+    if (t16 == 0) lred[wave][grow] = ls;
+  }
+  lds_barrier();
+  const int g = 4 * hh + grow;
+  if (g < G) {
     float *part = a.partials + ((grp * G + g) * a.num_splits + split) * kPartStride;
     if (wave == 0 && t16 == 0) {
-      part[0] = sel4(mref[nt], grow);
-      part[1] = (lred[0][nt][grow] + lred[1][nt][grow]) + (lred[2][nt][grow] + lred[3][nt][grow]);
+      part[0] = sel4(mref, grow);
+      part[1] = (lred[0][grow] + lred[1][grow]) + (lred[2][grow] + lred[3][grow]);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       float o = 0.0f;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const v4f &c = acc[nt][p][j];
+        const v4f &c = acc[p][j];
         o = fmaf(-beta[p], (c[0] + c[1]) + (c[2] + c[3]), o);
       }
       part[4 + 16 * (2 * wave + j) + t16] = o;
     }
   }
-
 }
 
 // ---- 3. merge: one wave per output row --------------------------------------
@@ -816,15 +823,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups, (unsigned)a.group), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.qa != nullptr) {  // matrix-core pass
-    dim3 grid((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
-    if (a.qk_tiles == 1) {
-      hipLaunchKernelGGL(split_mfma_kernel<1>, grid, dim3(256), 0, stream, a);
-    } else if (a.qk_tiles == 2) {
-      hipLaunchKernelGGL(split_mfma_kernel<2>, grid, dim3(256), 0, stream, a);
-    } else {
-      return hipErrorInvalidValue;
-    }
+  if (a.qa != nullptr) {  // matrix-core pass: one workgroup per (chunk, KV head, head tile)
+    if (a.qk_tiles != 1 && a.qk_tiles != 2) return hipErrorInvalidValue;
+    const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_splits;
+    const int64_t wgs = a.qk_tiles == 1 ? items : 2 * ((items + 7) / 8) * 8;
+    hipLaunchKernelGGL(split_mfma_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
   } else if (prefill_uses_mfma(a.q_len, a.group)) {
     e = launch_prefill(a, stream);
     if (e != hipSuccess) return e;

@@ -48,10 +48,16 @@ def _exec_step(stack: tuple, ins: str) -> tuple:
     if's s_and_saveexec pushes its save register (narrowing), a plain copy of
     exec (s_mov_b64 X, exec) pushes X (not narrowing), a loop's lane exit
     (s_andn2_b64 exec, exec, X) pushes X once, and restoring a saved mask
-    (s_or_b64 exec, exec, X) pops X and everything above it.  Else-switches
-    keep the stack; any other write of exec is a narrowing with no known
-    restore register."""
+    (s_or_b64 exec, exec, X) pops X and everything above it.  An if/else
+    moves its saved mask to the register that restores it
+    (s_xor_b64 Y, exec, X renames X to Y).  Else-switches keep the stack;
+    any other write of exec is a narrowing with no known restore register."""
     regs = [r for r, _ in stack]
+    # if/else: the saved mask moves to another register, which then restores
+    m = re.match(r"s_xor_b64 (s\[\d+:\d+\]), exec, (s\[\d+:\d+\])$", ins)
+    if m and m.group(2) in regs:
+        i = len(regs) - 1 - regs[::-1].index(m.group(2))
+        return stack[:i] + ((m.group(1), stack[i][1]),) + stack[i + 1:]
     m = re.match(r"s_and_saveexec_b64 (\S+),", ins)
     if m:
         return stack + ((m.group(1), True),)
@@ -215,6 +221,27 @@ def test_checker_follows_copied_exec_saves():
         "v_mfma_f32_16x16x32_f16 v[0:3], v[4:7], v[8:11], 0",
         "s_endpgm"])
     assert [ln for _, ln in mfma_under_partial_exec(asm)] == [6]
+
+
+def test_checker_follows_if_else_mask_moves():
+    # outer if/else saved in s[28:29], moved to s[14:15]; s[28:29] is reused by
+    # an inner if; the outer restore goes through s[14:15], inside a loop
+    asm = "\n".join([
+        "_Zife:",
+        ".LBB0_1:",
+        "s_and_saveexec_b64 s[28:29], s[14:15]",
+        "s_xor_b64 s[14:15], exec, s[28:29]",
+        "s_cbranch_execz .LBB0_2",
+        "s_and_saveexec_b64 s[28:29], vcc",
+        "v_add_f32_e32 v0, v1, v2",
+        "s_or_b64 exec, exec, s[28:29]",
+        ".LBB0_2:",
+        "s_andn2_saveexec_b64 s[14:15], s[14:15]",
+        "s_or_b64 exec, exec, s[14:15]",
+        "v_mfma_f32_16x16x32_f16 v[0:3], v[4:7], v[8:11], 0",
+        "s_cbranch_scc1 .LBB0_1",
+        "s_endpgm"])
+    assert mfma_under_partial_exec(asm) == []
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
