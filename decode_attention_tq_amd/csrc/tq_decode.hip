@@ -98,19 +98,6 @@ __device__ __forceinline__ int bound_exponent(float M) {  // M < 2^E for finite 
   return ex == 0 ? -126 : ex - 126;
 }
 
-// Digit r (0..3) of x in balanced base 32 under bound 2^E: with
-// Y = rint(x 2^(19-E)), Y = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16.
-__device__ __forceinline__ float query_digit(float x, int E, int r) {
-  const float y = rintf(ldexpf(x, 19 - E));  // |y| <= 2^19
-  const float d0 = rintf(y * 0x1p-15f);
-  float rem = y - d0 * 32768.0f;
-  const float d1 = rintf(rem * 0x1p-10f);
-  rem -= d1 * 1024.0f;
-  const float d2 = rintf(rem * 0.03125f);
-  const float d3 = rem - d2 * 32.0f;
-  return r == 0 ? d0 : r == 1 ? d1 : r == 2 ? d2 : d3;
-}
-
 __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
@@ -168,72 +155,86 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   const int nwords = NT * 5 * 64 * 8;
   const int nt = g >> 2, gp = g & 3;
   uint32_t *qa = a.qa + grp * (int64_t)(NT * (5 * 64 * 9 + 32));
-  // this head's rows: lanes 16*ga + 4*gp + r of tile nt, as fp6 codes (K
-  // slot 32 ga + s at code s).  The digit of a K slot is scaled by the
-  // factor that goes with the b_split operands.
+  __shared__ __align__(16) uint8_t codes[5][4][128];  // [plane][digit][K slot] fp6 codes
+  __shared__ float spart[4][8];                       // per wave: start-value partial sums
+  // 1. digits of every (plane, K slot): the four digits of one value go to
+  // four A rows.  The digit of a K slot is scaled by the factor that goes
+  // with the b_split operands; the start values (per digit r, the weighted
+  // sum of the unscaled A values, see b_split) are summed on the way, for the
+  // code planes (p < 4) and the sign plane.
+  float sc4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = tid; e < 5 * 128; e += 256) {
+    const int p = e >> 7, kap = e & 127;
+    const bool pz = p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4];
+    const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
+    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
+    const float x = p < 4 ? -bp * qp[b_coord(kap)] : -qp[128 + b_coord(kap)];
+    // Y = rint(x 2^(19-E)) = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16
+    const float y = pz ? rintf(ldexpf(x, 19 - E)) : 0.0f;
+    const float d0 = rintf(y * 0x1p-15f);
+    float rem = y - d0 * 32768.0f;
+    const float d1 = rintf(rem * 0x1p-10f);
+    rem -= d1 * 1024.0f;
+    const float d2 = rintf(rem * 0.03125f);
+    const float d3 = rem - d2 * 32.0f;
+    const float f = b_split_factor(kap), wgt = b_split_weight(kap);
+    codes[p][0][kap] = (uint8_t)fp6_code(d0 * f);
+    codes[p][1][kap] = (uint8_t)fp6_code(d1 * f);
+    codes[p][2][kap] = (uint8_t)fp6_code(d2 * f);
+    codes[p][3][kap] = (uint8_t)fp6_code(d3 * f);
+    const float v0 = wgt * ldexpf(d0, E - 4), v1 = wgt * ldexpf(d1, E - 9);
+    const float v2 = wgt * ldexpf(d2, E - 14), v3 = wgt * ldexpf(d3, E - 19);
+    if (p < 4) {
+      sc4[0] += v0; sc4[1] += v1; sc4[2] += v2; sc4[3] += v3;
+    } else {
+      sq4[0] += v0; sq4[1] += v1; sq4[2] += v2; sq4[3] += v3;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc4[r] = wave_sum(sc4[r]);
+    sq4[r] = wave_sum(sq4[r]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      spart[wave][r] = sc4[r];
+      spart[wave][4 + r] = sq4[r];
+    }
+  }
+  lds_barrier();
+  // 2. this head's rows: lanes 16*ga + 4*gp + r of tile nt, 32 fp6 codes (K
+  // slot 32 ga + s at code s) packed into six words, and their E8M0 scales
   if (tid < 5 * 16) {
     const int li = tid & 15, p = tid >> 4;
     const int ga = li >> 2, r = li & 3, ln = 16 * ga + 4 * gp + r;
-    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    if (p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4]) {
-      const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
+    const uint4 c0 = *reinterpret_cast<const uint4 *>(&codes[p][r][32 * ga]);
+    const uint4 c1 = *reinterpret_cast<const uint4 *>(&codes[p][r][32 * ga + 16]);
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    // four 6-bit codes per byte-word to 24 bits, eight of those to six words
+    uint32_t q24[8];
 #pragma unroll
-      for (int s = 0; s < 32; ++s) {
-        const int kap = 32 * ga + s;
-        const float x = p < 4 ? -bp * qp[b_coord(kap)] : -qp[128 + b_coord(kap)];
-        const uint32_t code = fp6_code(query_digit(x, E, r) * b_split_factor(kap));
-        const int bit = 6 * s;
-        w[bit >> 5] |= code << (bit & 31);
-        if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
-      }
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t v = cw[k];
+      q24[k] = (v & 0x3Fu) | ((v >> 2) & 0xFC0u) | ((v >> 4) & 0x3F000u) | ((v >> 6) & 0xFC0000u);
+    }
+    uint32_t w[6];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {  // 4 x 24 bits = 3 words
+      w[3 * k + 0] = q24[4 * k] | (q24[4 * k + 1] << 24);
+      w[3 * k + 1] = (q24[4 * k + 1] >> 8) | (q24[4 * k + 2] << 16);
+      w[3 * k + 2] = (q24[4 * k + 2] >> 16) | (q24[4 * k + 3] << 8);
     }
     uint4 *dst = reinterpret_cast<uint4 *>(qa + ((nt * 5 + p) * 64 + ln) * 8);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], 0u, 0u);
-  }
-  // accumulator start values: per row (digit r) the weighted sum of the
-  // unscaled A values (b_split_weight), for the code planes (summed over
-  // p < 4) and the sign plane.  Lanes 0-127 take one K slot.
-  {
-    float sc4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (tid < 128 && b_reg(tid) < 3) {
-      const int ci = b_coord(tid);
-      const float wgt = b_split_weight(tid);
-#pragma unroll
-      for (int p = 0; p < 5; ++p) {
-        if (!nz[p]) continue;
-        const int E = Ep[p];
-        const float x = p < 4 ? -beta[p] * qp[ci] : -qp[128 + ci];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = wgt * ldexpf(query_digit(x, E, r), E - 4 - 5 * r);
-          if (p < 4) sc4[r] += v; else sq4[r] += v;
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc4[r] = wave_sum(sc4[r]);
-      sq4[r] = wave_sum(sq4[r]);
-    }
-    if (wave < 2 && lane == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        cpart[wave][r] = sc4[r];
-        cpart[wave][4 + r] = sq4[r];
-      }
-    }
-    lds_barrier();
-    if (tid < 8) qa[nwords + NT * 5 * 64 + (nt * 4 + gp) * 8 + tid] = __float_as_uint(cpart[0][tid] + cpart[1][tid]);
-  }
-  if (tid < 5 * 16) {
-    const int li = tid & 15, p = tid >> 4;
-    const int r = li & 3, ln = 16 * (li >> 2) + 4 * gp + r;
     const bool pz = p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4];
     const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
     qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)(pz ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One);
   }
+  if (tid < 8)
+    qa[nwords + NT * 5 * 64 + (nt * 4 + gp) * 8 + tid] =
+        __float_as_uint((spart[0][tid] + spart[1][tid]) + (spart[2][tid] + spart[3][tid]));
   // rows of absent heads (groups of one or two heads) stay zero
   if (g == 0 && G < 4) {
     for (int i = tid; i < (4 - G) * 8; i += 256) qa[nwords + NT * 5 * 64 + G * 8 + i] = 0u;
@@ -505,30 +506,27 @@ __device__ __forceinline__ void transpose_rows(uint32_t &r0, uint32_t &r1, uint3
   r3 = d[1];
 }
 
-// Block ids of the chunk's first kBtCap pages are staged in LDS once, so a
-// tile's page loads depend on no global load and the prefetch of the next
-// tile runs fully in the shadow of the current one.
-constexpr int kBtCap = 1024;
-
-__device__ __forceinline__ int64_t block_of(const int32_t *bts, const int32_t *btab, int pg_first, int pg) {
-  const int i = pg - pg_first;
-  return i < kBtCap ? bts[i] : btab[pg];
+// Block ids of a wave's pages, one per lane: lane j holds page j & 1 of the
+// wave's page pair in tile base + j/2 (32 tiles per register), so a tile's
+// page addresses come from readlane with no memory round trip.  A page past
+// the visible range re-reads its tile's first page (always visible; its
+// tokens are masked), and a tile past the chunk the chunk's first page.
+__device__ __forceinline__ int wave_page_ids(const int32_t *btab, int s0, int s1, int base, int wave, int lane) {
+  const int tile0 = s0 + 128 * (base + (lane >> 1));
+  const int tok = tile0 + 16 * (2 * wave + (lane & 1));
+  const int pg = tile0 >= s1 ? (s0 >> 4) : ((tok < s1 ? tok : tile0) >> 4);
+  return btab[pg];
 }
 
-__device__ __forceinline__ void mfma_load_tile(MfmaLoads &R, const DecodeArgs &a, const int32_t *btab,
-                                               const int32_t *bts, int pg_first, int h, int tok0, int s1,
-                                               int wave, int lane) {
-  const int pg0 = tok0 >> 4;
+// The two pages (block ids b0, b1, uniform) of the wave's page pair: K
+// records (plane lane/16, token lane%16), the scalars, and the value planes.
+__device__ __forceinline__ void mfma_load_tile(MfmaLoads &R, const uint8_t *k_cache, const uint8_t *v_cache,
+                                               int64_t hkv, int h, int b0, int b1, int lane) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    const int k = 2 * wave + kk;
-    // a page past the visible range re-reads the tile's first page (always
-    // visible); its tokens are masked.  The page is the same for the whole
-    // wave, so its address is formed in scalar registers.
-    const int pg = (tok0 + 16 * k < s1) ? pg0 + k : pg0;
-    const int64_t blk = __builtin_amdgcn_readfirstlane((int)block_of(bts, btab, pg_first, pg));
-    const uint8_t *kp = a.k_cache + (blk * a.num_kv_heads + h) * kKPage;
-    const uint8_t *vp = a.v_cache + (blk * a.num_kv_heads + h) * kVPage;
+    const int64_t blk = kk == 0 ? b0 : b1;
+    const uint8_t *kp = k_cache + (blk * hkv + h) * kKPage;
+    const uint8_t *vp = v_cache + (blk * hkv + h) * kVPage;
     R.kr[kk] = *reinterpret_cast<const uint4 *>(kp + 16 * lane);
     R.nk[kk] = *reinterpret_cast<const uint16_t *>(kp + kKNorm + 2 * (lane & 15));
     R.gm[kk] = *reinterpret_cast<const uint16_t *>(kp + kKGamma + 2 * (lane & 15));
@@ -585,7 +583,6 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
 
   __shared__ __align__(16) MfmaTile buf[2];
   __shared__ float lred[4][4];
-  __shared__ int32_t bts[kBtCap];
 
   // query-side operands of the score contraction: tile hh of the group
   v8i Aq[5];
@@ -609,13 +606,25 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
   const float cs = a.scale * kLog2e;
-  const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
-  const int pg_first = s0 >> 4;
-  {
-    const int npg = min((s1 - s0 + 15) >> 4, kBtCap);
-    for (int i = tid; i < npg; i += 256) bts[i] = btab[pg_first + i];
-  }
-  lds_barrier();
+  const int32_t *const btab = a.block_tables + (int64_t)b * a.max_blocks;
+  const uint8_t *const k_cache = a.k_cache, *const v_cache = a.v_cache;
+  const int64_t hkv = a.num_kv_heads;
+  const int ntiles = (s1 - s0 + 127) >> 7;
+  // block ids of this wave's pages, 32 tiles per register (the next 32 are
+  // fetched a block ahead)
+  int ids_cur = wave_page_ids(btab, s0, s1, 0, wave, lane);
+  int ids_nxt = ntiles > 32 ? wave_page_ids(btab, s0, s1, 32, wave, lane) : 0;
+  int ids_base = 0;
+  auto load_tile = [&](MfmaLoads &R, int k) {
+    if (k >= ids_base + 32) {  // uniform
+      ids_cur = ids_nxt;
+      ids_base += 32;
+      if (ids_base + 32 < ntiles) ids_nxt = wave_page_ids(btab, s0, s1, ids_base + 32, wave, lane);
+    }
+    const int j = 2 * (k - ids_base);
+    mfma_load_tile(R, k_cache, v_cache, hkv, h, __builtin_amdgcn_readlane(ids_cur, j),
+                   __builtin_amdgcn_readlane(ids_cur, j + 1), lane);
+  };
 
   float mref[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // shared running maximum per head
   float lsum = 0.0f;
@@ -749,20 +758,19 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  const int ntiles = (s1 - s0 + 127) >> 7;
   MfmaLoads RA, RB;
   float psA = 0.0f, miA = -INFINITY, psB = 0.0f, miB = -INFINITY;
-  mfma_load_tile(RA, a, btab, bts, pg_first, h, s0, s1, wave, lane);
-  if (ntiles > 1) mfma_load_tile(RB, a, btab, bts, pg_first, h, s0 + 128, s1, wave, lane);
+  load_tile(RA, 0);
+  if (ntiles > 1) load_tile(RB, 1);
   scores(RA, s0, buf[0], psA, miA);
   // tile i (odd: RB, buf[1]; even: RA, buf[0]) with the values of tile i-1
   for (int i = 1; i < ntiles; i += 2) {
-    if (i + 1 < ntiles) mfma_load_tile(RA, a, btab, bts, pg_first, h, s0 + 128 * (i + 1), s1, wave, lane);
+    if (i + 1 < ntiles) load_tile(RA, i + 1);
     lds_barrier();
     values(buf[0], psA, miA);
     scores(RB, s0 + 128 * i, buf[1], psB, miB);
     if (i + 1 >= ntiles) break;
-    if (i + 2 < ntiles) mfma_load_tile(RB, a, btab, bts, pg_first, h, s0 + 128 * (i + 2), s1, wave, lane);
+    if (i + 2 < ntiles) load_tile(RB, i + 2);
     lds_barrier();
     values(buf[1], psB, miB);
     scores(RA, s0 + 128 * (i + 1), buf[0], psA, miA);
