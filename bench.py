@@ -15,9 +15,15 @@ that consecutive steps never share data (> 512 MB in total).
 
 Prints one JSON line: the whole step's effective HBM rate (algorithmic bytes /
 time) as ``value``, the encode rate in vectors/s and the attention rate in
-GB/s alongside, the roofline of the dominant kernel from HIP events recorded
-around it on its stream, and the CPU oracle timed on the host for the same
-step.
+GB/s alongside, the decode attention rate on its own over a long context
+(131,072 tokens, 32 query / 4 KV heads) as ``attention_long``, the roofline
+of the dominant kernel from HIP events recorded around it on its stream, and
+the CPU oracle timed on the host for the same step.
+
+Byte counters: ``--counters`` runs only encode launches and a 512 MiB copy,
+for two ``rocprofv3 --pmc`` passes (FETCH_SIZE, then WRITE_SIZE);
+``--traffic-from FETCH_CSV WRITE_CSV`` turns them into profiles/traffic.json
+(scaled by the copy's known traffic).
 """
 
 from __future__ import annotations
@@ -35,7 +41,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 64 lanes x 2 FLOP x 2.4 GHz, packed FP32 disabled
 MALL_BYTES = 256 << 20
 
 T, HQ, HKV, D = 8192, 32, 8, 128
@@ -60,7 +65,7 @@ def encode_flops_per_key():
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("tq_encode.hip", "tq_decode.hip", "tq_common.hpp"):
+    for f in ("tq_encode.hip", "tq_decode.hip", "tq_common.hpp", "tq_mfma.hpp", "tq_internal.h"):
         with open(os.path.join(ROOT, "decode_attention_tq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -79,6 +84,109 @@ def load_traffic(kernel: str):
     if not k or k.get("source_hash") != kernel_source_hash():
         return None
     return k.get("hbm_bytes_per_launch")
+
+
+# Long-context decode: one query per head over 131,072 compressed tokens,
+# 32 query heads over 4 KV heads (the decode attention rate on its own).
+T_LONG, HKV_LONG = 131072, 4
+
+
+def long_context_attention(tq, cb, dev, stream, steps=30, warmup=5):
+    """Decode attention alone over a long compressed context: pages encoded
+    from device-drawn outlier-channel bf16 KV, rotated over enough replicas
+    that consecutive calls share no data through the 256 MB Infinity Cache."""
+    import torch
+    import synth
+    nb = T_LONG // 16
+    per_replica = nb * HKV_LONG * (1088 + 800)
+    R = max(2, -(-2 * MALL_BYTES // per_replica) + 1)
+    rng = np.random.default_rng(4)
+    table = torch.from_numpy(rng.permutation(nb).astype(np.int32)[None, :]).to(dev)
+    slots = (table[0].to(torch.int64)[:, None] * 16 + torch.arange(16, device=dev)).reshape(-1)
+    k = synth.kv_tensor_device(41, T_LONG, HKV_LONG, dev)
+    v = synth.kv_tensor_device(42, T_LONG, HKV_LONG, dev)
+    pools = []
+    for r in range(R):
+        kp = torch.empty((nb, HKV_LONG, 1088), dtype=torch.uint8, device=dev)
+        vp = torch.empty((nb, HKV_LONG, 800), dtype=torch.uint8, device=dev)
+        tq.tq_encode_kv(cb, k, v, slots, kp, vp, stream=stream)
+        pools.append((kp, vp))
+    del k, v
+    q = torch.from_numpy(synth.queries(rng, 1, 1, HQ)).to(dev, torch.bfloat16)
+    clens = torch.tensor([T_LONG], dtype=torch.int32, device=dev)
+    out = torch.empty((1, 1, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_decode_workspace_bytes(cb, 1, 1, HQ, HKV_LONG, T_LONG), dtype=torch.uint8,
+                     device=dev)
+    for i in range(warmup):
+        kp, vp = pools[i % R]
+        tq.tq_decode_attention(cb, q, kp, vp, table, clens, T_LONG, HKV_LONG, out=out, workspace=ws,
+                               stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        kp, vp = pools[(warmup + i) % R]
+        tq.tq_decode_attention(cb, q, kp, vp, table, clens, T_LONG, HKV_LONG, out=out, workspace=ws,
+                               stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    by = T_LONG * HKV_LONG * 118 + nb * 4 + HQ * D * 2 + HQ * D * 4 + 4
+    del pools
+    return {"context": T_LONG, "q_heads": HQ, "kv_heads": HKV_LONG, "replicas": R,
+            "algorithmic_bytes": by, "us": round(us, 2), "GBps": round(by / (us / 1e6) / 1e9, 1),
+            "pct_peak": round(100 * by / (us / 1e6) / 1e9 / HBM_PEAK_GBPS, 2)}
+
+
+def counters_driver(tq, cb, dev, stream, reps, case_slots, launches=8):
+    """Launches for rocprofv3 --pmc passes: encode launches on cold replicas,
+    then plain device copies of 512 MiB (calibration of the byte counters)."""
+    import torch
+    for i in range(launches):
+        r = reps[i % len(reps)]
+        tq.tq_encode_kv(cb, r["k"], r["v"], case_slots, r["kp"], r["vp"], stream=stream)
+    torch.cuda.synchronize()
+    a = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def traffic_from(fetch_csv, write_csv):
+    """profiles/traffic.json from two counter runs of --counters: per encode
+    launch, FETCH_SIZE and WRITE_SIZE scaled by what the same counters read
+    for the 512 MiB copy (its true traffic: 512 MiB read, 512 MiB written)."""
+    import csv
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:
+            per.setdefault((r["Dispatch_Id"], r["Kernel_Name"]), 0.0)
+            per[(r["Dispatch_Id"], r["Kernel_Name"])] += float(r["Counter_Value"])
+        enc = [v for (d, n), v in per.items() if "encode_kernel" in n]
+        # the 512 MiB calibration copies are the largest copies of the run
+        cpy = [v for (d, n), v in per.items() if "copy" in n.lower()]
+        big = max(cpy)
+        cpy = [v for v in cpy if v >= 0.5 * big]
+        return sorted(enc), sorted(cpy)
+    ef, cf = load(fetch_csv, "FETCH_SIZE")
+    ew, cw = load(write_csv, "WRITE_SIZE")
+    true = 512 << 20
+    f_scale = true / cf[len(cf) // 2]
+    w_scale = true / cw[len(cw) // 2]
+    fetch = ef[len(ef) // 2] * f_scale
+    write = ew[len(ew) // 2] * w_scale
+    enc_b, _ = algorithmic_bytes()
+    rec = {"encode_kernel": {"source_hash": kernel_source_hash(), "hbm_bytes_per_launch": round(fetch + write),
+                             "fetch_bytes": round(fetch), "write_bytes": round(write),
+                             "algorithmic_bytes": enc_b,
+                             "copy_calibration": {"fetch_bytes_per_counter_unit": f_scale,
+                                                  "write_bytes_per_counter_unit": w_scale}}}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(case, target_s=10.0, max_s=30.0):
@@ -117,7 +225,15 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run the launches that the byte-counter passes profile")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two counter runs of --counters")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the method's multi-GPU sharding is described, not built)", file=sys.stderr)
@@ -151,6 +267,9 @@ def main():
     ws = torch.empty(tq.tq_decode_workspace_bytes(cb, 1, 1, HQ, HKV, T), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.counters:
+        counters_driver(tq, cb, dev, stream, reps, slots)
+        return
 
     def step(i, ev=None):
         r = reps[i % R]
@@ -194,8 +313,9 @@ def main():
         roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "avg_launch_us": round(dur_ms * 1e3, 2),
-                "alu_tflops": round(T * HKV * encode_flops_per_key() / (dur_ms / 1e3) / 1e12, 2),
-                "alu_peak_tflops": FP32_VALU_PEAK_TFLOPS}
+                # key-path work counted as fp32 FLOPs (QJL projection, rotations);
+                # the kernel runs the products on the matrix cores
+                "nominal_key_tflops": round(T * HKV * encode_flops_per_key() / (dur_ms / 1e3) / 1e12, 2)}
     else:
         name, dur_ms, traffic = "attention (prep+split+merge)", dec_ms, load_traffic("attention")
         achieved = dec_b / (dur_ms / 1e3) / 1e9
@@ -218,6 +338,9 @@ def main():
         "attention_us": round(dec_ms * 1e3, 2),
         "roofline": roof,
     }
+    if not args.no_long_context:
+        del reps
+        line["attention_long"] = long_context_attention(tq, cb, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(line), flush=True)

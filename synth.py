@@ -50,6 +50,22 @@ def kv_tensor(rng: np.random.Generator, T: int, Hkv: int, d: int = HEAD_DIM, *,
     return round_to_bf16(x) if bf16 else x
 
 
+def kv_tensor_device(seed: int, T: int, Hkv: int, device, d: int = HEAD_DIM, outliers: int = 3):
+    """The GQA recipe of ``kv_tensor`` drawn on the device with torch's
+    seeded generator (for workloads too large to draw on the host): a bf16
+    [T][Hkv][d] tensor, per-(KV head, channel) scale exp(N(0, 1)) and
+    ``outliers`` channels x20 per KV head.  Not bit-identical to
+    ``kv_tensor``; used for timing only."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    scale = torch.exp(torch.randn((Hkv, d), generator=g, device=device))
+    for h in range(Hkv):
+        ch = torch.randperm(d, generator=g, device=device)[:outliers]
+        scale[h, ch] *= 20.0
+    x = torch.randn((T, Hkv, d), generator=g, device=device)
+    return (x * scale[None]).to(torch.bfloat16)
+
+
 def queries(rng: np.random.Generator, B: int, q_len: int, Hq: int, d: int = HEAD_DIM,
             bf16: bool = True) -> np.ndarray:
     q = rng.standard_normal((B, q_len, Hq, d)).astype(np.float32)
