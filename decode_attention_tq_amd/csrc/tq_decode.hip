@@ -18,6 +18,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "tq_mfma.hpp"
 
 namespace tq {
@@ -87,7 +89,8 @@ __device__ void merge_row(const DecodeArgs &a, int64_t r, int lane) {
 // forms half of (S q)_i from S[i][64*half .. +64) held in registers; wave 0
 // rotates q.  For the matrix-core pass the workgroup also writes its head's
 // rows of the score contraction's A operands (see split_mfma_kernel): rows
-// (head, digit r).  With 2^E bounding |x| over the head, Y = rint(x 2^(19-E))
+// (head, digit r), for x the plane's values times scale * log2(e) (scores in
+// log2 units).  With 2^E bounding |x| over the head, Y = rint(x 2^(19-E))
 // is written in balanced base 32, Y = d0 2^15 + d1 2^10 + d2 2^5 + d3 with
 // every |d_r| <= 16, stored as the fp6 e2m3 code of d_r/8 (exact), and row r
 // carries it with scale 2^(E-4-5r+3): x to 2^-20 of the head's largest
@@ -141,13 +144,14 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   float beta[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
+  const float cs = a.scale * kLog2e;  // scores come out in log2 units
   // per plane: 2^E bounds |x| (E >= -100 keeps every scale encodable); no
   // digits at all when the plane is zero
   int Ep[5];
   bool nz[5];
 #pragma unroll
   for (int p = 0; p < 5; ++p) {
-    const float M = p < 4 ? fabsf(beta[p]) * hmax[0] : hmax[1];
+    const float M = cs * (p < 4 ? fabsf(beta[p]) * hmax[0] : hmax[1]);
     nz[p] = M > 0.0f;
     Ep[p] = max(bound_exponent(M), -100);
   }
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
     const bool pz = p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4];
     const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
     const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-    const float x = p < 4 ? -bp * qp[b_coord(kap)] : -qp[128 + b_coord(kap)];
+    const float x = cs * (p < 4 ? -bp * qp[b_coord(kap)] : -qp[128 + b_coord(kap)]);
     // Y = rint(x 2^(19-E)) = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16
     const float y = pz ? rintf(ldexpf(x, 19 - E)) : 0.0f;
     const float d0 = rintf(y * 0x1p-15f);
@@ -433,36 +437,46 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 }
 
 // ---- 2'. split pass on the matrix cores (single-query decode, G <= 8) -----
-// Both contractions run on the scaled f8f6f4 MFMA, with the stored bits as
-// the fp4 operand (B = 1 - 2 bit, one and_or per 8 values) and the float side
-// split into four digits in four A rows: the query side in balanced base 32
-// as fp6 codes (see query_prep_kernel; fp6 x fp4 runs at twice the fp8 x fp4
-// rate), the weights in base 16 as fp8.  With the bit-plane form
-// of the levels, c[idx] = -(beta0 B0 + beta1 B1 + beta2 B2 + beta3 Bx) where
-// Bx = B0 B1 B2 is the plane of b0^b1^b2:
+// Both contractions run on the scaled f8f6f4 MFMA with the stored bits as the
+// fp4 operand (b_split: one and_or per 8 values) and the float side split
+// into four digits in four A rows: the query side in balanced base 32 as fp6
+// codes (see query_prep_kernel, which also folds scale * log2(e) in, so that
+// scores come out in log2 units), the weights in base 16 as fp8 codes.
+// With the bit-plane form of the levels, c[idx] = -(beta0 B0 + beta1 B1 +
+// beta2 B2 + beta3 Bx) where Bx = B0 B1 B2 is the plane of b0^b1^b2:
 //   <q', c[idx]> = sum_p <-beta_p q', B_p>        (4 MFMAs per page)
 //   gamma <s, sigma> = gamma <-s, B_sign>          (1 MFMA per page)
 //   o' = -sum_p beta_p sum_j w_j B_p,j  with w_j = p_j n_v,j  (4 planes)
-// A workgroup (4 waves) walks its chunk in tiles of 128 tokens (8 pages).
-// Wave w scores pages 2w, 2w+1 of a tile (MFMA K-block w of the value
-// contraction), keeps the block maximum m_w (integer, log2 units) and writes
-// the digits of w_j / 2^E_w to LDS; 2^(E_w + m_w - m) enters as the E8M0
-// scale of K-block w, so no cross-wave agreement on exponents is needed.
-// The value contraction is split by coordinates: wave w owns N-tiles 2w and
-// 2w+1 (32 coordinates) for all four planes.  The running maximum m is
-// shared by all waves and moves only when a tile exceeds it by 2^64.
-struct MfmaTile {
-  uint8_t wq[4][4][128];   // [head][digit][K] fp8 digits of w
-  uint32_t vs[4][400];     // [page pair][plane * 128 + coord], padded
-  float mi[4][4];          // [head][K-block] block maxima (log2 units)
-  int ex[4][4];            // [head][K-block] digit exponents
-};
+//
+// A workgroup serves one chunk of one KV head and all of its G query heads:
+// T = ceil(G/4) head tiles of four heads, 4T waves.  The chunk is walked in
+// tiles of 128 tokens (8 pages, K-blocks of two pages).  Wave w scores the
+// page pair w%4 (K-block w%4) for head tile w/4, and in the value
+// contraction owns 32/T coordinates for all T head tiles, so every wave runs
+// 10 score and 8 value MFMAs per tile and builds each bit-plane operand once.
+// Pages go HBM -> registers (two tiles ahead) -> LDS (three slots); each
+// barrier interval holds the scores of tile i and the values of tile i-1.
+//
+// Weights: a scoring wave keeps a reference R per head (log2 units, moved
+// only when a score exceeds it by 64), p = 2^(score - R), w = p n_v, and
+// X = rint(w 2^(141-ex)) < 2^15 for ex the exponent field of the block's
+// largest w.  The four base-16 digits of X are written as fp8 codes 0..15,
+// which are exactly d 2^-9 (subnormals and the first binade), so the digit
+// needs no conversion: row r's E8M0 scale 2^(ex - 120 - 4r + R - Racc)
+// restores its place value relative to the accumulator reference Racc.
+// The value operand from b_split has the affine form alpha_v + beta_v b per
+// register v; digits of K slots in registers 0..2 are negated (fp8 sign bit)
+// and the offsets become one per-row correction, sum_k c_v A_k with
+// c = (-5, -3, -1, 0) per register, taken by two MFMAs against constant
+// operands (-4, -3, -1, 0) and (-1, 0, 0, 0): acc_p + corr = sum w (1 - 2b).
 
-struct MfmaLoads {
-  uint4 kr[2];                 // K page records: plane lane/16, token lane%16
-  uint32_t nk[2], gm[2], nv[2];
-  uint4 vp[2];                 // value planes of the wave's page pair (lanes < 48)
-};
+constexpr int kTilePages = 8;
+constexpr int kMaxSplitTiles = 64;          // tiles of 128 tokens per workgroup (chunks up to 8192 tokens)
+constexpr int kKRec = 1120;                 // per page: K planes and signs (1024) | K n (32) | K gamma (32) | V n (32)
+constexpr int kVPair = 4 * 512 + 64;        // per page pair: [plane][coordinate] words (page a | page b << 16);
+                                            // plane 3 takes the spare lanes' stores, +64 spreads the pairs over the banks
+constexpr int kWqRow = 144;                 // 128 fp8 digits of one A row, padded
+constexpr int kRefStep = 64;                // a reference moves when exceeded by 2^64
 
 // Maximum over the 16 lanes of a row on integer keys that order like the
 // floats (NaN-free inputs): no canonicalisation between the DPP steps.
@@ -486,325 +500,563 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += xchg4(v);
   return v + xchg8(v);
 }
-__device__ __forceinline__ float half_bits(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
-__device__ __forceinline__ float sel4(const float (&v)[4], int i) {
-  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-}
+__device__ __forceinline__ float half_lo(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 __device__ __forceinline__ float uniform(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
-
-// 4x4 transpose of (16-lane row, register): row g register j -> row j register g.
-__device__ __forceinline__ void transpose_rows(uint32_t &r0, uint32_t &r1, uint32_t &r2, uint32_t &r3) {
-  const auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
-  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  r0 = c[0];
-  r1 = c[1];
-  r2 = d[0];
-  r3 = d[1];
+// A value the compiler keeps in a vector register (wave-uniform constants of
+// three-operand bit operations, which cannot take two scalar operands).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
-// Block ids of a wave's pages, one per lane: lane j holds page j & 1 of the
-// wave's page pair in tile base + j/2 (32 tiles per register), so a tile's
-// page addresses come from readlane with no memory round trip.  A page past
-// the visible range re-reads its tile's first page (always visible; its
-// tokens are masked), and a tile past the chunk the chunk's first page.
-__device__ __forceinline__ int wave_page_ids(const int32_t *btab, int s0, int s1, int base, int wave, int lane) {
-  const int tile0 = s0 + 128 * (base + (lane >> 1));
-  const int tok = tile0 + 16 * (2 * wave + (lane & 1));
-  const int pg = tile0 >= s1 ? (s0 >> 4) : ((tok < s1 ? tok : tile0) >> 4);
-  return btab[pg];
-}
-
-// The two pages (block ids b0, b1, uniform) of the wave's page pair: K
-// records (plane lane/16, token lane%16), the scalars, and the value planes.
-__device__ __forceinline__ void mfma_load_tile(MfmaLoads &R, const uint8_t *k_cache, const uint8_t *v_cache,
-                                               int64_t hkv, int h, int b0, int b1, int lane) {
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int64_t blk = kk == 0 ? b0 : b1;
-    const uint8_t *kp = k_cache + (blk * hkv + h) * kKPage;
-    const uint8_t *vp = v_cache + (blk * hkv + h) * kVPage;
-    R.kr[kk] = *reinterpret_cast<const uint4 *>(kp + 16 * lane);
-    R.nk[kk] = *reinterpret_cast<const uint16_t *>(kp + kKNorm + 2 * (lane & 15));
-    R.gm[kk] = *reinterpret_cast<const uint16_t *>(kp + kKGamma + 2 * (lane & 15));
-    R.nv[kk] = *reinterpret_cast<const uint16_t *>(vp + kVNorm + 2 * (lane & 15));
-    // value planes of the wave's own page pair: lane < 48 takes 16 bytes
-    if (lane < 48) R.vp[kk] = *reinterpret_cast<const uint4 *>(vp + kKPlane * (lane >> 4) + 16 * (lane & 15));
-  }
-}
-
-// A workgroup serves one chunk of one KV head and up to four of its query
-// heads (one operand tile); eight heads per KV head take two workgroups whose
-// dispatch ids differ by 8, so that they run on the same XCD at the same time
-// and the second reads the pages from L2.  Each barrier interval holds two
-// independent chains for the scheduler to interleave: the value contraction
-// of tile i-1 and the scores and weight digits of tile i.
-struct SplitItem {
-  int b, h, hh, split;
-  bool ok;
+// b_split with its constants in vector registers: one v_and_or per register.
+struct BSplitK {
+  uint32_t m0, m1, m2, m3, c0, c1, c3;
 };
-__device__ __forceinline__ SplitItem split_item(const DecodeArgs &a, int halves) {
-  const int lin = blockIdx.x;
-  SplitItem it;
-  int item;
-  if (halves == 2) {
-    item = 8 * (lin >> 4) + (lin & 7);
-    it.hh = (lin >> 3) & 1;
-  } else {
-    item = lin;
-    it.hh = 0;
-  }
-  const int per_seq = a.num_kv_heads * a.num_splits;
-  it.ok = item < a.num_seqs * per_seq;
-  item = it.ok ? item : 0;
-  it.b = item / per_seq;
-  it.h = (item / a.num_splits) % a.num_kv_heads;
-  it.split = item % a.num_splits;
-  return it;
+__device__ __forceinline__ BSplitK bsplit_consts() {
+  return BSplitK{in_vgpr(0x11111111u), in_vgpr(0x22222222u), in_vgpr(0x44444444u), in_vgpr(0x88888888u),
+                 in_vgpr(0x66666666u), in_vgpr(0x44444444u), in_vgpr(0x22222222u)};
+}
+__device__ __forceinline__ v8i bsplit(uint32_t P, const BSplitK &k) {
+  v8i b;
+  b[0] = (int)((P & k.m0) | k.c0);
+  b[1] = (int)((P & k.m1) | k.c1);
+  b[2] = (int)(P & k.m2);
+  b[3] = (int)((P & k.m3) | k.c3);
+  b[4] = b[5] = b[6] = b[7] = 0;
+  return b;
 }
 
-__global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
-  const int halves = a.qk_tiles;
-  const SplitItem item = split_item(a, halves);
-  if (!item.ok) return;  // uniform: padding of the interleaved grid
-  const int b = item.b, h = item.h, hh = item.hh, split = item.split;
+// Maximum over the 16 lanes of a row for non-negative integer keys (0 is
+// the identity, so the DPP moves fold into the max).
+__device__ __forceinline__ int row_max16_nonneg(int k) {
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  k = max(k, __builtin_amdgcn_update_dpp(0, k, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return max(k, __builtin_amdgcn_update_dpp(0, k, 0x140, 0xF, 0xF, true));  // row_mirror
+}
+
+// Loads of one tile by one wave into registers and their copies into LDS,
+// addressed from a page base in scalar registers plus a fixed lane offset.
+// Per page, the K part (used by the scores): code planes and signs (64
+// lanes x 16 bytes), the K norms and residual norms (16 lanes x 4 bytes)
+// and the V norms (8 lanes x 4 bytes); the V part (used by the value
+// contraction): the V code planes (48 lanes x 16 bytes).  The K part of
+// tile t is fetched three intervals ahead and copied to LDS one interval
+// ahead; the V part is fetched two intervals ahead and copied in the
+// interval of its own tile, so two LDS buffers of each suffice.  Role 2
+// (T = 1) takes both parts of its page pair; with T = 2, role 0 (waves 0..3)
+// takes the K planes and role 1 (waves 4..7) the rest of page pair w%4.  The
+// role is a compile-time parameter, so that every loaded register has one
+// producer and the counters of outstanding loads stay exact.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// A wave-uniform byte pointer, kept in scalar registers so that loads take
+// the scalar-base plus 32-bit lane-offset form.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+}
+typedef __attribute__((address_space(1))) const uint8_t gbyte;
+template <typename V>
+__device__ __forceinline__ V load_at(const uint8_t *base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) V *>(
+      reinterpret_cast<gbyte *>(reinterpret_cast<uint64_t>(base)) + off);
+}
+template <int R>
+struct StageSet {
+  u32x4 a[2];      // K planes (roles 0, 2) or V planes (role 1)
+  u32x4 b[2];      // V planes (role 2)
+  uint32_t t[4];   // K norm words, V norm words (roles 1, 2)
+};
+struct StagePtrs {
+  const uint8_t *k_cache, *v_cache;
+  int64_t hkv;
+  int h, pr;
+  uint32_t o16, o48, o16w, o8w;  // 16 lane; 16 (lane % 48); 4 (lane % 16); 4 (lane % 8)
+};
+template <int R>
+__device__ __forceinline__ void load_k_part(StageSet<R> &S, const StagePtrs &P, int b0, int b1) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t blk = (e ? b1 : b0) * P.hkv + P.h;
+    const uint8_t *kp = uniform_ptr(P.k_cache + blk * kKPage);
+    if (R != 1) S.a[e] = load_at<u32x4>(kp, P.o16);
+    if (R != 0) {
+      S.t[e] = load_at<uint32_t>(kp + kKNorm, P.o16w);
+      S.t[2 + e] = load_at<uint32_t>(uniform_ptr(P.v_cache + blk * kVPage + kVNorm), P.o8w);
+    }
+  }
+}
+template <int R>
+__device__ __forceinline__ void load_v_part(StageSet<R> &S, const StagePtrs &P, int b0, int b1) {
+  if (R == 0) return;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int64_t blk = (e ? b1 : b0) * P.hkv + P.h;
+    const u32x4 v = load_at<u32x4>(uniform_ptr(P.v_cache + blk * kVPage), P.o48);
+    if (R == 2) S.b[e] = v;
+    else S.a[e] = v;
+  }
+}
+template <int R>
+__device__ __forceinline__ void store_k_part(uint8_t *kbuf, const StageSet<R> &S, const StagePtrs &P, int lane) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    uint8_t *rec = kbuf + kKRec * (2 * P.pr + e);
+    if (R != 1) *reinterpret_cast<u32x4 *>(rec + P.o16) = S.a[e];
+    if (R != 0) {  // lanes 16.. and 8.. repeat the words of lanes l % 16, l % 8 (no lane branches)
+      *reinterpret_cast<uint32_t *>(rec + 1024 + P.o16w) = S.t[e];
+      *reinterpret_cast<uint32_t *>(rec + 1088 + P.o8w) = S.t[2 + e];
+    }
+  }
+}
+// V planes of the page pair, interleaved: word (plane, coordinate c) holds
+// page a's 16 token bits in its low half and page b's in its high half.
+template <int R>
+__device__ __forceinline__ void store_v_part(uint8_t *vbuf, const StageSet<R> &S, const StagePtrs &P, int lane) {
+  if (R == 0) return;
+  const u32x4 va = R == 2 ? S.b[0] : S.a[0], vb = R == 2 ? S.b[1] : S.a[1];
+  u32x4 lo, hi;
+  lo[0] = __builtin_amdgcn_perm(vb[0], va[0], 0x05040100u);
+  lo[1] = __builtin_amdgcn_perm(vb[0], va[0], 0x07060302u);
+  lo[2] = __builtin_amdgcn_perm(vb[1], va[1], 0x05040100u);
+  lo[3] = __builtin_amdgcn_perm(vb[1], va[1], 0x07060302u);
+  hi[0] = __builtin_amdgcn_perm(vb[2], va[2], 0x05040100u);
+  hi[1] = __builtin_amdgcn_perm(vb[2], va[2], 0x07060302u);
+  hi[2] = __builtin_amdgcn_perm(vb[3], va[3], 0x05040100u);
+  hi[3] = __builtin_amdgcn_perm(vb[3], va[3], 0x07060302u);
+  // lane: plane lane/16, coordinates 8 (lane % 16) .. +7
+  uint8_t *dst = vbuf + kVPair * P.pr + 512 * (lane >> 4) + 32 * (lane & 15);  // lanes 48..: spare plane
+  *reinterpret_cast<u32x4 *>(dst) = lo;
+  *reinterpret_cast<u32x4 *>(dst + 16) = hi;
+}
+
+template <int T>
+struct SplitLds {
+  int ids[kMaxSplitTiles][kTilePages];      // block ids of the chunk's pages
+  uint8_t kbuf[2][kTilePages * kKRec];
+  uint8_t vbuf[2][4 * kVPair];
+  uint8_t wq[2][T][16][kWqRow];  // [buffer][head tile][head * 4 + digit][K slot] fp8 digits
+  int2 stats[2][T][4][4];        // [buffer][head tile][head][K-block]: (exponent field, R bits)
+  float lred[T][4][4][2];        // [head tile][head][K-block]: (probability sum, R)
+  float cred[4 * T][T][4][4];    // [wave][head tile][head][digit]: correction partials
+};
+
+template <bool B>
+using flag = std::integral_constant<bool, B>;
+
+template <int T, int R>
+__device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, SplitLds<T> &sm) {
+  constexpr int NW = 4 * T;   // waves
+  constexpr int NJ = 2 / T;   // value N-tiles (16 coordinates) per wave
+  const int per_seq = a.num_kv_heads * a.num_splits;
+  const int item = blockIdx.x;
+  if (item >= a.num_seqs * per_seq) return;
+  const int b = item / per_seq;
+  const int h = (item / a.num_splits) % a.num_kv_heads;
+  const int split = item % a.num_splits;
   const int L = clamped_context(a, b);
   const int s0 = split * a.split_tokens;
   const int s1 = min(s0 + a.split_tokens, L);
   if (s0 >= s1) return;  // uniform
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int su = wave >> 2, sq = wave & 3;  // scoring: head tile, page pair (K-block)
   const int t16 = lane & 15, grow = lane >> 4;
   const int64_t grp = (int64_t)b * a.num_kv_heads + h;
   const int G = a.group;
+  const int ntiles = min((s1 - s0 + 127) >> 7, kMaxSplitTiles);  // the host caps chunks at 64 tiles
 
-  __shared__ __align__(16) MfmaTile buf[2];
-  __shared__ float lred[4][4];
+  // block ids of the chunk's pages; a page past the visible range re-reads
+  // its tile's first page (always visible; its tokens are masked)
+  {
+    const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
+    for (int idx = tid; idx < ntiles * kTilePages; idx += 64 * NW) {
+      const int tile0 = s0 + 128 * (idx >> 3);
+      const int tok = tile0 + 16 * (idx & 7);
+      sm.ids[idx >> 3][idx & 7] = btab[(tok < s1 ? tok : tile0) >> 4];
+    }
+  }
 
-  // query-side operands of the score contraction: tile hh of the group
+  // query-side operands of the score contraction: head tile su
   v8i Aq[5];
   int scq[5];
   v4f cinit, qinit;  // accumulator start values (see b_split)
   {
-    const uint32_t *qa = a.qa + grp * (int64_t)(halves * (5 * 64 * 9 + 32));
+    const uint32_t *qa = a.qa + grp * (int64_t)(T * (5 * 64 * 9 + 32));
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((hh * 5 + p) * 64 + lane) * 8);
+      const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((su * 5 + p) * 64 + lane) * 8);
       const uint4 u0 = src[0];
       const uint2 u1 = *reinterpret_cast<const uint2 *>(src + 1);
       Aq[p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, 0, 0};
-      scq[p] = (int)qa[halves * 5 * 64 * 8 + (hh * 5 + p) * 64 + lane];
+      scq[p] = (int)qa[T * 5 * 64 * 8 + (su * 5 + p) * 64 + lane];
     }
-    const float *ci = reinterpret_cast<const float *>(qa + halves * 5 * 64 * 9) + (hh * 4 + grow) * 8;
+    const float *ci = reinterpret_cast<const float *>(qa + T * 5 * 64 * 9) + (su * 4 + grow) * 8;
     cinit = v4f{ci[0], ci[1], ci[2], ci[3]};
     qinit = v4f{ci[4], ci[5], ci[6], ci[7]};
   }
   float beta[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
-  const float cs = a.scale * kLog2e;
-  const int32_t *const btab = a.block_tables + (int64_t)b * a.max_blocks;
-  const uint8_t *const k_cache = a.k_cache, *const v_cache = a.v_cache;
-  const int64_t hkv = a.num_kv_heads;
-  const int ntiles = (s1 - s0 + 127) >> 7;
-  // block ids of this wave's pages, 32 tiles per register (the next 32 are
-  // fetched a block ahead)
-  int ids_cur = wave_page_ids(btab, s0, s1, 0, wave, lane);
-  int ids_nxt = ntiles > 32 ? wave_page_ids(btab, s0, s1, 32, wave, lane) : 0;
-  int ids_base = 0;
-  auto load_tile = [&](MfmaLoads &R, int k) {
-    if (k >= ids_base + 32) {  // uniform
-      ids_cur = ids_nxt;
-      ids_base += 32;
-      if (ids_base + 32 < ntiles) ids_nxt = wave_page_ids(btab, s0, s1, ids_base + 32, wave, lane);
-    }
-    const int j = 2 * (k - ids_base);
-    mfma_load_tile(R, k_cache, v_cache, hkv, h, __builtin_amdgcn_readlane(ids_cur, j),
-                   __builtin_amdgcn_readlane(ids_cur, j + 1), lane);
+  const BSplitK bk = bsplit_consts();
+  const uint32_t nib = in_vgpr(0x0F0F0F0Fu);
+  // fp8 sign of the digits of K slots held by b_split registers 0..2: the
+  // lane's token t sits in register t & 3
+  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80808080u);
+  const int kap0 = 8 * (t16 & 3) + (t16 >> 2);  // K slot of token t16 of the pair's first page
+  const StagePtrs sp{a.k_cache, a.v_cache, (int64_t)a.num_kv_heads, h, sq, 16u * (uint32_t)lane,
+                     16u * (uint32_t)(lane % 48), 4u * (uint32_t)t16, 4u * (uint32_t)(lane & 7)};
+  auto pair_ids = [&](int k, int &b0, int &b1) __attribute__((always_inline)) {
+    const int2 v = *reinterpret_cast<const int2 *>(&sm.ids[k][2 * sq]);
+    b0 = __builtin_amdgcn_readfirstlane(v.x);
+    b1 = __builtin_amdgcn_readfirstlane(v.y);
   };
 
-  float mref[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // shared running maximum per head
-  float lsum = 0.0f;
-  v4f acc[4][2];
+  // scoring state (lane: head grow of tile su, token t16)
+  float rl = -INFINITY;  // reference R of the lane's head
+  float lsum = 0.0f;     // sum of p relative to rl
+  // value state (lane: A row (head gA, digit rA), K-block kb; C rows head grow)
+  const int gA = t16 >> 2, rA = lane & 3, kb = grow;
+  // Racc per head tile, in two per-lane copies: of head gA (A rows) and of
+  // head grow (C rows); both follow the same rule on the same statistics
+  float raA[T], raC[T];
+  v4f acc[T][4][NJ];
+  v4f corr[T];
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+  for (int u = 0; u < T; ++u) {
+    corr[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    raA[u] = raC[u] = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  const int gA = t16 >> 2, rA = lane & 3, kb = grow;  // A-operand row and scale block of this lane
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[u][p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  // Scores of pages 2*wave, 2*wave+1 of the tile at tok0 (lane: head grow,
-  // token t16), their block maximum and the weight digits, into Bf; returns
-  // the lane's probability sum and block maximum through ps, mi.  The matrix
-  // ops write all 64 lanes whatever the exec mask, so they must never sit
-  // under a lane-dependent branch: every lane computes its score, and keys
-  // past the visible range are masked afterwards with a select.
-  auto scores = [&](const MfmaLoads &R, int tok0, MfmaTile &Bf, float &ps, float &mi) {
-    float sc[2];
-    bool valid[2];
+  // E8M0 scales of the weight rows of the tile whose statistics are in
+  // buffer bf, after moving Racc of every head whose block reference
+  // exceeds it by 2^64 (rare: first tile, large score jumps).
+  auto value_scales = [&](int bf, int (&sw)[T]) __attribute__((always_inline)) {
+    int2 st[T];
+    bool move = false;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint32_t r0 = R.kr[kk].x, r1 = R.kr[kk].y, r2 = R.kr[kk].z, r3 = R.kr[kk].w;
-      transpose_rows(r0, r1, r2, r3);  // now plane p's word grow in r_p, signs in r3
-      const v8i B0 = b_split(r0), B1 = b_split(r1), B2 = b_split(r2), Bx = b_split(r0 ^ r1 ^ r2),
-                Bs = b_split(r3);
-      const float nk = half_bits(R.nk[kk] & 0xFFFFu), gm = half_bits(R.gm[kk] & 0xFFFFu);
-      valid[kk] = tok0 + 16 * (2 * wave + kk) + t16 < s1;
-      v4f c = mfma_f6f4(Aq[0], B0, cinit, scq[0]);
-      c = mfma_f6f4(Aq[1], B1, c, scq[1]);
-      c = mfma_f6f4(Aq[2], B2, c, scq[2]);
-      c = mfma_f6f4(Aq[3], Bx, c, scq[3]);
-      const v4f q = mfma_f6f4(Aq[4], Bs, qinit, scq[4]);
-      const float code = (c[0] + c[1]) + (c[2] + c[3]);
-      const float qj = (q[0] + q[1]) + (q[2] + q[3]);
-      float raw = cs * nk * fmaf(gm, qj, code);
-      // pin the score (and the matrix ops feeding it) to the unconditional
-      // path: otherwise they may be sunk into the branch of the select below
-      asm volatile("" : "+v"(raw));
-      sc[kk] = valid[kk] ? raw : -INFINITY;
+    for (int u = 0; u < T; ++u) {
+      st[u] = sm.stats[bf][u][gA][kb];
+      move |= __int_as_float(st[u].y) > raA[u] + (float)kRefStep;
     }
-    mi = ceilf(row_max16(fmaxf(sc[0], sc[1])));
-    float w[2];
-    ps = 0.0f;
+    if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const float p = sc[kk] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[kk] - mi);
-      ps += p;
-      // the norm of a slot past the visible range may hold any bits
-      w[kk] = (valid[kk] && p > 0.0f) ? p * half_bits(R.nv[kk] & 0xFFFFu) : 0.0f;
-    }
-    const float wm = row_max16(fmaxf(w[0], w[1]));
-    const int E = wm > 0.0f ? bound_exponent(wm) : 0;
+      for (int u = 0; u < T; ++u) {
+        float MA = -INFINITY, MC = -INFINITY;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t X = (uint32_t)fminf(rintf(ldexpf(w[kk], 16 - E)), 65535.0f);
-      uint32_t pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)(X >> 12), (float)((X >> 8) & 15u), 0, false);
-      pk = __builtin_amdgcn_cvt_pk_fp8_f32((float)((X >> 4) & 15u), (float)(X & 15u), pk, true);
-      const int kap = b_kappa(32 * wave + 16 * kk + t16);
+        for (int q = 0; q < 4; ++q) {
+          MA = fmaxf(MA, __int_as_float(sm.stats[bf][u][gA][q].y));
+          MC = fmaxf(MC, __int_as_float(sm.stats[bf][u][grow][q].y));
+        }
+        if (MA > raA[u] + (float)kRefStep) raA[u] = MA;
+        float fc = 1.0f;
+        if (MC > raC[u] + (float)kRefStep) {
+          fc = raC[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(raC[u] - MC);
+          raC[u] = MC;
+        }
+        corr[u] *= fc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Bf.wq[grow][r][kap] = (uint8_t)(pk >> (8 * r));
-    }
-    if (t16 == 0) {
-      Bf.mi[grow][wave] = mi;
-      Bf.ex[grow][wave] = E;
-    }
-    // value planes of this wave's page pair: interleave the 16-bit words
-    if (lane < 48) {
-      const uint4 &va = R.vp[0], &vb = R.vp[1];
-      const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
-      uint4 o0, o1;
-      o0.x = __builtin_amdgcn_perm(vb.x, va.x, sel_lo);
-      o0.y = __builtin_amdgcn_perm(vb.x, va.x, sel_hi);
-      o0.z = __builtin_amdgcn_perm(vb.y, va.y, sel_lo);
-      o0.w = __builtin_amdgcn_perm(vb.y, va.y, sel_hi);
-      o1.x = __builtin_amdgcn_perm(vb.z, va.z, sel_lo);
-      o1.y = __builtin_amdgcn_perm(vb.z, va.z, sel_hi);
-      o1.z = __builtin_amdgcn_perm(vb.w, va.w, sel_lo);
-      o1.w = __builtin_amdgcn_perm(vb.w, va.w, sel_hi);
-      uint4 *dst = reinterpret_cast<uint4 *>(&Bf.vs[wave][128 * (lane >> 4) + 8 * (lane & 15)]);
-      dst[0] = o0;
-      dst[1] = o1;
-    }
-  };
-
-  // Value contraction of a tile whose digits are in Bf (after the barrier),
-  // with the lane's probability sum ps and block maximum mi of that tile.
-  auto values = [&](const MfmaTile &Bf, float ps, float mi) {
-    // shared running maximum: moves only when a tile exceeds it by 2^64
-    bool moved = false;
-    float fct[4];
+        for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 m4 = *reinterpret_cast<const float4 *>(&Bf.mi[g][0]);
-      const float Mt = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
-      fct[g] = 1.0f;
-      if (Mt > mref[g] + 64.0f) {
-        fct[g] = __builtin_amdgcn_exp2f(mref[g] - Mt);
-        mref[g] = Mt;
-        moved = true;
+          for (int j = 0; j < NJ; ++j) acc[u][p][j] *= fc;
       }
     }
-    if (moved) {
-      const float f = sel4(fct, grow);
-      lsum *= f;
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[p][j] *= f;
-    }
-    if (ps > 0.0f) lsum += ps * __builtin_amdgcn_exp2f(mi - sel4(mref, grow));
-    // weight operand: row (head gA, digit rA), K-block scale from wave kb
-    const uint4 u0 = *reinterpret_cast<const uint4 *>(&Bf.wq[gA][rA][16 * grow]);
-    const uint4 u1 = *reinterpret_cast<const uint4 *>(&Bf.wq[gA][rA][64 + 16 * grow]);
-    const v8i Aw = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-    const float mb = Bf.mi[gA][kb];
-    int sw = kE8M0One;
-    if (mb != -INFINITY) {
-      const float d = fmaxf(mb - sel4(mref, gA), -300.0f);
-      sw = min(max(Bf.ex[gA][kb] - 4 - 4 * rA + (int)d + kE8M0One, 0), 254);
-    }
-    // this wave's coordinates 32*wave .. +31
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = 16 * (2 * wave + j) + t16;
-      const uint32_t p0 = Bf.vs[grow][col], p1 = Bf.vs[grow][128 + col], p2 = Bf.vs[grow][256 + col];
-      const v8i V0 = b_pm1(p0), V1 = b_pm1(p1), V2 = b_pm1(p2), Vx = b_pm1(p0 ^ p1 ^ p2);
-      acc[0][j] = mfma_f8f4(Aw, V0, acc[0][j], sw);
-      acc[1][j] = mfma_f8f4(Aw, V1, acc[1][j], sw);
-      acc[2][j] = mfma_f8f4(Aw, V2, acc[2][j], sw);
-      acc[3][j] = mfma_f8f4(Aw, Vx, acc[3][j], sw);
+    for (int u = 0; u < T; ++u) {
+      const float d = fmaxf(__int_as_float(st[u].y) - raA[u], -300.0f);  // NaN (both -inf) -> -300
+      sw[u] = min(max(st[u].x + 7 - 4 * rA + (int)d, 0), 254);  // E8M0 of 2^(ex-120-4r+R-Racc)
     }
   };
 
-  MfmaLoads RA, RB;
-  float psA = 0.0f, miA = -INFINITY, psB = 0.0f, miB = -INFINITY;
-  load_tile(RA, 0);
-  if (ntiles > 1) load_tile(RB, 1);
-  scores(RA, s0, buf[0], psA, miA);
-  // tile i (odd: RB, buf[1]; even: RA, buf[0]) with the values of tile i-1
-  for (int i = 1; i < ntiles; i += 2) {
-    if (i + 1 < ntiles) load_tile(RA, i + 1);
-    lds_barrier();
-    values(buf[0], psA, miA);
-    scores(RB, s0 + 128 * i, buf[1], psB, miB);
-    if (i + 1 >= ntiles) break;
-    if (i + 2 < ntiles) load_tile(RB, i + 2);
-    lds_barrier();
-    values(buf[1], psB, miB);
-    scores(RA, s0 + 128 * (i + 1), buf[0], psA, miA);
+  // One barrier interval, for tile k of parity PAR: copy the K part of tile
+  // k+1 (set SK) and the V part of tile k (set SV) to LDS and fetch the K
+  // part of tile k+3 and the V part of tile k+2 into the same sets; then the
+  // scores of tile k and the value contraction of tile k-1 (without scores:
+  // the value contraction of tile k).  The LDS reads, operand expansions and
+  // all matrix ops of both contractions form one block for the scheduler to
+  // interleave; the rare reference moves sit outside it.
+  auto interval = [&](auto HS, auto HV, auto PAR, StageSet<R> &SK, StageSet<R> &SV, int k)
+                      __attribute__((always_inline)) {
+    constexpr bool has_s = decltype(HS)::value, has_v = decltype(HV)::value;
+    constexpr int par = decltype(PAR)::value;
+    constexpr int bs = par, bv = has_s ? (par ^ 1) : par;
+    const int kv = has_s ? k - 1 : k;
+    int sw[T];
+    if constexpr (has_v) value_scales(bv, sw);
+    if constexpr (has_s) {
+      // unconditional copies and fetches (past the chunk's end they repeat its
+      // last tile from L2), so that the counts of outstanding loads are static
+      int k3a, k3b, k2a, k2b;
+      pair_ids(min(k + 3, ntiles - 1), k3a, k3b);
+      pair_ids(min(k + 2, ntiles - 1), k2a, k2b);
+      store_v_part<R>(sm.vbuf[par], SV, sp, lane);
+      store_k_part<R>(sm.kbuf[par ^ 1], SK, sp, lane);
+      load_k_part<R>(SK, sp, k3a, k3b);
+      load_v_part<R>(SV, sp, k2a, k2b);
+    }
+    // LDS reads
+    uint32_t kw[2][4];
+    uint32_t nrm[2][3];  // half bits: n_k, gamma, n_v
+    if constexpr (has_s) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint8_t *rec = sm.kbuf[bs] + kKRec * (2 * sq + e);
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(rec + 16 * t16 + 4 * grow);
+        kw[e][0] = p[0];
+        kw[e][1] = p[64];
+        kw[e][2] = p[128];
+        kw[e][3] = p[192];
+        const uint16_t *nr = reinterpret_cast<const uint16_t *>(rec + 1024);
+        nrm[e][0] = nr[t16];
+        nrm[e][1] = nr[16 + t16];
+        nrm[e][2] = nr[32 + t16];
+      }
+    }
+    v8i Aw[T];
+    uint32_t W[NJ][3];
+    if constexpr (has_v) {
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        const uint8_t *row = &sm.wq[bv][u][4 * gA + rA][0];
+        const uint4 u0 = *reinterpret_cast<const uint4 *>(row + 16 * kb);
+        const uint4 u1 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * kb);
+        Aw[u] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      }
+      const uint32_t *vw = reinterpret_cast<const uint32_t *>(sm.vbuf[bv] + kVPair * kb);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = 16 * (NJ * wave + j) + t16;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) W[j][p] = vw[128 * p + c];
+      }
+    }
+    // matrix ops
+    v4f cc[2], qq[2];
+    if constexpr (has_s) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t w0 = kw[e][0], w1 = kw[e][1], w2 = kw[e][2], w3 = kw[e][3];
+        v4f c = mfma_f6f4(Aq[0], bsplit(w0, bk), cinit, scq[0]);
+        c = mfma_f6f4(Aq[1], bsplit(w1, bk), c, scq[1]);
+        c = mfma_f6f4(Aq[2], bsplit(w2, bk), c, scq[2]);
+        cc[e] = mfma_f6f4(Aq[3], bsplit(w0 ^ w1 ^ w2, bk), c, scq[3]);
+        qq[e] = mfma_f6f4(Aq[4], bsplit(w3, bk), qinit, scq[4]);
+      }
+    }
+    if constexpr (has_v) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t W0 = W[j][0], W1 = W[j][1], W2 = W[j][2];
+        const v8i V0 = bsplit(W0, bk), V1 = bsplit(W1, bk), V2 = bsplit(W2, bk), Vx = bsplit(W0 ^ W1 ^ W2, bk);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          acc[u][0][j] = mfma_f8f4(Aw[u], V0, acc[u][0][j], sw[u]);
+          acc[u][1][j] = mfma_f8f4(Aw[u], V1, acc[u][1][j], sw[u]);
+          acc[u][2][j] = mfma_f8f4(Aw[u], V2, acc[u][2][j], sw[u]);
+          acc[u][3][j] = mfma_f8f4(Aw[u], Vx, acc[u][3][j], sw[u]);
+        }
+      }
+    }
+    // scores of page pair sq for head tile su: weights, digits, statistics.
+    // The common path assumes a full tile and no reference move, so that the
+    // whole interval stays one block; the first tile, the chunk's last
+    // (partial) tile and reference moves redo it at the end.
+    if constexpr (has_s) {
+      float inner[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const v4f &c = cc[e], &q = qq[e];
+        const float code = (c[0] + c[1]) + (c[2] + c[3]);
+        const float qj = (q[0] + q[1]) + (q[2] + q[3]);
+        inner[e] = fmaf(half_lo(nrm[e][1]), qj, code);
+      }
+      const float lsum0 = lsum;
+      auto weights = [&](float x0, float x1, bool v0, bool v1) __attribute__((always_inline)) {
+        const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
+        lsum += p0 + p1;
+        // a slot past the visible range may hold any norm bits
+        const float w0 = v0 ? p0 * half_lo(nrm[0][2]) : 0.0f;
+        const float w1 = v1 ? p1 * half_lo(nrm[1][2]) : 0.0f;
+        const int mk = row_max16_nonneg(max(__float_as_int(w0), __float_as_int(w1)));  // w >= 0
+        const uint32_t exb = max((uint32_t)mk & 0x7F800000u, 14u << 23);
+        const float mult = __uint_as_float(0x86000000u - exb);  // 2^(141 - ex)
+        const uint32_t X0 = __float_as_uint(fmaf(w0, mult, 8388608.0f));
+        const uint32_t X1 = __float_as_uint(fmaf(w1, mult, 8388608.0f));
+        const uint32_t XX = __builtin_amdgcn_perm(X1, X0, 0x05040100u);  // X0 lo16 | X1 lo16 << 16
+        const uint32_t Ev = (XX & nib) | s80;          // digits 3 and 1 of both tokens
+        const uint32_t Od = ((XX >> 4) & nib) | s80;   // digits 2 and 0
+        uint8_t *wr = &sm.wq[bs][su][4 * grow][32 * sq + kap0];
+        wr[3 * kWqRow] = (uint8_t)Ev;
+        wr[3 * kWqRow + 4] = (uint8_t)(Ev >> 16);
+        wr[1 * kWqRow] = (uint8_t)(Ev >> 8);
+        wr[1 * kWqRow + 4] = (uint8_t)(Ev >> 24);
+        wr[2 * kWqRow] = (uint8_t)Od;
+        wr[2 * kWqRow + 4] = (uint8_t)(Od >> 16);
+        wr[0] = (uint8_t)(Od >> 8);
+        wr[4] = (uint8_t)(Od >> 24);
+        // the 16 lanes of a head write the same statistics (no lane branch)
+        sm.stats[bs][su][grow][sq] = make_int2((int)(exb >> 23), __float_as_int(rl));
+      };
+      const float x0 = fmaf(half_lo(nrm[0][0]), inner[0], -rl);
+      const float x1 = fmaf(half_lo(nrm[1][0]), inner[1], -rl);
+      weights(x0, x1, true, true);
+      if constexpr (has_v) {
+        // keep the value matrix ops inside this block (not sunk past the
+        // branch below), where the scheduler overlaps them with the scores
+#pragma unroll
+        for (int u = 0; u < T; ++u)
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[u][p][j]));
+      }
+      const bool partial = s0 + 128 * (k + 1) > s1;  // uniform: the chunk's last tile
+      if (__builtin_amdgcn_ballot_w64(x0 > (float)kRefStep || x1 > (float)kRefStep) || partial) {
+        const int tok0 = s0 + 128 * k + 32 * sq + t16;
+        const bool v0 = tok0 < s1, v1 = tok0 + 16 < s1;
+        const float r0 = v0 ? half_lo(nrm[0][0]) * inner[0] : -INFINITY;
+        const float r1 = v1 ? half_lo(nrm[1][0]) * inner[1] : -INFINITY;
+        // move the reference of the heads that need it (first tile, rare after)
+        const float mh = row_max16(fmaxf(r0, r1));
+        const float nr = fmaxf(rl, ceilf(mh));
+        lsum = lsum0;
+        if (nr > rl && nr - rl > 0.0f) {
+          lsum = rl == -INFINITY ? 0.0f : lsum * __builtin_amdgcn_exp2f(rl - nr);
+          rl = nr;
+        }
+        // rl stays -inf while a head has no visible key
+        weights(r0 == -INFINITY ? -INFINITY : r0 - rl, r1 == -INFINITY ? -INFINITY : r1 - rl, v0, v1);
+      }
+    }
+    if constexpr (has_v) {
+      if (kv % NW == wave) {  // uniform: the offsets of b_split, one wave per tile
+        const v8i C1 = v8i{(int)0xEEEEEEEEu, (int)0xDDDDDDDDu, (int)0xAAAAAAAAu, 0, 0, 0, 0, 0};
+        const v8i C2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          corr[u] = mfma_f8f4(Aw[u], C1, corr[u], sw[u]);
+          corr[u] = mfma_f8f4(Aw[u], C2, corr[u], sw[u]);
+        }
+      }
+    }
+  };
+
+  // zero digits and empty statistics in buffer 1 for the first interval
+  for (int i = tid; i < T * 16 * kWqRow / 4; i += 64 * NW) reinterpret_cast<uint32_t *>(&sm.wq[1][0][0][0])[i] = 0u;
+  if (tid < T * 16) (&sm.stats[1][0][0][0])[tid] = make_int2(0, __float_as_int(-INFINITY));
+  lds_barrier();  // block ids, buffer 1
+  StageSet<R> SA, SB;  // register sets of even and odd tiles
+  {
+    // the order of the intervals before tile 0 (K part of tile j+3, V part
+    // of tile j+2 for j = -3, -2, -1), so that the counts of outstanding
+    // loads at the loop entry match those of the loop itself
+    // (scheduling barriers keep that order)
+    int b0, b1, c0, c1, d0, d1;
+    pair_ids(0, b0, b1);
+    pair_ids(min(1, ntiles - 1), c0, c1);
+    pair_ids(min(2, ntiles - 1), d0, d1);
+    load_k_part<R>(SA, sp, b0, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k_part<R>(SB, sp, c0, c1);
+    load_v_part<R>(SA, sp, b0, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_k_part<R>(sm.kbuf[0], SA, sp, lane);
+    load_k_part<R>(SA, sp, d0, d1);
+    load_v_part<R>(SB, sp, c0, c1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   lds_barrier();
-  if (ntiles & 1)
-    values(buf[0], psA, miA);
+  // Every interval holds both contractions; the first one's value pass
+  // reads the zeroed digit rows of buffer 1 and adds nothing.
+  for (int k = 0; k < ntiles; k += 2) {
+    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 0>{}, SB, SA, k);
+    lds_barrier();
+    if (k + 1 >= ntiles) break;
+    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 1>{}, SA, SB, k + 1);
+    lds_barrier();
+  }
+  if ((ntiles - 1) & 1)
+    interval(flag<false>{}, flag<true>{}, std::integral_constant<int, 1>{}, SA, SB, ntiles - 1);
   else
-    values(buf[1], psB, miB);
+    interval(flag<false>{}, flag<true>{}, std::integral_constant<int, 0>{}, SA, SB, ntiles - 1);
+  // Pin the accumulators here: the matrix ops write all 64 lanes whatever
+  // the exec mask and must not be sunk into the per-head branches below.
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    asm volatile("" : "+v"(corr[u]));
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[u][p][j]));
+  }
 
-  // row sums over the 16 lanes of a head, then over the waves
+  // probability sums per head (scoring lanes), correction partials per wave
   {
     const float ls = row_sum16(lsum);
-    if (t16 == 0) lred[wave][grow] = ls;
+    if (t16 == 0) {
+      sm.lred[su][grow][sq][0] = ls;
+      sm.lred[su][grow][sq][1] = rl;
+    }
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+      if (t16 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.cred[wave][u][grow][i] = corr[u][i];
+      }
   }
   lds_barrier();
-  const int g = 4 * hh + grow;
-  if (g < G) {
+  const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    const int g = 4 * u + grow;  // C rows of this lane: head grow of tile u
+    if (g >= G) continue;
+    const float ra = raC[u];
+    float cs = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cs += sm.cred[wv][u][grow][i];
     float *part = a.partials + ((grp * G + g) * a.num_splits + split) * kPartStride;
     if (wave == 0 && t16 == 0) {
-      part[0] = sel4(mref, grow);
-      part[1] = (lred[0][grow] + lred[1][grow]) + (lred[2][grow] + lred[3][grow]);
+      float l = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float rq = sm.lred[u][grow][q][1];
+        if (rq != -INFINITY) l += sm.lred[u][grow][q][0] * __builtin_amdgcn_exp2f(rq - ra);
+      }
+      part[0] = ra;
+      part[1] = l;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float o = 0.0f;
+    for (int j = 0; j < NJ; ++j) {
+      float o = -bsum * cs;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const v4f &c = acc[p][j];
+        const v4f &c = acc[u][p][j];
         o = fmaf(-beta[p], (c[0] + c[1]) + (c[2] + c[3]), o);
       }
-      part[4 + 16 * (2 * wave + j) + t16] = o;
+      part[4 + 16 * (NJ * wave + j) + t16] = o;
     }
   }
+}
+
+template <int T>
+__global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(DecodeArgs a) {
+  __shared__ __align__(16) SplitLds<T> sm;
+  if (T == 1)
+    split_body<T, 2>(a, sm);
+  else if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)  // uniform: the wave's staging role
+    split_body<T, 0>(a, sm);
+  else
+    split_body<T, 1>(a, sm);
 }
 
 // ---- 3. merge: one wave per output row --------------------------------------
@@ -834,8 +1086,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.qa != nullptr) {  // matrix-core pass: one workgroup per (chunk, KV head, head tile)
     if (a.qk_tiles != 1 && a.qk_tiles != 2) return hipErrorInvalidValue;
     const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_splits;
-    const int64_t wgs = a.qk_tiles == 1 ? items : 2 * ((items + 7) / 8) * 8;
-    hipLaunchKernelGGL(split_mfma_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
+    if (a.qk_tiles == 1)
+      hipLaunchKernelGGL(split_mfma_kernel<1>, dim3((unsigned)items), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)items), dim3(512), 0, stream, a);
   } else if (prefill_uses_mfma(a.q_len, a.group)) {
     e = launch_prefill(a, stream);
     if (e != hipSuccess) return e;

@@ -123,6 +123,9 @@ void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_c
     if (per < 256) per = 256;
     st = (int)per;
   }
+  // the matrix-core decode pass keeps a chunk's block ids in LDS: at most
+  // 64 tiles of 128 tokens per workgroup
+  if (tq::decode_uses_mfma(q_len, group) && st > 8192) st = 8192;
   int ns = max_ctx > 0 ? (max_ctx + st - 1) / st : 1;
   *split_tokens = st;
   *num_splits = ns;

@@ -163,6 +163,8 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
  *   out         device [num_seqs][q_len][num_q_heads][128], dtype out_dtype.
  *   tokens_per_split  0 -> chosen by the library; else a multiple of 256
  *               giving the split-K chunk (results agree to rounding).
+ *               Single-query decode with up to 8 query heads per KV head
+ *               uses at most 8192 tokens per chunk.
  *   workspace   device scratch of tq_decode_workspace_bytes() bytes (same
  *               arguments); contents on entry do not matter.
  * Errors: TQ_ERR_INVALID_ARGUMENT (nulls, Hq % Hkv != 0, q_len < 1,
