@@ -99,11 +99,15 @@ tq::Codebook device_codebook(const tq_codebook *cb) {
 bool dtype_ok(int d) { return d == TQ_F32 || d == TQ_F16 || d == TQ_BF16; }
 
 // ---- split-K planning ------------------------------------------------------
-// Chunks are multiples of 256 tokens (the workgroup's 4 waves x 64 tokens);
-// the automatic choice aims at about 1024 workgroups so that all 256 compute
-// units get several, and depends only on the call's sizes (no device query),
-// so the workspace size and the launch always agree.  Several queries per
-// sequence share a workgroup per block of query positions.
+// Chunks are multiples of 256 tokens.  The automatic choice depends only on
+// the call's sizes (no device query), so the workspace size and the launch
+// always agree, and aims at the 256 compute units of the part: the
+// matrix-core decode pass (single query, up to 8 heads per KV head) at one
+// 8-wave workgroup per unit for 8 heads and two 4-wave workgroups per unit
+// for up to 4 (each workgroup walks its chunk with a fixed start-up cost,
+// so more, shorter chunks only add it), the other passes at about 1024
+// workgroups.  Several queries per sequence share a workgroup per block of
+// query positions.
 void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested,
                  int *split_tokens, int *num_splits) {
   int st;
@@ -116,7 +120,8 @@ void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_c
       per_seq = (q_len + bq - 1) / bq;
     }
     const long rows = (long)num_seqs * per_seq * num_kv_heads;
-    long want = (1024 + rows - 1) / rows;
+    const long target = tq::decode_uses_mfma(q_len, group) ? (group > 4 ? 256 : 512) : 1024;
+    long want = (target + rows - 1) / rows;
     if (want < 1) want = 1;
     long per = (max_ctx + want - 1) / want;
     per = ((per + 255) / 256) * 256;
