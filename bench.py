@@ -230,6 +230,8 @@ def main():
                     help="only run the launches that the byte-counter passes profile")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two counter runs of --counters")
+    ap.add_argument("--long-context-only", action="store_true",
+                    help="only the long-context decode measurement (for kernel traces of it)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -245,8 +247,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case = synth.gqa_case(seed=2, T=T, Hq=HQ, Hkv=HKV)
     cb = tq.tq_codebook_init(128, 3, synth.QJL_SEED, device=dev)
+    if args.long_context_only:
+        print(json.dumps({"attention_long": long_context_attention(
+            tq, cb, dev, torch.cuda.current_stream(dev), steps=args.steps, warmup=args.warmup)}))
+        return
+    case = synth.gqa_case(seed=2, T=T, Hq=HQ, Hkv=HKV)
 
     enc_b, dec_b = algorithmic_bytes()
     per_replica = 2 * T * HKV * D * 2 + case["num_blocks"] * HKV * (1088 + 800)
