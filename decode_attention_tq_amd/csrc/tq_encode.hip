@@ -42,6 +42,7 @@ constexpr int kTok = 16;          // tokens per tile
 constexpr int kTiles = 4;         // tiles per round (one per wave)
 constexpr int kEHalves = 136;     // halves per staged residual row (128 + pad: spreads LDS banks)
 constexpr float kResScale = 256.0f;
+constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum
 
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -88,11 +89,14 @@ __device__ __forceinline__ v4f mfma16(const v8s &a, const v8s &b, const v4f &c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) uint32_t gword;
+
 // Raw inputs of one lane: token l%16, coordinates 32k + 8(l/16) .. +7 for
-// k = 0..3, as 16-bit pieces (pc = 1 for bf16/f16, 3 bf16 pieces for fp32).
+// k = 0..3, as loaded (16 bytes per k for 16-bit inputs, 32 for fp32).
 template <int PC>
 struct In {
-  v8s x[4][PC];
+  u32x4 w[4][PC == 3 ? 2 : 1];
 };
 
 // bf16 pieces hi + mid + lo of a float (exact for normal values).
@@ -109,29 +113,35 @@ __device__ __forceinline__ Split3 split3(float v) {
 }
 
 template <int PC>
-__device__ __forceinline__ void load_in(In<PC> &r, const void *base, int64_t elem0, bool ok) {
+__device__ __forceinline__ void load_in(In<PC> &r, const void *base, int64_t elem0) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if (PC == 1) {
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem0 + 32 * k);
-      r.x[k][0] = __builtin_bit_cast(v8s, u);
+    if constexpr (PC == 1) {
+      r.w[k][0] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem0 + 32 * k);
     } else {
-      float f[8];
+      const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + elem0 + 32 * k);
+      r.w[k][0] = p[0];
+      r.w[k][1] = p[1];
+    }
+  }
+}
+
+// Matrix operands of the raw inputs: 16-bit values as they are, fp32 as
+// three bf16 pieces.  Converted where they are used, so that the loads of a
+// prefetched round are not waited for when they are issued.
+template <int PC>
+__device__ __forceinline__ void pieces(const In<PC> &r, v8s (&x)[4][PC]) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = 0.0f;
-      if (ok) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem0 + 32 * k);
-        const float4 a = p[0], b = p[1];
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-      }
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (PC == 1) {
+      x[k][0] = __builtin_bit_cast(v8s, r.w[k][0]);
+    } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const Split3 sp = split3(f[j]);
-        r.x[k][0][j] = sp.h;
-        r.x[k][1][j] = sp.m;
-        r.x[k][2][j] = sp.l;
+        const Split3 sp = split3(__uint_as_float(r.w[k][j >> 2][j & 3]));
+        x[k][0][j] = sp.h;
+        x[k][1][j] = sp.m;
+        x[k][2][j] = sp.l;
       }
     }
   }
@@ -144,6 +154,7 @@ struct RoundLds {
   _Float16 ehi[kTiles][kTok][kEHalves];         // residual * 256 (hi), slot order
   _Float16 elo[kTiles][kTok][kEHalves];         // remainder (lo)
   int blk[kTiles][kTok], off[kTiles][kTok], valid[kTiles][kTok], leader[kTiles][kTok];
+  float nout[kTiles][kTok][3];                  // n_K, gamma, n_V in fp32 (optional output)
   int full[kTiles];
   int active[kTiles];
 };
@@ -290,47 +301,67 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
   // that its 64 registers are not held through the other phases.
   const uint4 *const shop = reinterpret_cast<const uint4 *>(a.SHop) + wave * 2 * 4 * 2 * 64 + lane;
 
-  auto tile_src = [&](int64_t tile, int64_t &t0, int &h) {
-    h = (int)(tile % H);
-    t0 = (tile / H) * kTok;
-  };
-  // raw inputs of this lane's token (l%16) for the wave's tile of round R
-  auto load_round = [&](int64_t R, In<PC> &ik, In<PC> &iv) {
-    const int64_t tile = R * kTiles + wave;
-    int64_t t0 = 0;
-    int h = 0;
-    tile_src(tile, t0, h);
-    const int64_t t = t0 + l16;
-    const bool ok = tile < num_tiles && t < ntok;
+  // Inputs and slot of this lane's token (l%16) in the wave's tile of round
+  // R.  Every load is unconditional (past the last tile or token the address
+  // repeats the last one and the result is discarded), so that the number
+  // of loads in flight is known at every point and a prefetched round is
+  // waited for only where it is used.
+  auto load_round = [&](int64_t R, In<PC> &ik, In<PC> &iv, int64_t &slot) {
+    int64_t tile = R * kTiles + wave;
+    tile = tile < num_tiles ? tile : num_tiles - 1;
+    const int h = (int)(tile % H);
+    int64_t t = (tile / H) * kTok + l16;
+    t = t < ntok ? t : ntok - 1;
     const int64_t e0 = t * tok_stride + (int64_t)h * head_stride + 8 * lg;
-    load_in<PC>(ik, kin, e0, ok);
-    load_in<PC>(iv, vin, e0, ok);
+    // in the order of use, kept by scheduling barriers: the compiler's
+    // count of loads in flight must agree at the loop entry and its back edge
+    slot = slots[t];
+    __builtin_amdgcn_sched_barrier(0);
+    load_in<PC>(iv, vin, e0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_in<PC>(ik, kin, e0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   In<PC> ik, iv;
-  if ((int64_t)blockIdx.x < nrounds) load_round(blockIdx.x, ik, iv);
+  int64_t slot;
+  load_round(blockIdx.x, ik, iv, slot);  // the grid has at most one workgroup per round
 
   for (int64_t R = blockIdx.x; R < nrounds; R += gridDim.x) {
     const int64_t tile = R * kTiles + wave;
     const bool active = tile < num_tiles;
-    int64_t t0 = 0;
-    int h = 0;
-    tile_src(tile, t0, h);
+    const int64_t t0 = (tile / H) * kTok;
 
-    // slots of the tile: lane t < 16 holds token t
+    // destinations of the tile's tokens (every lane holds that of token l%16);
+    // a skipped token gets a block id no other token has
+    const bool ok = active && t0 + l16 < ntok && slot >= 0;
+    const int blk = ok ? (int)((uint64_t)slot / kBlock) : -1 - l16;
+    const int off = ok ? (int)((uint64_t)slot % kBlock) : 0;
+    const bool in_order = ok && blk == __builtin_amdgcn_readlane(blk, 0) && off == l16;
+    const bool full = (__ballot(in_order) & 0xFFFFull) == 0xFFFFull;  // uniform: one page, in order
     if (lane < kTok) {
-      const int64_t t = t0 + lane;
-      const int64_t slot = (active && t < ntok) ? slots[t] : -1;
-      L.valid[wave][lane] = slot >= 0;
-      L.blk[wave][lane] = slot >= 0 ? (int)(slot / kBlock) : -1;
-      L.off[wave][lane] = slot >= 0 ? (int)(slot % kBlock) : 0;
+      L.valid[wave][lane] = ok;
+      L.blk[wave][lane] = blk;
+      L.off[wave][lane] = off;
     }
-    if (lane == 0) L.active[wave] = active;
+    if (lane == 0) {
+      L.active[wave] = active;
+      L.full[wave] = full;
+    }
+    if (!full) {
+      // pages filled token by token: the first token of each destination block
+      int dup = 0;
+#pragma unroll
+      for (int u = 0; u < kTok - 1; ++u) dup |= (u < l16) & (__builtin_amdgcn_readlane(blk, u) == blk);
+      if (lane < kTok) L.leader[wave][lane] = ok && !dup;
+    }
 
 
     if (active) {
       // ---- values: C = H X^T, lane l reg i = coordinate 16m + 4(l/16) + i, token l%16
       {
+        v8s xv[4][PC];
+        pieces<PC>(iv, xv);
         v4f vy[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -338,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
 #pragma unroll
           for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int pc = 0; pc < PC; ++pc) c = mfma16<kF16>(hop(hs, k, m), iv.x[k][pc], c);
+            for (int pc = 0; pc < PC; ++pc) c = mfma16<kF16>(hop(hs, k, m), xv[k][pc], c);
           vy[m] = c;
         }
         float s2 = 0.0f;
@@ -367,11 +398,13 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         const float nv = sn * kInvSqrt128;
         if (lg == 0) {
           reinterpret_cast<_Float16 *>(L.vimg[wave] + kVNorm)[l16] = to_half_sat(nv);
-          if (norms_out && t0 + l16 < ntok) norms_out[((t0 + l16) * H + h) * 3 + 2] = nv;
+          L.nout[wave][l16][2] = nv;
         }
       }
       // ---- keys: C = X H, lane l reg i = token 4(l/16) + i, coordinate 16n + l%16
       {
+        v8s xk[4][PC];
+        pieces<PC>(ik, xk);
         v4f ky[8];
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
@@ -379,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
 #pragma unroll
           for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int pc = 0; pc < PC; ++pc) c = mfma16<kF16>(ik.x[k][pc], hop(hs, k, n), c);
+            for (int pc = 0; pc < PC; ++pc) c = mfma16<kF16>(xk[k][pc], hop(hs, k, n), c);
           ky[n] = c;
         }
         float sn[4], r256[4], T[4][3];
@@ -436,18 +469,15 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           if (l16 == 0) {
             reinterpret_cast<_Float16 *>(L.kimg[wave] + kKNorm)[tok] = to_half_sat(nk);
             reinterpret_cast<_Float16 *>(L.kimg[wave] + kKGamma)[tok] = to_half_sat(gam);
-            if (norms_out && t0 + tok < ntok) {
-              float *no = norms_out + ((t0 + tok) * H + h) * 3;
-              no[0] = nk;
-              no[1] = gam;
-            }
+            L.nout[wave][tok][0] = nk;
+            L.nout[wave][tok][1] = gam;
           }
         }
       }
     }
-    // the raw inputs are consumed: load the next round's while the
-    // projection and the stores of this one run
-    if (R + gridDim.x < nrounds) load_round(R + gridDim.x, ik, iv);
+    // this wave's projection operands (the table stays in L2), then the
+    // next round's inputs (the last round repeats its own): the projection
+    // waits for the former only
     v8s shi[2][4], slo[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -456,17 +486,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         shi[u][k] = __builtin_bit_cast(v8s, shop[((u * 4 + k) * 2) * 64]);
         slo[u][k] = __builtin_bit_cast(v8s, shop[((u * 4 + k) * 2 + 1) * 64]);
       }
-
-    // leaders of destination blocks and the full-page test, per tile
-    if (lane < kTok) {
-      int lead = L.valid[wave][lane];
-      for (int u = 0; u < lane; ++u)
-        if (L.valid[wave][u] && L.blk[wave][u] == L.blk[wave][lane]) lead = 0;
-      L.leader[wave][lane] = lead;
-      const bool in_order = L.valid[wave][lane] && L.blk[wave][lane] == L.blk[wave][0] && L.off[wave][lane] == lane;
-      const uint64_t all = __ballot(in_order);
-      if (lane == 0) L.full[wave] = (all & 0xFFFFull) == 0xFFFFull;
-    }
+    load_round(R + gridDim.x < nrounds ? R + gridDim.x : R, ik, iv, slot);
     lds_barrier();
 
     // ---- QJL projection: rows 32w .. 32w+31 for the four tiles -------------
@@ -482,6 +502,12 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
     lds_barrier();
 
     // ---- write the round out --------------------------------------------------
+    if (norms_out && tid < kTiles * kTok * 3) {
+      const int tl = tid / (kTok * 3), n = (tid / 3) % kTok, c = tid % 3;
+      const int64_t tt = R * kTiles + tl;
+      const int64_t tok = (tt / H) * kTok + n;
+      if (tt < num_tiles && tok < ntok) norms_out[(tok * H + tt % H) * 3 + c] = L.nout[tl][n][c];
+    }
 #pragma unroll
     for (int tl = 0; tl < kTiles; ++tl) {
       if (!L.active[tl]) continue;  // uniform
@@ -533,13 +559,20 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
             }
             uint8_t *vp = v_cache + ((int64_t)L.blk[tl][j] * H + hh) * kVPage;
             const uintptr_t addr = reinterpret_cast<uintptr_t>(vp + kKPlane * p + 2 * c);
-            uint32_t *w32 = reinterpret_cast<uint32_t *>(addr & ~uintptr_t(3));
+            // a global (not flat) atomic: a pending flat operation would make every
+            // later wait on the memory counters wait for all of them
+            gword *w32 = reinterpret_cast<gword *>(addr & ~uintptr_t(3));
             const int sh = (addr & 2) ? 16 : 0;
             const uint32_t set = bits << sh, clr = (mask & ~bits) << sh;
-            if (clr) atomicAnd(w32, ~clr);
-            if (set) atomicOr(w32, set);
+            if (clr) __hip_atomic_fetch_and(w32, ~clr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (set) __hip_atomic_fetch_or(w32, set, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
+        // the stores in the loops above leave an unbounded count of memory
+        // operations in flight for the compiler, which would then wait for all
+        // of them (the next round's inputs included) at the next use of a
+        // load: wait here, on this path only
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
       }
     }
     lds_barrier();  // the round's LDS state is rewritten by the next round
