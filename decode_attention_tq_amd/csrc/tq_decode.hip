@@ -28,62 +28,6 @@ namespace {
 constexpr int kPartStride = 132;  // m (log2 units), l, pad, pad, acc[128]
 constexpr float kLog2e = 1.4426950408889634f;
 
-// LSE combine of the chunk partials of output row r by one wave, o' = acc'/l,
-// one inverse FWHT, store.  Lane l owns coordinates l and l + 64.  The chunk
-// accumulators are loaded 32 chunks at a time, the first batch issued before
-// the maxima are reduced, so a typical row costs one round trip to memory;
-// lane e computes the weight of chunk base + e and readlane broadcasts it.
-__device__ void merge_row(const DecodeArgs &a, int64_t r, int lane) {
-  const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
-  const int b = (int)(r / per_seq);
-  const int t = (int)((r / a.num_q_heads) % a.q_len);
-  const int L = clamped_context(a, b);
-  const int vis = max(0, L - a.q_len + t + 1);
-  const int ns = (vis + a.split_tokens - 1) / a.split_tokens;
-  const float *part = a.partials + r * a.num_splits * kPartStride;
-  constexpr int kBatch = 32;
-  float v0[kBatch], v1[kBatch];
-  auto load_batch = [&](int base) {
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e) {
-      const float *p = part + (int64_t)max(min(base + e, ns - 1), 0) * kPartStride;
-      v0[e] = p[4 + lane];
-      v1[e] = p[68 + lane];
-    }
-  };
-  if (ns > 0) load_batch(0);
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part[(int64_t)s * kPartStride]);
-  M = wave_max(M);
-  float Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;
-  for (int base = 0; base < ns; base += kBatch) {
-    if (base > 0) load_batch(base);
-    const int se = base + (lane & (kBatch - 1));
-    float f = 0.0f;
-    if (se < ns && lane < kBatch) {
-      const float m = part[(int64_t)se * kPartStride];
-      f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-      Ls = fmaf(f, part[(int64_t)se * kPartStride + 1], Ls);
-    }
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e) {
-      const float fe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), e));  // 0 past ns
-      A0 = fmaf(fe, v0[e], A0);
-      A1 = fmaf(fe, v1[e], A1);
-    }
-  }
-  Ls = wave_sum(Ls);
-  float o0 = 0.0f, o1 = 0.0f;
-  if (Ls > 0.0f) {
-    const float inv = 1.0f / Ls;
-    o0 = A0 * inv;
-    o1 = A1 * inv;
-  }
-  wave_fwht128(o0, o1, lane);
-  store_from_float(a.out, a.out_dtype, r * kHeadDim + lane, o0);
-  store_from_float(a.out, a.out_dtype, r * kHeadDim + 64 + lane, o1);
-}
-
 // ---- 1. query prep: a workgroup per query row --------------------------------
 // Grid (sequence x position x KV head, head of the group).  Thread (i, half)
 // forms half of (S q)_i from S[i][64*half .. +64) held in registers; wave 0
@@ -102,26 +46,34 @@ __device__ __forceinline__ int bound_exponent(float M) {  // M < 2^E for finite 
 }
 
 __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.group;
   const int64_t grp = blockIdx.x;
   const int g = blockIdx.y;
   const int64_t row = grp * G + g;
-  __shared__ float qs[kHeadDim];
+  __shared__ __align__(16) float qs[kHeadDim];
   __shared__ float part[2][kQjlDim];
   __shared__ float qp[256];
-  __shared__ float hmax[2];
-  __shared__ float cpart[2][8];
+  __shared__ float hmax[3];
   if (tid < kHeadDim) qs[tid] = load_as_float(a.q, a.q_dtype, row * kHeadDim + tid);
+  // thread (i, half): half of (S q)_i from S[i][64 half .. +64), read from
+  // S^T so that a wave's loads are 256 contiguous bytes; four independent sums
   const int i = tid & 127, half = tid >> 7;
   float sk[64];
 #pragma unroll
   for (int k = 0; k < 64; ++k) sk[k] = a.St[(half * 64 + k) * kQjlDim + i];
   lds_barrier();
-  float acc = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float4 *q4 = reinterpret_cast<const float4 *>(qs + 64 * half);
 #pragma unroll
-  for (int k = 0; k < 64; ++k) acc = fmaf(sk[k], qs[half * 64 + k], acc);
-  part[half][i] = acc;
+  for (int k = 0; k < 16; ++k) {
+    const float4 x = q4[k];  // the same address in every lane: a broadcast
+    acc[0] = fmaf(sk[4 * k], x.x, acc[0]);
+    acc[1] = fmaf(sk[4 * k + 1], x.y, acc[1]);
+    acc[2] = fmaf(sk[4 * k + 2], x.z, acc[2]);
+    acc[3] = fmaf(sk[4 * k + 3], x.w, acc[3]);
+  }
+  part[half][i] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   if (wave == 0) {
     float x0 = qs[lane], x1 = qs[lane + 64];
     wave_fwht128(x0, x1, lane);
@@ -131,48 +83,54 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
     if (lane == 0) hmax[0] = mq;
   }
   lds_barrier();
-  if (tid < kQjlDim) qp[128 + tid] = a.cb.qjl_scale * (part[0][tid] + part[1][tid]);
+  if (tid < kQjlDim) {  // waves 0 and 1: s, and the largest |s| of each wave
+    const float sv = a.cb.qjl_scale * (part[0][tid] + part[1][tid]);
+    qp[128 + tid] = sv;
+    const float ms = wave_max(fabsf(sv));
+    if (lane == 0) hmax[1 + wave] = ms;
+  }
   lds_barrier();
   a.qprep[row * 256 + tid] = qp[tid];
   if (a.qa == nullptr) return;
 
-  if (wave == 1) {
-    const float ms = wave_max(fmaxf(fabsf(qp[128 + lane]), fabsf(qp[192 + lane])));
-    if (lane == 0) hmax[1] = ms;
-  }
-  lds_barrier();
+  const float hq = hmax[0], hs = fmaxf(hmax[1], hmax[2]);
   float beta[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
   const float cs = a.scale * kLog2e;  // scores come out in log2 units
-  // per plane: 2^E bounds |x| (E >= -100 keeps every scale encodable); no
-  // digits at all when the plane is zero
-  int Ep[5];
-  bool nz[5];
-#pragma unroll
-  for (int p = 0; p < 5; ++p) {
-    const float M = cs * (p < 4 ? fabsf(beta[p]) * hmax[0] : hmax[1]);
-    nz[p] = M > 0.0f;
-    Ep[p] = max(bound_exponent(M), -100);
-  }
   const int NT = a.qk_tiles;
   const int nwords = NT * 5 * 64 * 8;
   const int nt = g >> 2, gp = g & 3;
   uint32_t *qa = a.qa + grp * (int64_t)(NT * (5 * 64 * 9 + 32));
   __shared__ __align__(16) uint8_t codes[5][4][128];  // [plane][digit][K slot] fp6 codes
-  __shared__ float spart[4][8];                       // per wave: start-value partial sums
+  __shared__ __align__(16) float sval[5][4][128];     // weighted digit values (start values)
+  __shared__ int plane_e[5];                          // per plane: E, or INT_MIN for a zero plane
+  // per plane: 2^E bounds |x| (E >= -100 keeps every scale encodable); no
+  // digits at all when the plane is zero
+  if (tid < 5) {
+    const float M = cs * (tid < 4 ? fabsf(a.cb.beta[tid]) * hq : hs);
+    plane_e[tid] = M > 0.0f ? max(bound_exponent(M), -100) : INT_MIN;
+  }
   // 1. digits of every (plane, K slot): the four digits of one value go to
   // four A rows.  The digit of a K slot is scaled by the factor that goes
   // with the b_split operands; the start values (per digit r, the weighted
   // sum of the unscaled A values, see b_split) are summed on the way, for the
-  // code planes (p < 4) and the sign plane.
-  float sc4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int e = tid; e < 5 * 128; e += 256) {
-    const int p = e >> 7, kap = e & 127;
-    const bool pz = p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4];
-    const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
-    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : beta[3];
-    const float x = cs * (p < 4 ? -bp * qp[b_coord(kap)] : -qp[128 + b_coord(kap)]);
+  // code planes (p < 4) and the sign plane, by the lanes that pack the rows
+  // below.  Thread (K slot, half) takes the planes half, half + 2, half + 4:
+  // one plane per wave at a time.
+  const int hw = wave >> 1;  // = half, known uniform
+  const int kap = tid & 127, bc = b_coord(kap);
+  const float f = b_split_factor(kap), wgt = b_split_weight(kap);
+  lds_barrier();  // plane exponents
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int p = 2 * j + hw;
+    if (p >= 5) break;  // uniform
+    const int Eraw = plane_e[p];
+    const bool pz = Eraw != INT_MIN;
+    const int E = pz ? Eraw : 0;
+    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : p == 3 ? beta[3] : 1.0f;
+    const float x = -cs * bp * qp[(p < 4 ? 0 : 128) + bc];
     // Y = rint(x 2^(19-E)) = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16
     const float y = pz ? rintf(ldexpf(x, 19 - E)) : 0.0f;
     const float d0 = rintf(y * 0x1p-15f);
@@ -181,30 +139,14 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
     rem -= d1 * 1024.0f;
     const float d2 = rintf(rem * 0.03125f);
     const float d3 = rem - d2 * 32.0f;
-    const float f = b_split_factor(kap), wgt = b_split_weight(kap);
     codes[p][0][kap] = (uint8_t)fp6_code(d0 * f);
     codes[p][1][kap] = (uint8_t)fp6_code(d1 * f);
     codes[p][2][kap] = (uint8_t)fp6_code(d2 * f);
     codes[p][3][kap] = (uint8_t)fp6_code(d3 * f);
-    const float v0 = wgt * ldexpf(d0, E - 4), v1 = wgt * ldexpf(d1, E - 9);
-    const float v2 = wgt * ldexpf(d2, E - 14), v3 = wgt * ldexpf(d3, E - 19);
-    if (p < 4) {
-      sc4[0] += v0; sc4[1] += v1; sc4[2] += v2; sc4[3] += v3;
-    } else {
-      sq4[0] += v0; sq4[1] += v1; sq4[2] += v2; sq4[3] += v3;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    sc4[r] = wave_sum(sc4[r]);
-    sq4[r] = wave_sum(sq4[r]);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      spart[wave][r] = sc4[r];
-      spart[wave][4 + r] = sq4[r];
-    }
+    sval[p][0][kap] = wgt * ldexpf(d0, E - 4);
+    sval[p][1][kap] = wgt * ldexpf(d1, E - 9);
+    sval[p][2][kap] = wgt * ldexpf(d2, E - 14);
+    sval[p][3][kap] = wgt * ldexpf(d3, E - 19);
   }
   lds_barrier();
   // 2. this head's rows: lanes 16*ga + 4*gp + r of tile nt, 32 fp6 codes (K
@@ -229,16 +171,31 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
       w[3 * k + 1] = (q24[4 * k + 1] >> 8) | (q24[4 * k + 2] << 16);
       w[3 * k + 2] = (q24[4 * k + 2] >> 16) | (q24[4 * k + 3] << 8);
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(qa + ((nt * 5 + p) * 64 + ln) * 8);
+    uint4 *dst = reinterpret_cast<uint4 *>(qa + ((nt * 5 + p) * 64 + ln) * 8);  // p = 4: wave 1
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], 0u, 0u);
-    const bool pz = p == 0 ? nz[0] : p == 1 ? nz[1] : p == 2 ? nz[2] : p == 3 ? nz[3] : nz[4];
-    const int E = p == 0 ? Ep[0] : p == 1 ? Ep[1] : p == 2 ? Ep[2] : p == 3 ? Ep[3] : Ep[4];
+    const int E = plane_e[p];
+    const bool pz = E != INT_MIN;
     qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)(pz ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One);
+    // start values: this lane's 24 weighted slots (the last 8 have weight
+    // 0), then the sum over the K blocks (lanes ^ 4, ^ 8) and, for the code
+    // planes (wave 0, plane = lane / 16), over the planes
+    const float4 *sv = reinterpret_cast<const float4 *>(&sval[p][r][32 * ga]);
+    float st = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const float4 x = sv[k];
+      st += (x.x + x.y) + (x.z + x.w);
+    }
+    st += xchg4(st);
+    st += xchg8(st);
+    if (wave == 0) {  // uniform: every lane of wave 0 is here
+      st += xchg16(st, lane);
+      st += xchg32(st, lane);
+    }
+    if (li < 4)  // r = li: code planes from wave 0, the sign plane from wave 1
+      qa[nwords + NT * 5 * 64 + (nt * 4 + gp) * 8 + 4 * wave + li] = __float_as_uint(st);
   }
-  if (tid < 8)
-    qa[nwords + NT * 5 * 64 + (nt * 4 + gp) * 8 + tid] =
-        __float_as_uint((spart[0][tid] + spart[1][tid]) + (spart[2][tid] + spart[3][tid]));
   // rows of absent heads (groups of one or two heads) stay zero
   if (g == 0 && G < 4) {
     for (int i = tid; i < (4 - G) * 8; i += 256) qa[nwords + NT * 5 * 64 + G * 8 + i] = 0u;
@@ -1059,12 +1016,102 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(Dec
     split_body<T, 1>(a, sm);
 }
 
-// ---- 3. merge: one wave per output row --------------------------------------
+// ---- 3. merge ---------------------------------------------------------------
+// LSE combine of the chunk partials of an output row, o' = acc'/l, one
+// inverse FWHT, store.  W waves share a row (4/W rows per workgroup); wave w
+// of a row takes chunks 16w .. 16w+15, then 16(w+W) .., and issues every load
+// of a batch of 16 together, so up to 16W chunks cost one memory round trip.
+// Lane l owns coordinates l and l + 64, lane e < 16 the statistics of chunk e
+// of the batch.  The waves of a row then meet in LDS.
+constexpr int kMergeBatch = 16;
+
+template <int W>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  if (r >= rows) return;
-  merge_row(a, r, lane);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave % W;
+  const int64_t r = (int64_t)blockIdx.x * (4 / W) + wave / W;
+  __shared__ float wm[4], wl[4];
+  __shared__ float wa[4][kHeadDim];
+  int ns = 0;
+  const float *part = a.partials;
+  if (r < rows) {
+    const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
+    const int b = (int)(r / per_seq);
+    const int t = (int)((r / a.num_q_heads) % a.q_len);
+    const int vis = max(0, clamped_context(a, b) - a.q_len + t + 1);
+    ns = (vis + a.split_tokens - 1) / a.split_tokens;
+    part += r * a.num_splits * kPartStride;
+  }
+  float M = -INFINITY, Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;  // Ls: lanes < 16, per chunk slot
+  for (int base = kMergeBatch * wr; base < ns; base += kMergeBatch * W) {  // uniform
+    float v0[kMergeBatch], v1[kMergeBatch];
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const float *p = part + (int64_t)min(base + e, ns - 1) * kPartStride;
+      v0[e] = p[4 + lane];
+      v1[e] = p[68 + lane];
+    }
+    const bool live = lane < kMergeBatch && base + lane < ns;
+    const float *ps = part + (int64_t)min(base + (lane & (kMergeBatch - 1)), ns - 1) * kPartStride;
+    const float m0 = ps[0], l = ps[1];  // unconditional loads
+    const float m = live ? m0 : -INFINITY;
+    const float mb = wave_max(m);
+    if (mb > M) {  // uniform: move the wave's reference (nothing to rescale while it is -inf)
+      const float c = M == -INFINITY ? 0.0f : exp2f(M - mb);
+      Ls *= c;
+      A0 *= c;
+      A1 *= c;
+      M = mb;
+    }
+    const float f = m == -INFINITY ? 0.0f : exp2f(m - M);
+    Ls = fmaf(f, live ? l : 0.0f, Ls);
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const float fe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), e));  // 0 past ns
+      A0 = fmaf(fe, v0[e], A0);
+      A1 = fmaf(fe, v1[e], A1);
+    }
+  }
+  const float Lw = wave_sum(Ls);
+  if (W > 1) {
+    if (lane == 0) {
+      wm[wave] = M;
+      wl[wave] = Lw;
+    }
+    wa[wave][lane] = A0;
+    wa[wave][64 + lane] = A1;
+    lds_barrier();
+  }
+  if (wr != 0 || r >= rows) return;
+  float Mx = M;
+#pragma unroll
+  for (int w = 1; w < W; ++w) Mx = fmaxf(Mx, wm[wave + w]);
+  float Lt = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  if (W == 1) {
+    Lt = Lw;
+    o0 = A0;
+    o1 = A1;
+  } else {
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = wm[wave + w];
+      const float c = mw == -INFINITY ? 0.0f : exp2f(mw - Mx);
+      Lt = fmaf(c, wl[wave + w], Lt);
+      o0 = fmaf(c, wa[wave + w][lane], o0);
+      o1 = fmaf(c, wa[wave + w][64 + lane], o1);
+    }
+  }
+  if (Lt > 0.0f) {
+    const float inv = 1.0f / Lt;
+    o0 *= inv;
+    o1 *= inv;
+  } else {  // no visible key
+    o0 = 0.0f;
+    o1 = 0.0f;
+  }
+  wave_fwht128(o0, o1, lane);
+  store_from_float(a.out, a.out_dtype, r * kHeadDim + lane, o0);
+  store_from_float(a.out, a.out_dtype, r * kHeadDim + 64 + lane, o1);
 }
 
 template <int G>
@@ -1106,7 +1153,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(row_blocks), dim3(256), 0, stream, a, rows);
+  // four waves per row when there are more chunks than one batch
+  if (a.num_splits > kMergeBatch)
+    hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, a, rows);
+  else
+    hipLaunchKernelGGL(merge_kernel<1>, dim3(row_blocks), dim3(256), 0, stream, a, rows);
   return hipGetLastError();
 }
 
