@@ -932,12 +932,20 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
   }
   lds_barrier();
   // Every interval holds both contractions; the first one's value pass
-  // reads the zeroed digit rows of buffer 1 and adds nothing.
-  for (int k = 0; k < ntiles; k += 2) {
+  // reads the zeroed digit rows of buffer 1 and adds nothing.  The loop takes
+  // whole pairs and an odd last tile follows it: with a break between the
+  // two halves the compiler keeps a path from the first half back to the
+  // loop head, on which the next fetches are not in flight, and then waits
+  // for every load at the head.
+  int k = 0;
+  for (; k + 1 < ntiles; k += 2) {
     interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 0>{}, SB, SA, k);
     lds_barrier();
-    if (k + 1 >= ntiles) break;
     interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 1>{}, SA, SB, k + 1);
+    lds_barrier();
+  }
+  if (k < ntiles) {  // uniform
+    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 0>{}, SB, SA, k);
     lds_barrier();
   }
   if ((ntiles - 1) & 1)
