@@ -1013,15 +1013,391 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
   }
 }
 
+// Five to eight heads per KV head (two head tiles): the waves specialise.
+// Waves 0..3 (role 0) score page pair w of every tile for both head tiles,
+// so each K page is expanded into operands once, and stage the K planes;
+// waves 4..7 (role 1) contract the values of coordinates 32(w-4) .. +31 for
+// both head tiles and stage the norms and V planes.  The two waves that share
+// a SIMD then issue different mixes (vector-heavy scores, matrix-heavy
+// values) and overlap, where identical waves run the same phases in lock
+// step.  Intervals, buffers and records are those of split_body.
+template <int R>
+__device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a, SplitLds<2> &sm) {
+  constexpr int T = 2;
+  constexpr int NW = 8;  // waves
+  constexpr int NJ = 2;  // value N-tiles (16 coordinates) per value wave
+  const int per_seq = a.num_kv_heads * a.num_splits;
+  const int item = blockIdx.x;
+  if (item >= a.num_seqs * per_seq) return;
+  const int b = item / per_seq;
+  const int h = (item / a.num_splits) % a.num_kv_heads;
+  const int split = item % a.num_splits;
+  const int L = clamped_context(a, b);
+  const int s0 = split * a.split_tokens;
+  const int s1 = min(s0 + a.split_tokens, L);
+  if (s0 >= s1) return;  // uniform
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sq = wave & 3;  // role 0: page pair (K-block); role 1: coordinate block
+  const int t16 = lane & 15, grow = lane >> 4;
+  const int64_t grp = (int64_t)b * a.num_kv_heads + h;
+  const int G = a.group;
+  const int ntiles = min((s1 - s0 + 127) >> 7, kMaxSplitTiles);  // the host caps chunks at 64 tiles
+
+  {
+    const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
+    for (int idx = tid; idx < ntiles * kTilePages; idx += 64 * NW) {
+      const int tile0 = s0 + 128 * (idx >> 3);
+      const int tok = tile0 + 16 * (idx & 7);
+      sm.ids[idx >> 3][idx & 7] = btab[(tok < s1 ? tok : tile0) >> 4];
+    }
+  }
+
+  // role 0: query-side operands of the score contraction, both head tiles
+  v8i Aq[T][5];
+  int scq[T][5];
+  v4f cinit[T], qinit[T];
+  if constexpr (R == 0) {
+    const uint32_t *qa = a.qa + grp * (int64_t)(T * (5 * 64 * 9 + 32));
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+#pragma unroll
+      for (int p = 0; p < 5; ++p) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((u * 5 + p) * 64 + lane) * 8);
+        const uint4 u0 = src[0];
+        const uint2 u1 = *reinterpret_cast<const uint2 *>(src + 1);
+        Aq[u][p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, 0, 0};
+        scq[u][p] = (int)qa[T * 5 * 64 * 8 + (u * 5 + p) * 64 + lane];
+      }
+      const float *ci = reinterpret_cast<const float *>(qa + T * 5 * 64 * 9) + (u * 4 + grow) * 8;
+      cinit[u] = v4f{ci[0], ci[1], ci[2], ci[3]};
+      qinit[u] = v4f{ci[4], ci[5], ci[6], ci[7]};
+    }
+  }
+  float beta[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
+  const BSplitK bk = bsplit_consts();
+  const uint32_t nib = in_vgpr(0x0F0F0F0Fu);
+  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80808080u);
+  const int kap0 = 8 * (t16 & 3) + (t16 >> 2);
+  const StagePtrs sp{a.k_cache, a.v_cache, (int64_t)a.num_kv_heads, h, sq, 16u * (uint32_t)lane,
+                     16u * (uint32_t)(lane % 48), 4u * (uint32_t)t16, 4u * (uint32_t)(lane & 7)};
+  auto pair_ids = [&](int k, int &b0, int &b1) __attribute__((always_inline)) {
+    const int2 v = *reinterpret_cast<const int2 *>(&sm.ids[k][2 * sq]);
+    b0 = __builtin_amdgcn_readfirstlane(v.x);
+    b1 = __builtin_amdgcn_readfirstlane(v.y);
+  };
+
+  // role 0 state (lane: head grow of tile u, token t16)
+  float rl[T], lsum[T];
+  // role 1 state (lane: A row (head gA, digit rA), K-block kb; C rows head grow)
+  const int gA = t16 >> 2, rA = lane & 3, kb = grow;
+  float raA[T], raC[T];
+  v4f acc[T][4][NJ];
+  v4f corr[T];
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    rl[u] = -INFINITY;
+    lsum[u] = 0.0f;
+    corr[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    raA[u] = raC[u] = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[u][p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // role 1: E8M0 scales of the weight rows in buffer bf (as in split_body)
+  auto value_scales = [&](int bf, int (&sw)[T]) __attribute__((always_inline)) {
+    int2 st[T];
+    bool move = false;
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      st[u] = sm.stats[bf][u][gA][kb];
+      move |= __int_as_float(st[u].y) > raA[u] + (float)kRefStep;
+    }
+    if (__builtin_amdgcn_ballot_w64(move)) {
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        float MA = -INFINITY, MC = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          MA = fmaxf(MA, __int_as_float(sm.stats[bf][u][gA][q].y));
+          MC = fmaxf(MC, __int_as_float(sm.stats[bf][u][grow][q].y));
+        }
+        if (MA > raA[u] + (float)kRefStep) raA[u] = MA;
+        float fc = 1.0f;
+        if (MC > raC[u] + (float)kRefStep) {
+          fc = raC[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(raC[u] - MC);
+          raC[u] = MC;
+        }
+        corr[u] *= fc;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[u][p][j] *= fc;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      const float d = fmaxf(__int_as_float(st[u].y) - raA[u], -300.0f);  // NaN (both -inf) -> -300
+      sw[u] = min(max(st[u].x + 7 - 4 * rA + (int)d, 0), 254);
+    }
+  };
+
+  // One barrier interval (as in split_body): the staging of both roles, then
+  // role 0 scores tile k, role 1 contracts the values of tile k-1 (without
+  // scores: of tile k).
+  auto interval = [&](auto HS, auto HV, auto PAR, StageSet<R> &SK, StageSet<R> &SV, int k)
+                      __attribute__((always_inline)) {
+    constexpr bool has_s = decltype(HS)::value, has_v = decltype(HV)::value;
+    constexpr int par = decltype(PAR)::value;
+    constexpr int bs = par, bv = has_s ? (par ^ 1) : par;
+    const int kv = has_s ? k - 1 : k;
+    if constexpr (has_s) {
+      int k3a, k3b, k2a, k2b;
+      pair_ids(min(k + 3, ntiles - 1), k3a, k3b);
+      pair_ids(min(k + 2, ntiles - 1), k2a, k2b);
+      store_v_part<R>(sm.vbuf[par], SV, sp, lane);
+      store_k_part<R>(sm.kbuf[par ^ 1], SK, sp, lane);
+      load_k_part<R>(SK, sp, k3a, k3b);
+      load_v_part<R>(SV, sp, k2a, k2b);
+    }
+    if constexpr (R == 0 && has_s) {
+      uint32_t kw[2][4];
+      uint32_t nrm[2][3];  // half bits: n_k, gamma, n_v
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint8_t *rec = sm.kbuf[bs] + kKRec * (2 * sq + e);
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(rec + 16 * t16 + 4 * grow);
+        kw[e][0] = p[0];
+        kw[e][1] = p[64];
+        kw[e][2] = p[128];
+        kw[e][3] = p[192];
+        const uint16_t *nr = reinterpret_cast<const uint16_t *>(rec + 1024);
+        nrm[e][0] = nr[t16];
+        nrm[e][1] = nr[16 + t16];
+        nrm[e][2] = nr[32 + t16];
+      }
+      // each page's operands once, for both head tiles
+      v4f cc[T][2], qq[T][2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t w0 = kw[e][0], w1 = kw[e][1], w2 = kw[e][2], w3 = kw[e][3];
+        const v8i B0 = bsplit(w0, bk), B1 = bsplit(w1, bk), B2 = bsplit(w2, bk);
+        const v8i Bx = bsplit(w0 ^ w1 ^ w2, bk), Bs = bsplit(w3, bk);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          v4f c = mfma_f6f4(Aq[u][0], B0, cinit[u], scq[u][0]);
+          c = mfma_f6f4(Aq[u][1], B1, c, scq[u][1]);
+          c = mfma_f6f4(Aq[u][2], B2, c, scq[u][2]);
+          cc[u][e] = mfma_f6f4(Aq[u][3], Bx, c, scq[u][3]);
+          qq[u][e] = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
+        }
+      }
+      const bool partial = s0 + 128 * (k + 1) > s1;  // uniform: the chunk's last tile
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        float inner[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const v4f &c = cc[u][e], &q = qq[u][e];
+          const float code = (c[0] + c[1]) + (c[2] + c[3]);
+          const float qj = (q[0] + q[1]) + (q[2] + q[3]);
+          inner[e] = fmaf(half_lo(nrm[e][1]), qj, code);
+        }
+        const float lsum0 = lsum[u];
+        auto weights = [&](float x0, float x1, bool v0, bool v1) __attribute__((always_inline)) {
+          const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
+          lsum[u] += p0 + p1;
+          const float w0 = v0 ? p0 * half_lo(nrm[0][2]) : 0.0f;
+          const float w1 = v1 ? p1 * half_lo(nrm[1][2]) : 0.0f;
+          const int mk = row_max16_nonneg(max(__float_as_int(w0), __float_as_int(w1)));  // w >= 0
+          const uint32_t exb = max((uint32_t)mk & 0x7F800000u, 14u << 23);
+          const float mult = __uint_as_float(0x86000000u - exb);  // 2^(141 - ex)
+          const uint32_t X0 = __float_as_uint(fmaf(w0, mult, 8388608.0f));
+          const uint32_t X1 = __float_as_uint(fmaf(w1, mult, 8388608.0f));
+          const uint32_t XX = __builtin_amdgcn_perm(X1, X0, 0x05040100u);
+          const uint32_t Ev = (XX & nib) | s80;
+          const uint32_t Od = ((XX >> 4) & nib) | s80;
+          uint8_t *wr = &sm.wq[bs][u][4 * grow][32 * sq + kap0];
+          wr[3 * kWqRow] = (uint8_t)Ev;
+          wr[3 * kWqRow + 4] = (uint8_t)(Ev >> 16);
+          wr[1 * kWqRow] = (uint8_t)(Ev >> 8);
+          wr[1 * kWqRow + 4] = (uint8_t)(Ev >> 24);
+          wr[2 * kWqRow] = (uint8_t)Od;
+          wr[2 * kWqRow + 4] = (uint8_t)(Od >> 16);
+          wr[0] = (uint8_t)(Od >> 8);
+          wr[4] = (uint8_t)(Od >> 24);
+          sm.stats[bs][u][grow][sq] = make_int2((int)(exb >> 23), __float_as_int(rl[u]));
+        };
+        const float x0 = fmaf(half_lo(nrm[0][0]), inner[0], -rl[u]);
+        const float x1 = fmaf(half_lo(nrm[1][0]), inner[1], -rl[u]);
+        weights(x0, x1, true, true);
+        if (__builtin_amdgcn_ballot_w64(x0 > (float)kRefStep || x1 > (float)kRefStep) || partial) {
+          const int tok0 = s0 + 128 * k + 32 * sq + t16;
+          const bool v0 = tok0 < s1, v1 = tok0 + 16 < s1;
+          const float r0 = v0 ? half_lo(nrm[0][0]) * inner[0] : -INFINITY;
+          const float r1 = v1 ? half_lo(nrm[1][0]) * inner[1] : -INFINITY;
+          const float mh = row_max16(fmaxf(r0, r1));
+          const float nr = fmaxf(rl[u], ceilf(mh));
+          lsum[u] = lsum0;
+          if (nr > rl[u] && nr - rl[u] > 0.0f) {
+            lsum[u] = rl[u] == -INFINITY ? 0.0f : lsum[u] * __builtin_amdgcn_exp2f(rl[u] - nr);
+            rl[u] = nr;
+          }
+          weights(r0 == -INFINITY ? -INFINITY : r0 - rl[u], r1 == -INFINITY ? -INFINITY : r1 - rl[u], v0, v1);
+        }
+      }
+    }
+    if constexpr (R == 1 && has_v) {
+      int sw[T];
+      value_scales(bv, sw);
+      v8i Aw[T];
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        const uint8_t *row = &sm.wq[bv][u][4 * gA + rA][0];
+        const uint4 u0 = *reinterpret_cast<const uint4 *>(row + 16 * kb);
+        const uint4 u1 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * kb);
+        Aw[u] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      }
+      const uint32_t *vw = reinterpret_cast<const uint32_t *>(sm.vbuf[bv] + kVPair * kb);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = 16 * (NJ * sq + j) + t16;
+        const uint32_t W0 = vw[c], W1 = vw[128 + c], W2 = vw[256 + c];
+        const v8i V0 = bsplit(W0, bk), V1 = bsplit(W1, bk), V2 = bsplit(W2, bk), Vx = bsplit(W0 ^ W1 ^ W2, bk);
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          acc[u][0][j] = mfma_f8f4(Aw[u], V0, acc[u][0][j], sw[u]);
+          acc[u][1][j] = mfma_f8f4(Aw[u], V1, acc[u][1][j], sw[u]);
+          acc[u][2][j] = mfma_f8f4(Aw[u], V2, acc[u][2][j], sw[u]);
+          acc[u][3][j] = mfma_f8f4(Aw[u], Vx, acc[u][3][j], sw[u]);
+        }
+      }
+      if (kv % 4 == sq) {  // uniform: the offsets of b_split, one value wave per tile
+        const v8i C1 = v8i{(int)0xEEEEEEEEu, (int)0xDDDDDDDDu, (int)0xAAAAAAAAu, 0, 0, 0, 0, 0};
+        const v8i C2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < T; ++u) {
+          corr[u] = mfma_f8f4(Aw[u], C1, corr[u], sw[u]);
+          corr[u] = mfma_f8f4(Aw[u], C2, corr[u], sw[u]);
+        }
+      }
+    }
+  };
+
+  for (int i = tid; i < T * 16 * kWqRow / 4; i += 64 * NW) reinterpret_cast<uint32_t *>(&sm.wq[1][0][0][0])[i] = 0u;
+  if (tid < T * 16) (&sm.stats[1][0][0][0])[tid] = make_int2(0, __float_as_int(-INFINITY));
+  lds_barrier();  // block ids, buffer 1
+  StageSet<R> SA, SB;
+  {
+    int b0, b1, c0, c1, d0, d1;
+    pair_ids(0, b0, b1);
+    pair_ids(min(1, ntiles - 1), c0, c1);
+    pair_ids(min(2, ntiles - 1), d0, d1);
+    load_k_part<R>(SA, sp, b0, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k_part<R>(SB, sp, c0, c1);
+    load_v_part<R>(SA, sp, b0, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_k_part<R>(sm.kbuf[0], SA, sp, lane);
+    load_k_part<R>(SA, sp, d0, d1);
+    load_v_part<R>(SB, sp, c0, c1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lds_barrier();
+  int k = 0;
+  for (; k + 1 < ntiles; k += 2) {
+    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 0>{}, SB, SA, k);
+    lds_barrier();
+    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 1>{}, SA, SB, k + 1);
+    lds_barrier();
+  }
+  if (k < ntiles) {  // uniform
+    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 0>{}, SB, SA, k);
+    lds_barrier();
+  }
+  if ((ntiles - 1) & 1)
+    interval(flag<false>{}, flag<true>{}, std::integral_constant<int, 1>{}, SA, SB, ntiles - 1);
+  else
+    interval(flag<false>{}, flag<true>{}, std::integral_constant<int, 0>{}, SA, SB, ntiles - 1);
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    asm volatile("" : "+v"(corr[u]));
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[u][p][j]));
+  }
+
+  if constexpr (R == 0) {  // probability sums per head
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      const float ls = row_sum16(lsum[u]);
+      if (t16 == 0) {
+        sm.lred[u][grow][sq][0] = ls;
+        sm.lred[u][grow][sq][1] = rl[u];
+      }
+    }
+  } else {  // correction partials per value wave
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+      if (t16 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.cred[sq][u][grow][i] = corr[u][i];
+      }
+  }
+  lds_barrier();
+  if constexpr (R == 1) {
+    const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      const int g = 4 * u + grow;  // C rows of this lane: head grow of tile u
+      if (g >= G) continue;
+      const float ra = raC[u];
+      float cs = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs += sm.cred[wv][u][grow][i];
+      float *part = a.partials + ((grp * G + g) * a.num_splits + split) * kPartStride;
+      if (sq == 0 && t16 == 0) {
+        float l = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float rq = sm.lred[u][grow][q][1];
+          if (rq != -INFINITY) l += sm.lred[u][grow][q][0] * __builtin_amdgcn_exp2f(rq - ra);
+        }
+        part[0] = ra;
+        part[1] = l;
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float o = -bsum * cs;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const v4f &c = acc[u][p][j];
+          o = fmaf(-beta[p], (c[0] + c[1]) + (c[2] + c[3]), o);
+        }
+        part[4 + 16 * (NJ * sq + j) + t16] = o;
+      }
+    }
+  }
+}
+
 template <int T>
 __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) SplitLds<T> sm;
-  if (T == 1)
+  if constexpr (T == 1) {
     split_body<T, 2>(a, sm);
-  else if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)  // uniform: the wave's staging role
-    split_body<T, 0>(a, sm);
-  else
-    split_body<T, 1>(a, sm);
+  } else {
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)  // uniform: the wave's role
+      split_body_ws<0>(a, sm);
+    else
+      split_body_ws<1>(a, sm);
+  }
 }
 
 // ---- 3. merge ---------------------------------------------------------------

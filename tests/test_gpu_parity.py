@@ -223,10 +223,11 @@ def test_caller_supplied_qjl_matrix():
     check_decode(out, case["q"], kp, vp, case["table"], case["context_lens"], tables=(c32, t32, S))
 
 
-@pytest.mark.parametrize("Hq,Hkv,T", [(4, 4, 777), (8, 4, 777), (8, 2, 131)])
+@pytest.mark.parametrize("Hq,Hkv,T", [(4, 4, 777), (8, 4, 777), (8, 2, 131), (16, 2, 131)])
 def test_small_groups(Hq, Hkv, T):
-    """One and two query heads per KV head (unused operand rows), and a
-    context shorter than one 128-token tile."""
+    """One and two query heads per KV head (unused operand rows), a context
+    shorter than one 128-token tile, and eight heads per KV head (the pass
+    whose waves split into scoring and value roles) over a partial tile."""
     case = synth.gqa_case(seed=11, T=T, Hq=Hq, Hkv=Hkv)
     cb = codebook()
     kpool, vpool = new_pools(case["num_blocks"], Hkv)
@@ -235,19 +236,20 @@ def test_small_groups(Hq, Hkv, T):
     check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"], case["context_lens"])
 
 
-def test_running_maximum_moves_along_the_sequence():
+@pytest.mark.parametrize("Hkv", [8, 4])
+def test_running_maximum_moves_along_the_sequence(Hkv):
     """Key norms ramp up 8x along the context with softmax scale 0.25: the
     maximum log2-score grows from about 40 to about 350, so later tiles
     overtake the running maximum by more than the rescale threshold (64)
-    several times; the output must still match."""
+    several times; the output must still match (4 and 8 heads per KV head)."""
     T = 4096
-    case = synth.gqa_case(seed=12, T=T, Hq=32, Hkv=8)
+    case = synth.gqa_case(seed=12, T=T, Hq=32, Hkv=Hkv)
     ramp = (1.0 + 7.0 * np.arange(T) / T)[:, None, None]
     k = synth.round_to_bf16(case["k"] * ramp)
     cb = codebook()
-    kpool, vpool = new_pools(case["num_blocks"], 8)
+    kpool, vpool = new_pools(case["num_blocks"], Hkv)
     encode_gpu(cb, k, case["v"], case["slots"], kpool, vpool, with_norms=False)
-    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 8,
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], Hkv,
                      scale=0.25, tokens_per_split=4096)
     err = check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"],
                        case["context_lens"], scale=0.25)
