@@ -28,18 +28,10 @@ namespace {
 constexpr int kPartStride = 132;  // m (log2 units), l, pad, pad, acc[128]
 constexpr float kLog2e = 1.4426950408889634f;
 
-// ---- 1. query prep: a workgroup per query row --------------------------------
+// ---- 1. query prep (vector and prefill passes): a workgroup per query row -----
 // Grid (sequence x position x KV head, head of the group).  Thread (i, half)
 // forms half of (S q)_i from S[i][64*half .. +64) held in registers; wave 0
-// rotates q.  For the matrix-core pass the workgroup also writes its head's
-// rows of the score contraction's A operands (see split_mfma_kernel): rows
-// (head, digit r), for x the plane's values times scale * log2(e) (scores in
-// log2 units).  With 2^E bounding |x| over the head, Y = rint(x 2^(19-E))
-// is written in balanced base 32, Y = d0 2^15 + d1 2^10 + d2 2^5 + d3 with
-// every |d_r| <= 16, stored as the fp6 e2m3 code of d_r/8 (exact), and row r
-// carries it with scale 2^(E-4-5r+3): x to 2^-20 of the head's largest
-// magnitude.  Logits of keys with large norms need these 19 bits; 16
-// (base-16 digits) leave errors near 1e-3 in peaked rows.
+// rotates q.  The matrix-core split pass forms its operands itself (below).
 __device__ __forceinline__ int bound_exponent(float M) {  // M < 2^E for finite M > 0
   const int ex = (int)((__float_as_uint(M) >> 23) & 0xFFu);
   return ex == 0 ? -126 : ex - 126;
@@ -54,7 +46,6 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
   __shared__ __align__(16) float qs[kHeadDim];
   __shared__ float part[2][kQjlDim];
   __shared__ float qp[256];
-  __shared__ float hmax[3];
   if (tid < kHeadDim) qs[tid] = load_as_float(a.q, a.q_dtype, row * kHeadDim + tid);
   // thread (i, half): half of (S q)_i from S[i][64 half .. +64), read from
   // S^T so that a wave's loads are 256 contiguous bytes; four independent sums
@@ -79,135 +70,11 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
     wave_fwht128(x0, x1, lane);
     qp[lane] = x0;
     qp[lane + 64] = x1;
-    const float mq = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    if (lane == 0) hmax[0] = mq;
   }
   lds_barrier();
-  if (tid < kQjlDim) {  // waves 0 and 1: s, and the largest |s| of each wave
-    const float sv = a.cb.qjl_scale * (part[0][tid] + part[1][tid]);
-    qp[128 + tid] = sv;
-    const float ms = wave_max(fabsf(sv));
-    if (lane == 0) hmax[1 + wave] = ms;
-  }
+  if (tid < kQjlDim) qp[128 + tid] = a.cb.qjl_scale * (part[0][tid] + part[1][tid]);
   lds_barrier();
   a.qprep[row * 256 + tid] = qp[tid];
-  if (a.qa == nullptr) return;
-
-  const float hq = hmax[0], hs = fmaxf(hmax[1], hmax[2]);
-  float beta[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
-  const float cs = a.scale * kLog2e;  // scores come out in log2 units
-  const int NT = a.qk_tiles;
-  const int nwords = NT * 5 * 64 * 8;
-  const int nt = g >> 2, gp = g & 3;
-  uint32_t *qa = a.qa + grp * (int64_t)(NT * (5 * 64 * 9 + 32));
-  __shared__ __align__(16) uint8_t codes[5][4][128];  // [plane][digit][K slot] fp6 codes
-  __shared__ __align__(16) float sval[5][4][128];     // weighted digit values (start values)
-  __shared__ int plane_e[5];                          // per plane: E, or INT_MIN for a zero plane
-  // per plane: 2^E bounds |x| (E >= -100 keeps every scale encodable); no
-  // digits at all when the plane is zero
-  if (tid < 5) {
-    const float M = cs * (tid < 4 ? fabsf(a.cb.beta[tid]) * hq : hs);
-    plane_e[tid] = M > 0.0f ? max(bound_exponent(M), -100) : INT_MIN;
-  }
-  // 1. digits of every (plane, K slot): the four digits of one value go to
-  // four A rows.  The digit of a K slot is scaled by the factor that goes
-  // with the b_split operands; the start values (per digit r, the weighted
-  // sum of the unscaled A values, see b_split) are summed on the way, for the
-  // code planes (p < 4) and the sign plane, by the lanes that pack the rows
-  // below.  Thread (K slot, half) takes the planes half, half + 2, half + 4:
-  // one plane per wave at a time.
-  const int hw = wave >> 1;  // = half, known uniform
-  const int kap = tid & 127, bc = b_coord(kap);
-  const float f = b_split_factor(kap), wgt = b_split_weight(kap);
-  lds_barrier();  // plane exponents
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int p = 2 * j + hw;
-    if (p >= 5) break;  // uniform
-    const int Eraw = plane_e[p];
-    const bool pz = Eraw != INT_MIN;
-    const int E = pz ? Eraw : 0;
-    const float bp = p == 0 ? beta[0] : p == 1 ? beta[1] : p == 2 ? beta[2] : p == 3 ? beta[3] : 1.0f;
-    const float x = -cs * bp * qp[(p < 4 ? 0 : 128) + bc];
-    // Y = rint(x 2^(19-E)) = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16
-    const float y = pz ? rintf(ldexpf(x, 19 - E)) : 0.0f;
-    const float d0 = rintf(y * 0x1p-15f);
-    float rem = y - d0 * 32768.0f;
-    const float d1 = rintf(rem * 0x1p-10f);
-    rem -= d1 * 1024.0f;
-    const float d2 = rintf(rem * 0.03125f);
-    const float d3 = rem - d2 * 32.0f;
-    codes[p][0][kap] = (uint8_t)fp6_code(d0 * f);
-    codes[p][1][kap] = (uint8_t)fp6_code(d1 * f);
-    codes[p][2][kap] = (uint8_t)fp6_code(d2 * f);
-    codes[p][3][kap] = (uint8_t)fp6_code(d3 * f);
-    sval[p][0][kap] = wgt * ldexpf(d0, E - 4);
-    sval[p][1][kap] = wgt * ldexpf(d1, E - 9);
-    sval[p][2][kap] = wgt * ldexpf(d2, E - 14);
-    sval[p][3][kap] = wgt * ldexpf(d3, E - 19);
-  }
-  lds_barrier();
-  // 2. this head's rows: lanes 16*ga + 4*gp + r of tile nt, 32 fp6 codes (K
-  // slot 32 ga + s at code s) packed into six words, and their E8M0 scales
-  if (tid < 5 * 16) {
-    const int li = tid & 15, p = tid >> 4;
-    const int ga = li >> 2, r = li & 3, ln = 16 * ga + 4 * gp + r;
-    const uint4 c0 = *reinterpret_cast<const uint4 *>(&codes[p][r][32 * ga]);
-    const uint4 c1 = *reinterpret_cast<const uint4 *>(&codes[p][r][32 * ga + 16]);
-    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    // four 6-bit codes per byte-word to 24 bits, eight of those to six words
-    uint32_t q24[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t v = cw[k];
-      q24[k] = (v & 0x3Fu) | ((v >> 2) & 0xFC0u) | ((v >> 4) & 0x3F000u) | ((v >> 6) & 0xFC0000u);
-    }
-    uint32_t w[6];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {  // 4 x 24 bits = 3 words
-      w[3 * k + 0] = q24[4 * k] | (q24[4 * k + 1] << 24);
-      w[3 * k + 1] = (q24[4 * k + 1] >> 8) | (q24[4 * k + 2] << 16);
-      w[3 * k + 2] = (q24[4 * k + 2] >> 16) | (q24[4 * k + 3] << 8);
-    }
-    uint4 *dst = reinterpret_cast<uint4 *>(qa + ((nt * 5 + p) * 64 + ln) * 8);  // p = 4: wave 1
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], 0u, 0u);
-    const int E = plane_e[p];
-    const bool pz = E != INT_MIN;
-    qa[nwords + (nt * 5 + p) * 64 + ln] = (uint32_t)(pz ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One);
-    // start values: this lane's 24 weighted slots (the last 8 have weight
-    // 0), then the sum over the K blocks (lanes ^ 4, ^ 8) and, for the code
-    // planes (wave 0, plane = lane / 16), over the planes
-    const float4 *sv = reinterpret_cast<const float4 *>(&sval[p][r][32 * ga]);
-    float st = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
-      const float4 x = sv[k];
-      st += (x.x + x.y) + (x.z + x.w);
-    }
-    st += xchg4(st);
-    st += xchg8(st);
-    if (wave == 0) {  // uniform: every lane of wave 0 is here
-      st += xchg16(st, lane);
-      st += xchg32(st, lane);
-    }
-    if (li < 4)  // r = li: code planes from wave 0, the sign plane from wave 1
-      qa[nwords + NT * 5 * 64 + (nt * 4 + gp) * 8 + 4 * wave + li] = __float_as_uint(st);
-  }
-  // rows of absent heads (groups of one or two heads) stay zero
-  if (g == 0 && G < 4) {
-    for (int i = tid; i < (4 - G) * 8; i += 256) qa[nwords + NT * 5 * 64 + G * 8 + i] = 0u;
-    for (int widx = tid; widx < 5 * 64 * 8; widx += 256) {
-      const int ln = (widx >> 3) & 63;
-      if (((ln & 15) >> 2) >= G) qa[widx] = 0u;
-    }
-    for (int sidx = tid; sidx < 5 * 64; sidx += 256) {
-      const int ln = sidx & 63;
-      if (((ln & 15) >> 2) >= G) qa[nwords + sidx] = (uint32_t)kE8M0One;
-    }
-  }
 }
 
 // ---- 2. split pass (vector ALU) --------------------------------------------
@@ -605,6 +472,204 @@ struct SplitLds {
 template <bool B>
 using flag = std::integral_constant<bool, B>;
 
+// ---- query operands inside the split pass ------------------------------------
+// The matrix-core split pass forms the query-side operands of its G heads
+// itself while its first tiles are in flight: q' = H q, s = alpha S q, and
+// the A operands of the score contraction: rows (head, digit r), for x the
+// plane's values times scale * log2(e) (scores in log2 units).  With 2^E
+// bounding |x| over the head, Y = rint(x 2^(19-E)) is written in balanced
+// base 32, Y = d0 2^15 + d1 2^10 + d2 2^5 + d3 with every |d_r| <= 16, stored
+// as the fp6 e2m3 code of d_r/8 (exact), and row r carries it with scale
+// 2^(E-4-5r+3): x to 2^-20 of the head's largest magnitude.  Logits of keys
+// with large norms need these 19 bits; 16 (base-16 digits) leave errors near
+// 1e-3 in peaked rows.  Every workgroup of a (sequence, KV head) repeats this
+// small amount of work (16 K multiply-adds per head) instead of waiting for a
+// separate launch and a round trip of its results through memory.  The
+// scratch space aliases the staging buffers, which are first written after it.
+template <int T>
+struct QPrepLds {
+  float qs[4 * T][kHeadDim];           // q (zero rows for absent heads)
+  float qr[4 * T][kHeadDim];           // q' = H q
+  float sv[4 * T][kQjlDim];            // s = alpha S q
+  union {
+    float part[2][4 * T][kQjlDim];     // halves of S q
+    uint8_t codes[4 * T][5][4][128];   // [head][plane][digit][K slot] fp6 codes
+  };
+  int pe[4 * T][5];                    // per head and plane: E, or INT_MIN for a zero plane
+  float ssum[4 * T][8];                // start values: code planes (digit 0..3), sign plane
+};
+
+static_assert(sizeof(QPrepLds<1>) <= 2 * kTilePages * kKRec + 2 * 4 * kVPair, "query scratch exceeds the staging buffers");
+static_assert(sizeof(QPrepLds<2>) <= 2 * kTilePages * kKRec + 2 * 4 * kVPair, "query scratch exceeds the staging buffers");
+
+// Loads issued first in the workgroup, so that waiting for them does not wait
+// for the tile loads issued after them: this thread's q elements (one
+// unconditional dword each, converted later) and S^T column i for the k half
+// of S q it takes.
+template <int T>
+struct QPrepRegs {
+  uint32_t qw[2];
+  float sk[64];
+};
+template <int T>
+__device__ __forceinline__ void qprep_loads(const DecodeArgs &a, int64_t grp, int tid, QPrepRegs<T> &R) {
+  const int G = a.group;
+  const bool f32 = a.q_dtype == TQ_F32;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int e = min(tid + 256 * T * it, G * kHeadDim - 1);  // past the rows: repeats the last element
+    const int64_t idx = grp * G * kHeadDim + e;
+    const uint32_t *base = static_cast<const uint32_t *>(a.q);
+    R.qw[it] = base[f32 ? idx : (idx >> 1)];
+  }
+  const int i = tid & 127, half = (tid >> 7) & 1;
+#pragma unroll
+  for (int k = 0; k < 64; ++k) R.sk[k] = a.St[(half * 64 + k) * kQjlDim + i];
+}
+
+// The operands, for the head tiles NU the calling wave scores (all waves run
+// this; it ends on a barrier after which the scratch space may be reused).
+template <int T, int NU, bool PACK>
+__device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &L, const QPrepRegs<T> &R, int tid,
+                                              int wave, const int (&tiles)[NU], v8i (&Aq)[NU][5],
+                                              int (&scq)[NU][5], v4f (&cinit)[NU], v4f (&qinit)[NU]) {
+  const int lane = tid & 63, G = a.group;
+  // q to LDS, zero rows for absent heads
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int e = tid + 256 * T * it;
+    if (e < 4 * T * kHeadDim) {
+      float v = 0.0f;
+      if (e < G * kHeadDim) {
+        const uint32_t w = R.qw[it];
+        if (a.q_dtype == TQ_F32) v = __uint_as_float(w);
+        else {
+          const uint32_t hbits = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+          v = a.q_dtype == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hbits) : __uint_as_float(hbits << 16);
+        }
+      }
+      L.qs[e >> 7][e & 127] = v;
+    }
+  }
+  lds_barrier();
+  // thread (i, half, hg): half of (S q)_i for heads 4 hg .. 4 hg + 3
+  {
+    const int i = tid & 127, half = (tid >> 7) & 1, hg = tid >> 8;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 x = *reinterpret_cast<const float4 *>(&L.qs[4 * hg + j][64 * half + 4 * k]);  // broadcast
+        acc[j] = fmaf(R.sk[4 * k], x.x, acc[j]);
+        acc[j] = fmaf(R.sk[4 * k + 1], x.y, acc[j]);
+        acc[j] = fmaf(R.sk[4 * k + 2], x.z, acc[j]);
+        acc[j] = fmaf(R.sk[4 * k + 3], x.w, acc[j]);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L.part[half][4 * hg + j][i] = acc[j];
+  }
+  // wave w rotates head w
+  float x0 = L.qs[wave][lane], x1 = L.qs[wave][lane + 64];
+  wave_fwht128(x0, x1, lane);
+  L.qr[wave][lane] = x0;
+  L.qr[wave][lane + 64] = x1;
+  const float hq = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  lds_barrier();
+  const float qjl = a.cb.qjl_scale;
+  const float s0 = qjl * (L.part[0][wave][lane] + L.part[1][wave][lane]);
+  const float s1 = qjl * (L.part[0][wave][lane + 64] + L.part[1][wave][lane + 64]);
+  L.sv[wave][lane] = s0;
+  L.sv[wave][lane + 64] = s1;
+  const float hs = wave_max(fmaxf(fabsf(s0), fabsf(s1)));
+  lds_barrier();  // s of every head; part is reused for the codes
+  // wave w: the digits of head w (its own q' and s were written by itself)
+  float beta[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
+  const float cs = a.scale * kLog2e;
+  int pe[5];
+#pragma unroll
+  for (int p = 0; p < 5; ++p) {
+    const float M = cs * (p < 4 ? fabsf(beta[p]) * hq : hs);
+    pe[p] = M > 0.0f ? max(bound_exponent(M), -100) : INT_MIN;
+  }
+  if (lane < 5) L.pe[wave][lane] = lane == 0 ? pe[0] : lane == 1 ? pe[1] : lane == 2 ? pe[2] : lane == 3 ? pe[3] : pe[4];
+  float sc4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int hk = 0; hk < 2; ++hk) {
+    const int kap = lane + 64 * hk, bc = b_coord(kap);
+    const float f = b_split_factor(kap), wgt = b_split_weight(kap);
+    const float qv = L.qr[wave][bc], sv = L.sv[wave][bc];
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      const bool pz = pe[p] != INT_MIN;
+      const int E = pz ? pe[p] : 0;
+      const float x = p < 4 ? -cs * beta[p] * qv : -cs * sv;
+      // Y = rint(x 2^(19-E)) = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16
+      const float y = pz ? rintf(ldexpf(x, 19 - E)) : 0.0f;
+      const float d0 = rintf(y * 0x1p-15f);
+      float rem = y - d0 * 32768.0f;
+      const float d1 = rintf(rem * 0x1p-10f);
+      rem -= d1 * 1024.0f;
+      const float d2 = rintf(rem * 0.03125f);
+      const float d3 = rem - d2 * 32.0f;
+      L.codes[wave][p][0][kap] = (uint8_t)fp6_code(d0 * f);
+      L.codes[wave][p][1][kap] = (uint8_t)fp6_code(d1 * f);
+      L.codes[wave][p][2][kap] = (uint8_t)fp6_code(d2 * f);
+      L.codes[wave][p][3][kap] = (uint8_t)fp6_code(d3 * f);
+      const float v0 = wgt * ldexpf(d0, E - 4), v1 = wgt * ldexpf(d1, E - 9);
+      const float v2 = wgt * ldexpf(d2, E - 14), v3 = wgt * ldexpf(d3, E - 19);
+      if (p < 4) {
+        sc4[0] += v0; sc4[1] += v1; sc4[2] += v2; sc4[3] += v3;
+      } else {
+        sq4[0] += v0; sq4[1] += v1; sq4[2] += v2; sq4[3] += v3;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc4[r] = wave_sum(sc4[r]);
+    sq4[r] = wave_sum(sq4[r]);
+  }
+  if (lane == 0) {  // uniform values (no lane-indexed register arrays)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      L.ssum[wave][r] = sc4[r];
+      L.ssum[wave][4 + r] = sq4[r];
+    }
+  }
+  lds_barrier();
+  // this lane's operand rows: (head 4u + gp, digit r), K-block ga
+  const int ga = lane >> 4, gp = (lane & 15) >> 2, r = lane & 3, grow = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < (PACK ? NU : 0); ++n) {
+    const int hd = 4 * tiles[n] + gp;
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      const uint4 c0 = *reinterpret_cast<const uint4 *>(&L.codes[hd][p][r][32 * ga]);
+      const uint4 c1 = *reinterpret_cast<const uint4 *>(&L.codes[hd][p][r][32 * ga + 16]);
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      uint32_t q24[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t v = cw[k];
+        q24[k] = (v & 0x3Fu) | ((v >> 2) & 0xFC0u) | ((v >> 4) & 0x3F000u) | ((v >> 6) & 0xFC0000u);
+      }
+      Aq[n][p] = v8i{(int)(q24[0] | (q24[1] << 24)), (int)((q24[1] >> 8) | (q24[2] << 16)),
+                     (int)((q24[2] >> 16) | (q24[3] << 8)), (int)(q24[4] | (q24[5] << 24)),
+                     (int)((q24[5] >> 8) | (q24[6] << 16)), (int)((q24[6] >> 16) | (q24[7] << 8)), 0, 0};
+      const int E = L.pe[hd][p];
+      scq[n][p] = E != INT_MIN ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One;
+    }
+    const float *ss = L.ssum[4 * tiles[n] + grow];
+    cinit[n] = v4f{ss[0], ss[1], ss[2], ss[3]};
+    qinit[n] = v4f{ss[4], ss[5], ss[6], ss[7]};
+  }
+  lds_barrier();  // the scratch space is free again
+}
+
+
 template <int T, int R>
 __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, SplitLds<T> &sm) {
   constexpr int NW = 4 * T;   // waves
@@ -638,24 +703,16 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
     }
   }
 
-  // query-side operands of the score contraction: head tile su
-  v8i Aq[5];
-  int scq[5];
-  v4f cinit, qinit;  // accumulator start values (see b_split)
-  {
-    const uint32_t *qa = a.qa + grp * (int64_t)(T * (5 * 64 * 9 + 32));
-#pragma unroll
-    for (int p = 0; p < 5; ++p) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((su * 5 + p) * 64 + lane) * 8);
-      const uint4 u0 = src[0];
-      const uint2 u1 = *reinterpret_cast<const uint2 *>(src + 1);
-      Aq[p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, 0, 0};
-      scq[p] = (int)qa[T * 5 * 64 * 8 + (su * 5 + p) * 64 + lane];
-    }
-    const float *ci = reinterpret_cast<const float *>(qa + T * 5 * 64 * 9) + (su * 4 + grow) * 8;
-    cinit = v4f{ci[0], ci[1], ci[2], ci[3]};
-    qinit = v4f{ci[4], ci[5], ci[6], ci[7]};
-  }
+  // query-side operands of the score contraction (head tile su), formed in
+  // the prologue; their loads go out first
+  QPrepRegs<T> qpr;
+  qprep_loads<T>(a, grp, tid, qpr);
+  v8i AqT[1][5];
+  int scqT[1][5];
+  v4f ciT[1], qiT[1];
+  v8i (&Aq)[5] = AqT[0];
+  int (&scq)[5] = scqT[0];
+  v4f &cinit = ciT[0], &qinit = qiT[0];  // accumulator start values (see b_split)
   float beta[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
@@ -925,6 +982,13 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
     load_k_part<R>(SB, sp, c0, c1);
     load_v_part<R>(SA, sp, b0, b1);
     __builtin_amdgcn_sched_barrier(0);
+    // the query operands while these tiles are in flight (scratch in the
+    // staging buffers, which are written from here on)
+    {
+      const int tiles[1] = {su};
+      qprep_compute<T, 1, true>(a, *reinterpret_cast<QPrepLds<T> *>(&sm.kbuf[0][0]), qpr, tid, wave, tiles, AqT,
+                                scqT, ciT, qiT);
+    }
     store_k_part<R>(sm.kbuf[0], SA, sp, lane);
     load_k_part<R>(SA, sp, d0, d1);
     load_v_part<R>(SB, sp, c0, c1);
@@ -1053,27 +1117,13 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
     }
   }
 
-  // role 0: query-side operands of the score contraction, both head tiles
+  // role 0: query-side operands of the score contraction, both head tiles,
+  // formed in the prologue; their loads go out first
+  QPrepRegs<T> qpr;
+  qprep_loads<T>(a, grp, tid, qpr);
   v8i Aq[T][5];
   int scq[T][5];
   v4f cinit[T], qinit[T];
-  if constexpr (R == 0) {
-    const uint32_t *qa = a.qa + grp * (int64_t)(T * (5 * 64 * 9 + 32));
-#pragma unroll
-    for (int u = 0; u < T; ++u) {
-#pragma unroll
-      for (int p = 0; p < 5; ++p) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(qa + ((u * 5 + p) * 64 + lane) * 8);
-        const uint4 u0 = src[0];
-        const uint2 u1 = *reinterpret_cast<const uint2 *>(src + 1);
-        Aq[u][p] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, 0, 0};
-        scq[u][p] = (int)qa[T * 5 * 64 * 8 + (u * 5 + p) * 64 + lane];
-      }
-      const float *ci = reinterpret_cast<const float *>(qa + T * 5 * 64 * 9) + (u * 4 + grow) * 8;
-      cinit[u] = v4f{ci[0], ci[1], ci[2], ci[3]};
-      qinit[u] = v4f{ci[4], ci[5], ci[6], ci[7]};
-    }
-  }
   float beta[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
@@ -1302,6 +1352,14 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
     load_k_part<R>(SB, sp, c0, c1);
     load_v_part<R>(SA, sp, b0, b1);
     __builtin_amdgcn_sched_barrier(0);
+    // the query operands while these tiles are in flight (scratch in the
+    // staging buffers, which are written from here on); role 1 takes part in
+    // the work and the barriers but keeps no operands
+    {
+      const int tiles[2] = {0, 1};
+      qprep_compute<T, 2, R == 0>(a, *reinterpret_cast<QPrepLds<T> *>(&sm.kbuf[0][0]), qpr, tid, wave, tiles, Aq,
+                                  scq, cinit, qinit);
+    }
     store_k_part<R>(sm.kbuf[0], SA, sp, lane);
     load_k_part<R>(SA, sp, d0, d1);
     load_v_part<R>(SB, sp, c0, c1);
@@ -1511,27 +1569,29 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.q_len * a.num_q_heads;
   const unsigned row_blocks = (unsigned)((rows + 3) / 4);
   const int64_t groups = (int64_t)a.num_seqs * a.q_len * a.num_kv_heads;
-  hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups, (unsigned)a.group), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.qa != nullptr) {  // matrix-core pass: one workgroup per (chunk, KV head, head tile)
+  hipError_t e = hipSuccess;
+  if (a.qk_tiles > 0) {  // matrix-core pass, its own query operands: a workgroup per (chunk, KV head)
     if (a.qk_tiles != 1 && a.qk_tiles != 2) return hipErrorInvalidValue;
     const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_splits;
     if (a.qk_tiles == 1)
       hipLaunchKernelGGL(split_mfma_kernel<1>, dim3((unsigned)items), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)items), dim3(512), 0, stream, a);
-  } else if (prefill_uses_mfma(a.q_len, a.group)) {
-    e = launch_prefill(a, stream);
-    if (e != hipSuccess) return e;
   } else {
-    switch (a.group) {
-      case 1: e = launch_split<1>(a, stream); break;
-      case 2: e = launch_split<2>(a, stream); break;
-      case 4: e = launch_split<4>(a, stream); break;
-      case 8: e = launch_split<8>(a, stream); break;
-      case 16: e = launch_split<16>(a, stream); break;
-      default: return hipErrorInvalidValue;
+    hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups, (unsigned)a.group), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (prefill_uses_mfma(a.q_len, a.group)) {
+      e = launch_prefill(a, stream);
+    } else {
+      switch (a.group) {
+        case 1: e = launch_split<1>(a, stream); break;
+        case 2: e = launch_split<2>(a, stream); break;
+        case 4: e = launch_split<4>(a, stream); break;
+        case 8: e = launch_split<8>(a, stream); break;
+        case 16: e = launch_split<16>(a, stream); break;
+        default: return hipErrorInvalidValue;
+      }
     }
     if (e != hipSuccess) return e;
   }

@@ -147,10 +147,6 @@ size_t decode_partial_floats(int64_t rows, int num_splits) {
 }
 bool decode_uses_mfma(int q_len, int group) { return q_len == 1 && group <= 8; }
 int decode_qk_tiles(int group) { return group <= 4 ? 1 : group / 4; }
-size_t decode_qa_words(int64_t groups, int qk_tiles) {
-  // per tile: 8 operand words + 1 scale per lane and plane, 4 heads x 8 start values
-  return (size_t)groups * (size_t)qk_tiles * (5 * 64 * 9 + 32);
-}
 }  // namespace tq
 
 extern "C" {
@@ -343,12 +339,9 @@ size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
   const int grp = num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
   plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split, &stok, &ns);
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
-  size_t words = tq::decode_qprep_floats(rows) + tq::decode_partial_floats(rows, ns);
-  if (num_q_heads % num_kv_heads == 0) {
-    const int group = num_q_heads / num_kv_heads;
-    if (tq::decode_uses_mfma(q_len, group))
-      words += tq::decode_qa_words((int64_t)num_seqs * num_kv_heads, tq::decode_qk_tiles(group));
-  }
+  // the matrix-core split pass forms its query operands itself: partials only
+  const bool mfma = grp > 0 && tq::decode_uses_mfma(q_len, grp);
+  const size_t words = (mfma ? 0 : tq::decode_qprep_floats(rows)) + tq::decode_partial_floats(rows, ns);
   return words * sizeof(float);
 }
 
@@ -412,15 +405,14 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
   a.num_splits = ns;
   a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
-  a.qprep = (float *)workspace;
-  float *rest = (float *)workspace + tq::decode_qprep_floats(rows);
-  a.qa = nullptr;
   a.qk_tiles = 0;
+  a.qprep = nullptr;
+  float *rest = (float *)workspace;
   if (tq::decode_uses_mfma(q_len, group)) {
-    const int64_t groups = (int64_t)num_seqs * num_kv_heads;
-    a.qa = (uint32_t *)rest;
     a.qk_tiles = tq::decode_qk_tiles(group);
-    rest += tq::decode_qa_words(groups, a.qk_tiles);
+  } else {
+    a.qprep = rest;
+    rest += tq::decode_qprep_floats(rows);
   }
   a.partials = rest;
   a.cb = device_codebook(cb);

@@ -71,12 +71,11 @@ struct DecodeArgs {
   int split_tokens;
   int num_splits;
   const float *St;     // [d][m]
-  float *qprep;        // workspace: [rows][256] = rotated q | qjl_scale * S q
-  // Matrix-core path only (else null): per (sequence, KV head) group the
-  // query-side A operands of the score contraction, [tiles][5][64 lanes][8]
-  // words, followed by their E8M0 scales [tiles][5][64].
-  uint32_t *qa;
-  int qk_tiles;        // 16-row operand tiles per group: 4 heads x 4 digits each
+  float *qprep;        // workspace (vector and prefill passes): [rows][256] = rotated q | qjl_scale * S q
+  // Matrix-core split pass (single-query decode, at most 8 heads per KV
+  // head): 16-row operand tiles per group (4 heads x 4 digits each), which
+  // the pass forms itself; 0 for the other passes.
+  int qk_tiles;
   float *partials;     // workspace: [rows][num_splits][4 + 128], m in log2 units
   Codebook cb;
 };
@@ -93,7 +92,6 @@ bool decode_uses_mfma(int q_len, int group);
 bool prefill_uses_mfma(int q_len, int group);
 int prefill_block_queries(int group);
 int decode_qk_tiles(int group);
-size_t decode_qa_words(int64_t groups, int qk_tiles);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

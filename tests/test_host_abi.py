@@ -139,15 +139,14 @@ def test_decode_validation():
     assert _dec(cb, wsb=need - 1) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
 
 
-def _operand_words(B, q_len, Hq, Hkv):
-    """Matrix-core operand words: single-query decode with <= 8 heads per KV
-    head keeps, per (sequence, KV head) and operand tile, 5 x 64 lanes x (8 + 1)
-    words and 4 heads x 8 accumulator start values."""
+def _prep_words(B, q_len, Hq, Hkv):
+    """Query prep floats: the vector and prefill passes keep q' and s (256
+    floats) per query row; single-query decode with <= 8 heads per KV head
+    forms its operands inside the split pass and keeps none."""
     G = Hq // Hkv
-    if q_len != 1 or G > 8:
+    if q_len == 1 and G <= 8:
         return 0
-    tiles = 1 if G <= 4 else G // 4
-    return B * Hkv * tiles * (5 * 64 * 9 + 32)
+    return B * q_len * Hq * 256
 
 
 @pytest.mark.parametrize("B,q_len,Hq,Hkv", [(1, 1, 32, 8), (2, 1, 32, 4), (1, 1, 32, 32),
@@ -156,10 +155,10 @@ def test_workspace_plan_is_consistent(B, q_len, Hq, Hkv):
     cb = _fake_cb()
     ref = ctypes.byref(cb)
     rows = B * q_len * Hq
-    # 4 bytes x (rows x 256 prep floats + operand words + rows x splits x 132 partial floats)
+    # 4 bytes x (prep floats + rows x splits x 132 partial floats)
     for maxc, tps in ((8192, 256), (8192, 1024), (131072, 0), (0, 0), (1, 0)):
         ws = tq._lib.tq_decode_workspace_bytes(ref, B, q_len, Hq, Hkv, max(maxc, q_len), tps)
-        words = ws // 4 - rows * 256 - _operand_words(B, q_len, Hq, Hkv)
+        words = ws // 4 - _prep_words(B, q_len, Hq, Hkv)
         assert ws % 4 == 0 and words % (rows * 132) == 0
         splits = words // (rows * 132)
         assert splits >= 1
