@@ -486,104 +486,115 @@ using flag = std::integral_constant<bool, B>;
 // small amount of work (16 K multiply-adds per head) instead of waiting for a
 // separate launch and a round trip of its results through memory.  The
 // scratch space aliases the staging buffers, which are first written after it.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
 template <int T>
 struct QPrepLds {
-  float qs[4 * T][kHeadDim];           // q (zero rows for absent heads)
-  float qr[4 * T][kHeadDim];           // q' = H q
+  float qr[4 * T][kHeadDim];           // q' = H q (zero rows for absent heads)
   float sv[4 * T][kQjlDim];            // s = alpha S q
-  union {
-    float part[2][4 * T][kQjlDim];     // halves of S q
-    uint8_t codes[4 * T][5][4][128];   // [head][plane][digit][K slot] fp6 codes
-  };
+  _Float16 qh[4 * T][kHeadDim];        // q' as f16 hi + lo halves in slot order
+  _Float16 ql[4 * T][kHeadDim];        //   (slot s <-> coordinate 16 (s % 8) + s / 8)
+  uint8_t codes[4 * T][5][4][128];     // [head][plane][digit][K slot] fp6 codes
   int pe[4 * T][5];                    // per head and plane: E, or INT_MIN for a zero plane
-  float ssum[4 * T][8];                // start values: code planes (digit 0..3), sign plane
 };
-
 static_assert(sizeof(QPrepLds<1>) <= 2 * kTilePages * kKRec + 2 * 4 * kVPair, "query scratch exceeds the staging buffers");
 static_assert(sizeof(QPrepLds<2>) <= 2 * kTilePages * kKRec + 2 * 4 * kVPair, "query scratch exceeds the staging buffers");
 
 // Loads issued first in the workgroup, so that waiting for them does not wait
-// for the tile loads issued after them: this thread's q elements (one
-// unconditional dword each, converted later) and S^T column i for the k half
-// of S q it takes.
-template <int T>
+// for the tile loads issued after them: wave w's q elements lane and lane + 64
+// of head w (one unconditional dword each, converted later; an absent head
+// repeats the last one) and, for a wave that forms part of s (waves 0..3),
+// its rows 32 w .. 32 w + 31 of S H as the f16 operands of the projection.
+template <bool PROJ>
 struct QPrepRegs {
   uint32_t qw[2];
-  float sk[64];
+  uint4 sh[PROJ ? 16 : 1];
 };
-template <int T>
-__device__ __forceinline__ void qprep_loads(const DecodeArgs &a, int64_t grp, int tid, QPrepRegs<T> &R) {
+template <bool PROJ>
+__device__ __forceinline__ void qprep_loads(const DecodeArgs &a, int64_t grp, int wave, int lane, QPrepRegs<PROJ> &R) {
   const int G = a.group;
   const bool f32 = a.q_dtype == TQ_F32;
+  const int64_t row = grp * G + min(wave, G - 1);
+  const uint32_t *base = static_cast<const uint32_t *>(a.q);
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int e = min(tid + 256 * T * it, G * kHeadDim - 1);  // past the rows: repeats the last element
-    const int64_t idx = grp * G * kHeadDim + e;
-    const uint32_t *base = static_cast<const uint32_t *>(a.q);
-    R.qw[it] = base[f32 ? idx : (idx >> 1)];
+  for (int j = 0; j < 2; ++j) {
+    const int64_t idx = row * kHeadDim + lane + 64 * j;
+    R.qw[j] = base[f32 ? idx : (idx >> 1)];
   }
-  const int i = tid & 127, half = (tid >> 7) & 1;
+  if constexpr (PROJ) {
+    const uint4 *shop = reinterpret_cast<const uint4 *>(a.SHop) + wave * 2 * 4 * 2 * 64 + lane;
 #pragma unroll
-  for (int k = 0; k < 64; ++k) R.sk[k] = a.St[(half * 64 + k) * kQjlDim + i];
+    for (int e = 0; e < 16; ++e) R.sh[e] = shop[e * 64];
+  }
 }
 
-// The operands, for the head tiles NU the calling wave scores (all waves run
-// this; it ends on a barrier after which the scratch space may be reused).
-template <int T, int NU, bool PACK>
-__device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &L, const QPrepRegs<T> &R, int tid,
+// The operands, for the head tiles NU the calling wave scores (every wave of
+// the workgroup runs this; it ends on a barrier after which the scratch space
+// may be reused).  Wave w rotates and digitises head w.
+template <int T, int NU, bool PACK, bool PROJ>
+__device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &L, const QPrepRegs<PROJ> &R, int tid,
                                               int wave, const int (&tiles)[NU], v8i (&Aq)[NU][5],
                                               int (&scq)[NU][5], v4f (&cinit)[NU], v4f (&qinit)[NU]) {
   const int lane = tid & 63, G = a.group;
-  // q to LDS, zero rows for absent heads
+  float x[2];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int e = tid + 256 * T * it;
-    if (e < 4 * T * kHeadDim) {
-      float v = 0.0f;
-      if (e < G * kHeadDim) {
-        const uint32_t w = R.qw[it];
-        if (a.q_dtype == TQ_F32) v = __uint_as_float(w);
-        else {
-          const uint32_t hbits = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-          v = a.q_dtype == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hbits) : __uint_as_float(hbits << 16);
-        }
-      }
-      L.qs[e >> 7][e & 127] = v;
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t w = R.qw[j];
+    float v;
+    if (a.q_dtype == TQ_F32) {
+      v = __uint_as_float(w);
+    } else {
+      const uint32_t hb = (lane & 1) ? (w >> 16) : (w & 0xFFFFu);  // element lane + 64 j has the parity of lane
+      v = a.q_dtype == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hb) : __uint_as_float(hb << 16);
     }
+    x[j] = wave < G ? v : 0.0f;
+  }
+  wave_fwht128(x[0], x[1], lane);
+  L.qr[wave][lane] = x[0];
+  L.qr[wave][lane + 64] = x[1];
+  const float hq = wave_max(fmaxf(fabsf(x[0]), fabsf(x[1])));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = lane + 64 * j, sl = 8 * (c & 15) + (c >> 4);
+    const _Float16 hi = (_Float16)x[j];
+    L.qh[wave][sl] = hi;
+    L.ql[wave][sl] = (_Float16)(x[j] - (float)hi);
   }
   lds_barrier();
-  // thread (i, half, hg): half of (S q)_i for heads 4 hg .. 4 hg + 3
-  {
-    const int i = tid & 127, half = (tid >> 7) & 1, hg = tid >> 8;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (PROJ) {
+    // s = alpha (S H) q' for rows 32 w .. 32 w + 31, all heads: three f16
+    // passes (hi hi + hi lo + lo hi, ~22 bits); A rows past the heads are zero
+    const int hr = lane & 15;
+    const bool live = hr < 4 * T;
+    v4f z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < 4; ++k) {
+      const int row = live ? hr : 0, col = 32 * k + 8 * (lane >> 4);
+      const uint4 h4 = *reinterpret_cast<const uint4 *>(&L.qh[row][col]);
+      const uint4 l4 = *reinterpret_cast<const uint4 *>(&L.ql[row][col]);
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+      const v8h ah = __builtin_bit_cast(v8h, live ? h4 : zero), al = __builtin_bit_cast(v8h, live ? l4 : zero);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 x = *reinterpret_cast<const float4 *>(&L.qs[4 * hg + j][64 * half + 4 * k]);  // broadcast
-        acc[j] = fmaf(R.sk[4 * k], x.x, acc[j]);
-        acc[j] = fmaf(R.sk[4 * k + 1], x.y, acc[j]);
-        acc[j] = fmaf(R.sk[4 * k + 2], x.z, acc[j]);
-        acc[j] = fmaf(R.sk[4 * k + 3], x.w, acc[j]);
+      for (int u = 0; u < 2; ++u) {
+        const v8h bh = __builtin_bit_cast(v8h, R.sh[(u * 4 + k) * 2]), bl = __builtin_bit_cast(v8h, R.sh[(u * 4 + k) * 2 + 1]);
+        z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, z[u], 0, 0, 0);
+        z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, z[u], 0, 0, 0);
+        z[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, z[u], 0, 0, 0);
       }
+    }
+    // lane l, register i: head 4 (l / 16) + i, row 16 (2 w + u) + l % 16
+    const float qjl = a.cb.qjl_scale;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) L.part[half][4 * hg + j][i] = acc[j];
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * (lane >> 4) + i;
+        if (hd < 4 * T) L.sv[hd][16 * (2 * wave + u) + (lane & 15)] = qjl * z[u][i];
+      }
   }
-  // wave w rotates head w
-  float x0 = L.qs[wave][lane], x1 = L.qs[wave][lane + 64];
-  wave_fwht128(x0, x1, lane);
-  L.qr[wave][lane] = x0;
-  L.qr[wave][lane + 64] = x1;
-  const float hq = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
   lds_barrier();
-  const float qjl = a.cb.qjl_scale;
-  const float s0 = qjl * (L.part[0][wave][lane] + L.part[1][wave][lane]);
-  const float s1 = qjl * (L.part[0][wave][lane + 64] + L.part[1][wave][lane + 64]);
-  L.sv[wave][lane] = s0;
-  L.sv[wave][lane + 64] = s1;
-  const float hs = wave_max(fmaxf(fabsf(s0), fabsf(s1)));
-  lds_barrier();  // s of every head; part is reused for the codes
-  // wave w: the digits of head w (its own q' and s were written by itself)
+  const float hs = wave_max(fmaxf(fabsf(L.sv[wave][lane]), fabsf(L.sv[wave][lane + 64])));
+  // wave w: the digits of head w
   float beta[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
@@ -595,11 +606,10 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
     pe[p] = M > 0.0f ? max(bound_exponent(M), -100) : INT_MIN;
   }
   if (lane < 5) L.pe[wave][lane] = lane == 0 ? pe[0] : lane == 1 ? pe[1] : lane == 2 ? pe[2] : lane == 3 ? pe[3] : pe[4];
-  float sc4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int hk = 0; hk < 2; ++hk) {
     const int kap = lane + 64 * hk, bc = b_coord(kap);
-    const float f = b_split_factor(kap), wgt = b_split_weight(kap);
+    const float f = b_split_factor(kap);
     const float qv = L.qr[wave][bc], sv = L.sv[wave][bc];
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
@@ -618,30 +628,16 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
       L.codes[wave][p][1][kap] = (uint8_t)fp6_code(d1 * f);
       L.codes[wave][p][2][kap] = (uint8_t)fp6_code(d2 * f);
       L.codes[wave][p][3][kap] = (uint8_t)fp6_code(d3 * f);
-      const float v0 = wgt * ldexpf(d0, E - 4), v1 = wgt * ldexpf(d1, E - 9);
-      const float v2 = wgt * ldexpf(d2, E - 14), v3 = wgt * ldexpf(d3, E - 19);
-      if (p < 4) {
-        sc4[0] += v0; sc4[1] += v1; sc4[2] += v2; sc4[3] += v3;
-      } else {
-        sq4[0] += v0; sq4[1] += v1; sq4[2] += v2; sq4[3] += v3;
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    sc4[r] = wave_sum(sc4[r]);
-    sq4[r] = wave_sum(sq4[r]);
-  }
-  if (lane == 0) {  // uniform values (no lane-indexed register arrays)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      L.ssum[wave][r] = sc4[r];
-      L.ssum[wave][4 + r] = sq4[r];
     }
   }
   lds_barrier();
-  // this lane's operand rows: (head 4u + gp, digit r), K-block ga
-  const int ga = lane >> 4, gp = (lane & 15) >> 2, r = lane & 3, grow = lane >> 4;
+  // this lane's operand rows: (head 4u + gp, digit r), K-block ga.  The
+  // start values (see b_split), sum_k (1 - f_v alpha_v) A_k = -sum_k w_v A_k
+  // with w_v = 5, 3, 1, 0, are two matrix ops per plane against the constant
+  // operands -(4, 3, 1, 0) and -(1, 0, 0, 0) (e2m1 codes E, D, A and A).
+  const int ga = lane >> 4, gp = (lane & 15) >> 2, r = lane & 3;
+  const v8i W1 = v8i{(int)0xEEEEEEEEu, (int)0xDDDDDDDDu, (int)0xAAAAAAAAu, 0, 0, 0, 0, 0};
+  const v8i W2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int n = 0; n < (PACK ? NU : 0); ++n) {
     const int hd = 4 * tiles[n] + gp;
@@ -662,9 +658,15 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
       const int E = L.pe[hd][p];
       scq[n][p] = E != INT_MIN ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One;
     }
-    const float *ss = L.ssum[4 * tiles[n] + grow];
-    cinit[n] = v4f{ss[0], ss[1], ss[2], ss[3]};
-    qinit[n] = v4f{ss[4], ss[5], ss[6], ss[7]};
+    v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      c = mfma_f6f4(Aq[n][p], W1, c, scq[n][p]);
+      c = mfma_f6f4(Aq[n][p], W2, c, scq[n][p]);
+    }
+    cinit[n] = c;
+    const v4f z = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    qinit[n] = mfma_f6f4(Aq[n][4], W2, mfma_f6f4(Aq[n][4], W1, z, scq[n][4]), scq[n][4]);
   }
   lds_barrier();  // the scratch space is free again
 }
@@ -705,8 +707,8 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
 
   // query-side operands of the score contraction (head tile su), formed in
   // the prologue; their loads go out first
-  QPrepRegs<T> qpr;
-  qprep_loads<T>(a, grp, tid, qpr);
+  QPrepRegs<true> qpr;
+  qprep_loads<true>(a, grp, wave, lane, qpr);
   v8i AqT[1][5];
   int scqT[1][5];
   v4f ciT[1], qiT[1];
@@ -986,7 +988,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
     // staging buffers, which are written from here on)
     {
       const int tiles[1] = {su};
-      qprep_compute<T, 1, true>(a, *reinterpret_cast<QPrepLds<T> *>(&sm.kbuf[0][0]), qpr, tid, wave, tiles, AqT,
+      qprep_compute<T, 1, true, true>(a, *reinterpret_cast<QPrepLds<T> *>(&sm.kbuf[0][0]), qpr, tid, wave, tiles, AqT,
                                 scqT, ciT, qiT);
     }
     store_k_part<R>(sm.kbuf[0], SA, sp, lane);
@@ -1119,8 +1121,8 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
 
   // role 0: query-side operands of the score contraction, both head tiles,
   // formed in the prologue; their loads go out first
-  QPrepRegs<T> qpr;
-  qprep_loads<T>(a, grp, tid, qpr);
+  QPrepRegs<R == 0> qpr;
+  qprep_loads<R == 0>(a, grp, wave, lane, qpr);
   v8i Aq[T][5];
   int scq[T][5];
   v4f cinit[T], qinit[T];
@@ -1357,7 +1359,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
     // the work and the barriers but keeps no operands
     {
       const int tiles[2] = {0, 1};
-      qprep_compute<T, 2, R == 0>(a, *reinterpret_cast<QPrepLds<T> *>(&sm.kbuf[0][0]), qpr, tid, wave, tiles, Aq,
+      qprep_compute<T, 2, R == 0, R == 0>(a, *reinterpret_cast<QPrepLds<T> *>(&sm.kbuf[0][0]), qpr, tid, wave, tiles, Aq,
                                   scq, cinit, qinit);
     }
     store_k_part<R>(sm.kbuf[0], SA, sp, lane);

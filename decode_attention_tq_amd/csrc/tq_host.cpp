@@ -404,6 +404,7 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
   a.split_tokens = stok;
   a.num_splits = ns;
   a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
+  a.SHop = (const uint16_t *)(a.St + (size_t)tq::kQjlDim * tq::kHeadDim);
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   a.qk_tiles = 0;
   a.qprep = nullptr;

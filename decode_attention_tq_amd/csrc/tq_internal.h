@@ -71,6 +71,7 @@ struct DecodeArgs {
   int split_tokens;
   int num_splits;
   const float *St;     // [d][m]
+  const uint16_t *SHop;  // S H as f16 hi, lo halves in the projection's operand order
   float *qprep;        // workspace (vector and prefill passes): [rows][256] = rotated q | qjl_scale * S q
   // Matrix-core split pass (single-query decode, at most 8 heads per KV
   // head): 16-row operand tiles per group (4 heads x 4 digits each), which
