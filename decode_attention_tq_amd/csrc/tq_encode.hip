@@ -303,16 +303,18 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
 
   // Inputs and slot of this lane's token (l%16) in the wave's tile of round
   // R.  Every load is unconditional (past the last tile or token the address
-  // repeats the last one and the result is discarded), so that the number
-  // of loads in flight is known at every point and a prefetched round is
-  // waited for only where it is used.
-  auto load_round = [&](int64_t R, In<PC> &ik, In<PC> &iv, int64_t &slot) {
+  // repeats the last one and the result is discarded; after the wave's last
+  // round every lane reads the first element, one cache line), so that the
+  // number of loads in flight is known at every point and a prefetched round
+  // is waited for only where it is used.
+  auto load_round = [&](int64_t R, In<PC> &ik, In<PC> &iv, int64_t &slot, bool none) {
     int64_t tile = R * kTiles + wave;
     tile = tile < num_tiles ? tile : num_tiles - 1;
     const int h = (int)(tile % H);
     int64_t t = (tile / H) * kTok + l16;
     t = t < ntok ? t : ntok - 1;
-    const int64_t e0 = t * tok_stride + (int64_t)h * head_stride + 8 * lg;
+    t = none ? 0 : t;
+    const int64_t e0 = none ? 0 : t * tok_stride + (int64_t)h * head_stride + 8 * lg;
     // in the order of use, kept by scheduling barriers: the compiler's
     // count of loads in flight must agree at the loop entry and its back edge
     slot = slots[t];
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
 
   In<PC> ik, iv;
   int64_t slot;
-  load_round(blockIdx.x, ik, iv, slot);  // the grid has at most one workgroup per round
+  load_round(blockIdx.x, ik, iv, slot, false);  // the grid has at most one workgroup per round
 
   for (int64_t R = blockIdx.x; R < nrounds; R += gridDim.x) {
     const int64_t tile = R * kTiles + wave;
@@ -486,7 +488,8 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         shi[u][k] = __builtin_bit_cast(v8s, shop[((u * 4 + k) * 2) * 64]);
         slo[u][k] = __builtin_bit_cast(v8s, shop[((u * 4 + k) * 2 + 1) * 64]);
       }
-    load_round(R + gridDim.x < nrounds ? R + gridDim.x : R, ik, iv, slot);
+    const bool more = R + gridDim.x < nrounds;  // uniform
+    load_round(more ? R + gridDim.x : R, ik, iv, slot, !more);
     lds_barrier();
 
     // ---- QJL projection: rows 32w .. 32w+31 for the four tiles -------------
