@@ -181,6 +181,25 @@ def test_decode_edge_cases_and_dtypes():
     check_decode(out, q, kp, vp, case["table"], L, scale=0.3)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (16, 2)])
+def test_matrix_core_pass_query_dtypes(Hq, Hkv):
+    """The matrix-core pass forms its query operands from raw q words: fp16
+    and fp32 queries (elements in both halves of a word) with four and eight
+    heads per KV head, ragged contexts including an empty one."""
+    cb = codebook()
+    case = synth.ragged_case(seed=13, B=3, Hq=Hq, Hkv=Hkv, lengths=[0, 300, 1300])
+    kpool, vpool = new_pools(case["num_blocks"], Hkv)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    kp, vp = _np(kpool), _np(vpool)
+    L = case["lengths"].astype(np.int32)
+    q = case["q"][0]
+    for qd in (torch.float16, torch.float32):
+        out = decode_gpu(cb, q, kpool, vpool, case["table"], L, Hkv, q_dtype=qd)
+        qq = dev(q, qd).float().cpu().numpy()
+        check_decode(out, qq, kp, vp, case["table"], L)
+        assert np.all(out[0] == 0)
+
+
 def test_split_invariance_permutation_invariance_determinism():
     cb = codebook()
     case = synth.gqa_case(seed=9, T=3000, Hq=16, Hkv=2)
