@@ -488,6 +488,17 @@ using flag = std::integral_constant<bool, B>;
 // scratch space aliases the staging buffers, which are first written after it.
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
+// Query rows of a (sequence, KV head) workgroup of the matrix-core pass:
+// row = i G + g for position t = pos0 + i of the q_len new ones and head g
+// of the group.  Its output row is (b q_len + t) Hq + h G + g, and it sees
+// the keys before L - q_len + t + 1 (multi-token verify is causal over the
+// new ones).
+__device__ __forceinline__ int64_t query_out_row(const DecodeArgs &a, int64_t grp, int row) {
+  const int G = a.group;
+  const int64_t b = grp / a.num_kv_heads, h = grp % a.num_kv_heads;
+  return (b * a.q_len + a.pos0 + row / G) * a.num_q_heads + h * G + row % G;
+}
+
 template <int T>
 struct QPrepLds {
   float qr[4 * T][kHeadDim];           // q' = H q (zero rows for absent heads)
@@ -512,9 +523,9 @@ struct QPrepRegs {
 };
 template <bool PROJ>
 __device__ __forceinline__ void qprep_loads(const DecodeArgs &a, int64_t grp, int wave, int lane, QPrepRegs<PROJ> &R) {
-  const int G = a.group;
+  const int rows = a.group * a.pos_count;
   const bool f32 = a.q_dtype == TQ_F32;
-  const int64_t row = grp * G + min(wave, G - 1);
+  const int64_t row = query_out_row(a, grp, min(wave, rows - 1));
   const uint32_t *base = static_cast<const uint32_t *>(a.q);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -535,7 +546,7 @@ template <int T, int NU, bool PACK, bool PROJ>
 __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &L, const QPrepRegs<PROJ> &R, int tid,
                                               int wave, const int (&tiles)[NU], v8i (&Aq)[NU][5],
                                               int (&scq)[NU][5], v4f (&cinit)[NU], v4f (&qinit)[NU]) {
-  const int lane = tid & 63, G = a.group;
+  const int lane = tid & 63, rows = a.group * a.pos_count;
   float x[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -547,7 +558,7 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
       const uint32_t hb = (lane & 1) ? (w >> 16) : (w & 0xFFFFu);  // element lane + 64 j has the parity of lane
       v = a.q_dtype == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hb) : __uint_as_float(hb << 16);
     }
-    x[j] = wave < G ? v : 0.0f;
+    x[j] = wave < rows ? v : 0.0f;
   }
   wave_fwht128(x[0], x[1], lane);
   L.qr[wave][lane] = x[0];
@@ -686,6 +697,10 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
   const int s0 = split * a.split_tokens;
   const int s1 = min(s0 + a.split_tokens, L);
   if (s0 >= s1) return;  // uniform
+  // query rows (positions x heads); every row sees the keys before s1v, row
+  // r those before min(s1, L - q_len + pos0 + r / G + 1)
+  const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count;
+  const int s1v = min(s1, L - qlen + 1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int su = wave >> 2, sq = wave & 3;  // scoring: head tile, page pair (K-block)
@@ -934,10 +949,11 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
 #pragma unroll
             for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[u][p][j]));
       }
-      const bool partial = s0 + 128 * (k + 1) > s1;  // uniform: the chunk's last tile
+      const bool partial = s0 + 128 * (k + 1) > s1v;  // uniform: a tile some row does not see whole
       if (__builtin_amdgcn_ballot_w64(x0 > (float)kRefStep || x1 > (float)kRefStep) || partial) {
         const int tok0 = s0 + 128 * k + 32 * sq + t16;
-        const bool v0 = tok0 < s1, v1 = tok0 + 16 < s1;
+        const int lim = min(s1, L - qlen + (4 * su + grow) / G + 1);  // the lane's row
+        const bool v0 = tok0 < lim, v1 = tok0 + 16 < lim;
         const float r0 = v0 ? half_lo(nrm[0][0]) * inner[0] : -INFINITY;
         const float r1 = v1 ? half_lo(nrm[1][0]) * inner[1] : -INFINITY;
         // move the reference of the heads that need it (first tile, rare after)
@@ -1047,15 +1063,15 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
   const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
 #pragma unroll
   for (int u = 0; u < T; ++u) {
-    const int g = 4 * u + grow;  // C rows of this lane: head grow of tile u
-    if (g >= G) continue;
+    const int g = 4 * u + grow;  // C rows of this lane: row grow of tile u
+    if (g >= nrows) continue;
     const float ra = raC[u];
     float cs = 0.0f;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv)
 #pragma unroll
       for (int i = 0; i < 4; ++i) cs += sm.cred[wv][u][grow][i];
-    float *part = a.partials + ((grp * G + g) * a.num_splits + split) * kPartStride;
+    float *part = a.partials + (query_out_row(a, grp, g) * a.num_splits + split) * kPartStride;
     if (wave == 0 && t16 == 0) {
       float l = 0.0f;
 #pragma unroll
@@ -1102,6 +1118,10 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
   const int s0 = split * a.split_tokens;
   const int s1 = min(s0 + a.split_tokens, L);
   if (s0 >= s1) return;  // uniform
+  // query rows (positions x heads); every row sees the keys before s1v, row
+  // r those before min(s1, L - q_len + pos0 + r / G + 1)
+  const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count;
+  const int s1v = min(s1, L - qlen + 1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sq = wave & 3;  // role 0: page pair (K-block); role 1: coordinate block
@@ -1248,7 +1268,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
           qq[u][e] = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
         }
       }
-      const bool partial = s0 + 128 * (k + 1) > s1;  // uniform: the chunk's last tile
+      const bool partial = s0 + 128 * (k + 1) > s1v;  // uniform: a tile some row does not see whole
 #pragma unroll
       for (int u = 0; u < T; ++u) {
         float inner[2];
@@ -1289,7 +1309,8 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
         weights(x0, x1, true, true);
         if (__builtin_amdgcn_ballot_w64(x0 > (float)kRefStep || x1 > (float)kRefStep) || partial) {
           const int tok0 = s0 + 128 * k + 32 * sq + t16;
-          const bool v0 = tok0 < s1, v1 = tok0 + 16 < s1;
+          const int lim = min(s1, L - qlen + (4 * u + grow) / G + 1);  // the lane's row
+          const bool v0 = tok0 < lim, v1 = tok0 + 16 < lim;
           const float r0 = v0 ? half_lo(nrm[0][0]) * inner[0] : -INFINITY;
           const float r1 = v1 ? half_lo(nrm[1][0]) * inner[1] : -INFINITY;
           const float mh = row_max16(fmaxf(r0, r1));
@@ -1414,15 +1435,15 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
     const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
 #pragma unroll
     for (int u = 0; u < T; ++u) {
-      const int g = 4 * u + grow;  // C rows of this lane: head grow of tile u
-      if (g >= G) continue;
+      const int g = 4 * u + grow;  // C rows of this lane: row grow of tile u
+      if (g >= nrows) continue;
       const float ra = raC[u];
       float cs = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < 4; ++wv)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cs += sm.cred[wv][u][grow][i];
-      float *part = a.partials + ((grp * G + g) * a.num_splits + split) * kPartStride;
+      float *part = a.partials + (query_out_row(a, grp, g) * a.num_splits + split) * kPartStride;
       if (sq == 0 && t16 == 0) {
         float l = 0.0f;
 #pragma unroll
@@ -1573,12 +1594,21 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t groups = (int64_t)a.num_seqs * a.q_len * a.num_kv_heads;
   hipError_t e = hipSuccess;
   if (a.qk_tiles > 0) {  // matrix-core pass, its own query operands: a workgroup per (chunk, KV head)
-    if (a.qk_tiles != 1 && a.qk_tiles != 2) return hipErrorInvalidValue;
+    // one launch per group of at most 8 query rows (positions x heads)
+    const int per = decode_positions_per_launch(a.group);
     const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_splits;
-    if (a.qk_tiles == 1)
-      hipLaunchKernelGGL(split_mfma_kernel<1>, dim3((unsigned)items), dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)items), dim3(512), 0, stream, a);
+    for (int p0 = 0; p0 < a.q_len; p0 += per) {
+      DecodeArgs la = a;
+      la.pos0 = p0;
+      la.pos_count = min(per, a.q_len - p0);
+      la.qk_tiles = (la.group * la.pos_count + 3) / 4;
+      if (la.qk_tiles == 1)
+        hipLaunchKernelGGL(split_mfma_kernel<1>, dim3((unsigned)items), dim3(256), 0, stream, la);
+      else if (la.qk_tiles == 2)
+        hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)items), dim3(512), 0, stream, la);
+      else
+        return hipErrorInvalidValue;
+    }
   } else {
     hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups, (unsigned)a.group), dim3(256), 0, stream, a);
     e = hipGetLastError();

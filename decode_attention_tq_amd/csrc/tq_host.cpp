@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -102,12 +103,13 @@ bool dtype_ok(int d) { return d == TQ_F32 || d == TQ_F16 || d == TQ_BF16; }
 // Chunks are multiples of 256 tokens.  The automatic choice depends only on
 // the call's sizes (no device query), so the workspace size and the launch
 // always agree, and aims at the 256 compute units of the part: the
-// matrix-core decode pass (single query, up to 8 heads per KV head) at one
-// 8-wave workgroup per unit for 8 heads and two 4-wave workgroups per unit
-// for up to 4 (each workgroup walks its chunk with a fixed start-up cost,
-// so more, shorter chunks only add it), the other passes at about 1024
-// workgroups.  Several queries per sequence share a workgroup per block of
-// query positions.
+// matrix-core decode pass (at most 8 query rows, positions x heads, per KV
+// head) at one 8-wave workgroup per unit for 5 to 8 rows and two 4-wave
+// workgroups per unit for up to 4 (each workgroup walks its chunk with a
+// fixed start-up cost, so more, shorter chunks only add it), the other
+// passes at about 1024 workgroups.  The prefill pass shares a workgroup per
+// block of query positions; the decode passes take all of a sequence's
+// positions in one.
 void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested,
                  int *split_tokens, int *num_splits) {
   int st;
@@ -115,12 +117,15 @@ void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_c
     st = requested;
   } else {
     long per_seq = q_len;
-    if (tq::prefill_uses_mfma(q_len, group)) {
+    if (tq::decode_uses_mfma(q_len, group)) {
+      per_seq = 1;
+    } else if (tq::prefill_uses_mfma(q_len, group)) {
       const int bq = tq::prefill_block_queries(group);
       per_seq = (q_len + bq - 1) / bq;
     }
     const long rows = (long)num_seqs * per_seq * num_kv_heads;
-    const long target = tq::decode_uses_mfma(q_len, group) ? (group > 4 ? 256 : 512) : 1024;
+    const int mrows = group * std::min(q_len, tq::decode_positions_per_launch(group > 0 ? group : 1));
+    const long target = tq::decode_uses_mfma(q_len, group) ? (mrows > 4 ? 256 : 512) : 1024;
     long want = (target + rows - 1) / rows;
     if (want < 1) want = 1;
     long per = (max_ctx + want - 1) / want;
@@ -145,8 +150,18 @@ size_t decode_qprep_floats(int64_t rows) { return (size_t)rows * 256; }
 size_t decode_partial_floats(int64_t rows, int num_splits) {
   return (size_t)rows * (size_t)num_splits * kPartStride;
 }
-bool decode_uses_mfma(int q_len, int group) { return q_len == 1 && group <= 8; }
-int decode_qk_tiles(int group) { return group <= 4 ? 1 : group / 4; }
+// A workgroup of the matrix-core decode pass takes at most 8 query rows
+// (positions x heads) of a KV head, two 16-row operand tiles; more positions
+// run as one launch per group of 8 / group of them, each reading the cache
+// once.  Up to 4 such launches beat one prefill pass (measured at 32,768 and
+// 131,072 cached tokens); beyond, the prefill pass takes the block.
+bool decode_uses_mfma(int q_len, int group) {
+  if (q_len < 1 || group < 1 || group > 8) return false;
+  const int per = 8 / group;
+  return (q_len + per - 1) / per <= 4;
+}
+int decode_positions_per_launch(int group) { return 8 / group; }
+int decode_qk_tiles(int rows) { return (rows + 3) / 4; }
 }  // namespace tq
 
 extern "C" {
@@ -407,10 +422,12 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
   a.SHop = (const uint16_t *)(a.St + (size_t)tq::kQjlDim * tq::kHeadDim);
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   a.qk_tiles = 0;
+  a.pos0 = 0;
+  a.pos_count = q_len;
   a.qprep = nullptr;
   float *rest = (float *)workspace;
   if (tq::decode_uses_mfma(q_len, group)) {
-    a.qk_tiles = tq::decode_qk_tiles(group);
+    a.qk_tiles = tq::decode_qk_tiles(group * std::min(q_len, tq::decode_positions_per_launch(group)));
   } else {
     a.qprep = rest;
     rest += tq::decode_qprep_floats(rows);

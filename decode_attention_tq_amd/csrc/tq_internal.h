@@ -73,10 +73,13 @@ struct DecodeArgs {
   const float *St;     // [d][m]
   const uint16_t *SHop;  // S H as f16 hi, lo halves in the projection's operand order
   float *qprep;        // workspace (vector and prefill passes): [rows][256] = rotated q | qjl_scale * S q
-  // Matrix-core split pass (single-query decode, at most 8 heads per KV
-  // head): 16-row operand tiles per group (4 heads x 4 digits each), which
-  // the pass forms itself; 0 for the other passes.
+  // Matrix-core split pass: it forms its own query operands, for the
+  // positions pos0 .. pos0 + pos_count - 1 of the q_len new ones (at most 8
+  // query rows, positions x heads, per KV head and launch; several launches
+  // cover more positions), in qk_tiles 16-row operand tiles (4 rows x 4
+  // digits each); qk_tiles is 0 for the other passes.
   int qk_tiles;
+  int pos0, pos_count;
   float *partials;     // workspace: [rows][num_splits][4 + 128], m in log2 units
   Codebook cb;
 };
@@ -84,15 +87,18 @@ struct DecodeArgs {
 // Workspace split of tq_decode_attention.
 size_t decode_qprep_floats(int64_t rows);
 size_t decode_partial_floats(int64_t rows, int num_splits);
-// The matrix-core split pass serves single-query decode with up to 8 query
-// heads per KV head; single-query decode with 16 uses the vector pass.
+// The matrix-core split pass serves decode with up to 8 heads per KV head
+// and short query blocks (multi-token verify), one launch per group of
+// 8 / group positions, at most 4 launches; single-query decode with 16 heads
+// per KV head uses the vector pass, longer query blocks the prefill pass.
 bool decode_uses_mfma(int q_len, int group);
+int decode_positions_per_launch(int group);
 // Several queries per sequence (chunked prefill, causal) run on the
 // matrix-core prefill pass: 128 query rows (128 / group positions) per
 // workgroup.
 bool prefill_uses_mfma(int q_len, int group);
 int prefill_block_queries(int group);
-int decode_qk_tiles(int group);
+int decode_qk_tiles(int rows);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -403,7 +403,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
 }  // namespace
 
 bool prefill_uses_mfma(int q_len, int group) {
-  return q_len > 1 && (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+  return q_len > 1 && !decode_uses_mfma(q_len, group) &&
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
 }
 
 int prefill_block_queries(int group) { return kRows / group; }

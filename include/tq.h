@@ -153,8 +153,10 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
  * v~ = |v| H^T c[idx_v] -- the QJL-corrected inner-product estimate of the
  * SwiftLM README's K-cache step 5, attention over the whole compressed
  * history (its note on --turbo-kv recall) read through a block table.
- * q_len > 1 (chunked prefill, the README's --prefill-size) is causal: query t
- * sees keys 0 .. context_len - q_len + t.
+ * q_len > 1 (chunked prefill, the README's --prefill-size, or a block of
+ * tokens to verify in speculative multi-token decoding, the README's "MTP
+ * Speculative Decoding" performance section) is causal: query t sees keys
+ * 0 .. context_len - q_len + t.
  *   q           device [num_seqs][q_len][num_q_heads][128], dtype q_dtype.
  *   block_tables device int32[num_seqs][max_blocks_per_seq].
  *   context_lens device int32[num_seqs], each in [0, max_context_len]; the
@@ -163,8 +165,9 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
  *   out         device [num_seqs][q_len][num_q_heads][128], dtype out_dtype.
  *   tokens_per_split  0 -> chosen by the library; else a multiple of 256
  *               giving the split-K chunk (results agree to rounding).
- *               Single-query decode with up to 8 query heads per KV head
- *               uses at most 8192 tokens per chunk.
+ *               Decode with up to 8 query heads per KV head and a short
+ *               query block (at most 4 groups of 8 / group positions) uses
+ *               at most 8192 tokens per chunk.
  *   workspace   device scratch of tq_decode_workspace_bytes() bytes (same
  *               arguments); contents on entry do not matter.
  * Errors: TQ_ERR_INVALID_ARGUMENT (nulls, Hq % Hkv != 0, q_len < 1,

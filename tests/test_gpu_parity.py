@@ -275,6 +275,29 @@ def test_running_maximum_moves_along_the_sequence(Hkv):
     print("max rel err", err.max())
 
 
+@pytest.mark.parametrize("q_len,Hq,Hkv", [(2, 32, 8), (3, 4, 2), (8, 8, 8), (4, 32, 8), (3, 32, 4),
+                                         (8, 32, 4), (3, 16, 1)])
+def test_multi_token_verify(q_len, Hq, Hkv):
+    """Multi-token verify decode (speculative or multi-token prediction): 2 to
+    8 new queries per sequence over a compressed cache, each causal over the
+    cache plus the verified tokens before it, batched sequences of ragged
+    length.  The matrix-core decode pass takes up to 8 query rows (positions x
+    heads) per KV head and launch, up to 4 launches (4, 6 and 8 rows in one
+    launch, 2 and 3 launches here); longer blocks take the prefill pass."""
+    rng = np.random.default_rng(20 + q_len)
+    lens = np.array([q_len, 700, 2300], dtype=np.int64)
+    table, nb = synth.block_tables(rng, lens)
+    cb = codebook()
+    kpool, vpool = new_pools(nb, Hkv)
+    for b in range(len(lens)):
+        k = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        v = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        encode_gpu(cb, k, v, synth.slots_for(table, b, np.arange(lens[b])), kpool, vpool, with_norms=False)
+    q = synth.queries(rng, len(lens), q_len, Hq)
+    out = decode_gpu(cb, q, kpool, vpool, table, lens.astype(np.int32), Hkv)
+    check_decode(out, q, _np(kpool), _np(vpool), table, lens.astype(np.int32))
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 4), (32, 2)])
 def test_prefill_groups_batches_and_splits(Hq, Hkv):
     """Several queries per sequence for every supported group size (1, 2, 8,

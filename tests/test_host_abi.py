@@ -141,16 +141,17 @@ def test_decode_validation():
 
 def _prep_words(B, q_len, Hq, Hkv):
     """Query prep floats: the vector and prefill passes keep q' and s (256
-    floats) per query row; single-query decode with <= 8 heads per KV head
-    forms its operands inside the split pass and keeps none."""
+    floats) per query row; the matrix-core decode pass (up to 8 heads per KV
+    head, at most 4 launches of 8 // G positions) forms its operands inside
+    the split pass and keeps none."""
     G = Hq // Hkv
-    if q_len == 1 and G <= 8:
+    if G <= 8 and -(-q_len // (8 // G)) <= 4:
         return 0
     return B * q_len * Hq * 256
 
 
 @pytest.mark.parametrize("B,q_len,Hq,Hkv", [(1, 1, 32, 8), (2, 1, 32, 4), (1, 1, 32, 32),
-                                            (1, 4, 32, 8), (1, 1, 32, 2)])
+                                            (1, 4, 32, 8), (1, 1, 32, 2), (2, 2, 32, 8)])
 def test_workspace_plan_is_consistent(B, q_len, Hq, Hkv):
     cb = _fake_cb()
     ref = ctypes.byref(cb)
