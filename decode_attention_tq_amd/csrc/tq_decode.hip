@@ -17,6 +17,7 @@
 // rotated domain: <q, H^T c> = <H q, c>.
 
 #include <math.h>
+#include <stddef.h>
 
 #include <type_traits>
 
@@ -264,8 +265,9 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 // Both contractions run on the scaled f8f6f4 MFMA with the stored bits as the
 // fp4 operand (b_split: one and_or per 8 values) and the float side split
 // into four digits in four A rows: the query side in balanced base 32 as fp6
-// codes (see query_prep_kernel, which also folds scale * log2(e) in, so that
-// scores come out in log2 units), the weights in base 16 as fp8 codes.
+// codes (formed inside the pass, with scale * log2(e) folded in, so that
+// scores come out in log2 units), the weights in base 16, also as fp6 codes
+// (both contractions run at the fp6 x fp4 rate).
 // With the bit-plane form of the levels, c[idx] = -(beta0 B0 + beta1 B1 +
 // beta2 B2 + beta3 Bx) where Bx = B0 B1 B2 is the plane of b0^b1^b2:
 //   <q', c[idx]> = sum_p <-beta_p q', B_p>        (4 MFMAs per page)
@@ -284,12 +286,14 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 // Weights: a scoring wave keeps a reference R per head (log2 units, moved
 // only when a score exceeds it by 64), p = 2^(score - R), w = p n_v, and
 // X = rint(w 2^(141-ex)) < 2^15 for ex the exponent field of the block's
-// largest w.  The four base-16 digits of X are written as fp8 codes 0..15,
-// which are exactly d 2^-9 (subnormals and the first binade), so the digit
-// needs no conversion: row r's E8M0 scale 2^(ex - 120 - 4r + R - Racc)
+// largest w.  The four base-16 digits of X are written to LDS as the bit
+// patterns of f16 subnormals d 2^-24, which take no conversion on the
+// scoring side; the value side turns 32 of them into one fp6 operand of the
+// codes of d/8 with one conversion instruction (divisor 2^-21, which keeps
+// subnormal inputs), and row r's E8M0 scale 2^(ex - 126 - 4r + R - Racc)
 // restores its place value relative to the accumulator reference Racc.
 // The value operand from b_split has the affine form alpha_v + beta_v b per
-// register v; digits of K slots in registers 0..2 are negated (fp8 sign bit)
+// register v; digits of K slots in registers 0..2 are negated (sign bit)
 // and the offsets become one per-row correction, sum_k c_v A_k with
 // c = (-5, -3, -1, 0) per register, taken by two MFMAs against constant
 // operands (-4, -3, -1, 0) and (-1, 0, 0, 0): acc_p + corr = sum w (1 - 2b).
@@ -299,7 +303,7 @@ constexpr int kMaxSplitTiles = 64;          // tiles of 128 tokens per workgroup
 constexpr int kKRec = 1120;                 // per page: K planes and signs (1024) | K n (32) | K gamma (32) | V n (32)
 constexpr int kVPair = 4 * 512 + 64;        // per page pair: [plane][coordinate] words (page a | page b << 16);
                                             // plane 3 takes the spare lanes' stores, +64 spreads the pairs over the banks
-constexpr int kWqRow = 144;                 // 128 fp8 digits of one A row, padded
+constexpr int kWqRow = 144;                 // 128 digits of one A row, padded (288-byte rows)
 constexpr int kRefStep = 64;                // a reference moves when exceeded by 2^64
 
 // Maximum over the 16 lanes of a row on integer keys that order like the
@@ -458,16 +462,37 @@ __device__ __forceinline__ void store_v_part(uint8_t *vbuf, const StageSet<R> &S
   *reinterpret_cast<u32x4 *>(dst + 16) = hi;
 }
 
+// Scratch of the query operands (below), in the staging buffers and, where
+// it is larger, the space after them.
+template <int T>
+struct QPrepLds {
+  float qr[4 * T][kHeadDim];           // q' = H q (zero rows for absent heads)
+  float sv[4 * T][kQjlDim];            // s = alpha S q
+  _Float16 qh[4 * T][kHeadDim];        // q' as f16 hi + lo halves in slot order
+  _Float16 ql[4 * T][kHeadDim];        //   (slot s <-> coordinate 16 (s % 8) + s / 8)
+  _Float16 codes[4 * T][5][4][128];    // [head][plane][digit][K slot] digit values d f (exact)
+  int pe[4 * T][5];                    // per head and plane: E, or INT_MIN for a zero plane
+};
+constexpr int kStageBytes = 2 * kTilePages * kKRec + 2 * 4 * kVPair;
+template <int T>
+constexpr int qprep_pad() {
+  return (int)sizeof(QPrepLds<T>) > kStageBytes ? (int)sizeof(QPrepLds<T>) - kStageBytes : 16;
+}
+
 template <int T>
 struct SplitLds {
   int ids[kMaxSplitTiles][kTilePages];      // block ids of the chunk's pages
   uint8_t kbuf[2][kTilePages * kKRec];
   uint8_t vbuf[2][4 * kVPair];
-  uint8_t wq[2][T][16][kWqRow];  // [buffer][head tile][head * 4 + digit][K slot] fp8 digits
+  uint8_t qpad[qprep_pad<T>()];             // rest of the query scratch
+  alignas(16) uint16_t wq[2][T][16][kWqRow];  // [buffer][head tile][head * 4 + digit][K slot] digit bits as f16 subnormals
   int2 stats[2][T][4][4];        // [buffer][head tile][head][K-block]: (exponent field, R bits)
   float lred[T][4][4][2];        // [head tile][head][K-block]: (probability sum, R)
   float cred[4 * T][T][4][4];    // [wave][head tile][head][digit]: correction partials
 };
+
+static_assert(offsetof(SplitLds<1>, wq) - offsetof(SplitLds<1>, kbuf) >= sizeof(QPrepLds<1>), "query scratch");
+static_assert(offsetof(SplitLds<2>, wq) - offsetof(SplitLds<2>, kbuf) >= sizeof(QPrepLds<2>), "query scratch");
 
 template <bool B>
 using flag = std::integral_constant<bool, B>;
@@ -487,6 +512,19 @@ using flag = std::integral_constant<bool, B>;
 // separate launch and a round trip of its results through memory.  The
 // scratch space aliases the staging buffers, which are first written after it.
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v32h __attribute__((ext_vector_type(32)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// 32 f16 values at p (16-byte aligned) as one fp6 e2m3 operand, value / div
+// (code s at bits 6s .. 6s+5; the conversion keeps f16 subnormal inputs).
+__device__ __forceinline__ v8i fp6_operand(const uint16_t *p, float div) {
+  const uint4 *q = reinterpret_cast<const uint4 *>(p);
+  const uint4 a = q[0], b = q[1], c = q[2], d = q[3];
+  const v16i w = v16i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w,
+                      (int)c.x, (int)c.y, (int)c.z, (int)c.w, (int)d.x, (int)d.y, (int)d.z, (int)d.w};
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk32_fp6_f16(__builtin_bit_cast(v32h, w), div);
+  return v8i{(int)r[0], (int)r[1], (int)r[2], (int)r[3], (int)r[4], (int)r[5], 0, 0};
+}
 
 // Query rows of a (sequence, KV head) workgroup of the matrix-core pass:
 // row = i G + g for position t = pos0 + i of the q_len new ones and head g
@@ -499,17 +537,6 @@ __device__ __forceinline__ int64_t query_out_row(const DecodeArgs &a, int64_t gr
   return (b * a.q_len + a.pos0 + row / G) * a.num_q_heads + h * G + row % G;
 }
 
-template <int T>
-struct QPrepLds {
-  float qr[4 * T][kHeadDim];           // q' = H q (zero rows for absent heads)
-  float sv[4 * T][kQjlDim];            // s = alpha S q
-  _Float16 qh[4 * T][kHeadDim];        // q' as f16 hi + lo halves in slot order
-  _Float16 ql[4 * T][kHeadDim];        //   (slot s <-> coordinate 16 (s % 8) + s / 8)
-  uint8_t codes[4 * T][5][4][128];     // [head][plane][digit][K slot] fp6 codes
-  int pe[4 * T][5];                    // per head and plane: E, or INT_MIN for a zero plane
-};
-static_assert(sizeof(QPrepLds<1>) <= 2 * kTilePages * kKRec + 2 * 4 * kVPair, "query scratch exceeds the staging buffers");
-static_assert(sizeof(QPrepLds<2>) <= 2 * kTilePages * kKRec + 2 * 4 * kVPair, "query scratch exceeds the staging buffers");
 
 // Loads issued first in the workgroup, so that waiting for them does not wait
 // for the tile loads issued after them: wave w's q elements lane and lane + 64
@@ -635,10 +662,10 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
       rem -= d1 * 1024.0f;
       const float d2 = rintf(rem * 0.03125f);
       const float d3 = rem - d2 * 32.0f;
-      L.codes[wave][p][0][kap] = (uint8_t)fp6_code(d0 * f);
-      L.codes[wave][p][1][kap] = (uint8_t)fp6_code(d1 * f);
-      L.codes[wave][p][2][kap] = (uint8_t)fp6_code(d2 * f);
-      L.codes[wave][p][3][kap] = (uint8_t)fp6_code(d3 * f);
+      L.codes[wave][p][0][kap] = (_Float16)(d0 * f);
+      L.codes[wave][p][1][kap] = (_Float16)(d1 * f);
+      L.codes[wave][p][2][kap] = (_Float16)(d2 * f);
+      L.codes[wave][p][3][kap] = (_Float16)(d3 * f);
     }
   }
   lds_barrier();
@@ -654,18 +681,8 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
     const int hd = 4 * tiles[n] + gp;
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
-      const uint4 c0 = *reinterpret_cast<const uint4 *>(&L.codes[hd][p][r][32 * ga]);
-      const uint4 c1 = *reinterpret_cast<const uint4 *>(&L.codes[hd][p][r][32 * ga + 16]);
-      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      uint32_t q24[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t v = cw[k];
-        q24[k] = (v & 0x3Fu) | ((v >> 2) & 0xFC0u) | ((v >> 4) & 0x3F000u) | ((v >> 6) & 0xFC0000u);
-      }
-      Aq[n][p] = v8i{(int)(q24[0] | (q24[1] << 24)), (int)((q24[1] >> 8) | (q24[2] << 16)),
-                     (int)((q24[2] >> 16) | (q24[3] << 8)), (int)(q24[4] | (q24[5] << 24)),
-                     (int)((q24[5] >> 8) | (q24[6] << 16)), (int)((q24[6] >> 16) | (q24[7] << 8)), 0, 0};
+      // the 32 digit values of K slots 32 ga .. +31, as codes of d / 8
+      Aq[n][p] = fp6_operand(reinterpret_cast<const uint16_t *>(&L.codes[hd][p][r][32 * ga]), 8.0f);
       const int E = L.pe[hd][p];
       scq[n][p] = E != INT_MIN ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One;
     }
@@ -734,10 +751,10 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
   const BSplitK bk = bsplit_consts();
-  const uint32_t nib = in_vgpr(0x0F0F0F0Fu);
-  // fp8 sign of the digits of K slots held by b_split registers 0..2: the
-  // lane's token t sits in register t & 3
-  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80808080u);
+  const uint32_t nib = in_vgpr(0x000F000Fu);
+  // sign (f16 sign bit) of the digits of K slots held by b_split registers
+  // 0..2: the lane's token t sits in register t & 3
+  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80008000u);
   const int kap0 = 8 * (t16 & 3) + (t16 >> 2);  // K slot of token t16 of the pair's first page
   const StagePtrs sp{a.k_cache, a.v_cache, (int64_t)a.num_kv_heads, h, sq, 16u * (uint32_t)lane,
                      16u * (uint32_t)(lane % 48), 4u * (uint32_t)t16, 4u * (uint32_t)(lane & 7)};
@@ -803,7 +820,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
 #pragma unroll
     for (int u = 0; u < T; ++u) {
       const float d = fmaxf(__int_as_float(st[u].y) - raA[u], -300.0f);  // NaN (both -inf) -> -300
-      sw[u] = min(max(st[u].x + 7 - 4 * rA + (int)d, 0), 254);  // E8M0 of 2^(ex-120-4r+R-Racc)
+      sw[u] = min(max(st[u].x + 1 - 4 * rA + (int)d, 0), 254);  // E8M0 of 2^(ex-126-4r+R-Racc)
     }
   };
 
@@ -855,12 +872,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
     uint32_t W[NJ][3];
     if constexpr (has_v) {
 #pragma unroll
-      for (int u = 0; u < T; ++u) {
-        const uint8_t *row = &sm.wq[bv][u][4 * gA + rA][0];
-        const uint4 u0 = *reinterpret_cast<const uint4 *>(row + 16 * kb);
-        const uint4 u1 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * kb);
-        Aw[u] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-      }
+      for (int u = 0; u < T; ++u) Aw[u] = fp6_operand(&sm.wq[bv][u][4 * gA + rA][32 * kb], 0x1p-21f);  // d 2^-24 -> d/8
       const uint32_t *vw = reinterpret_cast<const uint32_t *>(sm.vbuf[bv] + kVPair * kb);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -889,10 +901,10 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
         const v8i V0 = bsplit(W0, bk), V1 = bsplit(W1, bk), V2 = bsplit(W2, bk), Vx = bsplit(W0 ^ W1 ^ W2, bk);
 #pragma unroll
         for (int u = 0; u < T; ++u) {
-          acc[u][0][j] = mfma_f8f4(Aw[u], V0, acc[u][0][j], sw[u]);
-          acc[u][1][j] = mfma_f8f4(Aw[u], V1, acc[u][1][j], sw[u]);
-          acc[u][2][j] = mfma_f8f4(Aw[u], V2, acc[u][2][j], sw[u]);
-          acc[u][3][j] = mfma_f8f4(Aw[u], Vx, acc[u][3][j], sw[u]);
+          acc[u][0][j] = mfma_f6f4(Aw[u], V0, acc[u][0][j], sw[u]);
+          acc[u][1][j] = mfma_f6f4(Aw[u], V1, acc[u][1][j], sw[u]);
+          acc[u][2][j] = mfma_f6f4(Aw[u], V2, acc[u][2][j], sw[u]);
+          acc[u][3][j] = mfma_f6f4(Aw[u], Vx, acc[u][3][j], sw[u]);
         }
       }
     }
@@ -922,17 +934,13 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
         const uint32_t X0 = __float_as_uint(fmaf(w0, mult, 8388608.0f));
         const uint32_t X1 = __float_as_uint(fmaf(w1, mult, 8388608.0f));
         const uint32_t XX = __builtin_amdgcn_perm(X1, X0, 0x05040100u);  // X0 lo16 | X1 lo16 << 16
-        const uint32_t Ev = (XX & nib) | s80;          // digits 3 and 1 of both tokens
-        const uint32_t Od = ((XX >> 4) & nib) | s80;   // digits 2 and 0
-        uint8_t *wr = &sm.wq[bs][su][4 * grow][32 * sq + kap0];
-        wr[3 * kWqRow] = (uint8_t)Ev;
-        wr[3 * kWqRow + 4] = (uint8_t)(Ev >> 16);
-        wr[1 * kWqRow] = (uint8_t)(Ev >> 8);
-        wr[1 * kWqRow + 4] = (uint8_t)(Ev >> 24);
-        wr[2 * kWqRow] = (uint8_t)Od;
-        wr[2 * kWqRow + 4] = (uint8_t)(Od >> 16);
-        wr[0] = (uint8_t)(Od >> 8);
-        wr[4] = (uint8_t)(Od >> 24);
+        uint16_t *wr = &sm.wq[bs][su][4 * grow][32 * sq + kap0];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // digit r (place 16^(3-r)) of both tokens, with the slot's sign
+          const uint32_t D = ((XX >> (12 - 4 * r)) & nib) | s80;
+          wr[r * kWqRow] = (uint16_t)D;
+          wr[r * kWqRow + 4] = (uint16_t)(D >> 16);
+        }
         // the 16 lanes of a head write the same statistics (no lane branch)
         sm.stats[bs][su][grow][sq] = make_int2((int)(exb >> 23), __float_as_int(rl));
       };
@@ -974,15 +982,15 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
         const v8i C2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int u = 0; u < T; ++u) {
-          corr[u] = mfma_f8f4(Aw[u], C1, corr[u], sw[u]);
-          corr[u] = mfma_f8f4(Aw[u], C2, corr[u], sw[u]);
+          corr[u] = mfma_f6f4(Aw[u], C1, corr[u], sw[u]);
+          corr[u] = mfma_f6f4(Aw[u], C2, corr[u], sw[u]);
         }
       }
     }
   };
 
   // zero digits and empty statistics in buffer 1 for the first interval
-  for (int i = tid; i < T * 16 * kWqRow / 4; i += 64 * NW) reinterpret_cast<uint32_t *>(&sm.wq[1][0][0][0])[i] = 0u;
+  for (int i = tid; i < T * 16 * kWqRow / 2; i += 64 * NW) reinterpret_cast<uint32_t *>(&sm.wq[1][0][0][0])[i] = 0u;
   if (tid < T * 16) (&sm.stats[1][0][0][0])[tid] = make_int2(0, __float_as_int(-INFINITY));
   lds_barrier();  // block ids, buffer 1
   StageSet<R> SA, SB;  // register sets of even and odd tiles
@@ -1150,8 +1158,8 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
 #pragma unroll
   for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
   const BSplitK bk = bsplit_consts();
-  const uint32_t nib = in_vgpr(0x0F0F0F0Fu);
-  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80808080u);
+  const uint32_t nib = in_vgpr(0x000F000Fu);
+  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80008000u);
   const int kap0 = 8 * (t16 & 3) + (t16 >> 2);
   const StagePtrs sp{a.k_cache, a.v_cache, (int64_t)a.num_kv_heads, h, sq, 16u * (uint32_t)lane,
                      16u * (uint32_t)(lane % 48), 4u * (uint32_t)t16, 4u * (uint32_t)(lane & 7)};
@@ -1214,7 +1222,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
 #pragma unroll
     for (int u = 0; u < T; ++u) {
       const float d = fmaxf(__int_as_float(st[u].y) - raA[u], -300.0f);  // NaN (both -inf) -> -300
-      sw[u] = min(max(st[u].x + 7 - 4 * rA + (int)d, 0), 254);
+      sw[u] = min(max(st[u].x + 1 - 4 * rA + (int)d, 0), 254);
     }
   };
 
@@ -1290,18 +1298,14 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
           const float mult = __uint_as_float(0x86000000u - exb);  // 2^(141 - ex)
           const uint32_t X0 = __float_as_uint(fmaf(w0, mult, 8388608.0f));
           const uint32_t X1 = __float_as_uint(fmaf(w1, mult, 8388608.0f));
-          const uint32_t XX = __builtin_amdgcn_perm(X1, X0, 0x05040100u);
-          const uint32_t Ev = (XX & nib) | s80;
-          const uint32_t Od = ((XX >> 4) & nib) | s80;
-          uint8_t *wr = &sm.wq[bs][u][4 * grow][32 * sq + kap0];
-          wr[3 * kWqRow] = (uint8_t)Ev;
-          wr[3 * kWqRow + 4] = (uint8_t)(Ev >> 16);
-          wr[1 * kWqRow] = (uint8_t)(Ev >> 8);
-          wr[1 * kWqRow + 4] = (uint8_t)(Ev >> 24);
-          wr[2 * kWqRow] = (uint8_t)Od;
-          wr[2 * kWqRow + 4] = (uint8_t)(Od >> 16);
-          wr[0] = (uint8_t)(Od >> 8);
-          wr[4] = (uint8_t)(Od >> 24);
+          const uint32_t XX = __builtin_amdgcn_perm(X1, X0, 0x05040100u);  // X0 lo16 | X1 lo16 << 16
+          uint16_t *wr = &sm.wq[bs][u][4 * grow][32 * sq + kap0];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {  // digit r (place 16^(3-r)) of both tokens, with the slot's sign
+            const uint32_t D = ((XX >> (12 - 4 * r)) & nib) | s80;
+            wr[r * kWqRow] = (uint16_t)D;
+            wr[r * kWqRow + 4] = (uint16_t)(D >> 16);
+          }
           sm.stats[bs][u][grow][sq] = make_int2((int)(exb >> 23), __float_as_int(rl[u]));
         };
         const float x0 = fmaf(half_lo(nrm[0][0]), inner[0], -rl[u]);
@@ -1329,12 +1333,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
       value_scales(bv, sw);
       v8i Aw[T];
 #pragma unroll
-      for (int u = 0; u < T; ++u) {
-        const uint8_t *row = &sm.wq[bv][u][4 * gA + rA][0];
-        const uint4 u0 = *reinterpret_cast<const uint4 *>(row + 16 * kb);
-        const uint4 u1 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * kb);
-        Aw[u] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-      }
+      for (int u = 0; u < T; ++u) Aw[u] = fp6_operand(&sm.wq[bv][u][4 * gA + rA][32 * kb], 0x1p-21f);  // d 2^-24 -> d/8
       const uint32_t *vw = reinterpret_cast<const uint32_t *>(sm.vbuf[bv] + kVPair * kb);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -1343,10 +1342,10 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
         const v8i V0 = bsplit(W0, bk), V1 = bsplit(W1, bk), V2 = bsplit(W2, bk), Vx = bsplit(W0 ^ W1 ^ W2, bk);
 #pragma unroll
         for (int u = 0; u < T; ++u) {
-          acc[u][0][j] = mfma_f8f4(Aw[u], V0, acc[u][0][j], sw[u]);
-          acc[u][1][j] = mfma_f8f4(Aw[u], V1, acc[u][1][j], sw[u]);
-          acc[u][2][j] = mfma_f8f4(Aw[u], V2, acc[u][2][j], sw[u]);
-          acc[u][3][j] = mfma_f8f4(Aw[u], Vx, acc[u][3][j], sw[u]);
+          acc[u][0][j] = mfma_f6f4(Aw[u], V0, acc[u][0][j], sw[u]);
+          acc[u][1][j] = mfma_f6f4(Aw[u], V1, acc[u][1][j], sw[u]);
+          acc[u][2][j] = mfma_f6f4(Aw[u], V2, acc[u][2][j], sw[u]);
+          acc[u][3][j] = mfma_f6f4(Aw[u], Vx, acc[u][3][j], sw[u]);
         }
       }
       if (kv % 4 == sq) {  // uniform: the offsets of b_split, one value wave per tile
@@ -1354,14 +1353,14 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
         const v8i C2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int u = 0; u < T; ++u) {
-          corr[u] = mfma_f8f4(Aw[u], C1, corr[u], sw[u]);
-          corr[u] = mfma_f8f4(Aw[u], C2, corr[u], sw[u]);
+          corr[u] = mfma_f6f4(Aw[u], C1, corr[u], sw[u]);
+          corr[u] = mfma_f6f4(Aw[u], C2, corr[u], sw[u]);
         }
       }
     }
   };
 
-  for (int i = tid; i < T * 16 * kWqRow / 4; i += 64 * NW) reinterpret_cast<uint32_t *>(&sm.wq[1][0][0][0])[i] = 0u;
+  for (int i = tid; i < T * 16 * kWqRow / 2; i += 64 * NW) reinterpret_cast<uint32_t *>(&sm.wq[1][0][0][0])[i] = 0u;
   if (tid < T * 16) (&sm.stats[1][0][0][0])[tid] = make_int2(0, __float_as_int(-INFINITY));
   lds_barrier();  // block ids, buffer 1
   StageSet<R> SA, SB;
