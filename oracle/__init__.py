@@ -29,7 +29,7 @@ from .encode import encode_k, encode_v, quantize_codes
 from .pages import (K_PAGE_BYTES, V_PAGE_BYTES, BLOCK, pack_k_page, pack_v_page,
                     unpack_k_page, unpack_v_page, write_slots, read_k_tokens,
                     read_v_tokens)
-from .attention import (dequant_k, dequant_v, attention_dense, decode_paged)
+from .attention import (dequant_k, dequant_v, attention_dense, decode_paged, decode_paged_hot)
 
 __all__ = [
     "lloyd_max_gaussian", "codebook_fp32",

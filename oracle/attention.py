@@ -20,6 +20,15 @@ Readings taken where the pages are silent:
     of q_len sees keys 0 .. L - q_len + t, L the context length including
     the new tokens.  An empty visible range gives a zero output.
   * Softmax scale 1/sqrt(d) unless given.
+  * Hot window (decode_paged_hot): the pages compress the cache only past a
+    threshold and keep the recent tokens uncompressed ([C] the --turbo-kv
+    option row of the server options table: compression starts after 2,048
+    tokens), and attention covers the compressed history as well as that
+    window ([C] the note on --turbo-kv long-range recall).  Sequence b holds
+    its first L_b tokens compressed and the next W_b tokens exactly; the
+    softmax runs over all L_b + W_b keys.  The q_len new tokens are the last
+    q_len of the window, and query t sees the whole history and window
+    tokens 0 .. W_b - q_len + t.
 """
 
 from __future__ import annotations
@@ -96,6 +105,43 @@ def decode_paged(q, k_pool, v_pool, block_tables, context_lens, centroids_f32, S
             vals = dequant_v(vc, vn, centroids_f32)
             for t in q_positions:
                 vis = max(0, L - q_len + t + 1)
+                for g in range(G):
+                    hq = h * G + g
+                    out[b, t, hq] = attention_dense(q[b, t, hq], keys[:vis], vals[:vis], scale)
+    return out
+
+
+def decode_paged_hot(q, k_pool, v_pool, block_tables, context_lens, hot_k, hot_v, hot_lens,
+                     centroids_f32, S_f32, scale: float | None = None, kv_heads=None,
+                     seqs=None) -> np.ndarray:
+    """Attention of ``q[B][q_len][Hq][d]`` over the compressed history of
+    ``context_lens[b]`` tokens followed by ``hot_lens[b]`` exact tokens
+    ``hot_k[b][j][h]``, ``hot_v[b][j][h]`` (any float dtype, taken exactly).
+
+    Returns float64 ``[B][q_len][Hq][d]``; rows outside the optional subsets
+    are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, q_len, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full(q.shape, np.nan)
+    seqs = range(B) if seqs is None else seqs
+    kv_heads = range(Hkv) if kv_heads is None else kv_heads
+    for b in seqs:
+        L, W = int(context_lens[b]), int(hot_lens[b])
+        row = block_tables[b]
+        for h in kv_heads:
+            kc, ks, kn, kg = read_k_tokens_fast(k_pool, row, L, h)
+            vc, vn = read_v_tokens_fast(v_pool, row, L, h)
+            keys = np.concatenate([dequant_k(kc, ks, kn, kg, centroids_f32, S_f32),
+                                   np.asarray(hot_k[b, :W, h], dtype=np.float64)])
+            vals = np.concatenate([dequant_v(vc, vn, centroids_f32),
+                                   np.asarray(hot_v[b, :W, h], dtype=np.float64)])
+            for t in range(q_len):
+                vis = L + max(0, W - q_len + t + 1)
                 for g in range(G):
                     hq = h * G + g
                     out[b, t, hq] = attention_dense(q[b, t, hq], keys[:vis], vals[:vis], scale)

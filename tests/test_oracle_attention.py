@@ -2,10 +2,11 @@
 import math
 
 import numpy as np
+import scipy.special
 import pytest
 import torch
 
-from oracle import (attention_dense, codebook_fp32, decode_paged, dequant_k, dequant_v,
+from oracle import (attention_dense, codebook_fp32, decode_paged, decode_paged_hot, dequant_k, dequant_v,
                     encode_k, encode_v, fwht, gaussian_matrix)
 from oracle.pages import K_PAGE_BYTES, V_PAGE_BYTES, write_slots_fast
 from oracle.qjl import qjl_alpha
@@ -146,3 +147,45 @@ def test_causal_rows_equal_single_query_calls():
         np.testing.assert_array_equal(o[:, t], single[:, 0])
     # the rows differ: each sees one more key than the previous
     assert not np.allclose(o[0, 0], o[0, 1])
+
+
+def test_hot_window_pins():
+    # Compressed history followed by an exact hot window in one softmax.
+    rng = np.random.default_rng(5)
+    c32, t32 = codebook_fp32()
+    S = gaussian_matrix(42)
+    T, Hkv, G, W = 60, 2, 3, 9
+    kp, vp, table, ek, ev = _pool(rng, T, Hkv, c32, t32, S)
+    hk = (rng.standard_normal((1, W, Hkv, 128)) * 3).astype(np.float32)
+    hv = rng.standard_normal((1, W, Hkv, 128)).astype(np.float32)
+    q = rng.standard_normal((1, 1, G * Hkv, 128))
+    scale = 1 / math.sqrt(128)
+    # no window: the compressed-cache attention itself
+    np.testing.assert_array_equal(decode_paged_hot(q, kp, vp, table, np.array([T]), hk, hv, np.array([0]), c32, S),
+                                  decode_paged(q, kp, vp, table, np.array([T]), c32, S))
+    # no history: library softmax attention on the exact window
+    o = decode_paged_hot(q, kp, vp, table, np.array([0]), hk, hv, np.array([W]), c32, S)
+    for hq in range(G * Hkv):
+        h = hq // G
+        np.testing.assert_allclose(o[0, 0, hq], _sdpa(q[0, 0, hq], hk[0, :, h].astype(np.float64),
+                                                      hv[0, :, h].astype(np.float64), scale), rtol=1e-12, atol=1e-13)
+    # both: the log-sum-exp combination of the two partitions' attentions
+    L, Wb = 37, 5
+    o = decode_paged_hot(q, kp, vp, table, np.array([L]), hk, hv, np.array([Wb]), c32, S)
+    for hq in range(G * Hkv):
+        h = hq // G
+        kc = dequant_k(ek["codes"][:L, h], ek["signs"][:L, h], ek["norm_f16"][:L, h], ek["gamma_f16"][:L, h], c32, S)
+        vc = dequant_v(ev["codes"][:L, h], ev["norm_f16"][:L, h], c32)
+        kh, vh = hk[0, :Wb, h].astype(np.float64), hv[0, :Wb, h].astype(np.float64)
+        lse_c = scipy.special.logsumexp(scale * (kc @ q[0, 0, hq]))
+        lse_h = scipy.special.logsumexp(scale * (kh @ q[0, 0, hq]))
+        wc = 1.0 / (1.0 + math.exp(lse_h - lse_c))
+        ref = wc * _sdpa(q[0, 0, hq], kc, vc, scale) + (1.0 - wc) * _sdpa(q[0, 0, hq], kh, vh, scale)
+        np.testing.assert_allclose(o[0, 0, hq], ref, rtol=1e-10, atol=1e-12)
+    # several new tokens at the end of the window: causal inside it, the last
+    # one equals the single-query call
+    q3 = rng.standard_normal((1, 3, G * Hkv, 128))
+    o3 = decode_paged_hot(q3, kp, vp, table, np.array([L]), hk, hv, np.array([Wb]), c32, S)
+    for t in range(3):
+        single = decode_paged_hot(q3[:, t:t + 1], kp, vp, table, np.array([L]), hk, hv, np.array([Wb - 2 + t]), c32, S)
+        np.testing.assert_array_equal(o3[:, t], single[:, 0])
