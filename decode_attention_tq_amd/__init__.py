@@ -43,7 +43,8 @@ V_PAGE_BYTES = 800
 EXPORTED = [
     "tq_codebook_compute", "tq_qjl_matrix", "tq_codebook_device_bytes", "tq_codebook_init",
     "tq_k_page_bytes", "tq_v_page_bytes", "tq_encode_kv", "tq_decode_workspace_bytes",
-    "tq_decode_attention", "tq_last_error",
+    "tq_decode_attention", "tq_decode_hot_workspace_bytes", "tq_decode_attention_hot",
+    "tq_last_error",
 ]
 
 
@@ -83,6 +84,12 @@ _lib.tq_decode_workspace_bytes.argtypes = [_CB, _I, _I, _I, _I, _I, _I]
 _lib.tq_decode_attention.restype = _I
 _lib.tq_decode_attention.argtypes = [_CB, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                      ctypes.c_float, _P, _I, _I, _P, _SZ, _P]
+_lib.tq_decode_hot_workspace_bytes.restype = _SZ
+_lib.tq_decode_hot_workspace_bytes.argtypes = [_CB, _I, _I, _I, _I, _I, _I]
+_lib.tq_decode_attention_hot.restype = _I
+_lib.tq_decode_attention_hot.argtypes = [_CB, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I,
+                                         _P, _P, _I, _P, _I, ctypes.c_float, _P, _I, _I, _P,
+                                         _SZ, _P]
 
 
 class TQError(RuntimeError):
@@ -245,5 +252,52 @@ def tq_decode_attention(cb: Codebook, q, k_cache, v_cache, block_tables, context
         cb.ref, _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), B, q_len, Hq, num_kv_heads,
         max_context_len, float(softmax_scale), _ptr(out), _dtype_code(out), tokens_per_split,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    return out
+
+
+def tq_decode_hot_workspace_bytes(cb: Codebook, num_seqs: int, num_q_heads: int,
+                                  num_kv_heads: int, max_context_len: int, hot_max: int,
+                                  tokens_per_split: int = 0) -> int:
+    return int(_lib.tq_decode_hot_workspace_bytes(cb.ref, num_seqs, num_q_heads, num_kv_heads,
+                                                  max_context_len, hot_max, tokens_per_split))
+
+
+def tq_decode_attention_hot(cb: Codebook, q, k_cache, v_cache, block_tables, context_lens,
+                            max_context_len: int, num_kv_heads: int, hot_k, hot_v, hot_lens,
+                            out=None, softmax_scale: float = 0.0, tokens_per_split: int = 0,
+                            workspace=None, out_dtype=None, stream=None):
+    """Decode attention (q: [B][1][Hq][128]) over the compressed history of
+    context_lens[b] tokens followed by hot_lens[b] exact tokens of
+    hot_k / hot_v ([B][hot_max][Hkv][128], f32 / f16 / bf16).  Returns ``out``."""
+    torch = _torch()
+    if q.dim() != 4 or q.shape[1] != 1 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][1][Hq][128] tensor")
+    if block_tables.dtype != torch.int32 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32")
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32")
+    if hot_lens.dtype != torch.int32 or not hot_lens.is_contiguous():
+        raise ValueError("hot_lens must be contiguous int32")
+    B, _, Hq, _ = q.shape
+    if (hot_k.dim() != 4 or hot_k.shape[0] != B or hot_k.shape[2] != num_kv_heads
+            or hot_k.shape[3] != HEAD_DIM or not hot_k.is_contiguous()):
+        raise ValueError("hot_k must be a contiguous [B][hot_max][Hkv][128] tensor")
+    if hot_v.shape != hot_k.shape or hot_v.dtype != hot_k.dtype or not hot_v.is_contiguous():
+        raise ValueError("hot_v must match hot_k")
+    hot_max = hot_k.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape:
+        raise ValueError("out must be contiguous with q's shape")
+    need = tq_decode_hot_workspace_bytes(cb, B, Hq, num_kv_heads, max_context_len, hot_max,
+                                         tokens_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    _check(_lib.tq_decode_attention_hot(
+        cb.ref, _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, Hq, num_kv_heads, max_context_len,
+        _ptr(hot_k), _ptr(hot_v), _dtype_code(hot_k), _ptr(hot_lens), hot_max,
+        float(softmax_scale), _ptr(out), _dtype_code(out), tokens_per_split,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
     return out

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
       Ls = fmaf(f, red_l[w][g], Ls);
       A = fmaf(f, red[(w * G + g) * 128 + d], A);
     }
-    float *part = a.partials + ((row0 + g) * a.num_splits + split) * kPartStride;
+    float *part = a.partials + ((row0 + g) * a.part_stride + split) * kPartStride;
     if (d == 0) {
       part[0] = M;
       part[1] = Ls;
@@ -1079,7 +1079,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
     for (int wv = 0; wv < NW; ++wv)
 #pragma unroll
       for (int i = 0; i < 4; ++i) cs += sm.cred[wv][u][grow][i];
-    float *part = a.partials + (query_out_row(a, grp, g) * a.num_splits + split) * kPartStride;
+    float *part = a.partials + (query_out_row(a, grp, g) * a.part_stride + split) * kPartStride;
     if (wave == 0 && t16 == 0) {
       float l = 0.0f;
 #pragma unroll
@@ -1442,7 +1442,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
       for (int wv = 0; wv < 4; ++wv)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cs += sm.cred[wv][u][grow][i];
-      float *part = a.partials + (query_out_row(a, grp, g) * a.num_splits + split) * kPartStride;
+      float *part = a.partials + (query_out_row(a, grp, g) * a.part_stride + split) * kPartStride;
       if (sq == 0 && t16 == 0) {
         float l = 0.0f;
 #pragma unroll
@@ -1480,6 +1480,178 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(Dec
   }
 }
 
+// ---- 2''. exact hot window ---------------------------------------------------
+// The recent tokens a deployment keeps uncompressed (the SwiftLM README
+// compresses only past 2,048 tokens, its --turbo-kv option row) enter the
+// same softmax as the compressed history (its note on --turbo-kv recall):
+// this pass turns window chunks of kHotChunk tokens into partial records of
+// the same form as the split pass (m in log2 units, l, acc' in the rotated
+// domain), placed right after each row's visible compressed chunks, and the
+// merge combines them all.  Single-query decode: every window token is
+// visible.  A workgroup takes one (sequence, KV head, chunk) and all G query
+// heads: thread t scores token t of the chunk against the G queries (held in
+// LDS, read as broadcasts), the block forms each head's maximum and sum,
+// wave w accumulates p v over tokens 64 w .. 64 w + 63 (lane l: coordinates
+// l and l + 64), the waves meet in LDS, and acc is rotated once (H is its
+// own inverse, so the merge's inverse rotation returns it).
+// A window element from the 16-bit pattern of an f16 or a bf16 value.
+template <int DT>
+__device__ __forceinline__ float half_bits_to_float(uint32_t hb) {
+  return DT == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hb) : __uint_as_float(hb << 16);
+}
+
+template <int G, int DT>
+__global__ __launch_bounds__(kHotChunk) void hot_window_kernel(DecodeArgs a) {
+  __shared__ __align__(16) float qs[G][kHeadDim];   // q * scale * log2(e)
+  __shared__ __align__(16) float ps[G][kHotChunk];  // p of each token
+  constexpr int NW = kHotChunk / 64;  // waves: one token per thread
+  __shared__ float red[NW][G];
+  __shared__ __align__(16) float accs[NW][G][kHeadDim];
+  constexpr bool F32 = DT == TQ_F32;
+  constexpr int kEsz = F32 ? 4 : 2;
+  const int c = blockIdx.x % a.hot_parts;
+  const int h = (blockIdx.x / a.hot_parts) % a.num_kv_heads;
+  const int b = blockIdx.x / (a.hot_parts * a.num_kv_heads);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = min(max(a.hot_lens[b], 0), a.hot_max);
+  const int j0 = c * kHotChunk;
+  const int n = max(0, min(W - j0, kHotChunk));  // uniform: tokens of this chunk
+  const int64_t row0 = (int64_t)b * a.num_q_heads + h * G;  // output rows (q_len 1)
+  const float qscale = a.scale * kLog2e;
+  for (int i = tid; i < G * kHeadDim; i += kHotChunk)
+    qs[i / kHeadDim][i % kHeadDim] = qscale * load_as_float(a.q, a.q_dtype, row0 * kHeadDim + i);
+  lds_barrier();
+  // scores: thread t, token j0 + t (past the chunk's end: its last token)
+  float sc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) sc[g] = 0.0f;
+  const int64_t tok_stride = (int64_t)a.num_kv_heads * kHeadDim;
+  const int64_t kbase = ((int64_t)b * a.hot_max + j0 + min(tid, max(n - 1, 0))) * tok_stride + (int64_t)h * kHeadDim;
+  if (n > 0) {  // uniform
+    const uint8_t *krow = static_cast<const uint8_t *>(a.hot_k) + kbase * kEsz;
+    constexpr int kPer = 16 / kEsz;  // elements per 16-byte load
+#pragma unroll 1
+    for (int l0 = 0; l0 < kHeadDim / kPer; l0 += 4) {  // four loads in flight per step
+      uint4 w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const uint4 *>(krow + 16 * (l0 + i));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c0 = (l0 + i) * kPer;
+        const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        float x[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+          x[e] = F32 ? __uint_as_float(ww[e]) : half_bits_to_float<DT>((ww[e / 2] >> (16 * (e & 1))) & 0xFFFFu);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float t = sc[g];
+#pragma unroll
+          for (int e4 = 0; e4 < kPer; e4 += 4) {
+            const float4 q4 = *reinterpret_cast<const float4 *>(&qs[g][c0 + e4]);
+            t = fmaf(q4.x, x[e4], t);
+            t = fmaf(q4.y, x[e4 + 1], t);
+            t = fmaf(q4.z, x[e4 + 2], t);
+            t = fmaf(q4.w, x[e4 + 3], t);
+          }
+          sc[g] = t;
+        }
+      }
+    }
+  }
+  const bool live = tid < n;
+  float mg[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float m = wave_max(live ? sc[g] : -INFINITY);
+    if (lane == 0) red[wave][g] = m;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    mg[g] = red[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mg[g] = fmaxf(mg[g], red[w][g]);
+  }
+  lds_barrier();  // red is reused for the sums
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float p = live ? exp2f(sc[g] - mg[g]) : 0.0f;
+    ps[g][tid] = p;
+    const float l = wave_sum(p);
+    if (lane == 0) red[wave][g] = l;
+  }
+  lds_barrier();
+  // p v over the wave's 64 tokens, eight per step with their loads in flight
+  // together (tokens past the chunk's end repeat its last one; their p is 0)
+  float a0[G], a1[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) a0[g] = a1[g] = 0.0f;
+  const int t0 = 64 * wave, t1 = min(t0 + 64, n);
+  const uint8_t *vbase = static_cast<const uint8_t *>(a.hot_v) +
+                         (((int64_t)b * a.hot_max + j0) * tok_stride + (int64_t)h * kHeadDim) * kEsz;
+  for (int t = t0; t < t1; t += 8) {  // uniform
+    float v0[8], v1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint8_t *o = vbase + (int64_t)min(t + u, t1 - 1) * tok_stride * kEsz;
+      if (F32) {
+        v0[u] = reinterpret_cast<const float *>(o)[lane];
+        v1[u] = reinterpret_cast<const float *>(o)[64 + lane];
+      } else {
+        v0[u] = half_bits_to_float<DT>(reinterpret_cast<const uint16_t *>(o)[lane]);
+        v1[u] = half_bits_to_float<DT>(reinterpret_cast<const uint16_t *>(o)[64 + lane]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float4 pa = *reinterpret_cast<const float4 *>(&ps[g][t]);
+      const float4 pb = *reinterpret_cast<const float4 *>(&ps[g][t + 4]);
+      const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a0[g] = fmaf(pv[u], v0[u], a0[g]);
+        a1[g] = fmaf(pv[u], v1[u], a1[g]);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    accs[wave][g][lane] = a0[g];
+    accs[wave][g][64 + lane] = a1[g];
+  }
+  lds_barrier();
+  // wave w writes the records of heads w, w + NW, ...
+  const int ns = (clamped_context(a, b) + a.split_tokens - 1) / a.split_tokens;  // the row's compressed chunks
+  for (int g = wave; g < G; g += NW) {  // uniform
+    float o0 = 0.0f, o1 = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      o0 += accs[w][g][lane];
+      o1 += accs[w][g][64 + lane];
+      l += red[w][g];
+    }
+    wave_fwht128(o0, o1, lane);
+    float *part = a.partials + ((row0 + g) * a.part_stride + ns + c) * kPartStride;
+    if (lane == 0) {
+      part[0] = n > 0 ? mg[g] : -INFINITY;
+      part[1] = l;
+    }
+    part[4 + lane] = o0;
+    part[68 + lane] = o1;
+  }
+}
+
+template <int G>
+void launch_hot(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  if (a.hot_dtype == TQ_F32)
+    hipLaunchKernelGGL((hot_window_kernel<G, TQ_F32>), grid, dim3(kHotChunk), 0, stream, a);
+  else if (a.hot_dtype == TQ_F16)
+    hipLaunchKernelGGL((hot_window_kernel<G, TQ_F16>), grid, dim3(kHotChunk), 0, stream, a);
+  else
+    hipLaunchKernelGGL((hot_window_kernel<G, TQ_BF16>), grid, dim3(kHotChunk), 0, stream, a);
+}
+
 // ---- 3. merge ---------------------------------------------------------------
 // LSE combine of the chunk partials of an output row, o' = acc'/l, one
 // inverse FWHT, store.  W waves share a row (4/W rows per workgroup); wave w
@@ -1503,8 +1675,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
     const int b = (int)(r / per_seq);
     const int t = (int)((r / a.num_q_heads) % a.q_len);
     const int vis = max(0, clamped_context(a, b) - a.q_len + t + 1);
-    ns = (vis + a.split_tokens - 1) / a.split_tokens;
-    part += r * a.num_splits * kPartStride;
+    ns = (vis + a.split_tokens - 1) / a.split_tokens + a.hot_parts;  // the window's records follow
+    part += r * a.part_stride * kPartStride;
   }
   float M = -INFINITY, Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;  // Ls: lanes < 16, per chunk slot
   for (int base = kMergeBatch * wr; base < ns; base += kMergeBatch * W) {  // uniform
@@ -1628,8 +1800,21 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // four waves per row when there are more chunks than one batch
-  if (a.num_splits > kMergeBatch)
+  if (a.hot_parts > 0) {  // the exact window's records
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.hot_parts));
+    switch (a.group) {
+      case 1: launch_hot<1>(a, grid, stream); break;
+      case 2: launch_hot<2>(a, grid, stream); break;
+      case 4: launch_hot<4>(a, grid, stream); break;
+      case 8: launch_hot<8>(a, grid, stream); break;
+      case 16: launch_hot<16>(a, grid, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // four waves per row when there are more records than one batch
+  if (a.part_stride > kMergeBatch)
     hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, a, rows);
   else
     hipLaunchKernelGGL(merge_kernel<1>, dim3(row_blocks), dim3(256), 0, stream, a, rows);

@@ -147,9 +147,10 @@ constexpr size_t kPartStride = 132;  // floats per partial record: m, l, pad, pa
 
 namespace tq {
 size_t decode_qprep_floats(int64_t rows) { return (size_t)rows * 256; }
-size_t decode_partial_floats(int64_t rows, int num_splits) {
-  return (size_t)rows * (size_t)num_splits * kPartStride;
+size_t decode_partial_floats(int64_t rows, int parts) {
+  return (size_t)rows * (size_t)parts * kPartStride;
 }
+int decode_hot_parts(int hot_max) { return hot_max > 0 ? (hot_max + kHotChunk - 1) / kHotChunk : 0; }
 // A workgroup of the matrix-core decode pass takes at most 8 query rows
 // (positions x heads) of a KV head, two 16-row operand tiles; more positions
 // run as one launch per group of 8 / group of them, each reading the cache
@@ -344,10 +345,11 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
   return TQ_OK;
 }
 
-size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
-                                 int num_q_heads, int num_kv_heads, int max_context_len,
-                                 int tokens_per_split) {
-  (void)cb;
+}  // extern "C"
+
+namespace {
+size_t decode_workspace(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
+                        int tokens_per_split, int hot_parts) {
   if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0)
     return 0;
   int stok, ns;
@@ -356,18 +358,27 @@ size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   // the matrix-core split pass forms its query operands itself: partials only
   const bool mfma = grp > 0 && tq::decode_uses_mfma(q_len, grp);
-  const size_t words = (mfma ? 0 : tq::decode_qprep_floats(rows)) + tq::decode_partial_floats(rows, ns);
+  const size_t words = (mfma ? 0 : tq::decode_qprep_floats(rows)) + tq::decode_partial_floats(rows, ns + hot_parts);
   return words * sizeof(float);
 }
 
-tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
-                              const uint8_t *k_cache, const uint8_t *v_cache,
-                              const int32_t *block_tables, int max_blocks_per_seq,
-                              const int32_t *context_lens, int num_seqs, int q_len,
-                              int num_q_heads, int num_kv_heads, int max_context_len,
-                              float softmax_scale, void *out, tq_dtype out_dtype,
-                              int tokens_per_split, void *workspace, size_t workspace_bytes,
-                              void *stream) {
+// Validation, planning and launch shared by the plain call and the call with
+// an exact hot window (hot: non-null window arguments).
+struct HotWindow {
+  const void *k, *v;
+  tq_dtype dtype;
+  const int32_t *lens;
+  int max;
+};
+
+tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                      const uint8_t *k_cache, const uint8_t *v_cache,
+                      const int32_t *block_tables, int max_blocks_per_seq,
+                      const int32_t *context_lens, int num_seqs, int q_len,
+                      int num_q_heads, int num_kv_heads, int max_context_len,
+                      float softmax_scale, void *out, tq_dtype out_dtype,
+                      int tokens_per_split, void *workspace, size_t workspace_bytes,
+                      void *stream, const HotWindow *hot) {
   tq_status st = check_cb(cb);
   if (st != TQ_OK) return st;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
@@ -396,8 +407,23 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
   int stok, ns;
   plan_splits(num_seqs, q_len, num_kv_heads, group, max_context_len, tokens_per_split, &stok, &ns);
   if (ns > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many splits (%d); raise tokens_per_split", ns);
-  const size_t need = tq_decode_workspace_bytes(cb, num_seqs, q_len, num_q_heads, num_kv_heads,
-                                                max_context_len, tokens_per_split);
+  int hot_parts = 0;
+  if (hot) {
+    if (q_len != 1) return fail(TQ_ERR_UNSUPPORTED, "a hot window is supported for q_len == 1 only (got %d)", q_len);
+    if (hot->max < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "hot_max < 0");
+    if (!dtype_ok(hot->dtype)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown hot_dtype %d", (int)hot->dtype);
+    if (hot->max > 0) {
+      if (!hot->k || !hot->v || !hot->lens) return fail(TQ_ERR_INVALID_ARGUMENT, "null hot window pointer");
+      if ((reinterpret_cast<uintptr_t>(hot->k) & 15) != 0 || (reinterpret_cast<uintptr_t>(hot->v) & 15) != 0)
+        return fail(TQ_ERR_UNSUPPORTED, "hot_k and hot_v must be 16-byte aligned");
+      if ((int64_t)num_seqs * hot->max * num_kv_heads > 0x7fffffffLL)
+        return fail(TQ_ERR_UNSUPPORTED, "hot window too large");
+    }
+    hot_parts = tq::decode_hot_parts(hot->max);
+    if (ns + hot_parts > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many partial records per row");
+  }
+  const size_t need = decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
+                                       tokens_per_split, hot_parts);
   if (workspace_bytes < need)
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   tq::DecodeArgs a;
@@ -433,10 +459,64 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
     rest += tq::decode_qprep_floats(rows);
   }
   a.partials = rest;
+  a.part_stride = ns + hot_parts;
+  a.hot_parts = hot_parts;
+  a.hot_k = hot ? hot->k : nullptr;
+  a.hot_v = hot ? hot->v : nullptr;
+  a.hot_dtype = hot ? hot->dtype : TQ_F32;
+  a.hot_lens = hot ? hot->lens : nullptr;
+  a.hot_max = hot ? hot->max : 0;
   a.cb = device_codebook(cb);
   hipError_t e = tq::launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return TQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
+                                 int num_q_heads, int num_kv_heads, int max_context_len,
+                                 int tokens_per_split) {
+  (void)cb;
+  return decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0);
+}
+
+tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                              const uint8_t *k_cache, const uint8_t *v_cache,
+                              const int32_t *block_tables, int max_blocks_per_seq,
+                              const int32_t *context_lens, int num_seqs, int q_len,
+                              int num_q_heads, int num_kv_heads, int max_context_len,
+                              float softmax_scale, void *out, tq_dtype out_dtype,
+                              int tokens_per_split, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  return decode_impl(cb, q, q_dtype, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, softmax_scale, out,
+                     out_dtype, tokens_per_split, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t tq_decode_hot_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads,
+                                     int num_kv_heads, int max_context_len, int hot_max,
+                                     int tokens_per_split) {
+  (void)cb;
+  if (hot_max < 0) return 0;
+  return decode_workspace(num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, tokens_per_split,
+                          tq::decode_hot_parts(hot_max));
+}
+
+tq_status tq_decode_attention_hot(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                                  const uint8_t *k_cache, const uint8_t *v_cache,
+                                  const int32_t *block_tables, int max_blocks_per_seq,
+                                  const int32_t *context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int max_context_len, const void *hot_k,
+                                  const void *hot_v, tq_dtype hot_dtype, const int32_t *hot_lens,
+                                  int hot_max, float softmax_scale, void *out, tq_dtype out_dtype,
+                                  int tokens_per_split, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  const HotWindow hw{hot_k, hot_v, hot_dtype, hot_lens, hot_max};
+  return decode_impl(cb, q, q_dtype, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, softmax_scale, out,
+                     out_dtype, tokens_per_split, workspace, workspace_bytes, stream, &hw);
 }
 
 }  // extern "C"

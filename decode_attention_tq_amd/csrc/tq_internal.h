@@ -80,13 +80,26 @@ struct DecodeArgs {
   // digits each); qk_tiles is 0 for the other passes.
   int qk_tiles;
   int pos0, pos_count;
-  float *partials;     // workspace: [rows][num_splits][4 + 128], m in log2 units
+  float *partials;     // workspace: [rows][part_stride][4 + 128], m in log2 units
+  // Partial records per row: the num_splits chunks of the compressed cache,
+  // then (for a call with an exact hot window) hot_parts chunks of
+  // kHotChunk window tokens, placed right after the row's visible chunks.
+  int part_stride;
+  int hot_parts;
+  const void *hot_k;   // [num_seqs][hot_max][num_kv_heads][128], dtype hot_dtype
+  const void *hot_v;
+  int hot_dtype;
+  const int32_t *hot_lens;  // [num_seqs], cut to [0, hot_max]
+  int hot_max;
   Codebook cb;
 };
 
+constexpr int kHotChunk = 256;  // exact window tokens per partial record
+
 // Workspace split of tq_decode_attention.
 size_t decode_qprep_floats(int64_t rows);
-size_t decode_partial_floats(int64_t rows, int num_splits);
+size_t decode_partial_floats(int64_t rows, int parts);
+int decode_hot_parts(int hot_max);
 // The matrix-core split pass serves decode with up to 8 heads per KV head
 // and short query blocks (multi-token verify), one launch per group of
 // 8 / group positions, at most 4 launches; single-query decode with 16 heads

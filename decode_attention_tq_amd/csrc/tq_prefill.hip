@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     float l_row = l_part[u] + xchg16(l_part[u], lane);
     l_row += xchg32(l_row, lane);
     if (row_ok[u]) {
-      float *part = a.partials + (R[u] * a.num_splits + split) * kPartStride;
+      float *part = a.partials + (R[u] * a.part_stride + split) * kPartStride;
       if (g4 == 0) {
         part[0] = m_run[u];
         part[1] = l_row;

@@ -186,6 +186,40 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
                               int tokens_per_split, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* ---- attention with an exact hot window -----------------------------------
+ * The SwiftLM README keeps the recent tokens uncompressed and compresses only
+ * past a threshold (its --turbo-kv option row: after 2,048 tokens), and
+ * attention covers both (its note on --turbo-kv long-range recall).  This
+ * call is tq_decode_attention for one new token per sequence (q_len = 1)
+ * whose keys are the context_lens[b] compressed tokens of the paged cache
+ * followed by hot_lens[b] exact tokens: one softmax over all of them.
+ *   hot_k, hot_v device [num_seqs][hot_max][num_kv_heads][128], dtype
+ *               hot_dtype, 16-byte aligned (token j of sequence b, KV head h
+ *               at ((b * hot_max + j) * num_kv_heads + h) * 128).
+ *   hot_lens    device int32[num_seqs], each in [0, hot_max] (values outside
+ *               are cut to that range).  hot_max == 0: no window; the
+ *               pointers may then be NULL.
+ *   workspace   tq_decode_hot_workspace_bytes() bytes (same arguments).
+ * The other arguments are those of tq_decode_attention with q_len = 1 (the
+ * query is [num_seqs][1][num_q_heads][128]; context_lens may be 0).
+ * A sequence with no key at all gets a zero output.
+ * Errors: those of tq_decode_attention, TQ_ERR_INVALID_ARGUMENT (hot_max < 0,
+ * null window pointers with hot_max > 0, unknown hot_dtype),
+ * TQ_ERR_UNSUPPORTED (misaligned window, window too large). */
+size_t tq_decode_hot_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads,
+                                     int num_kv_heads, int max_context_len, int hot_max,
+                                     int tokens_per_split);
+
+tq_status tq_decode_attention_hot(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                                  const uint8_t *k_cache, const uint8_t *v_cache,
+                                  const int32_t *block_tables, int max_blocks_per_seq,
+                                  const int32_t *context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int max_context_len, const void *hot_k,
+                                  const void *hot_v, tq_dtype hot_dtype, const int32_t *hot_lens,
+                                  int hot_max, float softmax_scale, void *out, tq_dtype out_dtype,
+                                  int tokens_per_split, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* Thread-local text describing the last non-OK status on this thread. */
 const char *tq_last_error(void);
 

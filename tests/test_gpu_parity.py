@@ -8,8 +8,10 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import (check_decode, check_encoded_sequence, codebook, decode_gpu, dev,
+from gpu_helpers import (OUT_RTOL, check_decode, check_encoded_sequence, codebook, decode_gpu, dev,
                          encode_gpu, new_pools, oracle_tables, rel_rows)
+from oracle import decode_paged_hot
+import decode_attention_tq_amd as tq
 
 pytestmark = pytest.mark.gpu
 
@@ -324,3 +326,41 @@ def test_prefill_groups_batches_and_splits(Hq, Hkv):
         outs.append(out)
     # a different chunking changes only the rounding of the combine
     assert np.abs(outs[0] - outs[1]).max() <= 1e-4 * max(1.0, np.abs(outs[0]).max())
+
+
+@pytest.mark.parametrize("Hq,Hkv,hot_dtype", [(32, 8, torch.bfloat16), (16, 16, torch.float16),
+                                             (32, 4, torch.float32), (32, 2, torch.bfloat16)])
+def test_hot_window(Hq, Hkv, hot_dtype):
+    """Decode over a compressed history followed by an exact hot window of
+    recent tokens, one softmax over both: ragged histories (one empty) and
+    windows (one empty, one of 2,048 tokens, several 256-token chunks and a
+    ragged last one), a sequence with no key at all (zero output), 1 to 16
+    query heads per KV head, window tokens in bf16, f16 and f32."""
+    rng = np.random.default_rng(40 + Hq // Hkv)
+    lens = np.array([0, 700, 2300, 5, 0], dtype=np.int64)
+    hot = np.array([300, 0, 2048, 77, 0], dtype=np.int32)
+    B, hot_max = len(lens), 2048
+    table, nb = synth.block_tables(rng, np.maximum(lens, 1))
+    cb = codebook()
+    kpool, vpool = new_pools(nb, Hkv)
+    for b in range(B):
+        if lens[b] == 0:
+            continue
+        k = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        v = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        encode_gpu(cb, k, v, synth.slots_for(table, b, np.arange(lens[b])), kpool, vpool, with_norms=False)
+    hk = torch.from_numpy(synth.kv_tensor(rng, B * hot_max, Hkv).reshape(B, hot_max, Hkv, 128)).to(hot_dtype)
+    hv = torch.from_numpy(synth.kv_tensor(rng, B * hot_max, Hkv).reshape(B, hot_max, Hkv, 128)).to(hot_dtype)
+    q = synth.queries(rng, B, 1, Hq)
+    out = tq.tq_decode_attention_hot(
+        cb, dev(q, torch.bfloat16), kpool, vpool, torch.from_numpy(table).cuda(),
+        torch.from_numpy(lens.astype(np.int32)).cuda(), int(lens.max()), Hkv,
+        hk.cuda(), hv.cuda(), torch.from_numpy(hot).cuda())
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    c32, _, S = oracle_tables()
+    ref = decode_paged_hot(np.asarray(q, np.float64), _np(kpool), _np(vpool), table, lens, hk.double().numpy(),
+                           hv.double().numpy(), hot, c32, S)
+    err = rel_rows(out, ref)
+    assert err.max() <= OUT_RTOL, f"max row rel err {err.max():.3e}"
+    assert np.all(out[4] == 0)  # no key at all

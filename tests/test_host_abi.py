@@ -167,3 +167,36 @@ def test_workspace_plan_is_consistent(B, q_len, Hq, Hkv):
             assert splits == max(1, -(-max(maxc, q_len) // tps))
     assert tq._lib.tq_decode_workspace_bytes(ref, 0, 1, 32, 8, 10, 0) == 0
     assert tq._lib.tq_k_page_bytes(ref) == 1088 and tq._lib.tq_v_page_bytes(ref) == 800
+
+
+def _hot(cb, **kw):
+    a = dict(q=FAKE, qd=tq.TQ_BF16, kc=FAKE, vc=FAKE, bt=FAKE, mb=64, cl=FAKE, B=1,
+             Hq=32, Hkv=8, maxc=1024, hk=FAKE, hv=FAKE, hd=tq.TQ_BF16, hl=FAKE, hmax=300,
+             scale=0.0, out=FAKE, od=tq.TQ_F32, tps=0, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return tq._lib.tq_decode_attention_hot(
+        ctypes.byref(cb), a["q"], a["qd"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["B"],
+        a["Hq"], a["Hkv"], a["maxc"], a["hk"], a["hv"], a["hd"], a["hl"], a["hmax"], a["scale"],
+        a["out"], a["od"], a["tps"], a["ws"], a["wsb"], None)
+
+
+def test_hot_window_validation():
+    cb = _fake_cb()
+    E = tq.TQ_ERR_INVALID_ARGUMENT
+    assert _hot(_fake_cb(False)) == tq.TQ_ERR_NOT_INITIALIZED
+    assert _hot(cb, q=None) == E                                  # the plain call's checks
+    assert _hot(cb, Hq=24, Hkv=8) == tq.TQ_ERR_UNSUPPORTED
+    assert _hot(cb, hmax=-1) == E
+    assert _hot(cb, hk=None) == E
+    assert _hot(cb, hl=None) == E
+    assert _hot(cb, hd=7) == E
+    assert _hot(cb, hv=FAKE + 8) == tq.TQ_ERR_UNSUPPORTED         # misaligned window
+    ref = ctypes.byref(cb)
+    need = tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, 300, 0)
+    assert _hot(cb, wsb=need - 1) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+    # no window: the plain decode workspace; a window of 300 tokens adds two
+    # partial records (256-token chunks) per query row
+    plain = tq._lib.tq_decode_workspace_bytes(ref, 1, 1, 32, 8, 1024, 0)
+    assert tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, 0, 0) == plain
+    assert need == plain + 32 * 2 * 132 * 4
+    assert tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, -1, 0) == 0
