@@ -143,6 +143,58 @@ def long_context_attention(tq, cb, dev, stream, steps=30, warmup=5):
             "pct_peak": round(100 * by / (us / 1e6) / 1e9 / HBM_PEAK_GBPS, 2)}
 
 
+def hot_window_attention(tq, cb, dev, stream, steps=30, warmup=5, T=8192, W=2048):
+    """Decode with an exact bf16 hot window of W recent tokens after T
+    compressed ones (32q/8kv): the deployment the pages describe, with the
+    window at their 2,048-token compression threshold.  Replicas rotate so
+    that consecutive calls share no data through the Infinity Cache."""
+    import torch
+    import synth
+    nb = T // 16
+    per_replica = nb * HKV * (1088 + 800) + W * HKV * D * 2 * 2
+    R = max(2, -(-2 * MALL_BYTES // per_replica) + 1)
+    rng = np.random.default_rng(5)
+    table = torch.from_numpy(rng.permutation(nb).astype(np.int32)[None, :]).to(dev)
+    slots = (table[0].to(torch.int64)[:, None] * 16 + torch.arange(16, device=dev)).reshape(-1)
+    k = synth.kv_tensor_device(41, T, HKV, dev)
+    v = synth.kv_tensor_device(42, T, HKV, dev)
+    reps = []
+    for r in range(R):
+        kp = torch.empty((nb, HKV, 1088), dtype=torch.uint8, device=dev)
+        vp = torch.empty((nb, HKV, 800), dtype=torch.uint8, device=dev)
+        tq.tq_encode_kv(cb, k, v, slots, kp, vp, stream=stream)
+        hk = synth.kv_tensor_device(100 + 2 * r, W, HKV, dev).to(torch.bfloat16).reshape(1, W, HKV, D)
+        hv = synth.kv_tensor_device(101 + 2 * r, W, HKV, dev).to(torch.bfloat16).reshape(1, W, HKV, D)
+        reps.append((kp, vp, hk, hv))
+    del k, v
+    q = torch.from_numpy(synth.queries(rng, 1, 1, HQ)).to(dev, torch.bfloat16)
+    clens = torch.tensor([T], dtype=torch.int32, device=dev)
+    hlens = torch.tensor([W], dtype=torch.int32, device=dev)
+    out = torch.empty((1, 1, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_decode_hot_workspace_bytes(cb, 1, HQ, HKV, T, W), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        kp, vp, hk, hv = reps[i % R]
+        tq.tq_decode_attention_hot(cb, q, kp, vp, table, clens, T, HKV, hk, hv, hlens, out=out,
+                                   workspace=ws, stream=stream)
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        call(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    by = T * HKV * 118 + W * HKV * D * 2 * 2 + nb * 4 + HQ * D * 2 + HQ * D * 4 + 8
+    del reps
+    return {"context": T, "hot_window": W, "q_heads": HQ, "kv_heads": HKV, "replicas": R,
+            "algorithmic_bytes": by, "us": round(us, 2), "GBps": round(by / (us / 1e6) / 1e9, 1),
+            "pct_peak": round(100 * by / (us / 1e6) / 1e9 / HBM_PEAK_GBPS, 2)}
+
+
 def counters_driver(tq, cb, dev, stream, reps, case_slots, launches=8):
     """Launches for rocprofv3 --pmc passes: encode launches on cold replicas,
     then plain device copies of 512 MiB (calibration of the byte counters)."""
@@ -236,6 +288,8 @@ def main():
                     help="write profiles/traffic.json from two counter runs of --counters")
     ap.add_argument("--long-context-only", action="store_true",
                     help="only the long-context decode measurement (for kernel traces of it)")
+    ap.add_argument("--hot-window-only", action="store_true",
+                    help="only the decode with an exact 2,048-token window after 8,192 compressed tokens")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -252,6 +306,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cb = tq.tq_codebook_init(128, 3, synth.QJL_SEED, device=dev)
+    if args.hot_window_only:
+        print(json.dumps({"attention_hot_window": hot_window_attention(
+            tq, cb, dev, torch.cuda.current_stream(dev), steps=args.steps, warmup=args.warmup)}))
+        return
     if args.long_context_only:
         print(json.dumps({"attention_long": long_context_attention(
             tq, cb, dev, torch.cuda.current_stream(dev), steps=args.steps, warmup=args.warmup)}))
