@@ -364,3 +364,22 @@ def test_hot_window(Hq, Hkv, hot_dtype):
     err = rel_rows(out, ref)
     assert err.max() <= OUT_RTOL, f"max row rel err {err.max():.3e}"
     assert np.all(out[4] == 0)  # no key at all
+
+
+def test_hot_window_empty_is_the_plain_call():
+    """With no window (hot_max 0, null window pointers) the call is the plain
+    decode launch sequence: bit-identical output."""
+    case = synth.gqa_case(seed=13, T=1500, Hq=32, Hkv=8)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 8)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    q = dev(case["q"], torch.bfloat16)
+    bt = torch.from_numpy(case["table"]).cuda()
+    cl = torch.from_numpy(case["context_lens"]).cuda()
+    T = int(case["context_lens"].max())
+    plain = tq.tq_decode_attention(cb, q, kpool, vpool, bt, cl, T, 8)
+    empty = torch.empty((1, 0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    hot = tq.tq_decode_attention_hot(cb, q, kpool, vpool, bt, cl, T, 8, empty, empty,
+                                     torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(plain, hot)
