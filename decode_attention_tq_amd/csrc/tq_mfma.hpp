@@ -5,13 +5,10 @@
 //   B = fp4 e2m1 values read straight from packed bits: one and_or per 8
 //       values;
 //   A = a float operand written as integer digits, one digit per A row, each
-//       row's place value carried by its scale: fp8 e4m3 (exact for
-//       |d| <= 16), or fp6 e2m3 for the score contraction, where the code of
-//       d/8 is sign << 5 | |d| for |d| <= 16 and the instruction runs at the
-//       fp4/fp6 rate (about 1.8x the fp8 x fp4 rate, measured).
+//       row's place value carried by its scale, as fp6 e2m3 codes: the code
+//       of d/8 is sign << 5 | |d| for |d| <= 16, and the instruction runs at
+//       the fp4/fp6 rate (about 1.8x the fp8 x fp4 rate, measured).
 // Operand layouts (lane l, measured on gfx950 with one-hot operands):
-//   A fp8: row l%16; its 32 bytes (8 registers) hold logical K
-//      64*(s/16) + 16*(l/16) + s%16 for byte s = 0..31;
 //   A fp6: row l%16; its 32 six-bit codes, packed in order (code s at bits
 //      6s .. 6s+5 of registers 0..5), hold logical K 32*(l/16) + s;
 //   B fp4: column l%16; its 32 nibbles (4 registers) hold logical K
@@ -30,27 +27,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kE8M0One = 127;  // E8M0 encoding of 2^0
 
-// Logical K of A byte s in lane group ga.
-__device__ __forceinline__ int mfma_a_slot_k(int ga, int s) { return 64 * (s >> 4) + 16 * ga + (s & 15); }
-
-// Coordinate (token) that logical K index kap of a B operand made by b_pm1
+// Coordinate (token) that logical K index kap of a B operand made by b_split
 // from the 32-bit word of coordinates 32*(kap/32) .. +31 stands for: nibble
 // t of register v holds bit 4t + v.
 __device__ __forceinline__ int b_coord(int kap) { return 32 * (kap >> 5) + 4 * (kap & 7) + ((kap >> 3) & 3); }
-// Inverse within a 32-wide block: logical K of coordinate 32a + 4t + v.
-__device__ __forceinline__ int b_kappa(int c) { return 32 * (c >> 5) + 8 * (c & 3) + ((c & 31) >> 2); }
-
-// B operand of 32 values +-1 from 32 bits: value = 1 - 2 * bit.  Register v,
-// nibble t takes bit 4t + v (shifted to the fp4 sign position, magnitude 1.0).
-__device__ __forceinline__ v8i b_pm1(uint32_t P) {
-  v8i b;
-  b[0] = (int)(((P << 3) & 0x88888888u) | 0x22222222u);
-  b[1] = (int)(((P << 2) & 0x88888888u) | 0x22222222u);
-  b[2] = (int)(((P << 1) & 0x88888888u) | 0x22222222u);
-  b[3] = (int)((P & 0x88888888u) | 0x22222222u);
-  b[4] = b[5] = b[6] = b[7] = 0;
-  return b;
-}
 
 // B operand from 32 bits with one instruction per register, avoiding fp4
 // subnormals: register v keeps bit v of each nibble in place, giving the e2m1
@@ -62,7 +42,7 @@ __device__ __forceinline__ v8i b_pm1(uint32_t P) {
 // A contraction against the +-1 values 1 - 2 bit is recovered by scaling the
 // A value of a K slot in register v by f_v = -2/beta_v (-1, -1, -1, +1: no
 // digit grows, so fp6 digits stay exact) and adding sum_k A_k (1 - f_v
-// alpha_v), i.e. weights 5, 3, 1, 0 (b_split_weight):
+// alpha_v), i.e. weights 5, 3, 1, 0:
 //   sum_k A_k (1 - 2 b_k) = sum_k (f_v A_k) B'_k + sum_k (1 - f_v alpha_v) A_k.
 __device__ __forceinline__ v8i b_split(uint32_t P) {
   v8i b;
@@ -73,26 +53,14 @@ __device__ __forceinline__ v8i b_split(uint32_t P) {
   b[4] = b[5] = b[6] = b[7] = 0;
   return b;
 }
-// Register of logical K index kap inside its 32-wide block, the A factor and
-// the start-value weight that go with b_split.
+// Register of logical K index kap inside its 32-wide block and the A factor
+// that goes with b_split.
 __device__ __forceinline__ int b_reg(int kap) { return (kap >> 3) & 3; }
 __device__ __forceinline__ float b_split_factor(int kap) { return b_reg(kap) == 3 ? 1.0f : -1.0f; }
-__device__ __forceinline__ float b_split_weight(int kap) {
-  const int v = b_reg(kap);
-  return v == 0 ? 5.0f : v == 1 ? 3.0f : v == 2 ? 1.0f : 0.0f;
-}
 
-__device__ __forceinline__ v4f mfma_f8f4(const v8i &A, const v8i &B, const v4f &C, int scale_a) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, 0, 4, 0, scale_a, 0, kE8M0One);
-}
 // A fp6 e2m3 (registers 0..5), B fp4.
 __device__ __forceinline__ v4f mfma_f6f4(const v8i &A, const v8i &B, const v4f &C, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, 2, 4, 0, scale_a, 0, kE8M0One);
-}
-// fp6 e2m3 code of d/8 for an integer |d| <= 16.
-__device__ __forceinline__ uint32_t fp6_code(float d) {
-  const int n = (int)d;
-  return (uint32_t)((n < 0 ? 32 : 0) | (n < 0 ? -n : n));
 }
 constexpr int kFp6Exp = 3;  // fp6 digit codes stand for d / 8
 
