@@ -195,6 +195,50 @@ def hot_window_attention(tq, cb, dev, stream, steps=30, warmup=5, T=8192, W=2048
             "pct_peak": round(100 * by / (us / 1e6) / 1e9 / HBM_PEAK_GBPS, 2)}
 
 
+def verify_attention(tq, cb, dev, stream, steps=30, warmup=5, T=32768, q_lens=(1, 2, 4, 8)):
+    """Multi-token verify decode: q_len new tokens per sequence (causal over
+    the block) over T compressed tokens, 32q/8kv, the pages' speculative /
+    multi-token decoding step.  Replicas rotate beyond the Infinity Cache."""
+    import torch
+    import synth
+    nb = T // 16
+    per_replica = nb * HKV * (1088 + 800)
+    R = max(2, -(-2 * MALL_BYTES // per_replica) + 1)
+    rng = np.random.default_rng(6)
+    table = torch.from_numpy(rng.permutation(nb).astype(np.int32)[None, :]).to(dev)
+    slots = (table[0].to(torch.int64)[:, None] * 16 + torch.arange(16, device=dev)).reshape(-1)
+    k = synth.kv_tensor_device(41, T, HKV, dev)
+    v = synth.kv_tensor_device(42, T, HKV, dev)
+    pools = []
+    for r in range(R):
+        kp = torch.empty((nb, HKV, 1088), dtype=torch.uint8, device=dev)
+        vp = torch.empty((nb, HKV, 800), dtype=torch.uint8, device=dev)
+        tq.tq_encode_kv(cb, k, v, slots, kp, vp, stream=stream)
+        pools.append((kp, vp))
+    del k, v
+    clens = torch.tensor([T], dtype=torch.int32, device=dev)
+    res = {"context": T, "q_heads": HQ, "kv_heads": HKV, "replicas": R, "us_per_call": {}}
+    for q_len in q_lens:
+        q = torch.from_numpy(synth.queries(rng, 1, q_len, HQ)).to(dev, torch.bfloat16)
+        out = torch.empty((1, q_len, HQ, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(tq.tq_decode_workspace_bytes(cb, 1, q_len, HQ, HKV, T), dtype=torch.uint8, device=dev)
+        for i in range(warmup):
+            kp, vp = pools[i % R]
+            tq.tq_decode_attention(cb, q, kp, vp, table, clens, T, HKV, out=out, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            kp, vp = pools[(warmup + i) % R]
+            tq.tq_decode_attention(cb, q, kp, vp, table, clens, T, HKV, out=out, workspace=ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["us_per_call"][str(q_len)] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    del pools
+    return res
+
+
 def counters_driver(tq, cb, dev, stream, reps, case_slots, launches=8):
     """Launches for rocprofv3 --pmc passes: encode launches on cold replicas,
     then plain device copies of 512 MiB (calibration of the byte counters)."""
@@ -288,6 +332,8 @@ def main():
                     help="write profiles/traffic.json from two counter runs of --counters")
     ap.add_argument("--long-context-only", action="store_true",
                     help="only the long-context decode measurement (for kernel traces of it)")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="only multi-token verify decode (q_len 1, 2, 4, 8) over 32,768 compressed tokens")
     ap.add_argument("--hot-window-only", action="store_true",
                     help="only the decode with an exact 2,048-token window after 8,192 compressed tokens")
     args = ap.parse_args()
@@ -306,6 +352,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cb = tq.tq_codebook_init(128, 3, synth.QJL_SEED, device=dev)
+    if args.verify_only:
+        print(json.dumps({"attention_verify": verify_attention(
+            tq, cb, dev, torch.cuda.current_stream(dev), steps=args.steps, warmup=args.warmup)}))
+        return
     if args.hot_window_only:
         print(json.dumps({"attention_hot_window": hot_window_attention(
             tq, cb, dev, torch.cuda.current_stream(dev), steps=args.steps, warmup=args.warmup)}))
