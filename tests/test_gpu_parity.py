@@ -383,3 +383,29 @@ def test_hot_window_empty_is_the_plain_call():
                                      torch.zeros(1, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(plain, hot)
+
+
+def test_hot_window_bench_size_sampled():
+    """The hot-window decode at the size bench.py --hot-window-only times
+    (8,192 compressed tokens + a 2,048-token bf16 window, 32q/8kv), checked
+    on two sampled KV heads (eight query heads)."""
+    case = synth.gqa_case(seed=14, T=8192, Hq=32, Hkv=8)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 8)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    rng = np.random.default_rng(15)
+    W = 2048
+    hk = torch.from_numpy(synth.kv_tensor(rng, W, 8).reshape(1, W, 8, 128)).to(torch.bfloat16)
+    hv = torch.from_numpy(synth.kv_tensor(rng, W, 8).reshape(1, W, 8, 128)).to(torch.bfloat16)
+    hl = np.array([W], dtype=np.int32)
+    out = tq.tq_decode_attention_hot(
+        cb, dev(case["q"], torch.bfloat16), kpool, vpool, torch.from_numpy(case["table"]).cuda(),
+        torch.from_numpy(case["context_lens"]).cuda(), 8192, 8, hk.cuda(), hv.cuda(), torch.from_numpy(hl).cuda())
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    c32, _, S = oracle_tables()
+    ref = decode_paged_hot(np.asarray(case["q"], np.float64), _np(kpool), _np(vpool), case["table"],
+                           case["context_lens"], hk.double().numpy(), hv.double().numpy(), hl, c32, S,
+                           kv_heads=[0, 5])
+    err = rel_rows(out, ref)
+    assert err.size == 8 and err.max() <= OUT_RTOL, f"max row rel err {err.max():.3e}"
