@@ -409,3 +409,18 @@ def test_hot_window_bench_size_sampled():
                            kv_heads=[0, 5])
     err = rel_rows(out, ref)
     assert err.size == 8 and err.max() <= OUT_RTOL, f"max row rel err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("q_len", [2, 8])
+def test_multi_token_verify_bench_size_sampled(q_len):
+    """Multi-token verify at the size bench.py --verify-only times (32,768
+    compressed tokens, 32q/8kv; one and four launches), checked on two
+    sampled KV heads and every new position."""
+    case = synth.gqa_case(seed=16 + q_len, T=32768, Hq=32, Hkv=8, q_len=q_len)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], 8)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], 8)
+    err = check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"], case["context_lens"],
+                       kv_heads=[2, 7])
+    assert err.size == 2 * 4 * q_len
