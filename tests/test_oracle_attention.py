@@ -189,3 +189,72 @@ def test_hot_window_pins():
     for t in range(3):
         single = decode_paged_hot(q3[:, t:t + 1], kp, vp, table, np.array([L]), hk, hv, np.array([Wb - 2 + t]), c32, S)
         np.testing.assert_array_equal(o3[:, t], single[:, 0])
+
+
+def _sphere_coordinate_distortion(c32, t32, d):
+    """d * E[(y - Q(y))^2] for one coordinate y of a point drawn uniformly on
+    the unit sphere in R^d (density proportional to (1 - y^2)^((d-3)/2) on
+    [-1, 1]), by adaptive quadrature over the cells of the fp32 codebook."""
+    from scipy import integrate, special
+    c = np.asarray(c32, np.float64)
+    t = np.asarray(t32, np.float64)
+    log_c = special.gammaln(d / 2) - 0.5 * math.log(math.pi) - special.gammaln((d - 1) / 2)
+
+    def dens(y):
+        return math.exp(log_c + 0.5 * (d - 3) * math.log1p(-y * y))
+
+    edges = [-1.0, *t, 1.0]
+    total = 0.0
+    for k in range(len(c)):
+        total += integrate.quad(lambda y: (y - c[k]) ** 2 * dens(y), edges[k], edges[k + 1],
+                                epsabs=1e-14, epsrel=1e-12)[0]
+    return d * total
+
+
+def test_dequant_v_reconstruction_error_is_the_codebook_distortion():
+    # For an isotropic x, u = x/|x| is uniform on the sphere and so is y = H u
+    # (H orthogonal); dequant_v(encode_v(x)) = n H^T c[idx] differs from x by
+    # n H^T (c[idx] - y), so |x^ - x|^2 / |x|^2 = |y - c[idx]|^2 up to the
+    # half rounding of n.  Its mean is the quantiser's distortion on the
+    # sphere marginal, computed here by quadrature, and close to Max's
+    # Gaussian figure 0.03454 (the sphere marginal has lighter tails).
+    # With the centroid condition E<c[idx], y> = E|c[idx]|^2 = 1 - D, so the
+    # cosine between x^ and x is about sqrt(1 - D).
+    rng = np.random.default_rng(21)
+    c32, t32 = codebook_fp32(128, 3)
+    n = 20000
+    x = rng.standard_normal((n, 128)) * rng.exponential(5.0, (n, 1))
+    ev = encode_v(x, c32, t32)
+    xh = dequant_v(ev["codes"], ev["norm_f16"], c32)
+    rel = np.sum((xh - x) ** 2, axis=-1) / np.sum(x * x, axis=-1)
+    D = _sphere_coordinate_distortion(c32, t32, 128)
+    se = rel.std(ddof=1) / math.sqrt(n)
+    assert abs(rel.mean() - D) < 4 * se + 1e-6, (rel.mean(), D, se)
+    assert abs(D / 0.03454 - 1.0) < 0.03
+    cos = np.sum(xh * x, axis=-1) / (np.linalg.norm(xh, axis=-1) * np.linalg.norm(x, axis=-1))
+    assert abs(cos.mean() - math.sqrt(1.0 - D)) < 5e-4, (cos.mean(), math.sqrt(1.0 - D))
+
+
+def test_dequant_v_closed_forms():
+    # Every code at the top level: c[7] * (1, ..., 1) rotates back to
+    # c[7] sqrt(d) e_0 (the first Sylvester row is the only one with a
+    # non-zero sum).  Codes following the sign pattern of Sylvester row j
+    # (7 where the entry is positive, 0 where negative; c[0] = -c[7]) rotate
+    # back to c[7] sqrt(d) e_j.  The stored half norm multiplies the result.
+    c32, _ = codebook_fp32(128, 3)
+    c7 = float(c32[7])
+    assert c32[0] == -c32[7]
+    n16 = np.array([3.5], dtype=np.float16)
+    out = dequant_v(np.full((1, 128), 7, np.uint8), n16, c32)[0]
+    want = np.zeros(128)
+    want[0] = 3.5 * c7 * math.sqrt(128)
+    np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-13)
+    hrow = np.ones((1, 1))
+    while hrow.shape[0] < 128:
+        hrow = np.block([[hrow, hrow], [hrow, -hrow]])
+    for j in (1, 37, 127):
+        codes = np.where(hrow[j] > 0, 7, 0).astype(np.uint8)[None]
+        out = dequant_v(codes, np.array([2.0], np.float16), c32)[0]
+        want = np.zeros(128)
+        want[j] = 2.0 * c7 * math.sqrt(128)
+        np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-13)

@@ -1,6 +1,8 @@
 """Pins of the oracle's QJL generator and of the estimator it serves."""
 import math
 
+import pytest
+
 import numpy as np
 from scipy import stats
 
@@ -56,7 +58,8 @@ def _estimate_stats(draws=3000, seed=11):
     return est, float(x @ q), n, r, q
 
 
-def test_qjl_estimator_unbiased_with_closed_form_variance():
+def test_qjl_estimator_variance_at_128_rows():
+    # one 128-row S per draw, 3,000 draws: the per-draw variance at m = 128
     est, exact, n, r, q = _estimate_stats()
     se = est.std(ddof=1) / math.sqrt(est.size)
     # the half-precision norm moves the mean by at most 2^-11 relative
@@ -70,3 +73,40 @@ def test_qjl_estimator_unbiased_with_closed_form_variance():
 
 def test_alpha_value():
     assert qjl_alpha(128) == math.sqrt(math.pi / 2) / 128
+
+
+@pytest.mark.parametrize("pair", [0, 1, 2])
+def test_qjl_estimator_unbiased_over_20000_draws(pair):
+    """Unbiasedness over 20,000 independent 128 x 128 draws of S for three
+    (x, q) pairs.  The draws are stacked: encode_k and dequant_k are called
+    with the rows of 100 draws at once (m = 12,800).  The estimator is linear
+    in the rows, and qjl_alpha(m) = sqrt(pi/2)/m, so each call returns the mean
+    of its 100 per-draw estimates.  The 200 batch means must average to <q, x>
+    within 4 standard errors, and their variance must match the closed form
+    n^2 ((pi/2)|q|^2|r|^2 - <q, r>^2) / m at m = 12,800."""
+    d = 128
+    per_batch, batches = 100, 200
+    rng = np.random.default_rng(100 + pair)
+    c32, t32 = codebook_fp32(d, 3)
+    x = rng.standard_normal(d) * (1.0 + 4.0 * pair)
+    x[rng.choice(d, 2 + pair, replace=False)] *= 20.0
+    q = rng.standard_normal(d)
+    if pair == 2:  # a query nearly aligned with the key
+        q = 0.2 * q + x / np.linalg.norm(x) * 8.0
+    est = np.empty(batches)
+    for i in range(batches):
+        S = rng.standard_normal((d * per_batch, d), dtype=np.float32)
+        enc = encode_k(x[None], c32, t32, S)
+        kt = dequant_k(enc["codes"], enc["signs"], enc["norm_f16"], enc["gamma_f16"], c32, S)
+        est[i] = kt[0] @ q
+    exact = float(x @ q)
+    n = float(enc["norm_f16"][0])
+    r = enc["residual"][0]
+    se = est.std(ddof=1) / math.sqrt(batches)
+    # the half-precision norm moves the mean by at most 2^-11 relative
+    assert abs(est.mean() - exact) < 4 * se + abs(exact) * 2.0 ** -11, (est.mean(), exact, se)
+    m = d * per_batch
+    var_theory = n * n * ((math.pi / 2) * (q @ q) * (r @ r) - (q @ r) ** 2) / m
+    rel = est.var(ddof=1) / var_theory
+    # sample variance of 200 batch means: within 4 sd (sqrt(2/199) = 10 %)
+    assert 0.6 < rel < 1.4, rel
