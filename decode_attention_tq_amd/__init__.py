@@ -131,6 +131,29 @@ def _stream(stream, device=None):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _check_pools(k_cache, v_cache, num_kv_heads: int) -> None:
+    """The C ABI takes the pools as bare pointers with no size: their shape is
+    checked here, so that a pool built for another head count or page size
+    is rejected before any kernel reads or writes it."""
+    torch = _torch()
+    for name, pool, page in (("k_cache", k_cache, K_PAGE_BYTES), ("v_cache", v_cache, V_PAGE_BYTES)):
+        if not isinstance(pool, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if pool.dtype != torch.uint8 or not pool.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 tensor")
+        if pool.dim() != 3 or pool.shape[1] != num_kv_heads or pool.shape[2] != page:
+            raise ValueError(f"{name} must be [num_blocks][{num_kv_heads}][{page}], got {tuple(pool.shape)}")
+    if k_cache.shape[0] != v_cache.shape[0]:
+        raise ValueError("k_cache and v_cache must hold the same number of blocks")
+
+
+def _check_seq_tables(block_tables, context_lens, num_seqs: int) -> None:
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError(f"block_tables must be [{num_seqs}][max_blocks]")
+    if context_lens.dim() != 1 or context_lens.shape[0] != num_seqs:
+        raise ValueError(f"context_lens must have one entry per sequence ({num_seqs})")
+
+
 # ---- host-only helpers ------------------------------------------------------
 
 def tq_codebook_compute(head_dim: int = HEAD_DIM, bits: int = 3):
@@ -212,6 +235,12 @@ def tq_encode_kv(cb: Codebook, k, v, slot_mapping, k_cache, v_cache, norms_out=N
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be contiguous int64")
     T, H = k.shape[0], k.shape[1]
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != T:
+        raise ValueError(f"slot_mapping must have one entry per token ({T})")
+    _check_pools(k_cache, v_cache, H)
+    if norms_out is not None and (norms_out.dtype != torch.float32 or not norms_out.is_contiguous()
+                                  or tuple(norms_out.shape) != (T, H, 3)):
+        raise ValueError(f"norms_out must be a contiguous float32 [{T}][{H}][3] tensor")
     _check(_lib.tq_encode_kv(cb.ref, _ptr(k), _ptr(v), _dtype_code(k), T, H, k.stride(0),
                              k.stride(1), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
                              _ptr(norms_out), _stream(stream, k.device)))
@@ -240,6 +269,8 @@ def tq_decode_attention(cb: Codebook, q, k_cache, v_cache, block_tables, context
     if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous int32")
     B, q_len, Hq, _ = q.shape
+    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_seq_tables(block_tables, context_lens, B)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
     if not out.is_contiguous() or out.shape != q.shape:
@@ -280,6 +311,10 @@ def tq_decode_attention_hot(cb: Codebook, q, k_cache, v_cache, block_tables, con
     if hot_lens.dtype != torch.int32 or not hot_lens.is_contiguous():
         raise ValueError("hot_lens must be contiguous int32")
     B, _, Hq, _ = q.shape
+    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_seq_tables(block_tables, context_lens, B)
+    if hot_lens.dim() != 1 or hot_lens.shape[0] != B:
+        raise ValueError(f"hot_lens must have one entry per sequence ({B})")
     if (hot_k.dim() != 4 or hot_k.shape[0] != B or hot_k.shape[2] != num_kv_heads
             or hot_k.shape[3] != HEAD_DIM or not hot_k.is_contiguous()):
         raise ValueError("hot_k must be a contiguous [B][hot_max][Hkv][128] tensor")

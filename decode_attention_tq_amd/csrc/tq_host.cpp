@@ -134,8 +134,10 @@ void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_c
     st = (int)per;
   }
   // the matrix-core decode pass keeps a chunk's block ids in LDS: at most
-  // 64 tiles of 128 tokens per workgroup
-  if (tq::decode_uses_mfma(q_len, group) && st > 8192) st = 8192;
+  // kMaxMfmaSplitTokens per workgroup (the automatic choice stays below; a
+  // caller's larger request is rejected by decode_impl)
+  if (requested <= 0 && tq::decode_uses_mfma(q_len, group) && st > tq::kMaxMfmaSplitTokens)
+    st = tq::kMaxMfmaSplitTokens;
   int ns = max_ctx > 0 ? (max_ctx + st - 1) / st : 1;
   *split_tokens = st;
   *num_splits = ns;
@@ -401,6 +403,9 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
                 max_blocks_per_seq, max_context_len);
   if (tokens_per_split < 0 || (tokens_per_split > 0 && tokens_per_split % 256 != 0))
     return fail(TQ_ERR_INVALID_ARGUMENT, "tokens_per_split must be 0 or a positive multiple of 256");
+  if (tokens_per_split > tq::kMaxMfmaSplitTokens && tq::decode_uses_mfma(q_len, group))
+    return fail(TQ_ERR_UNSUPPORTED, "tokens_per_split %d exceeds the %d tokens per chunk of this pass",
+                tokens_per_split, tq::kMaxMfmaSplitTokens);
   if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
     return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
   if ((int64_t)num_seqs * q_len > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_seqs * q_len too large");

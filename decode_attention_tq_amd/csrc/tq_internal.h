@@ -94,7 +94,9 @@ struct DecodeArgs {
   Codebook cb;
 };
 
-constexpr int kHotChunk = 256;  // exact window tokens per partial record
+constexpr int kHotChunk = 256;
+// Largest chunk of the matrix-core decode pass (64 tiles of 128 tokens).
+constexpr int kMaxMfmaSplitTokens = 8192;  // exact window tokens per partial record
 
 // Workspace split of tq_decode_attention.
 size_t decode_qprep_floats(int64_t rows);

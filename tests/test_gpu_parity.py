@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import (OUT_RTOL, check_decode, check_encoded_sequence, codebook, decode_gpu, dev,
-                         encode_gpu, new_pools, oracle_tables, rel_rows)
+from gpu_helpers import (OUT_RTOL, assert_rows_close, check_decode, check_encoded_sequence, codebook,
+                         decode_gpu, dev, encode_gpu, new_pools, oracle_tables, rel_rows)
 from oracle import decode_paged_hot
 import decode_attention_tq_amd as tq
 
@@ -361,8 +361,7 @@ def test_hot_window(Hq, Hkv, hot_dtype):
     c32, _, S = oracle_tables()
     ref = decode_paged_hot(np.asarray(q, np.float64), _np(kpool), _np(vpool), table, lens, hk.double().numpy(),
                            hv.double().numpy(), hot, c32, S)
-    err = rel_rows(out, ref)
-    assert err.max() <= OUT_RTOL, f"max row rel err {err.max():.3e}"
+    assert_rows_close(out, ref)
     assert np.all(out[4] == 0)  # no key at all
 
 
@@ -407,8 +406,8 @@ def test_hot_window_bench_size_sampled():
     ref = decode_paged_hot(np.asarray(case["q"], np.float64), _np(kpool), _np(vpool), case["table"],
                            case["context_lens"], hk.double().numpy(), hv.double().numpy(), hl, c32, S,
                            kv_heads=[0, 5])
-    err = rel_rows(out, ref)
-    assert err.size == 8 and err.max() <= OUT_RTOL, f"max row rel err {err.max():.3e}"
+    err = assert_rows_close(out, ref)
+    assert err.size == 8
 
 
 @pytest.mark.parametrize("q_len", [2, 8])
@@ -424,3 +423,19 @@ def test_multi_token_verify_bench_size_sampled(q_len):
     err = check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"], case["context_lens"],
                        kv_heads=[2, 7])
     assert err.size == 2 * 4 * q_len
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 4), (32, 8)])
+def test_largest_chunk_of_the_matrix_core_pass(Hq, Hkv):
+    """A caller's tokens_per_split of 8,192 (64 tiles of 128 tokens, the
+    largest chunk the pass keeps block ids for) followed by a ragged second
+    chunk; 8 and 4 query heads per KV head, checked on two sampled KV heads."""
+    T = 8192 + 700
+    case = synth.gqa_case(seed=30 + Hkv, T=T, Hq=Hq, Hkv=Hkv)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], Hkv)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    out = decode_gpu(cb, case["q"], kpool, vpool, case["table"], case["context_lens"], Hkv,
+                     tokens_per_split=8192)
+    check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"], case["context_lens"],
+                 kv_heads=[0, Hkv - 1])

@@ -200,3 +200,58 @@ def test_hot_window_validation():
     assert tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, 0, 0) == plain
     assert need == plain + 32 * 2 * 132 * 4
     assert tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, -1, 0) == 0
+
+
+def test_oversized_chunk_is_rejected_not_clamped():
+    # the matrix-core decode pass takes at most 8,192 tokens per chunk; an
+    # explicit larger request is an error (the automatic plan stays below)
+    cb = _fake_cb()
+    assert _dec(cb, maxc=32768, mb=2048, tps=8192 + 256) == tq.TQ_ERR_UNSUPPORTED
+    assert "exceeds" in tq.tq_last_error()
+    # (an accepted 8,192-token request would launch: that case runs in the GPU tests)
+    ref = ctypes.byref(cb)
+    # automatic plan for many (sequence, KV head) pairs: chunks of at most 8,192 tokens
+    ws = tq._lib.tq_decode_workspace_bytes(ref, 128, 1, 32, 8, 131072, 0)
+    assert ws // 4 == 128 * 32 * 16 * 132
+
+
+def test_binding_rejects_mismatched_pools_before_any_launch():
+    # the pools reach the C ABI as bare pointers, so the binding checks their
+    # dtype, layout and page sizes; these all fail before any device call
+    import torch
+    cb = tq.Codebook(_fake_cb(), None)
+    q = torch.zeros((1, 1, 32, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    cl = torch.zeros(1, dtype=torch.int32)
+    good_k = torch.zeros((4, 8, 1088), dtype=torch.uint8)
+    good_v = torch.zeros((4, 8, 800), dtype=torch.uint8)
+    bad = [
+        (torch.zeros((4, 4, 1088), dtype=torch.uint8), good_v, "k_cache"),    # other head count
+        (good_k, torch.zeros((4, 8, 1088), dtype=torch.uint8), "v_cache"),    # K page size for V
+        (good_k.to(torch.int16), good_v, "uint8"),
+        (good_k, good_v[:, :, :400], "v_cache"),
+        (good_k, torch.zeros((5, 8, 800), dtype=torch.uint8), "same number"),
+        (good_k.transpose(0, 1), good_v, "contiguous"),
+    ]
+    for kc, vc, msg in bad:
+        with pytest.raises((ValueError, TypeError), match=msg):
+            tq.tq_decode_attention(cb, q, kc, vc, bt, cl, 64, 8)
+    with pytest.raises(ValueError, match="block_tables"):
+        tq.tq_decode_attention(cb, q, good_k, good_v, torch.zeros((2, 4), dtype=torch.int32), cl, 64, 8)
+    with pytest.raises(ValueError, match="context_lens"):
+        tq.tq_decode_attention(cb, q, good_k, good_v, bt, torch.zeros(3, dtype=torch.int32), 64, 8)
+    hk = torch.zeros((1, 16, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="hot_lens"):
+        tq.tq_decode_attention_hot(cb, q, good_k, good_v, bt, cl, 64, 8, hk, hk,
+                                   torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="k_cache"):
+        tq.tq_decode_attention_hot(cb, q, good_k[:, :4].contiguous(), good_v, bt, cl, 64, 8, hk, hk,
+                                   torch.zeros(1, dtype=torch.int32))
+    k = torch.zeros((16, 8, 128), dtype=torch.bfloat16)
+    slots = torch.zeros(16, dtype=torch.int64)
+    with pytest.raises(ValueError, match="k_cache"):
+        tq.tq_encode_kv(cb, k, k, slots, torch.zeros((4, 2, 1088), dtype=torch.uint8), good_v)
+    with pytest.raises(ValueError, match="slot_mapping"):
+        tq.tq_encode_kv(cb, k, k, slots[:8], good_k, good_v)
+    with pytest.raises(ValueError, match="norms_out"):
+        tq.tq_encode_kv(cb, k, k, slots, good_k, good_v, norms_out=torch.zeros((16, 8, 2)))
