@@ -22,7 +22,9 @@
 //        logits of large-norm keys need;
 //   O^T += V^T W^T  with W = p n^V as the B operand straight from the score
 //        registers (lane l holds one query row, so no transpose is needed):
-//        two passes (V_hi, V_lo).
+//        three passes (V_hi W_hi + V_lo W_hi + V_hi W_lo).  A single f16 W
+//        (2^-11 relative) left errors near 3e-3 of a row's largest output
+//        where a dominant value's outlier channels cancel in the output.
 // The running maximum is exact (W <= n^V fits f16); the partial record
 // (m in log2 units, l, acc[128]) goes to the merge pass, which applies the
 // inverse WHT.
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
       kgv[ct][0] = kg4.x; kgv[ct][1] = kg4.y; kgv[ct][2] = kg4.z; kgv[ct][3] = kg4.w;
       vnv[ct][0] = vn4.x; vnv[ct][1] = vn4.y; vnv[ct][2] = vn4.z; vnv[ct][3] = vn4.w;
     }
-    v8h wb[kRowTiles];
+    v8h wb[kRowTiles], wbl[kRowTiles];
 #pragma unroll
     for (int u = 0; u < kRowTiles; ++u) {
       float sc[2][4];
@@ -362,7 +364,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
           const float p = vis[ct][i] ? __builtin_amdgcn_exp2f(sc[ct][i] - m_new) : 0.0f;
           l_part[u] += p;
           // the norm of a masked key may hold any bits: its weight is selected to 0
-          wb[u][4 * ct + i] = (_Float16)(vis[ct][i] ? p * vnv[ct][i] : 0.0f);
+          const float w = vis[ct][i] ? p * vnv[ct][i] : 0.0f;
+          const _Float16 wh = (_Float16)w;
+          wb[u][4 * ct + i] = wh;
+          wbl[u][4 * ct + i] = (_Float16)(w - (float)wh);
         }
       }
     }
@@ -376,6 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
       for (int u = 0; u < kRowTiles; ++u) {
         acc[u][cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, wb[u], acc[u][cv], 0, 0, 0);
         acc[u][cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, wb[u], acc[u][cv], 0, 0, 0);
+        acc[u][cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, wbl[u], acc[u][cv], 0, 0, 0);
       }
     }
   }
