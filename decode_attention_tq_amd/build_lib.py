@@ -1,6 +1,8 @@
 """Build libtq.so in-tree with hipcc for gfx950.
 
-    python -m decode_attention_tq_amd.build_lib [-v]
+    python decode_attention_tq_amd/build_lib.py [-v]
+
+(run as a file: importing the package would load the library being rebuilt)
 
 Every HIP source is compiled for gfx950 only, with packed-FP32 VALU
 instructions disabled (-Xclang -target-feature -Xclang -packed-fp32-ops),
