@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libtq.so not found at {LIB_PATH}; build it with "
-        "`python -m decode_attention_tq_amd.build_lib` (hipcc, gfx950)")
+        "`python decode_attention_tq_amd/build_lib.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -44,7 +44,7 @@ EXPORTED = [
     "tq_codebook_compute", "tq_qjl_matrix", "tq_codebook_device_bytes", "tq_codebook_init",
     "tq_k_page_bytes", "tq_v_page_bytes", "tq_encode_kv", "tq_decode_workspace_bytes",
     "tq_decode_attention", "tq_decode_hot_workspace_bytes", "tq_decode_attention_hot",
-    "tq_last_error",
+    "tq_decode_noalloc_scratch_bytes", "tq_decode_attention_noalloc", "tq_last_error",
 ]
 
 
@@ -84,6 +84,11 @@ _lib.tq_decode_workspace_bytes.argtypes = [_CB, _I, _I, _I, _I, _I, _I]
 _lib.tq_decode_attention.restype = _I
 _lib.tq_decode_attention.argtypes = [_CB, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                      ctypes.c_float, _P, _I, _I, _P, _SZ, _P]
+_lib.tq_decode_noalloc_scratch_bytes.restype = _SZ
+_lib.tq_decode_noalloc_scratch_bytes.argtypes = []
+_lib.tq_decode_attention_noalloc.restype = _I
+_lib.tq_decode_attention_noalloc.argtypes = [_CB, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
+                                             ctypes.c_float, _P, _I, _I, _P]
 _lib.tq_decode_hot_workspace_bytes.restype = _SZ
 _lib.tq_decode_hot_workspace_bytes.argtypes = [_CB, _I, _I, _I, _I, _I, _I]
 _lib.tq_decode_attention_hot.restype = _I
@@ -284,6 +289,36 @@ def tq_decode_attention(cb: Codebook, q, k_cache, v_cache, block_tables, context
         block_tables.shape[1], _ptr(context_lens), B, q_len, Hq, num_kv_heads,
         max_context_len, float(softmax_scale), _ptr(out), _dtype_code(out), tokens_per_split,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    return out
+
+
+def tq_decode_noalloc_scratch_bytes() -> int:
+    return int(_lib.tq_decode_noalloc_scratch_bytes())
+
+
+def tq_decode_attention_noalloc(cb: Codebook, q, k_cache, v_cache, block_tables, context_lens,
+                                max_context_len: int, num_kv_heads: int, out,
+                                softmax_scale: float = 0.0, tokens_per_split: int = 0, stream=None):
+    """tq_decode_attention without a workspace: the library's device scratch
+    holds the partial records, and ``out`` (allocated by the caller) is
+    filled.  Allocates nothing."""
+    torch = _torch()
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][q_len][Hq][128] tensor")
+    if block_tables.dtype != torch.int32 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32")
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32")
+    B, q_len, Hq, _ = q.shape
+    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_seq_tables(block_tables, context_lens, B)
+    if out is None or not out.is_contiguous() or out.shape != q.shape:
+        raise ValueError("out must be a contiguous tensor with q's shape")
+    _check(_lib.tq_decode_attention_noalloc(
+        cb.ref, _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, q_len, Hq, num_kv_heads,
+        max_context_len, float(softmax_scale), _ptr(out), _dtype_code(out), tokens_per_split,
+        _stream(stream, q.device)))
     return out
 
 

@@ -19,6 +19,7 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "tq_mfma.hpp"
@@ -1758,6 +1759,37 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ---- device scratch of the no-allocation decode call ------------------------
+// In host code `scratch` names a host-side stand-in, never the device array:
+// its device address comes only from hipGetSymbolAddress, once per device
+// with that device current, and every launch takes that address.  Calls of
+// tq_decode_attention_noalloc on one device share the array: overlapping
+// calls (several streams, several threads) race.  Nothing in it needs to
+// start at zero: the split passes write every partial record the merge reads.
+namespace {
+__device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  if (ptr) *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.q_len * a.num_q_heads;

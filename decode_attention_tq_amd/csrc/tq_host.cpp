@@ -290,6 +290,10 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(tables)");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  // the no-allocation decode call's scratch address on this device, resolved
+  // here at set-up so that the call itself never loads or allocates anything
+  e = tq::noalloc_scratch(nullptr);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
   c.d_tables = d_tables;
   c.magic = tq::kMagic;
   *cb = c;
@@ -380,10 +384,10 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
                       int num_q_heads, int num_kv_heads, int max_context_len,
                       float softmax_scale, void *out, tq_dtype out_dtype,
                       int tokens_per_split, void *workspace, size_t workspace_bytes,
-                      void *stream, const HotWindow *hot) {
+                      void *stream, const HotWindow *hot, bool noalloc = false) {
   tq_status st = check_cb(cb);
   if (st != TQ_OK) return st;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || (!workspace && !noalloc))
     return fail(TQ_ERR_INVALID_ARGUMENT, "null device pointer");
   if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return fail(TQ_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1)
@@ -429,6 +433,18 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   }
   const size_t need = decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
                                        tokens_per_split, hot_parts);
+  if (noalloc) {
+    // every check above is on the host; the scratch array's address is
+    // resolved (once per device) only for a call that will launch
+    if (need > tq::kNoAllocScratchBytes)
+      return fail(TQ_ERR_WORKSPACE_TOO_SMALL,
+                  "the call needs %zu bytes of partial records, more than the %zu-byte device scratch of "
+                  "tq_decode_attention_noalloc; use tq_decode_attention with a workspace",
+                  need, (size_t)tq::kNoAllocScratchBytes);
+    hipError_t e = tq::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    workspace_bytes = tq::kNoAllocScratchBytes;
+  }
   if (workspace_bytes < need)
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   tq::DecodeArgs a;
@@ -499,6 +515,20 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
                      num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, softmax_scale, out,
                      out_dtype, tokens_per_split, workspace, workspace_bytes, stream, nullptr);
 }
+
+tq_status tq_decode_attention_noalloc(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                                      const uint8_t *k_cache, const uint8_t *v_cache,
+                                      const int32_t *block_tables, int max_blocks_per_seq,
+                                      const int32_t *context_lens, int num_seqs, int q_len,
+                                      int num_q_heads, int num_kv_heads, int max_context_len,
+                                      float softmax_scale, void *out, tq_dtype out_dtype,
+                                      int tokens_per_split, void *stream) {
+  return decode_impl(cb, q, q_dtype, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, softmax_scale, out,
+                     out_dtype, tokens_per_split, nullptr, 0, stream, nullptr, true);
+}
+
+size_t tq_decode_noalloc_scratch_bytes(void) { return tq::kNoAllocScratchBytes; }
 
 size_t tq_decode_hot_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads,
                                      int num_kv_heads, int max_context_len, int hot_max,

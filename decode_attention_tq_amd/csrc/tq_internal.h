@@ -115,6 +115,14 @@ bool prefill_uses_mfma(int q_len, int group);
 int prefill_block_queries(int group);
 int decode_qk_tiles(int rows);
 
+// Device scratch of tq_decode_attention_noalloc: a file-scope __device__
+// array (one copy per device, held until the process ends).  noalloc_scratch
+// returns its address on the current device, resolved with
+// hipGetSymbolAddress on the first request per device and kept; ptr may be
+// null to resolve only.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);

@@ -186,6 +186,31 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
                               int tokens_per_split, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* ---- attention without a caller workspace ----------------------------------
+ * For callers that cannot allocate device memory around the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results as tq_decode_attention, minus the
+ * workspace: its partial records go to a device scratch array inside the
+ * library (one per device, tq_decode_noalloc_scratch_bytes() = 16 MiB, held
+ * until the process ends; its address on a device is resolved by
+ * tq_codebook_init on the current device, or by the first call on another).
+ * The call allocates and frees nothing.  All calls on one device share that
+ * array: calls that overlap on a device (several streams or threads) race
+ * and must be serialised by the caller.
+ * Errors: those of tq_decode_attention; TQ_ERR_WORKSPACE_TOO_SMALL when the
+ * call's partial records (tq_decode_workspace_bytes() for the same
+ * arguments) exceed the scratch size; TQ_ERR_HIP if the scratch address
+ * cannot be resolved. */
+size_t tq_decode_noalloc_scratch_bytes(void);
+
+tq_status tq_decode_attention_noalloc(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                                      const uint8_t *k_cache, const uint8_t *v_cache,
+                                      const int32_t *block_tables, int max_blocks_per_seq,
+                                      const int32_t *context_lens, int num_seqs, int q_len,
+                                      int num_q_heads, int num_kv_heads, int max_context_len,
+                                      float softmax_scale, void *out, tq_dtype out_dtype,
+                                      int tokens_per_split, void *stream);
+
 /* ---- attention with an exact hot window -----------------------------------
  * The SwiftLM README keeps the recent tokens uncompressed and compresses only
  * past a threshold (its --turbo-kv option row: after 2,048 tokens), and

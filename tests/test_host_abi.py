@@ -255,3 +255,30 @@ def test_binding_rejects_mismatched_pools_before_any_launch():
         tq.tq_encode_kv(cb, k, k, slots[:8], good_k, good_v)
     with pytest.raises(ValueError, match="norms_out"):
         tq.tq_encode_kv(cb, k, k, slots, good_k, good_v, norms_out=torch.zeros((16, 8, 2)))
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_call():
+    cb = _fake_cb()
+    ref = ctypes.byref(cb)
+    cap = tq.tq_decode_noalloc_scratch_bytes()
+    assert cap == 16 << 20
+
+    def call(**kw):
+        a = dict(B=1, q_len=1, Hq=32, Hkv=8, maxc=1024, mb=64)
+        a.update(kw)
+        return tq._lib.tq_decode_attention_noalloc(
+            ref, FAKE, tq.TQ_BF16, FAKE, FAKE, FAKE, a["mb"], FAKE, a["B"], a["q_len"], a["Hq"],
+            a["Hkv"], a["maxc"], 0.0, FAKE, tq.TQ_F32, 0, None)
+    # 64 sequences x 32 heads over 131,072 tokens: 16 chunks of partial records per row
+    need = tq._lib.tq_decode_workspace_bytes(ref, 64, 1, 32, 8, 131072, 0)
+    assert need > cap
+    assert call(B=64, maxc=131072, mb=8192) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+    assert "scratch" in tq.tq_last_error()
+    # the plain call's argument checks come first
+    assert call(Hq=30) == tq.TQ_ERR_INVALID_ARGUMENT
+    assert tq._lib.tq_decode_attention_noalloc(
+        ctypes.byref(_fake_cb(False)), FAKE, tq.TQ_BF16, FAKE, FAKE, FAKE, 64, FAKE, 1, 1, 32, 8, 1024,
+        0.0, FAKE, tq.TQ_F32, 0, None) == tq.TQ_ERR_NOT_INITIALIZED
+    assert tq._lib.tq_decode_attention_noalloc(
+        ref, None, tq.TQ_BF16, FAKE, FAKE, FAKE, 64, FAKE, 1, 1, 32, 8, 1024,
+        0.0, FAKE, tq.TQ_F32, 0, None) == tq.TQ_ERR_INVALID_ARGUMENT
