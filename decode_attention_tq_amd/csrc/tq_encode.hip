@@ -153,7 +153,7 @@ struct RoundLds {
   uint8_t vimg[kTiles][kVPage];                 // V page images
   _Float16 ehi[kTiles][kTok][kEHalves];         // residual * 256 (hi), slot order
   _Float16 elo[kTiles][kTok][kEHalves];         // remainder (lo)
-  int blk[kTiles][kTok], off[kTiles][kTok], valid[kTiles][kTok], leader[kTiles][kTok];
+  int blk[kTiles][kTok], off[kTiles][kTok], valid[kTiles][kTok];
   float nout[kTiles][kTok][3];                  // n_K, gamma, n_V in fp32 (optional output)
   int full[kTiles];
   int active[kTiles];
@@ -350,14 +350,6 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
       L.active[wave] = active;
       L.full[wave] = full;
     }
-    if (!full) {
-      // pages filled token by token: the first token of each destination block
-      int dup = 0;
-#pragma unroll
-      for (int u = 0; u < kTok - 1; ++u) dup |= (u < l16) & (__builtin_amdgcn_readlane(blk, u) == blk);
-      if (lane < kTok) L.leader[wave][lane] = ok && !dup;
-    }
-
 
     if (active) {
       // ---- values: C = H X^T, lane l reg i = coordinate 16m + 4(l/16) + i, token l%16
@@ -548,27 +540,27 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
             *reinterpret_cast<uint16_t *>(vp + kVNorm + 2 * o) = *reinterpret_cast<const uint16_t *>(L.vimg[tl] + kVNorm + 2 * n);
           }
         }
-        for (int w = tid; w < 3 * kHeadDim; w += 256) {
-          const int p = w / kHeadDim, c = w % kHeadDim;
-          const uint32_t word = reinterpret_cast<const uint16_t *>(L.vimg[tl] + kKPlane * p)[c];
-          for (int j = 0; j < kTok; ++j) {
-            if (!L.leader[tl][j]) continue;
-            uint32_t mask = 0, bits = 0;
-            for (int u = j; u < kTok; ++u) {
-              if (L.valid[tl][u] && L.blk[tl][u] == L.blk[tl][j]) {
-                mask |= 1u << L.off[tl][u];
-                bits |= ((word >> u) & 1u) << L.off[tl][u];
-              }
-            }
-            uint8_t *vp = v_cache + ((int64_t)L.blk[tl][j] * H + hh) * kVPage;
-            const uintptr_t addr = reinterpret_cast<uintptr_t>(vp + kKPlane * p + 2 * c);
-            // a global (not flat) atomic: a pending flat operation would make every
-            // later wait on the memory counters wait for all of them
-            gword *w32 = reinterpret_cast<gword *>(addr & ~uintptr_t(3));
-            const int sh = (addr & 2) ? 16 : 0;
-            const uint32_t set = bits << sh, clr = (mask & ~bits) << sh;
-            if (clr) __hip_atomic_fetch_and(w32, ~clr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (set) __hip_atomic_fetch_or(w32, set, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // value bits, one token at a time: wave w merges tokens w, w + 4, ..
+        // of the tile; lane l owns the 32-bit word of coordinates 2l, 2l + 1
+        // of each plane (16-bit words, token o of the page at bit o), so a
+        // token is two coalesced 256-byte atomics per plane.  Tokens that share
+        // a page touch different bits of the same words: the atomics keep them
+        // apart, in this call and across the waves of the grid.
+        for (int n = wave; n < kTok; n += 4) {  // uniform
+          if (!__builtin_amdgcn_readfirstlane((int)L.valid[tl][n])) continue;  // uniform
+          const int bn = __builtin_amdgcn_readfirstlane(L.blk[tl][n]);
+          const int o = __builtin_amdgcn_readfirstlane(L.off[tl][n]);
+          uint8_t *vp = v_cache + ((int64_t)bn * H + hh) * kVPage;
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            const uint32_t w2 = reinterpret_cast<const uint32_t *>(L.vimg[tl] + kKPlane * p)[lane];
+            const uint32_t b = ((w2 >> n) & 1u) | (((w2 >> (16 + n)) & 1u) << 16);
+            const uint32_t set = b << o, clr = (0x10001u << o) & ~set;
+            // global (not flat) atomics: a pending flat operation would make
+            // every later wait on the memory counters wait for all of them
+            gword *w32 = reinterpret_cast<gword *>(reinterpret_cast<uintptr_t>(vp + kKPlane * p + 4 * lane));
+            __hip_atomic_fetch_and(w32, ~clr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(w32, set, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
         // the stores in the loops above leave an unbounded count of memory
