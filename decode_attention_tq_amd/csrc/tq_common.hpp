@@ -23,8 +23,7 @@ __device__ __forceinline__ void lds_barrier() {
 // is cut to what the block table row and the split plan cover, so that no
 // access leaves the block table or the partials.
 __device__ __forceinline__ int clamped_context(const DecodeArgs &a, int b) {
-  const int cap = min(a.max_blocks * kBlock, a.num_splits * a.split_tokens);
-  return min(max(a.context_lens[b], 0), cap);
+  return min(max(a.context_lens[b], 0), a.ctx_cap);
 }
 
 __device__ __forceinline__ float load_as_float(const void *p, int dtype, int64_t i) {

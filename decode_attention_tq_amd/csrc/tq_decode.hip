@@ -30,6 +30,106 @@ namespace {
 constexpr int kPartStride = 132;  // m (log2 units), l, pad, pad, acc[128]
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---- balanced plan of the matrix-core decode pass ----------------------------
+// Sequence s has T_s = ceil(L_s / 128) tiles; each of its Hkv groups is cut
+// into k_s = ceil(T_s / per) ranges of per tiles, one workgroup each, and the
+// ranges are numbered densely, sequence-major then head-major.  per is the
+// smallest value in [bal_min, 64] whose ranges number at most bal_target
+// (the count that fills the compute units once), or 64; a caller's fixed
+// bal_per overrides it.  Every wave of a workgroup (and of the merge and
+// window passes) computes the same values from the context lengths, 64
+// sequences at a time.
+// Inclusive prefix sum over the wave: scans inside each 16-lane row (DPP
+// row_shr 1, 2, 4, 8; out-of-row sources read 0), then row_bcast:15 and
+// row_bcast:31 carry the row totals up.
+__device__ __forceinline__ int wave_incl_scan_int(int x, int lane) {
+  (void)lane;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+// ceil(T / p) for 0 <= T < 2^24 and 1 <= p <= 64, from a float estimate of
+// the quotient (within 2 of the true one) corrected in two steps either way.
+__device__ __forceinline__ int ceil_div_small(int T, int p, float rp) {
+  int q = (int)((float)T * rp);
+  int r = T - q * p;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (r < 0) { --q; r += p; }
+    if (r >= p) { ++q; r -= p; }
+  }
+  return q + (r > 0 ? 1 : 0);
+}
+__device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int s) {
+  return s < a.num_seqs ? (clamped_context(a, s) + 127) >> 7 : 0;
+}
+// The tile counts of sequences c0 + lane: for up to 64 sequences they are
+// read once (t0, loaded by the caller at its start) and every later step
+// works in registers; larger batches read them again per block of 64.
+__device__ __forceinline__ int block_tiles(const DecodeArgs &a, int t0, int c0, int lane) {
+  return a.num_seqs <= 64 ? t0 : seq_tiles(a, c0 + lane);
+}
+// Ranges of all groups for a range length of p tiles.
+__device__ __forceinline__ int bal_ranges(const DecodeArgs &a, int t0, int p) {
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64)  // uniform
+    tot += __builtin_amdgcn_readlane(wave_incl_scan_int((block_tiles(a, t0, c0, lane) + p - 1) / p, lane), 63);
+  return tot * a.num_kv_heads;
+}
+__device__ __forceinline__ int bal_per(const DecodeArgs &a, int t0) {
+  if (a.bal_per > 0) return a.bal_per;
+  if (a.num_seqs <= 64) {
+    // lane l tries p = l + 2 (lanes 0..62 cover 2..64): its ranges over all
+    // groups; the smallest p that fits wins
+    const int lane = threadIdx.x & 63;
+    const int p = min(lane + 2, 64);
+    const float rp = 1.0f / (float)p;
+    int tot = 0;
+    for (int b = 0; b < a.num_seqs; ++b)  // uniform
+      tot += ceil_div_small(__builtin_amdgcn_readlane(t0, b), p, rp);
+    const uint64_t fit = __ballot(p >= a.bal_min && tot * a.num_kv_heads <= a.bal_target);
+    return fit ? __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)fit) - 1) + 2 : 64;
+  }
+  int lo = a.bal_min, hi = 64;
+  while (lo < hi) {  // uniform
+    const int mid = (lo + hi) >> 1;
+    if (bal_ranges(a, t0, mid) <= a.bal_target) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+// Workgroup w's range: sequence b, KV head h, range index j of the group
+// and the group's tile count; b = num_seqs when w is past the last range.
+__device__ __forceinline__ void bal_locate(const DecodeArgs &a, int t0, int per, int w, int &b, int &h, int &j,
+                                           int &Tb) {
+  const int lane = threadIdx.x & 63, H = a.num_kv_heads;
+  int base = 0;
+  b = a.num_seqs;
+  h = j = Tb = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
+    const int T = block_tiles(a, t0, c0, lane);
+    const int k = (T + per - 1) / per;
+    const int incl = wave_incl_scan_int(H * k, lane);
+    const int ctot = __builtin_amdgcn_readlane(incl, 63);
+    if (w < base + ctot) {  // uniform: w lies in this block of sequences
+      // sequences whose ranges end at or before w (empty ones included) come first
+      const int i = __builtin_amdgcn_readfirstlane(__popcll(__ballot(base + incl <= w)));
+      b = c0 + i;
+      Tb = __builtin_amdgcn_readlane(T, i);
+      const int kb = __builtin_amdgcn_readlane(k, i);
+      const int off = w - (base + __builtin_amdgcn_readlane(incl, i) - H * kb);
+      h = off / kb;
+      j = off - h * kb;
+      return;
+    }
+    base += ctot;
+  }
+}
+
 // ---- 1. query prep (vector and prefill passes): a workgroup per query row -----
 // Grid (sequence x position x KV head, head of the group).  Thread (i, half)
 // forms half of (S q)_i from S[i][64*half .. +64) held in registers; wave 0
@@ -702,19 +802,11 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
 
 
 template <int T, int R>
-__device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, SplitLds<T> &sm) {
+__device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, SplitLds<T> &sm, int b, int h,
+                                                          int split, int s0, int s1) {
   constexpr int NW = 4 * T;   // waves
   constexpr int NJ = 2 / T;   // value N-tiles (16 coordinates) per wave
-  const int per_seq = a.num_kv_heads * a.num_splits;
-  const int item = blockIdx.x;
-  if (item >= a.num_seqs * per_seq) return;
-  const int b = item / per_seq;
-  const int h = (item / a.num_splits) % a.num_kv_heads;
-  const int split = item % a.num_splits;
   const int L = clamped_context(a, b);
-  const int s0 = split * a.split_tokens;
-  const int s1 = min(s0 + a.split_tokens, L);
-  if (s0 >= s1) return;  // uniform
   // query rows (positions x heads); every row sees the keys before s1v, row
   // r those before min(s1, L - q_len + pos0 + r / G + 1)
   const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count;
@@ -1113,20 +1205,12 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
 // values) and overlap, where identical waves run the same phases in lock
 // step.  Intervals, buffers and records are those of split_body.
 template <int R>
-__device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a, SplitLds<2> &sm) {
+__device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a, SplitLds<2> &sm, int b, int h,
+                                                             int split, int s0, int s1) {
   constexpr int T = 2;
   constexpr int NW = 8;  // waves
   constexpr int NJ = 2;  // value N-tiles (16 coordinates) per value wave
-  const int per_seq = a.num_kv_heads * a.num_splits;
-  const int item = blockIdx.x;
-  if (item >= a.num_seqs * per_seq) return;
-  const int b = item / per_seq;
-  const int h = (item / a.num_splits) % a.num_kv_heads;
-  const int split = item % a.num_splits;
   const int L = clamped_context(a, b);
-  const int s0 = split * a.split_tokens;
-  const int s1 = min(s0 + a.split_tokens, L);
-  if (s0 >= s1) return;  // uniform
   // query rows (positions x heads); every row sees the keys before s1v, row
   // r those before min(s1, L - q_len + pos0 + r / G + 1)
   const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count;
@@ -1468,16 +1552,23 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
   }
 }
 
+// One workgroup per range of the balanced plan.
 template <int T>
 __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) SplitLds<T> sm;
+  const int t0 = seq_tiles(a, threadIdx.x & 63);
+  const int per = bal_per(a, t0);
+  int b, h, j, Tb;
+  bal_locate(a, t0, per, blockIdx.x, b, h, j, Tb);
+  if (b >= a.num_seqs) return;  // uniform: past the last range
+  const int s0 = 128 * per * j, s1 = min(128 * per * (j + 1), clamped_context(a, b));
   if constexpr (T == 1) {
-    split_body<T, 2>(a, sm);
+    split_body<T, 2>(a, sm, b, h, j, s0, s1);
   } else {
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)  // uniform: the wave's role
-      split_body_ws<0>(a, sm);
+      split_body_ws<0>(a, sm, b, h, j, s0, s1);
     else
-      split_body_ws<1>(a, sm);
+      split_body_ws<1>(a, sm, b, h, j, s0, s1);
   }
 }
 
@@ -1623,7 +1714,14 @@ __global__ __launch_bounds__(kHotChunk) void hot_window_kernel(DecodeArgs a) {
   }
   lds_barrier();
   // wave w writes the records of heads w, w + NW, ...
-  const int ns = (clamped_context(a, b) + a.split_tokens - 1) / a.split_tokens;  // the row's compressed chunks
+  // the row's compressed records come first
+  int ns;
+  if (a.balanced) {
+    const int per = bal_per(a, seq_tiles(a, lane));
+    ns = (seq_tiles(a, b) + per - 1) / per;
+  } else {
+    ns = (clamped_context(a, b) + a.split_tokens - 1) / a.split_tokens;
+  }
   for (int g = wave; g < G; g += NW) {  // uniform
     float o0 = 0.0f, o1 = 0.0f, l = 0.0f;
 #pragma unroll
@@ -1675,8 +1773,14 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
     const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
     const int b = (int)(r / per_seq);
     const int t = (int)((r / a.num_q_heads) % a.q_len);
-    const int vis = max(0, clamped_context(a, b) - a.q_len + t + 1);
-    ns = (vis + a.split_tokens - 1) / a.split_tokens + a.hot_parts;  // the window's records follow
+    if (a.balanced) {
+      const int per = bal_per(a, seq_tiles(a, lane));
+      ns = (seq_tiles(a, b) + per - 1) / per;
+    } else {
+      const int vis = max(0, clamped_context(a, b) - a.q_len + t + 1);
+      ns = (vis + a.split_tokens - 1) / a.split_tokens;
+    }
+    ns += a.hot_parts;  // the window's records follow
     part += r * a.part_stride * kPartStride;
   }
   float M = -INFINITY, Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;  // Ls: lanes < 16, per chunk slot
@@ -1799,7 +1903,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.qk_tiles > 0) {  // matrix-core pass, its own query operands: a workgroup per (chunk, KV head)
     // one launch per group of at most 8 query rows (positions x heads)
     const int per = decode_positions_per_launch(a.group);
-    const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_splits;
+    const int64_t items = a.bal_grid;
     for (int p0 = 0; p0 < a.q_len; p0 += per) {
       DecodeArgs la = a;
       la.pos0 = p0;

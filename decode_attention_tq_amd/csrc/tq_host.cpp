@@ -100,47 +100,78 @@ tq::Codebook device_codebook(const tq_codebook *cb) {
 bool dtype_ok(int d) { return d == TQ_F32 || d == TQ_F16 || d == TQ_BF16; }
 
 // ---- split-K planning ------------------------------------------------------
-// Chunks are multiples of 256 tokens.  The automatic choice depends only on
-// the call's sizes (no device query), so the workspace size and the launch
-// always agree, and aims at the 256 compute units of the part: the
-// matrix-core decode pass (at most 8 query rows, positions x heads, per KV
-// head) at one 8-wave workgroup per unit for 5 to 8 rows and two 4-wave
-// workgroups per unit for up to 4 (each workgroup walks its chunk with a
-// fixed start-up cost, so more, shorter chunks only add it), the other
-// passes at about 1024 workgroups.  The prefill pass shares a workgroup per
-// block of query positions; the decode passes take all of a sequence's
-// positions in one.
-void plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested,
-                 int *split_tokens, int *num_splits) {
+// The plan depends only on the call's sizes (no device query), so the
+// workspace size and the launch always agree.
+//
+// Matrix-core decode pass (q_len = 1 or a short verify block, up to 8 query
+// heads per KV head): the balanced plan.  Every (sequence, KV head) group is
+// cut into ranges of `per` 128-token tiles, one workgroup each; per is chosen
+// on the device from the actual context lengths as the smallest value in
+// [2, 64] whose ranges fit in the count that fills the 256 compute units
+// once (one 8-wave workgroup per unit for 5 to 8 query rows, two 4-wave ones
+// for up to 4), so a ragged batch keeps the workgroups about equally busy.
+// Each workgroup pays a fixed start-up (block ids, query operands, the first
+// tiles in flight), so longer ranges are preferred once the units are full;
+// a range holds at most 64 tiles (its block ids are kept in LDS).  The grid
+// covers the ranges at per = 64 for every sequence at max_ctx; workgroups
+// past the last range exit.  Records per row: k = ceil(T / per) <= T / 2,
+// and below 64 tiles Hkv k fits the filling count.
+// Other passes (vector pass, prefill): chunks of split_tokens (multiples of
+// 256) per (sequence or query block, KV head), aiming at about 1024
+// workgroups.
+struct SplitPlan {
+  int split_tokens, num_splits;  // num_splits: partial records per row (compressed part)
+  int balanced, grid, target, per, min_tiles;
+};
+constexpr int kBalMinTiles = 2;
+constexpr int kBalMaxTiles = tq::kMaxMfmaSplitTokens / 128;
+
+SplitPlan plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested) {
+  SplitPlan p{};
+  if (tq::decode_uses_mfma(q_len, group)) {
+    const int mrows = group * std::min(q_len, tq::decode_positions_per_launch(group));
+    const long slots = mrows > 4 ? 256 : 512;
+    const long tmax = (std::max(max_ctx, 0) + 127) / 128;
+    const long groups = (long)num_seqs * num_kv_heads;
+    p.balanced = 1;
+    p.min_tiles = kBalMinTiles;
+    p.target = (int)slots;
+    long recs;
+    if (requested > 0) {
+      p.per = requested / 128;
+      const long k = (tmax + p.per - 1) / p.per;
+      p.grid = (int)std::max(1L, groups * k);
+      recs = k;
+    } else {
+      p.per = 0;
+      const long k64 = (tmax + kBalMaxTiles - 1) / kBalMaxTiles;
+      p.grid = (int)std::max(slots, groups * k64);
+      recs = std::max(std::min((tmax + kBalMinTiles - 1) / kBalMinTiles, slots / num_kv_heads), k64);
+    }
+    p.num_splits = (int)std::max(1L, std::min(recs, tmax));
+    p.split_tokens = 128;
+    return p;
+  }
   int st;
   if (requested > 0) {
     st = requested;
   } else {
     long per_seq = q_len;
-    if (tq::decode_uses_mfma(q_len, group)) {
-      per_seq = 1;
-    } else if (tq::prefill_uses_mfma(q_len, group)) {
+    if (tq::prefill_uses_mfma(q_len, group)) {
       const int bq = tq::prefill_block_queries(group);
       per_seq = (q_len + bq - 1) / bq;
     }
     const long rows = (long)num_seqs * per_seq * num_kv_heads;
-    const int mrows = group * std::min(q_len, tq::decode_positions_per_launch(group > 0 ? group : 1));
-    const long target = tq::decode_uses_mfma(q_len, group) ? (mrows > 4 ? 256 : 512) : 1024;
-    long want = (target + rows - 1) / rows;
+    long want = (1024 + rows - 1) / rows;
     if (want < 1) want = 1;
     long per = (max_ctx + want - 1) / want;
     per = ((per + 255) / 256) * 256;
     if (per < 256) per = 256;
     st = (int)per;
   }
-  // the matrix-core decode pass keeps a chunk's block ids in LDS: at most
-  // kMaxMfmaSplitTokens per workgroup (the automatic choice stays below; a
-  // caller's larger request is rejected by decode_impl)
-  if (requested <= 0 && tq::decode_uses_mfma(q_len, group) && st > tq::kMaxMfmaSplitTokens)
-    st = tq::kMaxMfmaSplitTokens;
-  int ns = max_ctx > 0 ? (max_ctx + st - 1) / st : 1;
-  *split_tokens = st;
-  *num_splits = ns;
+  p.split_tokens = st;
+  p.num_splits = max_ctx > 0 ? (max_ctx + st - 1) / st : 1;
+  return p;
 }
 
 constexpr size_t kPartStride = 132;  // floats per partial record: m, l, pad, pad, acc[128]
@@ -358,9 +389,8 @@ size_t decode_workspace(int num_seqs, int q_len, int num_q_heads, int num_kv_hea
                         int tokens_per_split, int hot_parts) {
   if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0)
     return 0;
-  int stok, ns;
   const int grp = num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
-  plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split, &stok, &ns);
+  const int ns = plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split).num_splits;
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   // the matrix-core split pass forms its query operands itself: partials only
   const bool mfma = grp > 0 && tq::decode_uses_mfma(q_len, grp);
@@ -413,9 +443,11 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
     return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
   if ((int64_t)num_seqs * q_len > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_seqs * q_len too large");
-  int stok, ns;
-  plan_splits(num_seqs, q_len, num_kv_heads, group, max_context_len, tokens_per_split, &stok, &ns);
+  const SplitPlan plan = plan_splits(num_seqs, q_len, num_kv_heads, group, max_context_len, tokens_per_split);
+  const int ns = plan.num_splits;
   if (ns > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many splits (%d); raise tokens_per_split", ns);
+  if ((int64_t)num_seqs * num_kv_heads * ((max_context_len + 127) / 128) > 0x7fffffffLL)
+    return fail(TQ_ERR_UNSUPPORTED, "num_seqs * num_kv_heads * tiles of max_context_len too large");
   int hot_parts = 0;
   if (hot) {
     if (q_len != 1) return fail(TQ_ERR_UNSUPPORTED, "a hot window is supported for q_len == 1 only (got %d)", q_len);
@@ -463,8 +495,15 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)tq::kHeadDim));
   a.out = out;
   a.out_dtype = out_dtype;
-  a.split_tokens = stok;
+  a.split_tokens = plan.split_tokens;
   a.num_splits = ns;
+  a.ctx_cap = plan.balanced ? std::min((int64_t)max_blocks_per_seq * tq::kBlock, (int64_t)max_context_len)
+                            : (int)std::min((int64_t)max_blocks_per_seq * tq::kBlock, (int64_t)ns * plan.split_tokens);
+  a.balanced = plan.balanced;
+  a.bal_grid = plan.grid;
+  a.bal_target = plan.target;
+  a.bal_per = plan.per;
+  a.bal_min = plan.min_tiles;
   a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
   a.SHop = (const uint16_t *)(a.St + (size_t)tq::kQjlDim * tq::kHeadDim);
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;

@@ -70,6 +70,19 @@ struct DecodeArgs {
   int out_dtype;
   int split_tokens;
   int num_splits;
+  // Context lengths are cut to ctx_cap (what the block table row and the
+  // plan of partial records cover).
+  int ctx_cap;
+  // Balanced plan of the matrix-core decode pass (balanced = 1): the tiles
+  // of 128 tokens of every (sequence, KV head) group are cut into ranges of
+  // `per` tiles, one workgroup each, numbered densely sequence-major then
+  // head-major; per = bal_per if > 0, else the smallest value in
+  // [bal_min, 64] whose ranges number at most bal_target (or 64), computed
+  // on the device from the context lengths.  Range j of a group writes the
+  // group's partial record j.  The grid has bal_grid workgroups, enough for
+  // every range.
+  int balanced;
+  int bal_grid, bal_target, bal_per, bal_min;
   const float *St;     // [d][m]
   const uint16_t *SHop;  // S H as f16 hi, lo halves in the projection's operand order
   float *qprep;        // workspace (vector and prefill passes): [rows][256] = rotated q | qjl_scale * S q
@@ -120,7 +133,7 @@ int decode_qk_tiles(int rows);
 // returns its address on the current device, resolved with
 // hipGetSymbolAddress on the first request per device and kept; ptr may be
 // null to resolve only.
-constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 hipError_t noalloc_scratch(void **ptr);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);

@@ -191,7 +191,7 @@ tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_d
  * HIP graph capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments, kernels and results as tq_decode_attention, minus the
  * workspace: its partial records go to a device scratch array inside the
- * library (one per device, tq_decode_noalloc_scratch_bytes() = 16 MiB, held
+ * library (one per device, tq_decode_noalloc_scratch_bytes() = 64 MiB, held
  * until the process ends; its address on a device is resolved by
  * tq_codebook_init on the current device, or by the first call on another).
  * The call allocates and frees nothing.  All calls on one device share that

@@ -150,23 +150,61 @@ def _prep_words(B, q_len, Hq, Hkv):
     return B * q_len * Hq * 256
 
 
+def _balanced_records(lengths, Hkv, per_fixed, target, min_tiles=2):
+    """Records per group under the balanced plan of the matrix-core pass, by
+    brute force: tiles of 128 tokens; each (sequence, KV head) group cut into
+    ranges of per tiles, per fixed or the smallest value in [min_tiles, 64]
+    whose ranges over all groups number at most ``target`` (else 64)."""
+    T = [(int(L) + 127) // 128 for L in lengths]
+
+    def ranges(p):
+        return Hkv * sum(-(-t // p) for t in T)
+    per = per_fixed or next((p for p in range(min_tiles, 65) if ranges(p) <= target), 64)
+    return [-(-t // per) for t in T for _ in range(Hkv)], per
+
+
 @pytest.mark.parametrize("B,q_len,Hq,Hkv", [(1, 1, 32, 8), (2, 1, 32, 4), (1, 1, 32, 32),
-                                            (1, 4, 32, 8), (1, 1, 32, 2), (2, 2, 32, 8)])
-def test_workspace_plan_is_consistent(B, q_len, Hq, Hkv):
+                                            (1, 4, 32, 8), (16, 1, 32, 8), (2, 2, 32, 8)])
+def test_workspace_plan_covers_every_record(B, q_len, Hq, Hkv):
     cb = _fake_cb()
     ref = ctypes.byref(cb)
     rows = B * q_len * Hq
-    # 4 bytes x (prep floats + rows x splits x 132 partial floats)
-    for maxc, tps in ((8192, 256), (8192, 1024), (131072, 0), (0, 0), (1, 0)):
-        ws = tq._lib.tq_decode_workspace_bytes(ref, B, q_len, Hq, Hkv, max(maxc, q_len), tps)
+    G = Hq // Hkv
+    rng = np.random.default_rng(B * 100 + Hkv)
+    for maxc, tps in ((8192, 256), (8192, 1024), (131072, 0), (32768, 0), (0, 0), (1, 0)):
+        maxc = max(maxc, q_len)
+        ws = tq._lib.tq_decode_workspace_bytes(ref, B, q_len, Hq, Hkv, maxc, tps)
         words = ws // 4 - _prep_words(B, q_len, Hq, Hkv)
         assert ws % 4 == 0 and words % (rows * 132) == 0
-        splits = words // (rows * 132)
-        assert splits >= 1
-        if tps:
-            assert splits == max(1, -(-max(maxc, q_len) // tps))
+        recs = words // (rows * 132)
+        assert recs >= 1
+        # the ranges should fill the 256 compute units once: 8-wave
+        # workgroups for 5 to 8 query rows, two 4-wave ones per unit for up to 4
+        mrows = G * min(q_len, 8 // G)
+        target = 256 if mrows > 4 else 512
+        for trial in range(20):
+            if trial == 0:
+                lengths = np.full(B, maxc)
+            else:
+                lengths = np.minimum(np.floor(np.exp(rng.uniform(0, np.log(maxc + 1), B))), maxc)
+                lengths[rng.integers(B)] = maxc
+            counts, per = _balanced_records(lengths, Hkv, tps // 128, target)
+            assert per <= 64
+            assert max(counts, default=0) <= recs, (maxc, tps, trial, max(counts), recs)
     assert tq._lib.tq_decode_workspace_bytes(ref, 0, 1, 32, 8, 10, 0) == 0
     assert tq._lib.tq_k_page_bytes(ref) == 1088 and tq._lib.tq_v_page_bytes(ref) == 800
+
+
+def test_workspace_of_the_vector_and_prefill_passes():
+    # chunks of tokens_per_split per (sequence or query block, KV head)
+    cb = _fake_cb()
+    ref = ctypes.byref(cb)
+    for B, q_len, Hq, Hkv in ((1, 1, 32, 2), (2, 21, 32, 8)):
+        rows = B * q_len * Hq
+        for maxc, tps in ((8192, 256), (8192, 1024)):
+            ws = tq._lib.tq_decode_workspace_bytes(ref, B, q_len, Hq, Hkv, maxc, tps)
+            words = ws // 4 - _prep_words(B, q_len, Hq, Hkv)
+            assert words == rows * 132 * max(1, -(-maxc // tps))
 
 
 def _hot(cb, **kw):
@@ -210,9 +248,11 @@ def test_oversized_chunk_is_rejected_not_clamped():
     assert "exceeds" in tq.tq_last_error()
     # (an accepted 8,192-token request would launch: that case runs in the GPU tests)
     ref = ctypes.byref(cb)
-    # automatic plan for many (sequence, KV head) pairs: chunks of at most 8,192 tokens
+    # automatic plan for many (sequence, KV head) groups of up to 131,072
+    # tokens: ranges found on the device fill 512 workgroups, so a group
+    # spans at most 512 / 8 of them
     ws = tq._lib.tq_decode_workspace_bytes(ref, 128, 1, 32, 8, 131072, 0)
-    assert ws // 4 == 128 * 32 * 16 * 132
+    assert ws // 4 == 128 * 32 * 64 * 132
 
 
 def test_binding_rejects_mismatched_pools_before_any_launch():
@@ -261,7 +301,7 @@ def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_call():
     cb = _fake_cb()
     ref = ctypes.byref(cb)
     cap = tq.tq_decode_noalloc_scratch_bytes()
-    assert cap == 16 << 20
+    assert cap == 64 << 20
 
     def call(**kw):
         a = dict(B=1, q_len=1, Hq=32, Hkv=8, maxc=1024, mb=64)
@@ -269,10 +309,10 @@ def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_call():
         return tq._lib.tq_decode_attention_noalloc(
             ref, FAKE, tq.TQ_BF16, FAKE, FAKE, FAKE, a["mb"], FAKE, a["B"], a["q_len"], a["Hq"],
             a["Hkv"], a["maxc"], 0.0, FAKE, tq.TQ_F32, 0, None)
-    # 64 sequences x 32 heads over 131,072 tokens: 16 chunks of partial records per row
-    need = tq._lib.tq_decode_workspace_bytes(ref, 64, 1, 32, 8, 131072, 0)
+    # 256 sequences x 32 heads over 131,072 tokens: 64 partial records per row
+    need = tq._lib.tq_decode_workspace_bytes(ref, 256, 1, 32, 8, 131072, 0)
     assert need > cap
-    assert call(B=64, maxc=131072, mb=8192) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+    assert call(B=256, maxc=131072, mb=8192) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
     assert "scratch" in tq.tq_last_error()
     # the plain call's argument checks come first
     assert call(Hq=30) == tq.TQ_ERR_INVALID_ARGUMENT
