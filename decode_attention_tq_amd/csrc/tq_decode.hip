@@ -34,9 +34,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Sequence s has T_s = ceil(L_s / 128) tiles; each of its Hkv groups is cut
 // into k_s = ceil(T_s / per) ranges of per tiles, one workgroup each, and the
 // ranges are numbered densely, sequence-major then head-major.  per is the
-// smallest value in [bal_min, 64] whose ranges number at most bal_target
-// (the count that fills the compute units once), or 64; a caller's fixed
-// bal_per overrides it.  Every wave of a workgroup (and of the merge and
+// smallest multiple of 4 in [bal_min, 64] (the four waves of a workgroup
+// then get equal tiles) whose ranges number at most bal_target (the count
+// that fills the compute units once), or 64; a caller's fixed bal_per
+// overrides it.  Every wave of a workgroup (and of the merge and
 // window passes) computes the same values from the context lengths, 64
 // sequences at a time.
 // Inclusive prefix sum over the wave: scans inside each 16-lane row (DPP
@@ -84,23 +85,23 @@ __device__ __forceinline__ int bal_ranges(const DecodeArgs &a, int t0, int p) {
 __device__ __forceinline__ int bal_per(const DecodeArgs &a, int t0) {
   if (a.bal_per > 0) return a.bal_per;
   if (a.num_seqs <= 64) {
-    // lane l tries p = l + 2 (lanes 0..62 cover 2..64): its ranges over all
-    // groups; the smallest p that fits wins
+    // lane l < 16 tries p = 4 (l + 1): its ranges over all groups; the
+    // smallest p that fits wins
     const int lane = threadIdx.x & 63;
-    const int p = min(lane + 2, 64);
+    const int p = 4 * (min(lane, 15) + 1);
     const float rp = 1.0f / (float)p;
     int tot = 0;
     for (int b = 0; b < a.num_seqs; ++b)  // uniform
       tot += ceil_div_small(__builtin_amdgcn_readlane(t0, b), p, rp);
-    const uint64_t fit = __ballot(p >= a.bal_min && tot * a.num_kv_heads <= a.bal_target);
-    return fit ? __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)fit) - 1) + 2 : 64;
+    const uint64_t fit = __ballot(lane < 16 && p >= a.bal_min && tot * a.num_kv_heads <= a.bal_target);
+    return fit ? 4 * (__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)fit) - 1) + 1) : 64;
   }
-  int lo = a.bal_min, hi = 64;
+  int lo = (a.bal_min + 3) >> 2, hi = 16;  // p = 4 m
   while (lo < hi) {  // uniform
     const int mid = (lo + hi) >> 1;
-    if (bal_ranges(a, t0, mid) <= a.bal_target) hi = mid; else lo = mid + 1;
+    if (bal_ranges(a, t0, 4 * mid) <= a.bal_target) hi = mid; else lo = mid + 1;
   }
-  return lo;
+  return 4 * lo;
 }
 // Workgroup w's range: sequence b, KV head h, range index j of the group
 // and the group's tile count; b = num_seqs when w is past the last range.
@@ -245,17 +246,18 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
       const int64_t page = (int64_t)btab[j >> 4] * a.num_kv_heads + h;
       const int o = j & 15;
       const uint8_t *kp = a.k_cache + page * kKPage;
-      const uint4 P0 = *reinterpret_cast<const uint4 *>(kp + 16 * o);
-      const uint4 P1 = *reinterpret_cast<const uint4 *>(kp + kKPlane + 16 * o);
-      const uint4 P2 = *reinterpret_cast<const uint4 *>(kp + 2 * kKPlane + 16 * o);
-      const uint4 Q = *reinterpret_cast<const uint4 *>(kp + kKSigns + 16 * o);
+      // record of coordinate chunk g: code planes 0..2 and signs of 32 coordinates
+      const uint4 C0 = *reinterpret_cast<const uint4 *>(kp + k_record(0, o));
+      const uint4 C1 = *reinterpret_cast<const uint4 *>(kp + k_record(1, o));
+      const uint4 C2 = *reinterpret_cast<const uint4 *>(kp + k_record(2, o));
+      const uint4 C3 = *reinterpret_cast<const uint4 *>(kp + k_record(3, o));
       const float nk = (float)*reinterpret_cast<const _Float16 *>(kp + kKNorm + 2 * o);
       const float gm = (float)*reinterpret_cast<const _Float16 *>(kp + kKGamma + 2 * o);
       nv = (float)*reinterpret_cast<const _Float16 *>(a.v_cache + page * kVPage + kVNorm + 2 * o);
-      const uint32_t w0[4] = {P0.x, P0.y, P0.z, P0.w};
-      const uint32_t w1[4] = {P1.x, P1.y, P1.z, P1.w};
-      const uint32_t w2[4] = {P2.x, P2.y, P2.z, P2.w};
-      const uint32_t wq[4] = {Q.x, Q.y, Q.z, Q.w};
+      const uint32_t w0[4] = {C0.x, C1.x, C2.x, C3.x};
+      const uint32_t w1[4] = {C0.y, C1.y, C2.y, C3.y};
+      const uint32_t w2[4] = {C0.z, C1.z, C2.z, C3.z};
+      const uint32_t wq[4] = {C0.w, C1.w, C2.w, C3.w};
       float dk[G], ds[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -304,11 +306,11 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
         if (tok0 >= s1) break;
         const uint8_t *vp = a.v_cache + ((int64_t)btab[tok0 >> 4] * a.num_kv_heads + h) * kVPage;
         const uint32_t a0 = *reinterpret_cast<const uint16_t *>(vp + 2 * lane);
-        const uint32_t a1 = *reinterpret_cast<const uint16_t *>(vp + kKPlane + 2 * lane);
-        const uint32_t a2 = *reinterpret_cast<const uint16_t *>(vp + 2 * kKPlane + 2 * lane);
+        const uint32_t a1 = *reinterpret_cast<const uint16_t *>(vp + kVPlane + 2 * lane);
+        const uint32_t a2 = *reinterpret_cast<const uint16_t *>(vp + 2 * kVPlane + 2 * lane);
         const uint32_t b0 = *reinterpret_cast<const uint16_t *>(vp + 128 + 2 * lane);
-        const uint32_t b1 = *reinterpret_cast<const uint16_t *>(vp + kKPlane + 128 + 2 * lane);
-        const uint32_t b2 = *reinterpret_cast<const uint16_t *>(vp + 2 * kKPlane + 128 + 2 * lane);
+        const uint32_t b1 = *reinterpret_cast<const uint16_t *>(vp + kVPlane + 128 + 2 * lane);
+        const uint32_t b2 = *reinterpret_cast<const uint16_t *>(vp + 2 * kVPlane + 128 + 2 * lane);
 #pragma unroll 4
         for (int tt = 0; tt < 16; ++tt) {
           const int ia = ((a0 >> tt) & 1) | (((a1 >> tt) & 1) << 1) | (((a2 >> tt) & 1) << 2);
@@ -649,6 +651,29 @@ struct QPrepRegs {
   uint32_t qw[2];
   uint4 sh[PROJ ? 16 : 1];
 };
+// The projection operands alone (they depend on no argument of the call's
+// plan, so they can be requested before it is known).
+template <bool PROJ>
+__device__ __forceinline__ void qprep_load_sh(const DecodeArgs &a, int wave, int lane, QPrepRegs<PROJ> &R) {
+  if constexpr (PROJ) {
+    const uint4 *shop = reinterpret_cast<const uint4 *>(a.SHop) + wave * 2 * 4 * 2 * 64 + lane;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) R.sh[e] = shop[e * 64];
+  }
+}
+// The query words alone.
+template <bool PROJ>
+__device__ __forceinline__ void qprep_load_q(const DecodeArgs &a, int64_t grp, int wave, int lane, QPrepRegs<PROJ> &R) {
+  const int rows = a.group * a.pos_count;
+  const bool f32 = a.q_dtype == TQ_F32;
+  const int64_t row = query_out_row(a, grp, min(wave, rows - 1));
+  const uint32_t *base = static_cast<const uint32_t *>(a.q);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t idx = row * kHeadDim + lane + 64 * j;
+    R.qw[j] = base[f32 ? idx : (idx >> 1)];
+  }
+}
 template <bool PROJ>
 __device__ __forceinline__ void qprep_loads(const DecodeArgs &a, int64_t grp, int wave, int lane, QPrepRegs<PROJ> &R) {
   const int rows = a.group * a.pos_count;
@@ -950,11 +975,11 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const uint8_t *rec = sm.kbuf[bs] + kKRec * (2 * sq + e);
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(rec + 16 * t16 + 4 * grow);
-        kw[e][0] = p[0];
-        kw[e][1] = p[64];
-        kw[e][2] = p[128];
-        kw[e][3] = p[192];
+        const u32x4 kr = *reinterpret_cast<const u32x4 *>(rec + k_record(grow, t16));  // planes 0..2, signs
+        kw[e][0] = kr[0];
+        kw[e][1] = kr[1];
+        kw[e][2] = kr[2];
+        kw[e][3] = kr[3];
         const uint16_t *nr = reinterpret_cast<const uint16_t *>(rec + 1024);
         nrm[e][0] = nr[t16];
         nrm[e][1] = nr[16 + t16];
@@ -1335,11 +1360,11 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const uint8_t *rec = sm.kbuf[bs] + kKRec * (2 * sq + e);
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(rec + 16 * t16 + 4 * grow);
-        kw[e][0] = p[0];
-        kw[e][1] = p[64];
-        kw[e][2] = p[128];
-        kw[e][3] = p[192];
+        const u32x4 kr = *reinterpret_cast<const u32x4 *>(rec + k_record(grow, t16));  // planes 0..2, signs
+        kw[e][0] = kr[0];
+        kw[e][1] = kr[1];
+        kw[e][2] = kr[2];
+        kw[e][3] = kr[3];
         const uint16_t *nr = reinterpret_cast<const uint16_t *>(rec + 1024);
         nrm[e][0] = nr[t16];
         nrm[e][1] = nr[16 + t16];
@@ -1569,6 +1594,372 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(Dec
       split_body_ws<0>(a, sm, b, h, j, s0, s1);
     else
       split_body_ws<1>(a, sm, b, h, j, s0, s1);
+  }
+}
+
+// ---- 2'''. split pass on the matrix cores, one tile per wave ----------------
+// The same contractions as split_body (fp6 query digits x fp4 bit-planes for
+// the scores, base-16 weight digits x fp4 value planes), arranged so that
+// every wave works alone: a workgroup of 4T waves forms the query operands
+// of its 4T heads once, then wave w takes tiles w, w + 4T, w + 8T, ... of
+// the range, with its own online softmax and accumulators, and the waves
+// meet only at the end to combine their records.  Per tile (8 pages, 128
+// tokens) a wave
+//   * loads the K planes and signs straight into score-operand layout (lane
+//     l: token l % 16, 32 coordinates of dword l / 16 of each 16-byte token
+//     record: one coalesced 256-byte load per plane and page) and the tile's
+//     norms (one 16-byte piece per lane, staged in its own LDS region);
+//   * scores page pairs (10 MFMAs per head tile), turns the weights of each
+//     pair into base-16 digits with one exponent per (head, pair) and writes
+//     them to its own LDS region in the value operand's order;
+//   * loads the V planes as 16-byte pieces, lane l holding coordinates
+//     8 (l % 16) .. +7 of pages 2 (l / 16) and 2 (l / 16) + 1, and
+//     interleaves the two pages per coordinate in registers: register r of
+//     the lane is then the B operand of coordinates 8 j + r (j = column), so
+//     value MFMA r yields those coordinates and no transpose is needed;
+//   * contracts the values of the tile (4 planes x 8 coordinate groups per
+//     head tile) and folds the planes into 8 running sums per head tile
+//     (o' = -sum_p beta_p acc_p), so its accumulators stay small.
+// The K part of tile k + 4T is fetched right after tile k's scores and the V
+// part right after its values, so each fetch has the other phase to arrive.
+// One reference R per head serves the scores and the accumulators: it moves
+// (rarely) when a score exceeds it by 2^64, and the digits of a pair carry
+// the R they were formed with.
+// 128 digits of one A row, padded to 68 dwords: the rows of the four heads a
+// wave writes together (4 rows apart) start 16 banks apart
+constexpr int kWqRowW = 136;
+template <int T>
+struct WaveLds {
+  union {
+    QPrepLds<T> q;  // start-up scratch of the query operands
+    struct {
+      alignas(16) uint16_t wq[4 * T][T][16][kWqRowW];  // per wave: [head tile][head*4+digit][K slot]
+      alignas(16) uint32_t nrm[4 * T][64][4];         // per wave: the tile's norms, 16 bytes per lane
+      int2 stats[4 * T][T][4][4];                      // per wave: [head tile][head][pair]: (exponent field, R bits)
+    } w;
+    struct {
+      float acc[4 * T][4 * T][kHeadDim];  // [wave][head][coordinate]
+      float m[4 * T][4 * T], l[4 * T][4 * T];
+    } red;
+  };
+};
+
+template <int T>
+__global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(DecodeArgs a) {
+  constexpr int NW = 4 * T;
+  __shared__ __align__(16) WaveLds<T> sm;
+  // the context lengths (the plan needs them first), then the projection
+  // operands, which do not depend on the plan (loads return in order: the
+  // plan then waits for the lengths only)
+  constexpr bool kProjAll = T == 1;
+  QPrepRegs<true> qpr;
+  QPrepRegs<false> qpn;
+  const int t0s = seq_tiles(a, threadIdx.x & 63);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const int w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (kProjAll || w0 < 4) qprep_load_sh<true>(a, w0, threadIdx.x & 63, qpr);  // uniform
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int per = bal_per(a, t0s);
+  int b, h, jr, Tb;
+  bal_locate(a, t0s, per, blockIdx.x, b, h, jr, Tb);
+  if (b >= a.num_seqs) return;  // uniform: past the last range
+  const int L = clamped_context(a, b);
+  const int s0 = 128 * per * jr, s1 = min(128 * per * (jr + 1), L);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t16 = lane & 15, grow = lane >> 4;
+  const int64_t grp = (int64_t)b * a.num_kv_heads + h;
+  const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count, G = a.group;
+  const int s1v = min(s1, L - qlen + 1);  // every row sees the keys before s1v
+  const int ntiles = (s1 - s0 + 127) >> 7;
+
+  // block ids of this wave's tiles w, w + NW, ... (at most 16): lane l holds
+  // page l % 8 of tile slot l / 8 (ids0) and of slot 8 + l / 8 (ids1); a page
+  // past the range re-reads its tile's first page (its tokens are masked)
+  int ids0, ids1;
+  {
+    const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
+    const int e = lane & 7;
+    int k = wave + NW * (lane >> 3);
+    int tile0 = s0 + 128 * min(k, ntiles - 1);
+    int tok = tile0 + 16 * e;
+    ids0 = btab[(tok < s1 ? tok : tile0) >> 4];
+    k += 8 * NW;
+    tile0 = s0 + 128 * min(k, ntiles - 1);
+    tok = tile0 + 16 * e;
+    ids1 = btab[(tok < s1 ? tok : tile0) >> 4];
+  }
+  auto page_id = [&](int slot, int e) __attribute__((always_inline)) {
+    const int src = slot < 8 ? ids0 : ids1;
+    return __builtin_amdgcn_readlane(src, 8 * (slot & 7) + e);
+  };
+
+  if (kProjAll || wave < 4)  // uniform
+    qprep_load_q<true>(a, grp, wave, lane, qpr);
+  else
+    qprep_load_q<false>(a, grp, wave, lane, qpn);
+
+  float beta[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
+  const BSplitK bk = bsplit_consts();
+  const uint32_t nib = in_vgpr(0x000F000Fu);
+  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80008000u);
+  const int kap0 = 8 * (t16 & 3) + (t16 >> 2);
+  const int gA = t16 >> 2, rA = lane & 3;
+  const int64_t hkv = a.num_kv_heads;
+  const uint8_t *const kc = a.k_cache, *const vc = a.v_cache;
+  // the lane's K record: coordinate chunk grow, token t16 (planes 0..2, signs)
+  const uint32_t ko = (uint32_t)k_record(grow, t16);
+  // norms: lanes 0..31 K page l / 4 at 1024 + 16 (l % 4) (n_k, gamma), lanes
+  // 32..47 V page (l - 32) / 2 at 768 + 16 (l % 2), lanes 48..63 repeat 32..47
+  const int ne = lane < 32 ? lane >> 2 : ((lane - 32) & 15) >> 1;
+  const uint32_t no = lane < 32 ? 1024u + 16u * (uint32_t)(lane & 3) : 768u + 16u * (uint32_t)(lane & 1);
+  const bool nk = lane < 32;
+
+  // per-wave state (lane: head grow of tile u)
+  float R[T], lsum[T];
+  float tot[T][8];
+  v4f corr[T];
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    R[u] = -INFINITY;
+    lsum[u] = 0.0f;
+    corr[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) tot[u][r] = 0.0f;
+  }
+
+  u32x4 KP[8];
+  u32x4 NR;
+  u32x4 VA[3][2];
+  // fetches of tile slot i (unconditional: past the wave's last tile they
+  // repeat its own pages, which are valid)
+  auto load_k = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint8_t *kp = uniform_ptr(kc + ((int64_t)page_id(i, e) * hkv + h) * kKPage);
+      KP[e] = load_at<u32x4>(kp, ko);
+    }
+    const int64_t pid = (int64_t)__builtin_amdgcn_ds_bpermute(4 * (8 * (i & 7) + ne), i < 8 ? ids0 : ids1);
+    const uint8_t *np = nk ? kc + (pid * hkv + h) * kKPage : vc + (pid * hkv + h) * kVPage;
+    NR = *reinterpret_cast<const u32x4 *>(np + no);
+  };
+  auto load_v = [&](int i) __attribute__((always_inline)) {
+    const int src = i < 8 ? ids0 : ids1;
+    const int pa = __builtin_amdgcn_ds_bpermute(4 * (8 * (i & 7) + 2 * grow), src);
+    const int pb = __builtin_amdgcn_ds_bpermute(4 * (8 * (i & 7) + 2 * grow + 1), src);
+    const uint8_t *va = vc + ((int64_t)pa * hkv + h) * kVPage + 16 * t16;
+    const uint8_t *vb = vc + ((int64_t)pb * hkv + h) * kVPage + 16 * t16;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      VA[p][0] = *reinterpret_cast<const u32x4 *>(va + kVPlane * p);
+      VA[p][1] = *reinterpret_cast<const u32x4 *>(vb + kVPlane * p);
+    }
+  };
+
+  int slot = 0;
+  int k = wave;
+  // the first tile's pages are requested before the query operands are
+  // formed, so that their memory latency overlaps that work
+  if (k < ntiles) {  // uniform
+    load_k(0);
+    load_v(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // query operands of all head tiles (every wave scores)
+  v8i Aq[T][5];
+  int scq[T][5];
+  v4f cinit[T], qinit[T];
+  int tiles_all[T];
+#pragma unroll
+  for (int u = 0; u < T; ++u) tiles_all[u] = u;
+  if (kProjAll || wave < 4)  // uniform
+    qprep_compute<T, T, true, true>(a, sm.q, qpr, tid, wave, tiles_all, Aq, scq, cinit, qinit);
+  else
+    qprep_compute<T, T, true, false>(a, sm.q, qpn, tid, wave, tiles_all, Aq, scq, cinit, qinit);
+  uint32_t *const nrm = &sm.w.nrm[wave][0][0];
+  const uint16_t *const nh = reinterpret_cast<const uint16_t *>(nrm);
+  // the last key each of the lane's rows sees (causal over a verify block)
+  int lim[T];
+#pragma unroll
+  for (int u = 0; u < T; ++u) lim[u] = min(s1, L - qlen + (4 * u + grow) / G + 1);
+  for (; k < ntiles; k += NW, ++slot) {  // uniform per wave
+    const int nslot = k + NW < ntiles ? slot + 1 : slot;
+    const int tok0 = s0 + 128 * k;
+    // ---- raw scores of the tile's 8 pages (log2 units) ------------------------
+    // K page e: n_k at halves 32 e + t, gamma at 32 e + 16 + t; V page e: 256 + 16 e + t
+    *reinterpret_cast<u32x4 *>(nrm + 4 * lane) = NR;
+    float rs[T][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float nkv = half_lo(nh[32 * e + t16]), gmv = half_lo(nh[32 * e + 16 + t16]);
+      const uint32_t w0 = KP[e][0], w1 = KP[e][1], w2 = KP[e][2], w3 = KP[e][kKSignField];
+      const v8i B0 = bsplit(w0, bk), B1 = bsplit(w1, bk), B2 = bsplit(w2, bk);
+      const v8i Bx = bsplit(w0 ^ w1 ^ w2, bk), Bs = bsplit(w3, bk);
+      const int tq = tok0 + 16 * e + t16;
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        v4f c = mfma_f6f4(Aq[u][0], B0, cinit[u], scq[u][0]);
+        c = mfma_f6f4(Aq[u][1], B1, c, scq[u][1]);
+        c = mfma_f6f4(Aq[u][2], B2, c, scq[u][2]);
+        c = mfma_f6f4(Aq[u][3], Bx, c, scq[u][3]);
+        const v4f qv = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
+        const float inner = fmaf(gmv, (qv[0] + qv[1]) + (qv[2] + qv[3]), (c[0] + c[1]) + (c[2] + c[3]));
+        // a slot the lane's row does not see (past the range, or causal) is -inf
+        rs[u][e] = tq < lim[u] ? nkv * inner : -INFINITY;
+      }
+    }
+    // the K part of the next tile (the last tile re-reads its own), issued as
+    // soon as this tile's K registers are consumed: scheduling barriers keep
+    // the compiler from sinking the loads to their use, which would expose
+    // the whole memory latency
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(nslot);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- the head's reference moves when a score exceeds it by 2^64 (or it is
+    // still -inf); the lanes of a head move together
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      float mx = rs[u][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, rs[u][e]);
+      if (__builtin_amdgcn_ballot_w64(mx > R[u] + (float)kRefStep)) {  // uniform, rare
+        const float nr = fmaxf(R[u], ceilf(row_max16(mx)));
+        if (nr > R[u]) {
+          const float f = R[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(R[u] - nr);
+          lsum[u] *= f;
+          corr[u] *= f;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) tot[u][r] *= f;
+          R[u] = nr;
+        }
+      }
+    }
+    // ---- weights of the 4 page pairs as base-16 digits -------------------------
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float nv0 = half_lo(nh[256 + 32 * q + t16]), nv1 = half_lo(nh[256 + 32 * q + 16 + t16]);
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        const float r0 = rs[u][2 * q], r1 = rs[u][2 * q + 1];
+        // (R stays -inf while the head has seen no key: select, never -inf - -inf)
+        const float p0 = r0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(r0 - R[u]);
+        const float p1 = r1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(r1 - R[u]);
+        lsum[u] += p0 + p1;
+        // a slot past the visible range may hold any norm bits (Inf, NaN)
+        const float w0 = r0 == -INFINITY ? 0.0f : p0 * nv0;
+        const float w1 = r1 == -INFINITY ? 0.0f : p1 * nv1;
+        const int mk = row_max16_nonneg(max(__float_as_int(w0), __float_as_int(w1)));  // w >= 0
+        const uint32_t exb = max((uint32_t)mk & 0x7F800000u, 14u << 23);
+        const float mult = __uint_as_float(0x86000000u - exb);  // 2^(141 - ex)
+        const uint32_t X0 = __float_as_uint(fmaf(w0, mult, 8388608.0f));
+        const uint32_t X1 = __float_as_uint(fmaf(w1, mult, 8388608.0f));
+        const uint32_t XX = __builtin_amdgcn_perm(X1, X0, 0x05040100u);  // X0 lo16 | X1 lo16 << 16
+        uint16_t *wr = &sm.w.wq[wave][u][4 * grow][32 * q + kap0];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // digit r (place 16^(3-r)) of both tokens, with the slot's sign
+          const uint32_t D = ((XX >> (12 - 4 * r)) & nib) | s80;
+          wr[r * kWqRowW] = (uint16_t)D;
+          wr[r * kWqRowW + 4] = (uint16_t)(D >> 16);
+        }
+        sm.w.stats[wave][u][grow][q] = make_int2((int)(exb >> 23), __float_as_int(R[u]));
+      }
+    }
+    // ---- values of the tile --------------------------------------------------
+    v8i Aw[T];
+    int sw[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      Aw[u] = fp6_operand(&sm.w.wq[wave][u][t16][32 * grow], 0x1p-21f);  // d 2^-24 -> d/8 (row: 272 bytes)
+      const int2 st = sm.w.stats[wave][u][gA][grow];
+      const float ra = __shfl(R[u], 16 * gA, 64);  // R of head gA now
+      const float d = fmaxf(__int_as_float(st.y) - ra, -300.0f);  // NaN (both -inf) -> -300
+      sw[u] = min(max(st.x + 1 - 4 * rA + (int)d, 0), 254);  // E8M0 of 2^(ex-126-4r+R_pair-R)
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      uint32_t W[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)  // coordinate 8 t16 + r of both pages: page a low, page b high
+        W[p] = __builtin_amdgcn_perm(VA[p][1][r >> 1], VA[p][0][r >> 1], (r & 1) ? 0x07060302u : 0x05040100u);
+      const v8i V0 = bsplit(W[0], bk), V1 = bsplit(W[1], bk), V2 = bsplit(W[2], bk);
+      const v8i Vx = bsplit(W[0] ^ W[1] ^ W[2], bk);
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        const v4f z = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        const v4f c0 = mfma_f6f4(Aw[u], V0, z, sw[u]);
+        const v4f c1 = mfma_f6f4(Aw[u], V1, z, sw[u]);
+        const v4f c2 = mfma_f6f4(Aw[u], V2, z, sw[u]);
+        const v4f c3 = mfma_f6f4(Aw[u], Vx, z, sw[u]);
+        float o = tot[u][r];
+        o = fmaf(-beta[0], (c0[0] + c0[1]) + (c0[2] + c0[3]), o);
+        o = fmaf(-beta[1], (c1[0] + c1[1]) + (c1[2] + c1[3]), o);
+        o = fmaf(-beta[2], (c2[0] + c2[1]) + (c2[2] + c2[3]), o);
+        tot[u][r] = fmaf(-beta[3], (c3[0] + c3[1]) + (c3[2] + c3[3]), o);
+      }
+    }
+    {
+      const v8i C1 = v8i{(int)0xEEEEEEEEu, (int)0xDDDDDDDDu, (int)0xAAAAAAAAu, 0, 0, 0, 0, 0};
+      const v8i C2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        corr[u] = mfma_f6f4(Aw[u], C1, corr[u], sw[u]);
+        corr[u] = mfma_f6f4(Aw[u], C2, corr[u], sw[u]);
+      }
+    }
+    // the V part of the next tile
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(nslot);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // keep the matrix ops out of the per-head branches below
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    asm volatile("" : "+v"(corr[u]));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(tot[u][r]));
+  }
+
+  // ---- the waves combine their records -----------------------------------------
+  lds_barrier();  // every wave is done with its LDS region
+  const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    const int hd = 4 * u + grow;
+    const float cs = (corr[u][0] + corr[u][1]) + (corr[u][2] + corr[u][3]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sm.red.acc[wave][hd][8 * t16 + r] = tot[u][r] - bsum * cs;
+    const float ls = row_sum16(lsum[u]);
+    if (t16 == 0) {
+      sm.red.m[wave][hd] = R[u];
+      sm.red.l[wave][hd] = ls;
+    }
+  }
+  lds_barrier();
+  // wave w writes the record of head w
+  if (wave < nrows) {  // uniform
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, sm.red.m[v][wave]);
+    float l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float mv = sm.red.m[v][wave];
+      const float f = mv == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+      l = fmaf(f, sm.red.l[v][wave], l);
+      o0 = fmaf(f, sm.red.acc[v][wave][lane], o0);
+      o1 = fmaf(f, sm.red.acc[v][wave][lane + 64], o1);
+    }
+    float *part = a.partials + (query_out_row(a, grp, wave) * a.part_stride + jr) * kPartStride;
+    if (lane == 0) {
+      part[0] = M;
+      part[1] = l;
+    }
+    part[4 + lane] = o0;
+    part[68 + lane] = o1;
   }
 }
 
@@ -1910,7 +2301,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
       la.pos_count = min(per, a.q_len - p0);
       la.qk_tiles = (la.group * la.pos_count + 3) / 4;
       if (la.qk_tiles == 1)
-        hipLaunchKernelGGL(split_mfma_kernel<1>, dim3((unsigned)items), dim3(256), 0, stream, la);
+        hipLaunchKernelGGL(split_wave_kernel<1>, dim3((unsigned)items), dim3(256), 0, stream, la);
       else if (la.qk_tiles == 2)
         hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)items), dim3(512), 0, stream, la);
       else

@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           const int q = lane >> 1, hf = lane & 1, m = q >> 2, i = q & 3;
 #pragma unroll
           for (int p = 0; p < 3; ++p) {
-            uint16_t *img = reinterpret_cast<uint16_t *>(L.vimg[wave] + kKPlane * p);
+            uint16_t *img = reinterpret_cast<uint16_t *>(L.vimg[wave] + kVPlane * p);
             img[16 * m + 4 * (2 * hf) + i] = (uint16_t)vb[p];
             img[16 * m + 4 * (2 * hf + 1) + i] = (uint16_t)(vb[p] >> 16);
           }
@@ -428,14 +428,15 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         float g2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float es[8][4];
         key_steps(std::make_integer_sequence<int, 32>{}, ky, T, r256, cp0, cp1, cp2, cp3, kb, es, g2);
-        // lane L = 2(4n + i) + hf holds 16-bit pieces (coordinates 16n..+15) of tokens 4g + i, g = 2hf, 2hf+1
+        // lane L = 2(4n + i) + hf holds 16-bit pieces (coordinates 16n..+15) of tokens 4g + i, g = 2hf, 2hf+1;
+        // piece n of plane p of token t is half (n & 1) of word p of record (n / 2, t)
         {
           const int q = lane >> 1, hf = lane & 1, n = q >> 2, i = q & 3;
+          uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[wave]);
 #pragma unroll
           for (int p = 0; p < 3; ++p) {
-            uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[wave] + kKPlane * p);
-            img[8 * (4 * (2 * hf) + i) + n] = (uint16_t)kb[p];
-            img[8 * (4 * (2 * hf + 1) + i) + n] = (uint16_t)(kb[p] >> 16);
+            img[k_record(n >> 1, 4 * (2 * hf) + i) / 2 + 2 * p + (n & 1)] = (uint16_t)kb[p];
+            img[k_record(n >> 1, 4 * (2 * hf + 1) + i) / 2 + 2 * p + (n & 1)] = (uint16_t)(kb[p] >> 16);
           }
         }
         // residual halves, slot 8 (l%16) + n of token 4(l/16) + i
@@ -488,11 +489,12 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
     {
       uint32_t sbits = 0u;
       qjl_tiles(std::make_integer_sequence<int, kTiles>{}, L, l16, lg, shi, slo, sbits);
-      // lane L = 2(8 tl + 4u + i) + hf: rows 16(2w+u)..+15 of tokens 4g + i, g = 2hf, 2hf+1
+      // lane L = 2(8 tl + 4u + i) + hf: rows 16(2w+u)..+15 of tokens 4g + i, g = 2hf, 2hf+1,
+      // half u of the sign word of record (w, t)
       const int q = lane >> 1, hf = lane & 1, tl = q >> 3, u = (q >> 2) & 1, i = q & 3;
-      uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[tl] + kKSigns);
-      img[8 * (4 * (2 * hf) + i) + 2 * wave + u] = (uint16_t)sbits;
-      img[8 * (4 * (2 * hf + 1) + i) + 2 * wave + u] = (uint16_t)(sbits >> 16);
+      uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[tl]);
+      img[k_record(wave, 4 * (2 * hf) + i) / 2 + 2 * kKSignField + u] = (uint16_t)sbits;
+      img[k_record(wave, 4 * (2 * hf + 1) + i) / 2 + 2 * kKSignField + u] = (uint16_t)(sbits >> 16);
     }
     lds_barrier();
 
@@ -519,15 +521,14 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           *reinterpret_cast<uint4 *>(vp + 16 * q) = *reinterpret_cast<const uint4 *>(L.vimg[tl] + 16 * q);
         }
       } else {
-        // token by token: K records (3 planes + signs as 16-byte pieces), the
-        // scalars, and value bits merged into their pages atomically
+        // token by token: K records (the four 16-byte chunk records of the
+        // token), the scalars, and value bits merged into their pages atomically
         if (tid < 4 * kTok) {
-          const int n = tid >> 2, piece = tid & 3;
+          const int n = tid >> 2, g = tid & 3;
           if (L.valid[tl][n]) {
             uint8_t *kp = k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
-            const int src = piece < 3 ? kKPlane * piece + 16 * n : kKSigns + 16 * n;
-            const int dst = piece < 3 ? kKPlane * piece + 16 * L.off[tl][n] : kKSigns + 16 * L.off[tl][n];
-            *reinterpret_cast<uint4 *>(kp + dst) = *reinterpret_cast<const uint4 *>(L.kimg[tl] + src);
+            *reinterpret_cast<uint4 *>(kp + k_record(g, L.off[tl][n])) =
+                *reinterpret_cast<const uint4 *>(L.kimg[tl] + k_record(g, n));
           }
         } else if (tid < 5 * kTok) {
           const int n = tid - 4 * kTok;
@@ -553,12 +554,12 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           uint8_t *vp = v_cache + ((int64_t)bn * H + hh) * kVPage;
 #pragma unroll
           for (int p = 0; p < 3; ++p) {
-            const uint32_t w2 = reinterpret_cast<const uint32_t *>(L.vimg[tl] + kKPlane * p)[lane];
+            const uint32_t w2 = reinterpret_cast<const uint32_t *>(L.vimg[tl] + kVPlane * p)[lane];
             const uint32_t b = ((w2 >> n) & 1u) | (((w2 >> (16 + n)) & 1u) << 16);
             const uint32_t set = b << o, clr = (0x10001u << o) & ~set;
             // global (not flat) atomics: a pending flat operation would make
             // every later wait on the memory counters wait for all of them
-            gword *w32 = reinterpret_cast<gword *>(reinterpret_cast<uintptr_t>(vp + kKPlane * p + 4 * lane));
+            gword *w32 = reinterpret_cast<gword *>(reinterpret_cast<uintptr_t>(vp + kVPlane * p + 4 * lane));
             __hip_atomic_fetch_and(w32, ~clr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_or(w32, set, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }

@@ -106,15 +106,15 @@ bool dtype_ok(int d) { return d == TQ_F32 || d == TQ_F16 || d == TQ_BF16; }
 // Matrix-core decode pass (q_len = 1 or a short verify block, up to 8 query
 // heads per KV head): the balanced plan.  Every (sequence, KV head) group is
 // cut into ranges of `per` 128-token tiles, one workgroup each; per is chosen
-// on the device from the actual context lengths as the smallest value in
-// [2, 64] whose ranges fit in the count that fills the 256 compute units
+// on the device from the actual context lengths as the smallest multiple of
+// 4 in [4, 64] whose ranges fit in the count that fills the 256 compute units
 // once (one 8-wave workgroup per unit for 5 to 8 query rows, two 4-wave ones
 // for up to 4), so a ragged batch keeps the workgroups about equally busy.
 // Each workgroup pays a fixed start-up (block ids, query operands, the first
 // tiles in flight), so longer ranges are preferred once the units are full;
 // a range holds at most 64 tiles (its block ids are kept in LDS).  The grid
 // covers the ranges at per = 64 for every sequence at max_ctx; workgroups
-// past the last range exit.  Records per row: k = ceil(T / per) <= T / 2,
+// past the last range exit.  Records per row: k = ceil(T / per) <= T / 4,
 // and below 64 tiles Hkv k fits the filling count.
 // Other passes (vector pass, prefill): chunks of split_tokens (multiples of
 // 256) per (sequence or query block, KV head), aiming at about 1024
@@ -123,7 +123,7 @@ struct SplitPlan {
   int split_tokens, num_splits;  // num_splits: partial records per row (compressed part)
   int balanced, grid, target, per, min_tiles;
 };
-constexpr int kBalMinTiles = 2;
+constexpr int kBalMinTiles = 4;  // and per is a multiple of 4 (one tile per wave and step)
 constexpr int kBalMaxTiles = tq::kMaxMfmaSplitTokens / 128;
 
 SplitPlan plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested) {

@@ -17,12 +17,19 @@ constexpr int kVPage = 800;
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one workgroup
 constexpr uint32_t kMagic = 0x54513031u;  // "TQ01"
 
-// Offsets inside a K page / V page (see tq.h).
-constexpr int kKPlane = 256;        // bytes per code bit-plane
-constexpr int kKSigns = 768;
+// Offsets inside a K page / V page (see tq.h).  K page: 64 records of 16
+// bytes, record (chunk g, token t) at 16 (16 g + t) holding the 32-bit words
+// of code bit-planes 0, 1, 2 and of the QJL signs for coordinates (rows)
+// 32 g .. 32 g + 31; then the half norms and residual lengths.  V page: three
+// coordinate-major bit-planes of 256 bytes, then the half norms.
+constexpr int kKRecords = 1024;     // bytes of 16-byte (chunk, token) records
+constexpr int kKSignField = 3;      // word of a record holding the QJL signs
 constexpr int kKNorm = 1024;
 constexpr int kKGamma = 1056;
+constexpr int kVPlane = 256;        // bytes per V code bit-plane
 constexpr int kVNorm = 768;
+// Byte offset of the record of coordinate chunk g, token t of a K page.
+constexpr int k_record(int g, int t) { return 16 * (16 * g + t); }
 
 struct Codebook {
   float c[8];        // ascending levels
@@ -76,7 +83,7 @@ struct DecodeArgs {
   // Balanced plan of the matrix-core decode pass (balanced = 1): the tiles
   // of 128 tokens of every (sequence, KV head) group are cut into ranges of
   // `per` tiles, one workgroup each, numbered densely sequence-major then
-  // head-major; per = bal_per if > 0, else the smallest value in
+  // head-major; per = bal_per if > 0, else the smallest multiple of 4 in
   // [bal_min, 64] whose ranges number at most bal_target (or 64), computed
   // on the device from the context lengths.  Range j of a group writes the
   // group's partial record j.  The grid has bal_grid workgroups, enough for

@@ -108,10 +108,13 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
   for (int it = tid; it < 512; it += kThreads) {
     const int key = it >> 4, p16 = it & 15, pg = key >> 4, tok = key & 15;
     const uint8_t *pk = rawk[pg];
-    const uint32_t w0 = pk[kKPlane * 0 + 16 * tok + p16];
-    const uint32_t w1 = pk[kKPlane * 1 + 16 * tok + p16];
-    const uint32_t w2 = pk[kKPlane * 2 + 16 * tok + p16];
-    const uint32_t ws = pk[kKSigns + 16 * tok + p16];
+    // byte p16 of a token's 128-bit field: coordinates (rows) 8 p16 .. +7, in
+    // byte p16 % 4 of that field's word of the record of chunk p16 / 4
+    const int kb = k_record(p16 >> 2, tok) + (p16 & 3);
+    const uint32_t w0 = pk[kb];
+    const uint32_t w1 = pk[kb + 4];
+    const uint32_t w2 = pk[kb + 8];
+    const uint32_t ws = pk[kb + 4 * kKSignField];
     uint32_t hv[4], lv[4], sv[4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -133,9 +136,9 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
   for (int it = tid; it < 512; it += kThreads) {
     const int c = it >> 2, pg = (it >> 1) & 1, th8 = it & 1;
     const uint8_t *pv = rawv[pg];
-    const uint32_t w0 = pv[kKPlane * 0 + 2 * c + th8];
-    const uint32_t w1 = pv[kKPlane * 1 + 2 * c + th8];
-    const uint32_t w2 = pv[kKPlane * 2 + 2 * c + th8];
+    const uint32_t w0 = pv[kVPlane * 0 + 2 * c + th8];
+    const uint32_t w1 = pv[kVPlane * 1 + 2 * c + th8];
+    const uint32_t w2 = pv[kVPlane * 2 + 2 * c + th8];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int g = 2 * th8 + q;

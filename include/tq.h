@@ -31,10 +31,12 @@
  * Page layout (little-endian; bit b of a byte has weight 2^b), one page per
  * (block, KV head), pools k_cache[num_blocks][num_kv_heads][1088] and
  * v_cache[num_blocks][num_kv_heads][800], slot = block * 16 + offset:
- *   K page: [256p, 256p+256), p = 0..2: bit-plane p of the codes, token t at
- *           256p + 16t, coordinate i at bit i of that 128-bit record;
- *           [768, 1024): QJL sign bits (1 = projection >= 0), token t at
- *           768 + 16t; [1024, 1056): half norm of token t at 1024 + 2t;
+ *   K page: [0, 1024): 64 records of 16 bytes, record (chunk g, token t)
+ *           at 16 (16 g + t) for g = 0..3; its 32-bit word f = 0..2 holds
+ *           bit-plane f of the codes of coordinates 32g .. 32g+31
+ *           (coordinate 32g + k at bit k), word 3 the QJL sign bits of
+ *           projection rows 32g .. 32g+31 (1 = projection >= 0);
+ *           [1024, 1056): half norm of token t at 1024 + 2t;
  *           [1056, 1088): half residual length gamma at 1056 + 2t.
  *   V page: [256p, 256p+256), p = 0..2: bit-plane p, coordinate-major:
  *           coordinate i owns the 16-bit word at 256p + 2i, token t at its

@@ -12,11 +12,14 @@ Pools: ``k_pool[num_blocks][num_kv_heads][1088]``,
 All multi-byte fields little-endian; bit b of a byte has weight 2^b.
 
 K page (1088 B):
-  [256p, 256p + 256), p = 0, 1, 2 : code bit-plane p, token-major:
-      token t owns bytes 256p + 16t .. +16; coordinate i is bit (i % 8) of
-      byte 256p + 16t + i // 8 and holds bit p of code_i.
-  [768, 1024)   : QJL signs, token t at 768 + 16t, row i at bit i as above;
-                  1 means z_i >= 0.
+  [0, 1024)     : 64 records of 16 bytes, chunk-major: the record of
+      coordinate chunk g = 0..3 (coordinates 32g .. 32g + 31) and token t is
+      at 16 (16 g + t); its four little-endian 32-bit words are field
+      f = 0, 1, 2 (code bit-plane f: bit i % 32 of the word holds bit f of
+      code_i for coordinate i = 32 g + i % 32) and f = 3 (QJL signs: bit
+      i % 32 holds the sign bit of projection row i = 32 g + i % 32; 1 means
+      z_i >= 0).  So bit f of code_i / the sign of row i sits at byte
+      16 (16 (i // 32) + t) + 4 f + (i % 32) // 8, bit i % 8.
   [1024, 1056)  : half n_t at 1024 + 2t.
   [1056, 1088)  : half gamma_t at 1056 + 2t.
 V page (800 B):
@@ -60,12 +63,18 @@ def _get_half(buf: np.ndarray, off: int) -> np.float16:
     return np.array([raw], dtype=np.uint16).view(np.float16)[0]
 
 
+def k_bit_byte(t: int, i: int, field: int) -> int:
+    """Byte of the K page holding field ``field`` (0..2: code bit-plane,
+    3: QJL sign) of coordinate / row ``i`` of token ``t``; the bit is i % 8."""
+    return 16 * (16 * (i // 32) + t) + 4 * field + (i % 32) // 8
+
+
 def set_k_slot(page: np.ndarray, t: int, codes, signs, n16, g16) -> None:
     for i in range(HEAD_DIM):
         for p in range(3):
-            _put_bit(page, 256 * p + 16 * t + i // 8, i % 8, (int(codes[i]) >> p) & 1)
+            _put_bit(page, k_bit_byte(t, i, p), i % 8, (int(codes[i]) >> p) & 1)
     for i in range(QJL_DIM):
-        _put_bit(page, 768 + 16 * t + i // 8, i % 8, int(signs[i]))
+        _put_bit(page, k_bit_byte(t, i, 3), i % 8, int(signs[i]))
     _put_half(page, 1024 + 2 * t, n16)
     _put_half(page, 1056 + 2 * t, g16)
 
@@ -76,10 +85,10 @@ def get_k_slot(page: np.ndarray, t: int):
     for i in range(HEAD_DIM):
         v = 0
         for p in range(3):
-            v |= _get_bit(page, 256 * p + 16 * t + i // 8, i % 8) << p
+            v |= _get_bit(page, k_bit_byte(t, i, p), i % 8) << p
         codes[i] = v
     for i in range(QJL_DIM):
-        signs[i] = _get_bit(page, 768 + 16 * t + i // 8, i % 8)
+        signs[i] = _get_bit(page, k_bit_byte(t, i, 3), i % 8)
     return codes, signs, _get_half(page, 1024 + 2 * t), _get_half(page, 1056 + 2 * t)
 
 
@@ -203,11 +212,14 @@ def write_slots_fast(k_pool: np.ndarray, v_pool: np.ndarray, slot_mapping, enc_k
     ar16 = np.arange(16)[None, :]
     ar2 = np.arange(2)[None, :]
     bcol = blk[:, None]
+    ar4 = np.arange(4)[None, :]
     for h in range(H):
-        for p in range(3):
-            planes = _pack_bits_le((kc[:, h, :] >> p) & 1)              # [T, 16]
-            k_pool[bcol, h, (256 * p + 16 * off)[:, None] + ar16] = planes
-        k_pool[bcol, h, (768 + 16 * off)[:, None] + ar16] = _pack_bits_le(ks[:, h, :])
+        # fields f = 0..2 (code bit-planes) and 3 (signs), 16 bytes per token,
+        # 4 bytes per coordinate chunk g at 16 (16 g + t) + 4 f
+        fields = [_pack_bits_le((kc[:, h, :] >> p) & 1) for p in range(3)] + [_pack_bits_le(ks[:, h, :])]
+        for f, fb in enumerate(fields):                                   # fb: [T, 16]
+            for g in range(4):
+                k_pool[bcol, h, (16 * (16 * g + off) + 4 * f)[:, None] + ar4] = fb[:, 4 * g: 4 * g + 4]
         k_pool[bcol, h, (1024 + 2 * off)[:, None] + ar2] = _half_bytes(enc_k["norm_f16"][keep][:, h])
         k_pool[bcol, h, (1056 + 2 * off)[:, None] + ar2] = _half_bytes(enc_k["gamma_f16"][keep][:, h])
         v_pool[bcol, h, (768 + 2 * off)[:, None] + ar2] = _half_bytes(enc_v["norm_f16"][keep][:, h])
@@ -226,10 +238,13 @@ def read_k_tokens_fast(k_pool: np.ndarray, block_row, length: int, head: int):
     nb = (length + BLOCK - 1) // BLOCK
     pages = k_pool[np.asarray(block_row[:nb], dtype=np.int64), head]    # [nb, 1088]
     codes = np.zeros((nb, BLOCK, HEAD_DIM), dtype=np.uint8)
+    # [nb, chunk g, token t, field f, 4 bytes] -> per field [nb, t, 16 bytes in chunk order]
+    rec = pages[:, :1024].reshape(nb, 4, BLOCK, 4, 4)
+    def field(f):
+        return np.ascontiguousarray(np.transpose(rec[:, :, :, f, :], (0, 2, 1, 3))).reshape(nb, BLOCK, 16)
     for p in range(3):
-        raw = pages[:, 256 * p: 256 * p + 256].reshape(nb, BLOCK, 16)
-        codes |= (_unpack_bits_le(raw, HEAD_DIM) << p).astype(np.uint8)
-    signs = _unpack_bits_le(pages[:, 768:1024].reshape(nb, BLOCK, 16), QJL_DIM)
+        codes |= (_unpack_bits_le(field(p), HEAD_DIM) << p).astype(np.uint8)
+    signs = _unpack_bits_le(field(3), QJL_DIM)
     n16 = pages[:, 1024:1056].copy().view(np.float16).reshape(nb, BLOCK)
     g16 = pages[:, 1056:1088].copy().view(np.float16).reshape(nb, BLOCK)
     return (codes.reshape(-1, HEAD_DIM)[:length], signs.reshape(-1, QJL_DIM)[:length],

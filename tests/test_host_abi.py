@@ -150,16 +150,17 @@ def _prep_words(B, q_len, Hq, Hkv):
     return B * q_len * Hq * 256
 
 
-def _balanced_records(lengths, Hkv, per_fixed, target, min_tiles=2):
+def _balanced_records(lengths, Hkv, per_fixed, target, min_tiles=4):
     """Records per group under the balanced plan of the matrix-core pass, by
     brute force: tiles of 128 tokens; each (sequence, KV head) group cut into
-    ranges of per tiles, per fixed or the smallest value in [min_tiles, 64]
-    whose ranges over all groups number at most ``target`` (else 64)."""
+    ranges of per tiles, per fixed or the smallest multiple of 4 in
+    [min_tiles, 64] whose ranges over all groups number at most ``target``
+    (else 64)."""
     T = [(int(L) + 127) // 128 for L in lengths]
 
     def ranges(p):
         return Hkv * sum(-(-t // p) for t in T)
-    per = per_fixed or next((p for p in range(min_tiles, 65) if ranges(p) <= target), 64)
+    per = per_fixed or next((p for p in range(min_tiles, 65, 4) if ranges(p) <= target), 64)
     return [-(-t // per) for t in T for _ in range(Hkv)], per
 
 

@@ -22,22 +22,34 @@ def test_hand_placed_bits():
     g16 = np.zeros(16, np.float16)
     n16[3] = np.float16(2.0)   # 0x4000
     g16[3] = np.float16(-0.5)  # 0xB800
+    codes[5, 100] = 6          # binary 110 -> planes 1 and 2, chunk 3
+    signs[5, 100] = 1
     k = P.pack_k_page(codes, signs, n16, g16)
-    # coordinate 9 -> byte 1, bit 1 of token 3's 16-byte record
-    assert k[0 * 256 + 16 * 3 + 1] == 0b10
-    assert k[1 * 256 + 16 * 3 + 1] == 0
-    assert k[2 * 256 + 16 * 3 + 1] == 0b10
-    assert k[768 + 16 * 3 + 1] == 0b10
+    # coordinate 9 of token 3: chunk 0, record 16 * (16 * 0 + 3) = 48; field f
+    # is the word at 48 + 4 f; bit 9 is byte 1, bit 1 of the word
+    assert k[48 + 0 + 1] == 0b10
+    assert k[48 + 4 + 1] == 0
+    assert k[48 + 8 + 1] == 0b10
+    assert k[48 + 12 + 1] == 0b10
+    # coordinate 100 of token 5: chunk 3, record 16 * (48 + 5) = 848; bit
+    # 100 % 32 = 4 is byte 0, bit 4 of each word
+    assert k[848 + 0] == 0
+    assert k[848 + 4] == 0b10000
+    assert k[848 + 8] == 0b10000
+    assert k[848 + 12] == 0b10000
     assert (k[1024 + 6], k[1025 + 6]) == (0x00, 0x40)
     assert (k[1056 + 6], k[1057 + 6]) == (0x00, 0xB8)
-    assert int(np.count_nonzero(k)) == 5
+    assert int(np.count_nonzero(k)) == 8
     v = P.pack_v_page(codes, n16)
     # coordinate 9's 16-bit word holds token 3 at bit 3
     assert v[0 * 256 + 2 * 9] == 0b1000 and v[0 * 256 + 2 * 9 + 1] == 0
     assert v[2 * 256 + 2 * 9] == 0b1000
     assert v[1 * 256 + 2 * 9] == 0
+    # coordinate 100's word holds token 5 at bit 5 (planes 1 and 2)
+    assert v[1 * 256 + 2 * 100] == 0b100000 and v[2 * 256 + 2 * 100] == 0b100000
+    assert v[0 * 256 + 2 * 100] == 0
     assert (v[768 + 6], v[769 + 6]) == (0x00, 0x40)
-    assert int(np.count_nonzero(v)) == 3
+    assert int(np.count_nonzero(v)) == 5
 
 
 def test_round_trips():
