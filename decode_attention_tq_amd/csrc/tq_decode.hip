@@ -85,16 +85,15 @@ __device__ __forceinline__ int bal_ranges(const DecodeArgs &a, int t0, int p) {
 __device__ __forceinline__ int bal_per(const DecodeArgs &a, int t0) {
   if (a.bal_per > 0) return a.bal_per;
   if (a.num_seqs <= 64) {
-    // lane l < 16 tries p = 4 (l + 1): its ranges over all groups; the
-    // smallest p that fits wins
+    // lane = sequence: try p = 4, 8, ... in turn (a short chain: the
+    // filling count is usually met within a few steps)
     const int lane = threadIdx.x & 63;
-    const int p = 4 * (min(lane, 15) + 1);
-    const float rp = 1.0f / (float)p;
-    int tot = 0;
-    for (int b = 0; b < a.num_seqs; ++b)  // uniform
-      tot += ceil_div_small(__builtin_amdgcn_readlane(t0, b), p, rp);
-    const uint64_t fit = __ballot(lane < 16 && p >= a.bal_min && tot * a.num_kv_heads <= a.bal_target);
-    return fit ? 4 * (__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)fit) - 1) + 1) : 64;
+    for (int p = max(4, (a.bal_min + 3) & ~3); p < 64; p += 4) {  // uniform
+      const int k = (t0 + p - 1) / p;  // t0 = 0 past the last sequence
+      const int tot = __builtin_amdgcn_readlane(wave_incl_scan_int(k, lane), 63);
+      if (tot * a.num_kv_heads <= a.bal_target) return p;
+    }
+    return 64;
   }
   int lo = (a.bal_min + 3) >> 2, hi = 16;  // p = 4 m
   while (lo < hi) {  // uniform
@@ -724,6 +723,45 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
     L.qh[wave][sl] = hi;
     L.ql[wave][sl] = (_Float16)(x[j] - (float)hi);
   }
+  // wave w: the digits of head w.  Planes 0..3 need only the wave's own q'
+  // (LDS operations of a wave complete in order), so they are formed before
+  // the first barrier; plane 4 waits for the projection.
+  float beta[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
+  const float cs = a.scale * kLog2e;
+  // Y = rint(x 2^(19-E)) = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16
+  auto digits = [&](int p, int kap, float x, int pe) __attribute__((always_inline)) {
+    const bool pz = pe != INT_MIN;
+    const float f = b_split_factor(kap);
+    const float y = pz ? rintf(ldexpf(x, 19 - (pz ? pe : 0))) : 0.0f;
+    const float d0 = rintf(y * 0x1p-15f);
+    float rem = y - d0 * 32768.0f;
+    const float d1 = rintf(rem * 0x1p-10f);
+    rem -= d1 * 1024.0f;
+    const float d2 = rintf(rem * 0.03125f);
+    const float d3 = rem - d2 * 32.0f;
+    L.codes[wave][p][0][kap] = (_Float16)(d0 * f);
+    L.codes[wave][p][1][kap] = (_Float16)(d1 * f);
+    L.codes[wave][p][2][kap] = (_Float16)(d2 * f);
+    L.codes[wave][p][3][kap] = (_Float16)(d3 * f);
+  };
+  {
+    int pe[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float M = cs * fabsf(beta[p]) * hq;
+      pe[p] = M > 0.0f ? max(bound_exponent(M), -100) : INT_MIN;
+    }
+    if (lane < 4) L.pe[wave][lane] = lane == 0 ? pe[0] : lane == 1 ? pe[1] : lane == 2 ? pe[2] : pe[3];
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+      const int kap = lane + 64 * hk;
+      const float qv = L.qr[wave][b_coord(kap)];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) digits(p, kap, -cs * beta[p] * qv, pe[p]);
+    }
+  }
   lds_barrier();
   if constexpr (PROJ) {
     // s = alpha (S H) q' for rows 32 w .. 32 w + 31, all heads: three f16
@@ -757,41 +795,15 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
       }
   }
   lds_barrier();
-  const float hs = wave_max(fmaxf(fabsf(L.sv[wave][lane]), fabsf(L.sv[wave][lane + 64])));
-  // wave w: the digits of head w
-  float beta[4];
+  {
+    const float hs = wave_max(fmaxf(fabsf(L.sv[wave][lane]), fabsf(L.sv[wave][lane + 64])));
+    const float M = cs * hs;
+    const int pe4 = M > 0.0f ? max(bound_exponent(M), -100) : INT_MIN;
+    if (lane == 4) L.pe[wave][4] = pe4;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) beta[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.beta[p])));
-  const float cs = a.scale * kLog2e;
-  int pe[5];
-#pragma unroll
-  for (int p = 0; p < 5; ++p) {
-    const float M = cs * (p < 4 ? fabsf(beta[p]) * hq : hs);
-    pe[p] = M > 0.0f ? max(bound_exponent(M), -100) : INT_MIN;
-  }
-  if (lane < 5) L.pe[wave][lane] = lane == 0 ? pe[0] : lane == 1 ? pe[1] : lane == 2 ? pe[2] : lane == 3 ? pe[3] : pe[4];
-#pragma unroll
-  for (int hk = 0; hk < 2; ++hk) {
-    const int kap = lane + 64 * hk, bc = b_coord(kap);
-    const float f = b_split_factor(kap);
-    const float qv = L.qr[wave][bc], sv = L.sv[wave][bc];
-#pragma unroll
-    for (int p = 0; p < 5; ++p) {
-      const bool pz = pe[p] != INT_MIN;
-      const int E = pz ? pe[p] : 0;
-      const float x = p < 4 ? -cs * beta[p] * qv : -cs * sv;
-      // Y = rint(x 2^(19-E)) = d0 2^15 + d1 2^10 + d2 2^5 + d3, |d_r| <= 16
-      const float y = pz ? rintf(ldexpf(x, 19 - E)) : 0.0f;
-      const float d0 = rintf(y * 0x1p-15f);
-      float rem = y - d0 * 32768.0f;
-      const float d1 = rintf(rem * 0x1p-10f);
-      rem -= d1 * 1024.0f;
-      const float d2 = rintf(rem * 0.03125f);
-      const float d3 = rem - d2 * 32.0f;
-      L.codes[wave][p][0][kap] = (_Float16)(d0 * f);
-      L.codes[wave][p][1][kap] = (_Float16)(d1 * f);
-      L.codes[wave][p][2][kap] = (_Float16)(d2 * f);
-      L.codes[wave][p][3][kap] = (_Float16)(d3 * f);
+    for (int hk = 0; hk < 2; ++hk) {
+      const int kap = lane + 64 * hk;
+      digits(4, kap, -cs * L.sv[wave][b_coord(kap)], pe4);
     }
   }
   lds_barrier();
