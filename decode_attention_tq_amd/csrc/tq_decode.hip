@@ -180,8 +180,12 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
 }
 
 // ---- 2. split pass (vector ALU) --------------------------------------------
+// G is the capacity (1, 2, 4, 8 or 16 heads); the call's group size
+// (a.group <= G) indexes the rows, the heads past it score zero queries and
+// write nothing.
 template <int G>
 __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
+  const int Gr = a.group;
   const int bt = blockIdx.x;  // b * q_len + t
   const int h = blockIdx.y;
   const int split = blockIdx.z;
@@ -201,10 +205,10 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
   float *sq = smem + G * 128;
   float *pn = smem + G * 256;
 
-  const int64_t row0 = (int64_t)bt * a.num_q_heads + (int64_t)h * G;
+  const int64_t row0 = (int64_t)bt * a.num_q_heads + (int64_t)h * Gr;
   for (int idx = tid; idx < G * 256; idx += 256) {
     const int g = idx >> 8, c = idx & 255;
-    const float v = a.qprep[(row0 + g) * 256 + c];
+    const float v = g < Gr ? a.qprep[(row0 + g) * 256 + c] : 0.0f;
     if (c < 128) qp[g * 128 + c] = v; else sq[g * 128 + c - 128] = v;
   }
   if (tid < 8) {
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
     red[(wave * G + g) * 128 + lane + 64] = acc1[g];
   }
   lds_barrier();
-  for (int idx = tid; idx < G * 128; idx += 256) {
+  for (int idx = tid; idx < Gr * 128; idx += 256) {
     const int g = idx >> 7, d = idx & 127;
     float M = red_m[0][g];
 #pragma unroll
@@ -1995,8 +1999,10 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t hb) {
   return DT == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hb) : __uint_as_float(hb << 16);
 }
 
+// G is the capacity (1, 2, 4, 8 or 16 heads), a.group <= G the group size.
 template <int G, int DT>
 __global__ __launch_bounds__(kHotChunk) void hot_window_kernel(DecodeArgs a) {
+  const int Gr = a.group;
   __shared__ __align__(16) float qs[G][kHeadDim];   // q * scale * log2(e)
   __shared__ __align__(16) float ps[G][kHotChunk];  // p of each token
   constexpr int NW = kHotChunk / 64;  // waves: one token per thread
@@ -2011,10 +2017,11 @@ __global__ __launch_bounds__(kHotChunk) void hot_window_kernel(DecodeArgs a) {
   const int W = min(max(a.hot_lens[b], 0), a.hot_max);
   const int j0 = c * kHotChunk;
   const int n = max(0, min(W - j0, kHotChunk));  // uniform: tokens of this chunk
-  const int64_t row0 = (int64_t)b * a.num_q_heads + h * G;  // output rows (q_len 1)
+  const int64_t row0 = (int64_t)b * a.num_q_heads + h * Gr;  // output rows (q_len 1)
   const float qscale = a.scale * kLog2e;
   for (int i = tid; i < G * kHeadDim; i += kHotChunk)
-    qs[i / kHeadDim][i % kHeadDim] = qscale * load_as_float(a.q, a.q_dtype, row0 * kHeadDim + i);
+    qs[i / kHeadDim][i % kHeadDim] =
+        i < Gr * kHeadDim ? qscale * load_as_float(a.q, a.q_dtype, row0 * kHeadDim + i) : 0.0f;
   lds_barrier();
   // scores: thread t, token j0 + t (past the chunk's end: its last token)
   float sc[G];
@@ -2125,7 +2132,7 @@ __global__ __launch_bounds__(kHotChunk) void hot_window_kernel(DecodeArgs a) {
   } else {
     ns = (clamped_context(a, b) + a.split_tokens - 1) / a.split_tokens;
   }
-  for (int g = wave; g < G; g += NW) {  // uniform
+  for (int g = wave; g < Gr; g += NW) {  // uniform
     float o0 = 0.0f, o1 = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -2298,6 +2305,10 @@ hipError_t noalloc_scratch(void **ptr) {
   return hipSuccess;
 }
 
+// Kernels templated on the group size are built for 1, 2, 4, 8 and 16
+// heads; another size runs on the next one up.
+static int group_capacity(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : g <= 16 ? 16 : 0; }
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.q_len * a.num_q_heads;
   const unsigned row_blocks = (unsigned)((rows + 3) / 4);
@@ -2326,7 +2337,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (prefill_uses_mfma(a.q_len, a.group)) {
       e = launch_prefill(a, stream);
     } else {
-      switch (a.group) {
+      switch (group_capacity(a.group)) {
         case 1: e = launch_split<1>(a, stream); break;
         case 2: e = launch_split<2>(a, stream); break;
         case 4: e = launch_split<4>(a, stream); break;
@@ -2341,7 +2352,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if (a.hot_parts > 0) {  // the exact window's records
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.hot_parts));
-    switch (a.group) {
+    switch (group_capacity(a.group)) {
       case 1: launch_hot<1>(a, grid, stream); break;
       case 2: launch_hot<2>(a, grid, stream); break;
       case 4: launch_hot<4>(a, grid, stream); break;

@@ -427,8 +427,6 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
                 num_q_heads, num_kv_heads);
   const int group = num_q_heads / num_kv_heads;
   if (group > tq::kMaxGroup) return fail(TQ_ERR_UNSUPPORTED, "more than %d query heads per KV head", tq::kMaxGroup);
-  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
-    return fail(TQ_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8 or 16 (got %d)", group);
   if (max_context_len < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "max_context_len < 0");
   if (q_len > 1 && q_len > max_context_len)
     return fail(TQ_ERR_INVALID_ARGUMENT, "q_len (%d) > max_context_len (%d)", q_len, max_context_len);

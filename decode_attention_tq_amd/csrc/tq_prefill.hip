@@ -156,9 +156,11 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
   }
 }
 
-template <int G>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a) {
-  constexpr int BQ = kRows / G;  // query positions per workgroup
+  // G query heads per KV head (any of 1 .. 16): BQ whole positions per
+  // workgroup, rows past BQ G unused
+  const int G = a.group;
+  const int BQ = kRows / G;  // query positions per workgroup
   const int qblocks = (a.q_len + BQ - 1) / BQ;
   const int b = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
   const int h = blockIdx.y, split = blockIdx.z;
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
   for (int u = 0; u < kRowTiles; ++u) {
     const int rw = 16 * (kRowTiles * wave + u) + l16;
     const int t = t0 + rw / G, hq = h * G + rw % G;
-    row_ok[u] = t < a.q_len;
+    row_ok[u] = t < a.q_len && rw < BQ * G;
     R[u] = ((int64_t)b * a.q_len + min(t, a.q_len - 1)) * a.num_q_heads + hq;
     lim[u] = L - a.q_len + t;  // last visible key of the row
   }
@@ -412,8 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
 }  // namespace
 
 bool prefill_uses_mfma(int q_len, int group) {
-  return q_len > 1 && !decode_uses_mfma(q_len, group) &&
-         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+  return q_len > 1 && !decode_uses_mfma(q_len, group) && group >= 1 && group <= kMaxGroup;
 }
 
 int prefill_block_queries(int group) { return kRows / group; }
@@ -422,14 +423,8 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
   const int bq = kRows / a.group;
   const int qblocks = (a.q_len + bq - 1) / bq;
   dim3 grid((unsigned)(a.num_seqs * qblocks), (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
-  switch (a.group) {
-    case 1: hipLaunchKernelGGL(prefill_mfma_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(prefill_mfma_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(prefill_mfma_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(prefill_mfma_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL(prefill_mfma_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (a.group < 1 || a.group > kMaxGroup) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -328,6 +328,44 @@ def test_prefill_groups_batches_and_splits(Hq, Hkv):
     assert np.abs(outs[0] - outs[1]).max() <= 1e-4 * max(1.0, np.abs(outs[0]).max())
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(12, 4), (15, 3), (24, 4), (28, 4), (24, 2)])
+def test_any_group_size(Hq, Hkv):
+    """Group sizes that are not powers of two (3, 5, 6, 7 and 12 query heads
+    per KV head, e.g. 28q/4kv): single-query decode (matrix-core pass for up
+    to 8 heads, vector pass above), a 3-token verify block, a 21-token
+    chunked prefill block and the exact hot window, each against the oracle
+    on two ragged sequences."""
+    G = Hq // Hkv
+    rng = np.random.default_rng(60 + G)
+    lens = np.array([700, 2300], dtype=np.int64)
+    table, nb = synth.block_tables(rng, lens)
+    cb = codebook()
+    kpool, vpool = new_pools(nb, Hkv)
+    for b in range(len(lens)):
+        k = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        v = synth.kv_tensor(rng, int(lens[b]), Hkv)
+        encode_gpu(cb, k, v, synth.slots_for(table, b, np.arange(lens[b])), kpool, vpool, with_norms=False)
+    kp, vp = _np(kpool), _np(vpool)
+    cl = lens.astype(np.int32)
+    for q_len in (1, 3, 21):
+        q = synth.queries(rng, len(lens), q_len, Hq)
+        out = decode_gpu(cb, q, kpool, vpool, table, cl, Hkv)
+        err = check_decode(out, q, kp, vp, table, cl)
+        print("G", G, "q_len", q_len, "max rel err", err.max())
+    W, hot_max = np.array([77, 300], dtype=np.int32), 300
+    hk = torch.from_numpy(synth.kv_tensor(rng, 2 * hot_max, Hkv).reshape(2, hot_max, Hkv, 128)).to(torch.bfloat16)
+    hv = torch.from_numpy(synth.kv_tensor(rng, 2 * hot_max, Hkv).reshape(2, hot_max, Hkv, 128)).to(torch.bfloat16)
+    q = synth.queries(rng, len(lens), 1, Hq)
+    out = tq.tq_decode_attention_hot(
+        cb, dev(q, torch.bfloat16), kpool, vpool, torch.from_numpy(table).cuda(), torch.from_numpy(cl).cuda(),
+        int(lens.max()), Hkv, hk.cuda(), hv.cuda(), torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    c32, _, S = oracle_tables()
+    ref = decode_paged_hot(np.asarray(q, np.float64), kp, vp, table, lens, hk.double().numpy(), hv.double().numpy(),
+                           W, c32, S)
+    assert_rows_close(out.float().cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("Hq,Hkv,hot_dtype", [(32, 8, torch.bfloat16), (16, 16, torch.float16),
                                              (32, 4, torch.float32), (32, 2, torch.bfloat16)])
 def test_hot_window(Hq, Hkv, hot_dtype):

@@ -126,7 +126,7 @@ def test_decode_validation():
     assert _dec(cb, Hq=30, Hkv=8) == E
     assert "multiple" in tq.tq_last_error()
     assert _dec(cb, Hq=64, Hkv=2) == tq.TQ_ERR_UNSUPPORTED      # 32 heads per KV head
-    assert _dec(cb, Hq=24, Hkv=8) == tq.TQ_ERR_UNSUPPORTED      # group of 3
+    assert _dec(cb, Hq=34, Hkv=2) == tq.TQ_ERR_UNSUPPORTED      # 17 heads per KV head
     assert _dec(cb, maxc=-1) == E
     assert _dec(cb, q_len=8, maxc=4, mb=1) == E                  # more queries than context
     assert _dec(cb, mb=63) == E                                  # 63 blocks < 1024 tokens
@@ -224,7 +224,7 @@ def test_hot_window_validation():
     E = tq.TQ_ERR_INVALID_ARGUMENT
     assert _hot(_fake_cb(False)) == tq.TQ_ERR_NOT_INITIALIZED
     assert _hot(cb, q=None) == E                                  # the plain call's checks
-    assert _hot(cb, Hq=24, Hkv=8) == tq.TQ_ERR_UNSUPPORTED
+    assert _hot(cb, Hq=34, Hkv=2) == tq.TQ_ERR_UNSUPPORTED       # 17 heads per KV head
     assert _hot(cb, hmax=-1) == E
     assert _hot(cb, hk=None) == E
     assert _hot(cb, hl=None) == E
