@@ -29,7 +29,8 @@ from .encode import encode_k, encode_v, quantize_codes
 from .pages import (K_PAGE_BYTES, V_PAGE_BYTES, BLOCK, pack_k_page, pack_v_page,
                     unpack_k_page, unpack_v_page, write_slots, read_k_tokens,
                     read_v_tokens)
-from .attention import (dequant_k, dequant_v, attention_dense, decode_paged, decode_paged_hot)
+from .attention import (dequant_k, dequant_v, attention_dense, decode_paged, decode_paged_hot,
+                        ring_row, decode_paged_window)
 
 __all__ = [
     "lloyd_max_gaussian", "codebook_fp32",
@@ -39,5 +40,6 @@ __all__ = [
     "K_PAGE_BYTES", "V_PAGE_BYTES", "BLOCK", "pack_k_page", "pack_v_page",
     "unpack_k_page", "unpack_v_page", "write_slots", "read_k_tokens",
     "read_v_tokens",
-    "dequant_k", "dequant_v", "attention_dense", "decode_paged",
+    "dequant_k", "dequant_v", "attention_dense", "decode_paged", "decode_paged_hot",
+    "ring_row", "decode_paged_window",
 ]

@@ -38,7 +38,7 @@ import math
 import numpy as np
 
 from .hadamard import sylvester_hadamard
-from .pages import read_k_tokens_fast, read_v_tokens_fast
+from .pages import BLOCK, read_k_tokens_fast, read_v_tokens_fast
 from .qjl import qjl_alpha
 
 
@@ -146,3 +146,58 @@ def decode_paged_hot(q, k_pool, v_pool, block_tables, context_lens, hot_k, hot_v
                     hq = h * G + g
                     out[b, t, hq] = attention_dense(q[b, t, hq], keys[:vis], vals[:vis], scale)
     return out
+
+
+def ring_row(block_row, length: int) -> np.ndarray:
+    """Block-table entries of logical pages 0 .. ceil(length / 16) - 1 when
+    the row is a ring of ``len(block_row)`` pages: page P sits in entry
+    P mod len(block_row), so a page is reused for the positions 16 R later."""
+    row = np.asarray(block_row)
+    nb = (length + BLOCK - 1) // BLOCK
+    return row[np.arange(nb) % len(row)]
+
+
+def decode_paged_window(q, k_pool, v_pool, block_tables, context_lens, window: int,
+                        centroids_f32, S_f32, scale: float | None = None, kv_heads=None,
+                        seqs=None, q_positions=None) -> np.ndarray:
+    """Sliding-window attention of ``q[B][q_len][Hq][d]`` over a rotating
+    paged cache.
+
+    The SwiftLM README ("Performance: Mac mini M6", the correction under its
+    tables and the --turbo-kv recall note) says sliding-window layers run on
+    a rotating cache (Gemma 4: 1,024-token window on 25 of 30 layers) that
+    keeps only the most recent tokens.  Reading taken: query t of sequence b
+    sits at position p = L - q_len + t and attends to the keys at positions
+    max(0, p - window + 1) .. p (its own and the window - 1 before it); the
+    cache keeps them in a ring of R = len(block_tables[b]) pages, position j
+    in page ``block_tables[b][(j // 16) mod R]`` at offset j % 16.
+
+    Returns float64 ``[B][q_len][Hq][d]``; rows outside the optional subsets
+    are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, q_len, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full(q.shape, np.nan)
+    seqs = range(B) if seqs is None else seqs
+    kv_heads = range(Hkv) if kv_heads is None else kv_heads
+    q_positions = range(q_len) if q_positions is None else q_positions
+    for b in seqs:
+        L = int(context_lens[b])
+        row = ring_row(block_tables[b], L)
+        for h in kv_heads:
+            kc, ks, kn, kg = read_k_tokens_fast(k_pool, row, L, h)
+            vc, vn = read_v_tokens_fast(v_pool, row, L, h)
+            keys = dequant_k(kc, ks, kn, kg, centroids_f32, S_f32)
+            vals = dequant_v(vc, vn, centroids_f32)
+            for t in q_positions:
+                hi = max(0, L - q_len + t + 1)
+                lo = max(0, hi - window)
+                for g in range(G):
+                    hq = h * G + g
+                    out[b, t, hq] = attention_dense(q[b, t, hq], keys[lo:hi], vals[lo:hi], scale)
+    return out
+
