@@ -44,7 +44,8 @@ EXPORTED = [
     "tq_codebook_compute", "tq_qjl_matrix", "tq_codebook_device_bytes", "tq_codebook_init",
     "tq_k_page_bytes", "tq_v_page_bytes", "tq_encode_kv", "tq_decode_workspace_bytes",
     "tq_decode_attention", "tq_decode_hot_workspace_bytes", "tq_decode_attention_hot",
-    "tq_decode_noalloc_scratch_bytes", "tq_decode_attention_noalloc", "tq_last_error",
+    "tq_decode_noalloc_scratch_bytes", "tq_decode_attention_noalloc",
+    "tq_decode_window_workspace_bytes", "tq_decode_attention_window", "tq_last_error",
 ]
 
 
@@ -89,6 +90,11 @@ _lib.tq_decode_noalloc_scratch_bytes.argtypes = []
 _lib.tq_decode_attention_noalloc.restype = _I
 _lib.tq_decode_attention_noalloc.argtypes = [_CB, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                              ctypes.c_float, _P, _I, _I, _P]
+_lib.tq_decode_window_workspace_bytes.restype = _SZ
+_lib.tq_decode_window_workspace_bytes.argtypes = [_CB, _I, _I, _I, _I, _I, _I, _I]
+_lib.tq_decode_attention_window.restype = _I
+_lib.tq_decode_attention_window.argtypes = [_CB, _P, _I, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I,
+                                            ctypes.c_float, _P, _I, _I, _P, _SZ, _P]
 _lib.tq_decode_hot_workspace_bytes.restype = _SZ
 _lib.tq_decode_hot_workspace_bytes.argtypes = [_CB, _I, _I, _I, _I, _I, _I]
 _lib.tq_decode_attention_hot.restype = _I
@@ -319,6 +325,47 @@ def tq_decode_attention_noalloc(cb: Codebook, q, k_cache, v_cache, block_tables,
         block_tables.shape[1], _ptr(context_lens), B, q_len, Hq, num_kv_heads,
         max_context_len, float(softmax_scale), _ptr(out), _dtype_code(out), tokens_per_split,
         _stream(stream, q.device)))
+    return out
+
+
+def tq_decode_window_workspace_bytes(cb: Codebook, num_seqs: int, q_len: int, num_q_heads: int,
+                                     num_kv_heads: int, max_context_len: int, window: int,
+                                     tokens_per_split: int = 0) -> int:
+    return int(_lib.tq_decode_window_workspace_bytes(cb.ref, num_seqs, q_len, num_q_heads, num_kv_heads,
+                                                     max_context_len, window, tokens_per_split))
+
+
+def tq_decode_attention_window(cb: Codebook, q, k_cache, v_cache, block_tables, context_lens,
+                               max_context_len: int, num_kv_heads: int, window: int, out=None,
+                               softmax_scale: float = 0.0, tokens_per_split: int = 0,
+                               workspace=None, out_dtype=None, stream=None):
+    """Sliding-window decode over a rotating cache: query t of sequence b sees
+    the last ``window`` positions up to its own; ``block_tables`` row b
+    (int32 [B][ring_blocks]) is a ring, position j in page
+    ``block_tables[b][(j // 16) % ring_blocks]``.  Returns ``out``."""
+    torch = _torch()
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][q_len][Hq][128] tensor")
+    if block_tables.dtype != torch.int32 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32")
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32")
+    B, q_len, Hq, _ = q.shape
+    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_seq_tables(block_tables, context_lens, B)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape:
+        raise ValueError("out must be contiguous with q's shape")
+    need = tq_decode_window_workspace_bytes(cb, B, q_len, Hq, num_kv_heads, max_context_len, window,
+                                            tokens_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    _check(_lib.tq_decode_attention_window(
+        cb.ref, _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, q_len, Hq, num_kv_heads, max_context_len, int(window),
+        float(softmax_scale), _ptr(out), _dtype_code(out), tokens_per_split,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
     return out
 
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "tq_internal.h"
@@ -24,6 +25,24 @@ __device__ __forceinline__ void lds_barrier() {
 // access leaves the block table or the partials.
 __device__ __forceinline__ int clamped_context(const DecodeArgs &a, int b) {
   return min(max(a.context_lens[b], 0), a.ctx_cap);
+}
+
+// Sliding window over a rotating cache: the first page-aligned position any
+// query of the call can see (the oldest key of its first query, rounded down
+// to its page); every pass walks sequence b's keys from there to its end.
+// Without a window the walk starts at 0.
+__device__ __forceinline__ int seq_base(const DecodeArgs &a, int L) {
+  return a.window > 0 ? (max(0, L - a.q_len - a.window + 1) & ~15) : 0;
+}
+// Block-table entry of logical page P: with a window the row is a ring of
+// max_blocks pages, so position p sits in entry (p / 16) mod max_blocks.
+__device__ __forceinline__ int page_entry(const DecodeArgs &a, int P) {
+  return a.window > 0 ? (int)((unsigned)P % (unsigned)a.max_blocks) : P;
+}
+// Lower end (inclusive) of the keys a query sees, given its exclusive upper
+// end `lim`: lim - window with a window, else none.
+__device__ __forceinline__ int window_low(const DecodeArgs &a, int lim) {
+  return a.window > 0 ? lim - a.window : INT_MIN;
 }
 
 __device__ __forceinline__ float load_as_float(const void *p, int dtype, int64_t i) {

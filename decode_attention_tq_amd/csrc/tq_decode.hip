@@ -66,7 +66,9 @@ __device__ __forceinline__ int ceil_div_small(int T, int p, float rp) {
   return q + (r > 0 ? 1 : 0);
 }
 __device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int s) {
-  return s < a.num_seqs ? (clamped_context(a, s) + 127) >> 7 : 0;
+  if (s >= a.num_seqs) return 0;
+  const int L = clamped_context(a, s);
+  return (L - seq_base(a, L) + 127) >> 7;
 }
 // The tile counts of sequences c0 + lane: for up to 64 sequences they are
 // read once (t0, loaded by the caller at its start) and every later step
@@ -192,7 +194,8 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
   const int b = bt / a.q_len, t = bt % a.q_len;
   const int L = clamped_context(a, b);
   const int vis = max(0, L - a.q_len + t + 1);
-  const int s0 = split * a.split_tokens;
+  const int lo = window_low(a, vis);  // keys before lo are outside the window
+  const int s0 = seq_base(a, L) + split * a.split_tokens;
   const int s1 = min(s0 + a.split_tokens, vis);
   if (s0 >= s1) return;  // uniform: this chunk holds no visible key
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -242,11 +245,11 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
     const int cbase = s0 + c * 64;
     // scores: one key per lane
     const int j = cbase + lane;
-    const bool valid = (c < nchunks) && (j < s1);
+    const bool valid = (c < nchunks) && (j < s1) && (j >= lo);
     float score[G];
     float nv = 0.0f;
     if (valid) {
-      const int64_t page = (int64_t)btab[j >> 4] * a.num_kv_heads + h;
+      const int64_t page = (int64_t)btab[page_entry(a, j >> 4)] * a.num_kv_heads + h;
       const int o = j & 15;
       const uint8_t *kp = a.k_cache + page * kKPage;
       // record of coordinate chunk g: code planes 0..2 and signs of 32 coordinates
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
       for (int pg = 0; pg < 4; ++pg) {
         const int tok0 = cbase + pg * 16;
         if (tok0 >= s1) break;
-        const uint8_t *vp = a.v_cache + ((int64_t)btab[tok0 >> 4] * a.num_kv_heads + h) * kVPage;
+        const uint8_t *vp = a.v_cache + ((int64_t)btab[page_entry(a, tok0 >> 4)] * a.num_kv_heads + h) * kVPage;
         const uint32_t a0 = *reinterpret_cast<const uint16_t *>(vp + 2 * lane);
         const uint32_t a1 = *reinterpret_cast<const uint16_t *>(vp + kVPlane + 2 * lane);
         const uint32_t a2 = *reinterpret_cast<const uint16_t *>(vp + 2 * kVPlane + 2 * lane);
@@ -842,401 +845,6 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
 }
 
 
-template <int T, int R>
-__device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, SplitLds<T> &sm, int b, int h,
-                                                          int split, int s0, int s1) {
-  constexpr int NW = 4 * T;   // waves
-  constexpr int NJ = 2 / T;   // value N-tiles (16 coordinates) per wave
-  const int L = clamped_context(a, b);
-  // query rows (positions x heads); every row sees the keys before s1v, row
-  // r those before min(s1, L - q_len + pos0 + r / G + 1)
-  const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count;
-  const int s1v = min(s1, L - qlen + 1);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int su = wave >> 2, sq = wave & 3;  // scoring: head tile, page pair (K-block)
-  const int t16 = lane & 15, grow = lane >> 4;
-  const int64_t grp = (int64_t)b * a.num_kv_heads + h;
-  const int G = a.group;
-  const int ntiles = min((s1 - s0 + 127) >> 7, kMaxSplitTiles);  // the host caps chunks at 64 tiles
-
-  // block ids of the chunk's pages; a page past the visible range re-reads
-  // its tile's first page (always visible; its tokens are masked)
-  {
-    const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
-    for (int idx = tid; idx < ntiles * kTilePages; idx += 64 * NW) {
-      const int tile0 = s0 + 128 * (idx >> 3);
-      const int tok = tile0 + 16 * (idx & 7);
-      sm.ids[idx >> 3][idx & 7] = btab[(tok < s1 ? tok : tile0) >> 4];
-    }
-  }
-
-  // query-side operands of the score contraction (head tile su), formed in
-  // the prologue; their loads go out first
-  QPrepRegs<true> qpr;
-  qprep_loads<true>(a, grp, wave, lane, qpr);
-  v8i AqT[1][5];
-  int scqT[1][5];
-  v4f ciT[1], qiT[1];
-  v8i (&Aq)[5] = AqT[0];
-  int (&scq)[5] = scqT[0];
-  v4f &cinit = ciT[0], &qinit = qiT[0];  // accumulator start values (see b_split)
-  float beta[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) beta[p] = uniform(a.cb.beta[p]);
-  const BSplitK bk = bsplit_consts();
-  const uint32_t nib = in_vgpr(0x000F000Fu);
-  // sign (f16 sign bit) of the digits of K slots held by b_split registers
-  // 0..2: the lane's token t sits in register t & 3
-  const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80008000u);
-  const int kap0 = 8 * (t16 & 3) + (t16 >> 2);  // K slot of token t16 of the pair's first page
-  const StagePtrs sp{a.k_cache, a.v_cache, (int64_t)a.num_kv_heads, h, sq, 16u * (uint32_t)lane,
-                     16u * (uint32_t)(lane % 48), 4u * (uint32_t)t16, 4u * (uint32_t)(lane & 7)};
-  auto pair_ids = [&](int k, int &b0, int &b1) __attribute__((always_inline)) {
-    const int2 v = *reinterpret_cast<const int2 *>(&sm.ids[k][2 * sq]);
-    b0 = __builtin_amdgcn_readfirstlane(v.x);
-    b1 = __builtin_amdgcn_readfirstlane(v.y);
-  };
-
-  // scoring state (lane: head grow of tile su, token t16)
-  float rl = -INFINITY;  // reference R of the lane's head
-  float lsum = 0.0f;     // sum of p relative to rl
-  // value state (lane: A row (head gA, digit rA), K-block kb; C rows head grow)
-  const int gA = t16 >> 2, rA = lane & 3, kb = grow;
-  // Racc per head tile, in two per-lane copies: of head gA (A rows) and of
-  // head grow (C rows); both follow the same rule on the same statistics
-  float raA[T], raC[T];
-  v4f acc[T][4][NJ];
-  v4f corr[T];
-#pragma unroll
-  for (int u = 0; u < T; ++u) {
-    corr[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    raA[u] = raC[u] = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[u][p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  // E8M0 scales of the weight rows of the tile whose statistics are in
-  // buffer bf, after moving Racc of every head whose block reference
-  // exceeds it by 2^64 (rare: first tile, large score jumps).
-  auto value_scales = [&](int bf, int (&sw)[T]) __attribute__((always_inline)) {
-    int2 st[T];
-    bool move = false;
-#pragma unroll
-    for (int u = 0; u < T; ++u) {
-      st[u] = sm.stats[bf][u][gA][kb];
-      move |= __int_as_float(st[u].y) > raA[u] + (float)kRefStep;
-    }
-    if (__builtin_amdgcn_ballot_w64(move)) {
-#pragma unroll
-      for (int u = 0; u < T; ++u) {
-        float MA = -INFINITY, MC = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          MA = fmaxf(MA, __int_as_float(sm.stats[bf][u][gA][q].y));
-          MC = fmaxf(MC, __int_as_float(sm.stats[bf][u][grow][q].y));
-        }
-        if (MA > raA[u] + (float)kRefStep) raA[u] = MA;
-        float fc = 1.0f;
-        if (MC > raC[u] + (float)kRefStep) {
-          fc = raC[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(raC[u] - MC);
-          raC[u] = MC;
-        }
-        corr[u] *= fc;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[u][p][j] *= fc;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < T; ++u) {
-      const float d = fmaxf(__int_as_float(st[u].y) - raA[u], -300.0f);  // NaN (both -inf) -> -300
-      sw[u] = min(max(st[u].x + 1 - 4 * rA + (int)d, 0), 254);  // E8M0 of 2^(ex-126-4r+R-Racc)
-    }
-  };
-
-  // One barrier interval, for tile k of parity PAR: copy the K part of tile
-  // k+1 (set SK) and the V part of tile k (set SV) to LDS and fetch the K
-  // part of tile k+3 and the V part of tile k+2 into the same sets; then the
-  // scores of tile k and the value contraction of tile k-1 (without scores:
-  // the value contraction of tile k).  The LDS reads, operand expansions and
-  // all matrix ops of both contractions form one block for the scheduler to
-  // interleave; the rare reference moves sit outside it.
-  auto interval = [&](auto HS, auto HV, auto PAR, StageSet<R> &SK, StageSet<R> &SV, int k)
-                      __attribute__((always_inline)) {
-    constexpr bool has_s = decltype(HS)::value, has_v = decltype(HV)::value;
-    constexpr int par = decltype(PAR)::value;
-    constexpr int bs = par, bv = has_s ? (par ^ 1) : par;
-    const int kv = has_s ? k - 1 : k;
-    int sw[T];
-    if constexpr (has_v) value_scales(bv, sw);
-    if constexpr (has_s) {
-      // unconditional copies and fetches (past the chunk's end they repeat its
-      // last tile from L2), so that the counts of outstanding loads are static
-      int k3a, k3b, k2a, k2b;
-      pair_ids(min(k + 3, ntiles - 1), k3a, k3b);
-      pair_ids(min(k + 2, ntiles - 1), k2a, k2b);
-      store_v_part<R>(sm.vbuf[par], SV, sp, lane);
-      store_k_part<R>(sm.kbuf[par ^ 1], SK, sp, lane);
-      load_k_part<R>(SK, sp, k3a, k3b);
-      load_v_part<R>(SV, sp, k2a, k2b);
-    }
-    // LDS reads
-    uint32_t kw[2][4];
-    uint32_t nrm[2][3];  // half bits: n_k, gamma, n_v
-    if constexpr (has_s) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint8_t *rec = sm.kbuf[bs] + kKRec * (2 * sq + e);
-        const u32x4 kr = *reinterpret_cast<const u32x4 *>(rec + k_record(grow, t16));  // planes 0..2, signs
-        kw[e][0] = kr[0];
-        kw[e][1] = kr[1];
-        kw[e][2] = kr[2];
-        kw[e][3] = kr[3];
-        const uint16_t *nr = reinterpret_cast<const uint16_t *>(rec + 1024);
-        nrm[e][0] = nr[t16];
-        nrm[e][1] = nr[16 + t16];
-        nrm[e][2] = nr[32 + t16];
-      }
-    }
-    v8i Aw[T];
-    uint32_t W[NJ][3];
-    if constexpr (has_v) {
-#pragma unroll
-      for (int u = 0; u < T; ++u) Aw[u] = fp6_operand(&sm.wq[bv][u][4 * gA + rA][32 * kb], 0x1p-21f);  // d 2^-24 -> d/8
-      const uint32_t *vw = reinterpret_cast<const uint32_t *>(sm.vbuf[bv] + kVPair * kb);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int c = 16 * (NJ * wave + j) + t16;
-#pragma unroll
-        for (int p = 0; p < 3; ++p) W[j][p] = vw[128 * p + c];
-      }
-    }
-    // matrix ops
-    v4f cc[2], qq[2];
-    if constexpr (has_s) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t w0 = kw[e][0], w1 = kw[e][1], w2 = kw[e][2], w3 = kw[e][3];
-        v4f c = mfma_f6f4(Aq[0], bsplit(w0, bk), cinit, scq[0]);
-        c = mfma_f6f4(Aq[1], bsplit(w1, bk), c, scq[1]);
-        c = mfma_f6f4(Aq[2], bsplit(w2, bk), c, scq[2]);
-        cc[e] = mfma_f6f4(Aq[3], bsplit(w0 ^ w1 ^ w2, bk), c, scq[3]);
-        qq[e] = mfma_f6f4(Aq[4], bsplit(w3, bk), qinit, scq[4]);
-      }
-    }
-    if constexpr (has_v) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const uint32_t W0 = W[j][0], W1 = W[j][1], W2 = W[j][2];
-        const v8i V0 = bsplit(W0, bk), V1 = bsplit(W1, bk), V2 = bsplit(W2, bk), Vx = bsplit(W0 ^ W1 ^ W2, bk);
-#pragma unroll
-        for (int u = 0; u < T; ++u) {
-          acc[u][0][j] = mfma_f6f4(Aw[u], V0, acc[u][0][j], sw[u]);
-          acc[u][1][j] = mfma_f6f4(Aw[u], V1, acc[u][1][j], sw[u]);
-          acc[u][2][j] = mfma_f6f4(Aw[u], V2, acc[u][2][j], sw[u]);
-          acc[u][3][j] = mfma_f6f4(Aw[u], Vx, acc[u][3][j], sw[u]);
-        }
-      }
-    }
-    // scores of page pair sq for head tile su: weights, digits, statistics.
-    // The common path assumes a full tile and no reference move, so that the
-    // whole interval stays one block; the first tile, the chunk's last
-    // (partial) tile and reference moves redo it at the end.
-    if constexpr (has_s) {
-      float inner[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const v4f &c = cc[e], &q = qq[e];
-        const float code = (c[0] + c[1]) + (c[2] + c[3]);
-        const float qj = (q[0] + q[1]) + (q[2] + q[3]);
-        inner[e] = fmaf(half_lo(nrm[e][1]), qj, code);
-      }
-      const float lsum0 = lsum;
-      auto weights = [&](float x0, float x1, bool v0, bool v1) __attribute__((always_inline)) {
-        const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
-        lsum += p0 + p1;
-        // a slot past the visible range may hold any norm bits
-        const float w0 = v0 ? p0 * half_lo(nrm[0][2]) : 0.0f;
-        const float w1 = v1 ? p1 * half_lo(nrm[1][2]) : 0.0f;
-        const int mk = row_max16_nonneg(max(__float_as_int(w0), __float_as_int(w1)));  // w >= 0
-        const uint32_t exb = max((uint32_t)mk & 0x7F800000u, 14u << 23);
-        const float mult = __uint_as_float(0x86000000u - exb);  // 2^(141 - ex)
-        const uint32_t X0 = __float_as_uint(fmaf(w0, mult, 8388608.0f));
-        const uint32_t X1 = __float_as_uint(fmaf(w1, mult, 8388608.0f));
-        const uint32_t XX = __builtin_amdgcn_perm(X1, X0, 0x05040100u);  // X0 lo16 | X1 lo16 << 16
-        uint16_t *wr = &sm.wq[bs][su][4 * grow][32 * sq + kap0];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {  // digit r (place 16^(3-r)) of both tokens, with the slot's sign
-          const uint32_t D = ((XX >> (12 - 4 * r)) & nib) | s80;
-          wr[r * kWqRow] = (uint16_t)D;
-          wr[r * kWqRow + 4] = (uint16_t)(D >> 16);
-        }
-        // the 16 lanes of a head write the same statistics (no lane branch)
-        sm.stats[bs][su][grow][sq] = make_int2((int)(exb >> 23), __float_as_int(rl));
-      };
-      const float x0 = fmaf(half_lo(nrm[0][0]), inner[0], -rl);
-      const float x1 = fmaf(half_lo(nrm[1][0]), inner[1], -rl);
-      weights(x0, x1, true, true);
-      if constexpr (has_v) {
-        // keep the value matrix ops inside this block (not sunk past the
-        // branch below), where the scheduler overlaps them with the scores
-#pragma unroll
-        for (int u = 0; u < T; ++u)
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[u][p][j]));
-      }
-      const bool partial = s0 + 128 * (k + 1) > s1v;  // uniform: a tile some row does not see whole
-      if (__builtin_amdgcn_ballot_w64(x0 > (float)kRefStep || x1 > (float)kRefStep) || partial) {
-        const int tok0 = s0 + 128 * k + 32 * sq + t16;
-        const int lim = min(s1, L - qlen + (4 * su + grow) / G + 1);  // the lane's row
-        const bool v0 = tok0 < lim, v1 = tok0 + 16 < lim;
-        const float r0 = v0 ? half_lo(nrm[0][0]) * inner[0] : -INFINITY;
-        const float r1 = v1 ? half_lo(nrm[1][0]) * inner[1] : -INFINITY;
-        // move the reference of the heads that need it (first tile, rare after)
-        const float mh = row_max16(fmaxf(r0, r1));
-        const float nr = fmaxf(rl, ceilf(mh));
-        lsum = lsum0;
-        if (nr > rl && nr - rl > 0.0f) {
-          lsum = rl == -INFINITY ? 0.0f : lsum * __builtin_amdgcn_exp2f(rl - nr);
-          rl = nr;
-        }
-        // rl stays -inf while a head has no visible key
-        weights(r0 == -INFINITY ? -INFINITY : r0 - rl, r1 == -INFINITY ? -INFINITY : r1 - rl, v0, v1);
-      }
-    }
-    if constexpr (has_v) {
-      if (kv % NW == wave) {  // uniform: the offsets of b_split, one wave per tile
-        const v8i C1 = v8i{(int)0xEEEEEEEEu, (int)0xDDDDDDDDu, (int)0xAAAAAAAAu, 0, 0, 0, 0, 0};
-        const v8i C2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < T; ++u) {
-          corr[u] = mfma_f6f4(Aw[u], C1, corr[u], sw[u]);
-          corr[u] = mfma_f6f4(Aw[u], C2, corr[u], sw[u]);
-        }
-      }
-    }
-  };
-
-  // zero digits and empty statistics in buffer 1 for the first interval
-  for (int i = tid; i < T * 16 * kWqRow / 2; i += 64 * NW) reinterpret_cast<uint32_t *>(&sm.wq[1][0][0][0])[i] = 0u;
-  if (tid < T * 16) (&sm.stats[1][0][0][0])[tid] = make_int2(0, __float_as_int(-INFINITY));
-  lds_barrier();  // block ids, buffer 1
-  StageSet<R> SA, SB;  // register sets of even and odd tiles
-  {
-    // the order of the intervals before tile 0 (K part of tile j+3, V part
-    // of tile j+2 for j = -3, -2, -1), so that the counts of outstanding
-    // loads at the loop entry match those of the loop itself
-    // (scheduling barriers keep that order)
-    int b0, b1, c0, c1, d0, d1;
-    pair_ids(0, b0, b1);
-    pair_ids(min(1, ntiles - 1), c0, c1);
-    pair_ids(min(2, ntiles - 1), d0, d1);
-    load_k_part<R>(SA, sp, b0, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k_part<R>(SB, sp, c0, c1);
-    load_v_part<R>(SA, sp, b0, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    // the query operands while these tiles are in flight (scratch in the
-    // staging buffers, which are written from here on)
-    {
-      const int tiles[1] = {su};
-      qprep_compute<T, 1, true, true>(a, *reinterpret_cast<QPrepLds<T> *>(&sm.kbuf[0][0]), qpr, tid, wave, tiles, AqT,
-                                scqT, ciT, qiT);
-    }
-    store_k_part<R>(sm.kbuf[0], SA, sp, lane);
-    load_k_part<R>(SA, sp, d0, d1);
-    load_v_part<R>(SB, sp, c0, c1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  lds_barrier();
-  // Every interval holds both contractions; the first one's value pass
-  // reads the zeroed digit rows of buffer 1 and adds nothing.  The loop takes
-  // whole pairs and an odd last tile follows it: with a break between the
-  // two halves the compiler keeps a path from the first half back to the
-  // loop head, on which the next fetches are not in flight, and then waits
-  // for every load at the head.
-  int k = 0;
-  for (; k + 1 < ntiles; k += 2) {
-    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 0>{}, SB, SA, k);
-    lds_barrier();
-    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 1>{}, SA, SB, k + 1);
-    lds_barrier();
-  }
-  if (k < ntiles) {  // uniform
-    interval(flag<true>{}, flag<true>{}, std::integral_constant<int, 0>{}, SB, SA, k);
-    lds_barrier();
-  }
-  if ((ntiles - 1) & 1)
-    interval(flag<false>{}, flag<true>{}, std::integral_constant<int, 1>{}, SA, SB, ntiles - 1);
-  else
-    interval(flag<false>{}, flag<true>{}, std::integral_constant<int, 0>{}, SA, SB, ntiles - 1);
-  // Pin the accumulators here: the matrix ops write all 64 lanes whatever
-  // the exec mask and must not be sunk into the per-head branches below.
-#pragma unroll
-  for (int u = 0; u < T; ++u) {
-    asm volatile("" : "+v"(corr[u]));
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[u][p][j]));
-  }
-
-  // probability sums per head (scoring lanes), correction partials per wave
-  {
-    const float ls = row_sum16(lsum);
-    if (t16 == 0) {
-      sm.lred[su][grow][sq][0] = ls;
-      sm.lred[su][grow][sq][1] = rl;
-    }
-#pragma unroll
-    for (int u = 0; u < T; ++u)
-      if (t16 == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.cred[wave][u][grow][i] = corr[u][i];
-      }
-  }
-  lds_barrier();
-  const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
-#pragma unroll
-  for (int u = 0; u < T; ++u) {
-    const int g = 4 * u + grow;  // C rows of this lane: row grow of tile u
-    if (g >= nrows) continue;
-    const float ra = raC[u];
-    float cs = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < NW; ++wv)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cs += sm.cred[wv][u][grow][i];
-    float *part = a.partials + (query_out_row(a, grp, g) * a.part_stride + split) * kPartStride;
-    if (wave == 0 && t16 == 0) {
-      float l = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float rq = sm.lred[u][grow][q][1];
-        if (rq != -INFINITY) l += sm.lred[u][grow][q][0] * __builtin_amdgcn_exp2f(rq - ra);
-      }
-      part[0] = ra;
-      part[1] = l;
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      float o = -bsum * cs;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const v4f &c = acc[u][p][j];
-        o = fmaf(-beta[p], (c[0] + c[1]) + (c[2] + c[3]), o);
-      }
-      part[4 + 16 * (NJ * wave + j) + t16] = o;
-    }
-  }
-}
-
 // Five to eight heads per KV head (two head tiles): the waves specialise.
 // Waves 0..3 (role 0) score page pair w of every tile for both head tiles,
 // so each K page is expanded into operands once, and stage the K planes;
@@ -1244,7 +852,7 @@ __device__ __attribute__((always_inline)) void split_body(const DecodeArgs &a, S
 // both head tiles and stage the norms and V planes.  The two waves that share
 // a SIMD then issue different mixes (vector-heavy scores, matrix-heavy
 // values) and overlap, where identical waves run the same phases in lock
-// step.  Intervals, buffers and records are those of split_body.
+// step.  Intervals, buffers and records are the ones described above.
 template <int R>
 __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a, SplitLds<2> &sm, int b, int h,
                                                              int split, int s0, int s1) {
@@ -1256,6 +864,8 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
   // r those before min(s1, L - q_len + pos0 + r / G + 1)
   const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count;
   const int s1v = min(s1, L - qlen + 1);
+  // with a window, every row sees the keys from s0v on (the latest row's lower end)
+  const int s0v = window_low(a, L - qlen + (a.group * a.pos_count - 1) / a.group + 1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sq = wave & 3;  // role 0: page pair (K-block); role 1: coordinate block
@@ -1269,7 +879,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
     for (int idx = tid; idx < ntiles * kTilePages; idx += 64 * NW) {
       const int tile0 = s0 + 128 * (idx >> 3);
       const int tok = tile0 + 16 * (idx & 7);
-      sm.ids[idx >> 3][idx & 7] = btab[(tok < s1 ? tok : tile0) >> 4];
+      sm.ids[idx >> 3][idx & 7] = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)];
     }
   }
 
@@ -1314,7 +924,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
       for (int j = 0; j < NJ; ++j) acc[u][p][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // role 1: E8M0 scales of the weight rows in buffer bf (as in split_body)
+  // role 1: E8M0 scales of the weight rows in buffer bf
   auto value_scales = [&](int bf, int (&sw)[T]) __attribute__((always_inline)) {
     int2 st[T];
     bool move = false;
@@ -1352,7 +962,7 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
     }
   };
 
-  // One barrier interval (as in split_body): the staging of both roles, then
+  // One barrier interval: the staging of both roles, then
   // role 0 scores tile k, role 1 contracts the values of tile k-1 (without
   // scores: of tile k).
   auto interval = [&](auto HS, auto HV, auto PAR, StageSet<R> &SK, StageSet<R> &SV, int k)
@@ -1402,7 +1012,8 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
           qq[u][e] = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
         }
       }
-      const bool partial = s0 + 128 * (k + 1) > s1v;  // uniform: a tile some row does not see whole
+      // uniform: a tile some row does not see whole
+      const bool partial = s0 + 128 * (k + 1) > s1v || s0 + 128 * k < s0v;
 #pragma unroll
       for (int u = 0; u < T; ++u) {
         float inner[2];
@@ -1439,8 +1050,9 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
         weights(x0, x1, true, true);
         if (__builtin_amdgcn_ballot_w64(x0 > (float)kRefStep || x1 > (float)kRefStep) || partial) {
           const int tok0 = s0 + 128 * k + 32 * sq + t16;
-          const int lim = min(s1, L - qlen + (4 * u + grow) / G + 1);  // the lane's row
-          const bool v0 = tok0 < lim, v1 = tok0 + 16 < lim;
+          const int hi = L - qlen + (4 * u + grow) / G + 1;  // the lane's row
+          const int lim = min(s1, hi), lo = window_low(a, hi);
+          const bool v0 = tok0 < lim && tok0 >= lo, v1 = tok0 + 16 < lim && tok0 + 16 >= lo;
           const float r0 = v0 ? half_lo(nrm[0][0]) * inner[0] : -INFINITY;
           const float r1 = v1 ? half_lo(nrm[1][0]) * inner[1] : -INFINITY;
           const float mh = row_max16(fmaxf(r0, r1));
@@ -1602,19 +1214,16 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(Dec
   int b, h, j, Tb;
   bal_locate(a, t0, per, blockIdx.x, b, h, j, Tb);
   if (b >= a.num_seqs) return;  // uniform: past the last range
-  const int s0 = 128 * per * j, s1 = min(128 * per * (j + 1), clamped_context(a, b));
-  if constexpr (T == 1) {
-    split_body<T, 2>(a, sm, b, h, j, s0, s1);
-  } else {
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)  // uniform: the wave's role
-      split_body_ws<0>(a, sm, b, h, j, s0, s1);
-    else
-      split_body_ws<1>(a, sm, b, h, j, s0, s1);
-  }
+  const int L = clamped_context(a, b), base = seq_base(a, L);
+  const int s0 = base + 128 * per * j, s1 = min(base + 128 * per * (j + 1), L);
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)  // uniform: the wave's role
+    split_body_ws<0>(a, sm, b, h, j, s0, s1);
+  else
+    split_body_ws<1>(a, sm, b, h, j, s0, s1);
 }
 
 // ---- 2'''. split pass on the matrix cores, one tile per wave ----------------
-// The same contractions as split_body (fp6 query digits x fp4 bit-planes for
+// The same contractions as the pass above (fp6 query digits x fp4 bit-planes for
 // the scores, base-16 weight digits x fp4 value planes), arranged so that
 // every wave works alone: a workgroup of 4T waves forms the query operands
 // of its 4T heads once, then wave w takes tiles w, w + 4T, w + 8T, ... of
@@ -1681,8 +1290,8 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   int b, h, jr, Tb;
   bal_locate(a, t0s, per, blockIdx.x, b, h, jr, Tb);
   if (b >= a.num_seqs) return;  // uniform: past the last range
-  const int L = clamped_context(a, b);
-  const int s0 = 128 * per * jr, s1 = min(128 * per * (jr + 1), L);
+  const int L = clamped_context(a, b), base = seq_base(a, L);
+  const int s0 = base + 128 * per * jr, s1 = min(base + 128 * per * (jr + 1), L);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t16 = lane & 15, grow = lane >> 4;
@@ -1701,11 +1310,11 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     int k = wave + NW * (lane >> 3);
     int tile0 = s0 + 128 * min(k, ntiles - 1);
     int tok = tile0 + 16 * e;
-    ids0 = btab[(tok < s1 ? tok : tile0) >> 4];
+    ids0 = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)];
     k += 8 * NW;
     tile0 = s0 + 128 * min(k, ntiles - 1);
     tok = tile0 + 16 * e;
-    ids1 = btab[(tok < s1 ? tok : tile0) >> 4];
+    ids1 = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)];
   }
   auto page_id = [&](int slot, int e) __attribute__((always_inline)) {
     const int src = slot < 8 ? ids0 : ids1;
@@ -1799,9 +1408,13 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   uint32_t *const nrm = &sm.w.nrm[wave][0][0];
   const uint16_t *const nh = reinterpret_cast<const uint16_t *>(nrm);
   // the last key each of the lane's rows sees (causal over a verify block)
-  int lim[T];
+  int lim[T], low[T];
 #pragma unroll
-  for (int u = 0; u < T; ++u) lim[u] = min(s1, L - qlen + (4 * u + grow) / G + 1);
+  for (int u = 0; u < T; ++u) {
+    const int hi = L - qlen + (4 * u + grow) / G + 1;
+    lim[u] = min(s1, hi);
+    low[u] = window_low(a, hi);
+  }
   for (; k < ntiles; k += NW, ++slot) {  // uniform per wave
     const int nslot = k + NW < ntiles ? slot + 1 : slot;
     const int tok0 = s0 + 128 * k;
@@ -1825,7 +1438,7 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
         const v4f qv = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
         const float inner = fmaf(gmv, (qv[0] + qv[1]) + (qv[2] + qv[3]), (c[0] + c[1]) + (c[2] + c[3]));
         // a slot the lane's row does not see (past the range, or causal) is -inf
-        rs[u][e] = tq < lim[u] ? nkv * inner : -INFINITY;
+        rs[u][e] = tq < lim[u] && tq >= low[u] ? nkv * inner : -INFINITY;
       }
     }
     // the K part of the next tile (the last tile re-reads its own), issued as
@@ -2187,7 +1800,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
       const int per = bal_per(a, seq_tiles(a, lane));
       ns = (seq_tiles(a, b) + per - 1) / per;
     } else {
-      const int vis = max(0, clamped_context(a, b) - a.q_len + t + 1);
+      const int L = clamped_context(a, b);
+      const int vis = max(0, L - seq_base(a, L) - a.q_len + t + 1);
       ns = (vis + a.split_tokens - 1) / a.split_tokens;
     }
     ns += a.hot_parts;  // the window's records follow

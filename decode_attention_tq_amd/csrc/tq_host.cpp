@@ -385,10 +385,18 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
 }  // extern "C"
 
 namespace {
+// Keys a sequence's walk covers at most: with a sliding window, from the
+// page holding the first query's oldest key to the end.
+int walk_span(int max_context_len, int q_len, int window) {
+  if (window <= 0) return max_context_len;
+  return (int)std::min<int64_t>(max_context_len, (int64_t)window + q_len - 1 + (tq::kBlock - 1));
+}
+
 size_t decode_workspace(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
-                        int tokens_per_split, int hot_parts) {
-  if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0)
+                        int tokens_per_split, int hot_parts, int window = 0) {
+  if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 || window < 0)
     return 0;
+  max_context_len = walk_span(max_context_len, q_len, window);
   const int grp = num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
   const int ns = plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split).num_splits;
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
@@ -414,7 +422,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
                       int num_q_heads, int num_kv_heads, int max_context_len,
                       float softmax_scale, void *out, tq_dtype out_dtype,
                       int tokens_per_split, void *workspace, size_t workspace_bytes,
-                      void *stream, const HotWindow *hot, bool noalloc = false) {
+                      void *stream, const HotWindow *hot, bool noalloc = false, int window = 0) {
   tq_status st = check_cb(cb);
   if (st != TQ_OK) return st;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || (!workspace && !noalloc))
@@ -430,9 +438,20 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   if (max_context_len < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "max_context_len < 0");
   if (q_len > 1 && q_len > max_context_len)
     return fail(TQ_ERR_INVALID_ARGUMENT, "q_len (%d) > max_context_len (%d)", q_len, max_context_len);
-  if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * tq::kBlock < max_context_len)
+  if (window < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "window < 0");
+  if (window > 0 && hot) return fail(TQ_ERR_UNSUPPORTED, "a sliding window does not combine with a hot window");
+  if (max_blocks_per_seq < 1) return fail(TQ_ERR_INVALID_ARGUMENT, "max_blocks_per_seq < 1");
+  if (window == 0 && (int64_t)max_blocks_per_seq * tq::kBlock < max_context_len)
     return fail(TQ_ERR_INVALID_ARGUMENT, "max_blocks_per_seq (%d) cannot hold max_context_len (%d)",
                 max_blocks_per_seq, max_context_len);
+  // a ring of R pages holds 16 R consecutive positions: enough for the keys
+  // of the whole query block (window + q_len - 1 positions)
+  if (window > 0 && (int64_t)max_blocks_per_seq * tq::kBlock <
+                        std::min<int64_t>(max_context_len, (int64_t)window + q_len - 1))
+    return fail(TQ_ERR_INVALID_ARGUMENT,
+                "a ring of %d pages cannot hold window (%d) + q_len (%d) - 1 positions", max_blocks_per_seq,
+                window, q_len);
+  const int span = walk_span(max_context_len, q_len, window);  // keys one sequence's walk covers
   if (tokens_per_split < 0 || (tokens_per_split > 0 && tokens_per_split % 256 != 0))
     return fail(TQ_ERR_INVALID_ARGUMENT, "tokens_per_split must be 0 or a positive multiple of 256");
   if (tokens_per_split > tq::kMaxMfmaSplitTokens && tq::decode_uses_mfma(q_len, group))
@@ -441,10 +460,10 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
     return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
   if ((int64_t)num_seqs * q_len > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_seqs * q_len too large");
-  const SplitPlan plan = plan_splits(num_seqs, q_len, num_kv_heads, group, max_context_len, tokens_per_split);
+  const SplitPlan plan = plan_splits(num_seqs, q_len, num_kv_heads, group, span, tokens_per_split);
   const int ns = plan.num_splits;
   if (ns > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many splits (%d); raise tokens_per_split", ns);
-  if ((int64_t)num_seqs * num_kv_heads * ((max_context_len + 127) / 128) > 0x7fffffffLL)
+  if ((int64_t)num_seqs * num_kv_heads * ((span + 127) / 128) > 0x7fffffffLL)
     return fail(TQ_ERR_UNSUPPORTED, "num_seqs * num_kv_heads * tiles of max_context_len too large");
   int hot_parts = 0;
   if (hot) {
@@ -462,7 +481,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     if (ns + hot_parts > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many partial records per row");
   }
   const size_t need = decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
-                                       tokens_per_split, hot_parts);
+                                       tokens_per_split, hot_parts, window);
   if (noalloc) {
     // every check above is on the host; the scratch array's address is
     // resolved (once per device) only for a call that will launch
@@ -495,8 +514,14 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.out_dtype = out_dtype;
   a.split_tokens = plan.split_tokens;
   a.num_splits = ns;
-  a.ctx_cap = plan.balanced ? std::min((int64_t)max_blocks_per_seq * tq::kBlock, (int64_t)max_context_len)
-                            : (int)std::min((int64_t)max_blocks_per_seq * tq::kBlock, (int64_t)ns * plan.split_tokens);
+  // a context length past the plan is cut to it (caller contract broken);
+  // with a window the ring and the walk from seq_base bound every access
+  a.window = window;
+  if (window > 0)
+    a.ctx_cap = max_context_len;
+  else
+    a.ctx_cap = plan.balanced ? std::min((int64_t)max_blocks_per_seq * tq::kBlock, (int64_t)max_context_len)
+                              : (int)std::min((int64_t)max_blocks_per_seq * tq::kBlock, (int64_t)ns * plan.split_tokens);
   a.balanced = plan.balanced;
   a.bal_grid = plan.grid;
   a.bal_target = plan.target;
@@ -566,6 +591,29 @@ tq_status tq_decode_attention_noalloc(const tq_codebook *cb, const void *q, tq_d
 }
 
 size_t tq_decode_noalloc_scratch_bytes(void) { return tq::kNoAllocScratchBytes; }
+
+size_t tq_decode_window_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len, int num_q_heads,
+                                        int num_kv_heads, int max_context_len, int window,
+                                        int tokens_per_split) {
+  (void)cb;
+  if (window < 1) return 0;
+  return decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0,
+                          window);
+}
+
+tq_status tq_decode_attention_window(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                                     const uint8_t *k_cache, const uint8_t *v_cache,
+                                     const int32_t *block_tables, int ring_blocks,
+                                     const int32_t *context_lens, int num_seqs, int q_len,
+                                     int num_q_heads, int num_kv_heads, int max_context_len, int window,
+                                     float softmax_scale, void *out, tq_dtype out_dtype,
+                                     int tokens_per_split, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+  if (window < 1) return fail(TQ_ERR_INVALID_ARGUMENT, "window must be >= 1 (got %d)", window);
+  return decode_impl(cb, q, q_dtype, k_cache, v_cache, block_tables, ring_blocks, context_lens, num_seqs,
+                     q_len, num_q_heads, num_kv_heads, max_context_len, softmax_scale, out, out_dtype,
+                     tokens_per_split, workspace, workspace_bytes, stream, nullptr, false, window);
+}
 
 size_t tq_decode_hot_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads,
                                      int num_kv_heads, int max_context_len, int hot_max,

@@ -71,6 +71,8 @@ struct DecodeArgs {
   int q_len;
   int num_q_heads;
   int num_kv_heads;
+  int window;          // > 0: query at position p sees keys p - window + 1 .. p, and the
+                       // block-table row is a ring (logical page P at entry P mod max_blocks)
   int group;           // num_q_heads / num_kv_heads
   float scale;
   void *out;

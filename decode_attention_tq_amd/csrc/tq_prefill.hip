@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
   const int L = clamped_context(a, b);
   const int t0 = qb * BQ;
   const int t_last = min(t0 + BQ, a.q_len) - 1;
-  const int s0 = split * a.split_tokens;
+  const int s0 = seq_base(a, L) + split * a.split_tokens;
   const int s1 = min(min(s0 + a.split_tokens, L), L - a.q_len + t_last + 1);
   if (s0 >= s1) return;  // uniform: no key of the chunk is visible to the block
   const int tid = threadIdx.x, lane = tid & 63;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
   // this lane's query rows (columns of S^T and O^T), one per row tile u
   bool row_ok[kRowTiles];
   int64_t R[kRowTiles];
-  int lim[kRowTiles];
+  int lim[kRowTiles], low[kRowTiles];
 #pragma unroll
   for (int u = 0; u < kRowTiles; ++u) {
     const int rw = 16 * (kRowTiles * wave + u) + l16;
@@ -187,6 +187,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     row_ok[u] = t < a.q_len && rw < BQ * G;
     R[u] = ((int64_t)b * a.q_len + min(t, a.q_len - 1)) * a.num_q_heads + hq;
     lim[u] = L - a.q_len + t;  // last visible key of the row
+    low[u] = window_low(a, lim[u] + 1);  // first one (with a window)
   }
 
   // B operands of S^T: chunk kc = 0..3 rotated query, 4..7 alpha S q, scaled
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
       // a page past the chunk's end re-reads the step's first page (its keys
       // are masked)
       const int pg = (k0 + 16 * pgi < s1) ? (k0 >> 4) + pgi : (k0 >> 4);
-      const int64_t blk = btab[pg];
+      const int64_t blk = btab[page_entry(a, pg)];
       const uint8_t *base = isk ? k_cache + (blk * hkv + h) * kKPage : v_cache + (blk * hkv + h) * kVPage;
       r = *reinterpret_cast<const uint4 *>(base + off);
     }
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 16 * ct + 4 * g4 + i;
-          vis[ct][i] = key < s1 && key <= lim[u];
+          vis[ct][i] = key < s1 && key <= lim[u] && key >= low[u];
           const float raw_s = fmaf(knv[ct][i], cc[u][ct][i], kgv[ct][i] * csg[u][ct][i]);
           sc[ct][i] = vis[ct][i] ? raw_s : -INFINITY;
           tmax = fmaxf(tmax, sc[ct][i]);

@@ -249,6 +249,41 @@ tq_status tq_decode_attention_hot(const tq_codebook *cb, const void *q, tq_dtype
                                   int tokens_per_split, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/* ---- sliding-window attention over a rotating cache -----------------------
+ * Sliding-window layers keep only their most recent tokens; the SwiftLM
+ * README ("Performance: Mac mini M6", the correction under its tables and the
+ * --turbo-kv recall note) points out that such layers run on a rotating
+ * cache (Gemma 4: 25 of 30 layers with a 1,024-token window) which its
+ * compression did not cover.  This call is tq_decode_attention where
+ *   - query t of sequence b (position p = context_lens[b] - q_len + t) sees
+ *     only the keys at positions max(0, p - window + 1) .. p;
+ *   - block_tables row b is a ring of ring_blocks pages: position j lives in
+ *     page block_tables[b][(j / 16) mod ring_blocks] at offset j % 16, so a
+ *     page is reused for the positions 16 ring_blocks later (the caller's
+ *     slot_mapping for tq_encode_kv follows the same rule; a ring with
+ *     16 ring_blocks >= max_context_len never wraps and is a plain table).
+ * The ring must hold the keys of the whole query block:
+ * 16 ring_blocks >= min(max_context_len, window + q_len - 1); the call then
+ * reads only the pages the windows overlap (about window + q_len - 1 + 15
+ * positions per sequence, whatever the context length).
+ *   window      >= 1.
+ *   workspace   tq_decode_window_workspace_bytes() bytes (same arguments).
+ * Other arguments as in tq_decode_attention (ring_blocks in the place of
+ * max_blocks_per_seq).  Errors: those of tq_decode_attention, and
+ * TQ_ERR_INVALID_ARGUMENT for window < 1 or a ring too small. */
+size_t tq_decode_window_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len, int num_q_heads,
+                                        int num_kv_heads, int max_context_len, int window,
+                                        int tokens_per_split);
+
+tq_status tq_decode_attention_window(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
+                                     const uint8_t *k_cache, const uint8_t *v_cache,
+                                     const int32_t *block_tables, int ring_blocks,
+                                     const int32_t *context_lens, int num_seqs, int q_len,
+                                     int num_q_heads, int num_kv_heads, int max_context_len, int window,
+                                     float softmax_scale, void *out, tq_dtype out_dtype,
+                                     int tokens_per_split, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /* Thread-local text describing the last non-OK status on this thread. */
 const char *tq_last_error(void);
 

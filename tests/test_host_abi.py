@@ -323,3 +323,49 @@ def test_noalloc_rejects_calls_beyond_its_scratch_before_any_device_call():
     assert tq._lib.tq_decode_attention_noalloc(
         ref, None, tq.TQ_BF16, FAKE, FAKE, FAKE, 64, FAKE, 1, 1, 32, 8, 1024,
         0.0, FAKE, tq.TQ_F32, 0, None) == tq.TQ_ERR_INVALID_ARGUMENT
+
+
+def _win(cb, **kw):
+    a = dict(q=FAKE, qd=tq.TQ_BF16, kc=FAKE, vc=FAKE, bt=FAKE, rb=70, cl=FAKE, B=1, q_len=1,
+             Hq=32, Hkv=8, maxc=100000, W=1024, scale=0.0, out=FAKE, od=tq.TQ_F32, tps=0, ws=FAKE,
+             wsb=1 << 40)
+    a.update(kw)
+    return tq._lib.tq_decode_attention_window(
+        ctypes.byref(cb), a["q"], a["qd"], a["kc"], a["vc"], a["bt"], a["rb"], a["cl"], a["B"],
+        a["q_len"], a["Hq"], a["Hkv"], a["maxc"], a["W"], a["scale"], a["out"], a["od"], a["tps"],
+        a["ws"], a["wsb"], None)
+
+
+def test_window_validation():
+    """Checks of the sliding-window call that run before any launch: the
+    window, the ring size against window + q_len - 1, the plain call's
+    checks, and the workspace (every case below fails on the host)."""
+    cb = _fake_cb()
+    E = tq.TQ_ERR_INVALID_ARGUMENT
+    assert _win(_fake_cb(False)) == tq.TQ_ERR_NOT_INITIALIZED
+    assert _win(cb, W=0) == E
+    assert "window" in tq.tq_last_error()
+    assert _win(cb, W=-5) == E
+    assert _win(cb, rb=63) == E                      # 63 pages < 1024 positions
+    assert "ring" in tq.tq_last_error()
+    assert _win(cb, rb=64, q_len=2) == E             # 1025 positions needed
+    assert _win(cb, q=None) == E
+    assert _win(cb, Hq=30) == E
+    assert _win(cb, Hq=34, Hkv=2) == tq.TQ_ERR_UNSUPPORTED
+    assert _win(cb, wsb=16) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+    assert _win(cb, ws=None) == E
+
+
+def test_window_workspace_covers_only_the_window():
+    """The window call plans over about window + q_len - 1 + 15 positions per
+    sequence whatever the context length; a window covering the context
+    plans exactly like the plain call."""
+    cb = ctypes.byref(_fake_cb())
+    plain_fn, win_fn = tq._lib.tq_decode_workspace_bytes, tq._lib.tq_decode_window_workspace_bytes
+    plain = plain_fn(cb, 16, 1, 32, 8, 131072, 0)
+    win = win_fn(cb, 16, 1, 32, 8, 131072, 1024, 0)
+    assert 0 < win < plain
+    assert win == win_fn(cb, 16, 1, 32, 8, 2 ** 30, 1024, 0)
+    for q_len, Hq, Hkv in [(1, 32, 8), (3, 32, 4), (21, 16, 2), (1, 32, 2)]:
+        assert win_fn(cb, 4, q_len, Hq, Hkv, 5000, 5000, 0) == plain_fn(cb, 4, q_len, Hq, Hkv, 5000, 0)
+    assert win_fn(cb, 4, 1, 32, 8, 5000, 0, 0) == 0
