@@ -119,3 +119,92 @@ def codebook_fp32(head_dim: int = 128, bits: int = 3):
     s = math.sqrt(float(head_dim))
     return (np.array([x / s for x in c], dtype=np.float64).astype(np.float32),
             np.array([x / s for x in t], dtype=np.float64).astype(np.float32))
+
+
+# ---- the exact marginal of one coordinate of a random unit vector -----------
+# The pages ([A] "Lloyd-Maxコードブックとは") fit the codebook to N(0, 1/d), the
+# large-d limit of one coordinate of a uniformly random unit vector in R^d.
+# The exact marginal has density f(y) = C_d (1 - y^2)^((d-3)/2) on (-1, 1),
+# C_d = Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)), and Y^2 ~ Beta(1/2, (d-1)/2).
+# The variant below runs the same Lloyd-Max iteration on that density (cell
+# masses and moments from the regularised incomplete beta function and the
+# antiderivative of y (1 - y^2)^k); it is a reference, not the codebook the
+# method uses.
+
+def sphere_marginal_pdf(y: float, d: int) -> float:
+    if abs(y) >= 1.0:
+        return 0.0
+    logc = math.lgamma(d / 2.0) - 0.5 * math.log(math.pi) - math.lgamma((d - 1) / 2.0)
+    return math.exp(logc + 0.5 * (d - 3) * math.log1p(-y * y))
+
+
+def _sphere_cdf(y: float, d: int) -> float:
+    """P(Y <= y): 1/2 + sign(y) I_{y^2}(1/2, (d-1)/2) / 2."""
+    import scipy.special
+    if y <= -1.0:
+        return 0.0
+    if y >= 1.0:
+        return 1.0
+    half = 0.5 * float(scipy.special.betainc(0.5, (d - 1) / 2.0, y * y))
+    return 0.5 + half if y >= 0.0 else 0.5 - half
+
+
+def _sphere_first_moment(a: float, b: float, d: int) -> float:
+    """Integral of y f(y) over (a, b]: C_d [(1-a^2)^(k+1) - (1-b^2)^(k+1)] / (2 (k+1)), k = (d-3)/2."""
+    k1 = 0.5 * (d - 1)
+    logc = math.lgamma(d / 2.0) - 0.5 * math.log(math.pi) - math.lgamma((d - 1) / 2.0)
+    ua = 0.0 if abs(a) >= 1.0 else math.exp(k1 * math.log1p(-a * a))
+    ub = 0.0 if abs(b) >= 1.0 else math.exp(k1 * math.log1p(-b * b))
+    return math.exp(logc) * (ua - ub) / (2.0 * k1)
+
+
+def _sphere_second_moment(a: float, b: float, d: int) -> float:
+    """Integral of y^2 f(y) over (a, b]: with X = Y^2 ~ Beta(1/2, (d-1)/2),
+    E[X 1{X <= s}] = I_s(3/2, (d-1)/2) / d, split at 0 by symmetry."""
+    import scipy.special
+
+    def upto(y):  # integral of y^2 f over [0, y] for y >= 0
+        y = min(y, 1.0)
+        return 0.5 * float(scipy.special.betainc(1.5, (d - 1) / 2.0, y * y)) / d
+
+    def signed(y):  # integral over (-1, y]
+        return 1.0 / (2 * d) + (upto(y) if y >= 0.0 else -upto(-y))
+
+    a, b = max(a, -1.0), min(b, 1.0)
+    return signed(b) - signed(a)
+
+
+def lloyd_max_sphere(levels: int, d: int, tol: float = 1e-15, max_iter: int = 100000):
+    """Lloyd-Max on the exact marginal f above, in the same order as
+    ``lloyd_max_gaussian`` (midpoint thresholds, conditional-mean levels,
+    repeat).  Returns ``(centroids, thresholds, iterations)`` in float64 on
+    the unit-vector scale (no further 1/sqrt(d) scaling)."""
+    if levels < 2 or d < 3:
+        raise ValueError("levels >= 2 and d >= 3")
+    s = 1.0 / math.sqrt(d)
+    c = np.array([(k - (levels - 1) / 2.0) * (4.0 / levels) * s for k in range(levels)])
+    c = np.clip(c, -0.99, 0.99)
+    it = 0
+    for it in range(1, max_iter + 1):
+        t = [(c[k] + c[k + 1]) / 2.0 for k in range(levels - 1)]
+        edges = [-1.0] + t + [1.0]
+        c_new = np.array([_sphere_first_moment(edges[k], edges[k + 1], d) /
+                          (_sphere_cdf(edges[k + 1], d) - _sphere_cdf(edges[k], d)) for k in range(levels)])
+        delta = float(np.max(np.abs(c_new - c)))
+        c = c_new
+        if delta < tol:
+            break
+    t = np.array([(c[k] + c[k + 1]) / 2.0 for k in range(levels - 1)])
+    return c, t, it
+
+
+def quantizer_mse_sphere(centroids: np.ndarray, thresholds: np.ndarray, d: int) -> float:
+    """E[(Y - Q(Y))^2] under the exact marginal, cell by cell:
+    E[Y^2 1_cell] - 2 c E[Y 1_cell] + c^2 P(cell)."""
+    edges = [-1.0] + list(thresholds) + [1.0]
+    total = 0.0
+    for k, c in enumerate(centroids):
+        a, b = edges[k], edges[k + 1]
+        p = _sphere_cdf(b, d) - _sphere_cdf(a, d)
+        total += _sphere_second_moment(a, b, d) - 2.0 * c * _sphere_first_moment(a, b, d) + c * c * p
+    return total

@@ -11,22 +11,25 @@ Pools: ``k_pool[num_blocks][num_kv_heads][1088]``,
 ``v_pool[num_blocks][num_kv_heads][800]``; slot = block * 16 + offset.
 All multi-byte fields little-endian; bit b of a byte has weight 2^b.
 
-K page (1088 B):
-  [0, 1024)     : 64 records of 16 bytes, chunk-major: the record of
+For b-bit codes (b = 2, 3, 4; the pages' method uses b = 3), with
+RB = 4 (b + 1) bytes per record:
+K page (256 (b + 1) + 64 B; 1088 for b = 3):
+  [0, 64 RB)    : 64 records of RB bytes, chunk-major: the record of
       coordinate chunk g = 0..3 (coordinates 32g .. 32g + 31) and token t is
-      at 16 (16 g + t); its four little-endian 32-bit words are field
-      f = 0, 1, 2 (code bit-plane f: bit i % 32 of the word holds bit f of
-      code_i for coordinate i = 32 g + i % 32) and f = 3 (QJL signs: bit
+      at RB (16 g + t); its little-endian 32-bit words are field
+      f = 0 .. b-1 (code bit-plane f: bit i % 32 of the word holds bit f of
+      code_i for coordinate i = 32 g + i % 32) and f = b (QJL signs: bit
       i % 32 holds the sign bit of projection row i = 32 g + i % 32; 1 means
       z_i >= 0).  So bit f of code_i / the sign of row i sits at byte
-      16 (16 (i // 32) + t) + 4 f + (i % 32) // 8, bit i % 8.
-  [1024, 1056)  : half n_t at 1024 + 2t.
-  [1056, 1088)  : half gamma_t at 1056 + 2t.
-V page (800 B):
-  [256p, 256p + 256), p = 0, 1, 2 : code bit-plane p, coordinate-major:
+      RB (16 (i // 32) + t) + 4 f + (i % 32) // 8, bit i % 8.
+  [64 RB, 64 RB + 32)      : half n_t at 64 RB + 2t.
+  [64 RB + 32, 64 RB + 64) : half gamma_t at 64 RB + 32 + 2t.
+V page (256 b + 32 B; 800 for b = 3):
+  [256p, 256p + 256), p = 0 .. b-1 : code bit-plane p, coordinate-major:
       coordinate i owns the 16-bit word at 256p + 2i; its bit t holds bit p
       of token t's code for coordinate i.
-  [768, 800)    : half n_t at 768 + 2t.
+  [256 b, 256 b + 32) : half n_t at 256 b + 2t.
+The functions below take the bit width from the page (or pool) size.
 Bits per coordinate: 1088*8/(16*128) = 4.25 and 800*8/(16*128) = 3.125.
 """
 
@@ -37,8 +40,43 @@ import numpy as np
 BLOCK = 16
 HEAD_DIM = 128
 QJL_DIM = 128
-K_PAGE_BYTES = 3 * 256 + 256 + 2 * BLOCK + 2 * BLOCK
-V_PAGE_BYTES = 3 * 256 + 2 * BLOCK
+
+
+def k_record_bytes(bits: int) -> int:
+    return 4 * (bits + 1)
+
+
+def k_page_bytes(bits: int) -> int:
+    return 64 * k_record_bytes(bits) + 2 * BLOCK + 2 * BLOCK
+
+
+def v_page_bytes(bits: int) -> int:
+    return 256 * bits + 2 * BLOCK
+
+
+def k_norm_offset(bits: int) -> int:
+    return 64 * k_record_bytes(bits)
+
+
+def v_norm_offset(bits: int) -> int:
+    return 256 * bits
+
+
+def k_page_bits(nbytes: int) -> int:
+    """Bit width of a K page of ``nbytes`` bytes."""
+    b = (nbytes - 4 * BLOCK) // 256 - 1
+    assert k_page_bytes(b) == nbytes, nbytes
+    return b
+
+
+def v_page_bits(nbytes: int) -> int:
+    b = (nbytes - 2 * BLOCK) // 256
+    assert v_page_bytes(b) == nbytes, nbytes
+    return b
+
+
+K_PAGE_BYTES = k_page_bytes(3)
+V_PAGE_BYTES = v_page_bytes(3)
 
 
 def _put_bit(buf: np.ndarray, byte: int, bit: int, value: int) -> None:
@@ -63,56 +101,62 @@ def _get_half(buf: np.ndarray, off: int) -> np.float16:
     return np.array([raw], dtype=np.uint16).view(np.float16)[0]
 
 
-def k_bit_byte(t: int, i: int, field: int) -> int:
-    """Byte of the K page holding field ``field`` (0..2: code bit-plane,
-    3: QJL sign) of coordinate / row ``i`` of token ``t``; the bit is i % 8."""
-    return 16 * (16 * (i // 32) + t) + 4 * field + (i % 32) // 8
+def k_bit_byte(t: int, i: int, field: int, bits: int = 3) -> int:
+    """Byte of the K page holding field ``field`` (0 .. bits-1: code
+    bit-plane, bits: QJL sign) of coordinate / row ``i`` of token ``t``; the
+    bit is i % 8."""
+    return k_record_bytes(bits) * (16 * (i // 32) + t) + 4 * field + (i % 32) // 8
 
 
 def set_k_slot(page: np.ndarray, t: int, codes, signs, n16, g16) -> None:
+    bits = k_page_bits(page.shape[-1])
     for i in range(HEAD_DIM):
-        for p in range(3):
-            _put_bit(page, k_bit_byte(t, i, p), i % 8, (int(codes[i]) >> p) & 1)
+        for p in range(bits):
+            _put_bit(page, k_bit_byte(t, i, p, bits), i % 8, (int(codes[i]) >> p) & 1)
     for i in range(QJL_DIM):
-        _put_bit(page, k_bit_byte(t, i, 3), i % 8, int(signs[i]))
-    _put_half(page, 1024 + 2 * t, n16)
-    _put_half(page, 1056 + 2 * t, g16)
+        _put_bit(page, k_bit_byte(t, i, bits, bits), i % 8, int(signs[i]))
+    _put_half(page, k_norm_offset(bits) + 2 * t, n16)
+    _put_half(page, k_norm_offset(bits) + 32 + 2 * t, g16)
 
 
 def get_k_slot(page: np.ndarray, t: int):
+    bits = k_page_bits(page.shape[-1])
     codes = np.zeros(HEAD_DIM, dtype=np.uint8)
     signs = np.zeros(QJL_DIM, dtype=np.uint8)
     for i in range(HEAD_DIM):
         v = 0
-        for p in range(3):
-            v |= _get_bit(page, k_bit_byte(t, i, p), i % 8) << p
+        for p in range(bits):
+            v |= _get_bit(page, k_bit_byte(t, i, p, bits), i % 8) << p
         codes[i] = v
     for i in range(QJL_DIM):
-        signs[i] = _get_bit(page, k_bit_byte(t, i, 3), i % 8)
-    return codes, signs, _get_half(page, 1024 + 2 * t), _get_half(page, 1056 + 2 * t)
+        signs[i] = _get_bit(page, k_bit_byte(t, i, bits, bits), i % 8)
+    no = k_norm_offset(bits)
+    return codes, signs, _get_half(page, no + 2 * t), _get_half(page, no + 32 + 2 * t)
 
 
 def set_v_slot(page: np.ndarray, t: int, codes, n16) -> None:
+    bits = v_page_bits(page.shape[-1])
     for i in range(HEAD_DIM):
-        for p in range(3):
+        for p in range(bits):
             word = 256 * p + 2 * i
             _put_bit(page, word + t // 8, t % 8, (int(codes[i]) >> p) & 1)
-    _put_half(page, 768 + 2 * t, n16)
+    _put_half(page, v_norm_offset(bits) + 2 * t, n16)
 
 
 def get_v_slot(page: np.ndarray, t: int):
+    bits = v_page_bits(page.shape[-1])
     codes = np.zeros(HEAD_DIM, dtype=np.uint8)
     for i in range(HEAD_DIM):
         v = 0
-        for p in range(3):
+        for p in range(bits):
             v |= _get_bit(page, 256 * p + 2 * i + t // 8, t % 8) << p
         codes[i] = v
-    return codes, _get_half(page, 768 + 2 * t)
+    return codes, _get_half(page, v_norm_offset(bits) + 2 * t)
 
 
-def pack_k_page(codes, signs, n16, g16) -> np.ndarray:
+def pack_k_page(codes, signs, n16, g16, bits: int = 3) -> np.ndarray:
     """One full K page from ``codes[16][128]``, ``signs[16][128]``, halves."""
-    page = np.zeros(K_PAGE_BYTES, dtype=np.uint8)
+    page = np.zeros(k_page_bytes(bits), dtype=np.uint8)
     for t in range(BLOCK):
         set_k_slot(page, t, codes[t], signs[t], n16[t], g16[t])
     return page
@@ -125,8 +169,8 @@ def unpack_k_page(page: np.ndarray):
             np.array([o[3] for o in out], dtype=np.float16))
 
 
-def pack_v_page(codes, n16) -> np.ndarray:
-    page = np.zeros(V_PAGE_BYTES, dtype=np.uint8)
+def pack_v_page(codes, n16, bits: int = 3) -> np.ndarray:
+    page = np.zeros(v_page_bytes(bits), dtype=np.uint8)
     for t in range(BLOCK):
         set_v_slot(page, t, codes[t], n16[t])
     return page
@@ -199,6 +243,9 @@ def _half_bytes(h) -> np.ndarray:
 def write_slots_fast(k_pool: np.ndarray, v_pool: np.ndarray, slot_mapping, enc_k: dict,
                      enc_v: dict) -> None:
     """Same effect as ``write_slots`` (slots must be distinct)."""
+    bits = k_page_bits(k_pool.shape[-1])
+    assert v_page_bits(v_pool.shape[-1]) == bits
+    RB, kn, vn = k_record_bytes(bits), k_norm_offset(bits), v_norm_offset(bits)
     slots = np.asarray(slot_mapping, dtype=np.int64)
     keep = slots >= 0
     slots = slots[keep]
@@ -209,56 +256,59 @@ def write_slots_fast(k_pool: np.ndarray, v_pool: np.ndarray, slot_mapping, enc_k
     vc = enc_v["codes"][keep]
     blk, off = slots // BLOCK, slots % BLOCK
     T, H = kc.shape[:2]
-    ar16 = np.arange(16)[None, :]
     ar2 = np.arange(2)[None, :]
     bcol = blk[:, None]
     ar4 = np.arange(4)[None, :]
     for h in range(H):
-        # fields f = 0..2 (code bit-planes) and 3 (signs), 16 bytes per token,
-        # 4 bytes per coordinate chunk g at 16 (16 g + t) + 4 f
-        fields = [_pack_bits_le((kc[:, h, :] >> p) & 1) for p in range(3)] + [_pack_bits_le(ks[:, h, :])]
+        # fields f = 0 .. bits-1 (code bit-planes) and bits (signs), RB bytes
+        # per token, 4 bytes per coordinate chunk g at RB (16 g + t) + 4 f
+        fields = [_pack_bits_le((kc[:, h, :] >> p) & 1) for p in range(bits)] + [_pack_bits_le(ks[:, h, :])]
         for f, fb in enumerate(fields):                                   # fb: [T, 16]
             for g in range(4):
-                k_pool[bcol, h, (16 * (16 * g + off) + 4 * f)[:, None] + ar4] = fb[:, 4 * g: 4 * g + 4]
-        k_pool[bcol, h, (1024 + 2 * off)[:, None] + ar2] = _half_bytes(enc_k["norm_f16"][keep][:, h])
-        k_pool[bcol, h, (1056 + 2 * off)[:, None] + ar2] = _half_bytes(enc_k["gamma_f16"][keep][:, h])
-        v_pool[bcol, h, (768 + 2 * off)[:, None] + ar2] = _half_bytes(enc_v["norm_f16"][keep][:, h])
+                k_pool[bcol, h, (RB * (16 * g + off) + 4 * f)[:, None] + ar4] = fb[:, 4 * g: 4 * g + 4]
+        k_pool[bcol, h, (kn + 2 * off)[:, None] + ar2] = _half_bytes(enc_k["norm_f16"][keep][:, h])
+        k_pool[bcol, h, (kn + 32 + 2 * off)[:, None] + ar2] = _half_bytes(enc_k["gamma_f16"][keep][:, h])
+        v_pool[bcol, h, (vn + 2 * off)[:, None] + ar2] = _half_bytes(enc_v["norm_f16"][keep][:, h])
         # V planes are coordinate-major: a 16-bit word per coordinate, a bit per token.
-        words = v_pool[:, h, :768].copy().view(np.uint16).reshape(-1, 3, HEAD_DIM)
+        words = v_pool[:, h, :vn].copy().view(np.uint16).reshape(-1, bits, HEAD_DIM)
         mask = (np.uint16(1) << off.astype(np.uint16)).astype(np.uint16)   # [T]
-        for p in range(3):
+        for p in range(bits):
             bitv = ((vc[:, h, :] >> p) & 1).astype(np.uint16)            # [T, 128]
             np.bitwise_and.at(words, (blk, p), (~mask)[:, None] & np.uint16(0xFFFF))
             np.bitwise_or.at(words, (blk, p), bitv * mask[:, None])
-        v_pool[:, h, :768] = words.reshape(-1, 3 * HEAD_DIM).view(np.uint8)
+        v_pool[:, h, :vn] = words.reshape(-1, bits * HEAD_DIM).view(np.uint8)
 
 
 def read_k_tokens_fast(k_pool: np.ndarray, block_row, length: int, head: int):
     """Same result as ``read_k_tokens``."""
+    bits = k_page_bits(k_pool.shape[-1])
+    RB, kn = k_record_bytes(bits), k_norm_offset(bits)
     nb = (length + BLOCK - 1) // BLOCK
-    pages = k_pool[np.asarray(block_row[:nb], dtype=np.int64), head]    # [nb, 1088]
+    pages = k_pool[np.asarray(block_row[:nb], dtype=np.int64), head]    # [nb, page bytes]
     codes = np.zeros((nb, BLOCK, HEAD_DIM), dtype=np.uint8)
     # [nb, chunk g, token t, field f, 4 bytes] -> per field [nb, t, 16 bytes in chunk order]
-    rec = pages[:, :1024].reshape(nb, 4, BLOCK, 4, 4)
+    rec = pages[:, :kn].reshape(nb, 4, BLOCK, bits + 1, 4)
     def field(f):
         return np.ascontiguousarray(np.transpose(rec[:, :, :, f, :], (0, 2, 1, 3))).reshape(nb, BLOCK, 16)
-    for p in range(3):
+    for p in range(bits):
         codes |= (_unpack_bits_le(field(p), HEAD_DIM) << p).astype(np.uint8)
-    signs = _unpack_bits_le(field(3), QJL_DIM)
-    n16 = pages[:, 1024:1056].copy().view(np.float16).reshape(nb, BLOCK)
-    g16 = pages[:, 1056:1088].copy().view(np.float16).reshape(nb, BLOCK)
+    signs = _unpack_bits_le(field(bits), QJL_DIM)
+    n16 = pages[:, kn:kn + 32].copy().view(np.float16).reshape(nb, BLOCK)
+    g16 = pages[:, kn + 32:kn + 64].copy().view(np.float16).reshape(nb, BLOCK)
     return (codes.reshape(-1, HEAD_DIM)[:length], signs.reshape(-1, QJL_DIM)[:length],
             n16.reshape(-1)[:length], g16.reshape(-1)[:length])
 
 
 def read_v_tokens_fast(v_pool: np.ndarray, block_row, length: int, head: int):
     """Same result as ``read_v_tokens``."""
+    bits = v_page_bits(v_pool.shape[-1])
+    vn = v_norm_offset(bits)
     nb = (length + BLOCK - 1) // BLOCK
-    pages = v_pool[np.asarray(block_row[:nb], dtype=np.int64), head]    # [nb, 800]
+    pages = v_pool[np.asarray(block_row[:nb], dtype=np.int64), head]    # [nb, page bytes]
     codes = np.zeros((nb, BLOCK, HEAD_DIM), dtype=np.uint8)
-    for p in range(3):
+    for p in range(bits):
         raw = pages[:, 256 * p: 256 * p + 256].reshape(nb, HEAD_DIM, 2)  # [nb, dim, 2 bytes]
-        bits = _unpack_bits_le(raw, BLOCK)                               # [nb, dim, token]
-        codes |= (np.transpose(bits, (0, 2, 1)) << p).astype(np.uint8)
-    n16 = pages[:, 768:800].copy().view(np.float16).reshape(nb, BLOCK)
+        bits_t = _unpack_bits_le(raw, BLOCK)                             # [nb, dim, token]
+        codes |= (np.transpose(bits_t, (0, 2, 1)) << p).astype(np.uint8)
+    n16 = pages[:, vn:vn + 32].copy().view(np.float16).reshape(nb, BLOCK)
     return codes.reshape(-1, HEAD_DIM)[:length], n16.reshape(-1)[:length]
