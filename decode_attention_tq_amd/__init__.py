@@ -37,7 +37,7 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 HEAD_DIM = 128
 QJL_DIM = 128
 BLOCK = 16
-K_PAGE_BYTES = 1088
+K_PAGE_BYTES = 1088   # page sizes of 3-bit codes; tq_k_page_bytes / tq_v_page_bytes give any width
 V_PAGE_BYTES = 800
 
 EXPORTED = [
@@ -52,8 +52,8 @@ EXPORTED = [
 class tq_codebook_t(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("qjl_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("qjl_seed", ctypes.c_uint64), ("centroids", ctypes.c_float * 8),
-                ("thresholds", ctypes.c_float * 7), ("qjl_scale", ctypes.c_float),
+                ("qjl_seed", ctypes.c_uint64), ("centroids", ctypes.c_float * 16),
+                ("thresholds", ctypes.c_float * 15), ("qjl_scale", ctypes.c_float),
                 ("d_tables", ctypes.c_void_p), ("magic", ctypes.c_uint32),
                 ("reserved", ctypes.c_uint32)]
 
@@ -142,12 +142,13 @@ def _stream(stream, device=None):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _check_pools(k_cache, v_cache, num_kv_heads: int) -> None:
+def _check_pools(cb, k_cache, v_cache, num_kv_heads: int) -> None:
     """The C ABI takes the pools as bare pointers with no size: their shape is
     checked here, so that a pool built for another head count or page size
-    is rejected before any kernel reads or writes it."""
+    (bit width) is rejected before any kernel reads or writes it."""
     torch = _torch()
-    for name, pool, page in (("k_cache", k_cache, K_PAGE_BYTES), ("v_cache", v_cache, V_PAGE_BYTES)):
+    kpage, vpage = int(_lib.tq_k_page_bytes(cb.ref)), int(_lib.tq_v_page_bytes(cb.ref))
+    for name, pool, page in (("k_cache", k_cache, kpage), ("v_cache", v_cache, vpage)):
         if not isinstance(pool, torch.Tensor):
             raise TypeError(f"{name} must be a torch tensor")
         if pool.dtype != torch.uint8 or not pool.is_contiguous():
@@ -198,12 +199,16 @@ class Codebook:
         return ctypes.byref(self.struct)
 
     @property
+    def bits(self) -> int:
+        return int(self.struct.bits)
+
+    @property
     def centroids(self) -> np.ndarray:
-        return np.array(self.struct.centroids[:], dtype=np.float32)
+        return np.array(self.struct.centroids[:1 << self.bits], dtype=np.float32)
 
     @property
     def thresholds(self) -> np.ndarray:
-        return np.array(self.struct.thresholds[:], dtype=np.float32)
+        return np.array(self.struct.thresholds[:(1 << self.bits) - 1], dtype=np.float32)
 
 
 def tq_codebook_init(head_dim: int = HEAD_DIM, bits: int = 3, qjl_seed: int = 42,
@@ -248,7 +253,7 @@ def tq_encode_kv(cb: Codebook, k, v, slot_mapping, k_cache, v_cache, norms_out=N
     T, H = k.shape[0], k.shape[1]
     if slot_mapping.dim() != 1 or slot_mapping.shape[0] != T:
         raise ValueError(f"slot_mapping must have one entry per token ({T})")
-    _check_pools(k_cache, v_cache, H)
+    _check_pools(cb, k_cache, v_cache, H)
     if norms_out is not None and (norms_out.dtype != torch.float32 or not norms_out.is_contiguous()
                                   or tuple(norms_out.shape) != (T, H, 3)):
         raise ValueError(f"norms_out must be a contiguous float32 [{T}][{H}][3] tensor")
@@ -280,7 +285,7 @@ def tq_decode_attention(cb: Codebook, q, k_cache, v_cache, block_tables, context
     if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous int32")
     B, q_len, Hq, _ = q.shape
-    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_pools(cb, k_cache, v_cache, num_kv_heads)
     _check_seq_tables(block_tables, context_lens, B)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
@@ -316,7 +321,7 @@ def tq_decode_attention_noalloc(cb: Codebook, q, k_cache, v_cache, block_tables,
     if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous int32")
     B, q_len, Hq, _ = q.shape
-    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_pools(cb, k_cache, v_cache, num_kv_heads)
     _check_seq_tables(block_tables, context_lens, B)
     if out is None or not out.is_contiguous() or out.shape != q.shape:
         raise ValueError("out must be a contiguous tensor with q's shape")
@@ -351,7 +356,7 @@ def tq_decode_attention_window(cb: Codebook, q, k_cache, v_cache, block_tables, 
     if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
         raise ValueError("context_lens must be contiguous int32")
     B, q_len, Hq, _ = q.shape
-    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_pools(cb, k_cache, v_cache, num_kv_heads)
     _check_seq_tables(block_tables, context_lens, B)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
@@ -393,7 +398,7 @@ def tq_decode_attention_hot(cb: Codebook, q, k_cache, v_cache, block_tables, con
     if hot_lens.dtype != torch.int32 or not hot_lens.is_contiguous():
         raise ValueError("hot_lens must be contiguous int32")
     B, _, Hq, _ = q.shape
-    _check_pools(k_cache, v_cache, num_kv_heads)
+    _check_pools(cb, k_cache, v_cache, num_kv_heads)
     _check_seq_tables(block_tables, context_lens, B)
     if hot_lens.dim() != 1 or hot_lens.shape[0] != B:
         raise ValueError(f"hot_lens must have one entry per sequence ({B})")

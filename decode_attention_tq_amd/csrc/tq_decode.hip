@@ -184,9 +184,11 @@ __global__ __launch_bounds__(256) void query_prep_kernel(DecodeArgs a) {
 // ---- 2. split pass (vector ALU) --------------------------------------------
 // G is the capacity (1, 2, 4, 8 or 16 heads); the call's group size
 // (a.group <= G) indexes the rows, the heads past it score zero queries and
-// write nothing.
-template <int G>
+// write nothing.  BITS: code width of the pages (2, 3 or 4).
+template <int G, int BITS>
 __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
+  constexpr int NL = 1 << BITS;  // levels
+  constexpr int KP = k_page_bytes(BITS), VP = v_page_bytes(BITS), RB = k_rec_bytes(BITS);
   const int Gr = a.group;
   const int bt = blockIdx.x;  // b * q_len + t
   const int h = blockIdx.y;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
   // main loop: qp[G][128] | sq[G][128] | pn[4][G][64]; after it: red[4][G][128]
   __shared__ float smem[G * 512];
   __shared__ float red_m[4][G], red_l[4][G];
-  __shared__ float lut[8];
+  __shared__ float lut[NL];
   float *qp = smem;
   float *sq = smem + G * 128;
   float *pn = smem + G * 256;
@@ -214,15 +216,15 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
     const float v = g < Gr ? a.qprep[(row0 + g) * 256 + c] : 0.0f;
     if (c < 128) qp[g * 128 + c] = v; else sq[g * 128 + c - 128] = v;
   }
-  if (tid < 8) {
+  if (tid < NL) {
     // read the levels into registers first: a select over kernel-argument
     // fields can be folded into a lane-indexed memory load
-    float cv[8];
+    float cv[NL];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cv[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[j])));
+    for (int j = 0; j < NL; ++j) cv[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[j])));
     float c = cv[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) c = (tid == j) ? cv[j] : c;
+    for (int j = 1; j < NL; ++j) c = (tid == j) ? cv[j] : c;
     lut[tid] = c;
   }
   lds_barrier();
@@ -251,19 +253,17 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
     if (valid) {
       const int64_t page = (int64_t)btab[page_entry(a, j >> 4)] * a.num_kv_heads + h;
       const int o = j & 15;
-      const uint8_t *kp = a.k_cache + page * kKPage;
-      // record of coordinate chunk g: code planes 0..2 and signs of 32 coordinates
-      const uint4 C0 = *reinterpret_cast<const uint4 *>(kp + k_record(0, o));
-      const uint4 C1 = *reinterpret_cast<const uint4 *>(kp + k_record(1, o));
-      const uint4 C2 = *reinterpret_cast<const uint4 *>(kp + k_record(2, o));
-      const uint4 C3 = *reinterpret_cast<const uint4 *>(kp + k_record(3, o));
-      const float nk = (float)*reinterpret_cast<const _Float16 *>(kp + kKNorm + 2 * o);
-      const float gm = (float)*reinterpret_cast<const _Float16 *>(kp + kKGamma + 2 * o);
-      nv = (float)*reinterpret_cast<const _Float16 *>(a.v_cache + page * kVPage + kVNorm + 2 * o);
-      const uint32_t w0[4] = {C0.x, C1.x, C2.x, C3.x};
-      const uint32_t w1[4] = {C0.y, C1.y, C2.y, C3.y};
-      const uint32_t w2[4] = {C0.z, C1.z, C2.z, C3.z};
-      const uint32_t wq[4] = {C0.w, C1.w, C2.w, C3.w};
+      const uint8_t *kp = a.k_cache + page * KP;
+      // record of coordinate chunk w: BITS code-plane words and the sign word
+      // of 32 coordinates
+      uint32_t wp[4][BITS + 1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int f = 0; f <= BITS; ++f) wp[w][f] = *reinterpret_cast<const uint32_t *>(kp + RB * (16 * w + o) + 4 * f);
+      const float nk = (float)*reinterpret_cast<const _Float16 *>(kp + k_norm_off(BITS) + 2 * o);
+      const float gm = (float)*reinterpret_cast<const _Float16 *>(kp + k_norm_off(BITS) + 32 + 2 * o);
+      nv = (float)*reinterpret_cast<const _Float16 *>(a.v_cache + page * VP + v_norm_off(BITS) + 2 * o);
       float dk[G], ds[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -275,9 +275,11 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
 #pragma unroll 8
         for (int bb = 0; bb < 32; ++bb) {
           const int i = w * 32 + bb;
-          const int idx = ((w0[w] >> bb) & 1) | (((w1[w] >> bb) & 1) << 1) | (((w2[w] >> bb) & 1) << 2);
+          int idx = 0;
+#pragma unroll
+          for (int f = 0; f < BITS; ++f) idx |= ((wp[w][f] >> bb) & 1) << f;
           const float cv = lut[idx];
-          const float sg = ((wq[w] >> bb) & 1) ? 1.0f : -1.0f;
+          const float sg = ((wp[w][BITS] >> bb) & 1) ? 1.0f : -1.0f;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             dk[g] = fmaf(qp[g * 128 + i], cv, dk[g]);
@@ -310,17 +312,22 @@ __global__ __launch_bounds__(256) void split_valu_kernel(DecodeArgs a) {
       for (int pg = 0; pg < 4; ++pg) {
         const int tok0 = cbase + pg * 16;
         if (tok0 >= s1) break;
-        const uint8_t *vp = a.v_cache + ((int64_t)btab[page_entry(a, tok0 >> 4)] * a.num_kv_heads + h) * kVPage;
-        const uint32_t a0 = *reinterpret_cast<const uint16_t *>(vp + 2 * lane);
-        const uint32_t a1 = *reinterpret_cast<const uint16_t *>(vp + kVPlane + 2 * lane);
-        const uint32_t a2 = *reinterpret_cast<const uint16_t *>(vp + 2 * kVPlane + 2 * lane);
-        const uint32_t b0 = *reinterpret_cast<const uint16_t *>(vp + 128 + 2 * lane);
-        const uint32_t b1 = *reinterpret_cast<const uint16_t *>(vp + kVPlane + 128 + 2 * lane);
-        const uint32_t b2 = *reinterpret_cast<const uint16_t *>(vp + 2 * kVPlane + 128 + 2 * lane);
+        const uint8_t *vp = a.v_cache + ((int64_t)btab[page_entry(a, tok0 >> 4)] * a.num_kv_heads + h) * VP;
+        // plane words of coordinates lane and lane + 64 (16 token bits each)
+        uint32_t pa[BITS], pb[BITS];
+#pragma unroll
+        for (int f = 0; f < BITS; ++f) {
+          pa[f] = *reinterpret_cast<const uint16_t *>(vp + kVPlane * f + 2 * lane);
+          pb[f] = *reinterpret_cast<const uint16_t *>(vp + kVPlane * f + 128 + 2 * lane);
+        }
 #pragma unroll 4
         for (int tt = 0; tt < 16; ++tt) {
-          const int ia = ((a0 >> tt) & 1) | (((a1 >> tt) & 1) << 1) | (((a2 >> tt) & 1) << 2);
-          const int ib = ((b0 >> tt) & 1) | (((b1 >> tt) & 1) << 1) | (((b2 >> tt) & 1) << 2);
+          int ia = 0, ib = 0;
+#pragma unroll
+          for (int f = 0; f < BITS; ++f) {
+            ia |= ((pa[f] >> tt) & 1) << f;
+            ib |= ((pb[f] >> tt) & 1) << f;
+          }
           const float ca = lut[ia], cb = lut[ib];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
@@ -1882,7 +1889,12 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
 template <int G>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t stream) {
   dim3 grid((unsigned)(a.num_seqs * a.q_len), (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
-  hipLaunchKernelGGL(split_valu_kernel<G>, grid, dim3(256), 0, stream, a);
+  switch (a.cb.bits) {
+    case 2: hipLaunchKernelGGL((split_valu_kernel<G, 2>), grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((split_valu_kernel<G, 3>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((split_valu_kernel<G, 4>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1948,7 +1960,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups, (unsigned)a.group), dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (prefill_uses_mfma(a.q_len, a.group)) {
+    if (prefill_uses_mfma(a.q_len, a.group, a.cb.bits)) {
       e = launch_prefill(a, stream);
     } else {
       switch (group_capacity(a.group)) {

@@ -147,10 +147,11 @@ __device__ __forceinline__ void pieces(const In<PC> &r, v8s (&x)[4][PC]) {
   }
 }
 
-// Per round LDS state.
+// Per round LDS state (pages of BITS-bit codes).
+template <int BITS>
 struct RoundLds {
-  uint8_t kimg[kTiles][kKPage];                 // K page images
-  uint8_t vimg[kTiles][kVPage];                 // V page images
+  uint8_t kimg[kTiles][k_page_bytes(BITS)];     // K page images
+  uint8_t vimg[kTiles][v_page_bytes(BITS)];     // V page images
   _Float16 ehi[kTiles][kTok][kEHalves];         // residual * 256 (hi), slot order
   _Float16 elo[kTiles][kTok][kEHalves];         // remainder (lo)
   int blk[kTiles][kTok], off[kTiles][kTok], valid[kTiles][kTok];
@@ -228,6 +229,72 @@ __device__ __forceinline__ void key_steps(std::integer_sequence<int, Q...>, cons
   (key_step<Q>(ky, T, r256, c0, c1, c2, c3, kb, es, g2), ...);
 }
 
+// Other code widths (2 and 4 bits) take the same steps with NT = 2^(B-1) - 1
+// positive thresholds: c = #{k : t_k < |y|} in thermometer masks A_1..A_NT,
+// and bit p of c is the xor of the A_j with 2^p | j (floor(c / 2^p) counts
+// them), so plane p < B - 1 of the rank is ~(P ^ that xor) and plane B - 1 is P.
+template <int B>
+__device__ __forceinline__ void code_masks(const uint64_t (&A)[(1 << (B - 1)) - 1], uint64_t P, uint64_t (&pl)[B]) {
+  constexpr int NT = (1 << (B - 1)) - 1;
+#pragma unroll
+  for (int p = 0; p < B - 1; ++p) {
+    uint64_t x = P;
+#pragma unroll
+    for (int j = 1; j <= NT; ++j)
+      if (j % (1 << p) == 0) x ^= A[j - 1];
+    pl[p] = ~x;
+  }
+  pl[B - 1] = P;
+}
+template <int B, int Q>
+__device__ __forceinline__ void value_step_b(const v4f (&vy)[8], const float (&T)[(1 << (B - 1)) - 1],
+                                             uint32_t (&vb)[B]) {
+  constexpr int m = Q >> 2, i = Q & 3, NT = (1 << (B - 1)) - 1;
+  const float y = vy[m][i], ay = fabsf(y);
+  uint64_t A[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) A[k] = __ballot(ay > T[k]);
+  uint64_t pl[B];
+  code_masks<B>(A, __ballot(y > 0.0f), pl);
+#pragma unroll
+  for (int p = 0; p < B; ++p) put_mask<Q>(vb[p], pl[p]);
+}
+template <int B, int... Q>
+__device__ __forceinline__ void value_steps_b(std::integer_sequence<int, Q...>, const v4f (&vy)[8],
+                                              const float (&T)[(1 << (B - 1)) - 1], uint32_t (&vb)[B]) {
+  (value_step_b<B, Q>(vy, T, vb), ...);
+}
+template <int B, int Q>
+__device__ __forceinline__ void key_step_b(const v4f (&ky)[8], const float (&T)[4][(1 << (B - 1)) - 1],
+                                           const float (&r256)[4], const float (&cp)[1 << (B - 1)], uint32_t (&kb)[B],
+                                           float (&es)[8][4], float (&g2)[4]) {
+  constexpr int n = Q >> 2, i = Q & 3, NT = (1 << (B - 1)) - 1;
+  const float y = ky[n][i], ay = fabsf(y);
+  const bool pp = y > 0.0f;
+  uint64_t A[NT];
+  float lv = cp[0];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    const bool ak = ay > T[i][k];
+    A[k] = __ballot(ak);
+    lv = ak ? cp[k + 1] : lv;
+  }
+  uint64_t pl[B];
+  code_masks<B>(A, __ballot(pp), pl);
+#pragma unroll
+  for (int p = 0; p < B; ++p) put_mask<Q>(kb[p], pl[p]);
+  const float e = fmaf(y, r256[i], pp ? -lv : lv);
+  es[n][i] = e;
+  g2[i] = fmaf(e, e, g2[i]);
+}
+template <int B, int... Q>
+__device__ __forceinline__ void key_steps_b(std::integer_sequence<int, Q...>, const v4f (&ky)[8],
+                                            const float (&T)[4][(1 << (B - 1)) - 1], const float (&r256)[4],
+                                            const float (&cp)[1 << (B - 1)], uint32_t (&kb)[B], float (&es)[8][4],
+                                            float (&g2)[4]) {
+  (key_step_b<B, Q>(ky, T, r256, cp, kb, es, g2), ...);
+}
+
 // Sign masks of register (u, i) = 4u + i of the projection of tile TL: lanes
 // of token 4(l/16) + i, row 16(2w + u) + l%16.
 template <int TL, int... Q>
@@ -237,8 +304,8 @@ __device__ __forceinline__ void sign_masks(std::integer_sequence<int, Q...>, con
 
 // Rows 32w .. 32w+31 of z = (S H) e for tile TL of the round: three f16
 // passes (e_hi S_hi + e_hi S_lo + e_lo S_hi) per K step, then its sign masks.
-template <int TL>
-__device__ __forceinline__ void qjl_tile(const RoundLds &L, int l16, int lg, const v8s (&shi)[2][4],
+template <int TL, int BITS>
+__device__ __forceinline__ void qjl_tile(const RoundLds<BITS> &L, int l16, int lg, const v8s (&shi)[2][4],
                                          const v8s (&slo)[2][4], uint32_t &sbits) {
   v4f z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -254,14 +321,17 @@ __device__ __forceinline__ void qjl_tile(const RoundLds &L, int l16, int lg, con
   }
   sign_masks<TL>(std::make_integer_sequence<int, 8>{}, z, sbits);
 }
-template <int... TL>
-__device__ __forceinline__ void qjl_tiles(std::integer_sequence<int, TL...>, const RoundLds &L, int l16, int lg,
+template <int BITS, int... TL>
+__device__ __forceinline__ void qjl_tiles(std::integer_sequence<int, TL...>, const RoundLds<BITS> &L, int l16, int lg,
                                           const v8s (&shi)[2][4], const v8s (&slo)[2][4], uint32_t &sbits) {
-  (qjl_tile<TL>(L, l16, lg, shi, slo, sbits), ...);
+  (qjl_tile<TL, BITS>(L, l16, lg, shi, slo, sbits), ...);
 }
 
-template <int DT>
+template <int DT, int BITS>
 __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t num_tiles) {
+  constexpr int NT = (1 << (BITS - 1)) - 1, NL = 1 << (BITS - 1);  // positive thresholds and levels
+  constexpr int KP = k_page_bytes(BITS), VP = v_page_bytes(BITS), RB = k_rec_bytes(BITS);
+  constexpr int KN = k_norm_off(BITS), VN = v_norm_off(BITS);
   constexpr bool kF16 = DT == TQ_F16;
   constexpr int PC = DT == TQ_F32 ? 3 : 1;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -278,20 +348,19 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
   float *const norms_out = a.norms_out;
   const int64_t nrounds = (num_tiles + kTiles - 1) / kTiles;
 
-  __shared__ __align__(16) RoundLds L;
+  __shared__ __align__(16) RoundLds<BITS> L;
 
   const HSets hs = make_hsets(lane, kF16 ? (uint16_t)0x3C00u : (uint16_t)0x3F80u);
 
   // positive thresholds and 256 x positive levels, uniform.  The levels are
   // separate scalars, chosen by selects: an array indexed by the code would
   // be moved to LDS and cost a load per coordinate.
-  float tpos[3];
+  float tpos[NT], cp[NL];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) tpos[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.t[4 + k])));
-  const float cp0 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[4])));
-  const float cp1 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[5])));
-  const float cp2 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[6])));
-  const float cp3 = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[7])));
+  for (int k = 0; k < NT; ++k) tpos[k] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.t[NL + k])));
+#pragma unroll
+  for (int k = 0; k < NL; ++k)
+    cp[k] = kResScale * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.cb.c[NL + k])));
 
   // This wave's QJL rows 32w .. 32w+31 of S H as the B operand of the f16
   // MFMA, K slots in the staged residual's order: slot s <-> coordinate
@@ -374,16 +443,21 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         s2 += xchg16(s2, lane);
         s2 += xchg32(s2, lane);
         const float sn = sqrtf(s2);  // = sqrt(128) |v|
-        float T[3];
+        float T[NT];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) T[k] = tpos[k] * sn;
-        uint32_t vb[3] = {0u, 0u, 0u};
-        value_steps(std::make_integer_sequence<int, 32>{}, vy, T[0], T[1], T[2], vb);
+        for (int k = 0; k < NT; ++k) T[k] = tpos[k] * sn;
+        uint32_t vb[BITS];
+#pragma unroll
+        for (int p = 0; p < BITS; ++p) vb[p] = 0u;
+        if constexpr (BITS == 3)
+          value_steps(std::make_integer_sequence<int, 32>{}, vy, T[0], T[1], T[2], vb);
+        else
+          value_steps_b<BITS>(std::make_integer_sequence<int, 32>{}, vy, T, vb);
         // lane L = 2(4m + i) + hf holds the words of coordinates 16m + 4g + i, g = 2hf, 2hf+1
         {
           const int q = lane >> 1, hf = lane & 1, m = q >> 2, i = q & 3;
 #pragma unroll
-          for (int p = 0; p < 3; ++p) {
+          for (int p = 0; p < BITS; ++p) {
             uint16_t *img = reinterpret_cast<uint16_t *>(L.vimg[wave] + kVPlane * p);
             img[16 * m + 4 * (2 * hf) + i] = (uint16_t)vb[p];
             img[16 * m + 4 * (2 * hf + 1) + i] = (uint16_t)(vb[p] >> 16);
@@ -391,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
         }
         const float nv = sn * kInvSqrt128;
         if (lg == 0) {
-          reinterpret_cast<_Float16 *>(L.vimg[wave] + kVNorm)[l16] = to_half_sat(nv);
+          reinterpret_cast<_Float16 *>(L.vimg[wave] + VN)[l16] = to_half_sat(nv);
           L.nout[wave][l16][2] = nv;
         }
       }
@@ -409,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
             for (int pc = 0; pc < PC; ++pc) c = mfma16<kF16>(xk[k][pc], hop(hs, k, n), c);
           ky[n] = c;
         }
-        float sn[4], r256[4], T[4][3];
+        float sn[4], r256[4], T[4][NT];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float s2 = 0.0f;
@@ -422,21 +496,26 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           sn[i] = sqrtf(s2);
           r256[i] = sn[i] > 0.0f ? kResScale / sn[i] : 0.0f;
 #pragma unroll
-          for (int k = 0; k < 3; ++k) T[i][k] = tpos[k] * sn[i];
+          for (int k = 0; k < NT; ++k) T[i][k] = tpos[k] * sn[i];
         }
-        uint32_t kb[3] = {0u, 0u, 0u};
+        uint32_t kb[BITS];
+#pragma unroll
+        for (int p = 0; p < BITS; ++p) kb[p] = 0u;
         float g2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float es[8][4];
-        key_steps(std::make_integer_sequence<int, 32>{}, ky, T, r256, cp0, cp1, cp2, cp3, kb, es, g2);
+        if constexpr (BITS == 3)
+          key_steps(std::make_integer_sequence<int, 32>{}, ky, T, r256, cp[0], cp[1], cp[2], cp[3], kb, es, g2);
+        else
+          key_steps_b<BITS>(std::make_integer_sequence<int, 32>{}, ky, T, r256, cp, kb, es, g2);
         // lane L = 2(4n + i) + hf holds 16-bit pieces (coordinates 16n..+15) of tokens 4g + i, g = 2hf, 2hf+1;
         // piece n of plane p of token t is half (n & 1) of word p of record (n / 2, t)
         {
           const int q = lane >> 1, hf = lane & 1, n = q >> 2, i = q & 3;
           uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[wave]);
 #pragma unroll
-          for (int p = 0; p < 3; ++p) {
-            img[k_record(n >> 1, 4 * (2 * hf) + i) / 2 + 2 * p + (n & 1)] = (uint16_t)kb[p];
-            img[k_record(n >> 1, 4 * (2 * hf + 1) + i) / 2 + 2 * p + (n & 1)] = (uint16_t)(kb[p] >> 16);
+          for (int p = 0; p < BITS; ++p) {
+            img[RB * (16 * (n >> 1) + 4 * (2 * hf) + i) / 2 + 2 * p + (n & 1)] = (uint16_t)kb[p];
+            img[RB * (16 * (n >> 1) + 4 * (2 * hf + 1) + i) / 2 + 2 * p + (n & 1)] = (uint16_t)(kb[p] >> 16);
           }
         }
         // residual halves, slot 8 (l%16) + n of token 4(l/16) + i
@@ -462,8 +541,8 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           const float nk = sn[i] * kInvSqrt128;
           const int tok = 4 * lg + i;
           if (l16 == 0) {
-            reinterpret_cast<_Float16 *>(L.kimg[wave] + kKNorm)[tok] = to_half_sat(nk);
-            reinterpret_cast<_Float16 *>(L.kimg[wave] + kKGamma)[tok] = to_half_sat(gam);
+            reinterpret_cast<_Float16 *>(L.kimg[wave] + KN)[tok] = to_half_sat(nk);
+            reinterpret_cast<_Float16 *>(L.kimg[wave] + KN + 32)[tok] = to_half_sat(gam);
             L.nout[wave][tok][0] = nk;
             L.nout[wave][tok][1] = gam;
           }
@@ -493,8 +572,8 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
       // half u of the sign word of record (w, t)
       const int q = lane >> 1, hf = lane & 1, tl = q >> 3, u = (q >> 2) & 1, i = q & 3;
       uint16_t *img = reinterpret_cast<uint16_t *>(L.kimg[tl]);
-      img[k_record(wave, 4 * (2 * hf) + i) / 2 + 2 * kKSignField + u] = (uint16_t)sbits;
-      img[k_record(wave, 4 * (2 * hf + 1) + i) / 2 + 2 * kKSignField + u] = (uint16_t)(sbits >> 16);
+      img[RB * (16 * wave + 4 * (2 * hf) + i) / 2 + 2 * BITS + u] = (uint16_t)sbits;
+      img[RB * (16 * wave + 4 * (2 * hf + 1) + i) / 2 + 2 * BITS + u] = (uint16_t)(sbits >> 16);
     }
     lds_barrier();
 
@@ -512,33 +591,42 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
       const int hh = (int)(tt % H);
       if (L.full[tl]) {
         const int b0 = L.blk[tl][0];
-        uint8_t *kp = k_cache + ((int64_t)b0 * H + hh) * kKPage;
-        uint8_t *vp = v_cache + ((int64_t)b0 * H + hh) * kVPage;
-        if (tid < kKPage / 16) {
+        uint8_t *kp = k_cache + ((int64_t)b0 * H + hh) * KP;
+        uint8_t *vp = v_cache + ((int64_t)b0 * H + hh) * VP;
+        if (tid < KP / 16) {
           *reinterpret_cast<uint4 *>(kp + 16 * tid) = *reinterpret_cast<const uint4 *>(L.kimg[tl] + 16 * tid);
-        } else if (tid < kKPage / 16 + kVPage / 16) {
-          const int q = tid - kKPage / 16;
+        } else if (tid < KP / 16 + VP / 16) {
+          const int q = tid - KP / 16;
           *reinterpret_cast<uint4 *>(vp + 16 * q) = *reinterpret_cast<const uint4 *>(L.vimg[tl] + 16 * q);
         }
       } else {
-        // token by token: K records (the four 16-byte chunk records of the
-        // token), the scalars, and value bits merged into their pages atomically
+        // token by token: K records (the four chunk records of the token,
+        // RB bytes each), the scalars, and value bits merged into their pages
+        // atomically
         if (tid < 4 * kTok) {
           const int n = tid >> 2, g = tid & 3;
           if (L.valid[tl][n]) {
-            uint8_t *kp = k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
-            *reinterpret_cast<uint4 *>(kp + k_record(g, L.off[tl][n])) =
-                *reinterpret_cast<const uint4 *>(L.kimg[tl] + k_record(g, n));
+            uint8_t *kp = k_cache + ((int64_t)L.blk[tl][n] * H + hh) * KP;
+            uint8_t *dst = kp + RB * (16 * g + L.off[tl][n]);
+            const uint8_t *src = L.kimg[tl] + RB * (16 * g + n);
+            if constexpr (RB == 16) {
+              *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+            } else {
+#pragma unroll
+              for (int f = 0; f < RB / 4; ++f)
+                reinterpret_cast<uint32_t *>(dst)[f] = reinterpret_cast<const uint32_t *>(src)[f];
+            }
           }
         } else if (tid < 5 * kTok) {
           const int n = tid - 4 * kTok;
           if (L.valid[tl][n]) {
-            uint8_t *kp = k_cache + ((int64_t)L.blk[tl][n] * H + hh) * kKPage;
-            uint8_t *vp = v_cache + ((int64_t)L.blk[tl][n] * H + hh) * kVPage;
+            uint8_t *kp = k_cache + ((int64_t)L.blk[tl][n] * H + hh) * KP;
+            uint8_t *vp = v_cache + ((int64_t)L.blk[tl][n] * H + hh) * VP;
             const int o = L.off[tl][n];
-            *reinterpret_cast<uint16_t *>(kp + kKNorm + 2 * o) = *reinterpret_cast<const uint16_t *>(L.kimg[tl] + kKNorm + 2 * n);
-            *reinterpret_cast<uint16_t *>(kp + kKGamma + 2 * o) = *reinterpret_cast<const uint16_t *>(L.kimg[tl] + kKGamma + 2 * n);
-            *reinterpret_cast<uint16_t *>(vp + kVNorm + 2 * o) = *reinterpret_cast<const uint16_t *>(L.vimg[tl] + kVNorm + 2 * n);
+            *reinterpret_cast<uint16_t *>(kp + KN + 2 * o) = *reinterpret_cast<const uint16_t *>(L.kimg[tl] + KN + 2 * n);
+            *reinterpret_cast<uint16_t *>(kp + KN + 32 + 2 * o) =
+                *reinterpret_cast<const uint16_t *>(L.kimg[tl] + KN + 32 + 2 * n);
+            *reinterpret_cast<uint16_t *>(vp + VN + 2 * o) = *reinterpret_cast<const uint16_t *>(L.vimg[tl] + VN + 2 * n);
           }
         }
         // value bits, one token at a time: wave w merges tokens w, w + 4, ..
@@ -551,9 +639,9 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncodeArgs a, int64_t nu
           if (!__builtin_amdgcn_readfirstlane((int)L.valid[tl][n])) continue;  // uniform
           const int bn = __builtin_amdgcn_readfirstlane(L.blk[tl][n]);
           const int o = __builtin_amdgcn_readfirstlane(L.off[tl][n]);
-          uint8_t *vp = v_cache + ((int64_t)bn * H + hh) * kVPage;
+          uint8_t *vp = v_cache + ((int64_t)bn * H + hh) * VP;
 #pragma unroll
-          for (int p = 0; p < 3; ++p) {
+          for (int p = 0; p < BITS; ++p) {
             const uint32_t w2 = reinterpret_cast<const uint32_t *>(L.vimg[tl] + kVPlane * p)[lane];
             const uint32_t b = ((w2 >> n) & 1u) | (((w2 >> (16 + n)) & 1u) << 16);
             const uint32_t set = b << o, clr = (0x10001u << o) & ~set;
@@ -579,7 +667,12 @@ template <int DT>
 hipError_t launch_dt(const EncodeArgs &a, int64_t tiles, hipStream_t stream) {
   const int64_t rounds = (tiles + kTiles - 1) / kTiles;
   const int64_t grid = rounds < 512 ? rounds : 512;  // persistent: two workgroups per CU
-  hipLaunchKernelGGL(encode_kernel<DT>, dim3((unsigned)grid), dim3(256), 0, stream, a, tiles);
+  switch (a.cb.bits) {
+    case 2: hipLaunchKernelGGL((encode_kernel<DT, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a, tiles); break;
+    case 3: hipLaunchKernelGGL((encode_kernel<DT, 3>), dim3((unsigned)grid), dim3(256), 0, stream, a, tiles); break;
+    case 4: hipLaunchKernelGGL((encode_kernel<DT, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a, tiles); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -71,8 +71,11 @@ void lloyd_max_positive_half(int half, std::vector<double> &c) {
 }
 
 bool codebook_supported(int head_dim, int bits, int qjl_dim) {
-  return head_dim == tq::kHeadDim && bits == 3 && qjl_dim == tq::kQjlDim;
+  return head_dim == tq::kHeadDim && bits >= 2 && bits <= 4 && qjl_dim == tq::kQjlDim;
 }
+// Bit width of an initialised codebook (3 for a struct that is not one: the
+// size queries accept any pointer).
+int cb_bits(const tq_codebook *cb) { return cb && cb->magic == tq::kMagic ? cb->bits : 3; }
 
 tq_status check_cb(const tq_codebook *cb) {
   if (!cb) return fail(TQ_ERR_INVALID_ARGUMENT, "codebook is NULL");
@@ -83,9 +86,13 @@ tq_status check_cb(const tq_codebook *cb) {
 
 tq::Codebook device_codebook(const tq_codebook *cb) {
   tq::Codebook d;
-  for (int i = 0; i < 8; ++i) d.c[i] = cb->centroids[i];
-  for (int i = 0; i < 7; ++i) d.t[i] = cb->thresholds[i];
+  std::memset(&d, 0, sizeof d);
+  const int n = 1 << cb->bits;
+  for (int i = 0; i < n; ++i) d.c[i] = cb->centroids[i];
+  for (int i = 0; i + 1 < n; ++i) d.t[i] = cb->thresholds[i];
+  d.bits = cb->bits;
   d.qjl_scale = cb->qjl_scale;
+  if (cb->bits != 3) return d;  // the bit-plane form serves the 3-bit matrix-core passes
   // c4 = -b0 - b1 + b2 + b3, c5 = b0 - b1 + b2 - b3, c6 = -b0 + b1 + b2 - b3,
   // c7 = b0 + b1 + b2 + b3 (signs of B_p at the codes 4..7), solved in double.
   const double c4 = cb->centroids[4], c5 = cb->centroids[5], c6 = cb->centroids[6],
@@ -126,9 +133,10 @@ struct SplitPlan {
 constexpr int kBalMinTiles = 4;  // and per is a multiple of 4 (one tile per wave and step)
 constexpr int kBalMaxTiles = tq::kMaxMfmaSplitTokens / 128;
 
-SplitPlan plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested) {
+SplitPlan plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int max_ctx, int requested,
+                      int bits) {
   SplitPlan p{};
-  if (tq::decode_uses_mfma(q_len, group)) {
+  if (tq::decode_uses_mfma(q_len, group, bits)) {
     const int mrows = group * std::min(q_len, tq::decode_positions_per_launch(group));
     const long slots = mrows > 4 ? 256 : 512;
     const long tmax = (std::max(max_ctx, 0) + 127) / 128;
@@ -157,7 +165,7 @@ SplitPlan plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int 
     st = requested;
   } else {
     long per_seq = q_len;
-    if (tq::prefill_uses_mfma(q_len, group)) {
+    if (tq::prefill_uses_mfma(q_len, group, bits)) {
       const int bq = tq::prefill_block_queries(group);
       per_seq = (q_len + bq - 1) / bq;
     }
@@ -189,8 +197,8 @@ int decode_hot_parts(int hot_max) { return hot_max > 0 ? (hot_max + kHotChunk - 
 // run as one launch per group of 8 / group of them, each reading the cache
 // once.  Up to 4 such launches beat one prefill pass (measured at 32,768 and
 // 131,072 cached tokens); beyond, the prefill pass takes the block.
-bool decode_uses_mfma(int q_len, int group) {
-  if (q_len < 1 || group < 1 || group > 8) return false;
+bool decode_uses_mfma(int q_len, int group, int bits) {
+  if (bits != 3 || q_len < 1 || group < 1 || group > 8) return false;
   const int per = 8 / group;
   return (q_len + per - 1) / per <= 4;
 }
@@ -258,7 +266,8 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
   if (!d_tables) return fail(TQ_ERR_INVALID_ARGUMENT, "d_tables is NULL");
   if ((uintptr_t)d_tables % 16 != 0) return fail(TQ_ERR_INVALID_ARGUMENT, "d_tables must be 16-byte aligned");
   if (!codebook_supported(head_dim, bits, tq::kQjlDim))
-    return fail(TQ_ERR_UNSUPPORTED, "only head_dim=128, bits=3 are supported (got %d, %d)", head_dim, bits);
+    return fail(TQ_ERR_UNSUPPORTED, "only head_dim=128 with bits 2, 3 or 4 are supported (got %d, %d)", head_dim,
+                bits);
   tq_codebook c;
   std::memset(&c, 0, sizeof c);
   c.head_dim = head_dim;
@@ -331,8 +340,8 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
   return TQ_OK;
 }
 
-size_t tq_k_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::kKPage : 0; }
-size_t tq_v_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::kVPage : 0; }
+size_t tq_k_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::k_page_bytes(cb_bits(cb)) : 0; }
+size_t tq_v_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::v_page_bytes(cb_bits(cb)) : 0; }
 
 tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_dtype in_dtype,
                        int64_t num_tokens, int num_kv_heads, int64_t tok_stride,
@@ -392,16 +401,16 @@ int walk_span(int max_context_len, int q_len, int window) {
   return (int)std::min<int64_t>(max_context_len, (int64_t)window + q_len - 1 + (tq::kBlock - 1));
 }
 
-size_t decode_workspace(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
+size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
                         int tokens_per_split, int hot_parts, int window = 0) {
   if (num_seqs < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 || window < 0)
     return 0;
   max_context_len = walk_span(max_context_len, q_len, window);
   const int grp = num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
-  const int ns = plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split).num_splits;
+  const int ns = plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split, bits).num_splits;
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   // the matrix-core split pass forms its query operands itself: partials only
-  const bool mfma = grp > 0 && tq::decode_uses_mfma(q_len, grp);
+  const bool mfma = grp > 0 && tq::decode_uses_mfma(q_len, grp, bits);
   const size_t words = (mfma ? 0 : tq::decode_qprep_floats(rows)) + tq::decode_partial_floats(rows, ns + hot_parts);
   return words * sizeof(float);
 }
@@ -454,13 +463,14 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   const int span = walk_span(max_context_len, q_len, window);  // keys one sequence's walk covers
   if (tokens_per_split < 0 || (tokens_per_split > 0 && tokens_per_split % 256 != 0))
     return fail(TQ_ERR_INVALID_ARGUMENT, "tokens_per_split must be 0 or a positive multiple of 256");
-  if (tokens_per_split > tq::kMaxMfmaSplitTokens && tq::decode_uses_mfma(q_len, group))
+  const int bits = cb->bits;
+  if (tokens_per_split > tq::kMaxMfmaSplitTokens && tq::decode_uses_mfma(q_len, group, bits))
     return fail(TQ_ERR_UNSUPPORTED, "tokens_per_split %d exceeds the %d tokens per chunk of this pass",
                 tokens_per_split, tq::kMaxMfmaSplitTokens);
   if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
     return fail(TQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
   if ((int64_t)num_seqs * q_len > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "num_seqs * q_len too large");
-  const SplitPlan plan = plan_splits(num_seqs, q_len, num_kv_heads, group, span, tokens_per_split);
+  const SplitPlan plan = plan_splits(num_seqs, q_len, num_kv_heads, group, span, tokens_per_split, bits);
   const int ns = plan.num_splits;
   if (ns > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many splits (%d); raise tokens_per_split", ns);
   if ((int64_t)num_seqs * num_kv_heads * ((span + 127) / 128) > 0x7fffffffLL)
@@ -480,7 +490,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     hot_parts = tq::decode_hot_parts(hot->max);
     if (ns + hot_parts > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many partial records per row");
   }
-  const size_t need = decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
+  const size_t need = decode_workspace(bits, num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
                                        tokens_per_split, hot_parts, window);
   if (noalloc) {
     // every check above is on the host; the scratch array's address is
@@ -535,7 +545,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.pos_count = q_len;
   a.qprep = nullptr;
   float *rest = (float *)workspace;
-  if (tq::decode_uses_mfma(q_len, group)) {
+  if (tq::decode_uses_mfma(q_len, group, bits)) {
     a.qk_tiles = tq::decode_qk_tiles(group * std::min(q_len, tq::decode_positions_per_launch(group)));
   } else {
     a.qprep = rest;
@@ -561,8 +571,9 @@ extern "C" {
 size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
                                  int num_q_heads, int num_kv_heads, int max_context_len,
                                  int tokens_per_split) {
-  (void)cb;
-  return decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0);
+
+  return decode_workspace(cb_bits(cb), num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
+                          tokens_per_split, 0);
 }
 
 tq_status tq_decode_attention(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
@@ -595,9 +606,9 @@ size_t tq_decode_noalloc_scratch_bytes(void) { return tq::kNoAllocScratchBytes; 
 size_t tq_decode_window_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len, int num_q_heads,
                                         int num_kv_heads, int max_context_len, int window,
                                         int tokens_per_split) {
-  (void)cb;
+
   if (window < 1) return 0;
-  return decode_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0,
+  return decode_workspace(cb_bits(cb), num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0,
                           window);
 }
 
@@ -618,9 +629,9 @@ tq_status tq_decode_attention_window(const tq_codebook *cb, const void *q, tq_dt
 size_t tq_decode_hot_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads,
                                      int num_kv_heads, int max_context_len, int hot_max,
                                      int tokens_per_split) {
-  (void)cb;
+
   if (hot_max < 0) return 0;
-  return decode_workspace(num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, tokens_per_split,
+  return decode_workspace(cb_bits(cb), num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, tokens_per_split,
                           tq::decode_hot_parts(hot_max));
 }
 

@@ -31,9 +31,21 @@ constexpr int kVNorm = 768;
 // Byte offset of the record of coordinate chunk g, token t of a K page.
 constexpr int k_record(int g, int t) { return 16 * (16 * g + t); }
 
+// Page geometry for b-bit codes (b = 2, 3, 4): K records of b code-plane
+// words and one sign word per (32-coordinate chunk, token), then the halves
+// n and gamma; V pages of b coordinate-major planes, then n.
+constexpr int k_rec_bytes(int b) { return 4 * (b + 1); }
+constexpr int k_norm_off(int b) { return 64 * k_rec_bytes(b); }
+constexpr int k_page_bytes(int b) { return k_norm_off(b) + 64; }
+constexpr int v_norm_off(int b) { return 256 * b; }
+constexpr int v_page_bytes(int b) { return v_norm_off(b) + 32; }
+static_assert(k_page_bytes(3) == kKPage && v_page_bytes(3) == kVPage && k_norm_off(3) == kKNorm &&
+                  v_norm_off(3) == kVNorm, "3-bit geometry");
+
 struct Codebook {
-  float c[8];        // ascending levels
-  float t[7];        // thresholds
+  float c[16];       // ascending levels (2^bits used)
+  float t[15];       // thresholds (2^bits - 1 used)
+  int bits;          // 2, 3 or 4
   float qjl_scale;   // sqrt(pi/2)/m
   // Bit-plane form of the levels: with B_p = 1 - 2 b_p for the code bits
   // b0, b1, b2 and their xor, c[idx] = -(beta0 B0 + beta1 B1 + beta2 B2 + beta3 Bx)
@@ -128,12 +140,12 @@ int decode_hot_parts(int hot_max);
 // and short query blocks (multi-token verify), one launch per group of
 // 8 / group positions, at most 4 launches; single-query decode with 16 heads
 // per KV head uses the vector pass, longer query blocks the prefill pass.
-bool decode_uses_mfma(int q_len, int group);
+bool decode_uses_mfma(int q_len, int group, int bits);
 int decode_positions_per_launch(int group);
 // Several queries per sequence (chunked prefill, causal) run on the
 // matrix-core prefill pass: 128 query rows (128 / group positions) per
 // workgroup.
-bool prefill_uses_mfma(int q_len, int group);
+bool prefill_uses_mfma(int q_len, int group, int bits);
 int prefill_block_queries(int group);
 int decode_qk_tiles(int rows);
 

@@ -414,8 +414,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
 
 }  // namespace
 
-bool prefill_uses_mfma(int q_len, int group) {
-  return q_len > 1 && !decode_uses_mfma(q_len, group) && group >= 1 && group <= kMaxGroup;
+bool prefill_uses_mfma(int q_len, int group, int bits) {
+  return bits == 3 && q_len > 1 && !decode_uses_mfma(q_len, group, bits) && group >= 1 && group <= kMaxGroup;
 }
 
 int prefill_block_queries(int group) { return kRows / group; }

@@ -22,27 +22,34 @@
  *     attention calls; work is enqueued on the caller's HIP stream
  *     (hipStream_t passed as void*, NULL = default stream) and is complete
  *     when that stream is.
- *   - Only head_dim = 128, qjl_dim = 128, 3-bit codes and 16-token blocks are
- *     supported; other values give TQ_ERR_UNSUPPORTED.
+ *   - Only head_dim = 128, qjl_dim = 128, 2-, 3- or 4-bit codes and 16-token
+ *     blocks are supported; other values give TQ_ERR_UNSUPPORTED.  3 bits
+ *     (the pages' method) decode on the matrix-core passes, 2 and 4 bits on
+ *     the vector pass.
  *   - Not checked (caller contract): block-table entries lie inside the
  *     pools, context lengths cover only slots that were encoded, and
  *     slot_mapping holds no duplicate slot.
  *
  * Page layout (little-endian; bit b of a byte has weight 2^b), one page per
- * (block, KV head), pools k_cache[num_blocks][num_kv_heads][1088] and
- * v_cache[num_blocks][num_kv_heads][800], slot = block * 16 + offset:
- *   K page: [0, 1024): 64 records of 16 bytes, record (chunk g, token t)
- *           at 16 (16 g + t) for g = 0..3; its 32-bit word f = 0..2 holds
+ * (block, KV head), pools k_cache[num_blocks][num_kv_heads][tq_k_page_bytes]
+ * and v_cache[num_blocks][num_kv_heads][tq_v_page_bytes], slot = block * 16 +
+ * offset.  For b-bit codes (b = cb->bits; 3 in the pages' method) and
+ * RB = 4 (b + 1) bytes per record:
+ *   K page (256 (b + 1) + 64 bytes; 1088 for b = 3):
+ *           [0, 64 RB): 64 records of RB bytes, record (chunk g, token t) at
+ *           RB (16 g + t) for g = 0..3; its 32-bit word f = 0 .. b-1 holds
  *           bit-plane f of the codes of coordinates 32g .. 32g+31
- *           (coordinate 32g + k at bit k), word 3 the QJL sign bits of
+ *           (coordinate 32g + k at bit k), word b the QJL sign bits of
  *           projection rows 32g .. 32g+31 (1 = projection >= 0);
- *           [1024, 1056): half norm of token t at 1024 + 2t;
- *           [1056, 1088): half residual length gamma at 1056 + 2t.
- *   V page: [256p, 256p+256), p = 0..2: bit-plane p, coordinate-major:
- *           coordinate i owns the 16-bit word at 256p + 2i, token t at its
- *           bit t; [768, 800): half norm of token t at 768 + 2t.
+ *           [64 RB, 64 RB + 32): half norm of token t at 64 RB + 2t;
+ *           [64 RB + 32, 64 RB + 64): half residual length gamma.
+ *   V page (256 b + 32 bytes; 800 for b = 3): [256p, 256p+256), p < b:
+ *           bit-plane p, coordinate-major: coordinate i owns the 16-bit word
+ *           at 256p + 2i, token t at its bit t; [256 b, 256 b + 32): half
+ *           norm of token t at 256 b + 2t.
  *   Code value = rank of the codebook level in ascending order.
- *   1088*8/(16*128) = 4.25 and 800*8/(16*128) = 3.125 bits per coordinate.
+ *   b = 3: 1088*8/(16*128) = 4.25 and 800*8/(16*128) = 3.125 bits per
+ *   coordinate; b = 2: 3.25 and 2.125; b = 4: 5.25 and 4.125.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -78,12 +85,12 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 } tq_dtype;
  * tq_codebook_device_bytes() bytes, which must outlive every call using it. */
 typedef struct tq_codebook {
   int32_t head_dim;        /* 128 */
-  int32_t bits;            /* 3 */
+  int32_t bits;            /* 2, 3 or 4 (the pages' method: 3) */
   int32_t qjl_dim;         /* 128 */
   int32_t block_size;      /* 16 */
   uint64_t qjl_seed;       /* seed of the generated S (0 if caller-supplied) */
-  float centroids[8];      /* ascending fp32 levels for N(0, 1/d) */
-  float thresholds[7];     /* fp32 midpoints of adjacent levels */
+  float centroids[16];     /* ascending fp32 levels for N(0, 1/d); 2^bits used */
+  float thresholds[15];    /* fp32 midpoints of adjacent levels; 2^bits - 1 used */
   float qjl_scale;         /* sqrt(pi/2) / qjl_dim */
   void *d_tables;          /* device, 16-byte aligned: S [m][d] fp32, S^T [d][m] fp32,
                               then S*H as half pairs (hi, lo = S*H - hi) in an
@@ -119,14 +126,17 @@ size_t tq_codebook_device_bytes(int head_dim, int qjl_dim);
  * call that copies host data to the device or synchronises).
  * qjl_host: NULL -> S generated from qjl_seed by tq_qjl_matrix; else the
  * caller's S (qjl_dim x head_dim fp32 row-major host array).
- * Errors: TQ_ERR_UNSUPPORTED for head_dim/bits/qjl_dim other than 128/3/128,
+ * bits 2, 3 or 4 (3 is the pages' method and runs on the matrix-core passes;
+ * 2 and 4 are codebook variants whose decode runs on the vector pass).
+ * Errors: TQ_ERR_UNSUPPORTED for head_dim/qjl_dim other than 128/128 or bits
+ * outside 2..4,
  * TQ_ERR_INVALID_ARGUMENT for null cb/d_tables or d_tables not 16-byte
  * aligned, TQ_ERR_HIP on copy failure. */
 tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl_seed,
                            const float *qjl_host, void *d_tables, void *stream);
 
-size_t tq_k_page_bytes(const tq_codebook *cb);   /* 1088 */
-size_t tq_v_page_bytes(const tq_codebook *cb);   /* 800 */
+size_t tq_k_page_bytes(const tq_codebook *cb);   /* 256 (bits + 1) + 64: 1088 for 3 bits */
+size_t tq_v_page_bytes(const tq_codebook *cb);   /* 256 bits + 32: 800 for 3 bits */
 
 /* ---- encode --------------------------------------------------------------
  * Compress num_tokens x num_kv_heads key and value vectors and store each

@@ -12,8 +12,7 @@ import torch
 import decode_attention_tq_amd as tq
 from oracle import codebook_fp32, decode_paged, encode_k, encode_v, gaussian_matrix
 from oracle.encode import residual_signs_from_codes
-from oracle.pages import (K_PAGE_BYTES, V_PAGE_BYTES, read_k_tokens_fast,
-                          read_v_tokens_fast)
+from oracle.pages import k_page_bytes, read_k_tokens_fast, read_v_tokens_fast, v_page_bytes
 
 CODE_BAND = 1e-5
 SIGN_BAND = 1e-5
@@ -24,14 +23,14 @@ QJL_SEED = 42
 _CB = {}
 
 
-def codebook(seed: int = QJL_SEED):
-    if seed not in _CB:
-        _CB[seed] = tq.tq_codebook_init(128, 3, seed, device="cuda")
-    return _CB[seed]
+def codebook(seed: int = QJL_SEED, bits: int = 3):
+    if (seed, bits) not in _CB:
+        _CB[(seed, bits)] = tq.tq_codebook_init(128, bits, seed, device="cuda")
+    return _CB[(seed, bits)]
 
 
-def oracle_tables(seed: int = QJL_SEED):
-    c32, t32 = codebook_fp32(128, 3)
+def oracle_tables(seed: int = QJL_SEED, bits: int = 3):
+    c32, t32 = codebook_fp32(128, bits)
     return c32, t32, gaussian_matrix(seed, 128, 128)
 
 
@@ -39,14 +38,15 @@ def dev(x, dtype=torch.float32):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).cuda()
 
 
-def new_pools(num_blocks: int, Hkv: int, fill: str = "random", seed: int = 0):
+def new_pools(num_blocks: int, Hkv: int, fill: str = "random", seed: int = 0, bits: int = 3):
+    kb, vb = k_page_bytes(bits), v_page_bytes(bits)
     if fill == "random":
         g = torch.Generator(device="cpu").manual_seed(seed)
-        k = torch.randint(0, 256, (num_blocks, Hkv, K_PAGE_BYTES), dtype=torch.uint8, generator=g)
-        v = torch.randint(0, 256, (num_blocks, Hkv, V_PAGE_BYTES), dtype=torch.uint8, generator=g)
+        k = torch.randint(0, 256, (num_blocks, Hkv, kb), dtype=torch.uint8, generator=g)
+        v = torch.randint(0, 256, (num_blocks, Hkv, vb), dtype=torch.uint8, generator=g)
         return k.cuda(), v.cuda()
-    return (torch.zeros((num_blocks, Hkv, K_PAGE_BYTES), dtype=torch.uint8, device="cuda"),
-            torch.zeros((num_blocks, Hkv, V_PAGE_BYTES), dtype=torch.uint8, device="cuda"))
+    return (torch.zeros((num_blocks, Hkv, kb), dtype=torch.uint8, device="cuda"),
+            torch.zeros((num_blocks, Hkv, vb), dtype=torch.uint8, device="cuda"))
 
 
 def encode_gpu(cb, k, v, slots, kpool, vpool, dtype=torch.bfloat16, with_norms=True):

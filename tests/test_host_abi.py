@@ -60,15 +60,16 @@ def test_host_helper_errors():
 def test_codebook_init_rejects_before_any_device_call():
     s = tq.tq_codebook_t()
     assert tq._lib.tq_codebook_init(ctypes.byref(s), 64, 3, 1, None, FAKE, None) == tq.TQ_ERR_UNSUPPORTED
-    assert tq._lib.tq_codebook_init(ctypes.byref(s), 128, 4, 1, None, FAKE, None) == tq.TQ_ERR_UNSUPPORTED
+    assert tq._lib.tq_codebook_init(ctypes.byref(s), 128, 5, 1, None, FAKE, None) == tq.TQ_ERR_UNSUPPORTED
+    assert tq._lib.tq_codebook_init(ctypes.byref(s), 128, 1, 1, None, FAKE, None) == tq.TQ_ERR_UNSUPPORTED
     assert tq._lib.tq_codebook_init(ctypes.byref(s), 128, 3, 1, None, None, None) == tq.TQ_ERR_INVALID_ARGUMENT
     assert tq._lib.tq_codebook_init(None, 128, 3, 1, None, FAKE, None) == tq.TQ_ERR_INVALID_ARGUMENT
     assert s.magic == 0
 
 
-def _fake_cb(initialised=True):
+def _fake_cb(initialised=True, bits=3):
     s = tq.tq_codebook_t()
-    s.head_dim, s.bits, s.qjl_dim, s.block_size = 128, 3, 128, 16
+    s.head_dim, s.bits, s.qjl_dim, s.block_size = 128, bits, 128, 16
     s.d_tables = FAKE
     s.magic = 0x54513031 if initialised else 0
     return s
@@ -369,3 +370,19 @@ def test_window_workspace_covers_only_the_window():
     for q_len, Hq, Hkv in [(1, 32, 8), (3, 32, 4), (21, 16, 2), (1, 32, 2)]:
         assert win_fn(cb, 4, q_len, Hq, Hkv, 5000, 5000, 0) == plain_fn(cb, 4, q_len, Hq, Hkv, 5000, 0)
     assert win_fn(cb, 4, 1, 32, 8, 5000, 0, 0) == 0
+
+
+def test_page_sizes_and_plans_of_the_other_bit_widths():
+    """2 and 4-bit codebooks: page sizes 256 (b + 1) + 64 and 256 b + 32, as
+    the oracle's layout, and a decode plan on the vector pass (query
+    operands in the workspace) where 3 bits take the matrix-core pass."""
+    from oracle import pages as P
+    for b in (2, 3, 4):
+        cb = ctypes.byref(_fake_cb(bits=b))
+        assert tq._lib.tq_k_page_bytes(cb) == P.k_page_bytes(b)
+        assert tq._lib.tq_v_page_bytes(cb) == P.v_page_bytes(b)
+    w3 = tq._lib.tq_decode_workspace_bytes(ctypes.byref(_fake_cb(bits=3)), 4, 1, 32, 8, 8192, 0)
+    for b in (2, 4):
+        wb = tq._lib.tq_decode_workspace_bytes(ctypes.byref(_fake_cb(bits=b)), 4, 1, 32, 8, 8192, 0)
+        assert wb > w3 and wb >= 4 * 32 * 256 * 4      # query operands of every row come first
+
