@@ -167,7 +167,7 @@ SplitPlan plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int 
     long per_seq = q_len;
     if (tq::prefill_uses_mfma(q_len, group, bits)) {
       const int bq = tq::prefill_block_queries(group);
-      per_seq = (q_len + bq - 1) / bq;
+      per_seq = ((long)q_len + bq - 1) / bq;
     }
     const long rows = (long)num_seqs * per_seq * num_kv_heads;
     long want = (1024 + rows - 1) / rows;
@@ -178,7 +178,7 @@ SplitPlan plan_splits(int num_seqs, int q_len, int num_kv_heads, int group, int 
     st = (int)per;
   }
   p.split_tokens = st;
-  p.num_splits = max_ctx > 0 ? (max_ctx + st - 1) / st : 1;
+  p.num_splits = max_ctx > 0 ? (int)(((int64_t)max_ctx + st - 1) / st) : 1;
   return p;
 }
 
@@ -203,6 +203,11 @@ bool decode_uses_mfma(int q_len, int group, int bits) {
   return (q_len + per - 1) / per <= 4;
 }
 int decode_positions_per_launch(int group) { return 8 / group; }
+// Longer query blocks of 3-bit caches take the matrix-core prefill pass.
+bool prefill_uses_mfma(int q_len, int group, int bits) {
+  return bits == 3 && q_len > 1 && !decode_uses_mfma(q_len, group, bits) && group >= 1 && group <= kMaxGroup;
+}
+int prefill_block_queries(int group) { return kPrefillRows / group; }
 int decode_qk_tiles(int rows) { return (rows + 3) / 4; }
 }  // namespace tq
 

@@ -97,6 +97,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowTiles = 1;                  // 16-row tiles per wave (each shares the tile reads)
 constexpr int kRows = 16 * kRowTiles * kWaves;  // query rows per workgroup
+static_assert(kRows == kPrefillRows, "the host plans prefill blocks of kPrefillRows rows");
 
 // Dequantize a step's staged pages into T (all threads of the workgroup).
 // Keys: item (key, 8 coordinates); values: item (coordinate, page, half of
@@ -414,17 +415,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
 
 }  // namespace
 
-bool prefill_uses_mfma(int q_len, int group, int bits) {
-  return bits == 3 && q_len > 1 && !decode_uses_mfma(q_len, group, bits) && group >= 1 && group <= kMaxGroup;
-}
-
-int prefill_block_queries(int group) { return kRows / group; }
-
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream) {
+  if (a.group < 1 || a.group > kMaxGroup) return hipErrorInvalidValue;
   const int bq = kRows / a.group;
   const int qblocks = (a.q_len + bq - 1) / bq;
   dim3 grid((unsigned)(a.num_seqs * qblocks), (unsigned)a.num_kv_heads, (unsigned)a.num_splits);
-  if (a.group < 1 || a.group > kMaxGroup) return hipErrorInvalidValue;
   hipLaunchKernelGGL(prefill_mfma_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
