@@ -703,6 +703,110 @@ def verify_attention(tq, cb, dev, stream, steps=30, warmup=5, T=32768, q_lens=(1
     return res
 
 
+def window_attention(tq, cb, dev, stream, steps=30, warmup=5, W=1024):
+    """Sliding-window decode over a rotating cache: the headline batch's 16
+    ragged sequences (contexts log-uniform in [512, 32768]), 32q/8kv, a
+    1,024-token window (the pages' Gemma 4 sliding layers) over a ring of
+    65 pages per sequence; only the pages the window overlaps are read."""
+    import torch
+    import synth
+    hkv, R_ring = 8, 65
+    rng = np.random.default_rng(SEED3)
+    L = synth.ragged_lengths(rng, B3)
+    per_rep = B3 * R_ring * hkv * (K_PAGE + V_PAGE)
+    R = replicas_for(per_rep)
+    nb = B3 * R_ring
+    table_np = rng.permutation(nb).astype(np.int32).reshape(B3, R_ring)
+    table = torch.from_numpy(table_np).to(dev)
+    # the last 16 R_ring positions of every sequence, written once (older ones
+    # would be overwritten by them)
+    pos = [np.arange(max(0, int(l) - 16 * R_ring), int(l)) for l in L]
+    slots = np.concatenate([table_np[b][(p // 16) % R_ring].astype(np.int64) * 16 + p % 16
+                            for b, p in enumerate(pos)])
+    n = len(slots)
+    k = synth.kv_tensor_device(61, n, hkv, dev)
+    v = synth.kv_tensor_device(62, n, hkv, dev)
+    st = torch.from_numpy(slots).to(dev)
+    pools = []
+    for _ in range(R):
+        kp = torch.empty((nb, hkv, K_PAGE), dtype=torch.uint8, device=dev)
+        vp = torch.empty((nb, hkv, V_PAGE), dtype=torch.uint8, device=dev)
+        tq.tq_encode_kv(cb, k, v, st, kp, vp, stream=stream)
+        pools.append((kp, vp))
+    del k, v
+    q = torch.from_numpy(synth.queries(rng, B3, 1, HQ)).to(dev, torch.bfloat16)
+    clens = torch.from_numpy(L.astype(np.int32)).to(dev)
+    out = torch.empty((B3, 1, HQ, D), dtype=torch.float32, device=dev)
+    maxc = int(L.max())
+    ws = torch.empty(tq.tq_decode_window_workspace_bytes(cb, B3, 1, HQ, hkv, maxc, W), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        kp, vp = pools[i % R]
+        tq.tq_decode_attention_window(cb, q, kp, vp, table, clens, maxc, hkv, W, out=out, workspace=ws,
+                                      stream=stream)
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        call(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    by = decode_bytes(np.minimum(L, W), HQ, hkv)
+    del pools
+    return {"workload": "sliding-window decode, batch 16 ragged contexts (headline lengths), window 1024, "
+                        "ring of 65 pages per sequence, GQA 32q/8kv",
+            "window": W, "ring_pages": R_ring, "replicas": R, "calls": steps, "algorithmic_bytes": by,
+            "us": round(us, 2), "GBps": round(by / (us / 1e6) / 1e9, 1),
+            "pct_peak": round(100 * by / (us / 1e6) / 1e9 / HBM_PEAK_GBPS, 2)}
+
+
+def bits_variants(tq, dev, stream, steps=20, warmup=3):
+    """The 2- and 4-bit codebook variants on one 8,192-token GQA layer
+    (32q/8kv): encode of the layer and its decode attention (vector pass),
+    beside the 3-bit pages' method."""
+    import torch
+    import synth
+    case = synth.gqa_case(seed=2, T=T2, Hq=HQ, Hkv=HKV2)
+    k = torch.from_numpy(case["k"]).to(dev, torch.bfloat16)
+    v = torch.from_numpy(case["v"]).to(dev, torch.bfloat16)
+    slots = torch.from_numpy(case["slots"]).to(dev)
+    q = torch.from_numpy(case["q"]).to(dev, torch.bfloat16)
+    table = torch.from_numpy(case["table"]).to(dev)
+    clens = torch.from_numpy(case["context_lens"]).to(dev)
+    res = {"workload": "one GQA layer: 8192 tokens x 8 KV heads, bf16; encode, then 1 query per head"}
+    for bits in (2, 3, 4):
+        cbb = tq.tq_codebook_init(128, bits, synth.QJL_SEED, device=dev)
+        kb, vb = tq.tq_k_page_bytes(cbb), tq.tq_v_page_bytes(cbb)
+        kp = torch.zeros((case["num_blocks"], HKV2, kb), dtype=torch.uint8, device=dev)
+        vp = torch.zeros((case["num_blocks"], HKV2, vb), dtype=torch.uint8, device=dev)
+        out = torch.empty((1, 1, HQ, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(tq.tq_decode_workspace_bytes(cbb, 1, 1, HQ, HKV2, T2), dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            tq.tq_encode_kv(cbb, k, v, slots, kp, vp, stream=stream)
+            tq.tq_decode_attention(cbb, q, kp, vp, table, clens, T2, HKV2, out=out, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in evs:
+            e[0].record(stream)
+            tq.tq_encode_kv(cbb, k, v, slots, kp, vp, stream=stream)
+            e[1].record(stream)
+            tq.tq_decode_attention(cbb, q, kp, vp, table, clens, T2, HKV2, out=out, workspace=ws, stream=stream)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        enc = statistics.median([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+        att = statistics.median([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
+        kv_bytes = T2 * HKV2 * (kb + vb) // 16
+        res[f"{bits}bit"] = {"k_page_bytes": kb, "v_page_bytes": vb,
+                             "bits_per_coordinate": round((kb + vb) * 8 / (2 * 16 * D), 4),
+                             "encode_us": round(enc, 2), "attention_us": round(att, 2),
+                             "attention_GBps": round((kv_bytes + HQ * D * 6) / (att / 1e6) / 1e9, 1),
+                             "decode_pass": "matrix cores" if bits == 3 else "vector"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -720,6 +824,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--verify-only", action="store_true")
     ap.add_argument("--hot-window-only", action="store_true")
+    ap.add_argument("--window-only", action="store_true")
+    ap.add_argument("--bits-only", action="store_true")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -748,6 +854,13 @@ def main():
         print(json.dumps({"attention_hot_window": hot_window_attention(tq, cb, dev, stream, steps=args.steps,
                                                                        warmup=args.warmup)}))
         return
+    if args.window_only:
+        print(json.dumps({"attention_window": window_attention(tq, cb, dev, stream, steps=args.steps,
+                                                               warmup=args.warmup)}))
+        return
+    if args.bits_only:
+        print(json.dumps({"bits_variants": bits_variants(tq, dev, stream, steps=args.steps, warmup=args.warmup)}))
+        return
     if args.long_context_only:
         print(json.dumps({"attention_long": long_context_attention(tq, cb, dev, stream, steps=args.steps,
                                                                    warmup=args.warmup)}))
@@ -763,6 +876,14 @@ def main():
         extra["prefill"] = prefill_bench(tq, cb, dev, stream)
         torch.cuda.empty_cache()
         extra["layer_8192"] = layer_bench(tq, cb, dev, stream)
+        torch.cuda.empty_cache()
+        extra["attention_verify"] = verify_attention(tq, cb, dev, stream)
+        torch.cuda.empty_cache()
+        extra["attention_hot_window"] = hot_window_attention(tq, cb, dev, stream)
+        torch.cuda.empty_cache()
+        extra["attention_window"] = window_attention(tq, cb, dev, stream)
+        torch.cuda.empty_cache()
+        extra["bits_variants"] = bits_variants(tq, dev, stream)
         torch.cuda.empty_cache()
         print(json.dumps({"progress": "side measurements done"}), file=sys.stderr, flush=True)
 
