@@ -145,6 +145,7 @@ int decode_positions_per_launch(int group);
 // Several queries per sequence (chunked prefill, causal) run on the
 // matrix-core prefill pass: 128 query rows (128 / group positions) per
 // workgroup.
+constexpr int64_t kAppendMaxVectors = 1024;  // encode calls of at most this many (token, KV head) vectors take one wave each
 constexpr int kPrefillRows = 128;  // query rows (positions x heads) per prefill workgroup
 bool prefill_uses_mfma(int q_len, int group, int bits);
 int prefill_block_queries(int group);
