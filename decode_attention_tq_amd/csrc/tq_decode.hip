@@ -1229,6 +1229,277 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(Dec
     split_body_ws<1>(a, sm, b, h, j, s0, s1);
 }
 
+// ---- 2''. exact hot window ---------------------------------------------------
+// The recent tokens a deployment keeps uncompressed (the SwiftLM README
+// compresses only past 2,048 tokens, its --turbo-kv option row) enter the
+// same softmax as the compressed history (its note on --turbo-kv recall):
+// this pass turns window chunks of kHotChunk tokens into partial records of
+// the same form as the split passes (m in log2 units, l, acc' in the rotated
+// domain), placed right after each row's compressed records, and the merge
+// combines them all.  Single-query decode: every window token is visible.
+//
+// A workgroup takes one (sequence, KV head, 64-token chunk) and the G <= 16
+// query heads of the group; wave w takes tokens 16w .. 16w + 15 of the chunk:
+//   * scores S = Q K^T on the matrix cores (16x16x32, bf16 or f16 as the
+//     window is stored; Q = scale log2(e) q as hi + lo halves of that type,
+//     rows past G zero): lane l reads 16 bytes of token l % 16's row per K
+//     step straight into the B operand, so a wave's 16 rows are read whole;
+//     f32 windows run as three bf16 pieces of K against Q hi + lo;
+//   * the heads' maxima and sums over the chunk meet in LDS; p goes to LDS;
+//   * p v on the vector ALU: lane l owns coordinates 2l, 2l + 1 and reads
+//     each of its 16 tokens' rows as one coalesced 256-byte (bf16/f16) or
+//     512-byte (f32) wave load;
+//   * the waves' sums meet in LDS and each head's is rotated once (H is its
+//     own inverse, so the merge's inverse rotation returns it).
+template <int DT>
+__device__ __forceinline__ float hot_elem(uint32_t hb) {
+  return DT == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hb) : __uint_as_float(hb << 16);
+}
+typedef short v8sh __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+template <int DT>
+__device__ __forceinline__ v4f hot_mfma(const v8sh &A, const v8sh &B, const v4f &C) {
+  if constexpr (DT == TQ_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, A), __builtin_bit_cast(v8h, B), C, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, A), __builtin_bit_cast(v8bf, B), C, 0, 0,
+                                                    0);
+}
+// The 16-bit pattern of v in the matrix type (bf16 round to nearest even,
+// or f16), and what it stands for.
+template <int DT>
+__device__ __forceinline__ uint16_t to_mat(float v, float &back) {
+  if constexpr (DT == TQ_F16) {
+    const _Float16 h = (_Float16)v;
+    back = (float)h;
+    return __builtin_bit_cast(uint16_t, h);
+  } else {
+    const __bf16 h = (__bf16)v;
+    back = (float)h;
+    return __builtin_bit_cast(uint16_t, h);
+  }
+}
+
+struct HotLds {
+  float mred[4][16], lred[4][16];
+  alignas(16) float ps[4][16][16];     // [wave][head][token]
+  alignas(16) float accs[4][16][kHeadDim];
+};
+
+// Window chunk `item` (sequence, KV head, chunk; chunk fastest) by a
+// workgroup of four waves.
+template <int DT>
+__device__ __attribute__((always_inline)) void hot_body(const DecodeArgs &a, HotLds &L, int item) {
+  static_assert(kHotChunk == 64, "four waves of 16 tokens");
+  constexpr int MT = DT == TQ_F32 ? TQ_BF16 : DT;  // matrix type of the scores
+  constexpr int kEsz = DT == TQ_F32 ? 4 : 2;
+  const int c = item % a.hot_parts;
+  const int h = (item / a.hot_parts) % a.num_kv_heads;
+  const int b = item / (a.hot_parts * a.num_kv_heads);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.group;
+  // the row's compressed records come first: their count needs the context
+  // lengths, requested before the window's rows
+  const int t0s = seq_tiles(a, lane);
+  const int W = min(max(a.hot_lens[b], 0), a.hot_max);
+  const int j0 = c * kHotChunk + 16 * wave;  // the wave's first token
+  const int64_t tok_stride = (int64_t)a.num_kv_heads * kHeadDim;
+  const uint8_t *const kb = static_cast<const uint8_t *>(a.hot_k) +
+                            (((int64_t)b * a.hot_max) * tok_stride + (int64_t)h * kHeadDim) * kEsz;
+  const uint8_t *const vb = static_cast<const uint8_t *>(a.hot_v) +
+                            (((int64_t)b * a.hot_max) * tok_stride + (int64_t)h * kHeadDim) * kEsz;
+  // tokens past the window read its last one (or token 0 of an empty window;
+  // hot_max >= 1 here), and get p = 0
+  const int jmax = max(W, 1) - 1;
+  const int n16 = lane & 15, kg = lane >> 4;
+
+  // the wave's V rows: lane l, coordinates 2l and 2l + 1 of each of its tokens
+  float vv[16][2];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const int64_t j = min(j0 + n, jmax);
+    const uint8_t *row = vb + j * tok_stride * kEsz;
+    if constexpr (DT == TQ_F32) {
+      const float2 x = reinterpret_cast<const float2 *>(row)[lane];
+      vv[n][0] = x.x;
+      vv[n][1] = x.y;
+    } else {
+      const uint32_t x = reinterpret_cast<const uint32_t *>(row)[lane];
+      vv[n][0] = hot_elem<DT>(x & 0xFFFFu);
+      vv[n][1] = hot_elem<DT>(x >> 16);
+    }
+  }
+  // the B operands: token n16's row, coordinates 32s + 8kg .. +7
+  v8sh Bk[4][DT == TQ_F32 ? 3 : 1];
+  {
+    const int64_t j = min(j0 + n16, jmax);
+    const uint8_t *row = kb + j * tok_stride * kEsz;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (DT == TQ_F32) {
+        const float4 *src = reinterpret_cast<const float4 *>(row) + (32 * s + 8 * kg) / 4;
+        const float4 x0 = src[0], x1 = src[1];
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // three bf16 pieces (exact for normal values)
+          float back, r = xs[e];
+          Bk[s][0][e] = (short)to_mat<TQ_BF16>(r, back);
+          r -= back;
+          Bk[s][1][e] = (short)to_mat<TQ_BF16>(r, back);
+          r -= back;
+          Bk[s][2][e] = (short)to_mat<TQ_BF16>(r, back);
+        }
+      } else {
+        Bk[s][0] = *reinterpret_cast<const v8sh *>(row + 2 * (32 * s + 8 * kg));
+      }
+    }
+  }
+  // the A operands: query row n16 (head n16 of the group; zero past G),
+  // coordinates 32s + 8kg .. +7, times scale log2(e), as hi + lo halves
+  v8sh Ah[4], Al[4];
+  {
+    const float qs = a.scale * kLog2e;
+    const bool live = n16 < G;
+    const int64_t qrow = (int64_t)b * a.num_q_heads + (int64_t)h * G + (live ? n16 : 0);
+    float xq[4][8];
+    if (a.q_dtype == TQ_F32) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + qrow * kHeadDim +
+                                                             32 * s + 8 * kg);
+        const float4 x0 = src[0], x1 = src[1];
+        xq[s][0] = x0.x; xq[s][1] = x0.y; xq[s][2] = x0.z; xq[s][3] = x0.w;
+        xq[s][4] = x1.x; xq[s][5] = x1.y; xq[s][6] = x1.z; xq[s][7] = x1.w;
+      }
+    } else {
+      const bool f16 = a.q_dtype == TQ_F16;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qrow * kHeadDim +
+                                                          32 * s + 8 * kg);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hb = (ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          xq[s][e] = f16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hb) : __uint_as_float(hb << 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = live ? qs * xq[s][e] : 0.0f;
+        float back;
+        Ah[s][e] = (short)to_mat<MT>(x, back);
+        float back2;
+        Al[s][e] = (short)to_mat<MT>(x - back, back2);
+      }
+  }
+  v4f sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    sc = hot_mfma<MT>(Ah[s], Bk[s][0], sc);
+    sc = hot_mfma<MT>(Al[s], Bk[s][0], sc);
+    if constexpr (DT == TQ_F32) {
+      sc = hot_mfma<MT>(Ah[s], Bk[s][1], sc);
+      sc = hot_mfma<MT>(Al[s], Bk[s][1], sc);
+      sc = hot_mfma<MT>(Ah[s], Bk[s][2], sc);
+    }
+  }
+  // lane l, register i: head 4 kg + i, token n16 of the wave
+  const bool valid = j0 + n16 < W;
+  float m4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m4[i] = row_max16(valid ? sc[i] : -INFINITY);
+    if (n16 == 0) L.mred[wave][4 * kg + i] = m4[i];
+  }
+  lds_barrier();
+  float p4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hd = 4 * kg + i;
+    const float M = fmaxf(fmaxf(L.mred[0][hd], L.mred[1][hd]), fmaxf(L.mred[2][hd], L.mred[3][hd]));
+    p4[i] = valid && M != -INFINITY ? __builtin_amdgcn_exp2f(sc[i] - M) : 0.0f;
+    L.ps[wave][hd][n16] = p4[i];
+    const float l = row_sum16(p4[i]);
+    if (n16 == 0) L.lred[wave][hd] = l;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // p v over the wave's 16 tokens for every head of the group
+  float acc[16][2];
+#pragma unroll
+  for (int g = 0; g < 16; ++g) acc[g][0] = acc[g][1] = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    if (g < G) {  // uniform
+#pragma unroll
+      for (int n = 0; n < 16; n += 4) {
+        const float4 pv = *reinterpret_cast<const float4 *>(&L.ps[wave][g][n]);
+        acc[g][0] = fmaf(pv.x, vv[n][0], acc[g][0]);
+        acc[g][1] = fmaf(pv.x, vv[n][1], acc[g][1]);
+        acc[g][0] = fmaf(pv.y, vv[n + 1][0], acc[g][0]);
+        acc[g][1] = fmaf(pv.y, vv[n + 1][1], acc[g][1]);
+        acc[g][0] = fmaf(pv.z, vv[n + 2][0], acc[g][0]);
+        acc[g][1] = fmaf(pv.z, vv[n + 2][1], acc[g][1]);
+        acc[g][0] = fmaf(pv.w, vv[n + 3][0], acc[g][0]);
+        acc[g][1] = fmaf(pv.w, vv[n + 3][1], acc[g][1]);
+      }
+      *reinterpret_cast<float2 *>(&L.accs[wave][g][2 * lane]) = make_float2(acc[g][0], acc[g][1]);
+    }
+  }
+  lds_barrier();
+  int ns;
+  if (a.balanced) {
+    const int per = bal_per(a, t0s);
+    ns = (__builtin_amdgcn_readlane(t0s, b & 63) + per - 1) / per;
+    if (a.num_seqs > 64) ns = (seq_tiles(a, b) + per - 1) / per;
+  } else {
+    ns = (clamped_context(a, b) + a.split_tokens - 1) / a.split_tokens;
+  }
+  // wave w writes the records of heads w, w + 4, ... (lane l: coordinates l, l + 64)
+  const int64_t row0 = (int64_t)b * a.num_q_heads + (int64_t)h * G;  // output rows (q_len 1)
+  for (int g = wave; g < G; g += 4) {  // uniform
+    const float M = fmaxf(fmaxf(L.mred[0][g], L.mred[1][g]), fmaxf(L.mred[2][g], L.mred[3][g]));
+    const float Ls = (L.lred[0][g] + L.lred[1][g]) + (L.lred[2][g] + L.lred[3][g]);
+    float o0 = (L.accs[0][g][lane] + L.accs[1][g][lane]) + (L.accs[2][g][lane] + L.accs[3][g][lane]);
+    float o1 = (L.accs[0][g][lane + 64] + L.accs[1][g][lane + 64]) + (L.accs[2][g][lane + 64] + L.accs[3][g][lane + 64]);
+    wave_fwht128(o0, o1, lane);
+    float *part = a.partials + ((row0 + g) * a.part_stride + ns + c) * kPartStride;
+    if (lane == 0) {
+      part[0] = M;
+      part[1] = Ls;
+    }
+    part[4 + lane] = o0;
+    part[68 + lane] = o1;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void hot_window_kernel(DecodeArgs a) {
+  __shared__ __align__(16) HotLds L;
+  hot_body<DT>(a, L, blockIdx.x);
+}
+__device__ __attribute__((always_inline)) void hot_body_any(const DecodeArgs &a, HotLds &L, int item) {
+  if (a.hot_dtype == TQ_F32)
+    hot_body<TQ_F32>(a, L, item);
+  else if (a.hot_dtype == TQ_F16)
+    hot_body<TQ_F16>(a, L, item);
+  else
+    hot_body<TQ_BF16>(a, L, item);
+}
+
+void launch_hot(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  if (a.hot_dtype == TQ_F32)
+    hipLaunchKernelGGL((hot_window_kernel<TQ_F32>), grid, dim3(256), 0, stream, a);
+  else if (a.hot_dtype == TQ_F16)
+    hipLaunchKernelGGL((hot_window_kernel<TQ_F16>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((hot_window_kernel<TQ_BF16>), grid, dim3(256), 0, stream, a);
+}
+
 // ---- 2'''. split pass on the matrix cores, one tile per wave ----------------
 // The same contractions as the pass above (fp6 query digits x fp4 bit-planes for
 // the scores, base-16 weight digits x fp4 value planes), arranged so that
@@ -1277,9 +1548,24 @@ struct WaveLds {
 };
 
 template <int T>
+union WaveOrHotLds {
+  WaveLds<T> w;
+  HotLds h;
+};
+
+// Workgroups past the plan's grid take the exact window's chunks (a call
+// with a hot window, T = 1): they run beside the split pass instead of after it.
+template <int T>
 __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(DecodeArgs a) {
   constexpr int NW = 4 * T;
-  __shared__ __align__(16) WaveLds<T> sm;
+  __shared__ __align__(16) WaveOrHotLds<T> smu;
+  if constexpr (T == 1) {
+    if ((int)blockIdx.x >= a.bal_grid) {  // uniform
+      hot_body_any(a, smu.h, (int)blockIdx.x - a.bal_grid);
+      return;
+    }
+  }
+  WaveLds<T> &sm = smu.w;
   // the context lengths (the plan needs them first), then the projection
   // operands, which do not depend on the plan (loads return in order: the
   // plan then waits for the lengths only)
@@ -1599,188 +1885,6 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   }
 }
 
-// ---- 2''. exact hot window ---------------------------------------------------
-// The recent tokens a deployment keeps uncompressed (the SwiftLM README
-// compresses only past 2,048 tokens, its --turbo-kv option row) enter the
-// same softmax as the compressed history (its note on --turbo-kv recall):
-// this pass turns window chunks of kHotChunk tokens into partial records of
-// the same form as the split pass (m in log2 units, l, acc' in the rotated
-// domain), placed right after each row's visible compressed chunks, and the
-// merge combines them all.  Single-query decode: every window token is
-// visible.  A workgroup takes one (sequence, KV head, chunk) and all G query
-// heads: thread t scores token t of the chunk against the G queries (held in
-// LDS, read as broadcasts), the block forms each head's maximum and sum,
-// wave w accumulates p v over tokens 64 w .. 64 w + 63 (lane l: coordinates
-// l and l + 64), the waves meet in LDS, and acc is rotated once (H is its
-// own inverse, so the merge's inverse rotation returns it).
-// A window element from the 16-bit pattern of an f16 or a bf16 value.
-template <int DT>
-__device__ __forceinline__ float half_bits_to_float(uint32_t hb) {
-  return DT == TQ_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)hb) : __uint_as_float(hb << 16);
-}
-
-// G is the capacity (1, 2, 4, 8 or 16 heads), a.group <= G the group size.
-template <int G, int DT>
-__global__ __launch_bounds__(kHotChunk) void hot_window_kernel(DecodeArgs a) {
-  const int Gr = a.group;
-  __shared__ __align__(16) float qs[G][kHeadDim];   // q * scale * log2(e)
-  __shared__ __align__(16) float ps[G][kHotChunk];  // p of each token
-  constexpr int NW = kHotChunk / 64;  // waves: one token per thread
-  __shared__ float red[NW][G];
-  __shared__ __align__(16) float accs[NW][G][kHeadDim];
-  constexpr bool F32 = DT == TQ_F32;
-  constexpr int kEsz = F32 ? 4 : 2;
-  const int c = blockIdx.x % a.hot_parts;
-  const int h = (blockIdx.x / a.hot_parts) % a.num_kv_heads;
-  const int b = blockIdx.x / (a.hot_parts * a.num_kv_heads);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int W = min(max(a.hot_lens[b], 0), a.hot_max);
-  const int j0 = c * kHotChunk;
-  const int n = max(0, min(W - j0, kHotChunk));  // uniform: tokens of this chunk
-  const int64_t row0 = (int64_t)b * a.num_q_heads + h * Gr;  // output rows (q_len 1)
-  const float qscale = a.scale * kLog2e;
-  for (int i = tid; i < G * kHeadDim; i += kHotChunk)
-    qs[i / kHeadDim][i % kHeadDim] =
-        i < Gr * kHeadDim ? qscale * load_as_float(a.q, a.q_dtype, row0 * kHeadDim + i) : 0.0f;
-  lds_barrier();
-  // scores: thread t, token j0 + t (past the chunk's end: its last token)
-  float sc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) sc[g] = 0.0f;
-  const int64_t tok_stride = (int64_t)a.num_kv_heads * kHeadDim;
-  const int64_t kbase = ((int64_t)b * a.hot_max + j0 + min(tid, max(n - 1, 0))) * tok_stride + (int64_t)h * kHeadDim;
-  if (n > 0) {  // uniform
-    const uint8_t *krow = static_cast<const uint8_t *>(a.hot_k) + kbase * kEsz;
-    constexpr int kPer = 16 / kEsz;  // elements per 16-byte load
-#pragma unroll 1
-    for (int l0 = 0; l0 < kHeadDim / kPer; l0 += 4) {  // four loads in flight per step
-      uint4 w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const uint4 *>(krow + 16 * (l0 + i));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c0 = (l0 + i) * kPer;
-        const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-        float x[kPer];
-#pragma unroll
-        for (int e = 0; e < kPer; ++e)
-          x[e] = F32 ? __uint_as_float(ww[e]) : half_bits_to_float<DT>((ww[e / 2] >> (16 * (e & 1))) & 0xFFFFu);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float t = sc[g];
-#pragma unroll
-          for (int e4 = 0; e4 < kPer; e4 += 4) {
-            const float4 q4 = *reinterpret_cast<const float4 *>(&qs[g][c0 + e4]);
-            t = fmaf(q4.x, x[e4], t);
-            t = fmaf(q4.y, x[e4 + 1], t);
-            t = fmaf(q4.z, x[e4 + 2], t);
-            t = fmaf(q4.w, x[e4 + 3], t);
-          }
-          sc[g] = t;
-        }
-      }
-    }
-  }
-  const bool live = tid < n;
-  float mg[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float m = wave_max(live ? sc[g] : -INFINITY);
-    if (lane == 0) red[wave][g] = m;
-  }
-  lds_barrier();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    mg[g] = red[0][g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) mg[g] = fmaxf(mg[g], red[w][g]);
-  }
-  lds_barrier();  // red is reused for the sums
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float p = live ? exp2f(sc[g] - mg[g]) : 0.0f;
-    ps[g][tid] = p;
-    const float l = wave_sum(p);
-    if (lane == 0) red[wave][g] = l;
-  }
-  lds_barrier();
-  // p v over the wave's 64 tokens, eight per step with their loads in flight
-  // together (tokens past the chunk's end repeat its last one; their p is 0)
-  float a0[G], a1[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) a0[g] = a1[g] = 0.0f;
-  const int t0 = 64 * wave, t1 = min(t0 + 64, n);
-  const uint8_t *vbase = static_cast<const uint8_t *>(a.hot_v) +
-                         (((int64_t)b * a.hot_max + j0) * tok_stride + (int64_t)h * kHeadDim) * kEsz;
-  for (int t = t0; t < t1; t += 8) {  // uniform
-    float v0[8], v1[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint8_t *o = vbase + (int64_t)min(t + u, t1 - 1) * tok_stride * kEsz;
-      if (F32) {
-        v0[u] = reinterpret_cast<const float *>(o)[lane];
-        v1[u] = reinterpret_cast<const float *>(o)[64 + lane];
-      } else {
-        v0[u] = half_bits_to_float<DT>(reinterpret_cast<const uint16_t *>(o)[lane]);
-        v1[u] = half_bits_to_float<DT>(reinterpret_cast<const uint16_t *>(o)[64 + lane]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float4 pa = *reinterpret_cast<const float4 *>(&ps[g][t]);
-      const float4 pb = *reinterpret_cast<const float4 *>(&ps[g][t + 4]);
-      const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a0[g] = fmaf(pv[u], v0[u], a0[g]);
-        a1[g] = fmaf(pv[u], v1[u], a1[g]);
-      }
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    accs[wave][g][lane] = a0[g];
-    accs[wave][g][64 + lane] = a1[g];
-  }
-  lds_barrier();
-  // wave w writes the records of heads w, w + NW, ...
-  // the row's compressed records come first
-  int ns;
-  if (a.balanced) {
-    const int per = bal_per(a, seq_tiles(a, lane));
-    ns = (seq_tiles(a, b) + per - 1) / per;
-  } else {
-    ns = (clamped_context(a, b) + a.split_tokens - 1) / a.split_tokens;
-  }
-  for (int g = wave; g < Gr; g += NW) {  // uniform
-    float o0 = 0.0f, o1 = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      o0 += accs[w][g][lane];
-      o1 += accs[w][g][64 + lane];
-      l += red[w][g];
-    }
-    wave_fwht128(o0, o1, lane);
-    float *part = a.partials + ((row0 + g) * a.part_stride + ns + c) * kPartStride;
-    if (lane == 0) {
-      part[0] = n > 0 ? mg[g] : -INFINITY;
-      part[1] = l;
-    }
-    part[4 + lane] = o0;
-    part[68 + lane] = o1;
-  }
-}
-
-template <int G>
-void launch_hot(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
-  if (a.hot_dtype == TQ_F32)
-    hipLaunchKernelGGL((hot_window_kernel<G, TQ_F32>), grid, dim3(kHotChunk), 0, stream, a);
-  else if (a.hot_dtype == TQ_F16)
-    hipLaunchKernelGGL((hot_window_kernel<G, TQ_F16>), grid, dim3(kHotChunk), 0, stream, a);
-  else
-    hipLaunchKernelGGL((hot_window_kernel<G, TQ_BF16>), grid, dim3(kHotChunk), 0, stream, a);
-}
-
 // ---- 3. merge ---------------------------------------------------------------
 // LSE combine of the chunk partials of an output row, o' = acc'/l, one
 // inverse FWHT, store.  W waves share a row (4/W rows per workgroup); wave w
@@ -1949,8 +2053,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
       la.pos0 = p0;
       la.pos_count = min(per, a.q_len - p0);
       la.qk_tiles = (la.group * la.pos_count + 3) / 4;
-      if (la.qk_tiles == 1)
-        hipLaunchKernelGGL(split_wave_kernel<1>, dim3((unsigned)items), dim3(256), 0, stream, la);
+      if (la.qk_tiles == 1) {
+        // the exact window's chunks ride in the same launch (q_len 1: one launch)
+        const int64_t hot_items = a.hot_parts > 0 ? (int64_t)a.num_seqs * a.num_kv_heads * a.hot_parts : 0;
+        hipLaunchKernelGGL(split_wave_kernel<1>, dim3((unsigned)(items + hot_items)), dim3(256), 0, stream, la);
+      }
       else if (la.qk_tiles == 2)
         hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)items), dim3(512), 0, stream, la);
       else
@@ -1976,16 +2083,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.hot_parts > 0) {  // the exact window's records
+  if (a.hot_parts > 0 && a.qk_tiles != 1) {  // the exact window's records (unless folded above)
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads * a.hot_parts));
-    switch (group_capacity(a.group)) {
-      case 1: launch_hot<1>(a, grid, stream); break;
-      case 2: launch_hot<2>(a, grid, stream); break;
-      case 4: launch_hot<4>(a, grid, stream); break;
-      case 8: launch_hot<8>(a, grid, stream); break;
-      case 16: launch_hot<16>(a, grid, stream); break;
-      default: return hipErrorInvalidValue;
-    }
+    if (a.group < 1 || a.group > 16) return hipErrorInvalidValue;
+    launch_hot(a, grid, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -128,9 +128,9 @@ struct DecodeArgs {
   Codebook cb;
 };
 
-constexpr int kHotChunk = 256;
+constexpr int kHotChunk = 64;  // exact window tokens per partial record
 // Largest chunk of the matrix-core decode pass (64 tiles of 128 tokens).
-constexpr int kMaxMfmaSplitTokens = 8192;  // exact window tokens per partial record
+constexpr int kMaxMfmaSplitTokens = 8192;
 
 // Workspace split of tq_decode_attention.
 size_t decode_qprep_floats(int64_t rows);
