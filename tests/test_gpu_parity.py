@@ -371,7 +371,7 @@ def test_any_group_size(Hq, Hkv):
 def test_hot_window(Hq, Hkv, hot_dtype):
     """Decode over a compressed history followed by an exact hot window of
     recent tokens, one softmax over both: ragged histories (one empty) and
-    windows (one empty, one of 2,048 tokens, several 256-token chunks and a
+    windows (one empty, one of 2,048 tokens, several 64-token chunks and a
     ragged last one), a sequence with no key at all (zero output), 1 to 16
     query heads per KV head, window tokens in bf16, f16 and f32."""
     rng = np.random.default_rng(40 + Hq // Hkv)

@@ -234,11 +234,11 @@ def test_hot_window_validation():
     ref = ctypes.byref(cb)
     need = tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, 300, 0)
     assert _hot(cb, wsb=need - 1) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
-    # no window: the plain decode workspace; a window of 300 tokens adds two
-    # partial records (256-token chunks) per query row
+    # no window: the plain decode workspace; a window of 300 tokens adds five
+    # partial records (64-token chunks) per query row
     plain = tq._lib.tq_decode_workspace_bytes(ref, 1, 1, 32, 8, 1024, 0)
     assert tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, 0, 0) == plain
-    assert need == plain + 32 * 2 * 132 * 4
+    assert need == plain + 32 * 5 * 132 * 4
     assert tq._lib.tq_decode_hot_workspace_bytes(ref, 1, 32, 8, 1024, -1, 0) == 0
 
 
