@@ -1214,12 +1214,20 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
 
 // One workgroup per range of the balanced plan.
 template <int T>
-__global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_mfma_kernel(DecodeArgs a0) {
   __shared__ __align__(16) SplitLds<T> sm;
+  // a verify block's position groups (pos_count positions each) share one
+  // launch: workgroup i takes group i % groups and range i / groups, so the
+  // groups of one range run side by side and read its pages together
+  const int groups = (a0.q_len - a0.pos0 + a0.pos_count - 1) / a0.pos_count;
+  const int pg = (int)blockIdx.x % groups, wid = (int)blockIdx.x / groups;
+  DecodeArgs a = a0;
+  a.pos0 = a0.pos0 + pg * a0.pos_count;
+  a.pos_count = min(a0.pos_count, a0.q_len - a.pos0);
   const int t0 = seq_tiles(a, threadIdx.x & 63);
   const int per = bal_per(a, t0);
   int b, h, j, Tb;
-  bal_locate(a, t0, per, blockIdx.x, b, h, j, Tb);
+  bal_locate(a, t0, per, wid, b, h, j, Tb);
   if (b >= a.num_seqs) return;  // uniform: past the last range
   const int L = clamped_context(a, b), base = seq_base(a, L);
   const int s0 = base + 128 * per * j, s1 = min(base + 128 * per * (j + 1), L);
@@ -2045,23 +2053,24 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t groups = (int64_t)a.num_seqs * a.q_len * a.num_kv_heads;
   hipError_t e = hipSuccess;
   if (a.qk_tiles > 0) {  // matrix-core pass, its own query operands: a workgroup per (chunk, KV head)
-    // one launch per group of at most 8 query rows (positions x heads)
+    // rows = (position, head) pairs, at most 8 per workgroup: up to 4 query
+    // rows take the one-tile-per-wave pass; 5 to 8, or several groups of
+    // positions (all in one launch), the two-head-tile pass
     const int per = decode_positions_per_launch(a.group);
     const int64_t items = a.bal_grid;
-    for (int p0 = 0; p0 < a.q_len; p0 += per) {
-      DecodeArgs la = a;
-      la.pos0 = p0;
-      la.pos_count = min(per, a.q_len - p0);
-      la.qk_tiles = (la.group * la.pos_count + 3) / 4;
-      if (la.qk_tiles == 1) {
-        // the exact window's chunks ride in the same launch (q_len 1: one launch)
-        const int64_t hot_items = a.hot_parts > 0 ? (int64_t)a.num_seqs * a.num_kv_heads * a.hot_parts : 0;
-        hipLaunchKernelGGL(split_wave_kernel<1>, dim3((unsigned)(items + hot_items)), dim3(256), 0, stream, la);
-      }
-      else if (la.qk_tiles == 2)
-        hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)items), dim3(512), 0, stream, la);
-      else
-        return hipErrorInvalidValue;
+    const int pgroups = (a.q_len + per - 1) / per;
+    DecodeArgs la = a;
+    la.pos0 = 0;
+    la.pos_count = min(per, a.q_len);
+    la.qk_tiles = (la.group * la.pos_count + 3) / 4;
+    if (pgroups == 1 && la.qk_tiles == 1) {
+      // the exact window's chunks ride in the same launch (q_len 1)
+      const int64_t hot_items = a.hot_parts > 0 ? (int64_t)a.num_seqs * a.num_kv_heads * a.hot_parts : 0;
+      hipLaunchKernelGGL(split_wave_kernel<1>, dim3((unsigned)(items + hot_items)), dim3(256), 0, stream, la);
+    } else if (la.qk_tiles == 2) {
+      hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)(items * pgroups)), dim3(512), 0, stream, la);
+    } else {
+      return hipErrorInvalidValue;
     }
   } else {
     hipLaunchKernelGGL(query_prep_kernel, dim3((unsigned)groups, (unsigned)a.group), dim3(256), 0, stream, a);
