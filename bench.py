@@ -164,26 +164,34 @@ def batch_setup(tq, cb, dev, total_steps):
 
 def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples):
     import torch
-    total = warmup + steps + warmup + samples
+    total = warmup + steps + 2 * (warmup + samples)
     st = batch_setup(tq, cb, dev, total)
     out = torch.empty((B3, 1, HQ3, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(tq.tq_decode_workspace_bytes(cb, B3, 1, HQ3, HKV3, st["max_ctx"]), dtype=torch.uint8,
+    ws = torch.empty(tq.tq_decode_step_workspace_bytes(cb, B3, HQ3, HKV3, st["max_ctx"]), dtype=torch.uint8,
                      device=dev)
     R = st["R"]
 
     def step(i, ev=None):
+        # the step call: append + attention (two launches when fused)
         kp, vp = st["pools"][i % R]
         if ev is not None:
             ev[0].record(stream)
-        tq.tq_encode_kv(cb, st["nk"][i], st["nv"][i], st["new_slots"][i], kp, vp, stream=stream)
+        tq.tq_decode_step(cb, st["nk"][i], st["nv"][i], st["new_slots"][i], st["qs"][i % 4], kp, vp,
+                          st["table"], st["clens"][i], st["max_ctx"], out=out, workspace=ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
+
+    def two_calls(i, ev):
+        # the same step as its two separate calls (the breakdown)
+        kp, vp = st["pools"][i % R]
+        ev[0].record(stream)
+        tq.tq_encode_kv(cb, st["nk"][i], st["nv"][i], st["new_slots"][i], kp, vp, stream=stream)
+        ev[1].record(stream)
         tq.tq_decode_attention(cb, st["qs"][i % 4], kp, vp, st["table"], st["clens"][i], st["max_ctx"], HKV3,
                                out=out, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        ev[2].record(stream)
 
-    # phase A: K steps back to back (value)
+    # phase A: K step calls back to back (value)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -199,27 +207,38 @@ def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples):
     s_per_step = max(wall, gpu_s) / steps
     bytes_a = float(np.mean(st["step_bytes"][warmup:warmup + steps]))
 
-    # phase B: sampled steps with events around the encode and the attention call
+    # phase B: sampled step calls with events around each
     base = warmup + steps
     for i in range(base, base + warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(samples)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(samples)]
     for j in range(samples):
         step(base + warmup + j, evs[j])
     torch.cuda.synchronize()
-    enc_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-    dec_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    step_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     idx = range(base + warmup, base + warmup + samples)
-    dec_b = float(np.mean([st["dec_bytes"][i] for i in idx]))
     step_b = float(np.mean([st["step_bytes"][i] for i in idx]))
+    # phase C: the same steps as the two separate calls, events between them
+    base += warmup + samples
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(samples)]
+    for i in range(base, base + warmup):
+        two_calls(i, evc[0])
+    torch.cuda.synchronize()
+    for j in range(samples):
+        two_calls(base + warmup + j, evc[j])
+    torch.cuda.synchronize()
+    enc_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evc]
+    dec_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evc]
+    idc = range(base + warmup, base + warmup + samples)
+    dec_b = float(np.mean([st["dec_bytes"][i] for i in idc]))
     res = dict(
         s_per_step=s_per_step, bytes_per_step=bytes_a, gpu_s=gpu_s, wall_s=wall, replicas=R,
         lengths=[int(x) for x in st["L"]], max_ctx=st["max_ctx"],
-        median_step_us=statistics.median([a + b for a, b in zip(enc_us, dec_us)]),
+        median_step_us=statistics.median(step_us), mean_step_us=float(np.mean(step_us)), sampled_step_bytes=step_b,
+        two_calls_median_step_us=statistics.median([a + b for a, b in zip(enc_us, dec_us)]),
         median_encode_us=statistics.median(enc_us), median_attention_us=statistics.median(dec_us),
-        mean_attention_us=float(np.mean(dec_us)), attention_bytes=dec_b, sampled_step_bytes=step_b,
-        samples=samples)
+        mean_attention_us=float(np.mean(dec_us)), attention_bytes=dec_b, samples=samples)
     del st
     return res
 
@@ -531,11 +550,13 @@ def counters_driver(tq, cb, dev, stream, launches=8):
     import synth
     st = batch_setup(tq, cb, dev, launches)
     out = torch.empty((B3, 1, HQ3, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.tq_decode_step_workspace_bytes(cb, B3, HQ3, HKV3, st["max_ctx"]), dtype=torch.uint8,
+                     device=dev)
     torch.cuda.synchronize()
     for i in range(launches):
         kp, vp = st["pools"][i % st["R"]]
-        tq.tq_decode_attention(cb, st["qs"][0], kp, vp, st["table"], st["clens"][i], st["max_ctx"], HKV3,
-                               out=out, stream=stream)
+        tq.tq_decode_step(cb, st["nk"][i], st["nv"][i], st["new_slots"][i], st["qs"][0], kp, vp, st["table"],
+                          st["clens"][i], st["max_ctx"], out=out, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     del st
     case = synth.gqa_case(seed=2, T=T2, Hq=HQ, Hkv=HKV2)
@@ -561,7 +582,8 @@ def traffic_from(fetch_csv, write_csv):
     """profiles/traffic.json from two counter runs of --counters: per launch
     of each kernel, FETCH_SIZE and WRITE_SIZE scaled by what the same counters
     read for the 512 MiB copy (its true traffic: 512 MiB read, 512 MiB
-    written).  The headline attention call is its split and merge kernels."""
+    written).  The headline decode step call is its prep, split and merge
+    kernels."""
     import csv
 
     def load(path, counter):
@@ -594,16 +616,17 @@ def traffic_from(fetch_csv, write_csv):
                             "hbm_bytes_per_launch": round(enc_f + enc_w), "fetch_bytes": round(enc_f),
                             "write_bytes": round(enc_w), "algorithmic_bytes": encode_bytes(T2, HKV2)}
     parts = {}
-    for needle in ("split_", "merge_kernel"):
+    for needle in ("step_prep_kernel", "split_", "merge_kernel"):
         ff, ww = med(f, needle, fs), med(w, needle, wsc)
         if ff is not None:
             parts[needle.strip("_")] = {"fetch_bytes": round(ff), "write_bytes": round(ww)}
     import synth
     L = synth.ragged_lengths(np.random.default_rng(SEED3), B3)
     tot = sum(p["fetch_bytes"] + p["write_bytes"] for p in parts.values())
-    rec["attention_call"] = {"source_hash": h, "workload": "headline batch: 16 ragged sequences, 32q/8kv",
-                             "hbm_bytes_per_launch": round(tot), "kernels": parts,
-                             "algorithmic_bytes_at_cached_lengths": decode_bytes(L + 1, HQ3, HKV3)}
+    rec["decode_step_call"] = {"source_hash": h, "workload": "decode step of 16 ragged sequences, 32q/8kv",
+                               "hbm_bytes_per_launch": round(tot), "kernels": parts,
+                               "algorithmic_bytes_at_cached_lengths": decode_bytes(L + 1, HQ3, HKV3)
+                               + encode_bytes(B3, HKV3)}
     rec["copy_calibration"] = {"fetch_bytes_per_counter_unit": fs, "write_bytes_per_counter_unit": wsc}
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fo:
         json.dump(rec, fo, indent=1)
@@ -889,8 +912,8 @@ def main():
 
     res = batch_step_bench(tq, cb, dev, stream, args.steps, args.warmup, max(args.samples, 50))
     value = res["bytes_per_step"] / res["s_per_step"] / 1e9
-    att_mean = res["mean_attention_us"]
-    achieved = res["attention_bytes"] / (att_mean / 1e6) / 1e9
+    step_mean = res["mean_step_us"]
+    achieved = res["sampled_step_bytes"] / (step_mean / 1e6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -906,14 +929,16 @@ def main():
                    "algorithmic_bytes_per_step": round(res["bytes_per_step"])},
         "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "median_step_us": round(res["median_step_us"], 2),
-        "median_encode_us": round(res["median_encode_us"], 2),
-        "median_attention_us": round(res["median_attention_us"], 2),
-        "attention_GBps_median": round(res["attention_bytes"] / (res["median_attention_us"] / 1e6) / 1e9, 1),
+        "two_calls": {"median_step_us": round(res["two_calls_median_step_us"], 2),
+                      "median_encode_us": round(res["median_encode_us"], 2),
+                      "median_attention_us": round(res["median_attention_us"], 2),
+                      "attention_GBps_median": round(res["attention_bytes"] / (res["median_attention_us"] / 1e6)
+                                                     / 1e9, 1)},
         "event_samples": res["samples"],
-        "roofline": {"kernel": "attention call (split_mfma_kernel + merge_kernel)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic("attention_call"),
-                     "avg_launch_us": round(att_mean, 2), "algorithmic_bytes": round(res["attention_bytes"])},
+        "roofline": {"kernel": "decode step call (step_prep_kernel + split_wave_kernel + merge_kernel)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic("decode_step_call"),
+                     "avg_launch_us": round(step_mean, 2), "algorithmic_bytes": round(res["sampled_step_bytes"])},
     }
     line.update(extra)
     if extra:

@@ -45,7 +45,8 @@ EXPORTED = [
     "tq_k_page_bytes", "tq_v_page_bytes", "tq_encode_kv", "tq_decode_workspace_bytes",
     "tq_decode_attention", "tq_decode_hot_workspace_bytes", "tq_decode_attention_hot",
     "tq_decode_noalloc_scratch_bytes", "tq_decode_attention_noalloc",
-    "tq_decode_window_workspace_bytes", "tq_decode_attention_window", "tq_last_error",
+    "tq_decode_window_workspace_bytes", "tq_decode_attention_window",
+    "tq_decode_step_workspace_bytes", "tq_decode_step", "tq_last_error",
 ]
 
 
@@ -236,6 +237,12 @@ def tq_k_page_bytes(cb: Codebook) -> int:
 def tq_v_page_bytes(cb: Codebook) -> int:
     return int(_lib.tq_v_page_bytes(cb.ref))
 
+_lib.tq_decode_step_workspace_bytes.restype = _SZ
+_lib.tq_decode_step_workspace_bytes.argtypes = [_CB, _I, _I, _I, _I, _I]
+_lib.tq_decode_step.restype = _I
+_lib.tq_decode_step.argtypes = [_CB, _P, _P, _I, _I64, _I64, _P, _P, _I, _P, _P, _P, _I, _P, _I, _I,
+                                _I, _I, ctypes.c_float, _P, _I, _I, _P, _SZ, _P]
+
 
 # ---- encode -------------------------------------------------------------------
 
@@ -300,6 +307,56 @@ def tq_decode_attention(cb: Codebook, q, k_cache, v_cache, block_tables, context
         block_tables.shape[1], _ptr(context_lens), B, q_len, Hq, num_kv_heads,
         max_context_len, float(softmax_scale), _ptr(out), _dtype_code(out), tokens_per_split,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
+    return out
+
+
+# ---- one decode step: append, then attend ------------------------------------------
+
+def tq_decode_step_workspace_bytes(cb: Codebook, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                   max_context_len: int, tokens_per_split: int = 0) -> int:
+    return int(_lib.tq_decode_step_workspace_bytes(cb.ref, num_seqs, num_q_heads, num_kv_heads,
+                                                   max_context_len, tokens_per_split))
+
+
+def tq_decode_step(cb: Codebook, k_new, v_new, slot_mapping, q, k_cache, v_cache, block_tables,
+                   context_lens, max_context_len: int, out=None, softmax_scale: float = 0.0,
+                   tokens_per_split: int = 0, workspace=None, out_dtype=None, stream=None):
+    """One new token per sequence: k_new, v_new [B][Hkv][128] (last dim
+    contiguous, same strides), slot_mapping int64 [B], q [B][1][Hq][128].
+    Appends the new keys and values, then attends; returns ``out``."""
+    torch = _torch()
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share shape, strides and dtype")
+    if k_new.dim() != 3 or k_new.shape[2] != HEAD_DIM or k_new.stride(2) != 1:
+        raise ValueError("k_new must be [B][Hkv][128] with a contiguous last dimension")
+    if q.dim() != 4 or q.shape[1] != 1 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B][1][Hq][128] tensor")
+    B, Hq = q.shape[0], q.shape[2]
+    H = k_new.shape[1]
+    if k_new.shape[0] != B:
+        raise ValueError(f"k_new must hold one token per sequence ({B})")
+    if (slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous()
+            or slot_mapping.dim() != 1 or slot_mapping.shape[0] != B):
+        raise ValueError(f"slot_mapping must be a contiguous int64 [{B}] tensor")
+    if block_tables.dtype != torch.int32 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32")
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32")
+    _check_pools(cb, k_cache, v_cache, H)
+    _check_seq_tables(block_tables, context_lens, B)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    if not out.is_contiguous() or out.shape != q.shape:
+        raise ValueError("out must be contiguous with q's shape")
+    need = tq_decode_step_workspace_bytes(cb, B, Hq, H, max_context_len, tokens_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    _check(_lib.tq_decode_step(
+        cb.ref, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), k_new.stride(0), k_new.stride(1),
+        _ptr(slot_mapping), _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), B, Hq, H, max_context_len, float(softmax_scale),
+        _ptr(out), _dtype_code(out), tokens_per_split, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, q.device)))
     return out
 
 

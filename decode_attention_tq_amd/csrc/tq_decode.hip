@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "tq_mfma.hpp"
+#include "tq_append.hpp"
 
 namespace tq {
 namespace {
@@ -1574,23 +1575,35 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     }
   }
   WaveLds<T> &sm = smu.w;
-  // the context lengths (the plan needs them first), then the projection
-  // operands, which do not depend on the plan (loads return in order: the
-  // plan then waits for the lengths only)
   constexpr bool kProjAll = T == 1;
   QPrepRegs<true> qpr;
   QPrepRegs<false> qpn;
-  const int t0s = seq_tiles(a, threadIdx.x & 63);
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    const int w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (kProjAll || w0 < 4) qprep_load_sh<true>(a, w0, threadIdx.x & 63, qpr);  // uniform
+  // the fused decode step hands over the plan and the query operands
+  const bool prepped = T == 1 && a.prep_table != nullptr;  // uniform
+  int per, b, h, jr;
+  if (prepped) {
+    const int32_t *e = a.prep_table + 4 * (int64_t)blockIdx.x;
+    b = e[0];
+    h = e[1];
+    jr = e[2];
+    per = e[3];
+    if (b < 0) return;  // uniform: past the last range
+  } else {
+    // the context lengths (the plan needs them first), then the projection
+    // operands, which do not depend on the plan (loads return in order: the
+    // plan then waits for the lengths only)
+    const int t0s = seq_tiles(a, threadIdx.x & 63);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const int w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      if (kProjAll || w0 < 4) qprep_load_sh<true>(a, w0, threadIdx.x & 63, qpr);  // uniform
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    per = bal_per(a, t0s);
+    int Tb;
+    bal_locate(a, t0s, per, blockIdx.x, b, h, jr, Tb);
+    if (b >= a.num_seqs) return;  // uniform: past the last range
   }
-  __builtin_amdgcn_sched_barrier(0);
-  const int per = bal_per(a, t0s);
-  int b, h, jr, Tb;
-  bal_locate(a, t0s, per, blockIdx.x, b, h, jr, Tb);
-  if (b >= a.num_seqs) return;  // uniform: past the last range
   const int L = clamped_context(a, b), base = seq_base(a, L);
   const int s0 = base + 128 * per * jr, s1 = min(base + 128 * per * (jr + 1), L);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1622,10 +1635,17 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     return __builtin_amdgcn_readlane(src, 8 * (slot & 7) + e);
   };
 
-  if (kProjAll || wave < 4)  // uniform
+  // the precomputed operands: kQopsDwords per lane as 16-byte pieces
+  u32x4 qo[kQopsDwords / 4];
+  if (prepped) {  // uniform
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.qops) + grp * (kQopsDwords / 4) * 64 + lane;
+#pragma unroll
+    for (int c = 0; c < kQopsDwords / 4; ++c) qo[c] = src[c * 64];
+  } else if (kProjAll || wave < 4) {  // uniform
     qprep_load_q<true>(a, grp, wave, lane, qpr);
-  else
+  } else {
     qprep_load_q<false>(a, grp, wave, lane, qpn);
+  }
 
   float beta[4];
 #pragma unroll
@@ -1702,10 +1722,21 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   int tiles_all[T];
 #pragma unroll
   for (int u = 0; u < T; ++u) tiles_all[u] = u;
-  if (kProjAll || wave < 4)  // uniform
+  if (prepped) {  // uniform
+    const auto wd = [&](int i) __attribute__((always_inline)) { return qo[i >> 2][i & 3]; };
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      Aq[0][p] = v8i{(int)wd(6 * p), (int)wd(6 * p + 1), (int)wd(6 * p + 2), (int)wd(6 * p + 3), (int)wd(6 * p + 4),
+                     (int)wd(6 * p + 5), 0, 0};
+      scq[0][p] = (int)wd(30 + p);
+    }
+    cinit[0] = v4f{__uint_as_float(wd(35)), __uint_as_float(wd(36)), __uint_as_float(wd(37)), __uint_as_float(wd(38))};
+    qinit[0] = v4f{__uint_as_float(wd(39)), __uint_as_float(wd(40)), __uint_as_float(wd(41)), __uint_as_float(wd(42))};
+  } else if (kProjAll || wave < 4) {  // uniform
     qprep_compute<T, T, true, true>(a, sm.q, qpr, tid, wave, tiles_all, Aq, scq, cinit, qinit);
-  else
+  } else {
     qprep_compute<T, T, true, false>(a, sm.q, qpn, tid, wave, tiles_all, Aq, scq, cinit, qinit);
+  }
   uint32_t *const nrm = &sm.w.nrm[wave][0][0];
   const uint16_t *const nh = reinterpret_cast<const uint16_t *>(nrm);
   // the last key each of the lane's rows sees (causal over a verify block)
@@ -1893,6 +1924,83 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   }
 }
 
+// ---- 0. fused decode step: the append, the query operands and the plan -------
+// A decode step appends each sequence's new token and then attends over the
+// whole cache.  The append is a short, latency-bound launch; this one also
+// does the work of the split pass's prologue that depends only on the
+// context lengths and (sequence, KV head) and not on the range: workgroups
+// past the append's form each group's query operands (the same code as the
+// split pass) and store them, and the last one writes the balanced plan as a
+// table, split workgroup w -> (sequence, KV head, range, per).  The split
+// pass then starts with one table entry and one operand load.
+union StepLds {
+  QPrepLds<1> q;
+  float rsh[kAppendWaves][kHeadDim];
+};
+
+template <int DT>
+__global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, DecodeArgs a, int n_append, int n_groups) {
+  __shared__ __align__(16) StepLds sm;
+  const int wg = blockIdx.x;
+  if (wg < n_append) {  // uniform
+    append_body<DT, 3>(ea, sm.rsh, wg);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wg < n_append + n_groups) {  // uniform: the query operands of one group
+    const int64_t grp = wg - n_append;
+    QPrepRegs<true> qpr;
+    qprep_load_sh<true>(a, wave, lane, qpr);
+    qprep_load_q<true>(a, grp, wave, lane, qpr);
+    v8i Aq[1][5];
+    int scq[1][5];
+    v4f ci[1], qi[1];
+    const int tiles[1] = {0};
+    qprep_compute<1, 1, true, true>(a, sm.q, qpr, tid, wave, tiles, Aq, scq, ci, qi);
+    if (wave == 0) {
+      uint32_t w[kQopsDwords];
+#pragma unroll
+      for (int p = 0; p < 5; ++p) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) w[6 * p + i] = (uint32_t)Aq[0][p][i];
+        w[30 + p] = (uint32_t)scq[0][p];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[35 + i] = __float_as_uint(ci[0][i]);
+        w[39 + i] = __float_as_uint(qi[0][i]);
+      }
+      w[43] = 0u;
+      u32x4 *dst = reinterpret_cast<u32x4 *>(a.qops) + grp * (kQopsDwords / 4) * 64 + lane;
+#pragma unroll
+      for (int c = 0; c < kQopsDwords / 4; ++c) dst[c * 64] = u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
+    }
+    return;
+  }
+  // the plan: ranges numbered as bal_locate numbers them (sequence-major, then
+  // KV head, then range); lane = sequence, 64 at a time
+  const int t0s = seq_tiles(a, lane);
+  const int per = bal_per(a, t0s);
+  const int H = a.num_kv_heads;
+  int32_t *const table = const_cast<int32_t *>(a.prep_table);
+  int base = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
+    const int T = block_tiles(a, t0s, c0, lane);
+    const int k = (T + per - 1) / per;
+    const int incl = wave_incl_scan_int(H * k, lane);
+    if (wave == 0 && c0 + lane < a.num_seqs) {
+      const int first = base + incl - H * k;
+      for (int hh = 0; hh < H; ++hh)
+        for (int j = 0; j < k; ++j) {
+          const int w = first + hh * k + j;  // < bal_grid: the grid covers every range
+          if (w < a.bal_grid) *reinterpret_cast<int4 *>(table + 4 * (int64_t)w) = make_int4(c0 + lane, hh, j, per);
+        }
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  for (int w = base + tid; w < a.bal_grid; w += 256) *reinterpret_cast<int4 *>(table + 4 * (int64_t)w) = make_int4(-1, 0, 0, 0);
+}
+
 // ---- 3. merge ---------------------------------------------------------------
 // LSE combine of the chunk partials of an output row, o' = acc'/l, one
 // inverse FWHT, store.  W waves share a row (4/W rows per workgroup); wave w
@@ -2046,6 +2154,20 @@ hipError_t noalloc_scratch(void **ptr) {
 // Kernels templated on the group size are built for 1, 2, 4, 8 and 16
 // heads; another size runs on the next one up.
 static int group_capacity(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : g <= 16 ? 16 : 0; }
+
+hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream_t stream) {
+  const int64_t vectors = ea.num_tokens * ea.num_kv_heads;
+  const int n_append = (int)((vectors + kAppendWaves - 1) / kAppendWaves);
+  const int n_groups = a.num_seqs * a.num_kv_heads;
+  const dim3 grid((unsigned)(n_append + n_groups + 1));
+  switch (ea.dtype) {
+    case TQ_BF16: hipLaunchKernelGGL(step_prep_kernel<TQ_BF16>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
+    case TQ_F16: hipLaunchKernelGGL(step_prep_kernel<TQ_F16>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
+    case TQ_F32: hipLaunchKernelGGL(step_prep_kernel<TQ_F32>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.q_len * a.num_q_heads;

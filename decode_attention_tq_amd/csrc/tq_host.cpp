@@ -348,10 +348,15 @@ tq_status tq_codebook_init(tq_codebook *cb, int head_dim, int bits, uint64_t qjl
 size_t tq_k_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::k_page_bytes(cb_bits(cb)) : 0; }
 size_t tq_v_page_bytes(const tq_codebook *cb) { return cb ? (size_t)tq::v_page_bytes(cb_bits(cb)) : 0; }
 
-tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_dtype in_dtype,
-                       int64_t num_tokens, int num_kv_heads, int64_t tok_stride,
-                       int64_t head_stride, const int64_t *slot_mapping, uint8_t *k_cache,
-                       uint8_t *v_cache, float *norms_out, void *stream) {
+}  // extern "C"
+
+namespace {
+// Checks of an encode call and its kernel arguments (shared by tq_encode_kv
+// and the fused decode step); *launch is false for an empty call.
+tq_status encode_args(const tq_codebook *cb, const void *k, const void *v, tq_dtype in_dtype, int64_t num_tokens,
+                      int num_kv_heads, int64_t tok_stride, int64_t head_stride, const int64_t *slot_mapping,
+                      uint8_t *k_cache, uint8_t *v_cache, float *norms_out, tq::EncodeArgs &a, bool *launch) {
+  *launch = false;
   tq_status st = check_cb(cb);
   if (st != TQ_OK) return st;
   if (num_tokens < 0) return fail(TQ_ERR_INVALID_ARGUMENT, "num_tokens < 0");
@@ -375,7 +380,6 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
                   "k and v must be 16-byte aligned with strides that are multiples of %d elements",
                   (int)vec);
   }
-  tq::EncodeArgs a;
   a.k = k;
   a.v = v;
   a.dtype = in_dtype;
@@ -391,6 +395,22 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
   a.St = (const float *)cb->d_tables + (size_t)tq::kQjlDim * tq::kHeadDim;
   a.SHop = (const uint16_t *)(a.St + (size_t)tq::kQjlDim * tq::kHeadDim);
   a.cb = device_codebook(cb);
+  *launch = true;
+  return TQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_dtype in_dtype,
+                       int64_t num_tokens, int num_kv_heads, int64_t tok_stride,
+                       int64_t head_stride, const int64_t *slot_mapping, uint8_t *k_cache,
+                       uint8_t *v_cache, float *norms_out, void *stream) {
+  tq::EncodeArgs a;
+  bool launch;
+  const tq_status st = encode_args(cb, k, v, in_dtype, num_tokens, num_kv_heads, tok_stride, head_stride,
+                                   slot_mapping, k_cache, v_cache, norms_out, a, &launch);
+  if (st != TQ_OK || !launch) return st;
   hipError_t e = tq::launch_encode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "encode launch");
   return TQ_OK;
@@ -404,6 +424,19 @@ namespace {
 int walk_span(int max_context_len, int q_len, int window) {
   if (window <= 0) return max_context_len;
   return (int)std::min<int64_t>(max_context_len, (int64_t)window + q_len - 1 + (tq::kBlock - 1));
+}
+
+// The fused decode step (append, query operands and plan in one launch, then
+// the one-tile-per-wave split pass reading them) serves 3-bit codes with up
+// to 4 query heads per KV head and appends of at most kAppendMaxVectors
+// vectors; other steps run the encode and the decode launches in turn.
+bool step_fused(int bits, int q_len, int group, int num_seqs, int num_kv_heads, int64_t num_tokens) {
+  return bits == 3 && q_len == 1 && group >= 1 && group <= 4 && tq::decode_uses_mfma(1, group, bits) &&
+         num_tokens * num_kv_heads <= tq::kAppendMaxVectors && (int64_t)num_seqs * num_kv_heads <= 0x7fffffffLL;
+}
+// Its workspace beyond the partial records: the groups' operands and the plan table.
+size_t step_extra_bytes(int num_seqs, int num_kv_heads, int grid) {
+  return (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64 * sizeof(uint32_t) + (size_t)grid * 16;
 }
 
 size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
@@ -436,7 +469,8 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
                       int num_q_heads, int num_kv_heads, int max_context_len,
                       float softmax_scale, void *out, tq_dtype out_dtype,
                       int tokens_per_split, void *workspace, size_t workspace_bytes,
-                      void *stream, const HotWindow *hot, bool noalloc = false, int window = 0) {
+                      void *stream, const HotWindow *hot, bool noalloc = false, int window = 0,
+                      const tq::EncodeArgs *step = nullptr) {
   tq_status st = check_cb(cb);
   if (st != TQ_OK) return st;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || (!workspace && !noalloc))
@@ -495,8 +529,10 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     hot_parts = tq::decode_hot_parts(hot->max);
     if (ns + hot_parts > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many partial records per row");
   }
-  const size_t need = decode_workspace(bits, num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
-                                       tokens_per_split, hot_parts, window);
+  size_t need = decode_workspace(bits, num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
+                                 tokens_per_split, hot_parts, window);
+  const bool fused = step && step_fused(bits, q_len, group, num_seqs, num_kv_heads, step->num_tokens);
+  if (fused) need += step_extra_bytes(num_seqs, num_kv_heads, plan.grid);
   if (noalloc) {
     // every check above is on the host; the scratch array's address is
     // resolved (once per device) only for a call that will launch
@@ -565,7 +601,20 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.hot_lens = hot ? hot->lens : nullptr;
   a.hot_max = hot ? hot->max : 0;
   a.cb = device_codebook(cb);
-  hipError_t e = tq::launch_decode(a, (hipStream_t)stream);
+  a.prep_table = nullptr;
+  a.qops = nullptr;
+  hipError_t e;
+  if (fused) {
+    // the step's extra workspace follows the partial records (16-byte aligned)
+    a.qops = reinterpret_cast<uint32_t *>(rest + tq::decode_partial_floats(rows, ns + hot_parts));
+    a.prep_table = reinterpret_cast<const int32_t *>(a.qops + (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64);
+    e = tq::launch_step_prep(*step, a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode step launch");
+  } else if (step) {
+    e = tq::launch_encode(*step, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "encode launch");
+  }
+  e = tq::launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return TQ_OK;
 }
@@ -638,6 +687,37 @@ size_t tq_decode_hot_workspace_bytes(const tq_codebook *cb, int num_seqs, int nu
   if (hot_max < 0) return 0;
   return decode_workspace(cb_bits(cb), num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, tokens_per_split,
                           tq::decode_hot_parts(hot_max));
+}
+
+size_t tq_decode_step_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int max_context_len, int tokens_per_split) {
+  const int bits = cb_bits(cb);
+  size_t need = decode_workspace(bits, num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0);
+  if (need == 0 || num_q_heads % num_kv_heads != 0) return need;
+  const int group = num_q_heads / num_kv_heads;
+  if (step_fused(bits, 1, group, num_seqs, num_kv_heads, num_seqs))
+    need += step_extra_bytes(num_seqs, num_kv_heads,
+                             plan_splits(num_seqs, 1, num_kv_heads, group, max_context_len, tokens_per_split, bits).grid);
+  return need;
+}
+
+tq_status tq_decode_step(const tq_codebook *cb, const void *k_new, const void *v_new, tq_dtype kv_dtype,
+                         int64_t tok_stride, int64_t head_stride, const int64_t *slot_mapping, const void *q,
+                         tq_dtype q_dtype, uint8_t *k_cache, uint8_t *v_cache, const int32_t *block_tables,
+                         int max_blocks_per_seq, const int32_t *context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int max_context_len, float softmax_scale, void *out, tq_dtype out_dtype,
+                         int tokens_per_split, void *workspace, size_t workspace_bytes, void *stream) {
+  if (num_seqs < 1) return fail(TQ_ERR_INVALID_ARGUMENT, "num_seqs must be >= 1");
+  tq::EncodeArgs ea;
+  bool launch;
+  const tq_status st = encode_args(cb, k_new, v_new, kv_dtype, num_seqs, num_kv_heads, tok_stride, head_stride,
+                                   slot_mapping, k_cache, v_cache, nullptr, ea, &launch);
+  if (st != TQ_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  return decode_impl(cb, q, q_dtype, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs, 1,
+                     num_q_heads, num_kv_heads, max_context_len, softmax_scale, out, out_dtype, tokens_per_split,
+                     workspace, workspace_bytes, stream, nullptr, false, 0, &ea);
 }
 
 tq_status tq_decode_attention_hot(const tq_codebook *cb, const void *q, tq_dtype q_dtype,

@@ -125,8 +125,15 @@ struct DecodeArgs {
   int hot_dtype;
   const int32_t *hot_lens;  // [num_seqs], cut to [0, hot_max]
   int hot_max;
+  // The fused decode step's precomputed plan and query operands (null
+  // otherwise): entry w of prep_table is (sequence, KV head, range, per) of
+  // split workgroup w (sequence -1: no range); qops holds each (sequence, KV
+  // head) group's matrix operands, kQopsDwords per lane.
+  const int32_t *prep_table;
+  uint32_t *qops;
   Codebook cb;
 };
+constexpr int kQopsDwords = 44;  // per lane: 5 fp6 operands of 6 dwords, 5 scales, 2 x 4 start values, 1 pad
 
 constexpr int kHotChunk = 64;  // exact window tokens per partial record
 // Largest chunk of the matrix-core decode pass (64 tiles of 128 tokens).
@@ -161,6 +168,9 @@ hipError_t noalloc_scratch(void **ptr);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// The fused decode step's append + query operands + plan launch (3-bit codes,
+// a precomputed-operand split pass: up to 4 query heads per KV head, q_len 1).
+hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace tq

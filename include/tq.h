@@ -294,6 +294,41 @@ tq_status tq_decode_attention_window(const tq_codebook *cb, const void *q, tq_dt
                                      int tokens_per_split, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/* ---- one decode step: append, then attend ---------------------------------
+ * A generation step compresses the new token's key and value into the cache
+ * and then attends over the whole compressed history with its query (the
+ * SwiftLM README, "TurboQuantization: KV Cache Compression": the K-cache
+ * steps 1-5 at write time, the step-5 estimate at read time; paging per the
+ * vLLM-MLX explainer, "Paged KVキャッシュ").  This call is exactly
+ *   tq_encode_kv(cb, k_new, v_new, kv_dtype, num_seqs, num_kv_heads,
+ *                tok_stride, head_stride, slot_mapping, k_cache, v_cache,
+ *                NULL, stream)
+ * followed by tq_decode_attention(..., q_len = 1, ...) with the remaining
+ * arguments, on `stream`, and gives bit-identical cache contents and output.
+ * With 3-bit codes, up to 4 query heads per KV head and at most 1,024 new
+ * (token, KV head) vectors, it runs as two launches instead of four: the
+ * append shares its launch with the attention's per-(sequence, KV head)
+ * query set-up and its split plan; otherwise it runs the two calls' launches.
+ *   k_new, v_new  device, element (b, h, i) of sequence b's new token at
+ *               k_new[b*tok_stride + h*head_stride + i], as in tq_encode_kv.
+ *   slot_mapping device int64[num_seqs]: the slot of sequence b's new token
+ *               (negative: no append for b).
+ *   context_lens include the new token.
+ *   workspace   tq_decode_step_workspace_bytes() bytes (same arguments),
+ *               16-byte aligned.
+ * Other arguments as in tq_decode_attention with q_len = 1.  Errors: those
+ * of tq_encode_kv and tq_decode_attention, TQ_ERR_INVALID_ARGUMENT for a
+ * misaligned workspace; on an error nothing is launched. */
+size_t tq_decode_step_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int max_context_len, int tokens_per_split);
+
+tq_status tq_decode_step(const tq_codebook *cb, const void *k_new, const void *v_new, tq_dtype kv_dtype,
+                         int64_t tok_stride, int64_t head_stride, const int64_t *slot_mapping, const void *q,
+                         tq_dtype q_dtype, uint8_t *k_cache, uint8_t *v_cache, const int32_t *block_tables,
+                         int max_blocks_per_seq, const int32_t *context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int max_context_len, float softmax_scale, void *out, tq_dtype out_dtype,
+                         int tokens_per_split, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Thread-local text describing the last non-OK status on this thread. */
 const char *tq_last_error(void);
 

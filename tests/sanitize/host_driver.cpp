@@ -80,7 +80,10 @@ int main() {
             for (int tps : {0, 256, 8192}) {
               (void)tq_decode_workspace_bytes(&cb, B, ql, hh[0], hh[1], L, tps);
               (void)tq_decode_window_workspace_bytes(&cb, B, ql, hh[0], hh[1], L, 1024, tps);
-              if (ql == 1) (void)tq_decode_hot_workspace_bytes(&cb, B, hh[0], hh[1], L, 2048, tps);
+              if (ql == 1) {
+                (void)tq_decode_hot_workspace_bytes(&cb, B, hh[0], hh[1], L, 2048, tps);
+                (void)tq_decode_step_workspace_bytes(&cb, B, hh[0], hh[1], L, tps);
+              }
             }
   }
   EXPECT(tq_decode_workspace_bytes(nullptr, 0, 1, 32, 8, 100, 0) == 0);
@@ -119,6 +122,17 @@ int main() {
          TQ_ERR_INVALID_ARGUMENT);
   EXPECT(tq_encode_kv(&cb, FAKE, FAKE, TQ_BF16, 4, 8, 1024, 100, static_cast<const int64_t *>(FAKE),
                       static_cast<uint8_t *>(FAKE), static_cast<uint8_t *>(FAKE), nullptr, nullptr) != TQ_OK);
+  auto step = [&](const void *k, int B, int hq, int hkv, int mb, int maxc, const void *ws, size_t wsb) {
+    return tq_decode_step(&cb, k, k, TQ_BF16, 1024, 128, static_cast<const int64_t *>(FAKE), FAKE, TQ_BF16,
+                          static_cast<uint8_t *>(FAKE), static_cast<uint8_t *>(FAKE), ip, mb, ip, B, hq, hkv, maxc,
+                          0.0f, FAKE, TQ_F32, 0, const_cast<void *>(ws), wsb, nullptr);
+  };
+  EXPECT(step(nullptr, 1, 32, 8, 64, 1024, FAKE, 1ull << 40) == TQ_ERR_INVALID_ARGUMENT);
+  EXPECT(step(FAKE, 0, 32, 8, 64, 1024, FAKE, 1ull << 40) == TQ_ERR_INVALID_ARGUMENT);
+  EXPECT(step(FAKE, 1, 32, 8, 64, 1024, static_cast<const char *>(FAKE) + 8, 1ull << 40) == TQ_ERR_INVALID_ARGUMENT);
+  EXPECT(step(FAKE, 1, 32, 8, 63, 1024, FAKE, 1ull << 40) == TQ_ERR_INVALID_ARGUMENT);
+  EXPECT(step(FAKE, 16, 32, 8, 2048, 32768, FAKE, 16) == TQ_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(step(FAKE, 1 << 20, 32, 8, 1 << 20, 1 << 24, FAKE, 1ull << 40) != TQ_OK);
   if (failures) {
     std::fprintf(stderr, "%d expectation(s) failed\n", failures);
     return 1;

@@ -1,0 +1,144 @@
+"""The fused decode step (append the new token's key and value, then attend)
+against the two calls it stands for, and against the oracle.
+
+tq_decode_step is tq_encode_kv of one token per sequence followed by
+tq_decode_attention with q_len 1: the cache pools and the output must be
+bit-identical to those two calls' on the same inputs, whether the step runs
+fused (3-bit codes, up to 4 query heads per KV head) or as the two calls'
+own launches.  The oracle then checks the step's output on sampled heads."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import check_decode, codebook, dev, encode_gpu, new_pools, oracle_tables
+import decode_attention_tq_amd as tq
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(seed, B, Hq, Hkv, bits=3, lo=512, hi=32768, steps=2, lengths=None):
+    case = synth.ragged_case(seed=seed, B=B, Hq=Hq, Hkv=Hkv, lo=lo, hi=hi, steps=steps, lengths=lengths)
+    cb = codebook(bits=bits)
+    kpool, vpool = new_pools(case["num_blocks"], Hkv, bits=bits)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    return case, cb, kpool, vpool
+
+
+def _two_calls(cb, kn, vn, slots, q, kpool, vpool, bt, cl, maxc, Hkv):
+    tq.tq_encode_kv(cb, kn, vn, slots, kpool, vpool)
+    return tq.tq_decode_attention(cb, q, kpool, vpool, bt, cl, maxc, Hkv)
+
+
+@pytest.mark.parametrize("Hq,Hkv,bits", [(32, 8, 3), (8, 8, 3), (16, 8, 3), (64, 8, 3), (32, 8, 2)])
+def test_step_is_append_then_decode(Hq, Hkv, bits):
+    """Two consecutive steps of a ragged batch of 16 (lengths in [512, 4096]):
+    pools and outputs equal to the separate calls' bit for bit, with one
+    sequence skipping its append (slot -1, context unchanged).  Group sizes 4,
+    1 and 2 run fused; 8 heads per KV head and 2-bit codes run unfused."""
+    B = 16
+    case, cb, kpool, vpool = _setup(11 + Hq + bits, B, Hq, Hkv, bits=bits, hi=4096)
+    ka, va = kpool.clone(), vpool.clone()
+    bt = torch.from_numpy(case["table"].astype(np.int32)).cuda()
+    L = case["lengths"].copy()
+    ws = None
+    for s in range(2):
+        slots = case["new_slots"][s].copy()
+        grow = np.ones(B, np.int64)
+        if s == 1:
+            slots[5] = -1
+            grow[5] = 0
+        L = L + grow
+        cl = torch.from_numpy(L.astype(np.int32)).cuda()
+        maxc = int(L.max())
+        kn, vn = dev(case["new_k"][s], torch.bfloat16), dev(case["new_v"][s], torch.bfloat16)
+        st = torch.from_numpy(slots).cuda()
+        q = dev(case["q"][s], torch.bfloat16)
+        ref = _two_calls(cb, kn, vn, st, q, ka, va, bt, cl, maxc, Hkv)
+        if ws is None:
+            need = tq.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, maxc + 1)
+            ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+        out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"Hq {Hq} Hkv {Hkv} bits {bits} step {s}", flush=True)
+        assert torch.equal(kpool, ka), "K pools differ"
+        assert torch.equal(vpool, va), "V pools differ"
+        assert torch.equal(out, ref), f"outputs differ: max {float((out - ref).abs().max()):.3e}"
+    if bits == 3:
+        kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
+        check_decode(out.cpu().numpy(), case["q"][1], kp, vp, case["table"], L, tables=oracle_tables(bits=bits),
+                     kv_heads=[0, Hkv - 1])
+
+
+def test_step_fp32_and_f16_inputs_and_outputs():
+    """New keys/values in fp32 with head-strided layout, an f16 query and a
+    bf16 output: equal to the separate calls."""
+    B, Hq, Hkv = 8, 32, 8
+    case, cb, kpool, vpool = _setup(21, B, Hq, Hkv, hi=2048, steps=1)
+    ka, va = kpool.clone(), vpool.clone()
+    bt = torch.from_numpy(case["table"].astype(np.int32)).cuda()
+    L = case["lengths"] + 1
+    cl = torch.from_numpy(L.astype(np.int32)).cuda()
+    maxc = int(L.max())
+    # [B][Hkv][128] views into a wider buffer: token stride 2 * Hkv * 128
+    buf = torch.zeros((B, 2 * Hkv, 128), dtype=torch.float32, device="cuda")
+    buf[:, ::2] = dev(case["new_k"][0])
+    buf[:, 1::2] = dev(case["new_v"][0])
+    kn, vn = buf[:, ::2], buf[:, 1::2]
+    st = torch.from_numpy(case["new_slots"][0].copy()).cuda()
+    q = dev(case["q"][0], torch.float16)
+    tq.tq_encode_kv(cb, kn, vn, st, ka, va)
+    ref = tq.tq_decode_attention(cb, q, ka, va, bt, cl, maxc, Hkv, out_dtype=torch.bfloat16)
+    out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(kpool, ka) and torch.equal(vpool, va)
+    assert torch.equal(out, ref)
+
+
+def test_step_short_and_empty_sequences():
+    """Context lengths 1 (the new token alone), 16, 17 and 0 with a skipped
+    append: the plan gives such sequences no range or one short one."""
+    B, Hq, Hkv = 4, 32, 8
+    case, cb, kpool, vpool = _setup(31, B, Hq, Hkv, steps=1, lengths=[0, 15, 16, 300])
+    ka, va = kpool.clone(), vpool.clone()
+    bt = torch.from_numpy(case["table"].astype(np.int32)).cuda()
+    slots = case["new_slots"][0].copy()
+    L = case["lengths"] + 1
+    slots[3] = -1
+    L[3] = 0
+    cl = torch.from_numpy(L.astype(np.int32)).cuda()
+    maxc = int(L.max())
+    kn, vn = dev(case["new_k"][0], torch.bfloat16), dev(case["new_v"][0], torch.bfloat16)
+    st = torch.from_numpy(slots).cuda()
+    q = dev(case["q"][0], torch.bfloat16)
+    ref = _two_calls(cb, kn, vn, st, q, ka, va, bt, cl, maxc, Hkv)
+    out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc)
+    torch.cuda.synchronize()
+    assert torch.equal(kpool, ka) and torch.equal(vpool, va)
+    assert torch.equal(out, ref)
+    o = out.cpu().numpy()
+    assert not np.any(o[3])                      # no key at all: zero output
+    check_decode(o, case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L)
+
+
+def test_step_decode_batch_full_size_sampled():
+    """The decode-step workload at full size: 16 sequences, log-uniform
+    lengths in [512, 32768], 32 query and 8 KV heads.  Equal to the separate
+    calls everywhere; the oracle checks sampled KV heads."""
+    B, Hq, Hkv = 16, 32, 8
+    case, cb, kpool, vpool = _setup(3, B, Hq, Hkv, steps=1)
+    ka, va = kpool.clone(), vpool.clone()
+    bt = torch.from_numpy(case["table"].astype(np.int32)).cuda()
+    L = case["lengths"] + 1
+    cl = torch.from_numpy(L.astype(np.int32)).cuda()
+    maxc = int(L.max())
+    kn, vn = dev(case["new_k"][0], torch.bfloat16), dev(case["new_v"][0], torch.bfloat16)
+    st = torch.from_numpy(case["new_slots"][0].copy()).cuda()
+    q = dev(case["q"][0], torch.bfloat16)
+    ref = _two_calls(cb, kn, vn, st, q, ka, va, bt, cl, maxc, Hkv)
+    out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc)
+    torch.cuda.synchronize()
+    assert torch.equal(kpool, ka) and torch.equal(vpool, va)
+    assert torch.equal(out, ref)
+    check_decode(out.cpu().numpy(), case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
+                 kv_heads=[2])

@@ -386,3 +386,56 @@ def test_page_sizes_and_plans_of_the_other_bit_widths():
         wb = tq._lib.tq_decode_workspace_bytes(ctypes.byref(_fake_cb(bits=b)), 4, 1, 32, 8, 8192, 0)
         assert wb > w3 and wb >= 4 * 32 * 256 * 4      # query operands of every row come first
 
+
+
+def _step(cb, **kw):
+    a = dict(k=FAKE, v=FAKE, kd=tq.TQ_BF16, ts=1024, hs=128, slots=FAKE, q=FAKE, qd=tq.TQ_BF16,
+             kc=FAKE, vc=FAKE, bt=FAKE, mb=64, cl=FAKE, B=2, Hq=32, Hkv=8, maxc=1024, scale=0.0,
+             out=FAKE, od=tq.TQ_F32, tps=0, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return tq._lib.tq_decode_step(
+        ctypes.byref(cb), a["k"], a["v"], a["kd"], a["ts"], a["hs"], a["slots"], a["q"], a["qd"],
+        a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["maxc"], a["scale"],
+        a["out"], a["od"], a["tps"], a["ws"], a["wsb"], None)
+
+
+def test_step_validation():
+    """Checks of the fused decode step that run before any launch: those of
+    the append (its new tokens, strides, alignment), those of the attention
+    call, and the workspace's size and alignment (every case fails on the
+    host, so nothing is launched)."""
+    cb = _fake_cb()
+    E = tq.TQ_ERR_INVALID_ARGUMENT
+    assert _step(_fake_cb(False)) == tq.TQ_ERR_NOT_INITIALIZED
+    assert _step(cb, B=0) == E
+    assert _step(cb, k=None) == E
+    assert _step(cb, slots=None) == E
+    assert _step(cb, kd=7) == E
+    assert _step(cb, ts=64, hs=64) == E
+    assert "overlap" in tq.tq_last_error()
+    assert _step(cb, k=FAKE + 2) == tq.TQ_ERR_UNSUPPORTED
+    assert _step(cb, ws=FAKE + 8) == E
+    assert "aligned" in tq.tq_last_error()
+    assert _step(cb, q=None) == E
+    assert _step(cb, Hq=30) == E
+    assert _step(cb, Hq=34, Hkv=2) == tq.TQ_ERR_UNSUPPORTED
+    assert _step(cb, mb=63) == E
+    assert _step(cb, scale=float("nan")) == E
+    need = tq._lib.tq_decode_step_workspace_bytes(ctypes.byref(cb), 2, 32, 8, 1024, 0)
+    assert _step(cb, wsb=need - 1) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("bits,Hq,Hkv,fused", [(3, 32, 8, True), (3, 8, 8, True), (3, 16, 8, True),
+                                                (3, 64, 8, False), (2, 32, 8, False), (4, 32, 8, False)])
+def test_step_workspace(bits, Hq, Hkv, fused):
+    """The fused step needs the attention call's partial records plus each
+    (sequence, KV head) group's query operands (44 words per lane of a
+    64-lane wave) and a 16-byte plan entry per workgroup of the split grid
+    (512 for 16 sequences of up to 32,768 tokens); an unfused step needs the
+    attention call's workspace only."""
+    cb = ctypes.byref(_fake_cb(bits=bits))
+    B, ctx = 16, 32768
+    dec = tq._lib.tq_decode_workspace_bytes(cb, B, 1, Hq, Hkv, ctx, 0)
+    step = tq._lib.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, ctx, 0)
+    extra = B * Hkv * 44 * 64 * 4 + 512 * 16 if fused else 0
+    assert step == dec + extra
