@@ -1929,14 +1929,36 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
 // whole cache.  The append is a short, latency-bound launch; this one also
 // does the work of the split pass's prologue that depends only on the
 // context lengths and (sequence, KV head) and not on the range: workgroups
-// past the append's form each group's query operands (the same code as the
-// split pass) and store them, and the last one writes the balanced plan as a
-// table, split workgroup w -> (sequence, KV head, range, per).  The split
-// pass then starts with one table entry and one operand load.
+// past the append's form one group's query operands each (the same code as
+// the split pass) and store them, and write the group's entries of the
+// balanced plan as a table, split workgroup w -> (sequence, KV head, range,
+// per); together they also mark the table's unused entries.  The split pass
+// then starts with one table entry and one operand load.
 union StepLds {
   QPrepLds<1> q;
   float rsh[kAppendWaves][kHeadDim];
 };
+
+// First plan entry of sequence b's ranges (sequence-major, then KV head, then
+// range, as bal_locate numbers them), its range count kb and the number of
+// ranges of all groups; every lane returns the same values.
+__device__ __forceinline__ int bal_first(const DecodeArgs &a, int t0, int per, int b, int &kb, int &total) {
+  const int lane = threadIdx.x & 63, H = a.num_kv_heads;
+  int base = 0, first = 0;
+  kb = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
+    const int T = block_tiles(a, t0, c0, lane);
+    const int k = (T + per - 1) / per;
+    const int incl = wave_incl_scan_int(H * k, lane);
+    if (b >= c0 && b < c0 + 64) {  // uniform
+      kb = __builtin_amdgcn_readlane(k, b - c0);
+      first = base + __builtin_amdgcn_readlane(incl, b - c0) - H * kb;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  total = base;
+  return first;
+}
 
 template <int DT>
 __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, DecodeArgs a, int n_append, int n_groups) {
@@ -1947,58 +1969,51 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wg < n_append + n_groups) {  // uniform: the query operands of one group
-    const int64_t grp = wg - n_append;
-    QPrepRegs<true> qpr;
-    qprep_load_sh<true>(a, wave, lane, qpr);
-    qprep_load_q<true>(a, grp, wave, lane, qpr);
-    v8i Aq[1][5];
-    int scq[1][5];
-    v4f ci[1], qi[1];
-    const int tiles[1] = {0};
-    qprep_compute<1, 1, true, true>(a, sm.q, qpr, tid, wave, tiles, Aq, scq, ci, qi);
-    if (wave == 0) {
-      uint32_t w[kQopsDwords];
-#pragma unroll
-      for (int p = 0; p < 5; ++p) {
-#pragma unroll
-        for (int i = 0; i < 6; ++i) w[6 * p + i] = (uint32_t)Aq[0][p][i];
-        w[30 + p] = (uint32_t)scq[0][p];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[35 + i] = __float_as_uint(ci[0][i]);
-        w[39 + i] = __float_as_uint(qi[0][i]);
-      }
-      w[43] = 0u;
-      u32x4 *dst = reinterpret_cast<u32x4 *>(a.qops) + grp * (kQopsDwords / 4) * 64 + lane;
-#pragma unroll
-      for (int c = 0; c < kQopsDwords / 4; ++c) dst[c * 64] = u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
-    }
-    return;
-  }
-  // the plan: ranges numbered as bal_locate numbers them (sequence-major, then
-  // KV head, then range); lane = sequence, 64 at a time
+  const int64_t grp = wg - n_append;
+  // the context lengths first (the plan needs them), then the operands' inputs
   const int t0s = seq_tiles(a, lane);
-  const int per = bal_per(a, t0s);
-  const int H = a.num_kv_heads;
-  int32_t *const table = const_cast<int32_t *>(a.prep_table);
-  int base = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
-    const int T = block_tiles(a, t0s, c0, lane);
-    const int k = (T + per - 1) / per;
-    const int incl = wave_incl_scan_int(H * k, lane);
-    if (wave == 0 && c0 + lane < a.num_seqs) {
-      const int first = base + incl - H * k;
-      for (int hh = 0; hh < H; ++hh)
-        for (int j = 0; j < k; ++j) {
-          const int w = first + hh * k + j;  // < bal_grid: the grid covers every range
-          if (w < a.bal_grid) *reinterpret_cast<int4 *>(table + 4 * (int64_t)w) = make_int4(c0 + lane, hh, j, per);
-        }
+  __builtin_amdgcn_sched_barrier(0);
+  QPrepRegs<true> qpr;
+  qprep_load_sh<true>(a, wave, lane, qpr);
+  qprep_load_q<true>(a, grp, wave, lane, qpr);
+  __builtin_amdgcn_sched_barrier(0);
+  if (wave == 3) {  // uniform: the group's plan entries, while the other loads are in flight
+    const int per = bal_per(a, t0s);
+    const int H = a.num_kv_heads, b = (int)(grp / H), h = (int)(grp % H);
+    int kb, total;
+    const int first = bal_first(a, t0s, per, b, kb, total) + h * kb;
+    int32_t *const table = const_cast<int32_t *>(a.prep_table);
+    for (int j = lane; j < kb; j += 64) {
+      const int w = first + j;  // < bal_grid: the grid covers every range
+      if (w < a.bal_grid) *reinterpret_cast<int4 *>(table + 4 * (int64_t)w) = make_int4(b, h, j, per);
     }
-    base += __builtin_amdgcn_readlane(incl, 63);
+    // unused entries: group g marks total + 64 g + lane, + 64 n_groups, ...
+    for (int64_t w = total + 64 * grp + lane; w < a.bal_grid; w += 64 * (int64_t)n_groups)
+      *reinterpret_cast<int4 *>(table + 4 * w) = make_int4(-1, 0, 0, 0);
   }
-  for (int w = base + tid; w < a.bal_grid; w += 256) *reinterpret_cast<int4 *>(table + 4 * (int64_t)w) = make_int4(-1, 0, 0, 0);
+  v8i Aq[1][5];
+  int scq[1][5];
+  v4f ci[1], qi[1];
+  const int tiles[1] = {0};
+  qprep_compute<1, 1, true, true>(a, sm.q, qpr, tid, wave, tiles, Aq, scq, ci, qi);
+  if (wave == 0) {
+    uint32_t w[kQopsDwords];
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) w[6 * p + i] = (uint32_t)Aq[0][p][i];
+      w[30 + p] = (uint32_t)scq[0][p];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[35 + i] = __float_as_uint(ci[0][i]);
+      w[39 + i] = __float_as_uint(qi[0][i]);
+    }
+    w[43] = 0u;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.qops) + grp * (kQopsDwords / 4) * 64 + lane;
+#pragma unroll
+    for (int c = 0; c < kQopsDwords / 4; ++c) dst[c * 64] = u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
+  }
 }
 
 // ---- 3. merge ---------------------------------------------------------------
@@ -2159,7 +2174,7 @@ hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream
   const int64_t vectors = ea.num_tokens * ea.num_kv_heads;
   const int n_append = (int)((vectors + kAppendWaves - 1) / kAppendWaves);
   const int n_groups = a.num_seqs * a.num_kv_heads;
-  const dim3 grid((unsigned)(n_append + n_groups + 1));
+  const dim3 grid((unsigned)(n_append + n_groups));
   switch (ea.dtype) {
     case TQ_BF16: hipLaunchKernelGGL(step_prep_kernel<TQ_BF16>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
     case TQ_F16: hipLaunchKernelGGL(step_prep_kernel<TQ_F16>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
