@@ -201,6 +201,7 @@ def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples):
     for i in range(warmup, warmup + steps):
         step(i)
     t1.record(stream)
+    enqueue = time.perf_counter() - w0
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     gpu_s = t0.elapsed_time(t1) / 1e3
@@ -233,7 +234,7 @@ def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples):
     idc = range(base + warmup, base + warmup + samples)
     dec_b = float(np.mean([st["dec_bytes"][i] for i in idc]))
     res = dict(
-        s_per_step=s_per_step, bytes_per_step=bytes_a, gpu_s=gpu_s, wall_s=wall, replicas=R,
+        s_per_step=s_per_step, bytes_per_step=bytes_a, gpu_s=gpu_s, wall_s=wall, enqueue_s=enqueue, replicas=R,
         lengths=[int(x) for x in st["L"]], max_ctx=st["max_ctx"],
         median_step_us=statistics.median(step_us), mean_step_us=float(np.mean(step_us)), sampled_step_bytes=step_b,
         two_calls_median_step_us=statistics.median([a + b for a, b in zip(enc_us, dec_us)]),
@@ -929,6 +930,8 @@ def main():
                    "algorithmic_bytes_per_step": round(res["bytes_per_step"])},
         "pct_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "median_step_us": round(res["median_step_us"], 2),
+        "timed_region": {"wall_s": round(res["wall_s"], 6), "gpu_event_s": round(res["gpu_s"], 6),
+                         "host_enqueue_s": round(res["enqueue_s"], 6)},
         "two_calls": {"median_step_us": round(res["two_calls_median_step_us"], 2),
                       "median_encode_us": round(res["median_encode_us"], 2),
                       "median_attention_us": round(res["median_attention_us"], 2),

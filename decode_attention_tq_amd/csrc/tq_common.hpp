@@ -213,4 +213,16 @@ __device__ __forceinline__ _Float16 to_half_sat(float v) {
   return (_Float16)fminf(v, 65504.0f);
 }
 
+// A matrix instruction writes its whole result, on every lane, whatever the
+// exec mask.  The compiler may nevertheless move one into a branch taken by
+// the lanes that use its result (a score formed only where the mask keeps
+// it): the lanes outside the branch then find their own value in the result
+// registers overwritten (a masked -inf replaced by a finite score).  Pinning
+// the result in registers right after the chain that forms it keeps the
+// instructions out of any such branch.
+template <class V>
+__device__ __forceinline__ void pin_result(V &x) {
+  asm volatile("" : "+v"(x));
+}
+
 }  // namespace tq

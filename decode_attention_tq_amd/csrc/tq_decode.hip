@@ -1018,6 +1018,8 @@ __device__ __attribute__((always_inline)) void split_body_ws(const DecodeArgs &a
           c = mfma_f6f4(Aq[u][2], B2, c, scq[u][2]);
           cc[u][e] = mfma_f6f4(Aq[u][3], Bx, c, scq[u][3]);
           qq[u][e] = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
+          pin_result(cc[u][e]);
+          pin_result(qq[u][e]);
         }
       }
       // uniform: a tile some row does not see whole
@@ -1417,6 +1419,7 @@ __device__ __attribute__((always_inline)) void hot_body(const DecodeArgs &a, Hot
       sc = hot_mfma<MT>(Ah[s], Bk[s][2], sc);
     }
   }
+  pin_result(sc);
   // lane l, register i: head 4 kg + i, token n16 of the wave
   const bool valid = j0 + n16 < W;
   float m4[4];
@@ -1767,7 +1770,9 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
         c = mfma_f6f4(Aq[u][1], B1, c, scq[u][1]);
         c = mfma_f6f4(Aq[u][2], B2, c, scq[u][2]);
         c = mfma_f6f4(Aq[u][3], Bx, c, scq[u][3]);
-        const v4f qv = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
+        v4f qv = mfma_f6f4(Aq[u][4], Bs, qinit[u], scq[u][4]);
+        pin_result(c);
+        pin_result(qv);
         const float inner = fmaf(gmv, (qv[0] + qv[1]) + (qv[2] + qv[3]), (c[0] + c[1]) + (c[2] + c[3]));
         // a slot the lane's row does not see (past the range, or causal) is -inf
         rs[u][e] = tq < lim[u] && tq >= low[u] ? nkv * inner : -INFINITY;

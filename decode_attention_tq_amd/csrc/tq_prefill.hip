@@ -324,6 +324,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < kRowTiles; ++u) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        pin_result(cc[u][ct]);
+        pin_result(csg[u][ct]);
+      }
+    }
 
     // ---- online softmax (log2 units), exact running maximum --------------
     float knv[2][4], kgv[2][4], vnv[2][4];

@@ -477,3 +477,23 @@ def test_largest_chunk_of_the_matrix_core_pass(Hq, Hkv):
                      tokens_per_split=8192)
     check_decode(out, case["q"], _np(kpool), _np(vpool), case["table"], case["context_lens"],
                  kv_heads=[0, Hkv - 1])
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 8)])
+def test_last_tile_with_a_few_tokens(Hq, Hkv):
+    """Sequences whose last 128-token tile holds 2, 3 or 15 tokens, with 1, 2
+    and 4 query heads per KV head and two chunk sizes: the masked slots of
+    that tile (pages re-read past the end, slots never written) must get no
+    weight.  Element-wise against the oracle on every head."""
+    lengths = [643, 1154, 3343, 836, 1249, 2, 130, 3]
+    case = synth.ragged_case(seed=17, B=len(lengths), Hq=Hq, Hkv=Hkv, steps=1, lengths=lengths)
+    cb = codebook()
+    kpool, vpool = new_pools(case["num_blocks"], Hkv)
+    encode_gpu(cb, case["k"], case["v"], case["slots"], kpool, vpool, with_norms=False)
+    L = case["lengths"]
+    kp, vp = _np(kpool), _np(vpool)
+    for tps in (0, 2048):
+        out = decode_gpu(cb, case["q"][0], kpool, vpool, case["table"], L.astype(np.int32), Hkv,
+                         tokens_per_split=tps)
+        err = check_decode(out, case["q"][0], kp, vp, case["table"], L)
+        print(f"Hq {Hq} tps {tps}: max rel err {err.max():.3e}")
