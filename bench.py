@@ -895,21 +895,17 @@ def main():
 
     extra = {}
     if not args.headline_only:
-        extra["attention_long"] = long_context_attention(tq, cb, dev, stream)
-        torch.cuda.empty_cache()
-        extra["prefill"] = prefill_bench(tq, cb, dev, stream)
-        torch.cuda.empty_cache()
-        extra["layer_8192"] = layer_bench(tq, cb, dev, stream)
-        torch.cuda.empty_cache()
-        extra["attention_verify"] = verify_attention(tq, cb, dev, stream)
-        torch.cuda.empty_cache()
-        extra["attention_hot_window"] = hot_window_attention(tq, cb, dev, stream)
-        torch.cuda.empty_cache()
-        extra["attention_window"] = window_attention(tq, cb, dev, stream)
-        torch.cuda.empty_cache()
-        extra["bits_variants"] = bits_variants(tq, dev, stream)
-        torch.cuda.empty_cache()
-        print(json.dumps({"progress": "side measurements done"}), file=sys.stderr, flush=True)
+        sides = (("attention_long", lambda: long_context_attention(tq, cb, dev, stream)),
+                 ("prefill", lambda: prefill_bench(tq, cb, dev, stream)),
+                 ("layer_8192", lambda: layer_bench(tq, cb, dev, stream)),
+                 ("attention_verify", lambda: verify_attention(tq, cb, dev, stream)),
+                 ("attention_hot_window", lambda: hot_window_attention(tq, cb, dev, stream)),
+                 ("attention_window", lambda: window_attention(tq, cb, dev, stream)),
+                 ("bits_variants", lambda: bits_variants(tq, dev, stream)))
+        for key, run in sides:
+            extra[key] = run()
+            torch.cuda.empty_cache()
+            print(json.dumps({"progress": key + " done"}), file=sys.stderr, flush=True)
 
     res = batch_step_bench(tq, cb, dev, stream, args.steps, args.warmup, max(args.samples, 50))
     value = res["bytes_per_step"] / res["s_per_step"] / 1e9

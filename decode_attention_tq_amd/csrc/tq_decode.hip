@@ -1939,6 +1939,22 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
 // balanced plan as a table, split workgroup w -> (sequence, KV head, range,
 // per); together they also mark the table's unused entries.  The split pass
 // then starts with one table entry and one operand load.
+// Workgroup w of a launch runs on accelerator die (XCD) w mod 8, each with
+// its own L2.  The ranges, numbered sequence-major r = 0 .. total - 1, go to
+// the dies in 8 contiguous runs (die x: ranges from ceil(x total / 8)), so
+// a group's ranges share one die and its L2 fetches the group's operands
+// once; range r of run x is workgroup 8 s + x, s its place in the run.  The
+// grid needs total + 7 workgroups.
+__device__ __forceinline__ int xcd_run_start(int x, int total) { return (x * total + 7) / 8; }
+__device__ __forceinline__ int xcd_slot(int r, int total) {
+  const int x = (8 * r) / total;
+  return 8 * (r - xcd_run_start(x, total)) + x;
+}
+__device__ __forceinline__ bool xcd_slot_used(int w, int total) {
+  const int x = w & 7;
+  return (w >> 3) < xcd_run_start(x + 1, total) - xcd_run_start(x, total);
+}
+
 union StepLds {
   QPrepLds<1> q;
   float rsh[kAppendWaves][kHeadDim];
@@ -1989,12 +2005,12 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
     const int first = bal_first(a, t0s, per, b, kb, total) + h * kb;
     int32_t *const table = const_cast<int32_t *>(a.prep_table);
     for (int j = lane; j < kb; j += 64) {
-      const int w = first + j;  // < bal_grid: the grid covers every range
+      const int w = xcd_slot(first + j, total);  // < bal_grid: the grid covers every range, plus 7
       if (w < a.bal_grid) *reinterpret_cast<int4 *>(table + 4 * (int64_t)w) = make_int4(b, h, j, per);
     }
-    // unused entries: group g marks total + 64 g + lane, + 64 n_groups, ...
-    for (int64_t w = total + 64 * grp + lane; w < a.bal_grid; w += 64 * (int64_t)n_groups)
-      *reinterpret_cast<int4 *>(table + 4 * w) = make_int4(-1, 0, 0, 0);
+    // unused entries: group g looks at 64 g + lane, + 64 n_groups, ...
+    for (int64_t w = 64 * grp + lane; w < a.bal_grid; w += 64 * (int64_t)n_groups)
+      if (!xcd_slot_used((int)w, total)) *reinterpret_cast<int4 *>(table + 4 * w) = make_int4(-1, 0, 0, 0);
   }
   v8i Aq[1][5];
   int scq[1][5];

@@ -434,6 +434,9 @@ bool step_fused(int bits, int q_len, int group, int num_seqs, int num_kv_heads, 
   return bits == 3 && q_len == 1 && group >= 1 && group <= 4 && tq::decode_uses_mfma(1, group, bits) &&
          num_tokens * num_kv_heads <= tq::kAppendMaxVectors && (int64_t)num_seqs * num_kv_heads <= 0x7fffffffLL;
 }
+// The fused step's split grid: the plan's, plus 7 workgroups (its table
+// places the ranges in one run per accelerator die, the last runs padded).
+int step_grid(int grid) { return grid + 7; }
 // Its workspace beyond the partial records: the groups' operands and the plan table.
 size_t step_extra_bytes(int num_seqs, int num_kv_heads, int grid) {
   return (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64 * sizeof(uint32_t) + (size_t)grid * 16;
@@ -532,7 +535,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   size_t need = decode_workspace(bits, num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
                                  tokens_per_split, hot_parts, window);
   const bool fused = step && step_fused(bits, q_len, group, num_seqs, num_kv_heads, step->num_tokens);
-  if (fused) need += step_extra_bytes(num_seqs, num_kv_heads, plan.grid);
+  if (fused) need += step_extra_bytes(num_seqs, num_kv_heads, step_grid(plan.grid));
   if (noalloc) {
     // every check above is on the host; the scratch array's address is
     // resolved (once per device) only for a call that will launch
@@ -605,6 +608,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.qops = nullptr;
   hipError_t e;
   if (fused) {
+    a.bal_grid = step_grid(plan.grid);
     // the step's extra workspace follows the partial records (16-byte aligned)
     a.qops = reinterpret_cast<uint32_t *>(rest + tq::decode_partial_floats(rows, ns + hot_parts));
     a.prep_table = reinterpret_cast<const int32_t *>(a.qops + (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64);
@@ -696,8 +700,9 @@ size_t tq_decode_step_workspace_bytes(const tq_codebook *cb, int num_seqs, int n
   if (need == 0 || num_q_heads % num_kv_heads != 0) return need;
   const int group = num_q_heads / num_kv_heads;
   if (step_fused(bits, 1, group, num_seqs, num_kv_heads, num_seqs))
-    need += step_extra_bytes(num_seqs, num_kv_heads,
-                             plan_splits(num_seqs, 1, num_kv_heads, group, max_context_len, tokens_per_split, bits).grid);
+    need += step_extra_bytes(
+        num_seqs, num_kv_heads,
+        step_grid(plan_splits(num_seqs, 1, num_kv_heads, group, max_context_len, tokens_per_split, bits).grid));
   return need;
 }
 

@@ -431,11 +431,12 @@ def test_step_workspace(bits, Hq, Hkv, fused):
     """The fused step needs the attention call's partial records plus each
     (sequence, KV head) group's query operands (44 words per lane of a
     64-lane wave) and a 16-byte plan entry per workgroup of the split grid
-    (512 for 16 sequences of up to 32,768 tokens); an unfused step needs the
-    attention call's workspace only."""
+    (512 for 16 sequences of up to 32,768 tokens, plus 7 for the runs of
+    ranges per accelerator die); an unfused step needs the attention call's
+    workspace only."""
     cb = ctypes.byref(_fake_cb(bits=bits))
     B, ctx = 16, 32768
     dec = tq._lib.tq_decode_workspace_bytes(cb, B, 1, Hq, Hkv, ctx, 0)
     step = tq._lib.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, ctx, 0)
-    extra = B * Hkv * 44 * 64 * 4 + 512 * 16 if fused else 0
+    extra = B * Hkv * 44 * 64 * 4 + (512 + 7) * 16 if fused else 0
     assert step == dec + extra
