@@ -142,3 +142,31 @@ def test_step_decode_batch_full_size_sampled():
     assert torch.equal(out, ref)
     check_decode(out.cpu().numpy(), case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
                  kv_heads=[2])
+
+
+def test_step_more_than_64_sequences_and_large_appends():
+    """80 sequences (the plan's sequence blocks of 64 lanes: the table,
+    the runs per die and the operand groups span two blocks), then 140
+    sequences x 8 KV heads = 1,120 appended vectors, past the one-wave
+    append (the step runs the tiled encoder and the attention call's own
+    launches).  Pools and outputs equal to the separate calls; the oracle
+    checks sampled heads."""
+    for B, hi in ((80, 3000), (140, 1500)):
+        Hq, Hkv = 32, 8
+        case, cb, kpool, vpool = _setup(41 + B, B, Hq, Hkv, lo=1, hi=hi, steps=1)
+        ka, va = kpool.clone(), vpool.clone()
+        bt = torch.from_numpy(case["table"].astype(np.int32)).cuda()
+        L = case["lengths"] + 1
+        cl = torch.from_numpy(L.astype(np.int32)).cuda()
+        maxc = int(L.max())
+        kn, vn = dev(case["new_k"][0], torch.bfloat16), dev(case["new_v"][0], torch.bfloat16)
+        st = torch.from_numpy(case["new_slots"][0].copy()).cuda()
+        q = dev(case["q"][0], torch.bfloat16)
+        ref = _two_calls(cb, kn, vn, st, q, ka, va, bt, cl, maxc, Hkv)
+        out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc)
+        torch.cuda.synchronize()
+        print(f"B {B}: step done", flush=True)
+        assert torch.equal(kpool, ka) and torch.equal(vpool, va)
+        assert torch.equal(out, ref), f"outputs differ: max {float((out - ref).abs().max()):.3e}"
+        check_decode(out.cpu().numpy(), case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
+                     kv_heads=[1, 6])
