@@ -167,7 +167,9 @@ def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples):
     total = warmup + steps + 2 * (warmup + samples)
     st = batch_setup(tq, cb, dev, total)
     out = torch.empty((B3, 1, HQ3, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(tq.tq_decode_step_workspace_bytes(cb, B3, HQ3, HKV3, st["max_ctx"]), dtype=torch.uint8,
+    # one buffer serves the step calls and the breakdown's attention calls
+    ws = torch.empty(max(tq.tq_decode_step_workspace_bytes(cb, B3, HQ3, HKV3, st["max_ctx"]),
+                         tq.tq_decode_workspace_bytes(cb, B3, 1, HQ3, HKV3, st["max_ctx"])), dtype=torch.uint8,
                      device=dev)
     R = st["R"]
 

@@ -1537,6 +1537,92 @@ void launch_hot(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
 //     (o' = -sum_p beta_p acc_p), so its accumulators stay small.
 // The K part of tile k + 4T is fetched right after tile k's scores and the V
 // part right after its values, so each fetch has the other phase to arrive.
+// Workgroup w of a launch runs on accelerator die (XCD) w mod 8, each with
+// its own L2.  Work numbered r = 0 .. total - 1 goes to the dies in 8
+// contiguous runs (die x: from ceil(x total / 8)), so neighbouring work
+// shares one die's L2; item r of run x is workgroup 8 s + x, s its place in
+// the run.  A grid of total + 7 workgroups covers every run.
+__device__ __forceinline__ int xcd_run_start(int x, int total) { return (x * total + 7) / 8; }
+
+// ---- stream plan (the fused decode step) -------------------------------------
+// The tiles of every (sequence, KV head) group in one order (sequence-major,
+// then KV head, then tile; group g = b H + h starts at C_g = H sum_{b'<b} T_b'
+// + h T_b, N tiles in all).  Wave i of the split pass takes the q tiles from
+// i q, q = ceil(N / (4 bal_target)) within [1, kStreamMaxTiles]: every wave
+// has the same work whatever the lengths (a plan of whole ranges per group
+// leaves some compute units with a third more tiles than the mean).  A wave
+// whose tiles span groups writes one partial record per group it touches:
+// the record of (wave i, group g) sits at place i + g, and group g's records
+// are the consecutive places from floor(C_g / q) + g to floor((C_g + T_g - 1)
+// / q) + g.  Waves are numbered along the dies' runs (4 per workgroup), so a
+// group's waves share one die.
+constexpr int kStreamMaxTiles = 16;
+__device__ __forceinline__ int lane_context(const DecodeArgs &a, int s) {
+  return s < a.num_seqs ? clamped_context(a, s) : 0;
+}
+__device__ __forceinline__ int span_tiles(const DecodeArgs &a, int L) { return (L - seq_base(a, L) + 127) >> 7; }
+// Tile count of sequence c0 + lane (t0: the caller's first load for lanes 0..63).
+__device__ __forceinline__ int stream_block_tiles(const DecodeArgs &a, int t0, int c0, int lane) {
+  return c0 == 0 ? t0 : span_tiles(a, lane_context(a, c0 + lane));
+}
+__device__ __forceinline__ int stream_total(const DecodeArgs &a, int t0) {
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64)  // uniform
+    tot += __builtin_amdgcn_readlane(wave_incl_scan_int(stream_block_tiles(a, t0, c0, lane), lane), 63);
+  return tot * a.num_kv_heads;
+}
+__device__ __forceinline__ int stream_per(const DecodeArgs &a, int N) {
+  const int waves = 4 * a.bal_target;
+  return min(max((N + waves - 1) / waves, 1), kStreamMaxTiles);
+}
+// Per lane: sequence b, KV head h and tile t of global tile c (0 <= c < N)
+// and the sequence's context length L.  Every lane of the wave takes part.
+__device__ __forceinline__ void stream_locate(const DecodeArgs &a, int t0, int L0, int c, int &b, int &h, int &t,
+                                              int &L) {
+  const int lane = threadIdx.x & 63, H = a.num_kv_heads;
+  int run = 0;
+  b = h = t = L = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
+    const int Ll = c0 == 0 ? L0 : lane_context(a, c0 + lane);
+    const int T = c0 == 0 ? t0 : span_tiles(a, Ll);
+    const int incl = wave_incl_scan_int(H * T, lane) + run;
+    const int excl = incl - H * T;
+    // the last lane j with excl_j <= c (excl does not decrease along the lanes)
+    int j = 0;
+#pragma unroll
+    for (int st = 32; st > 0; st >>= 1)
+      if (__builtin_amdgcn_ds_bpermute(4 * (j + st), excl) <= c) j += st;
+    const int ej = __builtin_amdgcn_ds_bpermute(4 * j, excl);
+    const int Tj = __builtin_amdgcn_ds_bpermute(4 * j, T);
+    const int Lj = __builtin_amdgcn_ds_bpermute(4 * j, Ll);
+    const int end = __builtin_amdgcn_readlane(incl, 63);
+    if (c >= run && c < end) {  // this lane's tile lies in this block (then Tj > 0)
+      b = c0 + j;
+      const int rel = c - ej;
+      h = rel / Tj;
+      t = rel - h * Tj;
+      L = Lj;
+    }
+    run = end;
+  }
+}
+// Exclusive prefix P_b = H sum_{b'<b} T_b' and T_b of sequence b (uniform b).
+__device__ __forceinline__ void stream_prefix(const DecodeArgs &a, int t0, int b, int &P, int &Tb) {
+  const int lane = threadIdx.x & 63, H = a.num_kv_heads;
+  int run = 0;
+  P = Tb = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
+    const int T = stream_block_tiles(a, t0, c0, lane);
+    const int incl = wave_incl_scan_int(H * T, lane) + run;
+    if (b >= c0 && b < c0 + 64) {  // uniform
+      Tb = __builtin_amdgcn_readlane(T, b - c0);
+      P = __builtin_amdgcn_readlane(incl, b - c0) - H * Tb;
+    }
+    run = __builtin_amdgcn_readlane(incl, 63);
+  }
+}
+
 // One reference R per head serves the scores and the accumulators: it moves
 // (rarely) when a score exceeds it by 2^64, and the digits of a pair carry
 // the R they were formed with.
@@ -1567,11 +1653,16 @@ union WaveOrHotLds {
 
 // Workgroups past the plan's grid take the exact window's chunks (a call
 // with a hot window, T = 1): they run beside the split pass instead of after it.
-template <int T>
+// STREAM: the fused decode step's pass, on the stream plan above, with the
+// query operands formed beforehand (one head tile; each wave on its own).
+template <int T, bool STREAM>
 __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(DecodeArgs a) {
+  static_assert(!STREAM || T == 1, "the stream plan serves one head tile");
   constexpr int NW = 4 * T;
   __shared__ __align__(16) WaveOrHotLds<T> smu;
-  if constexpr (T == 1) {
+  // stream plan: (sequence, KV head, tile, context length) of each tile slot of a wave
+  __shared__ int4 slot_sh[STREAM ? 4 : 1][kStreamMaxTiles];
+  if constexpr (T == 1 && !STREAM) {
     if ((int)blockIdx.x >= a.bal_grid) {  // uniform
       hot_body_any(a, smu.h, (int)blockIdx.x - a.bal_grid);
       return;
@@ -1581,69 +1672,92 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   constexpr bool kProjAll = T == 1;
   QPrepRegs<true> qpr;
   QPrepRegs<false> qpn;
-  // the fused decode step hands over the plan and the query operands
-  const bool prepped = T == 1 && a.prep_table != nullptr;  // uniform
-  int per, b, h, jr;
-  if (prepped) {
-    const int32_t *e = a.prep_table + 4 * (int64_t)blockIdx.x;
-    b = e[0];
-    h = e[1];
-    jr = e[2];
-    per = e[3];
-    if (b < 0) return;  // uniform: past the last range
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t16 = lane & 15, grow = lane >> 4;
+  const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count, G = a.group;
+  // the range (ranges plan) or the wave's current group (stream plan): its
+  // sequence b, KV head h, keys [s0, s1) and the sequence's length L
+  int b, h, L, s0, s1, ntiles, jr = 0;
+  int iw = 0;  // stream plan: the wave's place in the order
+  // block ids of this wave's tile slots (at most 16) as (block id) x (KV
+  // heads) + KV head: lane l holds page l % 8 of slot l / 8 (ids0) and of
+  // slot 8 + l / 8 (ids1); a page past the keys re-reads its tile's first
+  // page, and a slot past the wave's last tile repeats that tile (the tokens
+  // are masked)
+  int ids0, ids1;
+  if constexpr (STREAM) {
+    const int Lw = lane_context(a, lane);
+    const int t0s = span_tiles(a, Lw);
+    const int N = stream_total(a, t0s);
+    const int q = stream_per(a, N);
+    const int nwg = ((N + q - 1) / q + 3) >> 2;
+    const int x = (int)blockIdx.x & 7, rpos = xcd_run_start(x, nwg) + ((int)blockIdx.x >> 3);
+    if (rpos >= xcd_run_start(x + 1, nwg)) return;  // uniform: no waves in this workgroup
+    iw = 4 * rpos + wave;
+    ntiles = min(q, N - iw * q);
+    if (ntiles <= 0) return;  // uniform: past the last tile (this plan has no workgroup barrier)
+    const int e = lane & 7;
+    auto slot_ids = [&](int k) __attribute__((always_inline)) {
+      int sb, sh, st, sl;
+      stream_locate(a, t0s, Lw, iw * q + min(k, ntiles - 1), sb, sh, st, sl);
+      const int tile0 = seq_base(a, sl) + 128 * st, tok = tile0 + 16 * e;
+      if (e == 0) slot_sh[wave][k] = make_int4(sb, sh, st, sl);
+      const int id = a.block_tables[(int64_t)sb * a.max_blocks + page_entry(a, (tok < sl ? tok : tile0) >> 4)];
+      return id * a.num_kv_heads + sh;
+    };
+    ids0 = slot_ids(lane >> 3);
+    ids1 = slot_ids(8 + (lane >> 3));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    const int4 f0 = slot_sh[wave][0];
+    b = __builtin_amdgcn_readfirstlane(f0.x);
+    h = __builtin_amdgcn_readfirstlane(f0.y);
+    L = __builtin_amdgcn_readfirstlane(f0.w);
+    s0 = seq_base(a, L);
+    s1 = L;
   } else {
     // the context lengths (the plan needs them first), then the projection
     // operands, which do not depend on the plan (loads return in order: the
     // plan then waits for the lengths only)
-    const int t0s = seq_tiles(a, threadIdx.x & 63);
+    const int t0s = seq_tiles(a, lane);
     __builtin_amdgcn_sched_barrier(0);
-    {
-      const int w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-      if (kProjAll || w0 < 4) qprep_load_sh<true>(a, w0, threadIdx.x & 63, qpr);  // uniform
-    }
+    if (kProjAll || wave < 4) qprep_load_sh<true>(a, wave, lane, qpr);  // uniform
     __builtin_amdgcn_sched_barrier(0);
-    per = bal_per(a, t0s);
+    const int per = bal_per(a, t0s);
     int Tb;
     bal_locate(a, t0s, per, blockIdx.x, b, h, jr, Tb);
     if (b >= a.num_seqs) return;  // uniform: past the last range
-  }
-  const int L = clamped_context(a, b), base = seq_base(a, L);
-  const int s0 = base + 128 * per * jr, s1 = min(base + 128 * per * (jr + 1), L);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t16 = lane & 15, grow = lane >> 4;
-  const int64_t grp = (int64_t)b * a.num_kv_heads + h;
-  const int qlen = a.q_len - a.pos0, nrows = a.group * a.pos_count, G = a.group;
-  const int s1v = min(s1, L - qlen + 1);  // every row sees the keys before s1v
-  const int ntiles = (s1 - s0 + 127) >> 7;
-
-  // block ids of this wave's tiles w, w + NW, ... (at most 16): lane l holds
-  // page l % 8 of tile slot l / 8 (ids0) and of slot 8 + l / 8 (ids1); a page
-  // past the range re-reads its tile's first page (its tokens are masked)
-  int ids0, ids1;
-  {
+    L = clamped_context(a, b);
+    const int base = seq_base(a, L);
+    s0 = base + 128 * per * jr;
+    s1 = min(base + 128 * per * (jr + 1), L);
+    ntiles = (s1 - s0 + 127) >> 7;
     const int32_t *btab = a.block_tables + (int64_t)b * a.max_blocks;
     const int e = lane & 7;
     int k = wave + NW * (lane >> 3);
     int tile0 = s0 + 128 * min(k, ntiles - 1);
     int tok = tile0 + 16 * e;
-    ids0 = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)];
+    ids0 = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)] * a.num_kv_heads + h;
     k += 8 * NW;
     tile0 = s0 + 128 * min(k, ntiles - 1);
     tok = tile0 + 16 * e;
-    ids1 = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)];
+    ids1 = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)] * a.num_kv_heads + h;
   }
+  int64_t grp = (int64_t)b * a.num_kv_heads + h;
   auto page_id = [&](int slot, int e) __attribute__((always_inline)) {
     const int src = slot < 8 ? ids0 : ids1;
     return __builtin_amdgcn_readlane(src, 8 * (slot & 7) + e);
   };
 
-  // the precomputed operands: kQopsDwords per lane as 16-byte pieces
+  // the precomputed operands (stream plan): kQopsDwords per lane as 16-byte pieces
   u32x4 qo[kQopsDwords / 4];
-  if (prepped) {  // uniform
+  auto load_qops = [&]() __attribute__((always_inline)) {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(a.qops) + grp * (kQopsDwords / 4) * 64 + lane;
 #pragma unroll
     for (int c = 0; c < kQopsDwords / 4; ++c) qo[c] = src[c * 64];
+  };
+  if constexpr (STREAM) {
+    load_qops();
   } else if (kProjAll || wave < 4) {  // uniform
     qprep_load_q<true>(a, grp, wave, lane, qpr);
   } else {
@@ -1658,7 +1772,6 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   const uint32_t s80 = in_vgpr((t16 & 3) == 3 ? 0u : 0x80008000u);
   const int kap0 = 8 * (t16 & 3) + (t16 >> 2);
   const int gA = t16 >> 2, rA = lane & 3;
-  const int64_t hkv = a.num_kv_heads;
   const uint8_t *const kc = a.k_cache, *const vc = a.v_cache;
   // the lane's K record: coordinate chunk grow, token t16 (planes 0..2, signs)
   const uint32_t ko = (uint32_t)k_record(grow, t16);
@@ -1689,19 +1802,19 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   auto load_k = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint8_t *kp = uniform_ptr(kc + ((int64_t)page_id(i, e) * hkv + h) * kKPage);
+      const uint8_t *kp = uniform_ptr(kc + (int64_t)page_id(i, e) * kKPage);
       KP[e] = load_at<u32x4>(kp, ko);
     }
     const int64_t pid = (int64_t)__builtin_amdgcn_ds_bpermute(4 * (8 * (i & 7) + ne), i < 8 ? ids0 : ids1);
-    const uint8_t *np = nk ? kc + (pid * hkv + h) * kKPage : vc + (pid * hkv + h) * kVPage;
+    const uint8_t *np = nk ? kc + pid * kKPage : vc + pid * kVPage;
     NR = *reinterpret_cast<const u32x4 *>(np + no);
   };
   auto load_v = [&](int i) __attribute__((always_inline)) {
     const int src = i < 8 ? ids0 : ids1;
     const int pa = __builtin_amdgcn_ds_bpermute(4 * (8 * (i & 7) + 2 * grow), src);
     const int pb = __builtin_amdgcn_ds_bpermute(4 * (8 * (i & 7) + 2 * grow + 1), src);
-    const uint8_t *va = vc + ((int64_t)pa * hkv + h) * kVPage + 16 * t16;
-    const uint8_t *vb = vc + ((int64_t)pb * hkv + h) * kVPage + 16 * t16;
+    const uint8_t *va = vc + (int64_t)pa * kVPage + 16 * t16;
+    const uint8_t *vb = vc + (int64_t)pb * kVPage + 16 * t16;
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
       VA[p][0] = *reinterpret_cast<const u32x4 *>(va + kVPlane * p);
@@ -1710,7 +1823,9 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   };
 
   int slot = 0;
-  int k = wave;
+  // tile k of the range (wave w: w, w + NW, ...) or of the wave's own tiles
+  constexpr int kStep = STREAM ? 1 : NW;
+  int k = STREAM ? 0 : wave;
   // the first tile's pages are requested before the query operands are
   // formed, so that their memory latency overlaps that work
   if (k < ntiles) {  // uniform
@@ -1725,7 +1840,7 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   int tiles_all[T];
 #pragma unroll
   for (int u = 0; u < T; ++u) tiles_all[u] = u;
-  if (prepped) {  // uniform
+  auto set_qops = [&]() __attribute__((always_inline)) {
     const auto wd = [&](int i) __attribute__((always_inline)) { return qo[i >> 2][i & 3]; };
 #pragma unroll
     for (int p = 0; p < 5; ++p) {
@@ -1735,6 +1850,9 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     }
     cinit[0] = v4f{__uint_as_float(wd(35)), __uint_as_float(wd(36)), __uint_as_float(wd(37)), __uint_as_float(wd(38))};
     qinit[0] = v4f{__uint_as_float(wd(39)), __uint_as_float(wd(40)), __uint_as_float(wd(41)), __uint_as_float(wd(42))};
+  };
+  if constexpr (STREAM) {
+    set_qops();
   } else if (kProjAll || wave < 4) {  // uniform
     qprep_compute<T, T, true, true>(a, sm.q, qpr, tid, wave, tiles_all, Aq, scq, cinit, qinit);
   } else {
@@ -1744,15 +1862,62 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   const uint16_t *const nh = reinterpret_cast<const uint16_t *>(nrm);
   // the last key each of the lane's rows sees (causal over a verify block)
   int lim[T], low[T];
+  auto set_lims = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < T; ++u) {
-    const int hi = L - qlen + (4 * u + grow) / G + 1;
-    lim[u] = min(s1, hi);
-    low[u] = window_low(a, hi);
-  }
-  for (; k < ntiles; k += NW, ++slot) {  // uniform per wave
-    const int nslot = k + NW < ntiles ? slot + 1 : slot;
-    const int tok0 = s0 + 128 * k;
+    for (int u = 0; u < T; ++u) {
+      const int hi = L - qlen + (4 * u + grow) / G + 1;
+      lim[u] = min(s1, hi);
+      low[u] = window_low(a, hi);
+    }
+  };
+  set_lims();
+  const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
+  // stream plan: the wave's record of its current group (place iw + group)
+  auto write_record = [&]() __attribute__((always_inline)) {
+    // keep the matrix ops out of the per-head branch below
+    asm volatile("" : "+v"(corr[0]));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(tot[0][r]));
+    const float cs = (corr[0][0] + corr[0][1]) + (corr[0][2] + corr[0][3]);
+    const float ls = row_sum16(lsum[0]);
+    if (grow < nrows) {
+      float *part = a.partials + (((int64_t)iw + grp) * G + grow) * kPartStride;
+      if (t16 == 0) {
+        part[0] = R[0];
+        part[1] = ls;
+      }
+      float4 *o4 = reinterpret_cast<float4 *>(part + 4 + 8 * t16);
+      o4[0] = make_float4(tot[0][0] - bsum * cs, tot[0][1] - bsum * cs, tot[0][2] - bsum * cs, tot[0][3] - bsum * cs);
+      o4[1] = make_float4(tot[0][4] - bsum * cs, tot[0][5] - bsum * cs, tot[0][6] - bsum * cs, tot[0][7] - bsum * cs);
+    }
+  };
+  for (; k < ntiles; k += kStep, ++slot) {  // uniform per wave
+    const int nslot = k + kStep < ntiles ? slot + 1 : slot;
+    int tok0;
+    if constexpr (STREAM) {
+      const int4 si = slot_sh[wave][slot];
+      const int st = __builtin_amdgcn_readfirstlane(si.z);
+      if (slot > 0 && st == 0) {  // uniform: the wave's next group starts here
+        write_record();
+        b = __builtin_amdgcn_readfirstlane(si.x);
+        h = __builtin_amdgcn_readfirstlane(si.y);
+        L = __builtin_amdgcn_readfirstlane(si.w);
+        grp = (int64_t)b * a.num_kv_heads + h;
+        s0 = seq_base(a, L);
+        s1 = L;
+        load_qops();
+        set_qops();
+        set_lims();
+        R[0] = -INFINITY;
+        lsum[0] = 0.0f;
+        corr[0] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < 8; ++r) tot[0][r] = 0.0f;
+      }
+      tok0 = s0 + 128 * st;
+    } else {
+      tok0 = s0 + 128 * k;
+    }
     // ---- raw scores of the tile's 8 pages (log2 units) ------------------------
     // K page e: n_k at halves 32 e + t, gamma at 32 e + 16 + t; V page e: 256 + 16 e + t
     *reinterpret_cast<u32x4 *>(nrm + 4 * lane) = NR;
@@ -1889,9 +2054,12 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(tot[u][r]));
   }
 
+  if constexpr (STREAM) {
+    write_record();
+    return;
+  }
   // ---- the waves combine their records -----------------------------------------
   lds_barrier();  // every wave is done with its LDS region
-  const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
 #pragma unroll
   for (int u = 0; u < T; ++u) {
     const int hd = 4 * u + grow;
@@ -1929,57 +2097,17 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   }
 }
 
-// ---- 0. fused decode step: the append, the query operands and the plan -------
+// ---- 0. fused decode step: the append and the query operands ----------------
 // A decode step appends each sequence's new token and then attends over the
 // whole cache.  The append is a short, latency-bound launch; this one also
-// does the work of the split pass's prologue that depends only on the
-// context lengths and (sequence, KV head) and not on the range: workgroups
-// past the append's form one group's query operands each (the same code as
-// the split pass) and store them, and write the group's entries of the
-// balanced plan as a table, split workgroup w -> (sequence, KV head, range,
-// per); together they also mark the table's unused entries.  The split pass
-// then starts with one table entry and one operand load.
-// Workgroup w of a launch runs on accelerator die (XCD) w mod 8, each with
-// its own L2.  The ranges, numbered sequence-major r = 0 .. total - 1, go to
-// the dies in 8 contiguous runs (die x: ranges from ceil(x total / 8)), so
-// a group's ranges share one die and its L2 fetches the group's operands
-// once; range r of run x is workgroup 8 s + x, s its place in the run.  The
-// grid needs total + 7 workgroups.
-__device__ __forceinline__ int xcd_run_start(int x, int total) { return (x * total + 7) / 8; }
-__device__ __forceinline__ int xcd_slot(int r, int total) {
-  const int x = (8 * r) / total;
-  return 8 * (r - xcd_run_start(x, total)) + x;
-}
-__device__ __forceinline__ bool xcd_slot_used(int w, int total) {
-  const int x = w & 7;
-  return (w >> 3) < xcd_run_start(x + 1, total) - xcd_run_start(x, total);
-}
-
+// does the split pass's query set-up, which depends only on (sequence, KV
+// head): workgroups past the append's form one group's query operands each
+// (the same code as the split pass's prologue) and store them.  The split
+// pass (stream plan) then loads a group's operands where a wave starts on it.
 union StepLds {
   QPrepLds<1> q;
   float rsh[kAppendWaves][kHeadDim];
 };
-
-// First plan entry of sequence b's ranges (sequence-major, then KV head, then
-// range, as bal_locate numbers them), its range count kb and the number of
-// ranges of all groups; every lane returns the same values.
-__device__ __forceinline__ int bal_first(const DecodeArgs &a, int t0, int per, int b, int &kb, int &total) {
-  const int lane = threadIdx.x & 63, H = a.num_kv_heads;
-  int base = 0, first = 0;
-  kb = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
-    const int T = block_tiles(a, t0, c0, lane);
-    const int k = (T + per - 1) / per;
-    const int incl = wave_incl_scan_int(H * k, lane);
-    if (b >= c0 && b < c0 + 64) {  // uniform
-      kb = __builtin_amdgcn_readlane(k, b - c0);
-      first = base + __builtin_amdgcn_readlane(incl, b - c0) - H * kb;
-    }
-    base += __builtin_amdgcn_readlane(incl, 63);
-  }
-  total = base;
-  return first;
-}
 
 template <int DT>
 __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, DecodeArgs a, int n_append, int n_groups) {
@@ -1991,27 +2119,10 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t grp = wg - n_append;
-  // the context lengths first (the plan needs them), then the operands' inputs
-  const int t0s = seq_tiles(a, lane);
-  __builtin_amdgcn_sched_barrier(0);
   QPrepRegs<true> qpr;
   qprep_load_sh<true>(a, wave, lane, qpr);
   qprep_load_q<true>(a, grp, wave, lane, qpr);
   __builtin_amdgcn_sched_barrier(0);
-  if (wave == 3) {  // uniform: the group's plan entries, while the other loads are in flight
-    const int per = bal_per(a, t0s);
-    const int H = a.num_kv_heads, b = (int)(grp / H), h = (int)(grp % H);
-    int kb, total;
-    const int first = bal_first(a, t0s, per, b, kb, total) + h * kb;
-    int32_t *const table = const_cast<int32_t *>(a.prep_table);
-    for (int j = lane; j < kb; j += 64) {
-      const int w = xcd_slot(first + j, total);  // < bal_grid: the grid covers every range, plus 7
-      if (w < a.bal_grid) *reinterpret_cast<int4 *>(table + 4 * (int64_t)w) = make_int4(b, h, j, per);
-    }
-    // unused entries: group g looks at 64 g + lane, + 64 n_groups, ...
-    for (int64_t w = 64 * grp + lane; w < a.bal_grid; w += 64 * (int64_t)n_groups)
-      if (!xcd_slot_used((int)w, total)) *reinterpret_cast<int4 *>(table + 4 * w) = make_int4(-1, 0, 0, 0);
-  }
   v8i Aq[1][5];
   int scq[1][5];
   v4f ci[1], qi[1];
@@ -2040,13 +2151,14 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
 // ---- 3. merge ---------------------------------------------------------------
 // LSE combine of the chunk partials of an output row, o' = acc'/l, one
 // inverse FWHT, store.  W waves share a row (4/W rows per workgroup); wave w
-// of a row takes chunks 16w .. 16w+15, then 16(w+W) .., and issues every load
-// of a batch of 16 together, so up to 16W chunks cost one memory round trip.
-// Lane l owns coordinates l and l + 64, lane e < 16 the statistics of chunk e
-// of the batch.  The waves of a row then meet in LDS.
+// of a row takes chunks NB w .. NB w + NB - 1, then NB (w + W) .., and issues
+// every load of a batch of NB (16, or 32 for the stream plan's rows of up to
+// about a hundred records) together, so up to NB W chunks cost one memory
+// round trip.  Lane l owns coordinates l and l + 64, lane e < NB the
+// statistics of chunk e of the batch.  The waves of a row then meet in LDS.
 constexpr int kMergeBatch = 16;
 
-template <int W>
+template <int W, int NB = kMergeBatch>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave % W;
@@ -2055,32 +2167,47 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
   __shared__ float wa[4][kHeadDim];
   int ns = 0;
   const float *part = a.partials;
+  int64_t rstride = kPartStride;  // floats from one record of the row to the next
   if (r < rows) {
     const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
     const int b = (int)(r / per_seq);
     const int t = (int)((r / a.num_q_heads) % a.q_len);
-    if (a.balanced) {
-      const int per = bal_per(a, seq_tiles(a, lane));
-      ns = (seq_tiles(a, b) + per - 1) / per;
+    if (a.balanced == 2) {  // stream plan (q_len 1): the group's records are consecutive places
+      const int hq = (int)(r % a.num_q_heads), h = hq / a.group, hd = hq - h * a.group;
+      const int t0s = span_tiles(a, lane_context(a, lane));
+      const int q = stream_per(a, stream_total(a, t0s));
+      int P, Tb;
+      stream_prefix(a, t0s, b, P, Tb);
+      if (Tb > 0) {  // uniform
+        const int c0 = P + h * Tb, i0 = c0 / q;
+        ns = (c0 + Tb - 1) / q - i0 + 1;
+        part += (((int64_t)i0 + (int64_t)b * a.num_kv_heads + h) * a.group + hd) * kPartStride;
+        rstride = (int64_t)a.group * kPartStride;
+      }
     } else {
-      const int L = clamped_context(a, b);
-      const int vis = max(0, L - seq_base(a, L) - a.q_len + t + 1);
-      ns = (vis + a.split_tokens - 1) / a.split_tokens;
+      if (a.balanced) {
+        const int per = bal_per(a, seq_tiles(a, lane));
+        ns = (seq_tiles(a, b) + per - 1) / per;
+      } else {
+        const int L = clamped_context(a, b);
+        const int vis = max(0, L - seq_base(a, L) - a.q_len + t + 1);
+        ns = (vis + a.split_tokens - 1) / a.split_tokens;
+      }
+      ns += a.hot_parts;  // the window's records follow
+      part += r * a.part_stride * kPartStride;
     }
-    ns += a.hot_parts;  // the window's records follow
-    part += r * a.part_stride * kPartStride;
   }
   float M = -INFINITY, Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;  // Ls: lanes < 16, per chunk slot
-  for (int base = kMergeBatch * wr; base < ns; base += kMergeBatch * W) {  // uniform
-    float v0[kMergeBatch], v1[kMergeBatch];
+  for (int base = NB * wr; base < ns; base += NB * W) {  // uniform
+    float v0[NB], v1[NB];
 #pragma unroll
-    for (int e = 0; e < kMergeBatch; ++e) {
-      const float *p = part + (int64_t)min(base + e, ns - 1) * kPartStride;
+    for (int e = 0; e < NB; ++e) {
+      const float *p = part + (int64_t)min(base + e, ns - 1) * rstride;
       v0[e] = p[4 + lane];
       v1[e] = p[68 + lane];
     }
-    const bool live = lane < kMergeBatch && base + lane < ns;
-    const float *ps = part + (int64_t)min(base + (lane & (kMergeBatch - 1)), ns - 1) * kPartStride;
+    const bool live = lane < NB && base + lane < ns;
+    const float *ps = part + (int64_t)min(base + (lane & (NB - 1)), ns - 1) * rstride;
     const float m0 = ps[0], l = ps[1];  // unconditional loads
     const float m = live ? m0 : -INFINITY;
     const float mb = wave_max(m);
@@ -2094,7 +2221,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
     const float f = m == -INFINITY ? 0.0f : exp2f(m - M);
     Ls = fmaf(f, live ? l : 0.0f, Ls);
 #pragma unroll
-    for (int e = 0; e < kMergeBatch; ++e) {
+    for (int e = 0; e < NB; ++e) {
       const float fe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), e));  // 0 past ns
       A0 = fmaf(fe, v0[e], A0);
       A1 = fmaf(fe, v1[e], A1);
@@ -2221,10 +2348,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     la.pos0 = 0;
     la.pos_count = min(per, a.q_len);
     la.qk_tiles = (la.group * la.pos_count + 3) / 4;
-    if (pgroups == 1 && la.qk_tiles == 1) {
+    if (a.balanced == 2) {  // the fused decode step's pass (stream plan)
+      if (pgroups != 1 || la.qk_tiles != 1 || a.hot_parts > 0 || !a.qops) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((split_wave_kernel<1, true>), dim3((unsigned)items), dim3(256), 0, stream, la);
+    } else if (pgroups == 1 && la.qk_tiles == 1) {
       // the exact window's chunks ride in the same launch (q_len 1)
       const int64_t hot_items = a.hot_parts > 0 ? (int64_t)a.num_seqs * a.num_kv_heads * a.hot_parts : 0;
-      hipLaunchKernelGGL(split_wave_kernel<1>, dim3((unsigned)(items + hot_items)), dim3(256), 0, stream, la);
+      hipLaunchKernelGGL((split_wave_kernel<1, false>), dim3((unsigned)(items + hot_items)), dim3(256), 0, stream, la);
     } else if (la.qk_tiles == 2) {
       hipLaunchKernelGGL(split_mfma_kernel<2>, dim3((unsigned)(items * pgroups)), dim3(512), 0, stream, la);
     } else {
@@ -2258,7 +2388,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   // four waves per row when there are more records than one batch
-  if (a.part_stride > kMergeBatch)
+  if (a.balanced == 2)
+    hipLaunchKernelGGL((merge_kernel<4, 32>), dim3((unsigned)rows), dim3(256), 0, stream, a, rows);
+  else if (a.part_stride > kMergeBatch)
     hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, a, rows);
   else
     hipLaunchKernelGGL(merge_kernel<1>, dim3(row_blocks), dim3(256), 0, stream, a, rows);

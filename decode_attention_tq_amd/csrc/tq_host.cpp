@@ -426,20 +426,36 @@ int walk_span(int max_context_len, int q_len, int window) {
   return (int)std::min<int64_t>(max_context_len, (int64_t)window + q_len - 1 + (tq::kBlock - 1));
 }
 
-// The fused decode step (append, query operands and plan in one launch, then
-// the one-tile-per-wave split pass reading them) serves 3-bit codes with up
-// to 4 query heads per KV head and appends of at most kAppendMaxVectors
-// vectors; other steps run the encode and the decode launches in turn.
+// The fused decode step (append and query operands in one launch, then the
+// split pass on the stream plan reading them, then the merge) serves 3-bit
+// codes with up to 4 query heads per KV head and appends of at most
+// kAppendMaxVectors vectors; other steps run the encode and the decode
+// launches in turn.
 bool step_fused(int bits, int q_len, int group, int num_seqs, int num_kv_heads, int64_t num_tokens) {
   return bits == 3 && q_len == 1 && group >= 1 && group <= 4 && tq::decode_uses_mfma(1, group, bits) &&
          num_tokens * num_kv_heads <= tq::kAppendMaxVectors && (int64_t)num_seqs * num_kv_heads <= 0x7fffffffLL;
 }
-// The fused step's split grid: the plan's, plus 7 workgroups (its table
-// places the ranges in one run per accelerator die, the last runs padded).
-int step_grid(int grid) { return grid + 7; }
-// Its workspace beyond the partial records: the groups' operands and the plan table.
-size_t step_extra_bytes(int num_seqs, int num_kv_heads, int grid) {
-  return (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64 * sizeof(uint32_t) + (size_t)grid * 16;
+// The fused step's split pass runs the stream plan: the tiles of all groups in
+// one order, q = ceil(N / (4 kStreamTarget)) consecutive tiles per wave
+// (1 <= q <= 16, so at most max(4 kStreamTarget, N / 16) waves, 4 per
+// workgroup), the workgroups in one run per accelerator die (7 more cover
+// the runs' rounding).  Each wave writes a record per group it touches, at
+// place (wave + group): fewer than waves + groups places of G rows.
+constexpr int kStreamTarget = 512;  // workgroups that fill the compute units once
+int64_t stream_waves(int num_seqs, int num_kv_heads, int span) {
+  const int64_t N = (int64_t)num_seqs * num_kv_heads * ((std::max(span, 0) + 127) / 128);
+  return std::max<int64_t>(4 * kStreamTarget, (N + 15) / 16);
+}
+int stream_grid(int num_seqs, int num_kv_heads, int span) {
+  return (int)((stream_waves(num_seqs, num_kv_heads, span) + 3) / 4) + 7;
+}
+size_t stream_record_floats(int num_seqs, int group, int num_kv_heads, int span) {
+  return (size_t)(stream_waves(num_seqs, num_kv_heads, span) + (int64_t)num_seqs * num_kv_heads) * group * kPartStride;
+}
+// The fused step's workspace: the records, then the groups' query operands.
+size_t step_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int span) {
+  return stream_record_floats(num_seqs, num_q_heads / num_kv_heads, num_kv_heads, span) * sizeof(float) +
+         (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64 * sizeof(uint32_t);
 }
 
 size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
@@ -532,10 +548,10 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     hot_parts = tq::decode_hot_parts(hot->max);
     if (ns + hot_parts > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many partial records per row");
   }
-  size_t need = decode_workspace(bits, num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
-                                 tokens_per_split, hot_parts, window);
   const bool fused = step && step_fused(bits, q_len, group, num_seqs, num_kv_heads, step->num_tokens);
-  if (fused) need += step_extra_bytes(num_seqs, num_kv_heads, step_grid(plan.grid));
+  const size_t need = fused ? step_workspace(num_seqs, num_q_heads, num_kv_heads, span)
+                            : decode_workspace(bits, num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
+                                               tokens_per_split, hot_parts, window);
   if (noalloc) {
     // every check above is on the host; the scratch array's address is
     // resolved (once per device) only for a call that will launch
@@ -604,14 +620,15 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.hot_lens = hot ? hot->lens : nullptr;
   a.hot_max = hot ? hot->max : 0;
   a.cb = device_codebook(cb);
-  a.prep_table = nullptr;
   a.qops = nullptr;
   hipError_t e;
   if (fused) {
-    a.bal_grid = step_grid(plan.grid);
-    // the step's extra workspace follows the partial records (16-byte aligned)
-    a.qops = reinterpret_cast<uint32_t *>(rest + tq::decode_partial_floats(rows, ns + hot_parts));
-    a.prep_table = reinterpret_cast<const int32_t *>(a.qops + (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64);
+    // stream plan: the records, then the operands (16-byte aligned: records of 528 bytes)
+    a.balanced = 2;
+    a.bal_target = kStreamTarget;
+    a.bal_grid = stream_grid(num_seqs, num_kv_heads, span);
+    a.partials = (float *)workspace;
+    a.qops = reinterpret_cast<uint32_t *>(a.partials + stream_record_floats(num_seqs, group, num_kv_heads, span));
     e = tq::launch_step_prep(*step, a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode step launch");
   } else if (step) {
@@ -696,13 +713,12 @@ size_t tq_decode_hot_workspace_bytes(const tq_codebook *cb, int num_seqs, int nu
 size_t tq_decode_step_workspace_bytes(const tq_codebook *cb, int num_seqs, int num_q_heads, int num_kv_heads,
                                       int max_context_len, int tokens_per_split) {
   const int bits = cb_bits(cb);
-  size_t need = decode_workspace(bits, num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0);
+  const size_t need =
+      decode_workspace(bits, num_seqs, 1, num_q_heads, num_kv_heads, max_context_len, tokens_per_split, 0);
   if (need == 0 || num_q_heads % num_kv_heads != 0) return need;
   const int group = num_q_heads / num_kv_heads;
   if (step_fused(bits, 1, group, num_seqs, num_kv_heads, num_seqs))
-    need += step_extra_bytes(
-        num_seqs, num_kv_heads,
-        step_grid(plan_splits(num_seqs, 1, num_kv_heads, group, max_context_len, tokens_per_split, bits).grid));
+    return step_workspace(num_seqs, num_q_heads, num_kv_heads, max_context_len);
   return need;
 }
 

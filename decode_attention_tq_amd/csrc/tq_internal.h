@@ -125,11 +125,11 @@ struct DecodeArgs {
   int hot_dtype;
   const int32_t *hot_lens;  // [num_seqs], cut to [0, hot_max]
   int hot_max;
-  // The fused decode step's precomputed plan and query operands (null
-  // otherwise): entry w of prep_table is (sequence, KV head, range, per) of
-  // split workgroup w (sequence -1: no range); qops holds each (sequence, KV
-  // head) group's matrix operands, kQopsDwords per lane.
-  const int32_t *prep_table;
+  // The fused decode step (balanced = 2, the stream plan: the tiles of all
+  // groups in one order, an equal share per wave, one record per (wave,
+  // group) at place wave + group, G rows each; partials then hold those
+  // places): qops holds each (sequence, KV head) group's matrix operands,
+  // kQopsDwords per lane (null otherwise).
   uint32_t *qops;
   Codebook cb;
 };
@@ -168,8 +168,8 @@ hipError_t noalloc_scratch(void **ptr);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
-// The fused decode step's append + query operands + plan launch (3-bit codes,
-// a precomputed-operand split pass: up to 4 query heads per KV head, q_len 1).
+// The fused decode step's append + query operands launch (3-bit codes, up to
+// 4 query heads per KV head, q_len 1; the split pass then runs the stream plan).
 hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);
 

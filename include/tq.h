@@ -304,11 +304,15 @@ tq_status tq_decode_attention_window(const tq_codebook *cb, const void *q, tq_dt
  *                tok_stride, head_stride, slot_mapping, k_cache, v_cache,
  *                NULL, stream)
  * followed by tq_decode_attention(..., q_len = 1, ...) with the remaining
- * arguments, on `stream`, and gives bit-identical cache contents and output.
- * With 3-bit codes, up to 4 query heads per KV head and at most 1,024 new
- * (token, KV head) vectors, it runs as two launches instead of four: the
- * append shares its launch with the attention's per-(sequence, KV head)
- * query set-up and its split plan; otherwise it runs the two calls' launches.
+ * arguments, on `stream`: the cache contents are bit-identical to those two
+ * calls'.  With 3-bit codes, up to 4 query heads per KV head and at most
+ * 1,024 new (token, KV head) vectors it runs fused, in three launches
+ * instead of four: the append shares its launch with the attention's
+ * per-(sequence, KV head) query set-up, and the split pass gives every wave
+ * an equal share of all the batch's tiles (tokens_per_split is not used);
+ * the output then equals the two calls' up to fp32 rounding (the softmax is
+ * combined from other partial records).  Otherwise it runs the two calls'
+ * launches and the output is bit-identical.
  *   k_new, v_new  device, element (b, h, i) of sequence b's new token at
  *               k_new[b*tok_stride + h*head_stride + i], as in tq_encode_kv.
  *   slot_mapping device int64[num_seqs]: the slot of sequence b's new token

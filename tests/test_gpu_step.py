@@ -2,10 +2,14 @@
 against the two calls it stands for, and against the oracle.
 
 tq_decode_step is tq_encode_kv of one token per sequence followed by
-tq_decode_attention with q_len 1: the cache pools and the output must be
-bit-identical to those two calls' on the same inputs, whether the step runs
-fused (3-bit codes, up to 4 query heads per KV head) or as the two calls'
-own launches.  The oracle then checks the step's output on sampled heads."""
+tq_decode_attention with q_len 1.  The cache pools must be bit-identical to
+those two calls' on the same inputs.  Fused (3-bit codes, up to 4 query heads
+per KV head) the step splits each row's keys into other partial records than
+the attention call (an equal share of all tiles per wave), so its output may
+differ from the call's in the last bits of fp32: within 2e-5 of the row's
+largest element (one bf16 step for a bf16 output); unfused it runs the two
+calls' own launches and is bit-identical.  The oracle then checks the step's
+output on sampled heads."""
 import numpy as np
 import pytest
 import torch
@@ -28,6 +32,19 @@ def _setup(seed, B, Hq, Hkv, bits=3, lo=512, hi=32768, steps=2, lengths=None):
 def _two_calls(cb, kn, vn, slots, q, kpool, vpool, bt, cl, maxc, Hkv):
     tq.tq_encode_kv(cb, kn, vn, slots, kpool, vpool)
     return tq.tq_decode_attention(cb, q, kpool, vpool, bt, cl, maxc, Hkv)
+
+
+def _same_output(out, ref, fused):
+    """Bit-identical unfused; fused, within 2e-5 of each row's largest
+    magnitude (fp32 rounding of another split), or one step of a bf16 output."""
+    if not fused:
+        assert torch.equal(out, ref), f"outputs differ: max {float((out.float() - ref.float()).abs().max()):.3e}"
+        return
+    o, r = out.float(), ref.float()
+    rel = 2e-5 if out.dtype == torch.float32 else 2.0 ** -7
+    scale = r.abs().amax(dim=-1, keepdim=True)
+    err = (o - r).abs()
+    assert bool(torch.all(err <= rel * scale)), f"max err / row scale {float((err / scale.clamp_min(1e-30)).max()):.3e}"
 
 
 @pytest.mark.parametrize("Hq,Hkv,bits", [(32, 8, 3), (8, 8, 3), (16, 8, 3), (64, 8, 3), (32, 8, 2)])
@@ -63,7 +80,7 @@ def test_step_is_append_then_decode(Hq, Hkv, bits):
         print(f"Hq {Hq} Hkv {Hkv} bits {bits} step {s}", flush=True)
         assert torch.equal(kpool, ka), "K pools differ"
         assert torch.equal(vpool, va), "V pools differ"
-        assert torch.equal(out, ref), f"outputs differ: max {float((out - ref).abs().max()):.3e}"
+        _same_output(out, ref, fused=bits == 3 and Hq // Hkv <= 4)
     if bits == 3:
         kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
         check_decode(out.cpu().numpy(), case["q"][1], kp, vp, case["table"], L, tables=oracle_tables(bits=bits),
@@ -92,7 +109,7 @@ def test_step_fp32_and_f16_inputs_and_outputs():
     out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(kpool, ka) and torch.equal(vpool, va)
-    assert torch.equal(out, ref)
+    _same_output(out, ref, fused=True)
 
 
 def test_step_short_and_empty_sequences():
@@ -115,7 +132,7 @@ def test_step_short_and_empty_sequences():
     out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc)
     torch.cuda.synchronize()
     assert torch.equal(kpool, ka) and torch.equal(vpool, va)
-    assert torch.equal(out, ref)
+    _same_output(out, ref, fused=True)
     o = out.cpu().numpy()
     assert not np.any(o[3])                      # no key at all: zero output
     check_decode(o, case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L)
@@ -139,7 +156,7 @@ def test_step_decode_batch_full_size_sampled():
     out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc)
     torch.cuda.synchronize()
     assert torch.equal(kpool, ka) and torch.equal(vpool, va)
-    assert torch.equal(out, ref)
+    _same_output(out, ref, fused=True)
     check_decode(out.cpu().numpy(), case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
                  kv_heads=[2])
 
@@ -167,6 +184,6 @@ def test_step_more_than_64_sequences_and_large_appends():
         torch.cuda.synchronize()
         print(f"B {B}: step done", flush=True)
         assert torch.equal(kpool, ka) and torch.equal(vpool, va)
-        assert torch.equal(out, ref), f"outputs differ: max {float((out - ref).abs().max()):.3e}"
+        _same_output(out, ref, fused=B * Hkv <= 1024)
         check_decode(out.cpu().numpy(), case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
                      kv_heads=[1, 6])

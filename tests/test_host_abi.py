@@ -428,15 +428,19 @@ def test_step_validation():
 @pytest.mark.parametrize("bits,Hq,Hkv,fused", [(3, 32, 8, True), (3, 8, 8, True), (3, 16, 8, True),
                                                 (3, 64, 8, False), (2, 32, 8, False), (4, 32, 8, False)])
 def test_step_workspace(bits, Hq, Hkv, fused):
-    """The fused step needs the attention call's partial records plus each
+    """The fused step's split pass runs the stream plan: 16 sequences of up
+    to 32,768 tokens x Hkv KV heads are at most 16 x Hkv x 256 tiles, so at
+    most max(2,048, tiles / 16) waves; it needs one record (132 floats) per
+    query head of the group at each of waves + groups places, then each
     (sequence, KV head) group's query operands (44 words per lane of a
-    64-lane wave) and a 16-byte plan entry per workgroup of the split grid
-    (512 for 16 sequences of up to 32,768 tokens, plus 7 for the runs of
-    ranges per accelerator die); an unfused step needs the attention call's
-    workspace only."""
+    64-lane wave).  An unfused step needs the attention call's workspace."""
     cb = ctypes.byref(_fake_cb(bits=bits))
     B, ctx = 16, 32768
     dec = tq._lib.tq_decode_workspace_bytes(cb, B, 1, Hq, Hkv, ctx, 0)
     step = tq._lib.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, ctx, 0)
-    extra = B * Hkv * 44 * 64 * 4 + (512 + 7) * 16 if fused else 0
-    assert step == dec + extra
+    if fused:
+        G = Hq // Hkv
+        waves = max(2048, -(-(B * Hkv * 256) // 16))
+        assert step == (waves + B * Hkv) * G * 132 * 4 + B * Hkv * 44 * 64 * 4
+    else:
+        assert step == dec
