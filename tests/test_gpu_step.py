@@ -187,3 +187,32 @@ def test_step_more_than_64_sequences_and_large_appends():
         _same_output(out, ref, fused=B * Hkv <= 1024)
         check_decode(out.cpu().numpy(), case["q"][0], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
                      kv_heads=[1, 6])
+
+
+def test_step_eight_consecutive_steps_one_workspace():
+    """Eight fused steps in a row with one workspace (uninitialised at the
+    first call), new queries every step: after every step the pools are
+    bit-identical to the separate calls' and the output within rounding of
+    theirs; the oracle checks the last step."""
+    B, Hq, Hkv, S = 16, 32, 8, 8
+    case, cb, kpool, vpool = _setup(61, B, Hq, Hkv, hi=6000, steps=S)
+    ka, va = kpool.clone(), vpool.clone()
+    bt = torch.from_numpy(case["table"].astype(np.int32)).cuda()
+    L = case["lengths"].copy()
+    ws = torch.empty(tq.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, int(L.max()) + S), dtype=torch.uint8,
+                     device="cuda")
+    for s in range(S):
+        L = L + 1
+        cl = torch.from_numpy(L.astype(np.int32)).cuda()
+        maxc = int(L.max())
+        kn, vn = dev(case["new_k"][s], torch.bfloat16), dev(case["new_v"][s], torch.bfloat16)
+        st = torch.from_numpy(case["new_slots"][s].copy()).cuda()
+        q = dev(case["q"][s], torch.bfloat16)
+        ref = _two_calls(cb, kn, vn, st, q, ka, va, bt, cl, maxc, Hkv)
+        out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"step {s} done", flush=True)
+        assert torch.equal(kpool, ka) and torch.equal(vpool, va), f"pools differ after step {s}"
+        _same_output(out, ref, fused=True)
+    check_decode(out.cpu().numpy(), case["q"][S - 1], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
+                 kv_heads=[0, 5])
