@@ -216,3 +216,60 @@ def test_step_eight_consecutive_steps_one_workspace():
         _same_output(out, ref, fused=True)
     check_decode(out.cpu().numpy(), case["q"][S - 1], kpool.cpu().numpy(), vpool.cpu().numpy(), case["table"], L,
                  kv_heads=[0, 5])
+
+
+def _device_cache_case(seed, lengths, Hq=32, Hkv=8):
+    """Pools holding ``lengths`` cached tokens per sequence, drawn on the
+    device with the GQA recipe (synth.kv_tensor_device) and encoded; room
+    for one more token each; new tokens and queries for one step.  The
+    oracle checks read the encoded pages, so the raw cache stays on the
+    device."""
+    rng = np.random.default_rng(seed)
+    L = np.asarray(lengths, np.int64)
+    B = len(L)
+    table, nb = synth.block_tables(rng, L + 1)
+    cb = codebook()
+    kpool, vpool = new_pools(nb, Hkv, seed=seed)
+    slots = np.concatenate([synth.slots_for(table, b, np.arange(L[b])) for b in range(B)])
+    kt = synth.kv_tensor_device(seed, len(slots), Hkv, "cuda")
+    vt = synth.kv_tensor_device(seed + 1, len(slots), Hkv, "cuda")
+    tq.tq_encode_kv(cb, kt, vt, torch.from_numpy(slots).cuda(), kpool, vpool)
+    del kt, vt
+    new_slots = np.array([synth.slots_for(table, b, [L[b]])[0] for b in range(B)], np.int64)
+    kn = synth.kv_tensor_device(seed + 2, B, Hkv, "cuda")
+    vn = synth.kv_tensor_device(seed + 3, B, Hkv, "cuda")
+    q = rng.standard_normal((B, 1, Hq, 128)).astype(np.float32)
+    return cb, kpool, vpool, table, L + 1, new_slots, kn, vn, q
+
+
+@pytest.mark.parametrize("name,lengths", [
+    ("64 sequences of one tile", [1 + 2 * b for b in range(64)]),
+    ("two long sequences", [131071, 99999]),
+    ("more tiles than one round of waves", [40000] * 8 + [30000] * 8),
+])
+def test_step_stream_plan_extremes(name, lengths):
+    """The step's split plan at its ends: 64 one-tile sequences (one tile
+    per wave, one wave per group); two sequences of 131,072 and 100,000
+    tokens (8 tiles per wave, a group spread over hundreds of waves); 16
+    sequences of 30,000-40,000 tokens, 35,072 tiles (16 tiles per wave, more
+    workgroups than run at once).  Pools bit-identical to the separate
+    calls, outputs within rounding of theirs, the oracle on sampled
+    sequences and KV heads."""
+    Hq, Hkv = 32, 8
+    cb, kpool, vpool, table, L, new_slots, kn, vn, qn = _device_cache_case(71 + len(lengths), lengths, Hq, Hkv)
+    ka, va = kpool.clone(), vpool.clone()
+    bt = torch.from_numpy(table.astype(np.int32)).cuda()
+    cl = torch.from_numpy(L.astype(np.int32)).cuda()
+    maxc = int(L.max())
+    st = torch.from_numpy(new_slots).cuda()
+    q = dev(qn, torch.bfloat16)
+    ref = _two_calls(cb, kn, vn, st, q, ka, va, bt, cl, maxc, Hkv)
+    out = tq.tq_decode_step(cb, kn, vn, st, q, kpool, vpool, bt, cl, maxc)
+    torch.cuda.synchronize()
+    print(f"{name}: step done", flush=True)
+    assert torch.equal(kpool, ka) and torch.equal(vpool, va)
+    _same_output(out, ref, fused=True)
+    kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
+    q64 = q.float().cpu().numpy()
+    seqs = [0, len(L) - 1]
+    check_decode(out.cpu().numpy(), q64, kp, vp, table, L, seqs=seqs, kv_heads=[1, Hkv - 2])
