@@ -675,12 +675,13 @@ __device__ __forceinline__ void qprep_load_sh(const DecodeArgs &a, int wave, int
     for (int e = 0; e < 16; ++e) R.sh[e] = shop[e * 64];
   }
 }
-// The query words alone.
+// The query words alone (hbase: the first query row of the wave's head tile).
 template <bool PROJ>
-__device__ __forceinline__ void qprep_load_q(const DecodeArgs &a, int64_t grp, int wave, int lane, QPrepRegs<PROJ> &R) {
+__device__ __forceinline__ void qprep_load_q(const DecodeArgs &a, int64_t grp, int wave, int lane, QPrepRegs<PROJ> &R,
+                                             int hbase = 0) {
   const int rows = a.group * a.pos_count;
   const bool f32 = a.q_dtype == TQ_F32;
-  const int64_t row = query_out_row(a, grp, min(wave, rows - 1));
+  const int64_t row = query_out_row(a, grp, min(hbase + wave, rows - 1));
   const uint32_t *base = static_cast<const uint32_t *>(a.q);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -708,12 +709,15 @@ __device__ __forceinline__ void qprep_loads(const DecodeArgs &a, int64_t grp, in
 
 // The operands, for the head tiles NU the calling wave scores (every wave of
 // the workgroup runs this; it ends on a barrier after which the scratch space
-// may be reused).  Wave w rotates and digitises head w.
+// may be reused).  Wave w rotates and digitises head w of the workgroup's
+// heads, which start at query row hbase of the group (a head tile of its own
+// when a separate launch forms one tile's operands).
 template <int T, int NU, bool PACK, bool PROJ>
 __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &L, const QPrepRegs<PROJ> &R, int tid,
                                               int wave, const int (&tiles)[NU], v8i (&Aq)[NU][5],
-                                              int (&scq)[NU][5], v4f (&cinit)[NU], v4f (&qinit)[NU]) {
-  const int lane = tid & 63, rows = a.group * a.pos_count;
+                                              int (&scq)[NU][5], v4f (&cinit)[NU], v4f (&qinit)[NU],
+                                              int hbase = 0) {
+  const int lane = tid & 63, rows = a.group * a.pos_count - hbase;
   float x[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -1550,11 +1554,16 @@ __device__ __forceinline__ int xcd_run_start(int x, int total) { return (x * tot
 // + h T_b, N tiles in all).  Wave i of the split pass takes the q tiles from
 // i q, q = ceil(N / (4 bal_target)) within [1, kStreamMaxTiles]: every wave
 // has the same work whatever the lengths (a plan of whole ranges per group
-// leaves some compute units with a third more tiles than the mean).  A wave
-// whose tiles span groups writes one partial record per group it touches:
-// the record of (wave i, group g) sits at place i + g, and group g's records
-// are the consecutive places from floor(C_g / q) + g to floor((C_g + T_g - 1)
-// / q) + g.  Waves are numbered along the dies' runs (4 per workgroup), so a
+// leaves some compute units with a third more tiles than the mean).  With 5
+// to 8 query heads per KV head (two head tiles) the waves go in pairs: waves
+// 2 i and 2 i + 1 take the same run i of q tiles (q = ceil(2 N / (4
+// bal_target))), one head tile each, side by side in one workgroup, so the
+// second wave's page loads find the first's lines in the caches and HBM
+// serves each page once.  A run whose tiles span groups writes one partial
+// record per group it touches: the record of (run i, group g) sits at place
+// i + g (rows 4 u .. 4 u + 3 from head tile u), and group g's records are the
+// consecutive places from floor(C_g / q) + g to floor((C_g + T_g - 1) / q) +
+// g.  Waves are numbered along the dies' runs (4 per workgroup), so a
 // group's waves share one die.
 constexpr int kStreamMaxTiles = 16;
 __device__ __forceinline__ int lane_context(const DecodeArgs &a, int s) {
@@ -1572,9 +1581,11 @@ __device__ __forceinline__ int stream_total(const DecodeArgs &a, int t0) {
     tot += __builtin_amdgcn_readlane(wave_incl_scan_int(stream_block_tiles(a, t0, c0, lane), lane), 63);
   return tot * a.num_kv_heads;
 }
+// waves per run of tiles: one per head tile
+__device__ __forceinline__ int stream_pair(const DecodeArgs &a) { return a.group > 4 ? 2 : 1; }
 __device__ __forceinline__ int stream_per(const DecodeArgs &a, int N) {
-  const int waves = 4 * a.bal_target;
-  return min(max((N + waves - 1) / waves, 1), kStreamMaxTiles);
+  const int64_t waves = 4 * a.bal_target;
+  return (int)min<int64_t>(max<int64_t>(((int64_t)stream_pair(a) * N + waves - 1) / waves, 1), kStreamMaxTiles);
 }
 // Per lane: sequence b, KV head h and tile t of global tile c (0 <= c < N)
 // and the sequence's context length L.  Every lane of the wave takes part.
@@ -1679,7 +1690,8 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   // the range (ranges plan) or the wave's current group (stream plan): its
   // sequence b, KV head h, keys [s0, s1) and the sequence's length L
   int b, h, L, s0, s1, ntiles, jr = 0;
-  int iw = 0;  // stream plan: the wave's place in the order
+  int iw = 0;  // stream plan: the wave's run of tiles in the order
+  int ut = 0;  // stream plan: the wave's head tile (query rows 4 ut .. 4 ut + 3 of the group)
   // block ids of this wave's tile slots (at most 16) as (block id) x (KV
   // heads) + KV head: lane l holds page l % 8 of slot l / 8 (ids0) and of
   // slot 8 + l / 8 (ids1); a page past the keys re-reads its tile's first
@@ -1691,10 +1703,12 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     const int t0s = span_tiles(a, Lw);
     const int N = stream_total(a, t0s);
     const int q = stream_per(a, N);
-    const int nwg = ((N + q - 1) / q + 3) >> 2;
+    const int P = stream_pair(a);
+    const int nwg = (P * ((N + q - 1) / q) + 3) >> 2;
     const int x = (int)blockIdx.x & 7, rpos = xcd_run_start(x, nwg) + ((int)blockIdx.x >> 3);
     if (rpos >= xcd_run_start(x + 1, nwg)) return;  // uniform: no waves in this workgroup
-    iw = 4 * rpos + wave;
+    iw = (4 * rpos + wave) / P;
+    ut = (4 * rpos + wave) - iw * P;
     ntiles = min(q, N - iw * q);
     if (ntiles <= 0) return;  // uniform: past the last tile (this plan has no workgroup barrier)
     const int e = lane & 7;
@@ -1744,6 +1758,7 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     ids1 = btab[page_entry(a, (tok < s1 ? tok : tile0) >> 4)] * a.num_kv_heads + h;
   }
   int64_t grp = (int64_t)b * a.num_kv_heads + h;
+  const int pair = STREAM ? stream_pair(a) : 1;
   auto page_id = [&](int slot, int e) __attribute__((always_inline)) {
     const int src = slot < 8 ? ids0 : ids1;
     return __builtin_amdgcn_readlane(src, 8 * (slot & 7) + e);
@@ -1752,7 +1767,7 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   // the precomputed operands (stream plan): kQopsDwords per lane as 16-byte pieces
   u32x4 qo[kQopsDwords / 4];
   auto load_qops = [&]() __attribute__((always_inline)) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.qops) + grp * (kQopsDwords / 4) * 64 + lane;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.qops) + (grp * pair + ut) * (kQopsDwords / 4) * 64 + lane;
 #pragma unroll
     for (int c = 0; c < kQopsDwords / 4; ++c) qo[c] = src[c * 64];
   };
@@ -1865,14 +1880,15 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   auto set_lims = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < T; ++u) {
-      const int hi = L - qlen + (4 * u + grow) / G + 1;
+      const int hi = L - qlen + (4 * (u + ut) + grow) / G + 1;
       lim[u] = min(s1, hi);
       low[u] = window_low(a, hi);
     }
   };
   set_lims();
   const float bsum = (beta[0] + beta[1]) + (beta[2] + beta[3]);
-  // stream plan: the wave's record of its current group (place iw + group)
+  // stream plan: the wave's record of its current group (place iw + group,
+  // the rows of its head tile)
   auto write_record = [&]() __attribute__((always_inline)) {
     // keep the matrix ops out of the per-head branch below
     asm volatile("" : "+v"(corr[0]));
@@ -1880,8 +1896,8 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(tot[0][r]));
     const float cs = (corr[0][0] + corr[0][1]) + (corr[0][2] + corr[0][3]);
     const float ls = row_sum16(lsum[0]);
-    if (grow < nrows) {
-      float *part = a.partials + (((int64_t)iw + grp) * G + grow) * kPartStride;
+    if (4 * ut + grow < nrows) {
+      float *part = a.partials + (((int64_t)iw + grp) * G + 4 * ut + grow) * kPartStride;
       if (t16 == 0) {
         part[0] = R[0];
         part[1] = ls;
@@ -2110,7 +2126,7 @@ union StepLds {
 };
 
 template <int DT>
-__global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, DecodeArgs a, int n_append, int n_groups) {
+__global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, DecodeArgs a, int n_append, int n_items) {
   __shared__ __align__(16) StepLds sm;
   const int wg = blockIdx.x;
   if (wg < n_append) {  // uniform
@@ -2118,16 +2134,21 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t grp = wg - n_append;
+  // item: (group, head tile), the stream plan's pair factor of them per group
+  const int64_t item = wg - n_append;
+  if (item >= n_items) return;  // uniform
+  const int P = stream_pair(a);
+  const int64_t grp = item / P;
+  const int hbase = 4 * (int)(item - grp * P);
   QPrepRegs<true> qpr;
   qprep_load_sh<true>(a, wave, lane, qpr);
-  qprep_load_q<true>(a, grp, wave, lane, qpr);
+  qprep_load_q<true>(a, grp, wave, lane, qpr, hbase);
   __builtin_amdgcn_sched_barrier(0);
   v8i Aq[1][5];
   int scq[1][5];
   v4f ci[1], qi[1];
   const int tiles[1] = {0};
-  qprep_compute<1, 1, true, true>(a, sm.q, qpr, tid, wave, tiles, Aq, scq, ci, qi);
+  qprep_compute<1, 1, true, true>(a, sm.q, qpr, tid, wave, tiles, Aq, scq, ci, qi, hbase);
   if (wave == 0) {
     uint32_t w[kQopsDwords];
 #pragma unroll
@@ -2142,7 +2163,7 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
       w[39 + i] = __float_as_uint(qi[0][i]);
     }
     w[43] = 0u;
-    u32x4 *dst = reinterpret_cast<u32x4 *>(a.qops) + grp * (kQopsDwords / 4) * 64 + lane;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.qops) + item * (kQopsDwords / 4) * 64 + lane;
 #pragma unroll
     for (int c = 0; c < kQopsDwords / 4; ++c) dst[c * 64] = u32x4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]};
   }
@@ -2321,12 +2342,13 @@ static int group_capacity(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 :
 hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream_t stream) {
   const int64_t vectors = ea.num_tokens * ea.num_kv_heads;
   const int n_append = (int)((vectors + kAppendWaves - 1) / kAppendWaves);
-  const int n_groups = a.num_seqs * a.num_kv_heads;
-  const dim3 grid((unsigned)(n_append + n_groups));
+  // one operands workgroup per (group, head tile)
+  const int n_items = a.num_seqs * a.num_kv_heads * (a.group > 4 ? 2 : 1);
+  const dim3 grid((unsigned)(n_append + n_items));
   switch (ea.dtype) {
-    case TQ_BF16: hipLaunchKernelGGL(step_prep_kernel<TQ_BF16>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
-    case TQ_F16: hipLaunchKernelGGL(step_prep_kernel<TQ_F16>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
-    case TQ_F32: hipLaunchKernelGGL(step_prep_kernel<TQ_F32>, grid, dim3(256), 0, stream, ea, a, n_append, n_groups); break;
+    case TQ_BF16: hipLaunchKernelGGL(step_prep_kernel<TQ_BF16>, grid, dim3(256), 0, stream, ea, a, n_append, n_items); break;
+    case TQ_F16: hipLaunchKernelGGL(step_prep_kernel<TQ_F16>, grid, dim3(256), 0, stream, ea, a, n_append, n_items); break;
+    case TQ_F32: hipLaunchKernelGGL(step_prep_kernel<TQ_F32>, grid, dim3(256), 0, stream, ea, a, n_append, n_items); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2349,7 +2371,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     la.pos_count = min(per, a.q_len);
     la.qk_tiles = (la.group * la.pos_count + 3) / 4;
     if (a.balanced == 2) {  // the fused decode step's pass (stream plan)
-      if (pgroups != 1 || la.qk_tiles != 1 || a.hot_parts > 0 || !a.qops) return hipErrorInvalidValue;
+      if (pgroups != 1 || la.qk_tiles < 1 || la.qk_tiles > 2 || a.hot_parts > 0 || !a.qops) return hipErrorInvalidValue;
       hipLaunchKernelGGL((split_wave_kernel<1, true>), dim3((unsigned)items), dim3(256), 0, stream, la);
     } else if (pgroups == 1 && la.qk_tiles == 1) {
       // the exact window's chunks ride in the same launch (q_len 1)

@@ -428,34 +428,40 @@ int walk_span(int max_context_len, int q_len, int window) {
 
 // The fused decode step (append and query operands in one launch, then the
 // split pass on the stream plan reading them, then the merge) serves 3-bit
-// codes with up to 4 query heads per KV head and appends of at most
+// codes with up to 8 query heads per KV head and appends of at most
 // kAppendMaxVectors vectors; other steps run the encode and the decode
-// launches in turn.
+// launches in turn.  (A plain attention call keeps its own plan: without an
+// append to share it with, the operands' launch costs more than the stream
+// plan saves.)
 bool step_fused(int bits, int q_len, int group, int num_seqs, int num_kv_heads, int64_t num_tokens) {
-  return bits == 3 && q_len == 1 && group >= 1 && group <= 4 && tq::decode_uses_mfma(1, group, bits) &&
-         num_tokens * num_kv_heads <= tq::kAppendMaxVectors && (int64_t)num_seqs * num_kv_heads <= 0x7fffffffLL;
+  return bits == 3 && q_len == 1 && group >= 1 && group <= 8 && tq::decode_uses_mfma(1, group, bits) &&
+         num_tokens * num_kv_heads <= tq::kAppendMaxVectors && (int64_t)num_seqs * num_kv_heads <= 0x3fffffffLL;
 }
-// The fused step's split pass runs the stream plan: the tiles of all groups in
-// one order, q = ceil(N / (4 kStreamTarget)) consecutive tiles per wave
-// (1 <= q <= 16, so at most max(4 kStreamTarget, N / 16) waves, 4 per
-// workgroup), the workgroups in one run per accelerator die (7 more cover
-// the runs' rounding).  Each wave writes a record per group it touches, at
-// place (wave + group): fewer than waves + groups places of G rows.
+// The stream plan: the tiles of all groups in one order, q consecutive tiles
+// per run (1 <= q <= 16), one wave per run and head tile (P = 1 for up to 4
+// query heads per KV head, 2 for 5 to 8), q = ceil(P N / (4 kStreamTarget)):
+// at most max(4 kStreamTarget, N / 16) runs and P times as many waves, 4 per
+// workgroup, the workgroups in one run per accelerator die (7 more cover the
+// runs' rounding).  Each run writes a record per group it touches, at place
+// (run + group): fewer than runs + groups places of G rows.
 constexpr int kStreamTarget = 512;  // workgroups that fill the compute units once
-int64_t stream_waves(int num_seqs, int num_kv_heads, int span) {
+int stream_pair(int group) { return group > 4 ? 2 : 1; }
+int64_t stream_runs(int num_seqs, int num_kv_heads, int span) {
   const int64_t N = (int64_t)num_seqs * num_kv_heads * ((std::max(span, 0) + 127) / 128);
   return std::max<int64_t>(4 * kStreamTarget, (N + 15) / 16);
 }
-int stream_grid(int num_seqs, int num_kv_heads, int span) {
-  return (int)((stream_waves(num_seqs, num_kv_heads, span) + 3) / 4) + 7;
+int stream_grid(int num_seqs, int num_kv_heads, int group, int span) {
+  return (int)((stream_pair(group) * stream_runs(num_seqs, num_kv_heads, span) + 3) / 4) + 7;
 }
 size_t stream_record_floats(int num_seqs, int group, int num_kv_heads, int span) {
-  return (size_t)(stream_waves(num_seqs, num_kv_heads, span) + (int64_t)num_seqs * num_kv_heads) * group * kPartStride;
+  return (size_t)(stream_runs(num_seqs, num_kv_heads, span) + (int64_t)num_seqs * num_kv_heads) * group * kPartStride;
 }
-// The fused step's workspace: the records, then the groups' query operands.
+// The stream plan's workspace: the records, then the query operands of each
+// (group, head tile).
 size_t step_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int span) {
-  return stream_record_floats(num_seqs, num_q_heads / num_kv_heads, num_kv_heads, span) * sizeof(float) +
-         (size_t)num_seqs * num_kv_heads * tq::kQopsDwords * 64 * sizeof(uint32_t);
+  const int group = num_q_heads / num_kv_heads;
+  return stream_record_floats(num_seqs, group, num_kv_heads, span) * sizeof(float) +
+         (size_t)num_seqs * num_kv_heads * stream_pair(group) * tq::kQopsDwords * 64 * sizeof(uint32_t);
 }
 
 size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
@@ -626,7 +632,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     // stream plan: the records, then the operands (16-byte aligned: records of 528 bytes)
     a.balanced = 2;
     a.bal_target = kStreamTarget;
-    a.bal_grid = stream_grid(num_seqs, num_kv_heads, span);
+    a.bal_grid = stream_grid(num_seqs, num_kv_heads, group, span);
     a.partials = (float *)workspace;
     a.qops = reinterpret_cast<uint32_t *>(a.partials + stream_record_floats(num_seqs, group, num_kv_heads, span));
     e = tq::launch_step_prep(*step, a, (hipStream_t)stream);

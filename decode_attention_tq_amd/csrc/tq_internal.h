@@ -169,7 +169,7 @@ hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // The fused decode step's append + query operands launch (3-bit codes, up to
-// 4 query heads per KV head, q_len 1; the split pass then runs the stream plan).
+// 8 query heads per KV head, q_len 1; the split pass then runs the stream plan).
 hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);
 

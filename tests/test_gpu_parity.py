@@ -479,10 +479,10 @@ def test_largest_chunk_of_the_matrix_core_pass(Hq, Hkv):
                  kv_heads=[0, Hkv - 1])
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 8)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 8), (40, 8), (64, 8)])
 def test_last_tile_with_a_few_tokens(Hq, Hkv):
-    """Sequences whose last 128-token tile holds 2, 3 or 15 tokens, with 1, 2
-    and 4 query heads per KV head and two chunk sizes: the masked slots of
+    """Sequences whose last 128-token tile holds 2, 3 or 15 tokens, with 1, 2,
+    4, 5 and 8 query heads per KV head and two chunk sizes: the masked slots of
     that tile (pages re-read past the end, slots never written) must get no
     weight.  Element-wise against the oracle on every head."""
     lengths = [643, 1154, 3343, 836, 1249, 2, 130, 3]

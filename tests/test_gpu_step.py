@@ -34,14 +34,16 @@ def _two_calls(cb, kn, vn, slots, q, kpool, vpool, bt, cl, maxc, Hkv):
     return tq.tq_decode_attention(cb, q, kpool, vpool, bt, cl, maxc, Hkv)
 
 
-def _same_output(out, ref, fused):
+def _same_output(out, ref, fused, rel=None):
     """Bit-identical unfused; fused, within 2e-5 of each row's largest
-    magnitude (fp32 rounding of another split), or one step of a bf16 output."""
+    magnitude (fp32 rounding of another split), or one step of a bf16 output
+    (rel: another bound, for a step whose split pass is another kernel)."""
     if not fused:
         assert torch.equal(out, ref), f"outputs differ: max {float((out.float() - ref.float()).abs().max()):.3e}"
         return
     o, r = out.float(), ref.float()
-    rel = 2e-5 if out.dtype == torch.float32 else 2.0 ** -7
+    if rel is None:
+        rel = 2e-5 if out.dtype == torch.float32 else 2.0 ** -7
     scale = r.abs().amax(dim=-1, keepdim=True)
     err = (o - r).abs()
     assert bool(torch.all(err <= rel * scale)), f"max err / row scale {float((err / scale.clamp_min(1e-30)).max()):.3e}"
@@ -52,7 +54,12 @@ def test_step_is_append_then_decode(Hq, Hkv, bits):
     """Two consecutive steps of a ragged batch of 16 (lengths in [512, 4096]):
     pools and outputs equal to the separate calls' bit for bit, with one
     sequence skipping its append (slot -1, context unchanged).  Group sizes 4,
-    1 and 2 run fused; 8 heads per KV head and 2-bit codes run unfused."""
+    1, 2 and 8 run fused (8: two waves per run of tiles, one head tile each);
+    2-bit codes run unfused.  With 8 heads per KV head the separate attention
+    call runs the 8-wave pass, which cuts the 15-bit softmax weights into
+    other blocks than the step's waves: on long peaked rows their outputs
+    differ by up to a few 1e-4 of the row scale, so there both are held to
+    the oracle after every step and to each other within the parity bar."""
     B = 16
     case, cb, kpool, vpool = _setup(11 + Hq + bits, B, Hq, Hkv, bits=bits, hi=4096)
     ka, va = kpool.clone(), vpool.clone()
@@ -80,7 +87,15 @@ def test_step_is_append_then_decode(Hq, Hkv, bits):
         print(f"Hq {Hq} Hkv {Hkv} bits {bits} step {s}", flush=True)
         assert torch.equal(kpool, ka), "K pools differ"
         assert torch.equal(vpool, va), "V pools differ"
-        _same_output(out, ref, fused=bits == 3 and Hq // Hkv <= 4)
+        G = Hq // Hkv
+        if bits == 3 and G > 4:
+            _same_output(out, ref, fused=True, rel=2e-3)
+            kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
+            for o in (out, ref):
+                check_decode(o.cpu().numpy(), case["q"][s], kp, vp, case["table"], L,
+                             tables=oracle_tables(bits=bits), kv_heads=[0, Hkv - 1])
+        else:
+            _same_output(out, ref, fused=bits == 3 and G <= 4)
     if bits == 3:
         kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
         check_decode(out.cpu().numpy(), case["q"][1], kp, vp, case["table"], L, tables=oracle_tables(bits=bits),
@@ -242,20 +257,23 @@ def _device_cache_case(seed, lengths, Hq=32, Hkv=8):
     return cb, kpool, vpool, table, L + 1, new_slots, kn, vn, q
 
 
-@pytest.mark.parametrize("name,lengths", [
-    ("64 sequences of one tile", [1 + 2 * b for b in range(64)]),
-    ("two long sequences", [131071, 99999]),
-    ("more tiles than one round of waves", [40000] * 8 + [30000] * 8),
+@pytest.mark.parametrize("name,lengths,Hq", [
+    ("64 sequences of one tile", [1 + 2 * b for b in range(64)], 32),
+    ("two long sequences", [131071, 99999], 32),
+    ("more tiles than one round of waves", [40000] * 8 + [30000] * 8, 32),
+    ("64 sequences of one tile, 8 heads per KV head", [1 + 2 * b for b in range(64)], 64),
+    ("more tiles than one round of waves, 6 heads per KV head", [40000] * 8 + [30000] * 8, 48),
 ])
-def test_step_stream_plan_extremes(name, lengths):
+def test_step_stream_plan_extremes(name, lengths, Hq):
     """The step's split plan at its ends: 64 one-tile sequences (one tile
     per wave, one wave per group); two sequences of 131,072 and 100,000
     tokens (8 tiles per wave, a group spread over hundreds of waves); 16
     sequences of 30,000-40,000 tokens, 35,072 tiles (16 tiles per wave, more
     workgroups than run at once).  Pools bit-identical to the separate
     calls, outputs within rounding of theirs, the oracle on sampled
-    sequences and KV heads."""
-    Hq, Hkv = 32, 8
+    sequences and KV heads.  With 6 and 8 query heads per KV head the waves
+    go in pairs (one head tile each) over the same runs of tiles."""
+    Hkv = 8
     cb, kpool, vpool, table, L, new_slots, kn, vn, qn = _device_cache_case(71 + len(lengths), lengths, Hq, Hkv)
     ka, va = kpool.clone(), vpool.clone()
     bt = torch.from_numpy(table.astype(np.int32)).cuda()
@@ -268,7 +286,9 @@ def test_step_stream_plan_extremes(name, lengths):
     torch.cuda.synchronize()
     print(f"{name}: step done", flush=True)
     assert torch.equal(kpool, ka) and torch.equal(vpool, va)
-    _same_output(out, ref, fused=True)
+    # 5 to 8 heads: the separate call runs the 8-wave pass (other weight
+    # blocks), so the two are held to the oracle and to the parity bar
+    _same_output(out, ref, fused=True, rel=2e-3 if Hq // Hkv > 4 else None)
     kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
     q64 = q.float().cpu().numpy()
     seqs = [0, len(L) - 1]

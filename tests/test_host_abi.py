@@ -426,21 +426,122 @@ def test_step_validation():
 
 
 @pytest.mark.parametrize("bits,Hq,Hkv,fused", [(3, 32, 8, True), (3, 8, 8, True), (3, 16, 8, True),
-                                                (3, 64, 8, False), (2, 32, 8, False), (4, 32, 8, False)])
+                                                (3, 64, 8, True), (3, 40, 8, True), (3, 72, 8, False),
+                                                (2, 32, 8, False), (4, 32, 8, False)])
 def test_step_workspace(bits, Hq, Hkv, fused):
     """The fused step's split pass runs the stream plan: 16 sequences of up
     to 32,768 tokens x Hkv KV heads are at most 16 x Hkv x 256 tiles, so at
-    most max(2,048, tiles / 16) waves; it needs one record (132 floats) per
-    query head of the group at each of waves + groups places, then each
-    (sequence, KV head) group's query operands (44 words per lane of a
-    64-lane wave).  An unfused step needs the attention call's workspace."""
+    most max(2,048, tiles / 16) runs of tiles; it needs one record (132
+    floats) per query head of the group at each of runs + groups places, then
+    the query operands (44 words per lane of a 64-lane wave) of each
+    (sequence, KV head) group and head tile (two tiles for 5 to 8 heads).
+    An unfused step needs the attention call's workspace."""
     cb = ctypes.byref(_fake_cb(bits=bits))
     B, ctx = 16, 32768
     dec = tq._lib.tq_decode_workspace_bytes(cb, B, 1, Hq, Hkv, ctx, 0)
     step = tq._lib.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, ctx, 0)
     if fused:
         G = Hq // Hkv
-        waves = max(2048, -(-(B * Hkv * 256) // 16))
-        assert step == (waves + B * Hkv) * G * 132 * 4 + B * Hkv * 44 * 64 * 4
+        runs = max(2048, -(-(B * Hkv * 256) // 16))
+        assert step == (runs + B * Hkv) * G * 132 * 4 + B * Hkv * (2 if G > 4 else 1) * 44 * 64 * 4
     else:
         assert step == dec
+
+
+def _stream_plan(lengths, Hkv, G, target=512):
+    """The stream plan as the split pass and the merge compute it (a restatement
+    on the host of their index arithmetic): returns the written (place, row)
+    pairs per group, the operand items read, the (tile, head tile) pairs
+    covered, and the workgroup count the pass needs."""
+    T = [(int(L) + 127) // 128 for L in lengths]
+    N = Hkv * sum(T)
+    P = 2 if G > 4 else 1
+    q = min(max(-(-(P * N) // (4 * target)), 1), 16)
+    runs = -(-N // q)
+    nwg = (P * runs + 3) // 4
+    # the groups' first tiles in the order (sequence-major, then KV head)
+    starts, g = {}, 0
+    c = 0
+    for b, t in enumerate(T):
+        for h in range(Hkv):
+            starts[b * Hkv + h] = (c, t)
+            c += t
+    owner = []  # global tile -> group
+    for grp in range(len(T) * Hkv):
+        owner += [grp] * starts[grp][1]
+    return dict(N=N, P=P, q=q, runs=runs, nwg=nwg, starts=starts, owner=owner)
+
+
+def _xcd_run_start(x, total):
+    return (x * total + 7) // 8
+
+
+@pytest.mark.parametrize("G", [1, 3, 4, 5, 8])
+def test_stream_plan_covers_every_tile_within_the_workspace(G):
+    """CPU restatement of the stream plan's indexing, checked against the
+    workspace the library sizes: over ragged batches, single long sequences
+    and empty ones, every (tile, head tile) is taken by exactly one wave,
+    every record place and row lies inside the records, every operand item
+    inside the operands, the grid reaches every workgroup of the plan, and the
+    merge reads exactly the places the split pass writes."""
+    cb = ctypes.byref(_fake_cb())
+    rng = np.random.default_rng(100 + G)
+    cases = [([131072], 4), ([1], 8), ([0, 0, 5], 2), ([32768] * 16, 8), ([100000, 131072], 8), ([16] * 64, 8),
+             (list(range(0, 4000, 37)), 2)]
+    for _ in range(12):
+        B = int(rng.integers(1, 40))
+        hi = int(rng.choice([600, 4096, 40000]))
+        cases.append((list(rng.integers(0, hi, B)), int(rng.choice([1, 2, 4, 8]))))
+    for lengths, Hkv in cases:
+        B, maxc = len(lengths), max(max(lengths), 1)
+        Hq = G * Hkv
+        plan = _stream_plan(lengths, Hkv, G)
+        N, P, q, runs, nwg = plan["N"], plan["P"], plan["q"], plan["runs"], plan["nwg"]
+        groups = B * Hkv
+        # the host's bound on runs, places and the grid
+        run_bound = max(2048, -(-(B * Hkv * ((maxc + 127) // 128)) // 16))
+        grid = (P * run_bound + 3) // 4 + 7
+        ws = tq._lib.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, maxc, 0)
+        assert ws == (run_bound + groups) * G * 132 * 4 + groups * P * 44 * 64 * 4
+        assert runs <= run_bound
+        # workgroups: blockIdx -> (die x, place in the die's run)
+        reached = set()
+        for blk in range(grid):
+            x, s = blk & 7, blk >> 3
+            rpos = _xcd_run_start(x, nwg) + s
+            if rpos < _xcd_run_start(x + 1, nwg):
+                assert rpos not in reached
+                reached.add(rpos)
+        assert reached == set(range(nwg))
+        covered = {}
+        written = {}
+        items = set()
+        for rpos in range(nwg):
+            for wave in range(4):
+                iw, ut = divmod(4 * rpos + wave, P)
+                ntiles = min(q, N - iw * q)
+                if ntiles <= 0:
+                    continue
+                touched = set()
+                for k in range(ntiles):
+                    c = iw * q + k
+                    grp = plan["owner"][c]
+                    key = (c, ut)
+                    assert key not in covered
+                    covered[key] = True
+                    touched.add(grp)
+                for grp in touched:
+                    items.add(grp * P + ut)
+                    for row in range(4 * ut, min(4 * ut + 4, G)):
+                        place = iw + grp
+                        assert place < run_bound + groups
+                        written.setdefault(grp, set()).add((place, row))
+        assert set(covered) == {(c, u) for c in range(N) for u in range(P)}
+        assert items <= set(range(groups * P))
+        # the merge: group g's records are places floor(C/q) + g .. floor((C + T - 1)/q) + g
+        for grp, (c0, t) in plan["starts"].items():
+            if t == 0:
+                assert grp not in written
+                continue
+            places = set(range(c0 // q + grp, (c0 + t - 1) // q + grp + 1))
+            assert written[grp] == {(p, r) for p in places for r in range(G)}
