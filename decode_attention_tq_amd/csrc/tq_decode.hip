@@ -1554,17 +1554,18 @@ __device__ __forceinline__ int xcd_run_start(int x, int total) { return (x * tot
 // + h T_b, N tiles in all).  Wave i of the split pass takes the q tiles from
 // i q, q = ceil(N / (4 bal_target)) within [1, kStreamMaxTiles]: every wave
 // has the same work whatever the lengths (a plan of whole ranges per group
-// leaves some compute units with a third more tiles than the mean).  With 5
-// to 8 query heads per KV head (two head tiles) the waves go in pairs: waves
-// 2 i and 2 i + 1 take the same run i of q tiles (q = ceil(2 N / (4
-// bal_target))), one head tile each, side by side in one workgroup, so the
-// second wave's page loads find the first's lines in the caches and HBM
-// serves each page once.  A run whose tiles span groups writes one partial
-// record per group it touches: the record of (run i, group g) sits at place
-// i + g (rows 4 u .. 4 u + 3 from head tile u), and group g's records are the
-// consecutive places from floor(C_g / q) + g to floor((C_g + T_g - 1) / q) +
-// g.  Waves are numbered along the dies' runs (4 per workgroup), so a
-// group's waves share one die.
+// leaves some compute units with a third more tiles than the mean).  A
+// group has R = G q_len query rows (position-major: row i G + g is head g of
+// position i), in P = ceil(R / 4) head tiles of four rows; with P > 1 (5 to
+// 8 heads, or a verify block) the waves go in sets of P: waves P i .. P i +
+// P - 1 take the same run i of q tiles (q = ceil(P N / (4 bal_target))), one
+// head tile each, side by side on one die, so the later waves' page loads
+// find the first's lines in the caches and HBM serves each page once.  A run
+// whose tiles span groups writes one partial record per group it touches:
+// the record of (run i, group g) sits at place i + g (rows 4 u .. 4 u + 3
+// from head tile u), and group g's records are the consecutive places from
+// floor(C_g / q) + g to floor((C_g + T_g - 1) / q) + g.  Waves are numbered
+// along the dies' runs (4 per workgroup), so a group's waves share one die.
 constexpr int kStreamMaxTiles = 16;
 __device__ __forceinline__ int lane_context(const DecodeArgs &a, int s) {
   return s < a.num_seqs ? clamped_context(a, s) : 0;
@@ -1581,8 +1582,8 @@ __device__ __forceinline__ int stream_total(const DecodeArgs &a, int t0) {
     tot += __builtin_amdgcn_readlane(wave_incl_scan_int(stream_block_tiles(a, t0, c0, lane), lane), 63);
   return tot * a.num_kv_heads;
 }
-// waves per run of tiles: one per head tile
-__device__ __forceinline__ int stream_pair(const DecodeArgs &a) { return a.group > 4 ? 2 : 1; }
+// waves per run of tiles: one per head tile of the group's query rows
+__device__ __forceinline__ int stream_pair(const DecodeArgs &a) { return (a.group * a.pos_count + 3) / 4; }
 __device__ __forceinline__ int stream_per(const DecodeArgs &a, int N) {
   const int64_t waves = 4 * a.bal_target;
   return (int)min<int64_t>(max<int64_t>(((int64_t)stream_pair(a) * N + waves - 1) / waves, 1), kStreamMaxTiles);
@@ -1897,7 +1898,7 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
     const float cs = (corr[0][0] + corr[0][1]) + (corr[0][2] + corr[0][3]);
     const float ls = row_sum16(lsum[0]);
     if (4 * ut + grow < nrows) {
-      float *part = a.partials + (((int64_t)iw + grp) * G + 4 * ut + grow) * kPartStride;
+      float *part = a.partials + (((int64_t)iw + grp) * nrows + 4 * ut + grow) * kPartStride;
       if (t16 == 0) {
         part[0] = R[0];
         part[1] = ls;
@@ -2193,8 +2194,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
     const int64_t per_seq = (int64_t)a.q_len * a.num_q_heads;
     const int b = (int)(r / per_seq);
     const int t = (int)((r / a.num_q_heads) % a.q_len);
-    if (a.balanced == 2) {  // stream plan (q_len 1): the group's records are consecutive places
-      const int hq = (int)(r % a.num_q_heads), h = hq / a.group, hd = hq - h * a.group;
+    if (a.balanced == 2) {  // stream plan: the group's records are consecutive places
+      const int hq = (int)(r % a.num_q_heads), h = hq / a.group, hd = t * a.group + hq - h * a.group;
+      const int nrows = a.group * a.q_len;
       const int t0s = span_tiles(a, lane_context(a, lane));
       const int q = stream_per(a, stream_total(a, t0s));
       int P, Tb;
@@ -2202,8 +2204,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
       if (Tb > 0) {  // uniform
         const int c0 = P + h * Tb, i0 = c0 / q;
         ns = (c0 + Tb - 1) / q - i0 + 1;
-        part += (((int64_t)i0 + (int64_t)b * a.num_kv_heads + h) * a.group + hd) * kPartStride;
-        rstride = (int64_t)a.group * kPartStride;
+        part += (((int64_t)i0 + (int64_t)b * a.num_kv_heads + h) * nrows + hd) * kPartStride;
+        rstride = (int64_t)nrows * kPartStride;
       }
     } else {
       if (a.balanced) {
@@ -2339,16 +2341,20 @@ hipError_t noalloc_scratch(void **ptr) {
 // heads; another size runs on the next one up.
 static int group_capacity(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : g <= 16 ? 16 : 0; }
 
-hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream_t stream) {
-  const int64_t vectors = ea.num_tokens * ea.num_kv_heads;
+hipError_t launch_step_prep(const EncodeArgs *ea, const DecodeArgs &a, hipStream_t stream) {
+  // no append (ea null): the query operands of a verify block only
+  const int64_t vectors = ea ? ea->num_tokens * ea->num_kv_heads : 0;
   const int n_append = (int)((vectors + kAppendWaves - 1) / kAppendWaves);
   // one operands workgroup per (group, head tile)
-  const int n_items = a.num_seqs * a.num_kv_heads * (a.group > 4 ? 2 : 1);
+  const int n_items = a.num_seqs * a.num_kv_heads * ((a.group * a.pos_count + 3) / 4);
   const dim3 grid((unsigned)(n_append + n_items));
-  switch (ea.dtype) {
-    case TQ_BF16: hipLaunchKernelGGL(step_prep_kernel<TQ_BF16>, grid, dim3(256), 0, stream, ea, a, n_append, n_items); break;
-    case TQ_F16: hipLaunchKernelGGL(step_prep_kernel<TQ_F16>, grid, dim3(256), 0, stream, ea, a, n_append, n_items); break;
-    case TQ_F32: hipLaunchKernelGGL(step_prep_kernel<TQ_F32>, grid, dim3(256), 0, stream, ea, a, n_append, n_items); break;
+  EncodeArgs none{};
+  none.dtype = TQ_BF16;
+  const EncodeArgs &e = ea ? *ea : none;
+  switch (e.dtype) {
+    case TQ_BF16: hipLaunchKernelGGL(step_prep_kernel<TQ_BF16>, grid, dim3(256), 0, stream, e, a, n_append, n_items); break;
+    case TQ_F16: hipLaunchKernelGGL(step_prep_kernel<TQ_F16>, grid, dim3(256), 0, stream, e, a, n_append, n_items); break;
+    case TQ_F32: hipLaunchKernelGGL(step_prep_kernel<TQ_F32>, grid, dim3(256), 0, stream, e, a, n_append, n_items); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2370,8 +2376,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     la.pos0 = 0;
     la.pos_count = min(per, a.q_len);
     la.qk_tiles = (la.group * la.pos_count + 3) / 4;
-    if (a.balanced == 2) {  // the fused decode step's pass (stream plan)
-      if (pgroups != 1 || la.qk_tiles < 1 || la.qk_tiles > 2 || a.hot_parts > 0 || !a.qops) return hipErrorInvalidValue;
+    if (a.balanced == 2) {  // the stream plan (fused decode step, verify blocks): every position in one launch
+      la.pos_count = a.q_len;
+      la.qk_tiles = (la.group * la.pos_count + 3) / 4;
+      if (la.qk_tiles > 8 || a.hot_parts > 0 || !a.qops) return hipErrorInvalidValue;
       hipLaunchKernelGGL((split_wave_kernel<1, true>), dim3((unsigned)items), dim3(256), 0, stream, la);
     } else if (pgroups == 1 && la.qk_tiles == 1) {
       // the exact window's chunks ride in the same launch (q_len 1)

@@ -430,38 +430,48 @@ int walk_span(int max_context_len, int q_len, int window) {
 // split pass on the stream plan reading them, then the merge) serves 3-bit
 // codes with up to 8 query heads per KV head and appends of at most
 // kAppendMaxVectors vectors; other steps run the encode and the decode
-// launches in turn.  (A plain attention call keeps its own plan: without an
-// append to share it with, the operands' launch costs more than the stream
-// plan saves.)
+// launches in turn.  A verify block of more than 8 query rows per KV head
+// (G q_len, at most 32) runs the stream plan too, with a launch of its own
+// for the query operands: one pass over the cache for every position, where
+// the balanced plan's launches give each group of 8 / G positions a range of
+// workgroups of its own.  (A single-query call keeps the balanced plan:
+// without an append to share it with, the operands' launch costs more than
+// the stream plan saves.)
 bool step_fused(int bits, int q_len, int group, int num_seqs, int num_kv_heads, int64_t num_tokens) {
   return bits == 3 && q_len == 1 && group >= 1 && group <= 8 && tq::decode_uses_mfma(1, group, bits) &&
-         num_tokens * num_kv_heads <= tq::kAppendMaxVectors && (int64_t)num_seqs * num_kv_heads <= 0x3fffffffLL;
+         num_tokens * num_kv_heads <= tq::kAppendMaxVectors && (int64_t)num_seqs * num_kv_heads <= 0x0fffffffLL;
+}
+constexpr int kVerifyStreamRows = 8;
+bool verify_stream(int bits, int q_len, int group, int num_seqs, int num_kv_heads, int tokens_per_split,
+                   int hot_parts) {
+  return bits == 3 && q_len > 1 && tq::decode_uses_mfma(q_len, group, bits) && group * q_len > kVerifyStreamRows &&
+         tokens_per_split == 0 && hot_parts == 0 && (int64_t)num_seqs * num_kv_heads <= 0x0fffffffLL;
 }
 // The stream plan: the tiles of all groups in one order, q consecutive tiles
-// per run (1 <= q <= 16), one wave per run and head tile (P = 1 for up to 4
-// query heads per KV head, 2 for 5 to 8), q = ceil(P N / (4 kStreamTarget)):
-// at most max(4 kStreamTarget, N / 16) runs and P times as many waves, 4 per
-// workgroup, the workgroups in one run per accelerator die (7 more cover the
-// runs' rounding).  Each run writes a record per group it touches, at place
-// (run + group): fewer than runs + groups places of G rows.
+// per run (1 <= q <= 16), one wave per run and head tile (P = ceil(R / 4)
+// for the R = G q_len query rows of a group), q = ceil(P N / (4
+// kStreamTarget)): at most max(4 kStreamTarget, N / 16) runs and P times as
+// many waves, 4 per workgroup, the workgroups in one run per accelerator die
+// (7 more cover the runs' rounding).  Each run writes a record per group it
+// touches, at place (run + group): fewer than runs + groups places of R rows.
 constexpr int kStreamTarget = 512;  // workgroups that fill the compute units once
-int stream_pair(int group) { return group > 4 ? 2 : 1; }
+int stream_pair(int rows) { return (rows + 3) / 4; }
 int64_t stream_runs(int num_seqs, int num_kv_heads, int span) {
   const int64_t N = (int64_t)num_seqs * num_kv_heads * ((std::max(span, 0) + 127) / 128);
   return std::max<int64_t>(4 * kStreamTarget, (N + 15) / 16);
 }
-int stream_grid(int num_seqs, int num_kv_heads, int group, int span) {
-  return (int)((stream_pair(group) * stream_runs(num_seqs, num_kv_heads, span) + 3) / 4) + 7;
+int64_t stream_grid(int num_seqs, int num_kv_heads, int rows, int span) {
+  return (stream_pair(rows) * stream_runs(num_seqs, num_kv_heads, span) + 3) / 4 + 7;
 }
-size_t stream_record_floats(int num_seqs, int group, int num_kv_heads, int span) {
-  return (size_t)(stream_runs(num_seqs, num_kv_heads, span) + (int64_t)num_seqs * num_kv_heads) * group * kPartStride;
+size_t stream_record_floats(int num_seqs, int rows, int num_kv_heads, int span) {
+  return (size_t)(stream_runs(num_seqs, num_kv_heads, span) + (int64_t)num_seqs * num_kv_heads) * rows * kPartStride;
 }
 // The stream plan's workspace: the records, then the query operands of each
 // (group, head tile).
-size_t step_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int span) {
-  const int group = num_q_heads / num_kv_heads;
-  return stream_record_floats(num_seqs, group, num_kv_heads, span) * sizeof(float) +
-         (size_t)num_seqs * num_kv_heads * stream_pair(group) * tq::kQopsDwords * 64 * sizeof(uint32_t);
+size_t step_workspace(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int span) {
+  const int rows = num_q_heads / num_kv_heads * q_len;
+  return stream_record_floats(num_seqs, rows, num_kv_heads, span) * sizeof(float) +
+         (size_t)num_seqs * num_kv_heads * stream_pair(rows) * tq::kQopsDwords * 64 * sizeof(uint32_t);
 }
 
 size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
@@ -470,6 +480,8 @@ size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int 
     return 0;
   max_context_len = walk_span(max_context_len, q_len, window);
   const int grp = num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
+  if (grp > 0 && verify_stream(bits, q_len, grp, num_seqs, num_kv_heads, tokens_per_split, hot_parts))
+    return step_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len);
   const int ns = plan_splits(num_seqs, q_len, num_kv_heads, grp, max_context_len, tokens_per_split, bits).num_splits;
   const int64_t rows = (int64_t)num_seqs * q_len * num_q_heads;
   // the matrix-core split pass forms its query operands itself: partials only
@@ -555,7 +567,11 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     if (ns + hot_parts > 65535) return fail(TQ_ERR_UNSUPPORTED, "too many partial records per row");
   }
   const bool fused = step && step_fused(bits, q_len, group, num_seqs, num_kv_heads, step->num_tokens);
-  const size_t need = fused ? step_workspace(num_seqs, num_q_heads, num_kv_heads, span)
+  const bool verify = !step && verify_stream(bits, q_len, group, num_seqs, num_kv_heads, tokens_per_split,
+                                             hot_parts);
+  if ((fused || verify) && (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return fail(TQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  const size_t need = fused || verify ? step_workspace(num_seqs, q_len, num_q_heads, num_kv_heads, span)
                             : decode_workspace(bits, num_seqs, q_len, num_q_heads, num_kv_heads, max_context_len,
                                                tokens_per_split, hot_parts, window);
   if (noalloc) {
@@ -628,15 +644,18 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.cb = device_codebook(cb);
   a.qops = nullptr;
   hipError_t e;
-  if (fused) {
+  if (fused || verify) {
     // stream plan: the records, then the operands (16-byte aligned: records of 528 bytes)
+    const int64_t grid = stream_grid(num_seqs, num_kv_heads, group * q_len, span);
+    if (grid > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "too many tiles for one launch");
     a.balanced = 2;
     a.bal_target = kStreamTarget;
-    a.bal_grid = stream_grid(num_seqs, num_kv_heads, group, span);
+    a.bal_grid = (int)grid;
     a.partials = (float *)workspace;
-    a.qops = reinterpret_cast<uint32_t *>(a.partials + stream_record_floats(num_seqs, group, num_kv_heads, span));
-    e = tq::launch_step_prep(*step, a, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "decode step launch");
+    a.qops = reinterpret_cast<uint32_t *>(a.partials +
+                                          stream_record_floats(num_seqs, group * q_len, num_kv_heads, span));
+    e = tq::launch_step_prep(fused ? step : nullptr, a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fused ? "decode step launch" : "verify operands launch");
   } else if (step) {
     e = tq::launch_encode(*step, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
@@ -724,7 +743,7 @@ size_t tq_decode_step_workspace_bytes(const tq_codebook *cb, int num_seqs, int n
   if (need == 0 || num_q_heads % num_kv_heads != 0) return need;
   const int group = num_q_heads / num_kv_heads;
   if (step_fused(bits, 1, group, num_seqs, num_kv_heads, num_seqs))
-    return step_workspace(num_seqs, num_q_heads, num_kv_heads, max_context_len);
+    return step_workspace(num_seqs, 1, num_q_heads, num_kv_heads, max_context_len);
   return need;
 }
 

@@ -168,9 +168,11 @@ hipError_t noalloc_scratch(void **ptr);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
-// The fused decode step's append + query operands launch (3-bit codes, up to
-// 8 query heads per KV head, q_len 1; the split pass then runs the stream plan).
-hipError_t launch_step_prep(const EncodeArgs &ea, const DecodeArgs &a, hipStream_t stream);
+// The stream plan's query operands launch (3-bit codes; the split pass then
+// runs the stream plan), with the fused decode step's append in the same
+// launch (ea non-null; q_len 1, up to 8 query heads per KV head) or alone
+// (a verify block of up to 32 query rows per KV head).
+hipError_t launch_step_prep(const EncodeArgs *ea, const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace tq

@@ -15,5 +15,5 @@ hipError_t noalloc_scratch(void **) { reached("noalloc_scratch"); }
 hipError_t launch_encode(const EncodeArgs &, hipStream_t) { reached("launch_encode"); }
 hipError_t launch_decode(const DecodeArgs &, hipStream_t) { reached("launch_decode"); }
 hipError_t launch_prefill(const DecodeArgs &, hipStream_t) { reached("launch_prefill"); }
-hipError_t launch_step_prep(const EncodeArgs &, const DecodeArgs &, hipStream_t) { reached("launch_step_prep"); }
+hipError_t launch_step_prep(const EncodeArgs *, const DecodeArgs &, hipStream_t) { reached("launch_step_prep"); }
 }  // namespace tq

@@ -278,14 +278,16 @@ def test_running_maximum_moves_along_the_sequence(Hkv):
 
 
 @pytest.mark.parametrize("q_len,Hq,Hkv", [(2, 32, 8), (3, 4, 2), (8, 8, 8), (4, 32, 8), (3, 32, 4),
-                                         (8, 32, 4), (3, 16, 1)])
+                                         (8, 32, 4), (3, 16, 1), (8, 32, 8), (32, 8, 8), (5, 24, 8)])
 def test_multi_token_verify(q_len, Hq, Hkv):
     """Multi-token verify decode (speculative or multi-token prediction): 2 to
-    8 new queries per sequence over a compressed cache, each causal over the
+    32 new queries per sequence over a compressed cache, each causal over the
     cache plus the verified tokens before it, batched sequences of ragged
-    length.  The matrix-core decode pass takes up to 8 query rows (positions x
-    heads) per KV head and launch, up to 4 launches (4, 6 and 8 rows in one
-    launch, 2 and 3 launches here); longer blocks take the prefill pass."""
+    length (the first as long as the block).  Up to 8 query rows (positions x
+    heads) per KV head run the balanced plan's launch (4, 6 and 8 rows
+    here); 9 to 32 rows the stream plan, one wave per head tile of four rows
+    (12, 24, 32 and 15 rows here, with 1, 3, 4 and 8 heads per KV head);
+    longer blocks take the prefill pass."""
     rng = np.random.default_rng(20 + q_len)
     lens = np.array([q_len, 700, 2300], dtype=np.int64)
     table, nb = synth.block_tables(rng, lens)
