@@ -40,17 +40,20 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kPartStride = 132;  // m (log2 units), l, pad, pad, acc[128]
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKeys = 32;         // keys per step (two pages)
-constexpr int kKRow = 136;        // halves per K tile row (128 + pad)
-constexpr int kVRow = 40;         // halves per V tile row (32 + pad)
 constexpr float kTabScale = 16.0f;  // levels are tabulated x16: their lo halves stay normal f16
 
-// One step's dequantized tiles.
+// One step's dequantized tiles, each stored in the order the matrix ops read
+// it: entry [..][lane] is the 16-byte operand piece of lane 16 g + r, so a
+// wave's operand read is one contiguous 1 KiB and no two lanes of it share
+// a bank.  K tile (ct, kc): lane (g, r) holds coordinates 32 kc + 8 g .. +7
+// of key 16 ct + r; V tile cv: lane (g, r) holds slots 8 g .. 8 g + 7 of
+// coordinate 16 cv + r.
 struct Tile {
-  _Float16 kh[kKeys][kKRow];       // key levels x16, hi
-  _Float16 kl[kKeys][kKRow];       // lo
-  _Float16 ks[kKeys][kKRow];       // QJL signs +-1
-  _Float16 vh[kHeadDim][kVRow];    // value levels x16, hi, [coordinate][slot]
-  _Float16 vl[kHeadDim][kVRow];    // lo
+  v8h kh[2][4][64];                // key levels x16, hi: [key tile][coordinate block][lane]
+  v8h kl[2][4][64];                // lo
+  v8h ks[2][4][64];                // QJL signs +-1
+  v8h vh[8][64];                   // value levels x16, hi: [coordinate tile][lane]
+  v8h vl[8][64];                   // lo
   float kn[kKeys];                 // n_k / 16
   float kg[kKeys];                 // n_k gamma
   float vn[kKeys];                 // n_v
@@ -100,14 +103,16 @@ constexpr int kRows = 16 * kRowTiles * kWaves;  // query rows per workgroup
 static_assert(kRows == kPrefillRows, "the host plans prefill blocks of kPrefillRows rows");
 
 // Dequantize a step's staged pages into T (all threads of the workgroup).
-// Keys: item (key, 8 coordinates); values: item (coordinate, page, half of
-// the page's tokens), tokens 4g..4g+3 of page pg going to slots 8g + 4pg ..
-// +3 (the B operand order of the weights).  512 items of each kind.
+// Keys: item (key, 8 coordinates), the key fastest along the lanes (the
+// record bytes the lanes read then lie in distinct banks); values: item
+// (coordinate, page, half of the page's tokens), tokens 4g..4g+3 of page pg
+// going to slots 8g + 4pg .. +3 (the B operand order of the weights).  512
+// items of each kind.
 __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage], const uint8_t (*rawv)[kVPage],
                                            int tid, const uint32_t (&th)[4], const uint32_t (&tl)[4]) {
 #pragma unroll
   for (int it = tid; it < 512; it += kThreads) {
-    const int key = it >> 4, p16 = it & 15, pg = key >> 4, tok = key & 15;
+    const int tok = it & 15, p16 = (it >> 4) & 15, pg = it >> 8;
     const uint8_t *pk = rawk[pg];
     // byte p16 of a token's 128-bit field: coordinates (rows) 8 p16 .. +7, in
     // byte p16 % 4 of that field's word of the record of chunk p16 / 4
@@ -129,13 +134,15 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
       sv[2 * q] = sign_pair(ws, 4 * q);
       sv[2 * q + 1] = sign_pair(ws, 4 * q + 2);
     }
-    *reinterpret_cast<uint4 *>(&T.kh[key][8 * p16]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-    *reinterpret_cast<uint4 *>(&T.kl[key][8 * p16]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
-    *reinterpret_cast<uint4 *>(&T.ks[key][8 * p16]) = make_uint4(sv[0], sv[1], sv[2], sv[3]);
+    // coordinates 8 p16 .. +7 = block p16 / 4, lane group p16 % 4
+    const int kc = p16 >> 2, ln = 16 * (p16 & 3) + tok;
+    *reinterpret_cast<uint4 *>(&T.kh[pg][kc][ln]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    *reinterpret_cast<uint4 *>(&T.kl[pg][kc][ln]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+    *reinterpret_cast<uint4 *>(&T.ks[pg][kc][ln]) = make_uint4(sv[0], sv[1], sv[2], sv[3]);
   }
 #pragma unroll
   for (int it = tid; it < 512; it += kThreads) {
-    const int c = it >> 2, pg = (it >> 1) & 1, th8 = it & 1;
+    const int r = it & 15, pg = (it >> 4) & 1, th8 = (it >> 5) & 1, cv = it >> 6, c = 16 * cv + r;
     const uint8_t *pv = rawv[pg];
     const uint32_t w0 = pv[kVPlane * 0 + 2 * c + th8];
     const uint32_t w1 = pv[kVPlane * 1 + 2 * c + th8];
@@ -144,8 +151,11 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
     for (int q = 0; q < 2; ++q) {
       const int g = 2 * th8 + q;
       const uint32_t sel = code_bytes(w0, w1, w2, 4 * q);
-      *reinterpret_cast<uint2 *>(&T.vh[c][8 * g + 4 * pg]) = lut4(sel, th[0], th[1], th[2], th[3]);
-      *reinterpret_cast<uint2 *>(&T.vl[c][8 * g + 4 * pg]) = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
+      // slots 8 g + 4 pg .. +3: half 4 pg of lane (g, r)'s piece
+      _Float16 *vh = reinterpret_cast<_Float16 *>(&T.vh[cv][16 * g + r]) + 4 * pg;
+      _Float16 *vl = reinterpret_cast<_Float16 *>(&T.vl[cv][16 * g + r]) + 4 * pg;
+      *reinterpret_cast<uint2 *>(vh) = lut4(sel, th[0], th[1], th[2], th[3]);
+      *reinterpret_cast<uint2 *>(vl) = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
     }
   }
   if (tid < kKeys) {
@@ -311,9 +321,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const v8h ah = *reinterpret_cast<const v8h *>(&T.kh[16 * ct + l16][32 * kc + 8 * g4]);
-        const v8h al = *reinterpret_cast<const v8h *>(&T.kl[16 * ct + l16][32 * kc + 8 * g4]);
-        const v8h as = *reinterpret_cast<const v8h *>(&T.ks[16 * ct + l16][32 * kc + 8 * g4]);
+        const v8h ah = T.kh[ct][kc][lane];
+        const v8h al = T.kl[ct][kc][lane];
+        const v8h as = T.ks[ct][kc][lane];
 #pragma unroll
         for (int u = 0; u < kRowTiles; ++u) {
           cc[u][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[u][kc], cc[u][ct], 0, 0, 0);
@@ -390,8 +400,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     // ---- O^T += V^T W^T: A = value levels [coordinate][slot] -------------
 #pragma unroll
     for (int cv = 0; cv < 8; ++cv) {
-      const v8h vh = *reinterpret_cast<const v8h *>(&T.vh[16 * cv + l16][8 * g4]);
-      const v8h vl = *reinterpret_cast<const v8h *>(&T.vl[16 * cv + l16][8 * g4]);
+      const v8h vh = T.vh[cv][lane];
+      const v8h vl = T.vl[cv][lane];
 #pragma unroll
       for (int u = 0; u < kRowTiles; ++u) {
         acc[u][cv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, wb[u], acc[u][cv], 0, 0, 0);
