@@ -120,11 +120,12 @@ def encode_bytes(n_tokens, hkv, in_elem=2):
 # ---------------------------------------------------------------------------
 # headline: continuous-batching decode step
 
-def batch_setup(tq, cb, dev, total_steps):
+def batch_setup(tq, cb, dev, total_steps, hq=HQ3, hkv=HKV3):
     """Pools (replicas) holding the 16 ragged sequences, the per-step new
     tokens, their slots and context lengths, all resident on the device."""
     import torch
     import synth
+    HQ3, HKV3 = hq, hkv  # the step's head counts (locals shadowing the defaults)
     rng = np.random.default_rng(SEED3)
     L = synth.ragged_lengths(rng, B3)
     per_replica = int(L.sum()) * HKV3 * (K_PAGE + V_PAGE) // 16
@@ -162,10 +163,11 @@ def batch_setup(tq, cb, dev, total_steps):
                 table_np=table_np)
 
 
-def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples):
+def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples, hq=HQ3, hkv=HKV3):
     import torch
+    HQ3, HKV3 = hq, hkv  # the step's head counts (locals shadowing the defaults)
     total = warmup + steps + 2 * (warmup + samples)
-    st = batch_setup(tq, cb, dev, total)
+    st = batch_setup(tq, cb, dev, total, hq, hkv)
     out = torch.empty((B3, 1, HQ3, D), dtype=torch.float32, device=dev)
     # one buffer serves the step calls and the breakdown's attention calls
     ws = torch.empty(max(tq.tq_decode_step_workspace_bytes(cb, B3, HQ3, HKV3, st["max_ctx"]),
@@ -244,6 +246,19 @@ def batch_step_bench(tq, cb, dev, stream, steps, warmup, samples):
         mean_attention_us=float(np.mean(dec_us)), attention_bytes=dec_b, samples=samples)
     del st
     return res
+
+
+def step_gqa32q4kv(tq, cb, dev, stream, steps=100, warmup=10, samples=50):
+    """The same continuous-batching step with 32 query heads over 4 KV heads
+    (8 per KV head: the step's split pass runs two waves per run of tiles,
+    one head tile each)."""
+    r = batch_step_bench(tq, cb, dev, stream, steps, warmup, samples, hq=32, hkv=4)
+    v = r["bytes_per_step"] / r["s_per_step"] / 1e9
+    return {"workload": "continuous-batching decode step as the headline (same lengths and tables), GQA 32q/4kv",
+            "q_heads": 32, "kv_heads": 4, "algorithmic_bytes_per_step": round(r["bytes_per_step"]),
+            "us_per_step": round(r["s_per_step"] * 1e6, 2), "GBps": round(v, 1),
+            "pct_peak": round(100 * v / HBM_PEAK_GBPS, 2), "median_step_us": round(r["median_step_us"], 2),
+            "two_calls_median_step_us": round(r["two_calls_median_step_us"], 2)}
 
 
 # ---------------------------------------------------------------------------
@@ -852,6 +867,7 @@ def main():
     ap.add_argument("--hot-window-only", action="store_true")
     ap.add_argument("--window-only", action="store_true")
     ap.add_argument("--bits-only", action="store_true")
+    ap.add_argument("--step-32q4kv-only", action="store_true")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
@@ -894,6 +910,10 @@ def main():
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_bench(tq, cb, dev, stream, reps=args.steps, warmup=args.warmup)}))
         return
+    if args.step_32q4kv_only:
+        print(json.dumps({"decode_step_gqa32q4kv": step_gqa32q4kv(tq, cb, dev, stream, steps=args.steps,
+                                                                  warmup=args.warmup)}))
+        return
 
     extra = {}
     if not args.headline_only:
@@ -903,6 +923,7 @@ def main():
                  ("attention_verify", lambda: verify_attention(tq, cb, dev, stream)),
                  ("attention_hot_window", lambda: hot_window_attention(tq, cb, dev, stream)),
                  ("attention_window", lambda: window_attention(tq, cb, dev, stream)),
+                 ("decode_step_gqa32q4kv", lambda: step_gqa32q4kv(tq, cb, dev, stream)),
                  ("bits_variants", lambda: bits_variants(tq, dev, stream)))
         for key, run in sides:
             extra[key] = run()
