@@ -54,9 +54,9 @@ struct Tile {
   v8h ks[2][4][64];                // QJL signs +-1
   v8h vh[8][64];                   // value levels x16, hi: [coordinate tile][lane]
   v8h vl[8][64];                   // lo
-  float kn[kKeys];                 // n_k / 16
-  float kg[kKeys];                 // n_k gamma
-  float vn[kKeys];                 // n_v
+  float kn[2 * kKeys];             // n_k / 16 (entries past kKeys: copies no one reads)
+  float kg[2 * kKeys];             // n_k gamma
+  float vn[2 * kKeys];             // n_v
 };
 
 // Two steps in flight: the tiles of step i are read while those of step
@@ -102,16 +102,18 @@ constexpr int kRowTiles = 1;                  // 16-row tiles per wave (each sha
 constexpr int kRows = 16 * kRowTiles * kWaves;  // query rows per workgroup
 static_assert(kRows == kPrefillRows, "the host plans prefill blocks of kPrefillRows rows");
 
-// Dequantize a step's staged pages into T (all threads of the workgroup).
-// Keys: item (key, 8 coordinates), the key fastest along the lanes (the
-// record bytes the lanes read then lie in distinct banks); values: item
-// (coordinate, page, half of the page's tokens), tokens 4g..4g+3 of page pg
-// going to slots 8g + 4pg .. +3 (the B operand order of the weights).  512
-// items of each kind.
+// Dequantize a step's staged pages into T (all threads of the workgroup, one
+// item of each kind per thread, no branch: the step's matrix ops and this
+// vector work then share one basic block and interleave).  Keys: item (key,
+// 8 coordinates), the key fastest along the lanes (the record bytes the
+// lanes read then lie in distinct banks); values: item (coordinate, page,
+// half of the page's tokens), tokens 4g..4g+3 of page pg going to slots 8g +
+// 4pg .. +3 (the B operand order of the weights).  512 items of each kind.
+static_assert(kThreads == 512, "one dequantization item of each kind per thread");
 __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage], const uint8_t (*rawv)[kVPage],
                                            int tid, const uint32_t (&th)[4], const uint32_t (&tl)[4]) {
-#pragma unroll
-  for (int it = tid; it < 512; it += kThreads) {
+  {
+    const int it = tid;
     const int tok = it & 15, p16 = (it >> 4) & 15, pg = it >> 8;
     const uint8_t *pk = rawk[pg];
     // byte p16 of a token's 128-bit field: coordinates (rows) 8 p16 .. +7, in
@@ -140,8 +142,8 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
     *reinterpret_cast<uint4 *>(&T.kl[pg][kc][ln]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
     *reinterpret_cast<uint4 *>(&T.ks[pg][kc][ln]) = make_uint4(sv[0], sv[1], sv[2], sv[3]);
   }
-#pragma unroll
-  for (int it = tid; it < 512; it += kThreads) {
+  {
+    const int it = tid;
     const int r = it & 15, pg = (it >> 4) & 1, th8 = (it >> 5) & 1, cv = it >> 6, c = 16 * cv + r;
     const uint8_t *pv = rawv[pg];
     const uint32_t w0 = pv[kVPlane * 0 + 2 * c + th8];
@@ -158,12 +160,14 @@ __device__ __forceinline__ void dequantize(Tile &T, const uint8_t (*rawk)[kKPage
       *reinterpret_cast<uint2 *>(vl) = lut4(sel, tl[0], tl[1], tl[2], tl[3]);
     }
   }
-  if (tid < kKeys) {
-    const int pg = tid >> 4, tok = tid & 15;
+  {
+    // threads 0..31 the 32 keys' norms; threads 32..63 copies to the unread
+    // half (every thread past 63 repeats thread tid % 64's store)
+    const int e = tid & (2 * kKeys - 1), pg = (e >> 4) & 1, tok = e & 15;
     const float nk = half_at(&rawk[pg][kKNorm + 2 * tok]);
-    T.kn[tid] = nk * (1.0f / kTabScale);
-    T.kg[tid] = nk * half_at(&rawk[pg][kKGamma + 2 * tok]);
-    T.vn[tid] = half_at(&rawv[pg][kVNorm + 2 * tok]);
+    T.kn[e] = nk * (1.0f / kTabScale);
+    T.kg[e] = nk * half_at(&rawk[pg][kKGamma + 2 * tok]);
+    T.vn[e] = half_at(&rawv[pg][kVNorm + 2 * tok]);
   }
 }
 
@@ -306,9 +310,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
     // pages of step st + 1 are staged
     lds_barrier();
     raw = load_raw(k0 + 2 * kKeys);
-    // tiles of step st + 1 (past the last step: unused), written while this
-    // step's are read, so that vector and matrix work can interleave
-    dequantize(S.d[(st + 1) & 1], S.rawk[(st + 1) & 1], S.rawv[(st + 1) & 1], tid, th, tl);
 
     // ---- S^T = K Q^T for this wave's rows: lane l, register i of key tile
     // ct holds key 16 ct + 4 (l / 16) + i of row l % 16 of row tile u
@@ -334,6 +335,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
         }
       }
     }
+    // tiles of step st + 1 (past the last step: unused), written while this
+    // step's are read: independent of the score chains above, so their
+    // vector work runs while the matrix cores do
+    dequantize(S.d[(st + 1) & 1], S.rawk[(st + 1) & 1], S.rawv[(st + 1) & 1], tid, th, tl);
 #pragma unroll
     for (int u = 0; u < kRowTiles; ++u) {
 #pragma unroll
@@ -377,11 +382,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(DecodeArgs a)
       // m_run = -inf: nothing accumulated yet (acc and l are zero)
       const float f = m_run[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
       m_run[u] = m_new;
-      if (__ballot(f != 1.0f)) {  // wave-uniform: the maximum moved in some row
-        l_part[u] *= f;
+      // f = 1 (exact) where the row's maximum did not move: no branch
+      l_part[u] *= f;
 #pragma unroll
-        for (int cv = 0; cv < 8; ++cv) acc[u][cv] *= f;
-      }
+      for (int cv = 0; cv < 8; ++cv) acc[u][cv] *= f;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
