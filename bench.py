@@ -73,10 +73,17 @@ B3, HQ3, HKV3, SEED3 = 16, 32, 8, 3
 METRIC = "compressed-KV decode attention effective HBM GB/s (% peak); encode vectors/s"
 
 
-def kernel_source_hash():
+# the sources each counted launch is built from (its counters go stale when one changes)
+TRAFFIC_SOURCES = {
+    "encode_kernel": ("tq_encode.hip", "tq_append.hpp", "tq_common.hpp", "tq_internal.h", "tq_host.cpp"),
+    "decode_step_call": ("tq_decode.hip", "tq_append.hpp", "tq_common.hpp", "tq_mfma.hpp", "tq_internal.h",
+                         "tq_host.cpp"),
+}
+
+
+def kernel_source_hash(key):
     h = hashlib.sha256()
-    for f in ("tq_encode.hip", "tq_decode.hip", "tq_prefill.hip", "tq_common.hpp", "tq_mfma.hpp",
-              "tq_internal.h", "tq_host.cpp"):
+    for f in TRAFFIC_SOURCES[key]:
         with open(os.path.join(ROOT, "decode_attention_tq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -91,7 +98,7 @@ def load_traffic(key: str):
     except (OSError, ValueError):
         return None
     k = rec.get(key)
-    if not k or k.get("source_hash") != kernel_source_hash():
+    if not k or k.get("source_hash") != kernel_source_hash(key):
         return None
     return k.get("hbm_bytes_per_launch")
 
@@ -627,10 +634,9 @@ def traffic_from(fetch_csv, write_csv):
     def med(by, needle, scale):
         vals = sorted(v for n, vs in by.items() if needle in n for v in vs)
         return vals[len(vals) // 2] * scale if vals else None
-    h = kernel_source_hash()
     rec = {}
     enc_f, enc_w = med(f, "encode_kernel", fs), med(w, "encode_kernel", wsc)
-    rec["encode_kernel"] = {"source_hash": h, "workload": "one 8192-token layer, 8 KV heads",
+    rec["encode_kernel"] = {"source_hash": kernel_source_hash("encode_kernel"), "workload": "one 8192-token layer, 8 KV heads",
                             "hbm_bytes_per_launch": round(enc_f + enc_w), "fetch_bytes": round(enc_f),
                             "write_bytes": round(enc_w), "algorithmic_bytes": encode_bytes(T2, HKV2)}
     parts = {}
@@ -641,7 +647,7 @@ def traffic_from(fetch_csv, write_csv):
     import synth
     L = synth.ragged_lengths(np.random.default_rng(SEED3), B3)
     tot = sum(p["fetch_bytes"] + p["write_bytes"] for p in parts.values())
-    rec["decode_step_call"] = {"source_hash": h, "workload": "decode step of 16 ragged sequences, 32q/8kv",
+    rec["decode_step_call"] = {"source_hash": kernel_source_hash("decode_step_call"), "workload": "decode step of 16 ragged sequences, 32q/8kv",
                                "hbm_bytes_per_launch": round(tot), "kernels": parts,
                                "algorithmic_bytes_at_cached_lengths": decode_bytes(L + 1, HQ3, HKV3)
                                + encode_bytes(B3, HKV3)}
