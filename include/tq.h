@@ -181,10 +181,15 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
  *               query block (at most 4 groups of 8 / group positions) uses
  *               at most 8192 tokens per chunk.
  *   workspace   device scratch of tq_decode_workspace_bytes() bytes (same
- *               arguments); contents on entry do not matter.
+ *               arguments); contents on entry do not matter.  16-byte
+ *               aligned for a verify block of 9 to 32 query rows per KV
+ *               head (q_len x Hq / Hkv, with tokens_per_split 0), whose
+ *               query operands the library forms in a launch of their own
+ *               and keeps in the workspace.
  * Any group size num_q_heads / num_kv_heads from 1 to 16 is accepted.
  * Errors: TQ_ERR_INVALID_ARGUMENT (nulls, Hq % Hkv != 0, q_len < 1,
- * q_len > max_context_len, bad tokens_per_split), TQ_ERR_UNSUPPORTED
+ * q_len > max_context_len, bad tokens_per_split, a misaligned workspace
+ * where alignment is required), TQ_ERR_UNSUPPORTED
  * (num_q_heads / num_kv_heads > 16, or tokens_per_split above 8192 where the
  * chunk limit above applies), TQ_ERR_WORKSPACE_TOO_SMALL. */
 size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
@@ -305,14 +310,16 @@ tq_status tq_decode_attention_window(const tq_codebook *cb, const void *q, tq_dt
  *                NULL, stream)
  * followed by tq_decode_attention(..., q_len = 1, ...) with the remaining
  * arguments, on `stream`: the cache contents are bit-identical to those two
- * calls'.  With 3-bit codes, up to 4 query heads per KV head and at most
+ * calls'.  With 3-bit codes, up to 8 query heads per KV head and at most
  * 1,024 new (token, KV head) vectors it runs fused, in three launches
  * instead of four: the append shares its launch with the attention's
  * per-(sequence, KV head) query set-up, and the split pass gives every wave
  * an equal share of all the batch's tiles (tokens_per_split is not used);
- * the output then equals the two calls' up to fp32 rounding (the softmax is
- * combined from other partial records).  Otherwise it runs the two calls'
- * launches and the output is bit-identical.
+ * the output then equals the two calls' up to the rounding of the softmax
+ * combine (fp32 with up to 4 heads per KV head; with 5 to 8, within the
+ * weights' 15-bit rounding, since the separate call then runs another
+ * split pass).  Otherwise it runs the two calls' launches and the output
+ * is bit-identical.
  *   k_new, v_new  device, element (b, h, i) of sequence b's new token at
  *               k_new[b*tok_stride + h*head_stride + i], as in tq_encode_kv.
  *   slot_mapping device int64[num_seqs]: the slot of sequence b's new token

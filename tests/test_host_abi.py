@@ -138,6 +138,10 @@ def test_decode_validation():
     need = tq._lib.tq_decode_workspace_bytes(ctypes.byref(cb), 1, 1, 32, 8, 1024, 0)
     assert need > 0
     assert _dec(cb, wsb=need - 1) == tq.TQ_ERR_WORKSPACE_TOO_SMALL
+    # a verify block of 16 query rows per KV head (4 positions x 4 heads) keeps
+    # its query operands in the workspace: it must be 16-byte aligned
+    assert _dec(cb, q_len=4, ws=FAKE + 8) == E
+    assert "aligned" in tq.tq_last_error()
 
 
 def _prep_words(B, q_len, Hq, Hkv):
