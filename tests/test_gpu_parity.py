@@ -302,6 +302,36 @@ def test_multi_token_verify(q_len, Hq, Hkv):
     check_decode(out, q, _np(kpool), _np(vpool), table, lens.astype(np.int32))
 
 
+def test_verify_blocks_on_the_stream_plan_sweep():
+    """Seeded sweep of verify blocks that run the stream plan (9 to 32 query
+    rows per KV head, one wave per head tile of four (position, head) rows):
+    random group sizes (1 to 8), block lengths and KV head counts over
+    ragged batches holding a sequence exactly as long as the block, one
+    shorter than a tile and one of several tiles with a ragged tail; every
+    row against the oracle."""
+    rng = np.random.default_rng(91)
+    cb = codebook()
+    done = 0
+    while done < 8:
+        G = int(rng.integers(1, 9))
+        Hkv = int(rng.choice([1, 2, 4]))
+        q_len = int(rng.integers(2, 4 * (8 // G) + 1))  # at most four launches' worth of positions
+        if G * q_len <= 8:
+            continue
+        lens = np.array([q_len, int(rng.integers(q_len, 128)), int(rng.integers(300, 3000))], dtype=np.int64)
+        table, nb = synth.block_tables(rng, lens)
+        kpool, vpool = new_pools(nb, Hkv)
+        for b in range(len(lens)):
+            k = synth.kv_tensor(rng, int(lens[b]), Hkv)
+            v = synth.kv_tensor(rng, int(lens[b]), Hkv)
+            encode_gpu(cb, k, v, synth.slots_for(table, b, np.arange(lens[b])), kpool, vpool, with_norms=False)
+        q = synth.queries(rng, len(lens), q_len, G * Hkv)
+        print(f"G {G} Hkv {Hkv} q_len {q_len} lens {lens.tolist()}", flush=True)
+        out = decode_gpu(cb, q, kpool, vpool, table, lens.astype(np.int32), Hkv)
+        check_decode(out, q, _np(kpool), _np(vpool), table, lens.astype(np.int32))
+        done += 1
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 4), (32, 2)])
 def test_prefill_groups_batches_and_splits(Hq, Hkv):
     """Several queries per sequence for every supported group size (1, 2, 8,
