@@ -648,10 +648,11 @@ __device__ __forceinline__ v8i fp6_operand(const uint16_t *p, float div) {
 // of the group.  Its output row is (b q_len + t) Hq + h G + g, and it sees
 // the keys before L - q_len + t + 1 (multi-token verify is causal over the
 // new ones).
+// (The host bounds the group index below 2^31: 32-bit division.)
 __device__ __forceinline__ int64_t query_out_row(const DecodeArgs &a, int64_t grp, int row) {
   const int G = a.group;
-  const int64_t b = grp / a.num_kv_heads, h = grp % a.num_kv_heads;
-  return (b * a.q_len + a.pos0 + row / G) * a.num_q_heads + h * G + row % G;
+  const int g32 = (int)grp, b = g32 / a.num_kv_heads, h = g32 - b * a.num_kv_heads;
+  return ((int64_t)b * a.q_len + a.pos0 + row / G) * a.num_q_heads + h * G + row % G;
 }
 
 
@@ -708,11 +709,13 @@ __device__ __forceinline__ void qprep_loads(const DecodeArgs &a, int64_t grp, in
 }
 
 // The operands, for the head tiles NU the calling wave scores (every wave of
-// the workgroup runs this; it ends on a barrier after which the scratch space
-// may be reused).  Wave w rotates and digitises head w of the workgroup's
-// heads, which start at query row hbase of the group (a head tile of its own
-// when a separate launch forms one tile's operands).
-template <int T, int NU, bool PACK, bool PROJ>
+// the workgroup runs this; with TAIL it ends on a barrier after which the
+// scratch space may be reused).  Wave w rotates and digitises head w of the
+// workgroup's heads, which start at query row hbase of the group (a head tile
+// of its own when a separate launch forms one tile's operands).  The
+// operands and start values of code planes 0..3 are formed as soon as their
+// digits are (beside the projection); the sign plane's once s is.
+template <int T, int NU, bool PACK, bool PROJ, bool TAIL = true>
 __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &L, const QPrepRegs<PROJ> &R, int tid,
                                               int wave, const int (&tiles)[NU], v8i (&Aq)[NU][5],
                                               int (&scq)[NU][5], v4f (&cinit)[NU], v4f (&qinit)[NU],
@@ -782,6 +785,32 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
     }
   }
   lds_barrier();
+  // this lane's operand rows: (head 4u + gp, digit r), K-block ga.  The
+  // start values (see b_split), sum_k (1 - f_v alpha_v) A_k = -sum_k w_v A_k
+  // with w_v = 5, 3, 1, 0, are two matrix ops per plane against the constant
+  // operands -(4, 3, 1, 0) and -(1, 0, 0, 0) (e2m1 codes E, D, A and A).
+  const int ga = lane >> 4, gp = (lane & 15) >> 2, r = lane & 3;
+  const v8i W1 = v8i{(int)0xEEEEEEEEu, (int)0xDDDDDDDDu, (int)0xAAAAAAAAu, 0, 0, 0, 0, 0};
+  const v8i W2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
+  auto pack_plane = [&](int n, int p) __attribute__((always_inline)) {
+    const int hd = 4 * tiles[n] + gp;
+    // the 32 digit values of K slots 32 ga .. +31, as codes of d / 8
+    Aq[n][p] = fp6_operand(reinterpret_cast<const uint16_t *>(&L.codes[hd][p][r][32 * ga]), 8.0f);
+    const int E = L.pe[hd][p];
+    scq[n][p] = E != INT_MIN ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One;
+  };
+#pragma unroll
+  for (int n = 0; n < (PACK ? NU : 0); ++n) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) pack_plane(n, p);
+    v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      c = mfma_f6f4(Aq[n][p], W1, c, scq[n][p]);
+      c = mfma_f6f4(Aq[n][p], W2, c, scq[n][p]);
+    }
+    cinit[n] = c;
+  }
   if constexpr (PROJ) {
     // s = alpha (S H) q' for rows 32 w .. 32 w + 31, all heads: three f16
     // passes (hi hi + hi lo + lo hi, ~22 bits); A rows past the heads are zero
@@ -826,34 +855,13 @@ __device__ __forceinline__ void qprep_compute(const DecodeArgs &a, QPrepLds<T> &
     }
   }
   lds_barrier();
-  // this lane's operand rows: (head 4u + gp, digit r), K-block ga.  The
-  // start values (see b_split), sum_k (1 - f_v alpha_v) A_k = -sum_k w_v A_k
-  // with w_v = 5, 3, 1, 0, are two matrix ops per plane against the constant
-  // operands -(4, 3, 1, 0) and -(1, 0, 0, 0) (e2m1 codes E, D, A and A).
-  const int ga = lane >> 4, gp = (lane & 15) >> 2, r = lane & 3;
-  const v8i W1 = v8i{(int)0xEEEEEEEEu, (int)0xDDDDDDDDu, (int)0xAAAAAAAAu, 0, 0, 0, 0, 0};
-  const v8i W2 = v8i{(int)0xAAAAAAAAu, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int n = 0; n < (PACK ? NU : 0); ++n) {
-    const int hd = 4 * tiles[n] + gp;
-#pragma unroll
-    for (int p = 0; p < 5; ++p) {
-      // the 32 digit values of K slots 32 ga .. +31, as codes of d / 8
-      Aq[n][p] = fp6_operand(reinterpret_cast<const uint16_t *>(&L.codes[hd][p][r][32 * ga]), 8.0f);
-      const int E = L.pe[hd][p];
-      scq[n][p] = E != INT_MIN ? min(E - 4 - 5 * r + kFp6Exp + kE8M0One, 254) : kE8M0One;
-    }
-    v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      c = mfma_f6f4(Aq[n][p], W1, c, scq[n][p]);
-      c = mfma_f6f4(Aq[n][p], W2, c, scq[n][p]);
-    }
-    cinit[n] = c;
+    pack_plane(n, 4);
     const v4f z = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     qinit[n] = mfma_f6f4(Aq[n][4], W2, mfma_f6f4(Aq[n][4], W1, z, scq[n][4]), scq[n][4]);
   }
-  lds_barrier();  // the scratch space is free again
+  if constexpr (TAIL) lds_barrier();  // the scratch space is free again
 }
 
 
@@ -2149,7 +2157,7 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
   int scq[1][5];
   v4f ci[1], qi[1];
   const int tiles[1] = {0};
-  qprep_compute<1, 1, true, true>(a, sm.q, qpr, tid, wave, tiles, Aq, scq, ci, qi, hbase);
+  qprep_compute<1, 1, true, true, false>(a, sm.q, qpr, tid, wave, tiles, Aq, scq, ci, qi, hbase);
   if (wave == 0) {
     uint32_t w[kQopsDwords];
 #pragma unroll
