@@ -1596,36 +1596,44 @@ __device__ __forceinline__ int stream_per(const DecodeArgs &a, int N) {
   const int64_t waves = 4 * a.bal_target;
   return (int)min<int64_t>(max<int64_t>(((int64_t)stream_pair(a) * N + waves - 1) / waves, 1), kStreamMaxTiles);
 }
-// Per lane: sequence b, KV head h and tile t of global tile c (0 <= c < N)
-// and the sequence's context length L.  Every lane of the wave takes part.
-__device__ __forceinline__ void stream_locate(const DecodeArgs &a, int t0, int L0, int c, int &b, int &h, int &t,
-                                              int &L) {
-  const int lane = threadIdx.x & 63, H = a.num_kv_heads;
-  int run = 0;
-  b = h = t = L = 0;
+// Per lane: sequence b, KV head h and tile t of global tile cb + min(koff +
+// lane / 8, nt - 1) (a wave's slot of its run; cb, koff, nt wave-uniform,
+// every tile < N) and the sequence's context length L.  Every lane of the
+// wave takes part.  The eight slots' tiles are wave-uniform, so each finds
+// its sequence with one ballot (the lanes j with excl_j <= c, excl not
+// decreasing along the lanes), with no exchange between lanes.
+__device__ __forceinline__ void stream_locate(const DecodeArgs &a, int t0, int L0, int cb, int koff, int nt, int &b,
+                                              int &h, int &t, int &L) {
+  const int lane = threadIdx.x & 63, H = a.num_kv_heads, mine = lane >> 3;
+  int run = 0, sc = 0, se = 0, sT = 1;
+  b = L = 0;
   for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {  // uniform
     const int Ll = c0 == 0 ? L0 : lane_context(a, c0 + lane);
     const int T = c0 == 0 ? t0 : span_tiles(a, Ll);
     const int incl = wave_incl_scan_int(H * T, lane) + run;
     const int excl = incl - H * T;
-    // the last lane j with excl_j <= c (excl does not decrease along the lanes)
-    int j = 0;
-#pragma unroll
-    for (int st = 32; st > 0; st >>= 1)
-      if (__builtin_amdgcn_ds_bpermute(4 * (j + st), excl) <= c) j += st;
-    const int ej = __builtin_amdgcn_ds_bpermute(4 * j, excl);
-    const int Tj = __builtin_amdgcn_ds_bpermute(4 * j, T);
-    const int Lj = __builtin_amdgcn_ds_bpermute(4 * j, Ll);
     const int end = __builtin_amdgcn_readlane(incl, 63);
-    if (c >= run && c < end) {  // this lane's tile lies in this block (then Tj > 0)
-      b = c0 + j;
-      const int rel = c - ej;
-      h = rel / Tj;
-      t = rel - h * Tj;
-      L = Lj;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = cb + min(koff + k, nt - 1);  // uniform
+      if (c >= run && c < end) {  // uniform: slot k's tile lies in this block (then T_j > 0)
+        const int j = __builtin_popcountll(__ballot(excl <= c)) - 1;
+        const int ej = __builtin_amdgcn_readlane(excl, j), Tj = __builtin_amdgcn_readlane(T, j);
+        const int Lj = __builtin_amdgcn_readlane(Ll, j);
+        if (mine == k) {
+          b = c0 + j;
+          L = Lj;
+          sc = c;
+          se = ej;
+          sT = Tj;
+        }
+      }
     }
     run = end;
   }
+  const int rel = sc - se;
+  h = rel / sT;
+  t = rel - h * sT;
 }
 // Exclusive prefix P_b = H sum_{b'<b} T_b' and T_b of sequence b (uniform b).
 __device__ __forceinline__ void stream_prefix(const DecodeArgs &a, int t0, int b, int &P, int &Tb) {
@@ -1641,6 +1649,46 @@ __device__ __forceinline__ void stream_prefix(const DecodeArgs &a, int t0, int b
     }
     run = __builtin_amdgcn_readlane(incl, 63);
   }
+}
+
+// The descriptor of wave `wave` of workgroup `blk` of the split pass's grid
+// (all lanes of one wave call this): its run of tiles on the stream plan,
+// the block ids of its tile slots (as the split pass loads pages: lane l
+// holds page l % 8 of slot l / 8 in ids0 and of slot 8 + l / 8 in ids1; a
+// page past the keys re-reads its tile's first page, a slot past the wave's
+// last tile repeats that tile) and the slots' (sequence, KV head, tile,
+// length).  Words: [0, 64) ids0, [64, 128) ids1, [128, 192) the 16 slots,
+// [192, 196) (tiles, run, head tile, 0); tiles 0: no work for the wave.
+__device__ __forceinline__ void stream_describe(const DecodeArgs &a, int blk, int wave) {
+  const int lane = threadIdx.x & 63;
+  const int Lw = lane_context(a, lane);
+  const int t0s = span_tiles(a, Lw);
+  const int N = stream_total(a, t0s);
+  const int q = stream_per(a, N);
+  const int P = stream_pair(a);
+  const int nwg = (P * ((N + q - 1) / q) + 3) >> 2;
+  const int x = blk & 7, rpos = xcd_run_start(x, nwg) + (blk >> 3);
+  int ntiles = 0, iw = 0, ut = 0;
+  if (rpos < xcd_run_start(x + 1, nwg)) {  // uniform
+    iw = (4 * rpos + wave) / P;
+    ut = (4 * rpos + wave) - iw * P;
+    ntiles = max(min(q, N - iw * q), 0);
+  }
+  uint32_t *d = a.desc + ((int64_t)blk * 4 + wave) * kDescWords;
+  if (ntiles > 0) {  // uniform
+    const int e = lane & 7;
+    auto slot_ids = [&](int koff) __attribute__((always_inline)) {
+      int sb, sh, st, sl;
+      stream_locate(a, t0s, Lw, iw * q, koff, ntiles, sb, sh, st, sl);
+      const int tile0 = seq_base(a, sl) + 128 * st, tok = tile0 + 16 * e;
+      if (e == 0) reinterpret_cast<int4 *>(d + 128)[koff + (lane >> 3)] = make_int4(sb, sh, st, sl);
+      const int id = a.block_tables[(int64_t)sb * a.max_blocks + page_entry(a, (tok < sl ? tok : tile0) >> 4)];
+      return id * a.num_kv_heads + sh;
+    };
+    d[lane] = (uint32_t)slot_ids(0);
+    d[64 + lane] = (uint32_t)slot_ids(8);
+  }
+  if (lane == 0) *reinterpret_cast<int4 *>(d + 192) = make_int4(ntiles, iw, ut, 0);
 }
 
 // One reference R per head serves the scores and the accumulators: it moves
@@ -1708,29 +1756,18 @@ __global__ __launch_bounds__(256 * T, T == 1 ? 2 : 1) void split_wave_kernel(Dec
   // are masked)
   int ids0, ids1;
   if constexpr (STREAM) {
-    const int Lw = lane_context(a, lane);
-    const int t0s = span_tiles(a, Lw);
-    const int N = stream_total(a, t0s);
-    const int q = stream_per(a, N);
-    const int P = stream_pair(a);
-    const int nwg = (P * ((N + q - 1) / q) + 3) >> 2;
-    const int x = (int)blockIdx.x & 7, rpos = xcd_run_start(x, nwg) + ((int)blockIdx.x >> 3);
-    if (rpos >= xcd_run_start(x + 1, nwg)) return;  // uniform: no waves in this workgroup
-    iw = (4 * rpos + wave) / P;
-    ut = (4 * rpos + wave) - iw * P;
-    ntiles = min(q, N - iw * q);
-    if (ntiles <= 0) return;  // uniform: past the last tile (this plan has no workgroup barrier)
-    const int e = lane & 7;
-    auto slot_ids = [&](int k) __attribute__((always_inline)) {
-      int sb, sh, st, sl;
-      stream_locate(a, t0s, Lw, iw * q + min(k, ntiles - 1), sb, sh, st, sl);
-      const int tile0 = seq_base(a, sl) + 128 * st, tok = tile0 + 16 * e;
-      if (e == 0) slot_sh[wave][k] = make_int4(sb, sh, st, sl);
-      const int id = a.block_tables[(int64_t)sb * a.max_blocks + page_entry(a, (tok < sl ? tok : tile0) >> 4)];
-      return id * a.num_kv_heads + sh;
-    };
-    ids0 = slot_ids(lane >> 3);
-    ids1 = slot_ids(8 + (lane >> 3));
+    // the wave's descriptor, formed by the operands launch: every load at
+    // once (the descriptor exists for every wave of the grid)
+    const uint32_t *d = a.desc + ((int64_t)blockIdx.x * 4 + wave) * kDescWords;
+    const int4 meta = *reinterpret_cast<const int4 *>(d + 192);
+    ids0 = (int)d[lane];
+    ids1 = (int)d[64 + lane];
+    const int4 sl = reinterpret_cast<const int4 *>(d + 128)[lane & 15];
+    ntiles = __builtin_amdgcn_readfirstlane(meta.x);
+    if (ntiles <= 0) return;  // uniform: no run for this wave (this plan has no workgroup barrier)
+    iw = __builtin_amdgcn_readfirstlane(meta.y);
+    ut = __builtin_amdgcn_readfirstlane(meta.z);
+    if (lane < kStreamMaxTiles) slot_sh[wave][lane] = sl;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const int4 f0 = slot_sh[wave][0];
     b = __builtin_amdgcn_readfirstlane(f0.x);
@@ -2143,9 +2180,12 @@ __global__ __launch_bounds__(256, 2) void step_prep_kernel(EncodeArgs ea, Decode
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wg >= n_append + n_items) {  // uniform: the descriptors of split workgroup wg - n_append - n_items
+    stream_describe(a, wg - n_append - n_items, wave);
+    return;
+  }
   // item: (group, head tile), the stream plan's pair factor of them per group
   const int64_t item = wg - n_append;
-  if (item >= n_items) return;  // uniform
   const int P = stream_pair(a);
   const int64_t grp = item / P;
   const int hbase = 4 * (int)(item - grp * P);
@@ -2353,9 +2393,10 @@ hipError_t launch_step_prep(const EncodeArgs *ea, const DecodeArgs &a, hipStream
   // no append (ea null): the query operands of a verify block only
   const int64_t vectors = ea ? ea->num_tokens * ea->num_kv_heads : 0;
   const int n_append = (int)((vectors + kAppendWaves - 1) / kAppendWaves);
-  // one operands workgroup per (group, head tile)
+  // one operands workgroup per (group, head tile), then one per split
+  // workgroup for its waves' descriptors
   const int n_items = a.num_seqs * a.num_kv_heads * ((a.group * a.pos_count + 3) / 4);
-  const dim3 grid((unsigned)(n_append + n_items));
+  const dim3 grid((unsigned)(n_append + n_items + a.bal_grid));
   EncodeArgs none{};
   none.dtype = TQ_BF16;
   const EncodeArgs &e = ea ? *ea : none;

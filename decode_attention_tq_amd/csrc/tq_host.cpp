@@ -467,11 +467,15 @@ size_t stream_record_floats(int num_seqs, int rows, int num_kv_heads, int span) 
   return (size_t)(stream_runs(num_seqs, num_kv_heads, span) + (int64_t)num_seqs * num_kv_heads) * rows * kPartStride;
 }
 // The stream plan's workspace: the records, then the query operands of each
-// (group, head tile).
+// (group, head tile), then a descriptor per wave of the split pass's grid.
+size_t stream_qops_bytes(int num_seqs, int rows, int num_kv_heads) {
+  return (size_t)num_seqs * num_kv_heads * stream_pair(rows) * tq::kQopsDwords * 64 * sizeof(uint32_t);
+}
 size_t step_workspace(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int span) {
   const int rows = num_q_heads / num_kv_heads * q_len;
   return stream_record_floats(num_seqs, rows, num_kv_heads, span) * sizeof(float) +
-         (size_t)num_seqs * num_kv_heads * stream_pair(rows) * tq::kQopsDwords * 64 * sizeof(uint32_t);
+         stream_qops_bytes(num_seqs, rows, num_kv_heads) +
+         (size_t)stream_grid(num_seqs, num_kv_heads, rows, span) * 4 * tq::kDescWords * sizeof(uint32_t);
 }
 
 size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
@@ -643,6 +647,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.hot_max = hot ? hot->max : 0;
   a.cb = device_codebook(cb);
   a.qops = nullptr;
+  a.desc = nullptr;
   hipError_t e;
   if (fused || verify) {
     // stream plan: the records, then the operands (16-byte aligned: records of 528 bytes)
@@ -654,6 +659,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     a.partials = (float *)workspace;
     a.qops = reinterpret_cast<uint32_t *>(a.partials +
                                           stream_record_floats(num_seqs, group * q_len, num_kv_heads, span));
+    a.desc = a.qops + stream_qops_bytes(num_seqs, group * q_len, num_kv_heads) / sizeof(uint32_t);
     e = tq::launch_step_prep(fused ? step : nullptr, a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fused ? "decode step launch" : "verify operands launch");
   } else if (step) {

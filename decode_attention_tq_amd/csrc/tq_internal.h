@@ -131,9 +131,14 @@ struct DecodeArgs {
   // places): qops holds each (sequence, KV head) group's matrix operands,
   // kQopsDwords per lane (null otherwise).
   uint32_t *qops;
+  // The stream plan's per-wave descriptors (one per wave of the split pass's
+  // grid, kDescWords each), formed in the operands launch: the wave's block
+  // ids, tile slots and run, so the split pass starts on its pages at once.
+  uint32_t *desc;
   Codebook cb;
 };
 constexpr int kQopsDwords = 44;  // per lane: 5 fp6 operands of 6 dwords, 5 scales, 2 x 4 start values, 1 pad
+constexpr int kDescWords = 256;  // per wave: ids0 [64] | ids1 [64] | 16 slots x 4 | (tiles, run, head tile, 0) | pad
 
 constexpr int kHotChunk = 64;  // exact window tokens per partial record
 // Largest chunk of the matrix-core decode pass (64 tiles of 128 tokens).
