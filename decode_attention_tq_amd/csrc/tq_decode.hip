@@ -1689,6 +1689,16 @@ __device__ __forceinline__ void stream_describe(const DecodeArgs &a, int blk, in
     d[64 + lane] = (uint32_t)slot_ids(8);
   }
   if (lane == 0) *reinterpret_cast<int4 *>(d + 192) = make_int4(ntiles, iw, ut, 0);
+  // the merge's view of groups blk * 4 + wave, + 4 grid, ...: group g = (b,
+  // h)'s records are the places floor(C_g / q) + g .. floor((C_g + T_b - 1)
+  // / q) + g (no record when T_b = 0)
+  for (int g = blk * 4 + wave; g < a.num_seqs * a.num_kv_heads; g += 4 * a.bal_grid) {  // uniform
+    const int b = g / a.num_kv_heads, h = g - b * a.num_kv_heads;
+    int Pb, Tb;
+    stream_prefix(a, t0s, b, Pb, Tb);
+    const int c0 = Pb + h * Tb, i0 = c0 / q;
+    if (lane == 0) a.ginfo[g] = make_int2(i0 + g, Tb > 0 ? (c0 + Tb - 1) / q - i0 + 1 : 0);
+  }
 }
 
 // One reference R per head serves the scores and the accumulators: it moves
@@ -2245,16 +2255,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int64_t rows) 
     if (a.balanced == 2) {  // stream plan: the group's records are consecutive places
       const int hq = (int)(r % a.num_q_heads), h = hq / a.group, hd = t * a.group + hq - h * a.group;
       const int nrows = a.group * a.q_len;
-      const int t0s = span_tiles(a, lane_context(a, lane));
-      const int q = stream_per(a, stream_total(a, t0s));
-      int P, Tb;
-      stream_prefix(a, t0s, b, P, Tb);
-      if (Tb > 0) {  // uniform
-        const int c0 = P + h * Tb, i0 = c0 / q;
-        ns = (c0 + Tb - 1) / q - i0 + 1;
-        part += (((int64_t)i0 + (int64_t)b * a.num_kv_heads + h) * nrows + hd) * kPartStride;
-        rstride = (int64_t)nrows * kPartStride;
-      }
+      // the group's first place and record count, from the operands launch
+      const int2 gi = a.ginfo[(int64_t)b * a.num_kv_heads + h];
+      ns = __builtin_amdgcn_readfirstlane(gi.y);
+      part += ((int64_t)__builtin_amdgcn_readfirstlane(gi.x) * nrows + hd) * kPartStride;
+      rstride = (int64_t)nrows * kPartStride;
     } else {
       if (a.balanced) {
         const int per = bal_per(a, seq_tiles(a, lane));

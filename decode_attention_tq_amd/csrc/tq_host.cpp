@@ -471,11 +471,14 @@ size_t stream_record_floats(int num_seqs, int rows, int num_kv_heads, int span) 
 size_t stream_qops_bytes(int num_seqs, int rows, int num_kv_heads) {
   return (size_t)num_seqs * num_kv_heads * stream_pair(rows) * tq::kQopsDwords * 64 * sizeof(uint32_t);
 }
+size_t stream_desc_bytes(int num_seqs, int rows, int num_kv_heads, int span) {
+  return (size_t)stream_grid(num_seqs, num_kv_heads, rows, span) * 4 * tq::kDescWords * sizeof(uint32_t);
+}
 size_t step_workspace(int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int span) {
   const int rows = num_q_heads / num_kv_heads * q_len;
   return stream_record_floats(num_seqs, rows, num_kv_heads, span) * sizeof(float) +
-         stream_qops_bytes(num_seqs, rows, num_kv_heads) +
-         (size_t)stream_grid(num_seqs, num_kv_heads, rows, span) * 4 * tq::kDescWords * sizeof(uint32_t);
+         stream_qops_bytes(num_seqs, rows, num_kv_heads) + stream_desc_bytes(num_seqs, rows, num_kv_heads, span) +
+         (size_t)num_seqs * num_kv_heads * 2 * sizeof(int);  // the merge's (first place, records) per group
 }
 
 size_t decode_workspace(int bits, int num_seqs, int q_len, int num_q_heads, int num_kv_heads, int max_context_len,
@@ -648,6 +651,7 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   a.cb = device_codebook(cb);
   a.qops = nullptr;
   a.desc = nullptr;
+  a.ginfo = nullptr;
   hipError_t e;
   if (fused || verify) {
     // stream plan: the records, then the operands (16-byte aligned: records of 528 bytes)
@@ -660,6 +664,8 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
     a.qops = reinterpret_cast<uint32_t *>(a.partials +
                                           stream_record_floats(num_seqs, group * q_len, num_kv_heads, span));
     a.desc = a.qops + stream_qops_bytes(num_seqs, group * q_len, num_kv_heads) / sizeof(uint32_t);
+    a.ginfo = reinterpret_cast<int2 *>(a.desc + stream_desc_bytes(num_seqs, group * q_len, num_kv_heads, span) /
+                                                   sizeof(uint32_t));
     e = tq::launch_step_prep(fused ? step : nullptr, a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fused ? "decode step launch" : "verify operands launch");
   } else if (step) {

@@ -135,6 +135,9 @@ struct DecodeArgs {
   // grid, kDescWords each), formed in the operands launch: the wave's block
   // ids, tile slots and run, so the split pass starts on its pages at once.
   uint32_t *desc;
+  // and each (sequence, KV head) group's first record place and record
+  // count (x, y), formed in the same launch for the merge
+  int2 *ginfo;
   Codebook cb;
 };
 constexpr int kQopsDwords = 44;  // per lane: 5 fp6 operands of 6 dwords, 5 scales, 2 x 4 start values, 1 pad

@@ -441,8 +441,9 @@ def test_step_workspace(bits, Hq, Hkv, fused):
     floats) per query head of the group at each of runs + groups places, then
     the query operands (44 words per lane of a 64-lane wave) of each
     (sequence, KV head) group and head tile (two tiles for 5 to 8 heads),
-    then a descriptor of 256 words per wave of the split pass's grid.  An
-    unfused step needs the attention call's workspace."""
+    then a descriptor of 256 words per wave of the split pass's grid and two
+    words per group for the merge.  An unfused step needs the attention
+    call's workspace."""
     cb = ctypes.byref(_fake_cb(bits=bits))
     B, ctx = 16, 32768
     dec = tq._lib.tq_decode_workspace_bytes(cb, B, 1, Hq, Hkv, ctx, 0)
@@ -452,7 +453,8 @@ def test_step_workspace(bits, Hq, Hkv, fused):
         runs = max(2048, -(-(B * Hkv * 256) // 16))
         P = 2 if G > 4 else 1
         grid = (P * runs + 3) // 4 + 7
-        assert step == (runs + B * Hkv) * G * 132 * 4 + B * Hkv * P * 44 * 64 * 4 + grid * 4 * 256 * 4
+        assert step == ((runs + B * Hkv) * G * 132 * 4 + B * Hkv * P * 44 * 64 * 4 + grid * 4 * 256 * 4
+                        + B * Hkv * 8)
     else:
         assert step == dec
 
@@ -517,7 +519,8 @@ def test_stream_plan_covers_every_tile_within_the_workspace(G, q_len):
             ws = tq._lib.tq_decode_step_workspace_bytes(cb, B, Hq, Hkv, maxc, 0)
         else:
             ws = tq._lib.tq_decode_workspace_bytes(cb, B, q_len, Hq, Hkv, maxc, 0)
-        assert ws == (run_bound + groups) * rows * 132 * 4 + groups * P * 44 * 64 * 4 + grid * 4 * 256 * 4
+        assert ws == ((run_bound + groups) * rows * 132 * 4 + groups * P * 44 * 64 * 4 + grid * 4 * 256 * 4
+                      + groups * 8)
         assert runs <= run_bound
         # workgroups: blockIdx -> (die x, place in the die's run)
         reached = set()
