@@ -21,7 +21,7 @@ namespace {
 // fp32.  The record goes out as the token's chunk records, its scalars, and
 // the value bits merged with two atomics per plane word, so tokens that share
 // a page (and calls of the tiled kernel) never overwrite each other.
-constexpr int kAppendWaves = 4;
+// kAppendWaves such vectors share a workgroup.
 typedef __attribute__((address_space(1))) uint32_t append_gword;
 
 template <int DT>

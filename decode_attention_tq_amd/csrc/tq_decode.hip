@@ -2399,9 +2399,9 @@ hipError_t launch_step_prep(const EncodeArgs *ea, const DecodeArgs &a, hipStream
   const int64_t vectors = ea ? ea->num_tokens * ea->num_kv_heads : 0;
   const int n_append = (int)((vectors + kAppendWaves - 1) / kAppendWaves);
   // one operands workgroup per (group, head tile), then one per split
-  // workgroup for its waves' descriptors
+  // workgroup for its waves' descriptors (the host bounds the sum below 2^31)
   const int n_items = a.num_seqs * a.num_kv_heads * ((a.group * a.pos_count + 3) / 4);
-  const dim3 grid((unsigned)(n_append + n_items + a.bal_grid));
+  const dim3 grid((unsigned)((int64_t)n_append + n_items + a.bal_grid));
   EncodeArgs none{};
   none.dtype = TQ_BF16;
   const EncodeArgs &e = ea ? *ea : none;

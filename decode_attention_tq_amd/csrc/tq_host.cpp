@@ -467,7 +467,8 @@ size_t stream_record_floats(int num_seqs, int rows, int num_kv_heads, int span) 
   return (size_t)(stream_runs(num_seqs, num_kv_heads, span) + (int64_t)num_seqs * num_kv_heads) * rows * kPartStride;
 }
 // The stream plan's workspace: the records, then the query operands of each
-// (group, head tile), then a descriptor per wave of the split pass's grid.
+// (group, head tile), then a descriptor per wave of the split pass's grid,
+// then each group's (first record place, record count) for the merge.
 size_t stream_qops_bytes(int num_seqs, int rows, int num_kv_heads) {
   return (size_t)num_seqs * num_kv_heads * stream_pair(rows) * tq::kQopsDwords * 64 * sizeof(uint32_t);
 }
@@ -656,7 +657,10 @@ tq_status decode_impl(const tq_codebook *cb, const void *q, tq_dtype q_dtype,
   if (fused || verify) {
     // stream plan: the records, then the operands (16-byte aligned: records of 528 bytes)
     const int64_t grid = stream_grid(num_seqs, num_kv_heads, group * q_len, span);
-    if (grid > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "too many tiles for one launch");
+    // the first launch: the append's workgroups, one per (group, head tile), one per split workgroup
+    const int64_t first = (fused ? (step->num_tokens * num_kv_heads + tq::kAppendWaves - 1) / tq::kAppendWaves : 0) +
+                          (int64_t)num_seqs * num_kv_heads * stream_pair(group * q_len) + grid;
+    if (grid > 0x7fffffffLL || first > 0x7fffffffLL) return fail(TQ_ERR_UNSUPPORTED, "too many tiles for one launch");
     a.balanced = 2;
     a.bal_target = kStreamTarget;
     a.bal_grid = (int)grid;

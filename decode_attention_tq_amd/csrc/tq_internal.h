@@ -15,6 +15,7 @@ constexpr int kBlock = 16;
 constexpr int kKPage = 1088;
 constexpr int kVPage = 800;
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one workgroup
+constexpr int kAppendWaves = 4;     // appended vectors (one per wave) per workgroup of the step's first launch
 constexpr uint32_t kMagic = 0x54513031u;  // "TQ01"
 
 // Offsets inside a K page / V page (see tq.h).  K page: 64 records of 16
