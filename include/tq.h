@@ -190,8 +190,9 @@ tq_status tq_encode_kv(const tq_codebook *cb, const void *k, const void *v, tq_d
  * Errors: TQ_ERR_INVALID_ARGUMENT (nulls, Hq % Hkv != 0, q_len < 1,
  * q_len > max_context_len, bad tokens_per_split, a misaligned workspace
  * where alignment is required), TQ_ERR_UNSUPPORTED
- * (num_q_heads / num_kv_heads > 16, or tokens_per_split above 8192 where the
- * chunk limit above applies), TQ_ERR_WORKSPACE_TOO_SMALL. */
+ * (num_q_heads / num_kv_heads > 16, tokens_per_split above 8192 where the
+ * chunk limit above applies, or a batch whose launches would need 2^31 or
+ * more workgroups), TQ_ERR_WORKSPACE_TOO_SMALL. */
 size_t tq_decode_workspace_bytes(const tq_codebook *cb, int num_seqs, int q_len,
                                  int num_q_heads, int num_kv_heads, int max_context_len,
                                  int tokens_per_split);
